@@ -1,0 +1,168 @@
+"""Seeded synthetic inputs and the workload table.
+
+Shared by the GPU tests, the benchmark and the oracle's tests. Holds no part of
+the normalisation's arithmetic: ``gen.c`` draws counter-based SplitMix64 /
+Box-Muller numbers and encodes them in a storage format; this module wraps it
+and lists the workloads (shapes, dtypes, eps, distributions).
+
+Storage arrays are numpy ``float32`` for fp32 and ``uint16`` bit patterns for
+fp16 / bf16. Type codes: 0 = fp32, 1 = fp16, 2 = bf16, 3 = float64 (tests only).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import subprocess
+
+import numpy as np
+
+F32, F16, BF16, F64 = 0, 1, 2, 3
+DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
+ESIZE = {F32: 4, F16: 2, BF16: 2}
+
+# Stream ids per operand.
+STREAM_X, STREAM_R, STREAM_DY, STREAM_GAMMA = 1, 2, 3, 4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgen.so")
+SRC_PATH = os.path.join(_HERE, "gen.c")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    tmp = LIB_PATH + ".tmp"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC",
+                    "-shared", "-o", tmp, SRC_PATH, "-lm"], check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    u64, u32, i64, i32, d, vp = (ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64,
+                                 ctypes.c_int, ctypes.c_double, ctypes.c_void_p)
+    lib.gen_normal.argtypes = [u64, u32, i64, i64, i32, d, i64, vp, i32]
+    lib.gen_uniform.argtypes = [u64, u32, i64, d, d, i32, vp, i32]
+    lib.gen_bits.argtypes = [u64, u32, i64, vp]
+    for fn in (lib.gen_normal, lib.gen_uniform, lib.gen_bits):
+        fn.restype = None
+    lib.gen_splitmix64.argtypes = [u64]
+    lib.gen_splitmix64.restype = u64
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        return max(1, int(env))
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def storage_dtype(dt: int):
+    return {F32: np.float32, F64: np.float64}.get(dt, np.uint16)
+
+
+def normal(seed: int, stream: int, rows: int, cols: int, dt: int, row_scale: float = 1.0,
+           scale_every: int = 0, out: np.ndarray | None = None,
+           nthreads: int | None = None) -> np.ndarray:
+    """[rows, cols] standard normals in storage format dt. Rows whose index is
+    a multiple of ``scale_every`` (if > 0) are scaled by ``row_scale``."""
+    if out is None:
+        out = np.empty((rows, cols), storage_dtype(dt))
+    assert out.dtype == storage_dtype(dt) and out.size == rows * cols and out.flags.c_contiguous
+    _load().gen_normal(seed, stream, rows, cols, dt, row_scale, scale_every,
+                       out.ctypes.data, nthreads or default_threads())
+    return out
+
+
+def uniform(seed: int, stream: int, n: int, lo: float, hi: float, dt: int,
+            out: np.ndarray | None = None, nthreads: int | None = None) -> np.ndarray:
+    if out is None:
+        out = np.empty(n, storage_dtype(dt))
+    assert out.dtype == storage_dtype(dt) and out.size == n and out.flags.c_contiguous
+    _load().gen_uniform(seed, stream, n, lo, hi, dt, out.ctypes.data, nthreads or default_threads())
+    return out
+
+
+def splitmix64(z: int) -> int:
+    return int(_load().gen_splitmix64(z))
+
+
+def raw_bits(seed: int, stream: int, n: int) -> np.ndarray:
+    out = np.empty(n, np.uint64)
+    _load().gen_bits(seed, stream, n, out.ctypes.data)
+    return out
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One benchmark / parity workload."""
+    name: str
+    kind: str            # "fwd", "fused_add", "bwd"
+    M: int
+    N: int
+    x_dt: int
+    g_dt: int
+    eps: float
+    seed: int
+    store_rstd: bool = False
+    outlier_every: int = 0      # rows i with i % outlier_every == 0 are scaled
+    outlier_scale: float = 1.0
+
+    @property
+    def esize(self) -> int:
+        return ESIZE[self.x_dt]
+
+    @property
+    def gsize(self) -> int:
+        return ESIZE[self.g_dt]
+
+    def algorithmic_bytes(self) -> int:
+        """Each big operand read or written once, plus gamma, rstd, dgamma."""
+        big = self.M * self.N * self.esize
+        g = self.N * self.gsize
+        if self.kind == "fwd":
+            return 2 * big + g + (4 * self.M if self.store_rstd else 0)
+        if self.kind == "fused_add":
+            return 4 * big + g + (4 * self.M if self.store_rstd else 0)
+        # backward: read x, dy, rstd, gamma; write dx, dgamma (fp32)
+        return 3 * big + 4 * self.M + g + 4 * self.N
+
+
+# The five workloads: row-wise RMSNorm forward fp32 (short rows), forward bf16
+# with rstd (register-resident rows), fused residual add with fp32 gamma,
+# backward bf16, and forward fp16 with a row length that is not a multiple of
+# the 2048-element tile and with outlier rows.
+WORKLOADS = [
+    Workload("fwd_f32_m64_n1024", "fwd", 64, 1024, F32, F32, 1e-5, 1001),
+    Workload("fwd_bf16_m4096_n8192_rstd", "fwd", 4096, 8192, BF16, BF16, 1e-5, 1002,
+             store_rstd=True),
+    Workload("fusedadd_bf16_m16384_n4096_gf32", "fused_add", 16384, 4096, BF16, F32, 1e-5, 1003),
+    Workload("bwd_bf16_m8192_n8192", "bwd", 8192, 8192, BF16, BF16, 1e-5, 1004),
+    Workload("fwd_f16_m32768_n5000_outliers", "fwd", 32768, 5000, F16, F16, 1e-6, 1005,
+             outlier_every=97, outlier_scale=200.0),
+]
+WORKLOADS_BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def make_inputs(w: Workload, nthreads: int | None = None) -> dict:
+    """Host inputs for workload w: x, gamma, and r (fused add) or dy (backward).
+    The backward's saved rstd comes from the oracle forward and is not made here."""
+    out = {"x": normal(w.seed, STREAM_X, w.M, w.N, w.x_dt, w.outlier_scale, w.outlier_every,
+                       nthreads=nthreads),
+           "gamma": uniform(w.seed, STREAM_GAMMA, w.N, 0.5, 1.5, w.g_dt, nthreads=nthreads)}
+    if w.kind == "fused_add":
+        out["r"] = normal(w.seed, STREAM_R, w.M, w.N, w.x_dt, nthreads=nthreads)
+    if w.kind == "bwd":
+        out["dy"] = normal(w.seed, STREAM_DY, w.M, w.N, w.x_dt, nthreads=nthreads)
+    return out

@@ -1,0 +1,148 @@
+"""RMSNorm oracle (fp64, single-threaded C++), loaded through ctypes.
+
+TEST INFRASTRUCTURE ONLY: the reference the GPU path is checked against. Only
+the test suite, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg
+may import this package; the library under ``row_wise_normalization_fwd_amd``
+never does. The arithmetic lives in ``oracle.cpp`` (which cites the passages it
+follows); this module only marshals numpy arrays.
+
+Storage arrays are numpy ``float32`` for fp32 data and ``uint16`` bit patterns
+for fp16 / bf16 data. Type codes: 0 = fp32, 1 = fp16, 2 = bf16; 3 = plain float64 storage, used by
+the oracle's own checks (finite differences need unrounded inputs).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+F32, F16, BF16, F64 = 0, 1, 2, 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "oracle.cpp")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.cpp with g++ (host only). FP contraction is off so every
+    operation is a separately rounded double operation."""
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["g++", "-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-o", tmp, SRC_PATH]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32, dp = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                             ctypes.c_float, ctypes.c_void_p)
+    lib.oracle_decode.argtypes = [vp, i64, i32, dp]
+    lib.oracle_round.argtypes = [dp, i64, i32, vp]
+    lib.oracle_rmsnorm_fwd.argtypes = [vp, vp, i64, i64, f32, i32, i32, dp, vp, dp, vp, dp]
+    lib.oracle_rmsnorm_fused_add_fwd.argtypes = [vp, vp, vp, i64, i64, f32, i32, i32,
+                                                 vp, dp, vp, dp, vp, dp]
+    lib.oracle_rmsnorm_bwd.argtypes = [vp, vp, dp, vp, i64, i64, i32, i32,
+                                       dp, vp, dp, dp, dp, dp]
+    for fn in (lib.oracle_decode, lib.oracle_round, lib.oracle_rmsnorm_fwd,
+               lib.oracle_rmsnorm_fused_add_fwd, lib.oracle_rmsnorm_bwd):
+        fn.restype = None
+    _lib = lib
+    return lib
+
+
+def storage_dtype(dt: int):
+    return {F32: np.float32, F64: np.float64}.get(dt, np.uint16)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _check(a, dt, n, name):
+    a = np.ascontiguousarray(a)
+    if a.dtype != storage_dtype(dt):
+        raise TypeError(f"{name}: expected {storage_dtype(dt)} storage, got {a.dtype}")
+    if a.size != n:
+        raise ValueError(f"{name}: expected {n} elements, got {a.size}")
+    return a
+
+
+def decode(bits: np.ndarray, dt: int) -> np.ndarray:
+    bits = np.ascontiguousarray(bits)
+    out = np.empty(bits.shape, np.float64)
+    _load().oracle_decode(_ptr(bits), bits.size, dt, _ptr(out))
+    return out
+
+
+def round_to(v: np.ndarray, dt: int) -> np.ndarray:
+    """Round doubles to format dt (nearest, ties to even); returns storage array."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, storage_dtype(dt))
+    _load().oracle_round(_ptr(v), v.size, dt, _ptr(out))
+    return out
+
+
+def rmsnorm_fwd(x, gamma, M, N, eps, x_dt, g_dt, want_exact=True):
+    """Forward. Returns dict: y_exact (M,N) f64 or None, y (M,N) storage,
+    rstd_exact (M,) f64, rstd (M,) f32, ms (M,) f64."""
+    x = _check(x, x_dt, M * N, "x")
+    gamma = _check(gamma, g_dt, N, "gamma")
+    y_exact = np.empty((M, N), np.float64) if want_exact else None
+    y = np.empty((M, N), storage_dtype(x_dt))
+    rstd_exact = np.empty(M, np.float64)
+    rstd = np.empty(M, np.float32)
+    ms = np.empty(M, np.float64)
+    _load().oracle_rmsnorm_fwd(_ptr(x), _ptr(gamma), M, N, eps, x_dt, g_dt,
+                               _ptr(y_exact), _ptr(y), _ptr(rstd_exact), _ptr(rstd), _ptr(ms))
+    return dict(y_exact=y_exact, y=y, rstd_exact=rstd_exact, rstd=rstd, ms=ms)
+
+
+def rmsnorm_fused_add_fwd(x, r, gamma, M, N, eps, x_dt, g_dt, want_exact=True):
+    """Fused add + forward. Returns the forward's dict plus h (M,N) storage."""
+    x = _check(x, x_dt, M * N, "x")
+    r = _check(r, x_dt, M * N, "r")
+    gamma = _check(gamma, g_dt, N, "gamma")
+    h = np.empty((M, N), storage_dtype(x_dt))
+    y_exact = np.empty((M, N), np.float64) if want_exact else None
+    y = np.empty((M, N), storage_dtype(x_dt))
+    rstd_exact = np.empty(M, np.float64)
+    rstd = np.empty(M, np.float32)
+    ms = np.empty(M, np.float64)
+    _load().oracle_rmsnorm_fused_add_fwd(_ptr(x), _ptr(r), _ptr(gamma), M, N, eps, x_dt, g_dt,
+                                         _ptr(h), _ptr(y_exact), _ptr(y), _ptr(rstd_exact),
+                                         _ptr(rstd), _ptr(ms))
+    return dict(h=h, y_exact=y_exact, y=y, rstd_exact=rstd_exact, rstd=rstd, ms=ms)
+
+
+def rmsnorm_bwd(dy, x, rho, gamma, M, N, x_dt, g_dt, want_exact=True):
+    """Backward with saved rstd ``rho`` (any float array, widened to double).
+    Returns dict: dx_exact, dx (storage), dgamma, c, a, s (all f64 but dx)."""
+    dy = _check(dy, x_dt, M * N, "dy")
+    x = _check(x, x_dt, M * N, "x")
+    gamma = _check(gamma, g_dt, N, "gamma")
+    rho = np.ascontiguousarray(rho, dtype=np.float64)
+    if rho.size != M:
+        raise ValueError("rho: expected M elements")
+    dx_exact = np.empty((M, N), np.float64) if want_exact else None
+    dx = np.empty((M, N), storage_dtype(x_dt))
+    dgamma = np.empty(N, np.float64)
+    c = np.empty(M, np.float64)
+    a = np.empty(M, np.float64)
+    s = np.empty(N, np.float64)
+    _load().oracle_rmsnorm_bwd(_ptr(dy), _ptr(x), _ptr(rho), _ptr(gamma), M, N, x_dt, g_dt,
+                               _ptr(dx_exact), _ptr(dx), _ptr(dgamma), _ptr(c), _ptr(a), _ptr(s))
+    return dict(dx_exact=dx_exact, dx=dx, dgamma=dgamma, c=c, a=a, s=s)

@@ -1,0 +1,248 @@
+// RMSNorm oracle: plain, slow, single-threaded, fp64.
+//
+// TEST INFRASTRUCTURE ONLY. This file is the reference that GPU results are
+// checked against. Only the test suite, the smoke check and the CPU-baseline
+// leg of the benchmark may load it; the library's own code path never does,
+// and this file shares no code, header or constant table with the HIP kernels.
+//
+// Every function is the plain definition written out, with no blocking, fusion
+// or reordering:
+//
+//   * Forward ("Pre-built kernel library guide" (FlyDSL), section 1.2 RMSNorm):
+//       y_ij = x_ij / sqrt(mean_j(x_ij^2) + eps) * gamma_j,
+//     with the per-row reciprocal std rstd_i = 1 / sqrt(mean_j(x_ij^2) + eps)
+//     that the same section's optional store_rstd output holds (eps baked in).
+//   * Fused residual add ("TIRx kernels", FlashInfer ports, flashinfer.norm:
+//     fused_add_rmsnorm; FlyDSL guide section 1.2, fused-add wrappers): the pages
+//     name the operation without spelling it out. Reading taken: h = x + r is
+//     rounded once to the activation dtype, written back, and the rounded h is
+//     what is normalised.
+//   * Backward (FlyDSL guide section 1.2, "Backward"): inputs x, gamma, dy and
+//     the saved rstd (no eps); outputs dx and the fp32 weight gradient. The
+//     pages print no formula; it is the derivative of the forward above:
+//       c_i       = (1/N) sum_j dy_ij gamma_j x_ij
+//       dx_ij     = rho_i (gamma_j dy_ij - x_ij rho_i^2 c_i)
+//       dgamma_j  = sum_i dy_ij x_ij rho_i           (overwritten, not accumulated)
+//     where rho_i is the rstd handed in.
+//   * Rounding to bf16 / fp16 / fp32: round to nearest, ties to even (the FlyDSL
+//     guide, section 1.1, states RNE for the bf16 pack; IEEE default otherwise).
+//
+// Sums run sequentially in index order in double precision.
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+namespace {
+
+// Storage type codes used by this file's entry points.
+constexpr int kF32 = 0;
+constexpr int kF16 = 1;
+constexpr int kBF16 = 2;
+constexpr int kF64 = 3;  // plain double storage, used only by the oracle's own checks
+
+struct Format {
+  int frac_bits;      // stored fraction bits
+  int min_exp;        // exponent of the smallest normal number
+  double max_finite;  // largest finite value
+};
+
+Format format_of(int dt) {
+  switch (dt) {
+    case kF32:  return {23, -126, std::ldexp(2.0 - std::ldexp(1.0, -23), 127)};
+    case kF16:  return {10, -14, 65504.0};
+    default:    return {7, -126, std::ldexp(2.0 - std::ldexp(1.0, -7), 127)};
+  }
+}
+
+// Value of element idx of an array stored in format dt.
+double decode(const void* base, int64_t idx, int dt) {
+  if (dt == kF64) {
+    double d;
+    std::memcpy(&d, static_cast<const char*>(base) + 8 * idx, 8);
+    return d;
+  }
+  if (dt == kF32) {
+    float f;
+    std::memcpy(&f, static_cast<const char*>(base) + 4 * idx, 4);
+    return f;
+  }
+  uint16_t b;
+  std::memcpy(&b, static_cast<const char*>(base) + 2 * idx, 2);
+  if (dt == kBF16) {
+    // bf16 is the upper half of an fp32 pattern.
+    uint32_t u = static_cast<uint32_t>(b) << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+  }
+  // IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits.
+  int sign = b >> 15, e = (b >> 10) & 0x1f, m = b & 0x3ff;
+  double v;
+  if (e == 0) v = std::ldexp(static_cast<double>(m), -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = std::ldexp(static_cast<double>(1024 + m), e - 25);
+  return sign ? -v : v;
+}
+
+// Round v to the nearest value of format dt, ties to even; overflow gives inf.
+double round_to(double v, int dt) {
+  if (dt == kF64 || v == 0.0 || !std::isfinite(v)) return v;
+  Format f = format_of(dt);
+  int e;
+  std::frexp(std::fabs(v), &e);   // |v| = m * 2^e with m in [0.5, 1)
+  int lead = e - 1;               // exponent of the leading bit
+  if (lead < f.min_exp) lead = f.min_exp;  // subnormals share one quantum
+  double quantum = std::ldexp(1.0, lead - f.frac_bits);
+  double r = std::nearbyint(v / quantum) * quantum;  // default mode: ties to even
+  if (std::fabs(r) > f.max_finite) r = std::copysign(INFINITY, v);
+  return r;
+}
+
+// Bit pattern of a value that is already on the grid of format dt.
+uint32_t encode(double r, int dt) {
+  if (dt == kF32 || dt == kBF16) {
+    float f = static_cast<float>(r);  // exact: r is on the fp32 grid
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    return dt == kF32 ? u : (u >> 16);
+  }
+  uint32_t sign = std::signbit(r) ? 0x8000u : 0u;
+  double a = std::fabs(r);
+  if (std::isnan(r)) return 0x7e00u;
+  if (std::isinf(a)) return sign | 0x7c00u;
+  if (a < std::ldexp(1.0, -14))  // subnormal (or zero): units of 2^-24
+    return sign | static_cast<uint32_t>(a * std::ldexp(1.0, 24));
+  int e;
+  std::frexp(a, &e);
+  int lead = e - 1;
+  uint32_t frac = static_cast<uint32_t>(std::ldexp(a, 10 - lead)) - 1024u;
+  return sign | (static_cast<uint32_t>(lead + 15) << 10) | frac;
+}
+
+void store_bits(void* base, int64_t idx, uint32_t bits, int dt) {
+  if (dt == kF64) return;  // doubles are stored by store_value
+  if (dt == kF32) {
+    std::memcpy(static_cast<char*>(base) + 4 * idx, &bits, 4);
+  } else {
+    uint16_t b = static_cast<uint16_t>(bits);
+    std::memcpy(static_cast<char*>(base) + 2 * idx, &b, 2);
+  }
+}
+
+// Store v rounded to format dt.
+void store_value(void* base, int64_t idx, double v, int dt) {
+  if (dt == kF64) {
+    std::memcpy(static_cast<char*>(base) + 8 * idx, &v, 8);
+    return;
+  }
+  store_bits(base, idx, encode(round_to(v, dt), dt), dt);
+}
+
+// Forward on one row of values v[0..N): the definition, evaluated in double.
+void forward_row(const double* v, const void* gamma, int64_t N, float eps,
+                 int x_dt, int g_dt, int64_t row, double* y_exact, void* y_bits,
+                 double* rstd_exact, float* rstd_f32, double* ms_out) {
+  double ss = 0.0;
+  for (int64_t j = 0; j < N; ++j) ss += v[j] * v[j];
+  double ms = ss / static_cast<double>(N);
+  double denom = std::sqrt(ms + static_cast<double>(eps));
+  if (ms_out) ms_out[row] = ms;
+  if (rstd_exact) rstd_exact[row] = 1.0 / denom;
+  if (rstd_f32) rstd_f32[row] = static_cast<float>(round_to(1.0 / denom, kF32));
+  for (int64_t j = 0; j < N; ++j) {
+    double y = v[j] / denom * decode(gamma, j, g_dt);
+    if (y_exact) y_exact[row * N + j] = y;
+    if (y_bits) store_value(y_bits, row * N + j, y, x_dt);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+// Decode n stored values of format dt into doubles.
+void oracle_decode(const void* bits, int64_t n, int dt, double* out) {
+  for (int64_t k = 0; k < n; ++k) out[k] = decode(bits, k, dt);
+}
+
+// Round n doubles to format dt (nearest, ties to even) and store the patterns.
+void oracle_round(const double* v, int64_t n, int dt, void* bits) {
+  for (int64_t k = 0; k < n; ++k) store_value(bits, k, v[k], dt);
+}
+
+// RMSNorm forward over an [M, N] row-major array x (format x_dt) with weights
+// gamma[N] (format g_dt). Outputs, each optional (null = not wanted):
+//   y_exact[M*N]   the double-precision value before the output rounding
+//   y_bits[M*N]    that value rounded to x_dt
+//   rstd_exact[M]  1/sqrt(mean(x^2)+eps) in double;  rstd_f32[M] rounded to fp32
+//   ms[M]          mean(x^2)
+void oracle_rmsnorm_fwd(const void* x, const void* gamma, int64_t M, int64_t N,
+                        float eps, int x_dt, int g_dt, double* y_exact,
+                        void* y_bits, double* rstd_exact, float* rstd_f32,
+                        double* ms) {
+  std::vector<double> v(static_cast<size_t>(N));
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t j = 0; j < N; ++j) v[j] = decode(x, i * N + j, x_dt);
+    forward_row(v.data(), gamma, N, eps, x_dt, g_dt, i, y_exact, y_bits,
+                rstd_exact, rstd_f32, ms);
+  }
+}
+
+// Fused residual add + RMSNorm forward: h = round(x + r) is written to h_bits
+// (format x_dt) and the forward above is applied to h.
+void oracle_rmsnorm_fused_add_fwd(const void* x, const void* r, const void* gamma,
+                                  int64_t M, int64_t N, float eps, int x_dt,
+                                  int g_dt, void* h_bits, double* y_exact,
+                                  void* y_bits, double* rstd_exact,
+                                  float* rstd_f32, double* ms) {
+  std::vector<double> h(static_cast<size_t>(N));
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t j = 0; j < N; ++j) {
+      double s = decode(x, i * N + j, x_dt) + decode(r, i * N + j, x_dt);
+      h[j] = round_to(s, x_dt);
+      if (h_bits) store_value(h_bits, i * N + j, h[j], x_dt);
+    }
+    forward_row(h.data(), gamma, N, eps, x_dt, g_dt, i, y_exact, y_bits,
+                rstd_exact, rstd_f32, ms);
+  }
+}
+
+// RMSNorm backward. rho[M] is the saved rstd as doubles (the fp32 array the GPU
+// receives, widened exactly). Outputs, each optional:
+//   dx_exact[M*N], dx_bits[M*N] (rounded to x_dt), dgamma[N] (overwritten),
+//   c[M]  the per-row dot (1/N) sum_j dy gamma x,
+//   a[M]  (1/N) sum_j |dy gamma x|   and   s[N]  sum_i |dy x rho|,
+// the last two being the magnitudes the tests scale their error floors by.
+void oracle_rmsnorm_bwd(const void* dy, const void* x, const double* rho,
+                        const void* gamma, int64_t M, int64_t N, int x_dt,
+                        int g_dt, double* dx_exact, void* dx_bits,
+                        double* dgamma, double* c, double* a, double* s) {
+  if (dgamma) for (int64_t j = 0; j < N; ++j) dgamma[j] = 0.0;
+  if (s) for (int64_t j = 0; j < N; ++j) s[j] = 0.0;
+  for (int64_t i = 0; i < M; ++i) {
+    double dot = 0.0, mag = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+      double t = decode(dy, i * N + j, x_dt) * decode(gamma, j, g_dt) *
+                 decode(x, i * N + j, x_dt);
+      dot += t;
+      mag += std::fabs(t);
+    }
+    double ci = dot / static_cast<double>(N);
+    if (c) c[i] = ci;
+    if (a) a[i] = mag / static_cast<double>(N);
+    double p = rho[i];
+    for (int64_t j = 0; j < N; ++j) {
+      double xv = decode(x, i * N + j, x_dt);
+      double dyv = decode(dy, i * N + j, x_dt);
+      double d = p * (decode(gamma, j, g_dt) * dyv - xv * p * p * ci);
+      if (dx_exact) dx_exact[i * N + j] = d;
+      if (dx_bits) store_value(dx_bits, i * N + j, d, x_dt);
+      if (dgamma) dgamma[j] += dyv * xv * p;
+      if (s) s[j] += std::fabs(dyv * xv * p);
+    }
+  }
+}
+
+}  // extern "C"

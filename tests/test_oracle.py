@@ -1,0 +1,304 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test checks the oracle against something other than itself: hand-derived
+exact rows (tests/golden/exact_rows.txt), closed forms of special inputs,
+independent library rounding (numpy's float64->float16, torch's
+float32->bfloat16, C's double->float), exact decimal arithmetic, and central
+finite differences of the forward for the backward. Together they are chosen so
+that a plausible slip in the oracle (a dropped eps, N-1 for N, a wrong sign, a
+transposed operand, a misplaced gamma index, a wrong rounding tie) fails one.
+"""
+
+import decimal
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "exact_rows.txt")
+
+
+def _f16_all_finite():
+    p = np.arange(0, 0x7c00, dtype=np.uint16)
+    return p, p.view(np.float16).astype(np.float64)
+
+
+# ----------------------------------------------------------------- rounding
+
+def test_round_f16_matches_numpy_everywhere():
+    pats, vals = _f16_all_finite()
+    mids = (vals[:-1] + vals[1:]) / 2            # every tie between neighbours
+    rng = np.random.default_rng(1)
+    rand = rng.standard_normal(50000) * 10.0 ** rng.integers(-9, 6, 50000)
+    special = np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, -65520.0, 1e6, -1e6,
+                        2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14 - 2.0 ** -25,
+                        1 + 2.0 ** -11 + 2.0 ** -40])
+    v = np.concatenate([vals, -vals, mids, -mids, rand, special])
+    got = O.round_to(v, O.F16)
+    with np.errstate(over="ignore"):
+        want = v.astype(np.float16)
+    assert np.array_equal(got, want.view(np.uint16))
+
+
+def test_round_bf16_matches_torch_on_f32_values():
+    # All bf16 neighbours' midpoints are fp32 values, where torch's float32 ->
+    # bfloat16 conversion is round-to-nearest-even.
+    hi = np.arange(0, 0x7f80, dtype=np.uint32)
+    vals = (hi << 16).view(np.float32)
+    mids = ((hi[:-1] << 16) | 0x8000).view(np.float32)
+    rng = np.random.default_rng(2)
+    rand = (rng.standard_normal(50000) * 10.0 ** rng.integers(-30, 30, 50000)).astype(np.float32)
+    near_max = np.array([3.3895314e38, 3.3961776e38, 3.40e38, -3.40e38], np.float32)
+    v32 = np.concatenate([vals, -vals, mids, -mids, rand, near_max])
+    got = O.round_to(v32.astype(np.float64), O.BF16)
+    want = torch.from_numpy(v32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_round_f32_matches_c_conversion():
+    rng = np.random.default_rng(3)
+    rand = rng.standard_normal(100000) * 10.0 ** rng.integers(-40, 38, 100000)
+    f = rng.standard_normal(20000).astype(np.float32)
+    nxt = np.nextafter(f, np.float32(np.inf))
+    mids = (f.astype(np.float64) + nxt.astype(np.float64)) / 2    # exact ties
+    sub = np.array([1e-45, 7e-46, 2.0 ** -150, 3 * 2.0 ** -151, 1.2e-38, 3.5e38])
+    v = np.concatenate([rand, mids, -mids, sub])
+    with np.errstate(over="ignore"):
+        want = v.astype(np.float32)
+    assert np.array_equal(O.round_to(v, O.F32).view(np.uint32), want.view(np.uint32))
+
+
+def test_decode_all_16bit_patterns():
+    p = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f16 = O.decode(p, O.F16)
+    assert np.array_equal(f16, p.view(np.float16).astype(np.float64), equal_nan=True)
+    bf = O.decode(p, O.BF16)
+    want = torch.from_numpy(p.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(bf, want, equal_nan=True)
+
+
+# ------------------------------------------------------------------ forward
+
+def _golden_cases():
+    cases = []
+    with open(GOLDEN) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            eps, x, g, y, rstd = [part.strip() for part in line.split("|")]
+            cases.append((float(eps), [float(t) for t in x.split()],
+                          [float(t) for t in g.split()], [float(t) for t in y.split()],
+                          float(rstd)))
+    return cases
+
+
+@pytest.mark.parametrize("dt", [O.F32, O.F16, O.BF16, O.F64])
+def test_forward_exact_rows(dt):
+    cases = _golden_cases()
+    assert len(cases) >= 8
+    for eps, x, g, y, rstd in cases:
+        N = len(x)
+        xs, gs = O.round_to(np.array(x), dt), O.round_to(np.array(g), dt)
+        assert np.array_equal(O.decode(xs, dt), x) and np.array_equal(O.decode(gs, dt), g)
+        out = O.rmsnorm_fwd(xs, gs, 1, N, eps, dt, dt)
+        assert np.array_equal(out["y_exact"][0], np.array(y)), (eps, x)
+        assert np.array_equal(O.decode(out["y"], dt)[0], np.array(y)), (eps, x)
+        assert out["rstd_exact"][0] == pytest.approx(rstd, rel=1e-15)
+        assert out["rstd"][0] == np.float32(rstd)
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-5, 0.25])
+def test_forward_constant_row_closed_form(eps):
+    # Row of constant c: y_j = c / sqrt(c^2 + eps) * gamma_j.
+    # eps crosses the boundary as an fp32 value; both sides use that value.
+    N = 24
+    g = np.linspace(0.5, 1.5, N)
+    eps = float(np.float32(eps))
+    for c in [1e-3, 0.5, 3.0, -7.0, 2.0 ** -10, 123.25]:
+        out = O.rmsnorm_fwd(np.full(N, c), g, 1, N, eps, O.F64, O.F64)
+        want = c / math.sqrt(c * c + eps) * g
+        np.testing.assert_allclose(out["y_exact"][0], want, rtol=1e-14, atol=0)
+        assert out["rstd_exact"][0] == pytest.approx(1 / math.sqrt(c * c + eps), rel=1e-14)
+
+
+def test_forward_rms_is_one(gen_mod):
+    # gamma = 1: mean(y^2) = ms / (ms + eps), which is 1 at eps = 0.
+    M, N = 16, 1000
+    x = gen_mod.normal(7, 1, M, N, gen_mod.F64)
+    g = np.ones(N)
+    out0 = O.rmsnorm_fwd(x, g, M, N, 0.0, O.F64, O.F64)
+    np.testing.assert_allclose((out0["y_exact"] ** 2).mean(axis=1), 1.0, rtol=1e-13)
+    out1 = O.rmsnorm_fwd(x, g, M, N, 0.5, O.F64, O.F64)   # 0.5 is exact in fp32
+    ms = out0["ms"]
+    np.testing.assert_allclose((out1["y_exact"] ** 2).mean(axis=1), ms / (ms + 0.5), rtol=1e-13)
+    np.testing.assert_allclose(ms, (x ** 2).mean(axis=1), rtol=1e-13)
+
+
+def test_forward_scale_invariance(gen_mod):
+    M, N = 8, 257
+    x = gen_mod.normal(8, 1, M, N, gen_mod.F64)
+    g = gen_mod.uniform(8, 4, N, 0.5, 1.5, gen_mod.F64)
+    base = O.rmsnorm_fwd(x, g, M, N, 0.0, O.F64, O.F64)["y_exact"]
+    # Powers of two scale every intermediate exactly: results are identical.
+    for a in [2.0 ** -20, 0.25, 8.0, 2.0 ** 30]:
+        assert np.array_equal(O.rmsnorm_fwd(x * a, g, M, N, 0.0, O.F64, O.F64)["y_exact"], base)
+    for a in [3.0, 1e-3, 777.7]:
+        np.testing.assert_allclose(O.rmsnorm_fwd(x * a, g, M, N, 0.0, O.F64, O.F64)["y_exact"],
+                                   base, rtol=1e-13, atol=1e-300)
+    # With eps > 0: y(a x)_j = a x_j gamma_j / sqrt(a^2 ms + eps).
+    eps, a = float(np.float32(0.3)), 0.05
+    ms = (x ** 2).mean(axis=1, keepdims=True)
+    want = a * x * g / np.sqrt(a * a * ms + eps)
+    np.testing.assert_allclose(O.rmsnorm_fwd(x * a, g, M, N, eps, O.F64, O.F64)["y_exact"],
+                               want, rtol=1e-13)
+
+
+def test_forward_brute_force_decimal(gen_mod):
+    # 4 x 8 bf16 input, recomputed in 60-digit decimal arithmetic.
+    M, N, eps = 4, 8, 1e-5
+    x = gen_mod.normal(9, 1, M, N, gen_mod.BF16)
+    g = gen_mod.uniform(9, 4, N, 0.5, 1.5, gen_mod.BF16)
+    xd, gd = O.decode(x, O.BF16).reshape(M, N), O.decode(g, O.BF16)
+    out = O.rmsnorm_fwd(x, g, M, N, eps, O.BF16, O.BF16)
+    ctx = decimal.Context(prec=60)
+    D = decimal.Decimal
+    for i in range(M):
+        ss = D(0)
+        for j in range(N):
+            ss = ctx.add(ss, ctx.multiply(D(xd[i, j]), D(xd[i, j])))
+        denom = ctx.sqrt(ctx.add(ctx.divide(ss, D(N)), D(float(np.float32(eps)))))
+        for j in range(N):
+            want = ctx.multiply(ctx.divide(D(xd[i, j]), denom), D(gd[j]))
+            assert abs(out["y_exact"][i, j] - float(want)) <= 1e-15 * abs(float(want))
+        assert abs(out["rstd_exact"][i] - float(ctx.divide(D(1), denom))) <= 1e-15
+
+
+@pytest.mark.parametrize("dt", [O.F16, O.BF16])
+def test_fused_add_rounds_h_once_and_normalises_h(dt, gen_mod):
+    M, N = 32, 300
+    x = gen_mod.normal(10, 1, M, N, dt)
+    r = gen_mod.normal(10, 2, M, N, dt, row_scale=1e-3, scale_every=3)  # mixed magnitudes
+    g = gen_mod.uniform(10, 4, N, 0.5, 1.5, O.F32)
+    out = O.rmsnorm_fused_add_fwd(x, r, g, M, N, 1e-5, dt, O.F32)
+    s = O.decode(x, dt) + O.decode(r, dt)        # exact in double
+    if dt == O.F16:
+        want_h = s.astype(np.float16).view(np.uint16)
+    else:
+        want_h = torch.from_numpy(s.astype(np.float32)).to(torch.bfloat16).view(
+            torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(out["h"], want_h)
+    plain = O.rmsnorm_fwd(out["h"], g, M, N, 1e-5, dt, O.F32)
+    assert np.array_equal(out["y_exact"], plain["y_exact"])
+    assert np.array_equal(out["y"], plain["y"])
+    assert np.array_equal(out["rstd"], plain["rstd"])
+
+
+def test_forward_gamma_dtype_is_independent(gen_mod):
+    # fp32 gamma with bf16 activations uses the full fp32 gamma value.
+    M, N = 4, 64
+    x = gen_mod.normal(11, 1, M, N, O.BF16)
+    g32 = gen_mod.uniform(11, 4, N, 0.5, 1.5, O.F32)
+    out = O.rmsnorm_fwd(x, g32, M, N, 1e-5, O.BF16, O.F32)
+    xd = O.decode(x, O.BF16)
+    want = xd * out["rstd_exact"][:, None] * g32.astype(np.float64)[None, :]
+    np.testing.assert_allclose(out["y_exact"], want, rtol=1e-15)
+
+
+# ----------------------------------------------------------------- backward
+
+def _loss(x, g, dy, M, N, eps):
+    return float((dy * O.rmsnorm_fwd(x, g, M, N, eps, O.F64, O.F64)["y_exact"]).sum())
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-5, 0.3])
+def test_backward_matches_finite_differences(eps, gen_mod):
+    M, N = 4, 8
+    x = gen_mod.normal(12, 1, M, N, O.F64)
+    x[2, :] = 0.75                           # a constant row
+    x[3, :] *= 40.0                          # a large-scale row
+    dy = gen_mod.normal(12, 3, M, N, O.F64)
+    g = gen_mod.uniform(12, 4, N, 0.5, 1.5, O.F64)
+    fwd = O.rmsnorm_fwd(x, g, M, N, eps, O.F64, O.F64)
+    b = O.rmsnorm_bwd(dy, x, fwd["rstd_exact"], g, M, N, O.F64, O.F64)
+    fd_x = np.zeros((M, N))
+    for i in range(M):
+        for j in range(N):
+            h = 1e-5 * max(1.0, abs(x[i, j]))
+            xp, xm = x.copy(), x.copy()
+            xp[i, j] += h
+            xm[i, j] -= h
+            fd_x[i, j] = (_loss(xp, g, dy, M, N, eps) - _loss(xm, g, dy, M, N, eps)) / (2 * h)
+    fd_g = np.zeros(N)
+    for j in range(N):
+        h = 1e-5
+        gp, gm = g.copy(), g.copy()
+        gp[j] += h
+        gm[j] -= h
+        fd_g[j] = (_loss(x, gp, dy, M, N, eps) - _loss(x, gm, dy, M, N, eps)) / (2 * h)
+    for i in range(M):
+        scale = np.abs(fd_x[i]).max() + np.abs(dy[i] * g).max() / max(1.0, abs(x[i]).max())
+        assert np.abs(b["dx_exact"][i] - fd_x[i]).max() <= 1e-7 * scale, i
+    np.testing.assert_allclose(b["dgamma"], fd_g, rtol=1e-7, atol=1e-9)
+    # dx_bits is the exact value in fp64 storage
+    assert np.array_equal(b["dx"], b["dx_exact"])
+
+
+def test_backward_euler_invariant_with_saved_fp32_rstd(gen_mod):
+    # With the rho actually used: sum_j x_ij dx_ij = N c_i rho_i (1 - rho_i^2 ms_i).
+    M, N = 16, 512
+    x = gen_mod.normal(13, 1, M, N, O.BF16)
+    dy = gen_mod.normal(13, 3, M, N, O.BF16)
+    g = gen_mod.uniform(13, 4, N, 0.5, 1.5, O.BF16)
+    fwd = O.rmsnorm_fwd(x, g, M, N, 1e-5, O.BF16, O.BF16)
+    rho = fwd["rstd"].astype(np.float64)
+    b = O.rmsnorm_bwd(dy, x, rho, g, M, N, O.BF16, O.BF16)
+    xd = O.decode(x, O.BF16)
+    lhs = (xd * b["dx_exact"]).sum(axis=1)
+    rhs = N * b["c"] * rho * (1 - rho ** 2 * fwd["ms"])
+    mag = np.abs(xd * b["dx_exact"]).sum(axis=1)
+    assert np.all(np.abs(lhs - rhs) <= 1e-12 * mag)
+
+
+def test_backward_radial_direction(gen_mod):
+    # gamma = 1, dy = a x  =>  dx = a rho (1 - rho^2 ms) x; zero at eps = 0.
+    M, N, a = 6, 96, 2.0
+    x = gen_mod.normal(14, 1, M, N, O.F64)
+    g = np.ones(N)
+    for eps in [0.0, 0.2]:
+        fwd = O.rmsnorm_fwd(x, g, M, N, eps, O.F64, O.F64)
+        rho = fwd["rstd_exact"]
+        b = O.rmsnorm_bwd(a * x, x, rho, g, M, N, O.F64, O.F64)
+        want = a * rho[:, None] * (1 - rho[:, None] ** 2 * fwd["ms"][:, None]) * x
+        tol = 1e-13 * a * rho[:, None] * np.abs(x)
+        assert np.all(np.abs(b["dx_exact"] - want) <= tol + 1e-300)
+        if eps == 0.0:
+            assert np.abs(b["dx_exact"]).max() <= 1e-13 * a * rho.max() * np.abs(x).max()
+
+
+def test_dgamma_with_unit_dy_and_constant_rows():
+    # dy = 1 and row i constant c_i: dgamma_j = sum_i c_i / sqrt(c_i^2 + eps).
+    cs = np.array([0.5, -2.0, 3.0, 1e-3, 7.25])
+    M, N, eps = len(cs), 10, float(np.float32(1e-5))
+    x = np.repeat(cs[:, None], N, axis=1)
+    g = np.linspace(0.5, 1.5, N)
+    fwd = O.rmsnorm_fwd(x, g, M, N, eps, O.F64, O.F64)
+    b = O.rmsnorm_bwd(np.ones((M, N)), x, fwd["rstd_exact"], g, M, N, O.F64, O.F64)
+    want = float(sum(c / math.sqrt(c * c + eps) for c in cs))
+    np.testing.assert_allclose(b["dgamma"], want, rtol=1e-14)
+
+
+def test_backward_tolerance_magnitudes(gen_mod):
+    M, N = 3, 40
+    x = gen_mod.normal(15, 1, M, N, O.F64)
+    dy = gen_mod.normal(15, 3, M, N, O.F64)
+    g = gen_mod.uniform(15, 4, N, 0.5, 1.5, O.F64)
+    rho = np.array([0.9, 1.1, 2.0])
+    b = O.rmsnorm_bwd(dy, x, rho, g, M, N, O.F64, O.F64)
+    np.testing.assert_allclose(b["a"], np.abs(dy * g * x).mean(axis=1), rtol=1e-14)
+    np.testing.assert_allclose(b["s"], np.abs(dy * x * rho[:, None]).sum(axis=0), rtol=1e-14)
+    np.testing.assert_allclose(b["c"], (dy * g * x).mean(axis=1), rtol=1e-12, atol=1e-15)
