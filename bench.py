@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the row-wise RMSNorm library on one MI355X.
+
+A step is one call of the hot path on one batch: by default the bf16 forward
+over a [4096, 8192] batch that also writes the fp32 per-row rstd. Inputs are
+seeded synthetic data resident in HBM before timing starts. To measure HBM
+rather than the 256 MB Infinity Cache, consecutive steps rotate over R replicas
+of every operand (R * footprint >= --rotate-bytes, 1 GiB by default).
+
+Timing: W untimed warm-up steps, then exactly K steps between two HIP events
+recorded on the stream the kernels run on (torch's current stream), with a
+device synchronisation on both sides. value = algorithmic bytes per step
+(each big operand read or written once, plus gamma and rstd) / time per step.
+
+Also reported, in the same JSON line:
+  roofline      HBM-bound roofline of the step's kernel: achieved GB/s vs the
+                8 TB/s peak, and the measured HBM traffic per launch from the
+                committed rocprofv3 counter summary when it matches the
+                current kernel sources (else null);
+  cpu_baseline  the fp64 oracle, single-threaded, on the host, over repeated
+                full passes of the same batch for about --cpu-seconds;
+  workloads     the other four workloads (fp32 short rows, fused residual add,
+                backward, fp16 ragged rows) timed the same way;
+  calibration   a plain device-to-device copy of the step's byte count.
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0
+HEADLINE = "fwd_bf16_m4096_n8192_rstd"
+DT_NAMES = {0: "f32", 1: "f16", 2: "bf16"}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "row_wise_normalization_fwd_amd", "csrc")
+    for p in sorted(glob.glob(os.path.join(csrc, "*"))):
+        with open(p, "rb") as fh:
+            h.update(os.path.basename(p).encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+class Runner:
+    """Device replicas of one workload's operands and a launcher for step i."""
+
+    def __init__(self, w, rotate_bytes: float, host_inputs: dict):
+        import torch
+
+        import row_wise_normalization_fwd_amd as R
+
+        self.w = w
+        self.R = R
+        dev = torch.device("cuda:0")
+        tdt = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}
+        M, N = w.M, w.N
+
+        def dev_copy(a, dt):
+            import numpy as np
+            if dt == 0:
+                t = torch.from_numpy(a.reshape(-1))
+            else:
+                t = torch.from_numpy(a.reshape(-1).view(np.int16)).view(tdt[dt])
+            return t.to(dev)
+
+        big = M * N * w.esize
+        per_replica = {"fwd": 2 * big, "fused_add": 3 * big, "bwd": 3 * big}[w.kind]
+        self.replicas = max(1, int(-(-rotate_bytes // per_replica))) if rotate_bytes > 0 else 1
+        x0 = dev_copy(host_inputs["x"], w.x_dt)
+        g = dev_copy(host_inputs["gamma"], w.g_dt)
+        self.gamma = g
+        self.sets = []
+        stream = torch.cuda.current_stream(dev)
+        self.stream_handle = stream.cuda_stream
+        rstd_bwd = None
+        if w.kind == "bwd":
+            # The saved rstd comes from this library's own forward pass.
+            rstd_bwd = torch.empty(M, dtype=torch.float32, device=dev)
+            tmp = torch.empty_like(x0)
+            st = R.rmsnorm_fwd(x0, g, tmp, rstd_bwd, M, N, w.eps, w.x_dt, w.g_dt, stream)
+            assert st == 0, R.rmsnorm_status_string(st)
+            del tmp
+            dy0 = dev_copy(host_inputs["dy"], w.x_dt)
+            self.ws_bytes = R.rmsnorm_bwd_workspace_size(M, N, w.x_dt)
+        if w.kind == "fused_add":
+            r0 = dev_copy(host_inputs["r"], w.x_dt)
+        for i in range(self.replicas):
+            s = {"x": x0 if i == 0 else x0.clone()}
+            if w.kind == "fwd":
+                s["y"] = torch.empty_like(x0)
+                s["rstd"] = torch.empty(M, dtype=torch.float32, device=dev) if w.store_rstd else None
+            elif w.kind == "fused_add":
+                s["r"] = r0 if i == 0 else r0.clone()
+                s["y"] = torch.empty_like(x0)
+                s["rstd"] = torch.empty(M, dtype=torch.float32, device=dev) if w.store_rstd else None
+            else:
+                s["dy"] = dy0 if i == 0 else dy0.clone()
+                s["rstd"] = rstd_bwd
+                s["dx"] = torch.empty_like(x0)
+                s["dgamma"] = torch.empty(N, dtype=torch.float32, device=dev)
+                s["ws"] = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
+            self.sets.append(s)
+        torch.cuda.synchronize()
+        # Pre-marshalled integer arguments keep the host launch path short.
+        self.calls = []
+        lib = R.load_library()
+        for s in self.sets:
+            p = {k: (v.data_ptr() if v is not None else None) for k, v in s.items()}
+            if w.kind == "fwd":
+                args = (p["x"], g.data_ptr(), p["y"], p["rstd"], M, N, w.eps, w.x_dt, w.g_dt,
+                        self.stream_handle)
+                self.calls.append((lib.rmsnorm_fwd, args))
+            elif w.kind == "fused_add":
+                args = (p["x"], p["r"], g.data_ptr(), p["y"], p["rstd"], M, N, w.eps, w.x_dt,
+                        w.g_dt, self.stream_handle)
+                self.calls.append((lib.rmsnorm_fused_add_fwd, args))
+            else:
+                args = (p["dy"], p["x"], p["rstd"], g.data_ptr(), p["dx"], p["dgamma"], p["ws"],
+                        self.ws_bytes, M, N, w.x_dt, w.g_dt, self.stream_handle)
+                self.calls.append((lib.rmsnorm_bwd, args))
+
+    def step(self, i: int) -> None:
+        fn, args = self.calls[i % len(self.calls)]
+        st = fn(*args)
+        if st != 0:
+            raise RuntimeError(f"{self.w.name}: {self.R.rmsnorm_status_string(st)}")
+
+
+def time_steps(step, steps: int, warmup: int) -> float:
+    """Milliseconds per step over exactly `steps` back-to-back steps."""
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        step(warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def copy_calibration(nbytes: int, rotate_bytes: float, steps: int = 200) -> float:
+    """GB/s of a plain device-to-device tensor copy moving nbytes (read + write)
+    per step, over rotated buffers."""
+    import torch
+    half = nbytes // 2
+    reps = max(1, int(-(-rotate_bytes // nbytes)))
+    src = [torch.empty(half, dtype=torch.uint8, device="cuda").fill_(1) for _ in range(reps)]
+    dst = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(reps)]
+    ms = time_steps(lambda i: dst[i % reps].copy_(src[i % reps]), steps, 20)
+    del src, dst
+    return 2 * half / (ms * 1e-3) / 1e9
+
+
+def load_traffic(workload: str, src_hash: str):
+    """Measured HBM bytes per launch from the committed counter summary, if it
+    was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_src_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, host_inputs: dict, seconds: float) -> dict:
+    """The fp64 oracle, as it stands, timed on one host core."""
+    import oracle as O
+    O._load()
+    M, N = w.M, w.N
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        O.rmsnorm_fwd(host_inputs["x"], host_inputs["gamma"], M, N, w.eps, w.x_dt, w.g_dt,
+                      want_exact=False)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(w.algorithmic_bytes() * passes / el / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{passes} full passes over the {M}x{N} batch ({el:.1f} s, single thread,"
+                      f" host has {os.cpu_count()} logical CPUs)",
+            "rows_per_s": round(M * passes / el, 1)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-others", action="store_true", help="time only the headline workload")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world})", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import gen as G
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    src_hash = kernel_source_hash()
+
+    w = G.WORKLOADS_BY_NAME[args.workload]
+    host = G.make_inputs(w)
+    run = Runner(w, args.rotate_bytes, host)
+    ms = time_steps(run.step, args.steps, args.warmup)
+    nbytes = w.algorithmic_bytes()
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    hot = Runner(w, 0, host)
+    hot_ms = time_steps(hot.step, max(args.steps // 2, 10), max(args.warmup // 2, 5))
+    del hot
+    calib = copy_calibration(2 * w.M * w.N * w.esize, args.rotate_bytes)
+
+    result = {
+        "metric": "achieved HBM GB/s (% of MI355X peak) and rows/s, RMSNorm fwd/bwd",
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded SplitMix64/Box-Muller, inputs resident in HBM)",
+        "config": {"workload": w.name, "kind": w.kind, "M": w.M, "N": w.N,
+                   "io_dtype": DT_NAMES[w.x_dt], "gamma_dtype": DT_NAMES[w.g_dt], "eps": w.eps,
+                   "rstd_out": w.store_rstd, "rotation_replicas": run.replicas,
+                   "algorithmic_bytes_per_step": nbytes},
+        "rows_per_s": round(w.M / (ms * 1e-3), 1),
+        "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / PEAK_GBPS, 4),
+                     "traffic": load_traffic(w.name, src_hash),
+                     "kernel": "fwd_reg_kernel" if w.kind == "fwd" else w.kind,
+                     "kernel_src_hash": src_hash},
+        "hot_cache_gbps": round(nbytes / (hot_ms * 1e-3) / 1e9, 2),
+        "calibration": {"copy_gbps": round(calib, 2), "what": "torch device-to-device copy, "
+                        "same read+write bytes, rotated"},
+    }
+    del run
+    torch.cuda.empty_cache()
+
+    if not args.no_others:
+        others = {}
+        for ow in G.WORKLOADS:
+            if ow.name == w.name:
+                continue
+            oh = G.make_inputs(ow)
+            orun = Runner(ow, 0 if ow.M * ow.N < (1 << 20) else args.rotate_bytes, oh)
+            est = max(ow.algorithmic_bytes() / 6e12, 3e-6)
+            k = int(min(2000, max(50, 0.05 / est)))
+            oms = time_steps(orun.step, k, max(k // 10, 5))
+            ob = ow.algorithmic_bytes()
+            others[ow.name] = {"ms_per_step": round(oms, 6), "gbps": round(ob / (oms * 1e-3) / 1e9, 2),
+                               "pct_of_peak": round(100 * ob / (oms * 1e-3) / 1e9 / PEAK_GBPS, 2),
+                               "rows_per_s": round(ow.M / (oms * 1e-3), 1),
+                               "steps": k, "rotation_replicas": orun.replicas}
+            if ow.kind == "bwd":
+                others[ow.name]["workspace_bytes"] = orun.ws_bytes
+            del orun, oh
+            torch.cuda.empty_cache()
+        result["workloads"] = others
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

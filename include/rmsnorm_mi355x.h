@@ -1,0 +1,128 @@
+/* rmsnorm_mi355x.h -- C ABI of the row-wise RMSNorm library for MI355X (gfx950).
+ *
+ * The operation ("Pre-built kernel library guide" (FlyDSL), section 1.2 RMSNorm):
+ * for every row i of a row-major [M, N] array,
+ *     rstd_i = 1 / sqrt(mean_j(x_ij^2) + eps)
+ *     y_ij   = x_ij * rstd_i * gamma_j
+ * with fp32 accumulation and one round-to-nearest-even rounding at each store.
+ *
+ * Conventions shared by every call:
+ *   - All data pointers are DEVICE pointers owned by the caller; arrays are
+ *     contiguous and row-major ("contiguous 2-D ... row-major rows", FlyDSL guide
+ *     section 2.2). The library never allocates, frees or synchronises.
+ *   - Work is enqueued on the caller's stream and runs asynchronously; the call
+ *     returns once the kernels are launched.
+ *   - Type codes (rmsn_dtype): activations x, r/h, y, dy, dx share x_dtype in
+ *     {RMSN_F32, RMSN_F16, RMSN_BF16}; gamma_dtype is x_dtype or RMSN_F32 (fp32
+ *     weights with 16-bit activations, FlyDSL guide section 1.2); rstd and
+ *     dgamma are always fp32.
+ *   - Shapes: M >= 0 rows, N >= 1 columns. M == 0 is a no-op returning RMSN_OK
+ *     (pointers are not inspected). Every pointer must be aligned to its element
+ *     size; 16-byte-aligned rows (base aligned and N * element size a multiple
+ *     of 16) take the vectorised path, anything else a scalar path.
+ *   - Errors: argument errors are detected on the host before any HIP call and
+ *     returned as negative rmsn_status codes; nothing is enqueued then. A
+ *     failed launch returns RMSN_ERR_HIP and rmsnorm_last_hip_error() gives the
+ *     hipError_t. Faults during execution surface at the caller's next
+ *     synchronisation, as for any asynchronous HIP work.
+ *   - Thread safety: the calls keep no state besides the per-thread last HIP
+ *     error; concurrent calls on different buffers are safe.
+ */
+#ifndef RMSNORM_MI355X_H
+#define RMSNORM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RMSN_F32 = 0,
+  RMSN_F16 = 1,
+  RMSN_BF16 = 2
+} rmsn_dtype;
+
+typedef enum {
+  RMSN_OK = 0,
+  RMSN_ERR_NULL = -1,       /* a required pointer is null */
+  RMSN_ERR_SHAPE = -2,      /* M < 0, N < 1, or M * N too large to index */
+  RMSN_ERR_DTYPE = -3,      /* unsupported x_dtype / gamma_dtype pair */
+  RMSN_ERR_WORKSPACE = -4,  /* backward workspace null or too small */
+  RMSN_ERR_OVERLAP = -5,    /* buffers overlap in a way the call forbids */
+  RMSN_ERR_ALIGN = -6,      /* a pointer is not aligned to its element size */
+  RMSN_ERR_EPS = -7,        /* eps negative or not finite */
+  RMSN_ERR_HIP = -100       /* a kernel launch failed; see rmsnorm_last_hip_error */
+} rmsn_status;
+
+/* Forward RMSNorm (FlyDSL guide section 1.2, build_rmsnorm_module with
+ * store_rstd and weight_dtype_str).
+ *   x      [M, N] x_dtype, read.
+ *   gamma  [N] gamma_dtype, read.
+ *   y      [M, N] x_dtype, written. y == x (exact in-place) is allowed; any
+ *          other overlap with x, gamma or rstd is RMSN_ERR_OVERLAP.
+ *   rstd   [M] fp32, written with 1/sqrt(mean(x^2)+eps) per row; may be NULL.
+ *   eps    finite, >= 0; added to the mean square inside the square root.
+ * Rows with N <= 8192 stay in registers, longer rows are cached in LDS (or
+ * re-read when a row exceeds the LDS cache). */
+int rmsnorm_fwd(const void* x, const void* gamma, void* y, float* rstd,
+                int64_t M, int64_t N, float eps, int x_dtype, int gamma_dtype,
+                hipStream_t stream);
+
+/* Fused residual add + forward RMSNorm ("TIRx kernels", FlashInfer ports,
+ * flashinfer.norm fused_add_rmsnorm; FlyDSL guide section 1.2 fused-add
+ * wrappers). The pages name the operation without defining it; this library
+ * reads it as
+ *     h_ij = round_x_dtype(x_ij + r_ij)     (sum in fp32, one rounding)
+ *     residual <- h  (in place),   y = RMSNorm(h)   (of the rounded h)
+ *   x         [M, N] x_dtype, read. x == residual (exact) is allowed.
+ *   residual  [M, N] x_dtype, read as r and overwritten with h.
+ *   gamma, rstd, eps as in rmsnorm_fwd.
+ *   y         [M, N] x_dtype, written; may equal x exactly, must not overlap
+ *             residual, gamma or rstd. */
+int rmsnorm_fused_add_fwd(const void* x, void* residual, const void* gamma, void* y,
+                          float* rstd, int64_t M, int64_t N, float eps, int x_dtype,
+                          int gamma_dtype, hipStream_t stream);
+
+/* Bytes of device workspace rmsnorm_bwd needs for an [M, N] problem of the
+ * given activation dtype: fp32 per-workgroup dgamma partials (and per-row
+ * scalars for rows too long to keep on chip). Pure host function; returns 0
+ * for M <= 0 or N <= 0 and for an unknown dtype. */
+size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int x_dtype);
+
+/* Backward RMSNorm (FlyDSL guide section 1.2, "Backward": inputs x, gamma, dy
+ * and the saved rstd, no eps since the forward baked it into rstd). With
+ * rho_i = rstd[i] and c_i = (1/N) sum_j dy_ij gamma_j x_ij:
+ *     dx_ij     = rho_i * (gamma_j dy_ij - x_ij rho_i^2 c_i)
+ *     dgamma_j  = sum_i dy_ij x_ij rho_i          (fp32, OVERWRITTEN)
+ * dgamma is reduced in two stages (per-workgroup fp32 partials in the
+ * workspace, then a fixed-order column sum) with no atomics, so repeated calls
+ * with the same inputs give bit-identical dx and dgamma.
+ *   dy, x     [M, N] x_dtype, read.
+ *   rstd      [M] fp32, read.
+ *   gamma     [N] gamma_dtype, read.
+ *   dx        [M, N] x_dtype, written; may equal dy or x exactly.
+ *   dgamma    [N] fp32, written.
+ *   workspace at least rmsnorm_bwd_workspace_size(M, N, x_dtype) bytes of
+ *             device memory, 16-byte aligned, disjoint from every other buffer;
+ *             its contents on entry are ignored.
+ * The workgroup partition depends only on (M, N, x_dtype), which fixes the
+ * summation order. */
+int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* gamma,
+                void* dx, float* dgamma, void* workspace, size_t workspace_bytes,
+                int64_t M, int64_t N, int x_dtype, int gamma_dtype, hipStream_t stream);
+
+/* Static English description of a status code ("unknown status" otherwise). */
+const char* rmsnorm_status_string(int status);
+
+/* hipError_t (as int) of the last failed launch on the calling thread, or 0. */
+int rmsnorm_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_MI355X_H */

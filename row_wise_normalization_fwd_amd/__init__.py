@@ -1,0 +1,197 @@
+"""Row-wise RMSNorm for MI355X (gfx950): Python binding of librmsnorm_mi355x.so.
+
+The C ABI (include/rmsnorm_mi355x.h) is exposed under the same names
+(``rmsnorm_fwd``, ``rmsnorm_fused_add_fwd``, ``rmsnorm_bwd``,
+``rmsnorm_bwd_workspace_size``, ``rmsnorm_status_string``,
+``rmsnorm_last_hip_error``); those functions only marshal arguments. Pointers
+may be given as integers or as torch tensors (their ``data_ptr()``); streams as
+integers or ``torch.cuda.Stream`` objects.
+
+``fwd``, ``fused_add_fwd`` and ``bwd`` are torch conveniences on top: they use
+torch only to allocate outputs and to pick the current stream, and every step
+of the computation runs in the library's HIP kernels. There is no fallback: if
+the library is not built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "librmsnorm_mi355x.so"
+LIB_PATH = os.path.join(_HERE, LIB_NAME)
+
+RMSN_F32, RMSN_F16, RMSN_BF16 = 0, 1, 2
+RMSN_OK = 0
+STATUS_NAMES = {
+    0: "RMSN_OK", -1: "RMSN_ERR_NULL", -2: "RMSN_ERR_SHAPE", -3: "RMSN_ERR_DTYPE",
+    -4: "RMSN_ERR_WORKSPACE", -5: "RMSN_ERR_OVERLAP", -6: "RMSN_ERR_ALIGN",
+    -7: "RMSN_ERR_EPS", -100: "RMSN_ERR_HIP",
+}
+ENTRY_POINTS = ("rmsnorm_fwd", "rmsnorm_fused_add_fwd", "rmsnorm_bwd",
+                "rmsnorm_bwd_workspace_size", "rmsnorm_status_string", "rmsnorm_last_hip_error")
+
+
+class RMSNormError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = STATUS_NAMES.get(status, str(status))
+        msg = f"{where} failed: {name}: {rmsnorm_status_string(status)}"
+        if status == -100:
+            msg += f" (hipError {rmsnorm_last_hip_error()})"
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Load the built HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{LIB_NAME} is not built at {path}; build it with "
+            "`python -m row_wise_normalization_fwd_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    lib.rmsnorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.rmsnorm_fwd.restype = i32
+    lib.rmsnorm_fused_add_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.rmsnorm_fused_add_fwd.restype = i32
+    lib.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i32]
+    lib.rmsnorm_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i32, i32, vp]
+    lib.rmsnorm_bwd.restype = i32
+    lib.rmsnorm_status_string.argtypes = [i32]
+    lib.rmsnorm_status_string.restype = ctypes.c_char_p
+    lib.rmsnorm_last_hip_error.argtypes = []
+    lib.rmsnorm_last_hip_error.restype = i32
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _p(v):
+    """Pointer argument: None, an int address, or a tensor's data_ptr()."""
+    if v is None:
+        return None
+    if isinstance(v, int):
+        return v or None
+    return v.data_ptr() or None
+
+
+def _s(stream):
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+# ------------------------------------------------------- C ABI, same names
+
+def rmsnorm_fwd(x, gamma, y, rstd, M, N, eps, x_dtype, gamma_dtype, stream) -> int:
+    return load_library().rmsnorm_fwd(_p(x), _p(gamma), _p(y), _p(rstd), M, N, eps,
+                                      x_dtype, gamma_dtype, _s(stream))
+
+
+def rmsnorm_fused_add_fwd(x, residual, gamma, y, rstd, M, N, eps, x_dtype, gamma_dtype,
+                          stream) -> int:
+    return load_library().rmsnorm_fused_add_fwd(_p(x), _p(residual), _p(gamma), _p(y), _p(rstd),
+                                                M, N, eps, x_dtype, gamma_dtype, _s(stream))
+
+
+def rmsnorm_bwd_workspace_size(M, N, x_dtype) -> int:
+    return int(load_library().rmsnorm_bwd_workspace_size(M, N, x_dtype))
+
+
+def rmsnorm_bwd(dy, x, rstd, gamma, dx, dgamma, workspace, workspace_bytes, M, N, x_dtype,
+                gamma_dtype, stream) -> int:
+    return load_library().rmsnorm_bwd(_p(dy), _p(x), _p(rstd), _p(gamma), _p(dx), _p(dgamma),
+                                      _p(workspace), workspace_bytes, M, N, x_dtype, gamma_dtype,
+                                      _s(stream))
+
+
+def rmsnorm_status_string(status: int) -> str:
+    return load_library().rmsnorm_status_string(status).decode()
+
+
+def rmsnorm_last_hip_error() -> int:
+    return int(load_library().rmsnorm_last_hip_error())
+
+
+# ------------------------------------------------------- torch conveniences
+
+def dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: RMSN_F32, torch.float16: RMSN_F16, torch.bfloat16: RMSN_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _rows(t, N):
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    if t.shape[-1] != N:
+        raise ValueError(f"last dimension {t.shape[-1]} != N = {N}")
+    return t.numel() // N
+
+
+def _check(status, where):
+    if status != RMSN_OK:
+        raise RMSNormError(status, where)
+
+
+def fwd(x, gamma, eps: float = 1e-5, *, want_rstd: bool = False, out=None, rstd=None,
+        stream=None):
+    """y = RMSNorm(x) over the last dimension; returns (y, rstd or None)."""
+    import torch
+    N = gamma.numel()
+    M = _rows(x, N)
+    y = torch.empty_like(x) if out is None else out
+    if want_rstd and rstd is None:
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    stream = torch.cuda.current_stream(x.device) if stream is None else stream
+    _check(rmsnorm_fwd(x, gamma, y, rstd, M, N, eps, dtype_code(x), dtype_code(gamma), stream),
+           "rmsnorm_fwd")
+    return y, rstd
+
+
+def fused_add_fwd(x, residual, gamma, eps: float = 1e-5, *, want_rstd: bool = False, out=None,
+                  rstd=None, stream=None):
+    """residual <- x + residual (rounded), y = RMSNorm(residual); returns (y, rstd)."""
+    import torch
+    N = gamma.numel()
+    M = _rows(x, N)
+    if residual.shape != x.shape or residual.dtype != x.dtype:
+        raise ValueError("residual must match x in shape and dtype")
+    y = torch.empty_like(x) if out is None else out
+    if want_rstd and rstd is None:
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    stream = torch.cuda.current_stream(x.device) if stream is None else stream
+    _check(rmsnorm_fused_add_fwd(x, residual, gamma, y, rstd, M, N, eps, dtype_code(x),
+                                 dtype_code(gamma), stream), "rmsnorm_fused_add_fwd")
+    return y, rstd
+
+
+def bwd(dy, x, rstd, gamma, *, dx=None, dgamma=None, workspace=None, stream=None):
+    """Returns (dx, dgamma fp32). The workspace is allocated if not given."""
+    import torch
+    N = gamma.numel()
+    M = _rows(x, N)
+    if dy.shape != x.shape or dy.dtype != x.dtype:
+        raise ValueError("dy must match x in shape and dtype")
+    dx = torch.empty_like(x) if dx is None else dx
+    dgamma = torch.empty(N, dtype=torch.float32, device=x.device) if dgamma is None else dgamma
+    ws_bytes = rmsnorm_bwd_workspace_size(M, N, dtype_code(x))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    stream = torch.cuda.current_stream(x.device) if stream is None else stream
+    _check(rmsnorm_bwd(dy, x, rstd, gamma, dx, dgamma, workspace, workspace.numel(), M, N,
+                       dtype_code(x), dtype_code(gamma), stream), "rmsnorm_bwd")
+    return dx, dgamma

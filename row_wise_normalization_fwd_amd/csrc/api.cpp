@@ -1,0 +1,175 @@
+// Host side of the C ABI declared in include/rmsnorm_mi355x.h: argument
+// validation (before any HIP call), the backward partition, status strings.
+#include "rmsnorm_mi355x.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int esize_of(int dt) { return dt == RMSN_F32 ? 4 : 2; }
+
+bool valid_dtype(int dt) { return dt == RMSN_F32 || dt == RMSN_F16 || dt == RMSN_BF16; }
+
+// gamma is either the activation type or fp32.
+bool valid_pair(int x_dt, int g_dt) {
+  return valid_dtype(x_dt) && (g_dt == x_dt || g_dt == RMSN_F32);
+}
+
+bool aligned(const void* p, int bytes) {
+  return (reinterpret_cast<uintptr_t>(p) % static_cast<uintptr_t>(bytes)) == 0;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void* p, uint64_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return {a, a + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Overlap that is not an exact alias of two equal-size buffers.
+bool partial_overlap(Range a, Range b) { return overlap(a, b) && !(a.lo == b.lo && a.hi == b.hi); }
+
+// M * N elements must be addressable with 64-bit offsets and N by an int.
+bool shape_ok(int64_t M, int64_t N) {
+  if (M < 0 || N < 1 || N > INT32_MAX) return false;
+  return M == 0 || M <= (INT64_MAX / 8) / N;
+}
+
+int finish(hipError_t e) {
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return RMSN_ERR_HIP;
+  }
+  return RMSN_OK;
+}
+
+hipError_t launch_forward(const rmsn::FwdCall& c, int x_dtype) {
+  switch (x_dtype) {
+    case RMSN_F32: return rmsn::launch_fwd_f32(c);
+    case RMSN_F16: return rmsn::launch_fwd_f16(c);
+    default: return rmsn::launch_fwd_bf16(c);
+  }
+}
+
+// Shared validation of the forward calls; `fused` selects the residual add.
+int forward(bool fused, const void* x, void* residual, const void* gamma, void* y, float* rstd,
+            int64_t M, int64_t N, float eps, int x_dtype, int gamma_dtype, hipStream_t stream) {
+  if (!valid_pair(x_dtype, gamma_dtype)) return RMSN_ERR_DTYPE;
+  if (!shape_ok(M, N)) return RMSN_ERR_SHAPE;
+  if (!std::isfinite(eps) || eps < 0.0f) return RMSN_ERR_EPS;
+  if (M == 0) return RMSN_OK;
+  if (!x || !gamma || !y || (fused && !residual)) return RMSN_ERR_NULL;
+  const int es = esize_of(x_dtype), gs = esize_of(gamma_dtype);
+  if (!aligned(x, es) || !aligned(y, es) || !aligned(gamma, gs) || (rstd && !aligned(rstd, 4)) ||
+      (residual && !aligned(residual, es)))
+    return RMSN_ERR_ALIGN;
+  const uint64_t big = static_cast<uint64_t>(M) * static_cast<uint64_t>(N) * es;
+  const Range rx = span(x, big), ry = span(y, big), rg = span(gamma, static_cast<uint64_t>(N) * gs);
+  if (partial_overlap(ry, rx) || overlap(ry, rg)) return RMSN_ERR_OVERLAP;
+  if (rstd) {
+    const Range rr = span(rstd, static_cast<uint64_t>(M) * 4);
+    if (overlap(rr, rx) || overlap(rr, ry) || overlap(rr, rg)) return RMSN_ERR_OVERLAP;
+    if (residual && overlap(rr, span(residual, big))) return RMSN_ERR_OVERLAP;
+  }
+  if (residual) {
+    const Range rs = span(residual, big);
+    if (partial_overlap(rs, rx) || overlap(rs, ry) || overlap(rs, rg)) return RMSN_ERR_OVERLAP;
+  }
+  rmsn::FwdCall c{x, residual, gamma, y, rstd, M, N, eps, gamma_dtype, stream};
+  return finish(launch_forward(c, x_dtype));
+}
+
+}  // namespace
+
+namespace rmsn {
+
+BwdPlan plan_bwd(int64_t M, int64_t N, int x_dtype) {
+  BwdPlan p{false, 0, 0, 0};
+  if (!valid_dtype(x_dtype) || M <= 0 || N <= 0) return p;
+  p.supported = N <= bwd_max_n(esize_of(x_dtype));
+  p.rows_per_block = ceil_div(M, kBwdTargetBlocks);
+  p.blocks = ceil_div(M, p.rows_per_block);
+  // One fp32 partial row per block, rounded up to 256 bytes.
+  const uint64_t bytes = static_cast<uint64_t>(p.blocks) * static_cast<uint64_t>(N) * 4u;
+  p.workspace_bytes = static_cast<size_t>((bytes + 255u) & ~static_cast<uint64_t>(255u));
+  return p;
+}
+
+}  // namespace rmsn
+
+extern "C" {
+
+int rmsnorm_fwd(const void* x, const void* gamma, void* y, float* rstd, int64_t M, int64_t N,
+                float eps, int x_dtype, int gamma_dtype, hipStream_t stream) {
+  return forward(false, x, nullptr, gamma, y, rstd, M, N, eps, x_dtype, gamma_dtype, stream);
+}
+
+int rmsnorm_fused_add_fwd(const void* x, void* residual, const void* gamma, void* y, float* rstd,
+                          int64_t M, int64_t N, float eps, int x_dtype, int gamma_dtype,
+                          hipStream_t stream) {
+  return forward(true, x, residual, gamma, y, rstd, M, N, eps, x_dtype, gamma_dtype, stream);
+}
+
+size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int x_dtype) {
+  return rmsn::plan_bwd(M, N, x_dtype).workspace_bytes;
+}
+
+int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* gamma, void* dx,
+                float* dgamma, void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
+                int x_dtype, int gamma_dtype, hipStream_t stream) {
+  if (!valid_pair(x_dtype, gamma_dtype)) return RMSN_ERR_DTYPE;
+  if (!shape_ok(M, N)) return RMSN_ERR_SHAPE;
+  if (M == 0) return RMSN_OK;
+  const rmsn::BwdPlan plan = rmsn::plan_bwd(M, N, x_dtype);
+  if (!plan.supported) return RMSN_ERR_SHAPE;
+  if (!dy || !x || !rstd || !gamma || !dx || !dgamma) return RMSN_ERR_NULL;
+  if (!workspace || workspace_bytes < plan.workspace_bytes) return RMSN_ERR_WORKSPACE;
+  const int es = esize_of(x_dtype), gs = esize_of(gamma_dtype);
+  if (!aligned(dy, es) || !aligned(x, es) || !aligned(dx, es) || !aligned(gamma, gs) ||
+      !aligned(rstd, 4) || !aligned(dgamma, 4) || !aligned(workspace, 16))
+    return RMSN_ERR_ALIGN;
+  const uint64_t big = static_cast<uint64_t>(M) * static_cast<uint64_t>(N) * es;
+  const Range rdy = span(dy, big), rx = span(x, big), rdx = span(dx, big);
+  const Range rr = span(rstd, static_cast<uint64_t>(M) * 4);
+  const Range rg = span(gamma, static_cast<uint64_t>(N) * gs);
+  const Range rdg = span(dgamma, static_cast<uint64_t>(N) * 4);
+  const Range rw = span(workspace, plan.workspace_bytes);
+  if (partial_overlap(rdx, rdy) || partial_overlap(rdx, rx) || overlap(rdx, rr) ||
+      overlap(rdx, rg) || overlap(rdx, rdg) || overlap(rdx, rw))
+    return RMSN_ERR_OVERLAP;
+  const Range reads[] = {rdy, rx, rr, rg};
+  for (const Range& r : reads)
+    if (overlap(rdg, r) || overlap(rw, r)) return RMSN_ERR_OVERLAP;
+  if (overlap(rdg, rw)) return RMSN_ERR_OVERLAP;
+  rmsn::BwdCall c{dy, x, rstd, gamma, dx, dgamma, workspace, M, N, x_dtype, gamma_dtype, plan,
+                  stream};
+  return finish(rmsn::launch_bwd(c));
+}
+
+const char* rmsnorm_status_string(int status) {
+  switch (status) {
+    case RMSN_OK: return "ok";
+    case RMSN_ERR_NULL: return "a required pointer is null";
+    case RMSN_ERR_SHAPE: return "unsupported shape (M < 0, N < 1, or too large)";
+    case RMSN_ERR_DTYPE: return "unsupported dtype combination";
+    case RMSN_ERR_WORKSPACE: return "workspace missing or too small";
+    case RMSN_ERR_OVERLAP: return "buffers overlap in a forbidden way";
+    case RMSN_ERR_ALIGN: return "pointer not aligned to its element size";
+    case RMSN_ERR_EPS: return "eps must be finite and non-negative";
+    case RMSN_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int rmsnorm_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

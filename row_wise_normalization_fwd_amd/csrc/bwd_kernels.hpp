@@ -1,0 +1,189 @@
+// Backward RMSNorm kernels for gfx950.
+//
+// The FlyDSL guide (section 1.2, "Backward") gives the interface -- inputs x,
+// gamma, dy and the saved rstd (no eps), outputs dx and an fp32 weight
+// gradient -- but no formula and an atomic-add weight gradient. The formulas
+// are the derivative of the forward y_j = x_j rho gamma_j with
+// d rho / d x_k = -rho^3 x_k / N:
+//     c_i      = (1/N) sum_j dy_ij gamma_j x_ij
+//     dx_ij    = rho_i (gamma_j dy_ij - x_ij rho_i^2 c_i)
+//     dgamma_j = sum_i dy_ij x_ij rho_i
+// The weight gradient is reduced in two stages without atomics: stage 1 gives
+// each block a fixed, contiguous range of rows and writes one fp32 partial row
+// per block; stage 2 sums the partials of each column in a fixed order. The
+// partition depends only on (M, N, dtype), so results are bit-reproducible.
+#pragma once
+
+#include <type_traits>
+
+#include "device.hpp"
+
+namespace rmsn {
+
+template <class T, class G>
+struct BwdArgs {
+  const typename T::S* dy;
+  const typename T::S* x;
+  const float* rstd;
+  const typename G::S* gamma;
+  typename T::S* dx;
+  float* partial;          // [num_blocks, N] fp32
+  int64_t M;
+  int N;
+  int64_t rows_per_block;  // contiguous rows owned by each block
+};
+
+// dy * gamma * x, accumulated in double. For bf16 operands the fp32 product is
+// exact (8 + 8 + 8 significant bits), so one conversion suffices; otherwise
+// the product is formed in double.
+template <class T, class G>
+__device__ __forceinline__ double dot_term(float dyv, float g, float xv) {
+  if constexpr (std::is_same_v<T, BF16> && std::is_same_v<G, BF16>) {
+    return static_cast<double>(dyv * g * xv);
+  } else {
+    return static_cast<double>(dyv) * static_cast<double>(g) * static_cast<double>(xv);
+  }
+}
+
+// Stage 1. A block of BLOCK threads holds RG = BLOCK / TPR row groups; group
+// `grp` takes rows base + grp for base = r0, r0 + RG, ... inside the block's
+// range [r0, r1). Each lane keeps gamma and its columns' dgamma partial sums in
+// registers. With RG > 1 the groups' partials are combined through LDS in
+// group order before the block writes its partial row.
+template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
+  using U = Unit<T, VEC>;
+  constexpr int E = U::E;
+  constexpr int RG = BLOCK / TPR;
+  constexpr int COLS = TPR * UPT * E;  // columns covered by one row group
+  static_assert(BLOCK % TPR == 0 && BLOCK % kWave == 0, "block shape");
+  __shared__ double red[2 * (BLOCK / kWave)];
+  extern __shared__ __align__(16) unsigned char lds_bytes[];
+  float* comb = reinterpret_cast<float*>(lds_bytes);  // [RG][COLS] when RG > 1
+
+  const int nunits = a.N / E;
+  const int grp = threadIdx.x / TPR;
+  const int lane = threadIdx.x % TPR;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * a.rows_per_block;
+  const int64_t r1 = r0 + a.rows_per_block < a.M ? r0 + a.rows_per_block : a.M;
+
+  float gam[UPT][E];
+  float acc[UPT][E];
+#pragma unroll
+  for (int k = 0; k < UPT; ++k) {
+    const int u = lane + k * TPR;
+    if (u < nunits) {
+      load_gamma<G, E, VEC>(a.gamma, u * E, gam[k]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) gam[k][e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[k][e] = 0.0f;
+  }
+
+  int parity = 0;
+  for (int64_t base = r0; base < r1; base += RG) {  // uniform over the block
+    const int64_t row = base + grp;
+    const bool valid = row < r1;
+    const int64_t off = row * a.N;
+
+    typename U::Raw rx[UPT], rdy[UPT];
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const int u = lane + k * TPR;
+      const bool ok = valid && u < nunits;
+      rx[k] = ok ? U::load(a.x + off + u * E) : U::zero();
+      rdy[k] = ok ? U::load(a.dy + off + u * E) : U::zero();
+    }
+    const float rho = valid ? a.rstd[row] : 0.0f;
+
+    float xv[UPT][E], dyv[UPT][E];
+    double part[UPT];
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      U::widen(rx[k], xv[k]);
+      U::widen(rdy[k], dyv[k]);
+      double s = 0.0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) s = s + dot_term<T, G>(dyv[k][e], gam[k][e], xv[k][e]);
+      part[k] = s;
+    }
+    double dot = part[0];
+#pragma unroll
+    for (int k = 1; k < UPT; ++k) dot = dot + part[k];
+    dot = row_sum<TPR, BLOCK>(dot, red, parity);
+    parity ^= 1;
+
+    const double rd = static_cast<double>(rho);
+    const float kcoef = static_cast<float>(rd * rd * (dot / static_cast<double>(a.N)));
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const int u = lane + k * TPR;
+      float o[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        o[e] = rho * __builtin_fmaf(-xv[k][e], kcoef, gam[k][e] * dyv[k][e]);
+        acc[k][e] = __builtin_fmaf(dyv[k][e] * xv[k][e], rho, acc[k][e]);
+      }
+      if (valid && u < nunits) U::store_nt(a.dx + off + u * E, U::narrow(o));
+    }
+  }
+
+  float* out = a.partial + static_cast<int64_t>(blockIdx.x) * a.N;
+  if constexpr (RG == 1) {
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const int u = lane + k * TPR;
+      if (u < nunits) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) out[u * E + e] = acc[k][e];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) comb[grp * COLS + (k * TPR + lane) * E + e] = acc[k][e];
+    }
+    __syncthreads();
+    // Lane `lane`, unit k holds column (k * TPR + lane) * E + e, so entry c of
+    // a group's slice is column c; sum the groups in increasing order.
+    for (int c = threadIdx.x; c < nunits * E; c += BLOCK) {
+      float s = comb[c];
+      for (int g = 1; g < RG; ++g) s = s + comb[g * COLS + c];
+      out[c] = s;
+    }
+  }
+}
+
+// Stage 2: dgamma_j = sum over blocks of partial[b][j]. A 256-thread block
+// covers 64 columns with 4 interleaved slices of partial rows; each slice sums
+// in increasing row order in double, and the 4 slice sums are added in slice
+// order. The result is rounded to fp32 once.
+constexpr int kStage2Cols = 64;
+constexpr int kStage2Slices = 4;
+
+__global__ __launch_bounds__(kStage2Cols * kStage2Slices) void bwd_stage2_kernel(
+    const float* __restrict__ partial, float* __restrict__ dgamma, int nblocks, int N) {
+  __shared__ double red[kStage2Slices][kStage2Cols];
+  const int c = threadIdx.x % kStage2Cols;
+  const int slice = threadIdx.x / kStage2Cols;
+  const int col = blockIdx.x * kStage2Cols + c;
+  double s = 0.0;
+  if (col < N) {
+#pragma unroll 8
+    for (int b = slice; b < nblocks; b += kStage2Slices)
+      s = s + static_cast<double>(partial[static_cast<int64_t>(b) * N + col]);
+  }
+  red[slice][c] = s;
+  __syncthreads();
+  if (slice == 0 && col < N) {
+    double t = red[0][c];
+#pragma unroll
+    for (int q = 1; q < kStage2Slices; ++q) t = t + red[q][c];
+    dgamma[col] = static_cast<float>(t);
+  }
+}
+
+}  // namespace rmsn

@@ -1,0 +1,218 @@
+// Device helpers shared by the RMSNorm kernels (gfx950 / CDNA4, wave64).
+//
+//  * storage traits for fp32 / fp16 / bf16 with widening to fp32 and
+//    round-to-nearest-even narrowing (hardware v_cvt_pk_bf16_f32 and
+//    v_cvt_pk_f16_f32 on gfx950; the FlyDSL guide, section 1.1, notes the
+//    hardware bf16 pack on gfx950),
+//  * 16-byte "units" (one global_load/store_dwordx4 per lane) and 1-element
+//    units for rows that are not 16-byte aligned,
+//  * fixed-order reductions inside a group of lanes using DPP lane moves and
+//    readlane, then across the waves of a row through LDS (the XOR-butterfly-
+//    then-LDS scheme of the FlyDSL guide, section 1.1, with DPP in place of
+//    shuffles). Every lane of a group ends with the same, bitwise identical,
+//    value, and the order of additions never depends on timing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmsn {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------- storage traits
+
+struct F32 {
+  using S = float;
+  static constexpr int kSize = 4;
+  __device__ static float widen(S v) { return v; }
+  __device__ static S narrow(float v) { return v; }
+  // A 32-bit word holds one element.
+  static constexpr int kPerWord = 1;
+  __device__ static void widen_word(uint32_t w, float* f) { f[0] = __uint_as_float(w); }
+  __device__ static uint32_t narrow_word(const float* f) { return __float_as_uint(f[0]); }
+};
+
+struct BF16 {
+  using S = uint16_t;
+  static constexpr int kSize = 2;
+  __device__ static float widen(S v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+  __device__ static S narrow(float v) {
+    bf16x2 p = __builtin_convertvector((f32x2){v, 0.0f}, bf16x2);
+    return static_cast<S>(__builtin_bit_cast(uint32_t, p) & 0xffffu);
+  }
+  static constexpr int kPerWord = 2;
+  __device__ static void widen_word(uint32_t w, float* f) {
+    f[0] = __uint_as_float(w << 16);
+    f[1] = __uint_as_float(w & 0xffff0000u);
+  }
+  __device__ static uint32_t narrow_word(const float* f) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){f[0], f[1]}, bf16x2));
+  }
+};
+
+struct F16 {
+  using S = uint16_t;
+  static constexpr int kSize = 2;
+  __device__ static float widen(S v) { return static_cast<float>(__builtin_bit_cast(_Float16, v)); }
+  __device__ static S narrow(float v) { return __builtin_bit_cast(S, static_cast<_Float16>(v)); }
+  static constexpr int kPerWord = 2;
+  __device__ static void widen_word(uint32_t w, float* f) {
+    f32x2 v = __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+    f[0] = v.x;
+    f[1] = v.y;
+  }
+  __device__ static uint32_t narrow_word(const float* f) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){f[0], f[1]}, f16x2));
+  }
+};
+
+// ------------------------------------------------------------------- units
+//
+// A unit is what one lane moves with one memory instruction: 16 bytes when the
+// row is 16-byte aligned (VEC), else one element.
+
+template <class T, bool VEC>
+struct Unit;
+
+template <class T>
+struct Unit<T, true> {
+  static constexpr int E = 16 / T::kSize;  // elements per unit
+  using Raw = u32x4;
+  __device__ static Raw load(const typename T::S* p) { return *reinterpret_cast<const Raw*>(p); }
+  __device__ static void store(typename T::S* p, Raw v) { *reinterpret_cast<Raw*>(p) = v; }
+  __device__ static void store_nt(typename T::S* p, Raw v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<Raw*>(p));
+  }
+  __device__ static Raw zero() { return (Raw){0u, 0u, 0u, 0u}; }
+  __device__ static void widen(Raw v, float* f) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) T::widen_word(v[w], f + w * T::kPerWord);
+  }
+  __device__ static Raw narrow(const float* f) {
+    Raw v;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v[w] = T::narrow_word(f + w * T::kPerWord);
+    return v;
+  }
+};
+
+template <class T>
+struct Unit<T, false> {
+  static constexpr int E = 1;
+  using Raw = typename T::S;
+  __device__ static Raw load(const typename T::S* p) { return *p; }
+  __device__ static void store(typename T::S* p, Raw v) { *p = v; }
+  __device__ static void store_nt(typename T::S* p, Raw v) { __builtin_nontemporal_store(v, p); }
+  __device__ static Raw zero() { return Raw(0); }
+  __device__ static void widen(Raw v, float* f) { f[0] = T::widen(v); }
+  __device__ static Raw narrow(const float* f) { return T::narrow(f[0]); }
+};
+
+// Load E consecutive gamma values starting at element offset `off` as fp32.
+// In the vector case the caller guarantees 16-byte alignment of gamma + off.
+template <class G, int E, bool VEC>
+__device__ __forceinline__ void load_gamma(const typename G::S* g, int off, float* out) {
+  if constexpr (VEC) {
+    constexpr int kBytes = E * G::kSize;  // 16 or 32
+    const typename G::S* p = g + off;
+#pragma unroll
+    for (int c = 0; c < kBytes / 16; ++c) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(p + c * (16 / G::kSize));
+#pragma unroll
+      for (int w = 0; w < 4; ++w) G::widen_word(v[w], out + c * (16 / G::kSize) + w * G::kPerWord);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) out[e] = G::widen(g[off + e]);
+  }
+}
+
+// --------------------------------------------------------------- reductions
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+  int2 h = __builtin_bit_cast(int2, v);
+  h.x = __builtin_amdgcn_update_dpp(0, h.x, CTRL, 0xF, 0xF, false);
+  h.y = __builtin_amdgcn_update_dpp(0, h.y, CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, h);
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+__device__ __forceinline__ double readlane(double v, int lane) {
+  int2 h = __builtin_bit_cast(int2, v);
+  h.x = __builtin_amdgcn_readlane(h.x, lane);
+  h.y = __builtin_amdgcn_readlane(h.y, lane);
+  return __builtin_bit_cast(double, h);
+}
+
+// DPP controls (gfx9 encoding).
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7-i within 8
+constexpr int kRowMirror = 0x140;     // lane i <- lane 15-i within 16
+
+// Sum over aligned groups of G lanes (G a power of two, 1..64). Must be
+// reached by all 64 lanes of the wave (no divergence). Every lane of a group
+// receives the group's sum; equal in all lanes because each step adds two
+// values that are the same in both partner lanes (IEEE addition commutes).
+template <int G, class V>
+__device__ __forceinline__ V group_sum(V v) {
+  static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "group size");
+  if constexpr (G >= 2) v = v + dpp<kQuadXor1>(v);
+  if constexpr (G >= 4) v = v + dpp<kQuadXor2>(v);
+  if constexpr (G >= 8) v = v + dpp<kRowHalfMirror>(v);
+  if constexpr (G >= 16) v = v + dpp<kRowMirror>(v);
+  if constexpr (G == 32) {
+    const int lane = __lane_id();
+    V a = readlane(v, 0) + readlane(v, 16);
+    V b = readlane(v, 32) + readlane(v, 48);
+    v = lane < 32 ? a : b;
+  }
+  if constexpr (G == 64) {
+    v = (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
+  }
+  return v;
+}
+
+// Sum over groups of TPR consecutive threads of a block (TPR a power of two).
+// For TPR > 64 the per-wave sums go through LDS: `scratch` holds 2 * BLOCK/64
+// values, double-buffered through `parity`; callers that loop over rows flip
+// parity each time, so a buffer is rewritten only after a later barrier that
+// every reader of its previous contents has passed. Must be reached by every
+// thread of the block (TPR > 64) or of the wave (TPR <= 64).
+template <int TPR, int BLOCK, class V>
+__device__ __forceinline__ V row_sum(V v, V* scratch, int parity) {
+  if constexpr (TPR <= kWave) {
+    return group_sum<TPR>(v);
+  } else {
+    constexpr int kWaves = BLOCK / kWave;
+    constexpr int kWavesPerRow = TPR / kWave;
+    v = group_sum<kWave>(v);
+    const int wave = threadIdx.x / kWave;
+    V* buf = scratch + parity * kWaves;
+    if (__lane_id() == 0) buf[wave] = v;
+    __syncthreads();
+    const int first = (wave / kWavesPerRow) * kWavesPerRow;
+    V s = buf[first];
+#pragma unroll
+    for (int w = 1; w < kWavesPerRow; ++w) s = s + buf[first + w];
+    return s;
+  }
+}
+
+}  // namespace rmsn

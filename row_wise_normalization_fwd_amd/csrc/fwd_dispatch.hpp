@@ -1,0 +1,90 @@
+// Forward kernel choice and launch for one activation type. Included by one
+// translation unit per activation type so the instantiations compile in
+// parallel.
+//
+// Register path (N <= 8192): a group of TPR lanes per row with UPT units per
+// lane, TPR = next power of two of ceil(units / 4), so every lane issues up to
+// four 16-byte loads per operand. Short rows pack BLOCK / TPR rows per block.
+// Rows that are not 16-byte aligned use 1-element units (up to 8 per lane).
+// Longer rows: one 256-thread block per row, parked in LDS when the row fits
+// in 64 KiB, else re-read.
+#pragma once
+
+#include "fwd_kernels.hpp"
+#include "launch.hpp"
+
+namespace rmsn {
+
+template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool FUSED>
+hipError_t run_fwd_reg(const FwdArgs<T, G>& a, hipStream_t s) {
+  constexpr int RPB = BLOCK / TPR;
+  int64_t blocks = ceil_div(a.M, RPB);
+  if (blocks > kMaxGrid) blocks = kMaxGrid;
+  fwd_reg_kernel<T, G, VEC, TPR, UPT, BLOCK, FUSED>
+      <<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <class T, class G, bool VEC, int BLOCK, int UNROLL, bool FUSED, bool CACHE>
+hipError_t run_fwd_long(const FwdArgs<T, G>& a, hipStream_t s) {
+  int64_t blocks = a.M < kMaxGrid ? a.M : kMaxGrid;
+  const size_t lds = CACHE ? static_cast<size_t>(a.N) * T::kSize : 0;
+  fwd_long_kernel<T, G, VEC, BLOCK, UNROLL, FUSED, CACHE>
+      <<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), lds, s>>>(a);
+  return hipGetLastError();
+}
+
+template <class T, class G, bool FUSED>
+hipError_t fwd_typed(const FwdCall& c) {
+  FwdArgs<T, G> a;
+  a.x = static_cast<const typename T::S*>(c.x);
+  a.residual = static_cast<typename T::S*>(c.residual);
+  a.gamma = static_cast<const typename G::S*>(c.gamma);
+  a.y = static_cast<typename T::S*>(c.y);
+  a.rstd = c.rstd;
+  a.M = c.M;
+  a.N = static_cast<int>(c.N);
+  a.eps = c.eps;
+  hipStream_t s = c.stream;
+
+  const bool vec = (c.N * T::kSize) % 16 == 0 && aligned16(c.x) && aligned16(c.y) &&
+                   aligned16(c.gamma) && (!FUSED || aligned16(c.residual));
+  if (c.N <= kRegMaxN) {
+    if (vec) {
+      constexpr int E = 16 / T::kSize;
+      const int64_t units = c.N / E;
+      const int64_t tpr = next_pow2(ceil_div(units, 4));
+      if (tpr <= 4) return run_fwd_reg<T, G, true, 4, 4, 256, FUSED>(a, s);
+      if (tpr == 8) return run_fwd_reg<T, G, true, 8, 4, 256, FUSED>(a, s);
+      if (tpr == 16) return run_fwd_reg<T, G, true, 16, 4, 256, FUSED>(a, s);
+      if (tpr == 32) return run_fwd_reg<T, G, true, 32, 4, 256, FUSED>(a, s);
+      if (tpr == 64) return run_fwd_reg<T, G, true, 64, 4, 256, FUSED>(a, s);
+      if (tpr == 128) return run_fwd_reg<T, G, true, 128, 4, 256, FUSED>(a, s);
+      if (tpr == 256) {
+        if (units <= 3 * 256) return run_fwd_reg<T, G, true, 256, 3, 256, FUSED>(a, s);
+        return run_fwd_reg<T, G, true, 256, 4, 256, FUSED>(a, s);
+      }
+      if (units <= 3 * 512) return run_fwd_reg<T, G, true, 512, 3, 512, FUSED>(a, s);
+      return run_fwd_reg<T, G, true, 512, 4, 512, FUSED>(a, s);
+    }
+    const int64_t tpr = next_pow2(ceil_div(c.N, 8));
+    if (tpr <= 16) return run_fwd_reg<T, G, false, 16, 8, 256, FUSED>(a, s);
+    if (tpr <= 64) return run_fwd_reg<T, G, false, 64, 8, 256, FUSED>(a, s);
+    if (tpr <= 256) return run_fwd_reg<T, G, false, 256, 8, 256, FUSED>(a, s);
+    return run_fwd_reg<T, G, false, 1024, 8, 1024, FUSED>(a, s);
+  }
+  const bool cache = c.N * T::kSize <= kLdsRowBytes;
+  if (vec) {
+    if (cache) return run_fwd_long<T, G, true, 256, 4, FUSED, true>(a, s);
+    return run_fwd_long<T, G, true, 256, 4, FUSED, false>(a, s);
+  }
+  if (cache) return run_fwd_long<T, G, false, 256, 8, FUSED, true>(a, s);
+  return run_fwd_long<T, G, false, 256, 8, FUSED, false>(a, s);
+}
+
+template <class T, class G>
+hipError_t fwd_gamma_typed(const FwdCall& c) {
+  return c.residual ? fwd_typed<T, G, true>(c) : fwd_typed<T, G, false>(c);
+}
+
+}  // namespace rmsn

@@ -1,0 +1,203 @@
+// Forward RMSNorm kernels for gfx950 ("Pre-built kernel library guide"
+// (FlyDSL), section 1.2: y = x / sqrt(mean(x^2) + eps) * gamma, optional fp32
+// rstd output), with the optional fused residual add (h = x + r rounded once
+// to the activation type, written back over r, and the rounded h normalised).
+//
+// Two kernel families:
+//  * fwd_reg_kernel  -- the row stays in VGPRs between the sum of squares and
+//    the normalisation: one HBM read and one HBM write per element. A group
+//    of TPR lanes owns a row (several rows per block for short rows, the
+//    guide's multi-row packing of section 2.1); each lane holds UPT units.
+//  * fwd_long_kernel -- one block per row, looping over the row. With CACHE
+//    the loaded units are parked in LDS (each lane reads back only what it
+//    wrote, so no barrier is needed for the cache itself); without CACHE the
+//    second pass re-reads the row from global memory (L2 / MALL).
+// Every lane computes in fp32; sums of squares use per-unit partial sums
+// added in a fixed order, then the fixed-order group reduction, so results do
+// not depend on timing. Output stores are non-temporal (the guide's
+// USE_NONTEMPORAL for outputs).
+#pragma once
+
+#include "device.hpp"
+
+namespace rmsn {
+
+template <class T, class G>
+struct FwdArgs {
+  const typename T::S* x;
+  typename T::S* residual;  // fused: in r, out h
+  const typename G::S* gamma;
+  typename T::S* y;
+  float* rstd;  // may be null
+  int64_t M;
+  int N;
+  float eps;
+};
+
+// Widen unit `raw`, optionally add the residual unit and round (fused add),
+// and return the fp32 values that get normalised.
+template <class T, class U, bool FUSED>
+__device__ __forceinline__ void prepare_unit(typename U::Raw& raw, typename U::Raw rres,
+                                             float* v) {
+  U::widen(raw, v);
+  if constexpr (FUSED) {
+    float r[U::E];
+    U::widen(rres, r);
+#pragma unroll
+    for (int e = 0; e < U::E; ++e) v[e] = v[e] + r[e];
+    raw = U::narrow(v);   // h, rounded once to the activation type
+    U::widen(raw, v);     // normalise the rounded h
+  }
+}
+
+template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool FUSED>
+__global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
+  using U = Unit<T, VEC>;
+  constexpr int E = U::E;
+  constexpr int RPB = BLOCK / TPR;  // rows per block
+  static_assert(BLOCK % TPR == 0 && BLOCK % kWave == 0, "block shape");
+  __shared__ float red[2 * (BLOCK / kWave)];
+
+  const int nunits = a.N / E;
+  const int grp = threadIdx.x / TPR;
+  const int lane = threadIdx.x % TPR;
+
+  float gam[UPT][E];
+#pragma unroll
+  for (int k = 0; k < UPT; ++k) {
+    const int u = lane + k * TPR;
+    if (u < nunits) {
+      load_gamma<G, E, VEC>(a.gamma, u * E, gam[k]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) gam[k][e] = 0.0f;
+    }
+  }
+
+  int parity = 0;
+  // `base` is uniform over the block, so every thread runs the same number of
+  // iterations and reaches every reduction.
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * RPB; base < a.M;
+       base += static_cast<int64_t>(gridDim.x) * RPB) {
+    const int64_t row = base + grp;
+    const bool valid = row < a.M;
+    const int64_t off = row * a.N;
+
+    typename U::Raw raw[UPT];
+    typename U::Raw res[UPT];
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const int u = lane + k * TPR;
+      const bool ok = valid && u < nunits;
+      raw[k] = ok ? U::load(a.x + off + u * E) : U::zero();
+      if constexpr (FUSED) res[k] = ok ? U::load(a.residual + off + u * E) : U::zero();
+    }
+
+    float v[UPT][E];
+    float part[UPT];
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      prepare_unit<T, U, FUSED>(raw[k], res[k], v[k]);
+      if constexpr (FUSED) {
+        const int u = lane + k * TPR;
+        if (valid && u < nunits) U::store_nt(a.residual + off + u * E, raw[k]);
+      }
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) s = __builtin_fmaf(v[k][e], v[k][e], s);
+      part[k] = s;
+    }
+    float ss = part[0];
+#pragma unroll
+    for (int k = 1; k < UPT; ++k) ss = ss + part[k];
+
+    ss = row_sum<TPR, BLOCK>(ss, red, parity);
+    parity ^= 1;
+    const float rs = 1.0f / __builtin_sqrtf(ss / static_cast<float>(a.N) + a.eps);
+    if (a.rstd != nullptr && valid && lane == 0) a.rstd[row] = rs;
+
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const int u = lane + k * TPR;
+      if (valid && u < nunits) {
+        float o[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = v[k][e] * rs * gam[k][e];
+        U::store_nt(a.y + off + u * E, U::narrow(o));
+      }
+    }
+  }
+}
+
+template <class T, class G, bool VEC, int BLOCK, int UNROLL, bool FUSED, bool CACHE>
+__global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
+  using U = Unit<T, VEC>;
+  using Raw = typename U::Raw;
+  constexpr int E = U::E;
+  constexpr int STEP = BLOCK * UNROLL;
+  __shared__ float red[2 * (BLOCK / kWave)];
+  extern __shared__ __align__(16) unsigned char lds_bytes[];
+  Raw* cache = reinterpret_cast<Raw*>(lds_bytes);
+
+  const int nunits = a.N / E;
+  int parity = 0;
+  for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x) {
+    const int64_t off = row * a.N;
+    float ss = 0.0f;
+    for (int first = 0; first < nunits; first += STEP) {
+      Raw raw[UNROLL];
+      Raw res[UNROLL];
+#pragma unroll
+      for (int k = 0; k < UNROLL; ++k) {
+        const int u = first + threadIdx.x + k * BLOCK;
+        raw[k] = u < nunits ? U::load(a.x + off + u * E) : U::zero();
+        if constexpr (FUSED) res[k] = u < nunits ? U::load(a.residual + off + u * E) : U::zero();
+      }
+#pragma unroll
+      for (int k = 0; k < UNROLL; ++k) {
+        const int u = first + threadIdx.x + k * BLOCK;
+        float v[E];
+        prepare_unit<T, U, FUSED>(raw[k], res[k], v);
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) s = __builtin_fmaf(v[e], v[e], s);
+        ss = ss + s;
+        if (u < nunits) {
+          if constexpr (FUSED) U::store_nt(a.residual + off + u * E, raw[k]);
+          if constexpr (CACHE) cache[u] = raw[k];
+        }
+      }
+    }
+    ss = row_sum<BLOCK, BLOCK>(ss, red, parity);
+    parity ^= 1;
+    const float rs = 1.0f / __builtin_sqrtf(ss / static_cast<float>(a.N) + a.eps);
+    if (a.rstd != nullptr && threadIdx.x == 0) a.rstd[row] = rs;
+
+    // Second pass: the rounded h (fused) was written back to `residual`; each
+    // lane re-reads only units it wrote itself.
+    const typename T::S* src = FUSED ? a.residual : a.x;
+    for (int first = 0; first < nunits; first += STEP) {
+      Raw raw[UNROLL];
+#pragma unroll
+      for (int k = 0; k < UNROLL; ++k) {
+        const int u = first + threadIdx.x + k * BLOCK;
+        if constexpr (CACHE) raw[k] = u < nunits ? cache[u] : U::zero();
+        else raw[k] = u < nunits ? U::load(src + off + u * E) : U::zero();
+      }
+#pragma unroll
+      for (int k = 0; k < UNROLL; ++k) {
+        const int u = first + threadIdx.x + k * BLOCK;
+        if (u < nunits) {
+          float v[E], g[E], o[E];
+          U::widen(raw[k], v);
+          load_gamma<G, E, VEC>(a.gamma, u * E, g);
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
+          U::store_nt(a.y + off + u * E, U::narrow(o));
+        }
+      }
+    }
+  }
+}
+
+}  // namespace rmsn

@@ -1,0 +1,115 @@
+"""Helpers for the GPU parity tests: host <-> device transfer of storage arrays
+and the comparators that define the tolerances.
+
+Tolerances (fixed here, used by every GPU test):
+  * 16-bit outputs (y, h, dx): ordinal-ulp distance <= 1 from the oracle value
+    rounded to the same type (both neighbours of an exact value are correct
+    results); h must match bit for bit.
+  * fp32 outputs (y, rstd): relative error <= 1e-5 against the oracle's double
+    value (0/0 counts as 0).
+  * dx: within 1 ulp, or, where gamma*dy and x*rho^2*c cancel, absolute error
+    <= 2^-18 * rho * (|gamma dy| + |x| rho^2 A) with A = mean_j |dy gamma x|
+    (an fp32 evaluation cannot resolve a cancelled result below that scale).
+  * dgamma: |g - o| <= max(1e-3 |o|, 2^-24 S_j) with S_j = sum_i |dy x rho|.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+
+TORCH_DTYPES = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}
+
+
+def to_device(a: np.ndarray, dt: int, device="cuda") -> torch.Tensor:
+    if dt == O.F32:
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+    return t.view(TORCH_DTYPES[dt]).to(device)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.float32:
+        return t.numpy().copy()
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def ordinal16(bits: np.ndarray) -> np.ndarray:
+    b = bits.astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def ulp_distance16(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    return np.abs(ordinal16(a) - ordinal16(b))
+
+
+def rel_error(got: np.ndarray, exact: np.ndarray) -> np.ndarray:
+    got = got.astype(np.float64)
+    diff = np.abs(got - exact)
+    den = np.abs(exact)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(den > 0, diff / den, np.where(diff == 0, 0.0, np.inf))
+    return r
+
+
+def check_output(got: np.ndarray, exact: np.ndarray, rounded: np.ndarray, dt: int, what: str):
+    """Forward-style check of an output against the oracle."""
+    assert got.shape == rounded.shape, (what, got.shape, rounded.shape)
+    if dt == O.F32:
+        r = rel_error(got, exact)
+        worst = float(r.max()) if r.size else 0.0
+        assert worst <= 1e-5, f"{what}: max relative error {worst:.3e} > 1e-5"
+        return worst
+    d = ulp_distance16(got, rounded)
+    worst = int(d.max()) if d.size else 0
+    if worst > 1:
+        idx = np.unravel_index(int(d.argmax()), d.shape)
+        raise AssertionError(f"{what}: {int((d > 1).sum())} elements beyond 1 ulp; worst {worst} "
+                             f"at {idx}: got {got[idx]:#06x}, oracle {rounded[idx]:#06x}")
+    return worst
+
+
+def check_rstd(got: np.ndarray, exact: np.ndarray):
+    r = rel_error(got, exact)
+    worst = float(r.max()) if r.size else 0.0
+    assert worst <= 1e-5, f"rstd: max relative error {worst:.3e}"
+    return worst
+
+
+def check_dx(got: np.ndarray, ref: dict, x: np.ndarray, dy: np.ndarray, gamma: np.ndarray,
+             rho: np.ndarray, dt: int):
+    """Returns the number of elements that passed only through the floor."""
+    M, N = got.shape
+    xd = O.decode(x, dt).reshape(M, N)
+    dyd = O.decode(dy, dt).reshape(M, N)
+    gd = O.decode(gamma, O.F32 if gamma.dtype == np.float32 else dt)
+    exact = ref["dx_exact"]
+    if dt == O.F32:
+        ok_ulp = rel_error(got, exact) <= 1e-5
+        gotv = got.astype(np.float64)
+    else:
+        ok_ulp = ulp_distance16(got, ref["dx"]) <= 1
+        gotv = O.decode(got, dt).reshape(M, N)
+    rho2 = rho[:, None].astype(np.float64)
+    floor = 2.0 ** -18 * rho2 * (np.abs(gd[None, :] * dyd) + np.abs(xd) * rho2 ** 2 * ref["a"][:, None])
+    ok_floor = np.abs(gotv - exact) <= floor
+    bad = ~(ok_ulp | ok_floor)
+    if bad.any():
+        idx = np.unravel_index(int(np.argmax(bad)), bad.shape)
+        raise AssertionError(f"dx: {int(bad.sum())} elements out of tolerance; first at {idx}: "
+                             f"got {gotv[idx]!r}, exact {exact[idx]!r}, floor {floor[idx]!r}")
+    return int((~ok_ulp & ok_floor).sum())
+
+
+def check_dgamma(got: np.ndarray, ref: dict):
+    o = ref["dgamma"]
+    tol = np.maximum(1e-3 * np.abs(o), 2.0 ** -24 * ref["s"])
+    err = np.abs(got.astype(np.float64) - o)
+    bad = err > tol
+    assert not bad.any(), (f"dgamma: {int(bad.sum())} columns out of tolerance; worst ratio "
+                           f"{float((err / tol).max()):.3f}")
+    return float(np.linalg.norm(got - o) / max(np.linalg.norm(o), 1e-300))

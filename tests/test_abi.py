@@ -1,0 +1,139 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/rmsnorm_mi355x.h declares, and rejects bad arguments on the host before
+any HIP call (the addresses used here are never dereferenced)."""
+
+import os
+import re
+
+import pytest
+
+import row_wise_normalization_fwd_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER_DIR = os.path.join(ROOT, "include")
+
+OK, NULL, SHAPE, DTYPE, WORKSPACE, OVERLAP, ALIGN, EPS = 0, -1, -2, -3, -4, -5, -6, -7
+F32, F16, BF16 = 0, 1, 2
+
+# Fake, well-separated, 256-byte-aligned "device" addresses.
+A, B, C, D, E, F, G = (0x10000000 * k for k in range(1, 8))
+
+
+def _declared_functions():
+    names = []
+    for fn in sorted(os.listdir(HEADER_DIR)):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(HEADER_DIR, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(rmsnorm_\w+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return R.load_library()
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == sorted(R.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert callable(getattr(R, name)), name
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        R.load_library(str(tmp_path / "nope.so"))
+
+
+def test_status_strings(lib):
+    for code in (OK, NULL, SHAPE, DTYPE, WORKSPACE, OVERLAP, ALIGN, EPS, -100):
+        s = R.rmsnorm_status_string(code)
+        assert s and s != "unknown status"
+    assert R.rmsnorm_status_string(12345) == "unknown status"
+    assert R.rmsnorm_last_hip_error() == 0
+
+
+def fwd(x=A, g=B, y=C, rstd=None, M=4, N=64, eps=1e-5, xd=BF16, gd=BF16):
+    return R.rmsnorm_fwd(x, g, y, rstd, M, N, eps, xd, gd, None)
+
+
+def fused(x=A, r=D, g=B, y=C, rstd=None, M=4, N=64, eps=1e-5, xd=BF16, gd=BF16):
+    return R.rmsnorm_fused_add_fwd(x, r, g, y, rstd, M, N, eps, xd, gd, None)
+
+
+def test_forward_validation(lib):
+    assert fwd(xd=3) == DTYPE
+    assert fwd(xd=BF16, gd=F16) == DTYPE          # gamma must be x dtype or fp32
+    assert fwd(xd=F32, gd=BF16) == DTYPE
+    assert fwd(M=-1) == SHAPE
+    assert fwd(N=0) == SHAPE
+    assert fwd(N=2 ** 31) == SHAPE
+    assert fwd(eps=-1e-6) == EPS
+    assert fwd(eps=float("nan")) == EPS
+    assert fwd(eps=float("inf")) == EPS
+    assert fwd(M=0, x=None, g=None, y=None) == OK   # empty: no-op
+    assert fwd(x=None) == NULL
+    assert fwd(g=None) == NULL
+    assert fwd(y=None) == NULL
+    assert fwd(x=A + 1) == ALIGN
+    assert fwd(y=C + 1, xd=F32, gd=F32) == ALIGN
+    assert fwd(g=B + 2, xd=F16, gd=F32) == ALIGN
+    assert fwd(rstd=E + 2) == ALIGN
+    # y may equal x exactly, but not overlap it partially, gamma or rstd.
+    assert fwd(y=A + 128) == OVERLAP
+    assert fwd(y=B) == OVERLAP
+    assert fwd(rstd=A + 16) == OVERLAP
+    assert fwd(rstd=C) == OVERLAP
+    assert fwd(rstd=B) == OVERLAP
+
+
+def test_fused_validation(lib):
+    assert fused(r=None) == NULL
+    assert fused(M=0, r=None) == OK
+    assert fused(r=D + 2, xd=F32, gd=F32) == ALIGN
+    assert fused(r=A + 128) == OVERLAP        # partial overlap of x and residual
+    assert fused(r=C) == OVERLAP              # y must not overlap the residual (h)
+    assert fused(r=B) == OVERLAP              # residual written over gamma
+    assert fused(rstd=D) == OVERLAP
+
+
+def bwd(dy=A, x=B, rstd=C, g=D, dx=E, dg=F, ws=G, wsb=None, M=64, N=256, xd=BF16, gd=BF16):
+    if wsb is None:
+        wsb = R.rmsnorm_bwd_workspace_size(M, N, xd)
+    return R.rmsnorm_bwd(dy, x, rstd, g, dx, dg, ws, wsb, M, N, xd, gd, None)
+
+
+def test_workspace_size():
+    # One fp32 partial row per stage-1 block; at most 256 blocks.
+    assert R.rmsnorm_bwd_workspace_size(8192, 8192, BF16) == 256 * 8192 * 4
+    assert R.rmsnorm_bwd_workspace_size(3, 10, F32) == 256          # 3*10*4 = 120 -> 256
+    assert R.rmsnorm_bwd_workspace_size(1000, 64, F16) == 250 * 64 * 4
+    assert R.rmsnorm_bwd_workspace_size(0, 64, F16) == 0
+    assert R.rmsnorm_bwd_workspace_size(10, 0, F16) == 0
+    assert R.rmsnorm_bwd_workspace_size(10, 10, 7) == 0
+
+
+def test_backward_validation(lib):
+    assert bwd(xd=5) == DTYPE
+    assert bwd(xd=F32, gd=F16) == DTYPE
+    assert bwd(M=-3) == SHAPE
+    assert bwd(N=0) == SHAPE
+    assert bwd(N=40000) == SHAPE              # beyond the on-chip backward row limit
+    assert bwd(M=0, dy=None, x=None, rstd=None, g=None, dx=None, dg=None, ws=None) == OK
+    for k in ("dy", "x", "rstd", "g", "dx", "dg"):
+        assert bwd(**{k: None}) == NULL, k
+    assert bwd(ws=None) == WORKSPACE
+    assert bwd(wsb=R.rmsnorm_bwd_workspace_size(64, 256, BF16) - 4) == WORKSPACE
+    assert bwd(dy=A + 1) == ALIGN
+    assert bwd(ws=G + 8) == ALIGN
+    assert bwd(dg=F + 2) == ALIGN
+    assert bwd(dx=A + 64) == OVERLAP          # partial overlap with dy
+    assert bwd(dx=C) == OVERLAP               # dx over rstd
+    assert bwd(dg=A + 4) == OVERLAP
+    assert bwd(ws=B + 16) == OVERLAP
+    assert bwd(ws=F) == OVERLAP               # workspace over dgamma

@@ -1,0 +1,338 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the fp64
+oracle, element by element, on seeded inputs. Tolerances are defined in
+tests/gpu_util.py. Every case name carries its shape, dtypes and variant."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gen as G
+import oracle as O
+import row_wise_normalization_fwd_amd as R
+from gpu_util import (check_dgamma, check_dx, check_output, check_rstd, to_device, to_host,
+                      TORCH_DTYPES)
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [(O.F32, O.F32), (O.F16, O.F16), (O.F16, O.F32), (O.BF16, O.BF16), (O.BF16, O.F32)]
+PAIR_IDS = ["f32", "f16", "f16_gf32", "bf16", "bf16_gf32"]
+N_SWEEP = [1, 7, 8, 63, 64, 1000, 1024, 2047, 2048, 4096, 4999, 5000, 5001, 8191, 8192, 8193,
+           12288, 16384, 32768]
+N_REREAD = {O.F32: 20000, O.F16: 40000, O.BF16: 40000}   # rows beyond the 64 KiB LDS cache
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "exact_rows.txt")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    R.load_library()
+    torch.cuda.set_device(0)
+
+
+def _stream():
+    return torch.cuda.current_stream()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _empty(n, dt, misalign=0):
+    """Device buffer of n elements, optionally starting `misalign` elements past
+    a 256-byte boundary (breaks 16-byte row alignment)."""
+    buf = torch.empty(n + 16, dtype=TORCH_DTYPES[dt], device="cuda")
+    return buf[misalign:misalign + n]
+
+
+def _put(a, dt, misalign=0):
+    t = _empty(a.size, dt, misalign)
+    t.copy_(to_device(a.reshape(-1), dt))
+    return t
+
+
+def _inputs(M, N, xdt, gdt, seed, outlier_every=0, outlier_scale=1.0, with_r=False, with_dy=False):
+    x = G.normal(seed, G.STREAM_X, M, N, xdt, outlier_scale, outlier_every)
+    g = G.uniform(seed, G.STREAM_GAMMA, N, 0.5, 1.5, gdt)
+    r = G.normal(seed, G.STREAM_R, M, N, xdt) if with_r else None
+    dy = G.normal(seed, G.STREAM_DY, M, N, xdt) if with_dy else None
+    return x, g, r, dy
+
+
+# ------------------------------------------------------------------ forward
+
+def run_fwd(M, N, xdt, gdt, eps=1e-5, seed=7, want_rstd=True, misalign=0, inplace=False,
+            outlier_every=0, outlier_scale=1.0):
+    _log(f"fwd M={M} N={N} x={xdt} g={gdt} eps={eps} misalign={misalign} inplace={inplace}")
+    x, g, _, _ = _inputs(M, N, xdt, gdt, seed, outlier_every, outlier_scale)
+    ref = O.rmsnorm_fwd(x, g, M, N, eps, xdt, gdt)
+    xt = _put(x, xdt, misalign)
+    gt = _put(g, gdt)
+    yt = xt if inplace else _empty(M * N, xdt, misalign)
+    rt = torch.full((M,), -1.0, device="cuda") if want_rstd else None
+    st = R.rmsnorm_fwd(xt, gt, yt, rt, M, N, eps, xdt, gdt, _stream())
+    assert st == 0, R.rmsnorm_status_string(st)
+    torch.cuda.synchronize()
+    y = to_host(yt).reshape(M, N)
+    check_output(y, ref["y_exact"], ref["y"], xdt, "y")
+    if want_rstd:
+        check_rstd(to_host(rt), ref["rstd_exact"])
+    return x, g, ref, y
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("N", N_SWEEP)
+def test_fwd_sweep(N, pair):
+    run_fwd(3, N, *pair, seed=100 + N)
+    run_fwd(67, N, *pair, seed=200 + N, want_rstd=False)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_fwd_reread_path(pair):
+    run_fwd(5, N_REREAD[pair[0]], *pair, seed=31)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 64, 255, 4097])
+@pytest.mark.parametrize("N", [16, 64, 1000, 8192])
+def test_fwd_row_counts(M, N):
+    run_fwd(M, N, O.BF16, O.BF16, seed=M * 31 + N)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("N", [64, 1000, 4096, 8192, 12288])
+def test_fwd_misaligned_rows(N, pair):
+    # Base pointers one element past a 16-byte boundary take the scalar path.
+    run_fwd(9, N, *pair, seed=N + 5, misalign=1)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("N", [1000, 8192, 12288])
+def test_fwd_in_place(N, pair):
+    run_fwd(6, N, *pair, seed=N + 9, inplace=True)
+
+
+def test_fwd_empty_is_noop():
+    assert R.rmsnorm_fwd(None, None, None, None, 0, 128, 1e-5, O.BF16, O.BF16, _stream()) == 0
+
+
+def _golden_cases():
+    with open(GOLDEN) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                eps, x, g, y, rstd = [p.strip() for p in line.split("|")]
+                yield (float(eps), np.array(x.split(), float), np.array(g.split(), float),
+                       np.array(y.split(), float), float(rstd))
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_fwd_exact_rows(pair):
+    # Hand-derived rows whose outputs are exact in every type: the GPU must
+    # reproduce them exactly (the normalised values need no rounding).
+    xdt, gdt = pair
+    for eps, x, g, y, rstd in _golden_cases():
+        N = x.size
+        xt = _put(O.round_to(x, xdt), xdt)
+        gt = _put(O.round_to(g, gdt), gdt)
+        yt = _empty(N, xdt)
+        rt = torch.empty(1, device="cuda")
+        assert R.rmsnorm_fwd(xt, gt, yt, rt, 1, N, eps, xdt, gdt, _stream()) == 0
+        torch.cuda.synchronize()
+        got = O.decode(to_host(yt), xdt)
+        assert np.array_equal(got, y), (eps, x, got, y)
+        assert abs(float(to_host(rt)[0]) - rstd) <= 2e-7 * rstd
+
+
+@pytest.mark.parametrize("c", [1e-3, 0.5, 3.0, -7.0])
+def test_fwd_constant_row_closed_form(c):
+    N, eps = 4096, 1e-5
+    x = O.round_to(np.full(N, c), O.BF16)
+    cb = float(O.decode(x[:1], O.BF16)[0])
+    g = G.uniform(3, G.STREAM_GAMMA, N, 0.5, 1.5, O.BF16)
+    gd = O.decode(g, O.BF16)
+    want = O.round_to(cb / np.sqrt(cb * cb + float(np.float32(eps))) * gd, O.BF16)
+    yt = _empty(N, O.BF16)
+    assert R.rmsnorm_fwd(_put(x, O.BF16), _put(g, O.BF16), yt, None, 1, N, eps, O.BF16, O.BF16,
+                         _stream()) == 0
+    torch.cuda.synchronize()
+    from gpu_util import ulp_distance16
+    assert ulp_distance16(to_host(yt), want).max() <= 1
+
+
+def test_fwd_deterministic():
+    M, N = 512, 8192
+    x, g, _, _ = _inputs(M, N, O.BF16, O.BF16, 77)
+    xt, gt = _put(x, O.BF16), _put(g, O.BF16)
+    outs = []
+    for _ in range(3):
+        yt, rt = _empty(M * N, O.BF16), torch.empty(M, device="cuda")
+        assert R.rmsnorm_fwd(xt, gt, yt, rt, M, N, 1e-5, O.BF16, O.BF16, _stream()) == 0
+        torch.cuda.synchronize()
+        outs.append((to_host(yt), to_host(rt)))
+    for y, r in outs[1:]:
+        assert np.array_equal(y, outs[0][0]) and np.array_equal(r.view(np.uint32),
+                                                                outs[0][1].view(np.uint32))
+
+
+# --------------------------------------------------------------- fused add
+
+def run_fused(M, N, xdt, gdt, eps=1e-5, seed=11, want_rstd=False, misalign=0, x_is_r=False):
+    _log(f"fused M={M} N={N} x={xdt} g={gdt} misalign={misalign} x_is_r={x_is_r}")
+    x, g, r, _ = _inputs(M, N, xdt, gdt, seed, with_r=True)
+    if x_is_r:
+        r = x.copy()
+    ref = O.rmsnorm_fused_add_fwd(x, r, g, M, N, eps, xdt, gdt)
+    rt = _put(r, xdt, misalign)
+    xt = rt if x_is_r else _put(x, xdt, misalign)
+    gt = _put(g, gdt)
+    yt = _empty(M * N, xdt, misalign)
+    st_t = torch.empty(M, device="cuda") if want_rstd else None
+    st = R.rmsnorm_fused_add_fwd(xt, rt, gt, yt, st_t, M, N, eps, xdt, gdt, _stream())
+    assert st == 0, R.rmsnorm_status_string(st)
+    torch.cuda.synchronize()
+    h = to_host(rt).reshape(M, N)
+    if xdt == O.F32:
+        assert np.array_equal(h.view(np.uint32), ref["h"].view(np.uint32)), "h not bit-exact"
+    else:
+        assert np.array_equal(h, ref["h"]), f"h not bit-exact: {int((h != ref['h']).sum())} differ"
+    y = to_host(yt).reshape(M, N)
+    check_output(y, ref["y_exact"], ref["y"], xdt, "y")
+    if want_rstd:
+        check_rstd(to_host(st_t), ref["rstd_exact"])
+    # The fused result is the plain forward of the rounded h, bit for bit.
+    y2 = _empty(M * N, xdt, misalign)
+    assert R.rmsnorm_fwd(rt, gt, y2, None, M, N, eps, xdt, gdt, _stream()) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(y2).reshape(M, N).view(np.uint8), y.view(np.uint8))
+    return ref
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("N", [1, 7, 64, 1000, 2048, 4096, 5000, 8191, 8192, 8193, 16384])
+def test_fused_sweep(N, pair):
+    run_fused(5, N, *pair, seed=300 + N, want_rstd=(N % 2 == 0))
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_fused_reread_path(pair):
+    run_fused(3, N_REREAD[pair[0]], *pair, seed=41, want_rstd=True)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_fused_misaligned_and_aliased(pair):
+    run_fused(7, 4096, *pair, seed=51, misalign=1)
+    run_fused(7, 4096, *pair, seed=52, x_is_r=True)
+
+
+# ----------------------------------------------------------------- backward
+
+def run_bwd(M, N, xdt, gdt, seed=13, misalign=0, alias=None, gpu_rstd=False, eps=1e-5):
+    _log(f"bwd M={M} N={N} x={xdt} g={gdt} misalign={misalign} alias={alias} gpu_rstd={gpu_rstd}")
+    x, g, _, dy = _inputs(M, N, xdt, gdt, seed, with_dy=True)
+    xt, gt, dyt = _put(x, xdt, misalign), _put(g, gdt), _put(dy, xdt, misalign)
+    if gpu_rstd:
+        rt = torch.empty(M, device="cuda")
+        assert R.rmsnorm_fwd(xt, gt, _empty(M * N, xdt), rt, M, N, eps, xdt, gdt, _stream()) == 0
+        torch.cuda.synchronize()
+        rho = to_host(rt)
+    else:
+        rho = O.rmsnorm_fwd(x, g, M, N, eps, xdt, gdt, want_exact=False)["rstd"]
+        rt = torch.from_numpy(rho.copy()).cuda()
+    ref = O.rmsnorm_bwd(dy, x, rho, g, M, N, xdt, gdt)
+    dxt = {"dy": dyt, "x": xt}.get(alias) if alias else _empty(M * N, xdt, misalign)
+    dgt = torch.full((N,), float("nan"), device="cuda")
+    wsb = R.rmsnorm_bwd_workspace_size(M, N, xdt)
+    ws = torch.full((max(wsb, 16) // 4,), float("nan"), device="cuda")  # contents must not matter
+    st = R.rmsnorm_bwd(dyt, xt, rt, gt, dxt, dgt, ws, wsb, M, N, xdt, gdt, _stream())
+    assert st == 0, R.rmsnorm_status_string(st)
+    torch.cuda.synchronize()
+    floor_only = check_dx(to_host(dxt).reshape(M, N), ref, x, dy, g, rho, xdt)
+    check_dgamma(to_host(dgt), ref)
+    return floor_only
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("N", [1, 7, 8, 64, 1000, 2047, 4096, 5000, 8192, 8193, 16384, 32768])
+def test_bwd_sweep(N, pair):
+    if N > (16384 if pair[0] == O.F32 else 32768):
+        pytest.skip("beyond the on-chip backward row limit for this dtype")
+    run_bwd(3, N, *pair, seed=400 + N)
+    run_bwd(70, N, *pair, seed=500 + N)
+
+
+@pytest.mark.parametrize("M", [1, 255, 256, 257, 1000, 5000])
+def test_bwd_row_partitions(M):
+    run_bwd(M, 512, O.BF16, O.BF16, seed=M)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_bwd_misaligned_and_aliased(pair):
+    run_bwd(9, 4096, *pair, seed=61, misalign=1)
+    run_bwd(9, 4096, *pair, seed=62, alias="dy")
+    run_bwd(9, 4096, *pair, seed=63, alias="x")
+
+
+def test_bwd_with_gpu_forward_rstd():
+    run_bwd(300, 8192, O.BF16, O.BF16, seed=71, gpu_rstd=True)
+
+
+def test_bwd_radial_direction():
+    # gamma = 1 and dy = 2x: dx = 2 rho (1 - rho^2 ms) x, tiny; checked by the
+    # general tolerance (the floor covers the cancellation).
+    M, N = 16, 2048
+    x = G.normal(5, G.STREAM_X, M, N, O.BF16)
+    xd = O.decode(x, O.BF16)
+    dy = O.round_to(2.0 * xd, O.BF16)
+    g = O.round_to(np.ones(N), O.BF16)
+    rho = O.rmsnorm_fwd(x, g, M, N, 1e-5, O.BF16, O.BF16, want_exact=False)["rstd"]
+    ref = O.rmsnorm_bwd(dy, x, rho, g, M, N, O.BF16, O.BF16)
+    dxt, dgt = _empty(M * N, O.BF16), torch.empty(N, device="cuda")
+    wsb = R.rmsnorm_bwd_workspace_size(M, N, O.BF16)
+    ws = torch.empty(wsb // 4, device="cuda")
+    assert R.rmsnorm_bwd(_put(dy, O.BF16), _put(x, O.BF16), torch.from_numpy(rho).cuda(),
+                         _put(g, O.BF16), dxt, dgt, ws, wsb, M, N, O.BF16, O.BF16, _stream()) == 0
+    torch.cuda.synchronize()
+    check_dx(to_host(dxt).reshape(M, N), ref, x, dy, g, rho, O.BF16)
+    check_dgamma(to_host(dgt), ref)
+
+
+def test_bwd_bit_reproducible():
+    M, N = 2048, 8192
+    x, g, _, dy = _inputs(M, N, O.BF16, O.BF16, 81, with_dy=True)
+    rho = O.rmsnorm_fwd(x, g, M, N, 1e-5, O.BF16, O.BF16, want_exact=False)["rstd"]
+    xt, gt, dyt, rt = _put(x, O.BF16), _put(g, O.BF16), _put(dy, O.BF16), torch.from_numpy(rho).cuda()
+    wsb = R.rmsnorm_bwd_workspace_size(M, N, O.BF16)
+    outs = []
+    for k in range(3):
+        dxt, dgt = _empty(M * N, O.BF16), torch.empty(N, device="cuda")
+        ws = torch.full((wsb // 4,), float(k), device="cuda")
+        assert R.rmsnorm_bwd(dyt, xt, rt, gt, dxt, dgt, ws, wsb, M, N, O.BF16, O.BF16,
+                             _stream()) == 0
+        torch.cuda.synchronize()
+        outs.append((to_host(dxt), to_host(dgt)))
+    for dx, dg in outs[1:]:
+        assert np.array_equal(dx, outs[0][0])
+        assert np.array_equal(dg.view(np.uint32), outs[0][1].view(np.uint32))
+
+
+def test_bwd_empty_is_noop():
+    assert R.rmsnorm_bwd(None, None, None, None, None, None, None, 0, 0, 64, O.BF16, O.BF16,
+                         _stream()) == 0
+
+
+# ------------------------------------------------- the five full workloads
+
+@pytest.mark.parametrize("w", G.WORKLOADS, ids=[w.name for w in G.WORKLOADS])
+def test_workload_full_size(w):
+    """Each workload at full size, in the launch configuration the benchmark
+    times, checked element by element against the oracle."""
+    if w.kind == "fwd":
+        run_fwd(w.M, w.N, w.x_dt, w.g_dt, eps=w.eps, seed=w.seed, want_rstd=w.store_rstd,
+                outlier_every=w.outlier_every, outlier_scale=w.outlier_scale)
+    elif w.kind == "fused_add":
+        run_fused(w.M, w.N, w.x_dt, w.g_dt, eps=w.eps, seed=w.seed, want_rstd=w.store_rstd)
+    else:
+        floor_only = run_bwd(w.M, w.N, w.x_dt, w.g_dt, seed=w.seed, eps=w.eps)
+        _log(f"dx elements passing only by the cancellation floor: {floor_only}")
