@@ -208,6 +208,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-others", action="store_true", help="time only the headline workload")
+    ap.add_argument("--other-steps", type=int, default=0,
+                    help="steps per other workload (default: enough for ~50 ms each)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -276,7 +278,7 @@ def main() -> int:
             oh = G.make_inputs(ow)
             orun = Runner(ow, 0 if ow.M * ow.N < (1 << 20) else args.rotate_bytes, oh)
             est = max(ow.algorithmic_bytes() / 6e12, 3e-6)
-            k = int(min(2000, max(50, 0.05 / est)))
+            k = args.other_steps or int(min(2000, max(50, 0.05 / est)))
             oms = time_steps(orun.step, k, max(k // 10, 5))
             ob = ow.algorithmic_bytes()
             others[ow.name] = {"ms_per_step": round(oms, 6), "gbps": round(ob / (oms * 1e-3) / 1e9, 2),

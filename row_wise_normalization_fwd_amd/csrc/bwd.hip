@@ -1,9 +1,13 @@
 // Backward RMSNorm kernel choice and launch (stage 1 then stage 2, same stream).
 //
-// Stage 1 uses a group of TPR lanes per row with UPT units per lane (the same
-// shape rule as the forward register path) and BLOCK = max(TPR, 256) threads,
-// so short rows get several row groups per block. Rows that are not 16-byte
-// aligned use 1-element units.
+// Stage 1 uses a group of TPR lanes per row with two 16-byte units per lane
+// (TPR = next power of two of ceil(units / 2), at most 512 lanes; longer rows
+// use 1024 lanes with up to four units). When a block owns at least two rows,
+// it runs 1024 threads, i.e. 1024 / TPR row groups whose dgamma partials are
+// combined through LDS: at 8192 x 8192 bf16 this (two 512-lane groups per
+// block, one block per CU) measured fastest among 1, 2 and 4 groups, 256 to
+// 1024 lanes per row, 256 / 384 / 512 blocks and with or without prefetching
+// the next row. Rows that are not 16-byte aligned use 1-element units.
 #include "bwd_kernels.hpp"
 #include "launch.hpp"
 
@@ -13,10 +17,27 @@ template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK>
 hipError_t run_stage1(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s) {
   constexpr int RG = BLOCK / TPR;
   constexpr int E = Unit<T, VEC>::E;
-  const size_t lds = RG > 1 ? static_cast<size_t>(BLOCK) * UPT * E * sizeof(float) : 0;
-  bwd_stage1_kernel<T, G, VEC, TPR, UPT, BLOCK>
-      <<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), lds, s>>>(a);
+  constexpr size_t kLds = RG > 1 ? static_cast<size_t>(BLOCK) * UPT * E * sizeof(float) : 0;
+  auto* kernel = bwd_stage1_kernel<T, G, VEC, TPR, UPT, BLOCK, false>;
+  if constexpr (kLds > 48 * 1024) {
+    // Raise the dynamic LDS limit once per instantiation (gfx950 has 160 KiB).
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+        static_cast<int>(kLds));
+    if (attr != hipSuccess) return attr;
+  }
+  kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), kLds, s>>>(a);
   return hipGetLastError();
+}
+
+// Lanes per row TPR with UPT units each; a full 1024-thread block of row
+// groups when the block owns at least two rows.
+template <class T, class G, bool VEC, int TPR, int UPT>
+hipError_t run_stage1_rows(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s) {
+  if constexpr (TPR < 1024) {
+    if (a.rows_per_block >= 2) return run_stage1<T, G, VEC, TPR, UPT, 1024>(a, blocks, s);
+  }
+  return run_stage1<T, G, VEC, TPR, UPT, (TPR > 256 ? TPR : 256)>(a, blocks, s);
 }
 
 template <class T, class G>
@@ -24,16 +45,21 @@ hipError_t stage1_typed(const BwdArgs<T, G>& a, bool vec, int64_t blocks, hipStr
   const int64_t N = a.N;
   if (vec) {
     constexpr int E = 16 / T::kSize;
-    const int64_t tpr = next_pow2(ceil_div(N / E, 4));
-    if (tpr <= 4) return run_stage1<T, G, true, 4, 4, 256>(a, blocks, s);
-    if (tpr == 8) return run_stage1<T, G, true, 8, 4, 256>(a, blocks, s);
-    if (tpr == 16) return run_stage1<T, G, true, 16, 4, 256>(a, blocks, s);
-    if (tpr == 32) return run_stage1<T, G, true, 32, 4, 256>(a, blocks, s);
-    if (tpr == 64) return run_stage1<T, G, true, 64, 4, 256>(a, blocks, s);
-    if (tpr == 128) return run_stage1<T, G, true, 128, 4, 256>(a, blocks, s);
-    if (tpr == 256) return run_stage1<T, G, true, 256, 4, 256>(a, blocks, s);
-    if (tpr == 512) return run_stage1<T, G, true, 512, 4, 512>(a, blocks, s);
-    return run_stage1<T, G, true, 1024, 4, 1024>(a, blocks, s);
+    const int64_t units = N / E;
+    if (units > 2048) return run_stage1_rows<T, G, true, 1024, 4>(a, blocks, s);
+    if (units > 1024) return run_stage1_rows<T, G, true, 1024, 2>(a, blocks, s);
+    switch (next_pow2(ceil_div(units, 2))) {
+      case 1: return run_stage1_rows<T, G, true, 1, 2>(a, blocks, s);
+      case 2: return run_stage1_rows<T, G, true, 2, 2>(a, blocks, s);
+      case 4: return run_stage1_rows<T, G, true, 4, 2>(a, blocks, s);
+      case 8: return run_stage1_rows<T, G, true, 8, 2>(a, blocks, s);
+      case 16: return run_stage1_rows<T, G, true, 16, 2>(a, blocks, s);
+      case 32: return run_stage1_rows<T, G, true, 32, 2>(a, blocks, s);
+      case 64: return run_stage1_rows<T, G, true, 64, 2>(a, blocks, s);
+      case 128: return run_stage1_rows<T, G, true, 128, 2>(a, blocks, s);
+      case 256: return run_stage1_rows<T, G, true, 256, 2>(a, blocks, s);
+      default: return run_stage1_rows<T, G, true, 512, 2>(a, blocks, s);
+    }
   }
   if (N <= 512) return run_stage1<T, G, false, 64, 8, 256>(a, blocks, s);
   if (N <= 2048) return run_stage1<T, G, false, 256, 8, 256>(a, blocks, s);
@@ -58,10 +84,17 @@ hipError_t bwd_typed(const BwdCall& c) {
                    aligned16(c.dx) && aligned16(c.gamma);
   hipError_t e = stage1_typed<T, G>(a, vec, c.plan.blocks, c.stream);
   if (e != hipSuccess) return e;
-  const int64_t cols = ceil_div(c.N, kStage2Cols);
-  bwd_stage2_kernel<<<dim3(static_cast<unsigned>(cols)), dim3(kStage2Cols * kStage2Slices), 0,
-                      c.stream>>>(a.partial, c.dgamma, static_cast<int>(c.plan.blocks),
-                                  static_cast<int>(c.N));
+  // Partial rows are 16-byte aligned when N % 4 == 0 (workspace is).
+  constexpr int kGroups = kS2Threads / kS2Slices;
+  if (c.N % 4 == 0) {
+    const int64_t blocks = ceil_div(c.N, 4 * kGroups);
+    bwd_stage2_kernel<4><<<dim3(static_cast<unsigned>(blocks)), dim3(kS2Threads), 0, c.stream>>>(
+        a.partial, c.dgamma, static_cast<int>(c.plan.blocks), static_cast<int>(c.N));
+  } else {
+    const int64_t blocks = ceil_div(c.N, kGroups);
+    bwd_stage2_kernel<1><<<dim3(static_cast<unsigned>(blocks)), dim3(kS2Threads), 0, c.stream>>>(
+        a.partial, c.dgamma, static_cast<int>(c.plan.blocks), static_cast<int>(c.N));
+  }
   return hipGetLastError();
 }
 

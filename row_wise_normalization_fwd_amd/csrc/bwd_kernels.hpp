@@ -48,11 +48,14 @@ __device__ __forceinline__ double dot_term(float dyv, float g, float xv) {
 // Stage 1. A block of BLOCK threads holds RG = BLOCK / TPR row groups; group
 // `grp` takes rows base + grp for base = r0, r0 + RG, ... inside the block's
 // range [r0, r1). Each lane keeps gamma and its columns' dgamma partial sums in
-// registers. With RG > 1 the groups' partials are combined through LDS in
-// group order before the block writes its partial row.
-template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK>
+// registers. With PF the x and dy units of a group's next row are loaded
+// before the current row is reduced, so loads stay in flight across rows.
+// With RG > 1 the groups' partials are combined through LDS in group order
+// before the block writes its partial row.
+template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool PF>
 __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   using U = Unit<T, VEC>;
+  using Raw = typename U::Raw;
   constexpr int E = U::E;
   constexpr int RG = BLOCK / TPR;
   constexpr int COLS = TPR * UPT * E;  // columns covered by one row group
@@ -82,32 +85,58 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
     for (int e = 0; e < E; ++e) acc[k][e] = 0.0f;
   }
 
+  // x and dy units of `row` (zeros outside the block's rows).
+  auto load_row = [&](int64_t row, Raw* rx, Raw* rdy) {
+    const bool valid = row < r1;
+    const int64_t off = row * a.N;
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const int u = lane + k * TPR;
+      const bool ok = valid && u < nunits;
+      rx[k] = ok ? U::load_nt(a.x + off + u * E) : U::zero();
+      rdy[k] = ok ? U::load_nt(a.dy + off + u * E) : U::zero();
+    }
+  };
+
+  Raw nx[UPT], ndy[UPT];
+  if constexpr (PF) load_row(r0 + grp, nx, ndy);
+
   int parity = 0;
   for (int64_t base = r0; base < r1; base += RG) {  // uniform over the block
     const int64_t row = base + grp;
     const bool valid = row < r1;
     const int64_t off = row * a.N;
 
-    typename U::Raw rx[UPT], rdy[UPT];
+    Raw rx[UPT], rdy[UPT];
+    if constexpr (PF) {
 #pragma unroll
-    for (int k = 0; k < UPT; ++k) {
-      const int u = lane + k * TPR;
-      const bool ok = valid && u < nunits;
-      rx[k] = ok ? U::load(a.x + off + u * E) : U::zero();
-      rdy[k] = ok ? U::load(a.dy + off + u * E) : U::zero();
+      for (int k = 0; k < UPT; ++k) {
+        rx[k] = nx[k];
+        rdy[k] = ndy[k];
+      }
+      load_row(row + RG, nx, ndy);
+    } else {
+      load_row(row, rx, rdy);
     }
     const float rho = valid ? a.rstd[row] : 0.0f;
 
-    float xv[UPT][E], dyv[UPT][E];
     double part[UPT];
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
-      U::widen(rx[k], xv[k]);
-      U::widen(rdy[k], dyv[k]);
+      float xv[E], dyv[E];
+      U::widen(rx[k], xv);
+      U::widen(rdy[k], dyv);
       double s = 0.0;
 #pragma unroll
-      for (int e = 0; e < E; ++e) s = s + dot_term<T, G>(dyv[k][e], gam[k][e], xv[k][e]);
+      for (int e = 0; e < E; ++e) s = s + dot_term<T, G>(dyv[e], gam[k][e], xv[e]);
       part[k] = s;
+    }
+    // Re-widen x and dy after the reduction rather than holding the fp32
+    // copies across it: fewer live VGPRs, more row groups per CU.
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      opaque(rx[k]);
+      opaque(rdy[k]);
     }
     double dot = part[0];
 #pragma unroll
@@ -120,11 +149,13 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const int u = lane + k * TPR;
-      float o[E];
+      float xv[E], dyv[E], o[E];
+      U::widen(rx[k], xv);
+      U::widen(rdy[k], dyv);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        o[e] = rho * __builtin_fmaf(-xv[k][e], kcoef, gam[k][e] * dyv[k][e]);
-        acc[k][e] = __builtin_fmaf(dyv[k][e] * xv[k][e], rho, acc[k][e]);
+        o[e] = rho * __builtin_fmaf(-xv[e], kcoef, gam[k][e] * dyv[e]);
+        acc[k][e] = __builtin_fmaf(dyv[e] * xv[e], rho, acc[k][e]);
       }
       if (valid && u < nunits) U::store_nt(a.dx + off + u * E, U::narrow(o));
     }
@@ -157,32 +188,51 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   }
 }
 
-// Stage 2: dgamma_j = sum over blocks of partial[b][j]. A 256-thread block
-// covers 64 columns with 4 interleaved slices of partial rows; each slice sums
-// in increasing row order in double, and the 4 slice sums are added in slice
-// order. The result is rounded to fp32 once.
-constexpr int kStage2Cols = 64;
-constexpr int kStage2Slices = 4;
+// Stage 2: dgamma_j = sum over blocks b of partial[b][j], in a fixed order.
+// A 256-thread block covers kS2Cols columns: each thread owns CPT adjacent
+// columns (one 16-byte load per partial row when CPT == 4) and one of
+// kS2Slices interleaved slices of partial rows (b = slice, slice + kS2Slices,
+// ...), summed in increasing b in double; the slice sums are then added in
+// slice order through LDS and rounded to fp32 once.
+constexpr int kS2Threads = 256;
+constexpr int kS2Slices = 16;
 
-__global__ __launch_bounds__(kStage2Cols * kStage2Slices) void bwd_stage2_kernel(
+template <int CPT>
+__global__ __launch_bounds__(kS2Threads) void bwd_stage2_kernel(
     const float* __restrict__ partial, float* __restrict__ dgamma, int nblocks, int N) {
-  __shared__ double red[kStage2Slices][kStage2Cols];
-  const int c = threadIdx.x % kStage2Cols;
-  const int slice = threadIdx.x / kStage2Cols;
-  const int col = blockIdx.x * kStage2Cols + c;
-  double s = 0.0;
-  if (col < N) {
-#pragma unroll 8
-    for (int b = slice; b < nblocks; b += kStage2Slices)
-      s = s + static_cast<double>(partial[static_cast<int64_t>(b) * N + col]);
-  }
-  red[slice][c] = s;
-  __syncthreads();
-  if (slice == 0 && col < N) {
-    double t = red[0][c];
+  constexpr int kGroups = kS2Threads / kS2Slices;  // column groups per block
+  __shared__ double red[kS2Slices][kGroups][CPT];
+  const int grp = threadIdx.x % kGroups;
+  const int slice = threadIdx.x / kGroups;
+  const int col0 = (blockIdx.x * kGroups + grp) * CPT;
+  double s[CPT];
 #pragma unroll
-    for (int q = 1; q < kStage2Slices; ++q) t = t + red[q][c];
-    dgamma[col] = static_cast<float>(t);
+  for (int c = 0; c < CPT; ++c) s[c] = 0.0;
+  if (col0 < N) {  // with CPT == 4, N % 4 == 0, so all four columns exist
+#pragma unroll 4
+    for (int b = slice; b < nblocks; b += kS2Slices) {
+      const float* p = partial + static_cast<int64_t>(b) * N + col0;
+      if constexpr (CPT == 4) {
+        const float4 v = *reinterpret_cast<const float4*>(p);
+        s[0] = s[0] + static_cast<double>(v.x);
+        s[1] = s[1] + static_cast<double>(v.y);
+        s[2] = s[2] + static_cast<double>(v.z);
+        s[3] = s[3] + static_cast<double>(v.w);
+      } else {
+        s[0] = s[0] + static_cast<double>(p[0]);
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) red[slice][grp][c] = s[c];
+  __syncthreads();
+  if (slice == 0 && col0 < N) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      double t = red[0][grp][c];
+      for (int q = 1; q < kS2Slices; ++q) t = t + red[q][grp][c];
+      dgamma[col0 + c] = static_cast<float>(t);
+    }
   }
 }
 

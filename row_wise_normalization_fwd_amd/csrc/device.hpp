@@ -85,6 +85,10 @@ struct Unit<T, true> {
   static constexpr int E = 16 / T::kSize;  // elements per unit
   using Raw = u32x4;
   __device__ static Raw load(const typename T::S* p) { return *reinterpret_cast<const Raw*>(p); }
+  // Streaming load (nt): data read once is not kept in the caches.
+  __device__ static Raw load_nt(const typename T::S* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const Raw*>(p));
+  }
   __device__ static void store(typename T::S* p, Raw v) { *reinterpret_cast<Raw*>(p) = v; }
   __device__ static void store_nt(typename T::S* p, Raw v) {
     __builtin_nontemporal_store(v, reinterpret_cast<Raw*>(p));
@@ -107,12 +111,21 @@ struct Unit<T, false> {
   static constexpr int E = 1;
   using Raw = typename T::S;
   __device__ static Raw load(const typename T::S* p) { return *p; }
+  __device__ static Raw load_nt(const typename T::S* p) { return __builtin_nontemporal_load(p); }
   __device__ static void store(typename T::S* p, Raw v) { *p = v; }
   __device__ static void store_nt(typename T::S* p, Raw v) { __builtin_nontemporal_store(v, p); }
   __device__ static Raw zero() { return Raw(0); }
   __device__ static void widen(Raw v, float* f) { f[0] = T::widen(v); }
   __device__ static Raw narrow(const float* f) { return T::narrow(f[0]); }
 };
+
+// Make the compiler treat v as modified here, so values derived from it
+// before this point are recomputed afterwards instead of being kept live
+// (trades a few ALU ops for registers). Emits no instruction.
+template <class V>
+__device__ __forceinline__ void opaque(V& v) {
+  asm volatile("" : "+v"(v));
+}
 
 // Load E consecutive gamma values starting at element offset `off` as fp32.
 // In the vector case the caller guarantees 16-byte alignment of gamma + off.

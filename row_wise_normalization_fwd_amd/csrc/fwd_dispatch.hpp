@@ -3,11 +3,16 @@
 // parallel.
 //
 // Register path (N <= 8192): a group of TPR lanes per row with UPT units per
-// lane, TPR = next power of two of ceil(units / 4), so every lane issues up to
-// four 16-byte loads per operand. Short rows pack BLOCK / TPR rows per block.
-// Rows that are not 16-byte aligned use 1-element units (up to 8 per lane).
-// Longer rows: one 256-thread block per row, parked in LDS when the row fits
-// in 64 KiB, else re-read.
+// lane. TPR = next power of two of ceil(units / 2), so each lane moves two
+// 16-byte units per operand (measured best at 4096 x 8192 bf16 among 1, 2, 4
+// and 8 units per lane, with or without a prefetching persistent loop), and
+// rows of up to 1024 units use up to 512 lanes; longer register rows (fp32,
+// N <= 8192) use 4 units on 512 lanes. When that leaves over a third of the
+// lanes idle, half the lanes with 3 units each is used instead (at 32768 x
+// 5000 fp16, 625 units: 256 x 3 measured 7% faster than 512 x 2). Short rows pack BLOCK / TPR rows per
+// block. Rows that are not 16-byte aligned use 1-element units (up to 8 per
+// lane). Longer rows: one 256-thread block per row, parked in LDS when the row
+// fits the LDS budget, else re-read.
 #pragma once
 
 #include "fwd_kernels.hpp"
@@ -53,19 +58,31 @@ hipError_t fwd_typed(const FwdCall& c) {
     if (vec) {
       constexpr int E = 16 / T::kSize;
       const int64_t units = c.N / E;
-      const int64_t tpr = next_pow2(ceil_div(units, 4));
-      if (tpr <= 4) return run_fwd_reg<T, G, true, 4, 4, 256, FUSED>(a, s);
-      if (tpr == 8) return run_fwd_reg<T, G, true, 8, 4, 256, FUSED>(a, s);
-      if (tpr == 16) return run_fwd_reg<T, G, true, 16, 4, 256, FUSED>(a, s);
-      if (tpr == 32) return run_fwd_reg<T, G, true, 32, 4, 256, FUSED>(a, s);
-      if (tpr == 64) return run_fwd_reg<T, G, true, 64, 4, 256, FUSED>(a, s);
-      if (tpr == 128) return run_fwd_reg<T, G, true, 128, 4, 256, FUSED>(a, s);
-      if (tpr == 256) {
-        if (units <= 3 * 256) return run_fwd_reg<T, G, true, 256, 3, 256, FUSED>(a, s);
-        return run_fwd_reg<T, G, true, 256, 4, 256, FUSED>(a, s);
+      if (units > 1024) return run_fwd_reg<T, G, true, 512, 4, 512, FUSED>(a, s);
+      const int64_t tpr2 = next_pow2(ceil_div(units, 2));
+      if (tpr2 >= 8 && 3 * units < 4 * tpr2 && units <= 3 * (tpr2 / 2)) {
+        switch (tpr2 / 2) {  // 3 units on half the lanes
+          case 4: return run_fwd_reg<T, G, true, 4, 3, 256, FUSED>(a, s);
+          case 8: return run_fwd_reg<T, G, true, 8, 3, 256, FUSED>(a, s);
+          case 16: return run_fwd_reg<T, G, true, 16, 3, 256, FUSED>(a, s);
+          case 32: return run_fwd_reg<T, G, true, 32, 3, 256, FUSED>(a, s);
+          case 64: return run_fwd_reg<T, G, true, 64, 3, 256, FUSED>(a, s);
+          case 128: return run_fwd_reg<T, G, true, 128, 3, 256, FUSED>(a, s);
+          default: return run_fwd_reg<T, G, true, 256, 3, 256, FUSED>(a, s);
+        }
       }
-      if (units <= 3 * 512) return run_fwd_reg<T, G, true, 512, 3, 512, FUSED>(a, s);
-      return run_fwd_reg<T, G, true, 512, 4, 512, FUSED>(a, s);
+      switch (tpr2) {
+        case 1: return run_fwd_reg<T, G, true, 1, 2, 256, FUSED>(a, s);
+        case 2: return run_fwd_reg<T, G, true, 2, 2, 256, FUSED>(a, s);
+        case 4: return run_fwd_reg<T, G, true, 4, 2, 256, FUSED>(a, s);
+        case 8: return run_fwd_reg<T, G, true, 8, 2, 256, FUSED>(a, s);
+        case 16: return run_fwd_reg<T, G, true, 16, 2, 256, FUSED>(a, s);
+        case 32: return run_fwd_reg<T, G, true, 32, 2, 256, FUSED>(a, s);
+        case 64: return run_fwd_reg<T, G, true, 64, 2, 256, FUSED>(a, s);
+        case 128: return run_fwd_reg<T, G, true, 128, 2, 256, FUSED>(a, s);
+        case 256: return run_fwd_reg<T, G, true, 256, 2, 256, FUSED>(a, s);
+        default: return run_fwd_reg<T, G, true, 512, 2, 512, FUSED>(a, s);
+      }
     }
     const int64_t tpr = next_pow2(ceil_div(c.N, 8));
     if (tpr <= 16) return run_fwd_reg<T, G, false, 16, 8, 256, FUSED>(a, s);

@@ -15,7 +15,10 @@
 // Every lane computes in fp32; sums of squares use per-unit partial sums
 // added in a fixed order, then the fixed-order group reduction, so results do
 // not depend on timing. Output stores are non-temporal (the guide's
-// USE_NONTEMPORAL for outputs).
+// USE_NONTEMPORAL for outputs); the register path also streams its inputs
+// with non-temporal loads (measured faster on gfx950 when inputs are not
+// cache-resident). The re-read path keeps ordinary loads so its second pass
+// can hit in L2 / MALL.
 #pragma once
 
 #include "device.hpp"
@@ -89,8 +92,8 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
     for (int k = 0; k < UPT; ++k) {
       const int u = lane + k * TPR;
       const bool ok = valid && u < nunits;
-      raw[k] = ok ? U::load(a.x + off + u * E) : U::zero();
-      if constexpr (FUSED) res[k] = ok ? U::load(a.residual + off + u * E) : U::zero();
+      raw[k] = ok ? U::load_nt(a.x + off + u * E) : U::zero();
+      if constexpr (FUSED) res[k] = ok ? U::load_nt(a.residual + off + u * E) : U::zero();
     }
 
     float v[UPT][E];
@@ -150,8 +153,13 @@ __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
 #pragma unroll
       for (int k = 0; k < UNROLL; ++k) {
         const int u = first + threadIdx.x + k * BLOCK;
-        raw[k] = u < nunits ? U::load(a.x + off + u * E) : U::zero();
-        if constexpr (FUSED) res[k] = u < nunits ? U::load(a.residual + off + u * E) : U::zero();
+        if constexpr (CACHE) {  // read once: stream it
+          raw[k] = u < nunits ? U::load_nt(a.x + off + u * E) : U::zero();
+          if constexpr (FUSED) res[k] = u < nunits ? U::load_nt(a.residual + off + u * E) : U::zero();
+        } else {                // read twice: keep it cacheable for the second pass
+          raw[k] = u < nunits ? U::load(a.x + off + u * E) : U::zero();
+          if constexpr (FUSED) res[k] = u < nunits ? U::load(a.residual + off + u * E) : U::zero();
+        }
       }
 #pragma unroll
       for (int k = 0; k < UNROLL; ++k) {
