@@ -2,6 +2,7 @@
 // validation (before any HIP call), the backward partition, status strings.
 #include "rmsnorm_mi355x.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -92,15 +93,40 @@ int forward(bool fused, const void* x, void* residual, const void* gamma, void* 
 
 namespace rmsn {
 
+int64_t lds_row_budget() {
+  static std::atomic<int64_t> cache[64];  // per device; 0 = not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 64 * 1024 - kLdsReserve;
+  int64_t v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int bytes = 0;
+    if (hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess ||
+        bytes <= 0)
+      bytes = 64 * 1024;
+    v = static_cast<int64_t>(bytes) - kLdsReserve;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+hipError_t allow_dynamic_lds(const void* kernel, size_t bytes) {
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             static_cast<int>(bytes));
+}
+
 BwdPlan plan_bwd(int64_t M, int64_t N, int x_dtype) {
-  BwdPlan p{false, 0, 0, 0};
+  BwdPlan p{false, 0, 0, 0, 0};
   if (!valid_dtype(x_dtype) || M <= 0 || N <= 0) return p;
-  p.supported = N <= bwd_max_n(esize_of(x_dtype));
+  p.valid = true;
   p.rows_per_block = ceil_div(M, kBwdTargetBlocks);
   p.blocks = ceil_div(M, p.rows_per_block);
-  // One fp32 partial row per block, rounded up to 256 bytes.
-  const uint64_t bytes = static_cast<uint64_t>(p.blocks) * static_cast<uint64_t>(N) * 4u;
-  p.workspace_bytes = static_cast<size_t>((bytes + 255u) & ~static_cast<uint64_t>(255u));
+  auto round256 = [](uint64_t b) { return (b + 255u) & ~static_cast<uint64_t>(255u); };
+  // One fp32 partial row per block, then (long rows) one double per row.
+  p.partial_bytes = static_cast<size_t>(
+      round256(static_cast<uint64_t>(p.blocks) * static_cast<uint64_t>(N) * 4u));
+  const uint64_t dots = N > kBwdOnChipN ? round256(static_cast<uint64_t>(M) * 8u) : 0u;
+  p.workspace_bytes = p.partial_bytes + static_cast<size_t>(dots);
   return p;
 }
 
@@ -130,7 +156,6 @@ int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* ga
   if (!shape_ok(M, N)) return RMSN_ERR_SHAPE;
   if (M == 0) return RMSN_OK;
   const rmsn::BwdPlan plan = rmsn::plan_bwd(M, N, x_dtype);
-  if (!plan.supported) return RMSN_ERR_SHAPE;
   if (!dy || !x || !rstd || !gamma || !dx || !dgamma) return RMSN_ERR_NULL;
   if (!workspace || workspace_bytes < plan.workspace_bytes) return RMSN_ERR_WORKSPACE;
   const int es = esize_of(x_dtype), gs = esize_of(gamma_dtype);

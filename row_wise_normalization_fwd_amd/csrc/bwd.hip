@@ -1,8 +1,9 @@
 // Backward RMSNorm kernel choice and launch (stage 1 then stage 2, same stream).
 //
 // Stage 1 uses a group of TPR lanes per row with two 16-byte units per lane
-// (TPR = next power of two of ceil(units / 2), at most 512 lanes; longer rows
-// use 1024 lanes with up to four units). When a block owns at least two rows,
+// (TPR = next power of two of ceil(units / 2), up to 1024 lanes, i.e. 16384
+// bf16 / 8192 fp32 elements; unaligned rows up to 8192 elements). Longer rows
+// take the two-pass long-row tier (row dots, then 2-D tiles). When a block owns at least two rows,
 // it runs 1024 threads, i.e. 1024 / TPR row groups whose dgamma partials are
 // combined through LDS: at 8192 x 8192 bf16 this (two 512-lane groups per
 // block, one block per CU) measured fastest among 1, 2 and 4 groups, 256 to
@@ -40,13 +41,14 @@ hipError_t run_stage1_rows(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s
   return run_stage1<T, G, VEC, TPR, UPT, (TPR > 256 ? TPR : 256)>(a, blocks, s);
 }
 
+// One-pass path: returns hipErrorNotSupported when the row does not fit.
 template <class T, class G>
 hipError_t stage1_typed(const BwdArgs<T, G>& a, bool vec, int64_t blocks, hipStream_t s) {
   const int64_t N = a.N;
   if (vec) {
     constexpr int E = 16 / T::kSize;
     const int64_t units = N / E;
-    if (units > 2048) return run_stage1_rows<T, G, true, 1024, 4>(a, blocks, s);
+    if (units > 2048) return hipErrorNotSupported;
     if (units > 1024) return run_stage1_rows<T, G, true, 1024, 2>(a, blocks, s);
     switch (next_pow2(ceil_div(units, 2))) {
       case 1: return run_stage1_rows<T, G, true, 1, 2>(a, blocks, s);
@@ -61,11 +63,31 @@ hipError_t stage1_typed(const BwdArgs<T, G>& a, bool vec, int64_t blocks, hipStr
       default: return run_stage1_rows<T, G, true, 512, 2>(a, blocks, s);
     }
   }
+  if (N > kBwdOnChipN) return hipErrorNotSupported;
   if (N <= 512) return run_stage1<T, G, false, 64, 8, 256>(a, blocks, s);
   if (N <= 2048) return run_stage1<T, G, false, 256, 8, 256>(a, blocks, s);
-  if (N <= 8192) return run_stage1<T, G, false, 1024, 8, 1024>(a, blocks, s);
-  if (N <= 16384) return run_stage1<T, G, false, 1024, 16, 1024>(a, blocks, s);
-  return run_stage1<T, G, false, 1024, 32, 1024>(a, blocks, s);
+  return run_stage1<T, G, false, 1024, 8, 1024>(a, blocks, s);
+}
+
+// Long-row tier: pass A (row dots), pass B (tiles). Same partition and
+// partial layout as the one-pass path.
+template <class T, class G, bool VEC>
+hipError_t long_rows_typed(const BwdArgs<T, G>& a, double* cdot, int64_t blocks, hipStream_t s) {
+  constexpr int kUnroll = VEC ? 4 : 8;
+  constexpr int kTileBlock = 256;
+  constexpr int kTileUpt = VEC ? 2 : 8;
+  constexpr int E = Unit<T, VEC>::E;
+  const int64_t rows = a.M < kMaxGrid ? a.M : kMaxGrid;
+  bwd_rowdot_kernel<T, G, VEC, 1024, kUnroll>
+      <<<dim3(static_cast<unsigned>(rows)), dim3(1024), 0, s>>>(a, cdot);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t units = a.N / E;
+  const int64_t chunks = ceil_div(units, kTileBlock * kTileUpt);
+  bwd_tile_kernel<T, G, VEC, kTileBlock, kTileUpt>
+      <<<dim3(static_cast<unsigned>(chunks), static_cast<unsigned>(blocks)), dim3(kTileBlock), 0,
+         s>>>(a, cdot);
+  return hipGetLastError();
 }
 
 template <class T, class G>
@@ -83,6 +105,12 @@ hipError_t bwd_typed(const BwdCall& c) {
   const bool vec = (c.N * T::kSize) % 16 == 0 && aligned16(c.dy) && aligned16(c.x) &&
                    aligned16(c.dx) && aligned16(c.gamma);
   hipError_t e = stage1_typed<T, G>(a, vec, c.plan.blocks, c.stream);
+  if (e == hipErrorNotSupported) {
+    double* cdot =
+        reinterpret_cast<double*>(static_cast<char*>(c.workspace) + c.plan.partial_bytes);
+    e = vec ? long_rows_typed<T, G, true>(a, cdot, c.plan.blocks, c.stream)
+            : long_rows_typed<T, G, false>(a, cdot, c.plan.blocks, c.stream);
+  }
   if (e != hipSuccess) return e;
   // Partial rows are 16-byte aligned when N % 4 == 0 (workspace is).
   constexpr int kGroups = kS2Threads / kS2Slices;

@@ -188,6 +188,116 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   }
 }
 
+// Long rows (rows too long for stage 1's registers), in two passes.
+//
+// Pass A: c_i = (1/N) sum_j dy_ij gamma_j x_ij in double, one block per row,
+// looping over the row; ordinary (cacheable) loads since pass B reads the
+// same rows again.
+template <class T, class G, bool VEC, int BLOCK, int UNROLL>
+__global__ __launch_bounds__(BLOCK) void bwd_rowdot_kernel(BwdArgs<T, G> a, double* cdot) {
+  using U = Unit<T, VEC>;
+  using Raw = typename U::Raw;
+  constexpr int E = U::E;
+  constexpr int STEP = BLOCK * UNROLL;
+  __shared__ double red[2 * (BLOCK / kWave)];
+  const int nunits = a.N / E;
+  int parity = 0;
+  for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x) {
+    const int64_t off = row * a.N;
+    double dot = 0.0;
+    for (int first = 0; first < nunits; first += STEP) {
+      Raw rx[UNROLL], rdy[UNROLL];
+#pragma unroll
+      for (int k = 0; k < UNROLL; ++k) {
+        const int u = first + threadIdx.x + k * BLOCK;
+        rx[k] = u < nunits ? U::load(a.x + off + u * E) : U::zero();
+        rdy[k] = u < nunits ? U::load(a.dy + off + u * E) : U::zero();
+      }
+#pragma unroll
+      for (int k = 0; k < UNROLL; ++k) {
+        const int u = first + threadIdx.x + k * BLOCK;
+        if (u < nunits) {
+          float xv[E], dyv[E], g[E];
+          U::widen(rx[k], xv);
+          U::widen(rdy[k], dyv);
+          load_gamma<G, E, VEC>(a.gamma, u * E, g);
+          double s = 0.0;
+#pragma unroll
+          for (int e = 0; e < E; ++e) s = s + dot_term<T, G>(dyv[e], g[e], xv[e]);
+          dot = dot + s;
+        }
+      }
+    }
+    dot = row_sum<BLOCK, BLOCK>(dot, red, parity);
+    parity ^= 1;
+    if (threadIdx.x == 0) cdot[row] = dot / static_cast<double>(a.N);
+  }
+}
+
+// Pass B: block (bx, by) covers columns [bx * COLS, (bx + 1) * COLS) of rows
+// [by * rows_per_block, ...), COLS = BLOCK * UPT * E. Each lane keeps gamma and
+// the dgamma partial sums of its columns in registers over the block's rows
+// (in increasing row order) and writes them to partial[by][...]; dx uses the
+// row dots from pass A.
+template <class T, class G, bool VEC, int BLOCK, int UPT>
+__global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const double* cdot) {
+  using U = Unit<T, VEC>;
+  using Raw = typename U::Raw;
+  constexpr int E = U::E;
+  const int nunits = a.N / E;
+  const int ubase = blockIdx.x * (BLOCK * UPT);
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * a.rows_per_block;
+  const int64_t r1 = r0 + a.rows_per_block < a.M ? r0 + a.rows_per_block : a.M;
+  float gam[UPT][E], acc[UPT][E];
+#pragma unroll
+  for (int k = 0; k < UPT; ++k) {
+    const int u = ubase + threadIdx.x + k * BLOCK;
+    if (u < nunits) {
+      load_gamma<G, E, VEC>(a.gamma, u * E, gam[k]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) gam[k][e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[k][e] = 0.0f;
+  }
+  for (int64_t row = r0; row < r1; ++row) {
+    const int64_t off = row * a.N;
+    Raw rx[UPT], rdy[UPT];
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const int u = ubase + threadIdx.x + k * BLOCK;
+      rx[k] = u < nunits ? U::load(a.x + off + u * E) : U::zero();
+      rdy[k] = u < nunits ? U::load(a.dy + off + u * E) : U::zero();
+    }
+    const float rho = a.rstd[row];
+    const double rd = static_cast<double>(rho);
+    const float kcoef = static_cast<float>(rd * rd * cdot[row]);
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const int u = ubase + threadIdx.x + k * BLOCK;
+      float xv[E], dyv[E], o[E];
+      U::widen(rx[k], xv);
+      U::widen(rdy[k], dyv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        o[e] = rho * __builtin_fmaf(-xv[e], kcoef, gam[k][e] * dyv[e]);
+        acc[k][e] = __builtin_fmaf(dyv[e] * xv[e], rho, acc[k][e]);
+      }
+      if (u < nunits) U::store_nt(a.dx + off + u * E, U::narrow(o));
+    }
+  }
+  float* out = a.partial + static_cast<int64_t>(blockIdx.y) * a.N;
+#pragma unroll
+  for (int k = 0; k < UPT; ++k) {
+    const int u = ubase + threadIdx.x + k * BLOCK;
+    if (u < nunits) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) out[u * E + e] = acc[k][e];
+    }
+  }
+}
+
 // Stage 2: dgamma_j = sum over blocks b of partial[b][j], in a fixed order.
 // A 256-thread block covers kS2Cols columns: each thread owns CPT adjacent
 // columns (one 16-byte load per partial row when CPT == 4) and one of

@@ -11,8 +11,12 @@
 // lanes idle, half the lanes with 3 units each is used instead (at 32768 x
 // 5000 fp16, 625 units: 256 x 3 measured 7% faster than 512 x 2). Short rows pack BLOCK / TPR rows per
 // block. Rows that are not 16-byte aligned use 1-element units (up to 8 per
-// lane). Longer rows: one 256-thread block per row, parked in LDS when the row
-// fits the LDS budget, else re-read.
+// lane). Longer rows: one block per row, parked in LDS when the row fits the
+// device's per-workgroup LDS (160 KiB on gfx950), else re-read; 512 threads
+// for rows up to 32 KiB, 1024 above (measured at 128 MiB of bf16: 16384-
+// element rows 46 us with 512 threads vs 48 us with 256; 32768 and 65536
+// elements 48-50 us with 1024 threads and 64 / 128 KiB of LDS vs 61-63 us
+// re-reading).
 #pragma once
 
 #include "fwd_kernels.hpp"
@@ -34,8 +38,14 @@ template <class T, class G, bool VEC, int BLOCK, int UNROLL, bool FUSED, bool CA
 hipError_t run_fwd_long(const FwdArgs<T, G>& a, hipStream_t s) {
   int64_t blocks = a.M < kMaxGrid ? a.M : kMaxGrid;
   const size_t lds = CACHE ? static_cast<size_t>(a.N) * T::kSize : 0;
-  fwd_long_kernel<T, G, VEC, BLOCK, UNROLL, FUSED, CACHE>
-      <<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), lds, s>>>(a);
+  auto* kernel = fwd_long_kernel<T, G, VEC, BLOCK, UNROLL, FUSED, CACHE>;
+  if constexpr (CACHE) {
+    // Allow the largest row cache once; per-launch sizes stay below it.
+    static const hipError_t attr = allow_dynamic_lds(reinterpret_cast<const void*>(kernel),
+                                                     static_cast<size_t>(lds_row_budget()));
+    if (attr != hipSuccess) return attr;
+  }
+  kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -90,13 +100,15 @@ hipError_t fwd_typed(const FwdCall& c) {
     if (tpr <= 256) return run_fwd_reg<T, G, false, 256, 8, 256, FUSED>(a, s);
     return run_fwd_reg<T, G, false, 1024, 8, 1024, FUSED>(a, s);
   }
-  const bool cache = c.N * T::kSize <= kLdsRowBytes;
+  const int64_t row_bytes = c.N * T::kSize;
+  const bool cache = row_bytes <= lds_row_budget();
   if (vec) {
-    if (cache) return run_fwd_long<T, G, true, 256, 4, FUSED, true>(a, s);
-    return run_fwd_long<T, G, true, 256, 4, FUSED, false>(a, s);
+    if (!cache) return run_fwd_long<T, G, true, 1024, 4, FUSED, false>(a, s);
+    if (row_bytes <= 32 * 1024) return run_fwd_long<T, G, true, 512, 4, FUSED, true>(a, s);
+    return run_fwd_long<T, G, true, 1024, 4, FUSED, true>(a, s);
   }
-  if (cache) return run_fwd_long<T, G, false, 256, 8, FUSED, true>(a, s);
-  return run_fwd_long<T, G, false, 256, 8, FUSED, false>(a, s);
+  if (!cache) return run_fwd_long<T, G, false, 1024, 8, FUSED, false>(a, s);
+  return run_fwd_long<T, G, false, 1024, 8, FUSED, true>(a, s);
 }
 
 template <class T, class G>

@@ -14,11 +14,20 @@ constexpr int kDtF16 = 1;
 constexpr int kDtBF16 = 2;
 
 // Rows up to this many elements stay in registers; longer rows are parked in
-// LDS up to kLdsRowBytes per row (kept under the 64 KiB a workgroup can
-// always allocate, leaving room for the kernels' static LDS) and re-read from
-// global memory beyond that.
+// LDS when they fit the workgroup's LDS budget (lds_row_budget()) and are
+// re-read from global memory beyond that.
 constexpr int64_t kRegMaxN = 8192;
-constexpr int64_t kLdsRowBytes = 63 * 1024;
+// LDS kept free for the kernels' static arrays when sizing the row cache.
+constexpr int64_t kLdsReserve = 1024;
+
+// Bytes of dynamic LDS a workgroup may use on the current device for a row
+// cache (the device's per-workgroup limit minus kLdsReserve; 160 KiB on
+// gfx950). Queried once per device.
+int64_t lds_row_budget();
+
+// Raise a kernel's dynamic-LDS limit to `bytes` (needed above 64 KiB). The
+// result of the first call per kernel is cached by the caller.
+hipError_t allow_dynamic_lds(const void* kernel, size_t bytes);
 // Upper bound on launched blocks for grid-stride kernels.
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
 
@@ -40,18 +49,22 @@ hipError_t launch_fwd_f16(const FwdCall& c);
 hipError_t launch_fwd_bf16(const FwdCall& c);
 
 // Backward partition: block b owns rows [b * rows_per_block, ...). It depends
-// only on (M, N, dtype), which fixes the dgamma summation order.
+// only on (M, N, dtype), which fixes the dgamma summation order. The
+// workspace holds the fp32 partial rows [blocks, N] and, for rows longer than
+// kBwdOnChipN, the per-row dots [M] (double) of the two-pass long-row tier.
 struct BwdPlan {
-  bool supported;        // row fits the on-chip backward path
+  bool valid;
   int64_t rows_per_block;
   int64_t blocks;
+  size_t partial_bytes;    // offset of the row dots
   size_t workspace_bytes;
 };
 BwdPlan plan_bwd(int64_t M, int64_t N, int x_dtype);
 
-// Largest row the backward keeps on chip (elements), per element size.
-constexpr int64_t bwd_max_n(int esize) { return esize == 4 ? 16384 : 32768; }
 constexpr int64_t kBwdTargetBlocks = 256;
+// Rows up to this many elements may use the one-pass backward (registers);
+// longer rows use the two-pass long-row tier when they do not fit.
+constexpr int64_t kBwdOnChipN = 8192;
 
 struct BwdCall {
   const void* dy;

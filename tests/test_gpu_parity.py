@@ -20,7 +20,8 @@ PAIRS = [(O.F32, O.F32), (O.F16, O.F16), (O.F16, O.F32), (O.BF16, O.BF16), (O.BF
 PAIR_IDS = ["f32", "f16", "f16_gf32", "bf16", "bf16_gf32"]
 N_SWEEP = [1, 7, 8, 63, 64, 1000, 1024, 2047, 2048, 4096, 4999, 5000, 5001, 8191, 8192, 8193,
            12288, 16384, 32768]
-N_REREAD = {O.F32: 20000, O.F16: 40000, O.BF16: 40000}   # rows beyond the 64 KiB LDS cache
+N_LDS = {O.F32: 20000, O.F16: 40000, O.BF16: 40000}      # 80 KB rows: LDS-cached, 1024 threads
+N_REREAD = {O.F32: 45000, O.F16: 90000, O.BF16: 90000}   # 180 KB rows: beyond 160 KiB of LDS
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "exact_rows.txt")
 
 
@@ -90,8 +91,11 @@ def test_fwd_sweep(N, pair):
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
-def test_fwd_reread_path(pair):
+def test_fwd_long_rows(pair):
+    run_fwd(5, N_LDS[pair[0]], *pair, seed=30)
     run_fwd(5, N_REREAD[pair[0]], *pair, seed=31)
+    run_fwd(3, N_LDS[pair[0]] + 1, *pair, seed=32, misalign=1)     # scalar units, LDS
+    run_fwd(3, N_REREAD[pair[0]] + 3, *pair, seed=33, misalign=1)  # scalar units, re-read
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 64, 255, 4097])
@@ -216,7 +220,8 @@ def test_fused_sweep(N, pair):
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
-def test_fused_reread_path(pair):
+def test_fused_long_rows(pair):
+    run_fused(3, N_LDS[pair[0]], *pair, seed=40, want_rstd=True)
     run_fused(3, N_REREAD[pair[0]], *pair, seed=41, want_rstd=True)
 
 
@@ -254,12 +259,19 @@ def run_bwd(M, N, xdt, gdt, seed=13, misalign=0, alias=None, gpu_rstd=False, eps
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
-@pytest.mark.parametrize("N", [1, 7, 8, 64, 1000, 2047, 4096, 5000, 8192, 8193, 16384, 32768])
+@pytest.mark.parametrize("N", [1, 7, 8, 64, 1000, 2047, 4096, 5000, 8192, 8193, 16384, 16392,
+                               32768, 40000])
 def test_bwd_sweep(N, pair):
-    if N > (16384 if pair[0] == O.F32 else 32768):
-        pytest.skip("beyond the on-chip backward row limit for this dtype")
+    # N > 16384 (bf16/fp16) or > 8192 (fp32) takes the two-pass long-row tier.
     run_bwd(3, N, *pair, seed=400 + N)
     run_bwd(70, N, *pair, seed=500 + N)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_bwd_long_rows_misaligned_and_many_rows(pair):
+    run_bwd(5, 9000, *pair, seed=601, misalign=1)   # scalar long-row tier
+    run_bwd(600, 20000, *pair, seed=602)            # several rows per partition block
+    run_bwd(4, 100000, *pair, seed=603, alias="dy")
 
 
 @pytest.mark.parametrize("M", [1, 255, 256, 257, 1000, 5000])
