@@ -116,11 +116,10 @@ hipError_t allow_dynamic_lds(const void* kernel, size_t bytes) {
 }
 
 BwdPlan plan_bwd(int64_t M, int64_t N, int x_dtype) {
-  BwdPlan p{false, 0, 0, 0, 0};
+  BwdPlan p{false, 0, 0, 0};
   if (!valid_dtype(x_dtype) || M <= 0 || N <= 0) return p;
   p.valid = true;
-  p.rows_per_block = ceil_div(M, kBwdTargetBlocks);
-  p.blocks = ceil_div(M, p.rows_per_block);
+  p.blocks = M < kBwdTargetBlocks ? M : kBwdTargetBlocks;
   auto round256 = [](uint64_t b) { return (b + 255u) & ~static_cast<uint64_t>(255u); };
   // One fp32 partial row per block, then (long rows) one double per row.
   p.partial_bytes = static_cast<size_t>(

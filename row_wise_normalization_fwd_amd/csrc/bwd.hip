@@ -6,9 +6,8 @@
 // take the two-pass long-row tier (row dots, then 2-D tiles). When a block owns at least two rows,
 // it runs 1024 threads, i.e. 1024 / TPR row groups whose dgamma partials are
 // combined through LDS: at 8192 x 8192 bf16 this (two 512-lane groups per
-// block, one block per CU) measured fastest among 1, 2 and 4 groups, 256 to
-// 1024 lanes per row, 256 / 384 / 512 blocks and with or without prefetching
-// the next row. Rows that are not 16-byte aligned use 1-element units.
+// block, one block per CU, next-row prefetch) measured fastest among 1, 2 and
+// 4 groups, 256 to 1024 lanes per row and 256 / 384 / 512 blocks. Rows that are not 16-byte aligned use 1-element units.
 #include "bwd_kernels.hpp"
 #include "launch.hpp"
 
@@ -19,7 +18,7 @@ hipError_t run_stage1(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s) {
   constexpr int RG = BLOCK / TPR;
   constexpr int E = Unit<T, VEC>::E;
   constexpr size_t kLds = RG > 1 ? static_cast<size_t>(BLOCK) * UPT * E * sizeof(float) : 0;
-  auto* kernel = bwd_stage1_kernel<T, G, VEC, TPR, UPT, BLOCK, false>;
+  auto* kernel = bwd_stage1_kernel<T, G, VEC, TPR, UPT, BLOCK>;
   if constexpr (kLds > 48 * 1024) {
     // Raise the dynamic LDS limit once per instantiation (gfx950 has 160 KiB).
     static const hipError_t attr = hipFuncSetAttribute(
@@ -32,11 +31,11 @@ hipError_t run_stage1(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s) {
 }
 
 // Lanes per row TPR with UPT units each; a full 1024-thread block of row
-// groups when the block owns at least two rows.
+// groups when each block owns at least two rows.
 template <class T, class G, bool VEC, int TPR, int UPT>
 hipError_t run_stage1_rows(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s) {
   if constexpr (TPR < 1024) {
-    if (a.rows_per_block >= 2) return run_stage1<T, G, VEC, TPR, UPT, 1024>(a, blocks, s);
+    if (a.M >= 2 * a.nblk) return run_stage1<T, G, VEC, TPR, UPT, 1024>(a, blocks, s);
   }
   return run_stage1<T, G, VEC, TPR, UPT, (TPR > 256 ? TPR : 256)>(a, blocks, s);
 }
@@ -101,7 +100,7 @@ hipError_t bwd_typed(const BwdCall& c) {
   a.partial = static_cast<float*>(c.workspace);
   a.M = c.M;
   a.N = static_cast<int>(c.N);
-  a.rows_per_block = c.plan.rows_per_block;
+  a.nblk = c.plan.blocks;
   const bool vec = (c.N * T::kSize) % 16 == 0 && aligned16(c.dy) && aligned16(c.x) &&
                    aligned16(c.dx) && aligned16(c.gamma);
   hipError_t e = stage1_typed<T, G>(a, vec, c.plan.blocks, c.stream);
@@ -113,15 +112,18 @@ hipError_t bwd_typed(const BwdCall& c) {
   }
   if (e != hipSuccess) return e;
   // Partial rows are 16-byte aligned when N % 4 == 0 (workspace is).
-  constexpr int kGroups = kS2Threads / kS2Slices;
+  constexpr int kSlices = 16;
+  constexpr int kGroups = kS2Threads / kSlices;
   if (c.N % 4 == 0) {
     const int64_t blocks = ceil_div(c.N, 4 * kGroups);
-    bwd_stage2_kernel<4><<<dim3(static_cast<unsigned>(blocks)), dim3(kS2Threads), 0, c.stream>>>(
-        a.partial, c.dgamma, static_cast<int>(c.plan.blocks), static_cast<int>(c.N));
+    bwd_stage2_kernel<4, kSlices>
+        <<<dim3(static_cast<unsigned>(blocks)), dim3(kS2Threads), 0, c.stream>>>(
+            a.partial, c.dgamma, static_cast<int>(c.plan.blocks), static_cast<int>(c.N));
   } else {
     const int64_t blocks = ceil_div(c.N, kGroups);
-    bwd_stage2_kernel<1><<<dim3(static_cast<unsigned>(blocks)), dim3(kS2Threads), 0, c.stream>>>(
-        a.partial, c.dgamma, static_cast<int>(c.plan.blocks), static_cast<int>(c.N));
+    bwd_stage2_kernel<1, kSlices>
+        <<<dim3(static_cast<unsigned>(blocks)), dim3(kS2Threads), 0, c.stream>>>(
+            a.partial, c.dgamma, static_cast<int>(c.plan.blocks), static_cast<int>(c.N));
   }
   return hipGetLastError();
 }

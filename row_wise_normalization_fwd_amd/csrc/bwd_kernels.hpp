@@ -9,12 +9,13 @@
 //     dx_ij    = rho_i (gamma_j dy_ij - x_ij rho_i^2 c_i)
 //     dgamma_j = sum_i dy_ij x_ij rho_i
 // The weight gradient is reduced in two stages without atomics: stage 1 gives
-// each block a fixed, contiguous range of rows and writes one fp32 partial row
-// per block; stage 2 sums the partials of each column in a fixed order. The
-// partition depends only on (M, N, dtype), so results are bit-reproducible.
+// each of G blocks a fixed set of rows -- block b owns rows b, b + G, b + 2G,
+// ..., so at any moment all blocks work inside one compact window of rows
+// (measured 10% faster than contiguous row ranges at 8192 x 8192 bf16) -- and
+// writes one fp32 partial row per block; stage 2 sums the partials of each
+// column in a fixed order. G depends only on M, so results are bit-
+// reproducible.
 #pragma once
-
-#include <type_traits>
 
 #include "device.hpp"
 
@@ -27,32 +28,33 @@ struct BwdArgs {
   const float* rstd;
   const typename G::S* gamma;
   typename T::S* dx;
-  float* partial;          // [num_blocks, N] fp32
+  float* partial;  // [G, N] fp32, one row per partition block
   int64_t M;
   int N;
-  int64_t rows_per_block;  // contiguous rows owned by each block
+  int64_t nblk;    // partition blocks G: block b owns rows b + G * s
 };
 
-// dy * gamma * x, accumulated in double. For bf16 operands the fp32 product is
-// exact (8 + 8 + 8 significant bits), so one conversion suffices; otherwise
-// the product is formed in double.
-template <class T, class G>
-__device__ __forceinline__ double dot_term(float dyv, float g, float xv) {
-  if constexpr (std::is_same_v<T, BF16> && std::is_same_v<G, BF16>) {
-    return static_cast<double>(dyv * g * xv);
-  } else {
-    return static_cast<double>(dyv) * static_cast<double>(g) * static_cast<double>(xv);
-  }
+// The row dot sum_j dy gamma x is formed per 16-byte unit in fp32 (one FMA
+// per element; for bf16 every product is exact, otherwise each step rounds
+// once) and the unit sums are accumulated in double. The fp32 error of a
+// unit is at most E * 2^-24 of the unit's sum of |dy gamma x|, far below the
+// resolution dx needs.
+template <int E>
+__device__ __forceinline__ float unit_dot(const float* dyv, const float* g, const float* xv) {
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) s = __builtin_fmaf(g[e] * dyv[e], xv[e], s);
+  return s;
 }
 
-// Stage 1. A block of BLOCK threads holds RG = BLOCK / TPR row groups; group
-// `grp` takes rows base + grp for base = r0, r0 + RG, ... inside the block's
-// range [r0, r1). Each lane keeps gamma and its columns' dgamma partial sums in
-// registers. With PF the x and dy units of a group's next row are loaded
-// before the current row is reduced, so loads stay in flight across rows.
-// With RG > 1 the groups' partials are combined through LDS in group order
-// before the block writes its partial row.
-template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool PF>
+// Stage 1. A block of BLOCK threads holds RG = BLOCK / TPR row groups; block
+// b's rows are b + G * s, and group `grp` takes s = s0 + grp for s0 = 0, RG,
+// 2 RG, ... Each lane keeps gamma and its columns' dgamma partial sums in
+// registers. The x and dy units of a group's next row are loaded before the
+// current row is reduced, so loads stay in flight across rows. With RG > 1 the
+// groups' partials are combined through LDS in group order before the block
+// writes its partial row.
+template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   using U = Unit<T, VEC>;
   using Raw = typename U::Raw;
@@ -67,8 +69,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   const int nunits = a.N / E;
   const int grp = threadIdx.x / TPR;
   const int lane = threadIdx.x % TPR;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * a.rows_per_block;
-  const int64_t r1 = r0 + a.rows_per_block < a.M ? r0 + a.rows_per_block : a.M;
+  const int64_t b = blockIdx.x;
 
   float gam[UPT][E];
   float acc[UPT][E];
@@ -85,62 +86,83 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
     for (int e = 0; e < E; ++e) acc[k][e] = 0.0f;
   }
 
-  // x and dy units of `row` (zeros outside the block's rows).
-  auto load_row = [&](int64_t row, Raw* rx, Raw* rdy) {
-    const bool valid = row < r1;
-    const int64_t off = row * a.N;
+  // Rows handled in one iteration: row0 + nblk * g for the RG groups g. In
+  // the vector case the iteration's operands are reached through buffer
+  // resources based at row0 and ending at the array's end; masked units get an
+  // out-of-range offset, so loads and stores need no branches and the
+  // compiler waits only for the older loads rather than draining the
+  // prefetch and the previous row's stores. (The offsets span at most
+  // nblk * RG rows of at most TPR * UPT units, a few MiB.)
+  const int64_t row_bytes = static_cast<int64_t>(a.N) * T::kSize;
+  auto unit_offset = [&](int64_t row0, int g, int k) -> uint32_t {
+    const int u = lane + k * TPR;
+    const bool ok = row0 + a.nblk * g < a.M && u < nunits;
+    return ok ? static_cast<uint32_t>(a.nblk * g * row_bytes + static_cast<int64_t>(u) * 16)
+              : kBufOutOfRange;
+  };
+  auto span_bytes = [&](int64_t row0) -> uint32_t {
+    const int64_t rest = (a.M - row0) * row_bytes;
+    return static_cast<uint32_t>(rest < 0x7fffffff ? rest : 0x7fffffff);
+  };
+
+  // x and dy units of row row0 + nblk * grp (zeros past the last row or unit).
+  auto load_row = [&](int64_t row0, Raw* rx, Raw* rdy) {
+    if constexpr (VEC) {
+      const bool any = row0 < a.M;
+      const uint32_t n = any ? span_bytes(row0) : 0u;
+      const auto rsx = make_rsrc(a.x + (any ? row0 : 0) * a.N, n);
+      const auto rsd = make_rsrc(a.dy + (any ? row0 : 0) * a.N, n);
 #pragma unroll
-    for (int k = 0; k < UPT; ++k) {
-      const int u = lane + k * TPR;
-      const bool ok = valid && u < nunits;
-      rx[k] = ok ? U::load_nt(a.x + off + u * E) : U::zero();
-      rdy[k] = ok ? U::load_nt(a.dy + off + u * E) : U::zero();
+      for (int k = 0; k < UPT; ++k) {
+        const uint32_t o = unit_offset(row0, grp, k);
+        rx[k] = buf_load16_nt(rsx, o);
+        rdy[k] = buf_load16_nt(rsd, o);
+      }
+    } else {
+      const int64_t row = row0 + a.nblk * grp;
+      const bool valid = row < a.M;
+      const int64_t off = (valid ? row : a.M - 1) * a.N;
+#pragma unroll
+      for (int k = 0; k < UPT; ++k) {
+        const int u = lane + k * TPR;
+        const bool ok = valid && u < nunits;
+        const int uc = u < nunits ? u : nunits - 1;
+        const Raw vx = U::load_nt(a.x + off + uc * E);
+        const Raw vdy = U::load_nt(a.dy + off + uc * E);
+        rx[k] = ok ? vx : U::zero();
+        rdy[k] = ok ? vdy : U::zero();
+      }
     }
   };
 
-  Raw nx[UPT], ndy[UPT];
-  if constexpr (PF) load_row(r0 + grp, nx, ndy);
-
+  // One row per group and call: consume (cx, cdy), prefetch the group's next
+  // row into (nx, ndy). The loop below alternates two register sets, so the
+  // prefetched data is first touched inside the next call, after that call
+  // has issued its own prefetch.
   int parity = 0;
-  for (int64_t base = r0; base < r1; base += RG) {  // uniform over the block
-    const int64_t row = base + grp;
-    const bool valid = row < r1;
+  auto step = [&](int64_t row0, Raw* cx, Raw* cdy, Raw* nx, Raw* ndy) {
+    const int64_t row = row0 + a.nblk * grp;
+    const bool valid = row < a.M;
     const int64_t off = row * a.N;
+    const float rho_ld = a.rstd[valid ? row : a.M - 1];
+    const float rho = valid ? rho_ld : 0.0f;
+    load_row(row0 + a.nblk * RG, nx, ndy);
 
-    Raw rx[UPT], rdy[UPT];
-    if constexpr (PF) {
-#pragma unroll
-      for (int k = 0; k < UPT; ++k) {
-        rx[k] = nx[k];
-        rdy[k] = ndy[k];
-      }
-      load_row(row + RG, nx, ndy);
-    } else {
-      load_row(row, rx, rdy);
-    }
-    const float rho = valid ? a.rstd[row] : 0.0f;
-
-    double part[UPT];
+    double dot = 0.0;
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       float xv[E], dyv[E];
-      U::widen(rx[k], xv);
-      U::widen(rdy[k], dyv);
-      double s = 0.0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) s = s + dot_term<T, G>(dyv[e], gam[k][e], xv[e]);
-      part[k] = s;
+      U::widen(cx[k], xv);
+      U::widen(cdy[k], dyv);
+      dot = dot + static_cast<double>(unit_dot<E>(dyv, gam[k], xv));
     }
     // Re-widen x and dy after the reduction rather than holding the fp32
     // copies across it: fewer live VGPRs, more row groups per CU.
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
-      opaque(rx[k]);
-      opaque(rdy[k]);
+      opaque(cx[k]);
+      opaque(cdy[k]);
     }
-    double dot = part[0];
-#pragma unroll
-    for (int k = 1; k < UPT; ++k) dot = dot + part[k];
     dot = row_sum<TPR, BLOCK>(dot, red, parity);
     parity ^= 1;
 
@@ -150,15 +172,30 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
     for (int k = 0; k < UPT; ++k) {
       const int u = lane + k * TPR;
       float xv[E], dyv[E], o[E];
-      U::widen(rx[k], xv);
-      U::widen(rdy[k], dyv);
+      U::widen(cx[k], xv);
+      U::widen(cdy[k], dyv);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         o[e] = rho * __builtin_fmaf(-xv[e], kcoef, gam[k][e] * dyv[e]);
         acc[k][e] = __builtin_fmaf(dyv[e] * xv[e], rho, acc[k][e]);
       }
-      if (valid && u < nunits) U::store_nt(a.dx + off + u * E, U::narrow(o));
+      if constexpr (VEC) {
+        const auto rsdx = make_rsrc(a.dx + row0 * a.N, span_bytes(row0));
+        buf_store16_nt(U::narrow(o), rsdx, unit_offset(row0, grp, k));
+      } else {
+        if (valid && u < nunits) U::store_nt(a.dx + off + u * E, U::narrow(o));
+      }
     }
+  };
+
+  Raw ax[UPT], ady[UPT], bx[UPT], bdy[UPT];
+  load_row(b, ax, ady);
+  // Trip counts are uniform over the block, so every thread reaches every
+  // reduction.
+  for (int64_t s0 = 0; b + a.nblk * s0 < a.M; s0 += 2 * RG) {
+    step(b + a.nblk * s0, ax, ady, bx, bdy);
+    if (b + a.nblk * (s0 + RG) >= a.M) break;
+    step(b + a.nblk * (s0 + RG), bx, bdy, ax, ady);
   }
 
   float* out = a.partial + static_cast<int64_t>(blockIdx.x) * a.N;
@@ -221,10 +258,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_rowdot_kernel(BwdArgs<T, G> a, doub
           U::widen(rx[k], xv);
           U::widen(rdy[k], dyv);
           load_gamma<G, E, VEC>(a.gamma, u * E, g);
-          double s = 0.0;
-#pragma unroll
-          for (int e = 0; e < E; ++e) s = s + dot_term<T, G>(dyv[e], g[e], xv[e]);
-          dot = dot + s;
+          dot = dot + static_cast<double>(unit_dot<E>(dyv, g, xv));
         }
       }
     }
@@ -235,7 +269,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_rowdot_kernel(BwdArgs<T, G> a, doub
 }
 
 // Pass B: block (bx, by) covers columns [bx * COLS, (bx + 1) * COLS) of rows
-// [by * rows_per_block, ...), COLS = BLOCK * UPT * E. Each lane keeps gamma and
+// by, by + G, by + 2G, ..., COLS = BLOCK * UPT * E. Each lane keeps gamma and
 // the dgamma partial sums of its columns in registers over the block's rows
 // (in increasing row order) and writes them to partial[by][...]; dx uses the
 // row dots from pass A.
@@ -246,8 +280,6 @@ __global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const 
   constexpr int E = U::E;
   const int nunits = a.N / E;
   const int ubase = blockIdx.x * (BLOCK * UPT);
-  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * a.rows_per_block;
-  const int64_t r1 = r0 + a.rows_per_block < a.M ? r0 + a.rows_per_block : a.M;
   float gam[UPT][E], acc[UPT][E];
 #pragma unroll
   for (int k = 0; k < UPT; ++k) {
@@ -261,7 +293,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const 
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[k][e] = 0.0f;
   }
-  for (int64_t row = r0; row < r1; ++row) {
+  for (int64_t row = blockIdx.y; row < a.M; row += a.nblk) {
     const int64_t off = row * a.N;
     Raw rx[UPT], rdy[UPT];
 #pragma unroll
@@ -299,19 +331,18 @@ __global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const 
 }
 
 // Stage 2: dgamma_j = sum over blocks b of partial[b][j], in a fixed order.
-// A 256-thread block covers kS2Cols columns: each thread owns CPT adjacent
-// columns (one 16-byte load per partial row when CPT == 4) and one of
-// kS2Slices interleaved slices of partial rows (b = slice, slice + kS2Slices,
-// ...), summed in increasing b in double; the slice sums are then added in
-// slice order through LDS and rounded to fp32 once.
+// A 256-thread block covers 256 / SLICES column groups of CPT adjacent columns
+// (one 16-byte load per partial row when CPT == 4); each thread owns one
+// group and one of SLICES interleaved slices of partial rows (b = slice,
+// slice + SLICES, ...), summed in increasing b in double; the slice sums are
+// then added in slice order through LDS and rounded to fp32 once.
 constexpr int kS2Threads = 256;
-constexpr int kS2Slices = 16;
 
-template <int CPT>
+template <int CPT, int SLICES>
 __global__ __launch_bounds__(kS2Threads) void bwd_stage2_kernel(
     const float* __restrict__ partial, float* __restrict__ dgamma, int nblocks, int N) {
-  constexpr int kGroups = kS2Threads / kS2Slices;  // column groups per block
-  __shared__ double red[kS2Slices][kGroups][CPT];
+  constexpr int kGroups = kS2Threads / SLICES;  // column groups per block
+  __shared__ double red[SLICES][kGroups][CPT];
   const int grp = threadIdx.x % kGroups;
   const int slice = threadIdx.x / kGroups;
   const int col0 = (blockIdx.x * kGroups + grp) * CPT;
@@ -320,7 +351,7 @@ __global__ __launch_bounds__(kS2Threads) void bwd_stage2_kernel(
   for (int c = 0; c < CPT; ++c) s[c] = 0.0;
   if (col0 < N) {  // with CPT == 4, N % 4 == 0, so all four columns exist
 #pragma unroll 4
-    for (int b = slice; b < nblocks; b += kS2Slices) {
+    for (int b = slice; b < nblocks; b += SLICES) {
       const float* p = partial + static_cast<int64_t>(b) * N + col0;
       if constexpr (CPT == 4) {
         const float4 v = *reinterpret_cast<const float4*>(p);
@@ -340,7 +371,7 @@ __global__ __launch_bounds__(kS2Threads) void bwd_stage2_kernel(
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       double t = red[0][grp][c];
-      for (int q = 1; q < kS2Slices; ++q) t = t + red[q][grp][c];
+      for (int q = 1; q < SLICES; ++q) t = t + red[q][grp][c];
       dgamma[col0 + c] = static_cast<float>(t);
     }
   }

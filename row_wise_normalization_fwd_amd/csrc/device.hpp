@@ -119,6 +119,30 @@ struct Unit<T, false> {
   __device__ static Raw narrow(const float* f) { return T::narrow(f[0]); }
 };
 
+// ------------------------------------------------------------ buffer access
+//
+// 16-byte loads and stores through a raw buffer resource (base, size in
+// bytes): accesses at or beyond the size read 0 and drop the write, so masked
+// accesses need no branches around them (branches make the compiler wait for
+// all outstanding memory operations instead of just the older ones). The base
+// must be uniform across the wave. The 4th descriptor word selects 32-bit
+// data for the gfx9 family; aux bit 1 is the non-temporal cache policy.
+constexpr uint32_t kBufDword3 = 0x00020000u;
+constexpr int kBufNT = 2;
+constexpr uint32_t kBufOutOfRange = 0x80000000u;  // offset beyond any size used
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, kBufDword3);
+}
+
+__device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufNT);
+}
+
+__device__ __forceinline__ void buf_store16_nt(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kBufNT);
+}
+
 // Make the compiler treat v as modified here, so values derived from it
 // before this point are recomputed afterwards instead of being kept live
 // (trades a few ALU ops for registers). Emits no instruction.

@@ -48,14 +48,14 @@ hipError_t launch_fwd_f32(const FwdCall& c);
 hipError_t launch_fwd_f16(const FwdCall& c);
 hipError_t launch_fwd_bf16(const FwdCall& c);
 
-// Backward partition: block b owns rows [b * rows_per_block, ...). It depends
-// only on (M, N, dtype), which fixes the dgamma summation order. The
-// workspace holds the fp32 partial rows [blocks, N] and, for rows longer than
-// kBwdOnChipN, the per-row dots [M] (double) of the two-pass long-row tier.
+// Backward partition: G = min(M, kBwdTargetBlocks) blocks, block b owning
+// rows b, b + G, b + 2G, ... It depends only on M, which fixes the dgamma
+// summation order. The workspace holds the fp32 partial rows [G, N] and, for
+// rows longer than kBwdOnChipN, the per-row dots [M] (double) of the
+// two-pass long-row tier.
 struct BwdPlan {
   bool valid;
-  int64_t rows_per_block;
-  int64_t blocks;
+  int64_t blocks;  // G
   size_t partial_bytes;    // offset of the row dots
   size_t workspace_bytes;
 };

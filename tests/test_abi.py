@@ -109,16 +109,18 @@ def bwd(dy=A, x=B, rstd=C, g=D, dx=E, dg=F, ws=G, wsb=None, M=64, N=256, xd=BF16
 
 
 def test_workspace_size():
-    # One fp32 partial row per stage-1 block; at most 256 blocks.
+    # One fp32 partial row per partition block, min(M, 256) blocks, rounded
+    # up to 256 bytes.
     assert R.rmsnorm_bwd_workspace_size(8192, 8192, BF16) == 256 * 8192 * 4
     assert R.rmsnorm_bwd_workspace_size(3, 10, F32) == 256          # 3*10*4 = 120 -> 256
-    assert R.rmsnorm_bwd_workspace_size(1000, 64, F16) == 250 * 64 * 4
+    assert R.rmsnorm_bwd_workspace_size(1000, 64, F16) == 256 * 64 * 4
+    assert R.rmsnorm_bwd_workspace_size(200, 64, F16) == 200 * 64 * 4
     assert R.rmsnorm_bwd_workspace_size(0, 64, F16) == 0
     assert R.rmsnorm_bwd_workspace_size(10, 0, F16) == 0
     assert R.rmsnorm_bwd_workspace_size(10, 10, 7) == 0
     # Rows longer than 8192 also hold one double per row (row dots), each
     # region rounded up to 256 bytes.
-    assert R.rmsnorm_bwd_workspace_size(1000, 10000, BF16) == 10_000_128 + 8192
+    assert R.rmsnorm_bwd_workspace_size(1000, 10000, BF16) == 256 * 10000 * 4 + 8192
     assert R.rmsnorm_bwd_workspace_size(3, 8193, F32) == 98_560 + 256   # 98,316 -> 98,560
 
 
