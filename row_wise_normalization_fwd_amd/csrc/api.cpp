@@ -110,6 +110,22 @@ int64_t lds_row_budget() {
   return v;
 }
 
+int64_t device_cus() {
+  static std::atomic<int64_t> cache[64];  // per device; 0 = not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int64_t v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    v = cus;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 hipError_t allow_dynamic_lds(const void* kernel, size_t bytes) {
   return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                              static_cast<int>(bytes));

@@ -11,7 +11,10 @@
 // lanes idle, half the lanes with 3 units each is used instead (at 32768 x
 // 5000 fp16, 625 units: 256 x 3 measured 7% faster than 512 x 2). Short rows pack BLOCK / TPR rows per
 // block. Rows that are not 16-byte aligned use 1-element units (up to 8 per
-// lane). Longer rows: one block per row, parked in LDS when the row fits the
+// lane). Non-fused 16-bit rows of 769 to 1024 units (N in (6144, 8192]) use
+// the persistent fwd_pp_kernel instead (4096 x 8192 bf16: 22.0-22.6 us vs
+// 23.7-24.0 us; it did not help the fused add or 625-unit rows). Longer rows:
+// one block per row, parked in LDS when the row fits the
 // device's per-workgroup LDS (160 KiB on gfx950), else re-read; 512 threads
 // for rows up to 32 KiB, 1024 above (measured at 128 MiB of bf16: 16384-
 // element rows 46 us with 512 threads vs 48 us with 256; 32768 and 65536
@@ -30,6 +33,20 @@ hipError_t run_fwd_reg(const FwdArgs<T, G>& a, hipStream_t s) {
   int64_t blocks = ceil_div(a.M, RPB);
   if (blocks > kMaxGrid) blocks = kMaxGrid;
   fwd_reg_kernel<T, G, VEC, TPR, UPT, BLOCK, FUSED>
+      <<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <class T, class G, int TPR, int UPT, int BLOCK, bool FUSED>
+hipError_t run_fwd_pp(const FwdArgs<T, G>& a, hipStream_t s) {
+  // Two blocks per CU's worth of grid: at 4096 x 8192 bf16 every block then
+  // runs exactly two iterations (one prefetch), measured best among 256-1024
+  // blocks.
+  constexpr int RG = BLOCK / TPR;
+  int64_t blocks = 2 * device_cus();
+  const int64_t groups = ceil_div(a.M, RG);
+  if (blocks > groups) blocks = groups;
+  fwd_pp_kernel<T, G, TPR, UPT, BLOCK, FUSED>
       <<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), 0, s>>>(a);
   return hipGetLastError();
 }
@@ -69,6 +86,11 @@ hipError_t fwd_typed(const FwdCall& c) {
       constexpr int E = 16 / T::kSize;
       const int64_t units = c.N / E;
       if (units > 1024) return run_fwd_reg<T, G, true, 512, 4, 512, FUSED>(a, s);
+      if constexpr (T::kSize == 2 && !FUSED) {
+        // 16-bit rows of 769..1024 units: persistent kernel, four 256-lane
+        // row groups per block with next-row prefetch.
+        if (units > 768) return run_fwd_pp<T, G, 256, 4, 1024, FUSED>(a, s);
+      }
       const int64_t tpr2 = next_pow2(ceil_div(units, 2));
       if (tpr2 >= 8 && 3 * units < 4 * tpr2 && units <= 3 * (tpr2 / 2)) {
         switch (tpr2 / 2) {  // 3 units on half the lanes

@@ -132,6 +132,135 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
   }
 }
 
+// Persistent register path for 16-byte-aligned rows. The grid has one block
+// per CU (or a few); block b of G holds RG = BLOCK / TPR row groups and works
+// on rows b + G * (RG * t + g) for t = 0, 1, ..., group g -- so at any moment
+// all blocks are inside one compact window of rows. Two register sets
+// alternate between iterations: the next iteration's loads are issued before
+// this one's reduction and stores. Loads and stores go through buffer
+// resources with out-of-range offsets for masked units, so there are no
+// branches around them and the compiler waits only for the older loads.
+// Row results do not depend on G (each row's arithmetic is the same for any
+// grid), only on TPR and UPT.
+template <class T, class G, int TPR, int UPT, int BLOCK, bool FUSED>
+__global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
+  using U = Unit<T, true>;
+  using Raw = u32x4;
+  constexpr int E = U::E;
+  constexpr int RG = BLOCK / TPR;
+  constexpr int GW = E * G::kSize / 16;  // 16-byte words of gamma per unit (1 or 2)
+  static_assert(BLOCK % TPR == 0 && BLOCK % kWave == 0, "block shape");
+  __shared__ float red[2 * (BLOCK / kWave)];
+
+  const int nunits = a.N / E;
+  const int grp = threadIdx.x / TPR;
+  const int lane = threadIdx.x % TPR;
+  const int64_t nblk = gridDim.x;
+  const int64_t b = blockIdx.x;
+  const int64_t row_bytes = static_cast<int64_t>(a.N) * T::kSize;
+
+  // Gamma stays packed in registers and is widened where it is used.
+  u32x4 graw[UPT][GW];
+#pragma unroll
+  for (int k = 0; k < UPT; ++k) {
+    const int u = lane + k * TPR;
+    const typename G::S* gp = a.gamma + (u < nunits ? u : 0) * E;
+#pragma unroll
+    for (int w = 0; w < GW; ++w) graw[k][w] = *reinterpret_cast<const u32x4*>(gp + w * (16 / G::kSize));
+  }
+
+  // Byte offset of unit k of this group's row in the iteration starting at
+  // row0, or an out-of-range offset if the row or the unit does not exist.
+  auto unit_offset = [&](int64_t row0, int k) -> uint32_t {
+    const int u = lane + k * TPR;
+    const bool ok = row0 + nblk * grp < a.M && u < nunits;
+    return ok ? static_cast<uint32_t>(nblk * grp * row_bytes + static_cast<int64_t>(u) * 16)
+              : kBufOutOfRange;
+  };
+  // Bytes from row0 to the end of the array (clipped; offsets used are far
+  // smaller: nblk * RG rows of at most TPR * UPT units).
+  auto span_bytes = [&](int64_t row0) -> uint32_t {
+    const int64_t rest = row0 < a.M ? (a.M - row0) * row_bytes : 0;
+    return static_cast<uint32_t>(rest < 0x7fffffff ? rest : 0x7fffffff);
+  };
+  auto load_rows = [&](int64_t row0, Raw* rx, Raw* rr) {
+    const int64_t base = (row0 < a.M ? row0 : 0) * a.N;
+    const uint32_t n = span_bytes(row0);
+    const auto rsx = make_rsrc(a.x + base, n);
+    [[maybe_unused]] __amdgpu_buffer_rsrc_t rsr;
+    if constexpr (FUSED) rsr = make_rsrc(a.residual + base, n);
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const uint32_t o = unit_offset(row0, k);
+      rx[k] = buf_load16_nt(rsx, o);
+      if constexpr (FUSED) rr[k] = buf_load16_nt(rsr, o);
+    }
+  };
+
+  int parity = 0;
+  auto step = [&](int64_t row0, Raw* cx, Raw* cr, Raw* nx, Raw* nr) {
+    load_rows(row0 + nblk * RG, nx, nr);
+    const int64_t row = row0 + nblk * grp;
+    const uint32_t n = span_bytes(row0);
+    float part[UPT];
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      float v[E];
+      prepare_unit<T, U, FUSED>(cx[k], cr[k], v);
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) s = __builtin_fmaf(v[e], v[e], s);
+      part[k] = s;
+    }
+    if constexpr (FUSED) {  // h, rounded, back over the residual
+      const auto rsr = make_rsrc(a.residual + row0 * a.N, n);
+#pragma unroll
+      for (int k = 0; k < UPT; ++k) buf_store16_nt(cx[k], rsr, unit_offset(row0, k));
+    }
+    float ss = part[0];
+#pragma unroll
+    for (int k = 1; k < UPT; ++k) ss = ss + part[k];
+    // Widen again after the reduction instead of keeping fp32 copies live.
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) opaque(cx[k]);
+    ss = row_sum<TPR, BLOCK>(ss, red, parity);
+    parity ^= 1;
+    const float rs = 1.0f / __builtin_sqrtf(ss / static_cast<float>(a.N) + a.eps);
+    const auto rsy = make_rsrc(a.y + row0 * a.N, n);
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      float v[E], g[E], o[E];
+      U::widen(cx[k], v);
+#pragma unroll
+      for (int w = 0; w < GW; ++w)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) G::widen_word(graw[k][w][q], g + w * (16 / G::kSize) + q * G::kPerWord);
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
+      buf_store16_nt(U::narrow(o), rsy, unit_offset(row0, k));
+    }
+    if (a.rstd != nullptr) {
+      // One lane per row writes rstd, through a buffer like the rest.
+      const int64_t rest = (a.M - row0) * 4;
+      const auto rsr = make_rsrc(a.rstd + row0, static_cast<uint32_t>(rest < 0x7fffffff ? rest : 0x7fffffff));
+      const bool mine = lane == 0 && row < a.M;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rs), rsr,
+                                            mine ? static_cast<uint32_t>(nblk * grp * 4) : kBufOutOfRange,
+                                            0, 0);
+    }
+  };
+
+  Raw ax[UPT], ar[UPT], bx[UPT], br[UPT];
+  load_rows(b, ax, ar);
+  // Trip counts are uniform over the block, so every thread reaches every
+  // reduction.
+  for (int64_t s0 = 0; b + nblk * s0 < a.M; s0 += 2 * RG) {
+    step(b + nblk * s0, ax, ar, bx, br);
+    if (b + nblk * (s0 + RG) >= a.M) break;
+    step(b + nblk * (s0 + RG), bx, br, ax, ar);
+  }
+}
+
 template <class T, class G, bool VEC, int BLOCK, int UNROLL, bool FUSED, bool CACHE>
 __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
   using U = Unit<T, VEC>;

@@ -25,6 +25,9 @@ constexpr int64_t kLdsReserve = 1024;
 // gfx950). Queried once per device.
 int64_t lds_row_budget();
 
+// Compute units of the current device (256 on MI355X). Queried once per device.
+int64_t device_cus();
+
 // Raise a kernel's dynamic-LDS limit to `bytes` (needed above 64 KiB). The
 // result of the first call per kernel is cached by the caller.
 hipError_t allow_dynamic_lds(const void* kernel, size_t bytes);

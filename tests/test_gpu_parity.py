@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 PAIRS = [(O.F32, O.F32), (O.F16, O.F16), (O.F16, O.F32), (O.BF16, O.BF16), (O.BF16, O.F32)]
 PAIR_IDS = ["f32", "f16", "f16_gf32", "bf16", "bf16_gf32"]
-N_SWEEP = [1, 7, 8, 63, 64, 1000, 1024, 2047, 2048, 4096, 4999, 5000, 5001, 8191, 8192, 8193,
+N_SWEEP = [1, 7, 8, 63, 64, 1000, 1024, 2047, 2048, 4096, 4999, 5000, 5001, 6152, 7000, 8191, 8192, 8193,
            12288, 16384, 32768]
 N_LDS = {O.F32: 20000, O.F16: 40000, O.BF16: 40000}      # 80 KB rows: LDS-cached, 1024 threads
 N_REREAD = {O.F32: 45000, O.F16: 90000, O.BF16: 90000}   # 180 KB rows: beyond 160 KiB of LDS
