@@ -348,3 +348,63 @@ def test_workload_full_size(w):
     else:
         floor_only = run_bwd(w.M, w.N, w.x_dt, w.g_dt, seed=w.seed, eps=w.eps)
         _log(f"dx elements passing only by the cancellation floor: {floor_only}")
+
+
+# ------------------------------------------- streams and graph capture
+
+def test_non_default_stream_matches_default():
+    M, N = 257, 8192
+    x, g, _, _ = _inputs(M, N, O.BF16, O.BF16, 91)
+    xt, gt = _put(x, O.BF16), _put(g, O.BF16)
+    y0, y1 = _empty(M * N, O.BF16), _empty(M * N, O.BF16)
+    assert R.rmsnorm_fwd(xt, gt, y0, None, M, N, 1e-5, O.BF16, O.BF16, _stream()) == 0
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        assert R.rmsnorm_fwd(xt, gt, y1, None, M, N, 1e-5, O.BF16, O.BF16, side) == 0
+    side.synchronize()
+    assert np.array_equal(to_host(y0), to_host(y1))
+
+
+def test_graph_capture_and_replay():
+    # The library allocates nothing and issues no memsets, so its launches can
+    # be captured. Replays, with eager work in between, must match eager runs.
+    M, N = 512, 8192
+    x, g, r, dy = _inputs(M, N, O.BF16, O.BF16, 93, with_r=True, with_dy=True)
+    xt, gt, dyt = _put(x, O.BF16), _put(g, O.BF16), _put(dy, O.BF16)
+    r0 = _put(r, O.BF16)
+    rt = r0.clone()
+    y, rs, y2 = _empty(M * N, O.BF16), torch.empty(M, device="cuda"), _empty(M * N, O.BF16)
+    dx, dg = _empty(M * N, O.BF16), torch.empty(N, device="cuda")
+    wsb = R.rmsnorm_bwd_workspace_size(M, N, O.BF16)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
+    def run(stream):
+        assert R.rmsnorm_fwd(xt, gt, y, rs, M, N, 1e-5, O.BF16, O.BF16, stream) == 0
+        assert R.rmsnorm_fused_add_fwd(xt, rt, gt, y2, None, M, N, 1e-5, O.BF16, O.BF16,
+                                       stream) == 0
+        assert R.rmsnorm_bwd(dyt, xt, rs, gt, dx, dg, ws, wsb, M, N, O.BF16, O.BF16, stream) == 0
+
+    rt.copy_(r0)
+    run(_stream())
+    torch.cuda.synchronize()
+    want = [to_host(t) for t in (y, rs, rt, y2, dx, dg)]
+
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            run(side)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(4):
+        rt.copy_(r0)                      # eager work between replays
+        for t in (y, rs, y2, dx, dg):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [to_host(t) for t in (y, rs, rt, y2, dx, dg)]
+        for a, b in zip(got, want):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), rep
