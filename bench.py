@@ -20,7 +20,8 @@ Also reported, in the same JSON line:
   cpu_baseline  the fp64 oracle, single-threaded, on the host, over repeated
                 full passes of the same batch for about --cpu-seconds;
   workloads     the other four workloads (fp32 short rows, fused residual add,
-                backward, fp16 ragged rows) timed the same way;
+                backward, fp16 ragged rows) and the fused-add backward, timed
+                the same way;
   calibration   a plain device-to-device copy of the step's byte count.
 """
 
@@ -39,6 +40,15 @@ sys.path.insert(0, ROOT)
 
 PEAK_GBPS = 8000.0
 HEADLINE = "fwd_bf16_m4096_n8192_rstd"
+# The kernel that dominates each workload's step, as the dispatcher picks it.
+DOMINANT_KERNEL = {
+    "fwd_f32_m64_n1024": "fwd_reg_kernel",
+    "fwd_bf16_m4096_n8192_rstd": "fwd_pp_kernel",
+    "fusedadd_bf16_m16384_n4096_gf32": "fwd_reg_kernel",
+    "bwd_bf16_m8192_n8192": "bwd_stage1_kernel",
+    "fwd_f16_m32768_n5000_outliers": "fwd_reg_kernel",
+    "fusedadd_bwd_bf16_m8192_n8192": "bwd_stage1_kernel",
+}
 DT_NAMES = {0: "f32", 1: "f16", 2: "bf16"}
 
 
@@ -74,7 +84,8 @@ class Runner:
             return t.to(dev)
 
         big = M * N * w.esize
-        per_replica = {"fwd": 2 * big, "fused_add": 3 * big, "bwd": 3 * big}[w.kind]
+        per_replica = {"fwd": 2 * big, "fused_add": 3 * big, "bwd": 3 * big,
+                       "fused_add_bwd": 4 * big}[w.kind]
         self.replicas = max(1, int(-(-rotate_bytes // per_replica))) if rotate_bytes > 0 else 1
         x0 = dev_copy(host_inputs["x"], w.x_dt)
         g = dev_copy(host_inputs["gamma"], w.g_dt)
@@ -83,7 +94,8 @@ class Runner:
         stream = torch.cuda.current_stream(dev)
         self.stream_handle = stream.cuda_stream
         rstd_bwd = None
-        if w.kind == "bwd":
+        backward = w.kind in ("bwd", "fused_add_bwd")
+        if backward:
             # The saved rstd comes from this library's own forward pass.
             rstd_bwd = torch.empty(M, dtype=torch.float32, device=dev)
             tmp = torch.empty_like(x0)
@@ -92,6 +104,8 @@ class Runner:
             del tmp
             dy0 = dev_copy(host_inputs["dy"], w.x_dt)
             self.ws_bytes = R.rmsnorm_bwd_workspace_size(M, N, w.x_dt)
+        if w.kind == "fused_add_bwd":
+            dres0 = dev_copy(host_inputs["dres"], w.x_dt)
         if w.kind == "fused_add":
             r0 = dev_copy(host_inputs["r"], w.x_dt)
         for i in range(self.replicas):
@@ -109,6 +123,8 @@ class Runner:
                 s["dx"] = torch.empty_like(x0)
                 s["dgamma"] = torch.empty(N, dtype=torch.float32, device=dev)
                 s["ws"] = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
+                if w.kind == "fused_add_bwd":
+                    s["dres"] = dres0 if i == 0 else dres0.clone()
             self.sets.append(s)
         torch.cuda.synchronize()
         # Pre-marshalled integer arguments keep the host launch path short.
@@ -124,10 +140,15 @@ class Runner:
                 args = (p["x"], p["r"], g.data_ptr(), p["y"], p["rstd"], M, N, w.eps, w.x_dt,
                         w.g_dt, self.stream_handle)
                 self.calls.append((lib.rmsnorm_fused_add_fwd, args))
-            else:
+            elif w.kind == "bwd":
                 args = (p["dy"], p["x"], p["rstd"], g.data_ptr(), p["dx"], p["dgamma"], p["ws"],
                         self.ws_bytes, M, N, w.x_dt, w.g_dt, self.stream_handle)
                 self.calls.append((lib.rmsnorm_bwd, args))
+            else:
+                args = (p["dy"], p["x"], p["rstd"], g.data_ptr(), p["dres"], p["dx"],
+                        p["dgamma"], p["ws"], self.ws_bytes, M, N, w.x_dt, w.g_dt,
+                        self.stream_handle)
+                self.calls.append((lib.rmsnorm_fused_add_bwd, args))
 
     def step(self, i: int) -> None:
         fn, args = self.calls[i % len(self.calls)]
@@ -183,10 +204,25 @@ def cpu_baseline(w, host_inputs: dict, seconds: float) -> dict:
     import oracle as O
     O._load()
     M, N = w.M, w.N
+    x, g = host_inputs["x"], host_inputs["gamma"]
+    if w.kind == "fwd":
+        def one_pass():
+            O.rmsnorm_fwd(x, g, M, N, w.eps, w.x_dt, w.g_dt, want_exact=False)
+    elif w.kind == "fused_add":
+        def one_pass():
+            O.rmsnorm_fused_add_fwd(x, host_inputs["r"], g, M, N, w.eps, w.x_dt, w.g_dt,
+                                    want_exact=False)
+    else:
+        # The saved rstd is an input of the backward, made outside the timing.
+        rho = O.rmsnorm_fwd(x, g, M, N, w.eps, w.x_dt, w.g_dt, want_exact=False)["rstd"]
+        dres = host_inputs.get("dres")
+
+        def one_pass():
+            O.rmsnorm_fused_add_bwd(host_inputs["dy"], x, rho, g, dres, M, N, w.x_dt, w.g_dt,
+                                    want_exact=False)
     passes, t0 = 0, time.perf_counter()
     while True:
-        O.rmsnorm_fwd(host_inputs["x"], host_inputs["gamma"], M, N, w.eps, w.x_dt, w.g_dt,
-                      want_exact=False)
+        one_pass()
         passes += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -261,7 +297,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / PEAK_GBPS, 4),
                      "traffic": load_traffic(w.name, src_hash),
-                     "kernel": "fwd_reg_kernel" if w.kind == "fwd" else w.kind,
+                     "kernel": DOMINANT_KERNEL.get(w.name, w.kind),
                      "kernel_src_hash": src_hash},
         "hot_cache_gbps": round(nbytes / (hot_ms * 1e-3) / 1e9, 2),
         "calibration": {"copy_gbps": round(calib, 2), "what": "torch device-to-device copy, "
@@ -272,7 +308,7 @@ def main() -> int:
 
     if not args.no_others:
         others = {}
-        for ow in G.WORKLOADS:
+        for ow in G.WORKLOADS + G.EXTRA_WORKLOADS:
             if ow.name == w.name:
                 continue
             oh = G.make_inputs(ow)
@@ -285,7 +321,7 @@ def main() -> int:
                                "pct_of_peak": round(100 * ob / (oms * 1e-3) / 1e9 / PEAK_GBPS, 2),
                                "rows_per_s": round(ow.M / (oms * 1e-3), 1),
                                "steps": k, "rotation_replicas": orun.replicas}
-            if ow.kind == "bwd":
+            if ow.kind in ("bwd", "fused_add_bwd"):
                 others[ow.name]["workspace_bytes"] = orun.ws_bytes
             del orun, oh
             torch.cuda.empty_cache()

@@ -23,7 +23,7 @@ DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
 ESIZE = {F32: 4, F16: 2, BF16: 2}
 
 # Stream ids per operand.
-STREAM_X, STREAM_R, STREAM_DY, STREAM_GAMMA = 1, 2, 3, 4
+STREAM_X, STREAM_R, STREAM_DY, STREAM_GAMMA, STREAM_DRES = 1, 2, 3, 4, 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgen.so")
@@ -108,7 +108,7 @@ def raw_bits(seed: int, stream: int, n: int) -> np.ndarray:
 class Workload:
     """One benchmark / parity workload."""
     name: str
-    kind: str            # "fwd", "fused_add", "bwd"
+    kind: str            # "fwd", "fused_add", "bwd", "fused_add_bwd"
     M: int
     N: int
     x_dt: int
@@ -135,6 +135,9 @@ class Workload:
             return 2 * big + g + (4 * self.M if self.store_rstd else 0)
         if self.kind == "fused_add":
             return 4 * big + g + (4 * self.M if self.store_rstd else 0)
+        if self.kind == "fused_add_bwd":
+            # read h, dy, dresidual, rstd, gamma; write dh, dgamma (fp32)
+            return 4 * big + 4 * self.M + g + 4 * self.N
         # backward: read x, dy, rstd, gamma; write dx, dgamma (fp32)
         return 3 * big + 4 * self.M + g + 4 * self.N
 
@@ -152,17 +155,25 @@ WORKLOADS = [
     Workload("fwd_f16_m32768_n5000_outliers", "fwd", 32768, 5000, F16, F16, 1e-6, 1005,
              outlier_every=97, outlier_scale=200.0),
 ]
-WORKLOADS_BY_NAME = {w.name: w for w in WORKLOADS}
+# Workloads of the operations beyond the five: the fused-add backward at the
+# backward's shape (h in place of x, plus the residual stream's gradient).
+EXTRA_WORKLOADS = [
+    Workload("fusedadd_bwd_bf16_m8192_n8192", "fused_add_bwd", 8192, 8192, BF16, BF16, 1e-5, 1006),
+]
+WORKLOADS_BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
 
 def make_inputs(w: Workload, nthreads: int | None = None) -> dict:
-    """Host inputs for workload w: x, gamma, and r (fused add) or dy (backward).
+    """Host inputs for workload w: x (h for the fused-add backward), gamma, and
+    r (fused add), dy (backward) or dy and dres (fused-add backward).
     The backward's saved rstd comes from the oracle forward and is not made here."""
     out = {"x": normal(w.seed, STREAM_X, w.M, w.N, w.x_dt, w.outlier_scale, w.outlier_every,
                        nthreads=nthreads),
            "gamma": uniform(w.seed, STREAM_GAMMA, w.N, 0.5, 1.5, w.g_dt, nthreads=nthreads)}
     if w.kind == "fused_add":
         out["r"] = normal(w.seed, STREAM_R, w.M, w.N, w.x_dt, nthreads=nthreads)
-    if w.kind == "bwd":
+    if w.kind in ("bwd", "fused_add_bwd"):
         out["dy"] = normal(w.seed, STREAM_DY, w.M, w.N, w.x_dt, nthreads=nthreads)
+    if w.kind == "fused_add_bwd":
+        out["dres"] = normal(w.seed, STREAM_DRES, w.M, w.N, w.x_dt, nthreads=nthreads)
     return out

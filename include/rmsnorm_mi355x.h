@@ -115,6 +115,25 @@ int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* ga
                 void* dx, float* dgamma, void* workspace, size_t workspace_bytes,
                 int64_t M, int64_t N, int x_dtype, int gamma_dtype, hipStream_t stream);
 
+/* Backward of the fused residual add + RMSNorm (rmsnorm_fused_add_fwd): with
+ * h the saved sum (the residual buffer after the forward) and rstd its saved
+ * rstd, the gradient of h is the norm's backward over h plus the gradient
+ * that reaches h through the residual stream:
+ *     dh_ij = rho_i (gamma_j dy_ij - h_ij rho_i^2 c_i) + dresidual_ij
+ * summed in fp32 and rounded once; dh is the gradient of both x and the old
+ * residual. dgamma and the workspace are as in rmsnorm_bwd (same size
+ * function). The pages list the fused add among the FlashInfer ports of the
+ * "TIRx kernels" page and FlyDSL's fused-add training wrappers without a
+ * formula; this is the derivative of the forward reading above.
+ *   dy, h      [M, N] x_dtype, read.
+ *   dresidual  [M, N] x_dtype, read; may be NULL (then dh is rmsnorm_bwd's dx).
+ *   dh         [M, N] x_dtype, written; may equal dy, h or dresidual exactly. */
+int rmsnorm_fused_add_bwd(const void* dy, const void* h, const float* rstd,
+                          const void* gamma, const void* dresidual, void* dh,
+                          float* dgamma, void* workspace, size_t workspace_bytes,
+                          int64_t M, int64_t N, int x_dtype, int gamma_dtype,
+                          hipStream_t stream);
+
 /* Static English description of a status code ("unknown status" otherwise). */
 const char* rmsnorm_status_string(int status);
 

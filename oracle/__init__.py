@@ -57,8 +57,11 @@ def _load():
                                                  vp, dp, vp, dp, vp, dp]
     lib.oracle_rmsnorm_bwd.argtypes = [vp, vp, dp, vp, i64, i64, i32, i32,
                                        dp, vp, dp, dp, dp, dp]
+    lib.oracle_rmsnorm_fused_add_bwd.argtypes = [vp, vp, dp, vp, vp, i64, i64, i32, i32,
+                                                 dp, vp, dp, dp, dp, dp]
     for fn in (lib.oracle_decode, lib.oracle_round, lib.oracle_rmsnorm_fwd,
-               lib.oracle_rmsnorm_fused_add_fwd, lib.oracle_rmsnorm_bwd):
+               lib.oracle_rmsnorm_fused_add_fwd, lib.oracle_rmsnorm_bwd,
+               lib.oracle_rmsnorm_fused_add_bwd):
         fn.restype = None
     _lib = lib
     return lib
@@ -145,4 +148,27 @@ def rmsnorm_bwd(dy, x, rho, gamma, M, N, x_dt, g_dt, want_exact=True):
     s = np.empty(N, np.float64)
     _load().oracle_rmsnorm_bwd(_ptr(dy), _ptr(x), _ptr(rho), _ptr(gamma), M, N, x_dt, g_dt,
                                _ptr(dx_exact), _ptr(dx), _ptr(dgamma), _ptr(c), _ptr(a), _ptr(s))
+    return dict(dx_exact=dx_exact, dx=dx, dgamma=dgamma, c=c, a=a, s=s)
+
+
+def rmsnorm_fused_add_bwd(dy, h, rho, gamma, dres, M, N, x_dt, g_dt, want_exact=True):
+    """Backward of the fused add: dh = RMSNorm backward over h + dres (dres may
+    be None). Returns the backward's dict, with dx_exact / dx holding dh."""
+    dy = _check(dy, x_dt, M * N, "dy")
+    h = _check(h, x_dt, M * N, "h")
+    gamma = _check(gamma, g_dt, N, "gamma")
+    if dres is not None:
+        dres = _check(dres, x_dt, M * N, "dres")
+    rho = np.ascontiguousarray(rho, dtype=np.float64)
+    if rho.size != M:
+        raise ValueError("rho: expected M elements")
+    dx_exact = np.empty((M, N), np.float64) if want_exact else None
+    dx = np.empty((M, N), storage_dtype(x_dt))
+    dgamma = np.empty(N, np.float64)
+    c = np.empty(M, np.float64)
+    a = np.empty(M, np.float64)
+    s = np.empty(N, np.float64)
+    _load().oracle_rmsnorm_fused_add_bwd(_ptr(dy), _ptr(h), _ptr(rho), _ptr(gamma), _ptr(dres),
+                                         M, N, x_dt, g_dt, _ptr(dx_exact), _ptr(dx),
+                                         _ptr(dgamma), _ptr(c), _ptr(a), _ptr(s))
     return dict(dx_exact=dx_exact, dx=dx, dgamma=dgamma, c=c, a=a, s=s)

@@ -17,6 +17,9 @@
 //     name the operation without spelling it out. Reading taken: h = x + r is
 //     rounded once to the activation dtype, written back, and the rounded h is
 //     what is normalised.
+//   * Fused-add backward: the gradient of h is the norm's backward plus the
+//     gradient arriving through the residual stream; it is the gradient of x
+//     and of r.
 //   * Backward (FlyDSL guide section 1.2, "Backward"): inputs x, gamma, dy and
 //     the saved rstd (no eps); outputs dx and the fp32 weight gradient. The
 //     pages print no formula; it is the derivative of the forward above:
@@ -209,16 +212,18 @@ void oracle_rmsnorm_fused_add_fwd(const void* x, const void* r, const void* gamm
   }
 }
 
-// RMSNorm backward. rho[M] is the saved rstd as doubles (the fp32 array the GPU
-// receives, widened exactly). Outputs, each optional:
-//   dx_exact[M*N], dx_bits[M*N] (rounded to x_dt), dgamma[N] (overwritten),
-//   c[M]  the per-row dot (1/N) sum_j dy gamma x,
-//   a[M]  (1/N) sum_j |dy gamma x|   and   s[N]  sum_i |dy x rho|,
-// the last two being the magnitudes the tests scale their error floors by.
-void oracle_rmsnorm_bwd(const void* dy, const void* x, const double* rho,
-                        const void* gamma, int64_t M, int64_t N, int x_dt,
-                        int g_dt, double* dx_exact, void* dx_bits,
-                        double* dgamma, double* c, double* a, double* s) {
+// Backward of the fused residual add + RMSNorm (h = x + r, y = RMSNorm(h)).
+// The gradient reaching h is the norm's backward plus the gradient dres that
+// arrives through the residual stream (dres may be null: zero):
+//     dh_ij = rho_i (gamma_j dy_ij - h_ij rho_i^2 c_i) + dres_ij,
+// and it is the gradient of both x and r. dgamma is the norm's, over h.
+// Outputs as in oracle_rmsnorm_bwd (dx_* hold dh).
+void oracle_rmsnorm_fused_add_bwd(const void* dy, const void* h, const double* rho,
+                                  const void* gamma, const void* dres, int64_t M,
+                                  int64_t N, int x_dt, int g_dt, double* dx_exact,
+                                  void* dx_bits, double* dgamma, double* c, double* a,
+                                  double* s) {
+  const void* x = h;
   if (dgamma) for (int64_t j = 0; j < N; ++j) dgamma[j] = 0.0;
   if (s) for (int64_t j = 0; j < N; ++j) s[j] = 0.0;
   for (int64_t i = 0; i < M; ++i) {
@@ -237,6 +242,7 @@ void oracle_rmsnorm_bwd(const void* dy, const void* x, const double* rho,
       double xv = decode(x, i * N + j, x_dt);
       double dyv = decode(dy, i * N + j, x_dt);
       double d = p * (decode(gamma, j, g_dt) * dyv - xv * p * p * ci);
+      if (dres) d += decode(dres, i * N + j, x_dt);
       if (dx_exact) dx_exact[i * N + j] = d;
       if (dx_bits) store_value(dx_bits, i * N + j, d, x_dt);
       if (dgamma) dgamma[j] += dyv * xv * p;
@@ -245,4 +251,19 @@ void oracle_rmsnorm_bwd(const void* dy, const void* x, const double* rho,
   }
 }
 
+// RMSNorm backward. rho[M] is the saved rstd as doubles (the fp32 array the GPU
+// receives, widened exactly). Outputs, each optional:
+//   dx_exact[M*N], dx_bits[M*N] (rounded to x_dt), dgamma[N] (overwritten),
+//   c[M]  the per-row dot (1/N) sum_j dy gamma x,
+//   a[M]  (1/N) sum_j |dy gamma x|   and   s[N]  sum_i |dy x rho|,
+// the last two being the magnitudes the tests scale their error floors by.
+void oracle_rmsnorm_bwd(const void* dy, const void* x, const double* rho,
+                        const void* gamma, int64_t M, int64_t N, int x_dt,
+                        int g_dt, double* dx_exact, void* dx_bits,
+                        double* dgamma, double* c, double* a, double* s) {
+  oracle_rmsnorm_fused_add_bwd(dy, x, rho, gamma, nullptr, M, N, x_dt, g_dt, dx_exact,
+                               dx_bits, dgamma, c, a, s);
+}
+
 }  // extern "C"
+

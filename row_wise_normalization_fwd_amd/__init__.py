@@ -2,12 +2,12 @@
 
 The C ABI (include/rmsnorm_mi355x.h) is exposed under the same names
 (``rmsnorm_fwd``, ``rmsnorm_fused_add_fwd``, ``rmsnorm_bwd``,
-``rmsnorm_bwd_workspace_size``, ``rmsnorm_status_string``,
+``rmsnorm_fused_add_bwd``, ``rmsnorm_bwd_workspace_size``, ``rmsnorm_status_string``,
 ``rmsnorm_last_hip_error``); those functions only marshal arguments. Pointers
 may be given as integers or as torch tensors (their ``data_ptr()``); streams as
 integers or ``torch.cuda.Stream`` objects.
 
-``fwd``, ``fused_add_fwd`` and ``bwd`` are torch conveniences on top: they use
+``fwd``, ``fused_add_fwd``, ``bwd`` and ``fused_add_bwd`` are torch conveniences on top: they use
 torch only to allocate outputs and to pick the current stream, and every step
 of the computation runs in the library's HIP kernels. There is no fallback: if
 the library is not built, every call raises.
@@ -29,7 +29,7 @@ STATUS_NAMES = {
     -4: "RMSN_ERR_WORKSPACE", -5: "RMSN_ERR_OVERLAP", -6: "RMSN_ERR_ALIGN",
     -7: "RMSN_ERR_EPS", -100: "RMSN_ERR_HIP",
 }
-ENTRY_POINTS = ("rmsnorm_fwd", "rmsnorm_fused_add_fwd", "rmsnorm_bwd",
+ENTRY_POINTS = ("rmsnorm_fwd", "rmsnorm_fused_add_fwd", "rmsnorm_bwd", "rmsnorm_fused_add_bwd",
                 "rmsnorm_bwd_workspace_size", "rmsnorm_status_string", "rmsnorm_last_hip_error")
 
 
@@ -66,6 +66,9 @@ def load_library(path: str | None = None):
     lib.rmsnorm_bwd_workspace_size.restype = ctypes.c_size_t
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i32, i32, vp]
     lib.rmsnorm_bwd.restype = i32
+    lib.rmsnorm_fused_add_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64,
+                                          i32, i32, vp]
+    lib.rmsnorm_fused_add_bwd.restype = i32
     lib.rmsnorm_status_string.argtypes = [i32]
     lib.rmsnorm_status_string.restype = ctypes.c_char_p
     lib.rmsnorm_last_hip_error.argtypes = []
@@ -114,6 +117,14 @@ def rmsnorm_bwd(dy, x, rstd, gamma, dx, dgamma, workspace, workspace_bytes, M, N
     return load_library().rmsnorm_bwd(_p(dy), _p(x), _p(rstd), _p(gamma), _p(dx), _p(dgamma),
                                       _p(workspace), workspace_bytes, M, N, x_dtype, gamma_dtype,
                                       _s(stream))
+
+
+def rmsnorm_fused_add_bwd(dy, h, rstd, gamma, dresidual, dh, dgamma, workspace, workspace_bytes,
+                          M, N, x_dtype, gamma_dtype, stream) -> int:
+    return load_library().rmsnorm_fused_add_bwd(_p(dy), _p(h), _p(rstd), _p(gamma),
+                                                _p(dresidual), _p(dh), _p(dgamma), _p(workspace),
+                                                workspace_bytes, M, N, x_dtype, gamma_dtype,
+                                                _s(stream))
 
 
 def rmsnorm_status_string(status: int) -> str:
@@ -195,3 +206,25 @@ def bwd(dy, x, rstd, gamma, *, dx=None, dgamma=None, workspace=None, stream=None
     _check(rmsnorm_bwd(dy, x, rstd, gamma, dx, dgamma, workspace, workspace.numel(), M, N,
                        dtype_code(x), dtype_code(gamma), stream), "rmsnorm_bwd")
     return dx, dgamma
+
+
+def fused_add_bwd(dy, h, rstd, gamma, dresidual=None, *, dh=None, dgamma=None, workspace=None,
+                  stream=None):
+    """Backward of fused_add_fwd: returns (dh, dgamma); dh is the gradient of
+    both x and the residual. ``h`` is the residual buffer after the forward."""
+    import torch
+    N = gamma.numel()
+    M = _rows(h, N)
+    for t in (dy, dresidual):
+        if t is not None and (t.shape != h.shape or t.dtype != h.dtype):
+            raise ValueError("dy / dresidual must match h in shape and dtype")
+    dh = torch.empty_like(h) if dh is None else dh
+    dgamma = torch.empty(N, dtype=torch.float32, device=h.device) if dgamma is None else dgamma
+    ws_bytes = rmsnorm_bwd_workspace_size(M, N, dtype_code(h))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=h.device)
+    stream = torch.cuda.current_stream(h.device) if stream is None else stream
+    _check(rmsnorm_fused_add_bwd(dy, h, rstd, gamma, dresidual, dh, dgamma, workspace,
+                                 workspace.numel(), M, N, dtype_code(h), dtype_code(gamma), stream),
+           "rmsnorm_fused_add_bwd")
+    return dh, dgamma

@@ -92,6 +92,54 @@ int forward(bool fused, const void* x, void* residual, const void* gamma, void* 
 }  // namespace
 
 namespace rmsn {
+BwdPlan plan_bwd(int64_t M, int64_t N, int x_dtype);
+}
+
+namespace {
+
+// Shared validation of the backward calls; dres (fused add) may be null.
+int backward(const void* dy, const void* x, const float* rstd, const void* gamma,
+             const void* dres, void* dx, float* dgamma, void* workspace, size_t workspace_bytes,
+             int64_t M, int64_t N, int x_dtype, int gamma_dtype, hipStream_t stream) {
+  if (!valid_pair(x_dtype, gamma_dtype)) return RMSN_ERR_DTYPE;
+  if (!shape_ok(M, N)) return RMSN_ERR_SHAPE;
+  if (M == 0) return RMSN_OK;
+  const rmsn::BwdPlan plan = rmsn::plan_bwd(M, N, x_dtype);
+  if (!dy || !x || !rstd || !gamma || !dx || !dgamma) return RMSN_ERR_NULL;
+  if (!workspace || workspace_bytes < plan.workspace_bytes) return RMSN_ERR_WORKSPACE;
+  const int es = esize_of(x_dtype), gs = esize_of(gamma_dtype);
+  if (!aligned(dy, es) || !aligned(x, es) || !aligned(dx, es) || !aligned(gamma, gs) ||
+      !aligned(rstd, 4) || !aligned(dgamma, 4) || !aligned(workspace, 16) ||
+      (dres && !aligned(dres, es)))
+    return RMSN_ERR_ALIGN;
+  const uint64_t big = static_cast<uint64_t>(M) * static_cast<uint64_t>(N) * es;
+  const Range rdy = span(dy, big), rx = span(x, big), rdx = span(dx, big);
+  const Range rr = span(rstd, static_cast<uint64_t>(M) * 4);
+  const Range rg = span(gamma, static_cast<uint64_t>(N) * gs);
+  const Range rdg = span(dgamma, static_cast<uint64_t>(N) * 4);
+  const Range rw = span(workspace, plan.workspace_bytes);
+  // dx may equal dy, x or dres exactly (each lane reads an element before it
+  // writes it); every other overlap with a written buffer is an error.
+  if (partial_overlap(rdx, rdy) || partial_overlap(rdx, rx) || overlap(rdx, rr) ||
+      overlap(rdx, rg) || overlap(rdx, rdg) || overlap(rdx, rw))
+    return RMSN_ERR_OVERLAP;
+  if (dres) {
+    const Range rres = span(dres, big);
+    if (partial_overlap(rdx, rres) || overlap(rdg, rres) || overlap(rw, rres))
+      return RMSN_ERR_OVERLAP;
+  }
+  const Range reads[] = {rdy, rx, rr, rg};
+  for (const Range& r : reads)
+    if (overlap(rdg, r) || overlap(rw, r)) return RMSN_ERR_OVERLAP;
+  if (overlap(rdg, rw)) return RMSN_ERR_OVERLAP;
+  rmsn::BwdCall c{dy, x, rstd, gamma, dres, dx, dgamma, workspace, M, N, x_dtype, gamma_dtype,
+                  plan, stream};
+  return finish(rmsn::launch_bwd(c));
+}
+
+}  // namespace
+
+namespace rmsn {
 
 int64_t lds_row_budget() {
   static std::atomic<int64_t> cache[64];  // per device; 0 = not queried yet
@@ -167,32 +215,16 @@ size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int x_dtype) {
 int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* gamma, void* dx,
                 float* dgamma, void* workspace, size_t workspace_bytes, int64_t M, int64_t N,
                 int x_dtype, int gamma_dtype, hipStream_t stream) {
-  if (!valid_pair(x_dtype, gamma_dtype)) return RMSN_ERR_DTYPE;
-  if (!shape_ok(M, N)) return RMSN_ERR_SHAPE;
-  if (M == 0) return RMSN_OK;
-  const rmsn::BwdPlan plan = rmsn::plan_bwd(M, N, x_dtype);
-  if (!dy || !x || !rstd || !gamma || !dx || !dgamma) return RMSN_ERR_NULL;
-  if (!workspace || workspace_bytes < plan.workspace_bytes) return RMSN_ERR_WORKSPACE;
-  const int es = esize_of(x_dtype), gs = esize_of(gamma_dtype);
-  if (!aligned(dy, es) || !aligned(x, es) || !aligned(dx, es) || !aligned(gamma, gs) ||
-      !aligned(rstd, 4) || !aligned(dgamma, 4) || !aligned(workspace, 16))
-    return RMSN_ERR_ALIGN;
-  const uint64_t big = static_cast<uint64_t>(M) * static_cast<uint64_t>(N) * es;
-  const Range rdy = span(dy, big), rx = span(x, big), rdx = span(dx, big);
-  const Range rr = span(rstd, static_cast<uint64_t>(M) * 4);
-  const Range rg = span(gamma, static_cast<uint64_t>(N) * gs);
-  const Range rdg = span(dgamma, static_cast<uint64_t>(N) * 4);
-  const Range rw = span(workspace, plan.workspace_bytes);
-  if (partial_overlap(rdx, rdy) || partial_overlap(rdx, rx) || overlap(rdx, rr) ||
-      overlap(rdx, rg) || overlap(rdx, rdg) || overlap(rdx, rw))
-    return RMSN_ERR_OVERLAP;
-  const Range reads[] = {rdy, rx, rr, rg};
-  for (const Range& r : reads)
-    if (overlap(rdg, r) || overlap(rw, r)) return RMSN_ERR_OVERLAP;
-  if (overlap(rdg, rw)) return RMSN_ERR_OVERLAP;
-  rmsn::BwdCall c{dy, x, rstd, gamma, dx, dgamma, workspace, M, N, x_dtype, gamma_dtype, plan,
-                  stream};
-  return finish(rmsn::launch_bwd(c));
+  return backward(dy, x, rstd, gamma, nullptr, dx, dgamma, workspace, workspace_bytes, M, N,
+                  x_dtype, gamma_dtype, stream);
+}
+
+int rmsnorm_fused_add_bwd(const void* dy, const void* h, const float* rstd, const void* gamma,
+                          const void* dresidual, void* dh, float* dgamma, void* workspace,
+                          size_t workspace_bytes, int64_t M, int64_t N, int x_dtype,
+                          int gamma_dtype, hipStream_t stream) {
+  return backward(dy, h, rstd, gamma, dresidual, dh, dgamma, workspace, workspace_bytes, M, N,
+                  x_dtype, gamma_dtype, stream);
 }
 
 const char* rmsnorm_status_string(int status) {

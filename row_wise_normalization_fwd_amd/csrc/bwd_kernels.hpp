@@ -8,6 +8,11 @@
 //     c_i      = (1/N) sum_j dy_ij gamma_j x_ij
 //     dx_ij    = rho_i (gamma_j dy_ij - x_ij rho_i^2 c_i)
 //     dgamma_j = sum_i dy_ij x_ij rho_i
+// For the fused residual add (h = x + r, y = RMSNorm(h)) the same kernels run
+// over h with RES set: the gradient arriving through the residual stream,
+// dres, is added to dx in fp32 before the one rounding, giving the gradient
+// of h (which is that of x and of r).
+//
 // The weight gradient is reduced in two stages without atomics: stage 1 gives
 // each of G blocks a fixed set of rows -- block b owns rows b, b + G, b + 2G,
 // ..., so at any moment all blocks work inside one compact window of rows
@@ -28,6 +33,7 @@ struct BwdArgs {
   const float* rstd;
   const typename G::S* gamma;
   typename T::S* dx;
+  const typename T::S* dres;  // fused-add backward: gradient added to dx (else null)
   float* partial;  // [G, N] fp32, one row per partition block
   int64_t M;
   int N;
@@ -54,7 +60,7 @@ __device__ __forceinline__ float unit_dot(const float* dyv, const float* g, cons
 // current row is reduced, so loads stay in flight across rows. With RG > 1 the
 // groups' partials are combined through LDS in group order before the block
 // writes its partial row.
-template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK>
+template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool RES>
 __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   using U = Unit<T, VEC>;
   using Raw = typename U::Raw;
@@ -105,18 +111,23 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
     return static_cast<uint32_t>(rest < 0x7fffffff ? rest : 0x7fffffff);
   };
 
-  // x and dy units of row row0 + nblk * grp (zeros past the last row or unit).
-  auto load_row = [&](int64_t row0, Raw* rx, Raw* rdy) {
+  // x, dy (and dres) units of row row0 + nblk * grp (zeros past the last row
+  // or unit).
+  auto load_row = [&](int64_t row0, Raw* rx, Raw* rdy, Raw* rr) {
     if constexpr (VEC) {
       const bool any = row0 < a.M;
       const uint32_t n = any ? span_bytes(row0) : 0u;
-      const auto rsx = make_rsrc(a.x + (any ? row0 : 0) * a.N, n);
-      const auto rsd = make_rsrc(a.dy + (any ? row0 : 0) * a.N, n);
+      const int64_t base = (any ? row0 : 0) * a.N;
+      const auto rsx = make_rsrc(a.x + base, n);
+      const auto rsd = make_rsrc(a.dy + base, n);
+      [[maybe_unused]] __amdgpu_buffer_rsrc_t rsr;
+      if constexpr (RES) rsr = make_rsrc(a.dres + base, n);
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
         const uint32_t o = unit_offset(row0, grp, k);
         rx[k] = buf_load16_nt(rsx, o);
         rdy[k] = buf_load16_nt(rsd, o);
+        if constexpr (RES) rr[k] = buf_load16_nt(rsr, o);
       }
     } else {
       const int64_t row = row0 + a.nblk * grp;
@@ -131,6 +142,10 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
         const Raw vdy = U::load_nt(a.dy + off + uc * E);
         rx[k] = ok ? vx : U::zero();
         rdy[k] = ok ? vdy : U::zero();
+        if constexpr (RES) {
+          const Raw vr = U::load_nt(a.dres + off + uc * E);
+          rr[k] = ok ? vr : U::zero();
+        }
       }
     }
   };
@@ -140,13 +155,13 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   // prefetched data is first touched inside the next call, after that call
   // has issued its own prefetch.
   int parity = 0;
-  auto step = [&](int64_t row0, Raw* cx, Raw* cdy, Raw* nx, Raw* ndy) {
+  auto step = [&](int64_t row0, Raw* cx, Raw* cdy, Raw* cr, Raw* nx, Raw* ndy, Raw* nr) {
     const int64_t row = row0 + a.nblk * grp;
     const bool valid = row < a.M;
     const int64_t off = row * a.N;
     const float rho_ld = a.rstd[valid ? row : a.M - 1];
     const float rho = valid ? rho_ld : 0.0f;
-    load_row(row0 + a.nblk * RG, nx, ndy);
+    load_row(row0 + a.nblk * RG, nx, ndy, nr);
 
     double dot = 0.0;
 #pragma unroll
@@ -179,6 +194,12 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
         o[e] = rho * __builtin_fmaf(-xv[e], kcoef, gam[k][e] * dyv[e]);
         acc[k][e] = __builtin_fmaf(dyv[e] * xv[e], rho, acc[k][e]);
       }
+      if constexpr (RES) {
+        float rv[E];
+        U::widen(cr[k], rv);
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = o[e] + rv[e];
+      }
       if constexpr (VEC) {
         const auto rsdx = make_rsrc(a.dx + row0 * a.N, span_bytes(row0));
         buf_store16_nt(U::narrow(o), rsdx, unit_offset(row0, grp, k));
@@ -188,14 +209,14 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
     }
   };
 
-  Raw ax[UPT], ady[UPT], bx[UPT], bdy[UPT];
-  load_row(b, ax, ady);
+  Raw ax[UPT], ady[UPT], ar[UPT], bx[UPT], bdy[UPT], br[UPT];
+  load_row(b, ax, ady, ar);
   // Trip counts are uniform over the block, so every thread reaches every
   // reduction.
   for (int64_t s0 = 0; b + a.nblk * s0 < a.M; s0 += 2 * RG) {
-    step(b + a.nblk * s0, ax, ady, bx, bdy);
+    step(b + a.nblk * s0, ax, ady, ar, bx, bdy, br);
     if (b + a.nblk * (s0 + RG) >= a.M) break;
-    step(b + a.nblk * (s0 + RG), bx, bdy, ax, ady);
+    step(b + a.nblk * (s0 + RG), bx, bdy, br, ax, ady, ar);
   }
 
   float* out = a.partial + static_cast<int64_t>(blockIdx.x) * a.N;
@@ -273,7 +294,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_rowdot_kernel(BwdArgs<T, G> a, doub
 // the dgamma partial sums of its columns in registers over the block's rows
 // (in increasing row order) and writes them to partial[by][...]; dx uses the
 // row dots from pass A.
-template <class T, class G, bool VEC, int BLOCK, int UPT>
+template <class T, class G, bool VEC, int BLOCK, int UPT, bool RES>
 __global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const double* cdot) {
   using U = Unit<T, VEC>;
   using Raw = typename U::Raw;
@@ -295,12 +316,13 @@ __global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const 
   }
   for (int64_t row = blockIdx.y; row < a.M; row += a.nblk) {
     const int64_t off = row * a.N;
-    Raw rx[UPT], rdy[UPT];
+    Raw rx[UPT], rdy[UPT], rr[UPT];
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const int u = ubase + threadIdx.x + k * BLOCK;
       rx[k] = u < nunits ? U::load(a.x + off + u * E) : U::zero();
       rdy[k] = u < nunits ? U::load(a.dy + off + u * E) : U::zero();
+      if constexpr (RES) rr[k] = u < nunits ? U::load_nt(a.dres + off + u * E) : U::zero();
     }
     const float rho = a.rstd[row];
     const double rd = static_cast<double>(rho);
@@ -315,6 +337,12 @@ __global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const 
       for (int e = 0; e < E; ++e) {
         o[e] = rho * __builtin_fmaf(-xv[e], kcoef, gam[k][e] * dyv[e]);
         acc[k][e] = __builtin_fmaf(dyv[e] * xv[e], rho, acc[k][e]);
+      }
+      if constexpr (RES) {
+        float rv[E];
+        U::widen(rr[k], rv);
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = o[e] + rv[e];
       }
       if (u < nunits) U::store_nt(a.dx + off + u * E, U::narrow(o));
     }

@@ -55,11 +55,11 @@ template <class T, class G, bool VEC, int BLOCK, int UNROLL, bool FUSED, bool CA
 hipError_t run_fwd_long(const FwdArgs<T, G>& a, hipStream_t s) {
   int64_t blocks = a.M < kMaxGrid ? a.M : kMaxGrid;
   const size_t lds = CACHE ? static_cast<size_t>(a.N) * T::kSize : 0;
-  auto* kernel = fwd_long_kernel<T, G, VEC, BLOCK, UNROLL, FUSED, CACHE>;
+  constexpr auto kernel = fwd_long_kernel<T, G, VEC, BLOCK, UNROLL, FUSED, CACHE>;
   if constexpr (CACHE) {
     // Allow the largest row cache once; per-launch sizes stay below it.
-    static const hipError_t attr = allow_dynamic_lds(reinterpret_cast<const void*>(kernel),
-                                                     static_cast<size_t>(lds_row_budget()));
+    const hipError_t attr =
+        ensure_dynamic_lds<kernel>(static_cast<size_t>(lds_row_budget()));
     if (attr != hipSuccess) return attr;
   }
   kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), lds, s>>>(a);

@@ -3,8 +3,10 @@
 #pragma once
 
 #include <hip/hip_runtime_api.h>
-#include <stdint.h>
 #include <stddef.h>
+#include <stdint.h>
+
+#include <atomic>
 
 namespace rmsn {
 
@@ -28,9 +30,21 @@ int64_t lds_row_budget();
 // Compute units of the current device (256 on MI355X). Queried once per device.
 int64_t device_cus();
 
-// Raise a kernel's dynamic-LDS limit to `bytes` (needed above 64 KiB). The
-// result of the first call per kernel is cached by the caller.
+// Raise a kernel's dynamic-LDS limit to `bytes` (needed above 64 KiB).
 hipError_t allow_dynamic_lds(const void* kernel, size_t bytes);
+
+// allow_dynamic_lds once per kernel and device (function attributes are per
+// device). KERNEL is the kernel's address.
+template <auto KERNEL>
+hipError_t ensure_dynamic_lds(size_t bytes) {
+  static std::atomic<int> done[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(KERNEL), bytes);
+  if (e == hipSuccess) done[dev].store(1, std::memory_order_release);
+  return e;
+}
 // Upper bound on launched blocks for grid-stride kernels.
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
 
@@ -74,6 +88,7 @@ struct BwdCall {
   const void* x;
   const float* rstd;
   const void* gamma;
+  const void* dres;  // fused-add backward: residual-stream gradient, else null
   void* dx;
   float* dgamma;
   void* workspace;

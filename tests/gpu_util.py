@@ -10,6 +10,8 @@ Tolerances (fixed here, used by every GPU test):
   * dx: within 1 ulp, or, where gamma*dy and x*rho^2*c cancel, absolute error
     <= 2^-18 * rho * (|gamma dy| + |x| rho^2 A) with A = mean_j |dy gamma x|
     (an fp32 evaluation cannot resolve a cancelled result below that scale).
+  * dh of the fused-add backward: as dx, with 2^-22 |dresidual| added to the
+    floor for the fp32 addition of the residual gradient.
   * dgamma: |g - o| <= max(1e-3 |o|, 2^-24 S_j) with S_j = sum_i |dy x rho|.
 """
 
@@ -81,8 +83,12 @@ def check_rstd(got: np.ndarray, exact: np.ndarray):
 
 
 def check_dx(got: np.ndarray, ref: dict, x: np.ndarray, dy: np.ndarray, gamma: np.ndarray,
-             rho: np.ndarray, dt: int):
-    """Returns the number of elements that passed only through the floor."""
+             rho: np.ndarray, dt: int, dres: np.ndarray | None = None):
+    """Returns the number of elements that passed only through the floor.
+
+    With ``dres`` (fused-add backward) the kernel adds it to the fp32 norm
+    gradient before the one rounding; that addition can cancel, so the floor
+    also covers one fp32 rounding of each addend (2^-22 |dres| is generous)."""
     M, N = got.shape
     xd = O.decode(x, dt).reshape(M, N)
     dyd = O.decode(dy, dt).reshape(M, N)
@@ -96,6 +102,8 @@ def check_dx(got: np.ndarray, ref: dict, x: np.ndarray, dy: np.ndarray, gamma: n
         gotv = O.decode(got, dt).reshape(M, N)
     rho2 = rho[:, None].astype(np.float64)
     floor = 2.0 ** -18 * rho2 * (np.abs(gd[None, :] * dyd) + np.abs(xd) * rho2 ** 2 * ref["a"][:, None])
+    if dres is not None:
+        floor = floor + 2.0 ** -22 * np.abs(O.decode(dres, dt).reshape(M, N))
     ok_floor = np.abs(gotv - exact) <= floor
     bad = ~(ok_ulp | ok_floor)
     if bad.any():

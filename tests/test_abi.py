@@ -143,3 +143,30 @@ def test_backward_validation(lib):
     assert bwd(dg=A + 4) == OVERLAP
     assert bwd(ws=B + 16) == OVERLAP
     assert bwd(ws=F) == OVERLAP               # workspace over dgamma
+
+
+H = 0x80000000  # an eighth well-separated address, for dresidual
+
+
+def fbwd(dy=A, h=B, rstd=C, g=D, dres=H, dh=E, dg=F, ws=G, wsb=None, M=64, N=256, xd=BF16,
+         gd=BF16):
+    if wsb is None:
+        wsb = R.rmsnorm_bwd_workspace_size(M, N, xd)
+    return R.rmsnorm_fused_add_bwd(dy, h, rstd, g, dres, dh, dg, ws, wsb, M, N, xd, gd, None)
+
+
+def test_fused_backward_validation(lib):
+    assert fbwd(xd=5) == DTYPE
+    assert fbwd(M=-1) == SHAPE
+    assert fbwd(M=0, dy=None, h=None, rstd=None, g=None, dres=None, dh=None, dg=None,
+                ws=None) == OK
+    for k in ("dy", "h", "rstd", "g", "dh", "dg"):
+        assert fbwd(**{k: None}) == NULL, k
+    assert fbwd(ws=None) == WORKSPACE
+    assert fbwd(dres=H + 1) == ALIGN
+    assert fbwd(dres=H + 2, xd=F32, gd=F32) == ALIGN
+    # dh may equal dresidual, dy or h exactly, but not overlap any of them
+    # partially, nor the outputs and workspace.
+    assert fbwd(dh=H + 64) == OVERLAP
+    assert fbwd(dres=F) == OVERLAP             # dresidual over dgamma
+    assert fbwd(dres=G + 256) == OVERLAP       # dresidual over the workspace

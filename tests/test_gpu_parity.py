@@ -334,9 +334,96 @@ def test_bwd_empty_is_noop():
                          _stream()) == 0
 
 
-# ------------------------------------------------- the five full workloads
+# ------------------------------------------------ fused-add backward
 
-@pytest.mark.parametrize("w", G.WORKLOADS, ids=[w.name for w in G.WORKLOADS])
+def run_fused_bwd(M, N, xdt, gdt, seed=17, misalign=0, alias=None, with_dres=True):
+    """h is the fused forward's sum (any array works: the backward only sees h
+    and its rstd); dresidual comes from its own generator stream."""
+    _log(f"fused_bwd M={M} N={N} x={xdt} g={gdt} misalign={misalign} alias={alias} "
+         f"dres={with_dres}")
+    h, g, _, dy = _inputs(M, N, xdt, gdt, seed, with_dy=True)
+    dres = G.normal(seed, G.STREAM_DRES, M, N, xdt) if with_dres else None
+    rho = O.rmsnorm_fwd(h, g, M, N, 1e-5, xdt, gdt, want_exact=False)["rstd"]
+    ref = O.rmsnorm_fused_add_bwd(dy, h, rho, g, dres, M, N, xdt, gdt)
+    ht, gt, dyt = _put(h, xdt, misalign), _put(g, gdt), _put(dy, xdt, misalign)
+    drt = _put(dres, xdt, misalign) if with_dres else None
+    rt = torch.from_numpy(rho.copy()).cuda()
+    dht = {"dy": dyt, "h": ht, "dres": drt}.get(alias) if alias else _empty(M * N, xdt, misalign)
+    dgt = torch.full((N,), float("nan"), device="cuda")
+    wsb = R.rmsnorm_bwd_workspace_size(M, N, xdt)
+    ws = torch.full((max(wsb, 16) // 4,), float("nan"), device="cuda")
+    st = R.rmsnorm_fused_add_bwd(dyt, ht, rt, gt, drt, dht, dgt, ws, wsb, M, N, xdt, gdt,
+                                 _stream())
+    assert st == 0, R.rmsnorm_status_string(st)
+    torch.cuda.synchronize()
+    check_dx(to_host(dht).reshape(M, N), ref, h, dy, g, rho, xdt, dres=dres)
+    check_dgamma(to_host(dgt), ref)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("N", [1, 7, 64, 1000, 4096, 5000, 8192, 8193, 16384, 32768])
+def test_fused_bwd_sweep(N, pair):
+    run_fused_bwd(3, N, *pair, seed=700 + N)
+    run_fused_bwd(300, N, *pair, seed=800 + N)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_fused_bwd_long_misaligned_aliased(pair):
+    run_fused_bwd(600, 20000, *pair, seed=901)                  # two-pass tier, many rows
+    run_fused_bwd(5, 9000, *pair, seed=902, misalign=1)         # scalar two-pass tier
+    run_fused_bwd(9, 4096, *pair, seed=903, misalign=1)         # scalar on-chip tier
+    run_fused_bwd(9, 4096, *pair, seed=904, alias="dres")
+    run_fused_bwd(9, 4096, *pair, seed=905, alias="dy")
+    run_fused_bwd(9, 20000, *pair, seed=906, alias="h")
+    run_fused_bwd(4, 100000, *pair, seed=907, alias="dres")
+
+
+def test_fused_bwd_without_dresidual_is_plain_backward():
+    M, N = 257, 4096
+    run_fused_bwd(M, N, O.BF16, O.BF16, seed=911, with_dres=False)
+    h, g, _, dy = _inputs(M, N, O.BF16, O.BF16, 912, with_dy=True)
+    rho = O.rmsnorm_fwd(h, g, M, N, 1e-5, O.BF16, O.BF16, want_exact=False)["rstd"]
+    ht, gt, dyt, rt = _put(h, O.BF16), _put(g, O.BF16), _put(dy, O.BF16), torch.from_numpy(rho).cuda()
+    wsb = R.rmsnorm_bwd_workspace_size(M, N, O.BF16)
+    ws = torch.empty(wsb // 4, device="cuda")
+    outs = []
+    for fused in (False, True):
+        dxt, dgt = _empty(M * N, O.BF16), torch.empty(N, device="cuda")
+        if fused:
+            st = R.rmsnorm_fused_add_bwd(dyt, ht, rt, gt, None, dxt, dgt, ws, wsb, M, N, O.BF16,
+                                         O.BF16, _stream())
+        else:
+            st = R.rmsnorm_bwd(dyt, ht, rt, gt, dxt, dgt, ws, wsb, M, N, O.BF16, O.BF16,
+                               _stream())
+        assert st == 0
+        torch.cuda.synchronize()
+        outs.append((to_host(dxt), to_host(dgt)))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+
+
+def test_fused_bwd_zero_upstream_passes_dresidual_through():
+    # dy = 0: the norm contributes exactly 0, so dh == dresidual bit for bit.
+    M, N = 64, 8192
+    h, g, _, _ = _inputs(M, N, O.BF16, O.BF16, 921)
+    dy = O.round_to(np.zeros((M, N)), O.BF16)
+    dres = G.normal(921, G.STREAM_DRES, M, N, O.BF16)
+    rho = O.rmsnorm_fwd(h, g, M, N, 1e-5, O.BF16, O.BF16, want_exact=False)["rstd"]
+    dht, dgt = _empty(M * N, O.BF16), torch.empty(N, device="cuda")
+    wsb = R.rmsnorm_bwd_workspace_size(M, N, O.BF16)
+    ws = torch.empty(wsb // 4, device="cuda")
+    assert R.rmsnorm_fused_add_bwd(_put(dy, O.BF16), _put(h, O.BF16), torch.from_numpy(rho).cuda(),
+                                   _put(g, O.BF16), _put(dres, O.BF16), dht, dgt, ws, wsb, M, N,
+                                   O.BF16, O.BF16, _stream()) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(dht).reshape(-1), dres.reshape(-1))
+    assert not to_host(dgt).any()
+
+
+# ------------------------------------------------- the full-size workloads
+
+@pytest.mark.parametrize("w", G.WORKLOADS + G.EXTRA_WORKLOADS,
+                         ids=[w.name for w in G.WORKLOADS + G.EXTRA_WORKLOADS])
 def test_workload_full_size(w):
     """Each workload at full size, in the launch configuration the benchmark
     times, checked element by element against the oracle."""
@@ -345,6 +432,8 @@ def test_workload_full_size(w):
                 outlier_every=w.outlier_every, outlier_scale=w.outlier_scale)
     elif w.kind == "fused_add":
         run_fused(w.M, w.N, w.x_dt, w.g_dt, eps=w.eps, seed=w.seed, want_rstd=w.store_rstd)
+    elif w.kind == "fused_add_bwd":
+        run_fused_bwd(w.M, w.N, w.x_dt, w.g_dt, seed=w.seed)
     else:
         floor_only = run_bwd(w.M, w.N, w.x_dt, w.g_dt, seed=w.seed, eps=w.eps)
         _log(f"dx elements passing only by the cancellation floor: {floor_only}")

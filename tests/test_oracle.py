@@ -302,3 +302,60 @@ def test_backward_tolerance_magnitudes(gen_mod):
     np.testing.assert_allclose(b["a"], np.abs(dy * g * x).mean(axis=1), rtol=1e-14)
     np.testing.assert_allclose(b["s"], np.abs(dy * x * rho[:, None]).sum(axis=0), rtol=1e-14)
     np.testing.assert_allclose(b["c"], (dy * g * x).mean(axis=1), rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------------------------ fused-add backward
+
+def _fused_loss(x, r, g, dy, dres, M, N, eps):
+    h = x + r                                   # fp64 storage: exact sum
+    y = O.rmsnorm_fwd(h, g, M, N, eps, O.F64, O.F64)["y_exact"]
+    return float((dy * y).sum() + (dres * h).sum())
+
+
+def test_fused_add_backward_matches_finite_differences(gen_mod):
+    # L = sum dy * RMSNorm(x + r) + sum dres * (x + r): dL/dx = dL/dr = dh.
+    M, N, eps = 3, 8, float(np.float32(1e-3))
+    x = gen_mod.normal(16, 1, M, N, O.F64)
+    r = gen_mod.normal(16, 2, M, N, O.F64)
+    dy = gen_mod.normal(16, 3, M, N, O.F64)
+    dres = gen_mod.normal(16, 5, M, N, O.F64)
+    g = gen_mod.uniform(16, 4, N, 0.5, 1.5, O.F64)
+    h = x + r
+    rho = O.rmsnorm_fwd(h, g, M, N, eps, O.F64, O.F64)["rstd_exact"]
+    out = O.rmsnorm_fused_add_bwd(dy, h, rho, g, dres, M, N, O.F64, O.F64)
+    for which in ("x", "r"):
+        fd = np.zeros((M, N))
+        for i in range(M):
+            for j in range(N):
+                step = 1e-5 * max(1.0, abs(h[i, j]))
+                p, m = x.copy(), x.copy()
+                q, n = r.copy(), r.copy()
+                if which == "x":
+                    p[i, j] += step
+                    m[i, j] -= step
+                else:
+                    q[i, j] += step
+                    n[i, j] -= step
+                fd[i, j] = (_fused_loss(p, q, g, dy, dres, M, N, eps) -
+                            _fused_loss(m, n, g, dy, dres, M, N, eps)) / (2 * step)
+        scale = np.abs(fd).max(axis=1, keepdims=True)
+        assert np.all(np.abs(out["dx_exact"] - fd) <= 1e-7 * scale), which
+
+
+def test_fused_add_backward_reduces_to_plain_and_to_dres(gen_mod):
+    M, N = 5, 96
+    h = gen_mod.normal(17, 1, M, N, O.BF16)
+    dy = gen_mod.normal(17, 3, M, N, O.BF16)
+    dres = gen_mod.normal(17, 5, M, N, O.BF16)
+    g = gen_mod.uniform(17, 4, N, 0.5, 1.5, O.BF16)
+    rho = O.rmsnorm_fwd(h, g, M, N, 1e-5, O.BF16, O.BF16)["rstd"]
+    plain = O.rmsnorm_bwd(dy, h, rho, g, M, N, O.BF16, O.BF16)
+    none = O.rmsnorm_fused_add_bwd(dy, h, rho, g, None, M, N, O.BF16, O.BF16)
+    assert np.array_equal(none["dx"], plain["dx"]) and np.array_equal(none["dgamma"], plain["dgamma"])
+    both = O.rmsnorm_fused_add_bwd(dy, h, rho, g, dres, M, N, O.BF16, O.BF16)
+    np.testing.assert_allclose(both["dx_exact"], plain["dx_exact"] + O.decode(dres, O.BF16).reshape(M, N),
+                               rtol=0, atol=1e-12)
+    zero_dy = np.zeros_like(dy)
+    only = O.rmsnorm_fused_add_bwd(zero_dy, h, rho, g, dres, M, N, O.BF16, O.BF16)
+    assert np.array_equal(only["dx"], dres.reshape(M, N))    # RNE(dres) == dres
+    assert np.all(only["dgamma"] == 0)
