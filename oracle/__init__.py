@@ -6,8 +6,9 @@ may import this package; the library under ``row_wise_normalization_fwd_amd``
 never does. The arithmetic lives in ``oracle.cpp`` (which cites the passages it
 follows); this module only marshals numpy arrays.
 
-Storage arrays are numpy ``float32`` for fp32 data and ``uint16`` bit patterns
-for fp16 / bf16 data. Type codes: 0 = fp32, 1 = fp16, 2 = bf16; 3 = plain float64 storage, used by
+Storage arrays are numpy ``float32`` for fp32 data, ``uint16`` bit patterns
+for fp16 / bf16 data and ``uint8`` codes for fp8 e4m3 (OCP "fn"). Type codes:
+0 = fp32, 1 = fp16, 2 = bf16, 4 = fp8 e4m3; 3 = plain float64 storage, used by
 the oracle's own checks (finite differences need unrounded inputs).
 """
 
@@ -19,7 +20,8 @@ import subprocess
 
 import numpy as np
 
-F32, F16, BF16, F64 = 0, 1, 2, 3
+F32, F16, BF16, F64, E4M3 = 0, 1, 2, 3, 4
+QUANT_TENSOR, QUANT_ROW = 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
@@ -59,16 +61,18 @@ def _load():
                                        dp, vp, dp, dp, dp, dp]
     lib.oracle_rmsnorm_fused_add_bwd.argtypes = [vp, vp, dp, vp, vp, i64, i64, i32, i32,
                                                  dp, vp, dp, dp, dp, dp]
+    lib.oracle_rmsnorm_quant_fwd.argtypes = [vp, vp, vp, i64, i64, f32, i32, i32, i32, f32,
+                                             vp, vp, dp, dp, vp, vp]
     for fn in (lib.oracle_decode, lib.oracle_round, lib.oracle_rmsnorm_fwd,
                lib.oracle_rmsnorm_fused_add_fwd, lib.oracle_rmsnorm_bwd,
-               lib.oracle_rmsnorm_fused_add_bwd):
+               lib.oracle_rmsnorm_fused_add_bwd, lib.oracle_rmsnorm_quant_fwd):
         fn.restype = None
     _lib = lib
     return lib
 
 
 def storage_dtype(dt: int):
-    return {F32: np.float32, F64: np.float64}.get(dt, np.uint16)
+    return {F32: np.float32, F64: np.float64, E4M3: np.uint8}.get(dt, np.uint16)
 
 
 def _ptr(a):
@@ -172,3 +176,30 @@ def rmsnorm_fused_add_bwd(dy, h, rho, gamma, dres, M, N, x_dt, g_dt, want_exact=
                                          M, N, x_dt, g_dt, _ptr(dx_exact), _ptr(dx),
                                          _ptr(dgamma), _ptr(c), _ptr(a), _ptr(s))
     return dict(dx_exact=dx_exact, dx=dx, dgamma=dgamma, c=c, a=a, s=s)
+
+
+def rmsnorm_quant_fwd(x, gamma, M, N, eps, x_dt, g_dt, mode, scale=None, r=None,
+                      want_exact=True):
+    """Forward with an fp8 e4m3 output. mode QUANT_TENSOR divides by the given
+    ``scale`` (a float, taken as fp32); QUANT_ROW by amax_i / 448 per row.
+    ``r`` (optional) selects the fused residual add. Returns dict: q (M,N)
+    uint8 codes, q_exact (M,N) f64 y/s before rounding or None, scale (M,)
+    fp32, scale_exact (M,) f64, rstd (M,) fp32, h (M,N) storage or None."""
+    if mode not in (QUANT_TENSOR, QUANT_ROW):
+        raise ValueError("mode must be QUANT_TENSOR or QUANT_ROW")
+    if mode == QUANT_TENSOR and scale is None:
+        raise ValueError("QUANT_TENSOR needs a scale")
+    x = _check(x, x_dt, M * N, "x")
+    gamma = _check(gamma, g_dt, N, "gamma")
+    if r is not None:
+        r = _check(r, x_dt, M * N, "r")
+    out = {"q": np.empty((M, N), np.uint8),
+           "q_exact": np.empty((M, N), np.float64) if want_exact else None,
+           "scale": np.empty(M, np.float32), "scale_exact": np.empty(M, np.float64),
+           "rstd": np.empty(M, np.float32),
+           "h": np.empty((M, N), storage_dtype(x_dt)) if r is not None else None}
+    _load().oracle_rmsnorm_quant_fwd(
+        _ptr(x), _ptr(r), _ptr(gamma), M, N, eps, x_dt, g_dt, mode,
+        float(np.float32(scale if scale is not None else 0.0)), _ptr(out["h"]), _ptr(out["q"]),
+        _ptr(out["q_exact"]), _ptr(out["scale_exact"]), _ptr(out["scale"]), _ptr(out["rstd"]))
+    return out

@@ -29,6 +29,16 @@
 //     where rho_i is the rstd handed in.
 //   * Rounding to bf16 / fp16 / fp32: round to nearest, ties to even (the FlyDSL
 //     guide, section 1.1, states RNE for the bf16 pack; IEEE default otherwise).
+//   * Quantised output ("TIRx kernels", FlashInfer ports, flashinfer.norm:
+//     rmsnorm_quant and fused_add_rmsnorm_quant, named without a definition).
+//     Reading taken: the forward's value y is divided by a scale and rounded
+//     to fp8 e4m3 in the OCP "fn" encoding -- the format the pages use on gfx950
+//     (FlyDSL guide, section 3b, fp8 forward: e4m3fn, not fnuz) -- nearest,
+//     ties to even, with magnitudes beyond the largest finite value 448
+//     saturated to 448 (the format has no infinity). The scale is either one
+//     caller-given value for the whole tensor or, per row, amax_i / 448 with
+//     amax_i = max_j |y_ij|, so that the largest element of each row maps to
+//     +-448; a row with amax 0 gets scale 0 and all-zero codes.
 //
 // Sums run sequentially in index order in double precision.
 
@@ -44,6 +54,7 @@ constexpr int kF32 = 0;
 constexpr int kF16 = 1;
 constexpr int kBF16 = 2;
 constexpr int kF64 = 3;  // plain double storage, used only by the oracle's own checks
+constexpr int kE4M3 = 4; // fp8 e4m3, OCP "fn" encoding (bias 7, no infinity, 448 max)
 
 struct Format {
   int frac_bits;      // stored fraction bits
@@ -55,6 +66,7 @@ Format format_of(int dt) {
   switch (dt) {
     case kF32:  return {23, -126, std::ldexp(2.0 - std::ldexp(1.0, -23), 127)};
     case kF16:  return {10, -14, 65504.0};
+    case kE4M3: return {3, -6, 448.0};
     default:    return {7, -126, std::ldexp(2.0 - std::ldexp(1.0, -7), 127)};
   }
 }
@@ -70,6 +82,17 @@ double decode(const void* base, int64_t idx, int dt) {
     float f;
     std::memcpy(&f, static_cast<const char*>(base) + 4 * idx, 4);
     return f;
+  }
+  if (dt == kE4M3) {
+    // 1 sign, 4 exponent (bias 7), 3 fraction bits; exponent 15 with fraction
+    // 7 is NaN, every other pattern is finite.
+    uint8_t b = static_cast<const uint8_t*>(base)[idx];
+    int sign = b >> 7, e = (b >> 3) & 0xf, m = b & 0x7;
+    double v;
+    if (e == 15 && m == 7) v = NAN;
+    else if (e == 0) v = std::ldexp(static_cast<double>(m), -9);
+    else v = std::ldexp(static_cast<double>(8 + m), e - 10);
+    return sign ? -v : v;
   }
   uint16_t b;
   std::memcpy(&b, static_cast<const char*>(base) + 2 * idx, 2);
@@ -91,6 +114,7 @@ double decode(const void* base, int64_t idx, int dt) {
 
 // Round v to the nearest value of format dt, ties to even; overflow gives inf.
 double round_to(double v, int dt) {
+  if (dt == kE4M3 && std::isinf(v)) return std::copysign(448.0, v);  // saturates too
   if (dt == kF64 || v == 0.0 || !std::isfinite(v)) return v;
   Format f = format_of(dt);
   int e;
@@ -99,7 +123,8 @@ double round_to(double v, int dt) {
   if (lead < f.min_exp) lead = f.min_exp;  // subnormals share one quantum
   double quantum = std::ldexp(1.0, lead - f.frac_bits);
   double r = std::nearbyint(v / quantum) * quantum;  // default mode: ties to even
-  if (std::fabs(r) > f.max_finite) r = std::copysign(INFINITY, v);
+  if (std::fabs(r) > f.max_finite)  // e4m3fn has no infinity: saturate
+    r = dt == kE4M3 ? std::copysign(f.max_finite, v) : std::copysign(INFINITY, v);
   return r;
 }
 
@@ -110,6 +135,18 @@ uint32_t encode(double r, int dt) {
     uint32_t u;
     std::memcpy(&u, &f, 4);
     return dt == kF32 ? u : (u >> 16);
+  }
+  if (dt == kE4M3) {
+    uint32_t sign = std::signbit(r) ? 0x80u : 0u;
+    double a = std::fabs(r);
+    if (std::isnan(r)) return 0x7fu;
+    if (a < std::ldexp(1.0, -6))  // subnormal (or zero): units of 2^-9
+      return sign | static_cast<uint32_t>(a * std::ldexp(1.0, 9));
+    int e;
+    std::frexp(a, &e);
+    int lead = e - 1;
+    uint32_t frac = static_cast<uint32_t>(std::ldexp(a, 3 - lead)) - 8u;
+    return sign | (static_cast<uint32_t>(lead + 7) << 3) | frac;
   }
   uint32_t sign = std::signbit(r) ? 0x8000u : 0u;
   double a = std::fabs(r);
@@ -128,6 +165,8 @@ void store_bits(void* base, int64_t idx, uint32_t bits, int dt) {
   if (dt == kF64) return;  // doubles are stored by store_value
   if (dt == kF32) {
     std::memcpy(static_cast<char*>(base) + 4 * idx, &bits, 4);
+  } else if (dt == kE4M3) {
+    static_cast<uint8_t*>(base)[idx] = static_cast<uint8_t>(bits);
   } else {
     uint16_t b = static_cast<uint16_t>(bits);
     std::memcpy(static_cast<char*>(base) + 2 * idx, &b, 2);
@@ -263,6 +302,50 @@ void oracle_rmsnorm_bwd(const void* dy, const void* x, const double* rho,
                         double* dgamma, double* c, double* a, double* s) {
   oracle_rmsnorm_fused_add_bwd(dy, x, rho, gamma, nullptr, M, N, x_dt, g_dt, dx_exact,
                                dx_bits, dgamma, c, a, s);
+}
+
+// RMSNorm forward (optionally after the fused residual add, when r is not
+// null) with an fp8 e4m3 output instead of the activation-type y:
+//   mode 1 (per tensor): s = scale_in for every row;
+//   mode 2 (per row):    s_i = max_j |y_ij| / 448,
+//   q_ij = e4m3(y_ij / s_i)   (nearest, ties to even, saturated at +-448;
+//                              a row with s_i = 0 gets all-zero codes),
+// where y_ij is the forward's double value (before any output rounding).
+// Outputs, each optional: h_bits[M*N] (fused: the rounded sum, format x_dt),
+// q[M*N] the fp8 codes, q_exact[M*N] the value y/s before the fp8 rounding,
+// scale_exact[M] s_i in double, scale_f32[M] s_i rounded to fp32, rstd_f32[M].
+void oracle_rmsnorm_quant_fwd(const void* x, const void* r, const void* gamma, int64_t M,
+                              int64_t N, float eps, int x_dt, int g_dt, int mode,
+                              float scale_in, void* h_bits, uint8_t* q, double* q_exact,
+                              double* scale_exact, float* scale_f32, float* rstd_f32) {
+  std::vector<double> v(static_cast<size_t>(N)), y(static_cast<size_t>(N));
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t j = 0; j < N; ++j) {
+      double xv = decode(x, i * N + j, x_dt);
+      if (r) {
+        xv = round_to(xv + decode(r, i * N + j, x_dt), x_dt);
+        if (h_bits) store_value(h_bits, i * N + j, xv, x_dt);
+      }
+      v[j] = xv;
+    }
+    float rs;
+    forward_row(v.data(), gamma, N, eps, x_dt, g_dt, 0, y.data(), nullptr, nullptr, &rs,
+                nullptr);
+    if (rstd_f32) rstd_f32[i] = rs;
+    double s = scale_in;
+    if (mode == 2) {
+      double amax = 0.0;
+      for (int64_t j = 0; j < N; ++j) amax = std::fmax(amax, std::fabs(y[j]));
+      s = amax / 448.0;
+    }
+    if (scale_exact) scale_exact[i] = s;
+    if (scale_f32) scale_f32[i] = static_cast<float>(round_to(s, kF32));
+    for (int64_t j = 0; j < N; ++j) {
+      double t = s == 0.0 ? 0.0 : y[j] / s;
+      if (q_exact) q_exact[i * N + j] = t;
+      if (q) store_value(q, i * N + j, t, kE4M3);
+    }
+  }
 }
 
 }  // extern "C"

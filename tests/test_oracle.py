@@ -359,3 +359,115 @@ def test_fused_add_backward_reduces_to_plain_and_to_dres(gen_mod):
     only = O.rmsnorm_fused_add_bwd(zero_dy, h, rho, g, dres, M, N, O.BF16, O.BF16)
     assert np.array_equal(only["dx"], dres.reshape(M, N))    # RNE(dres) == dres
     assert np.all(only["dgamma"] == 0)
+
+
+# ------------------------------------------------------ fp8 e4m3 quantised output
+
+def _e4m3_torch(v32: np.ndarray) -> np.ndarray:
+    """torch's float32 -> float8_e4m3fn conversion (nearest, ties to even; it
+    gives NaN instead of saturating beyond 464)."""
+    return torch.from_numpy(np.ascontiguousarray(v32, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _e4m3_saturating(v: np.ndarray) -> np.ndarray:
+    """torch's conversion where it is defined (|v| <= 464), +-448 beyond."""
+    v = np.asarray(v, np.float64)
+    big = np.abs(v) > 464.0
+    out = _e4m3_torch(np.where(big, 0.0, v))
+    out[big] = np.where(v[big] < 0, 0xfe, 0x7e)
+    return out
+
+
+def _e4m3_all_finite():
+    codes = np.arange(0, 0x7f, dtype=np.uint8)          # 0x7f is NaN
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    return codes, vals
+
+
+def test_decode_all_e4m3_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.decode(codes, O.E4M3)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2   # 0x7f, 0xff
+    assert np.array_equal(got[~nan], want[~nan])
+    assert got[0x7e] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+
+
+def test_round_e4m3_matches_torch_and_saturates():
+    _, vals = _e4m3_all_finite()
+    mids = (vals[:-1] + vals[1:]) / 2                   # every tie between neighbours
+    q1 = vals[:-1] + (vals[1:] - vals[:-1]) / 4
+    q3 = vals[:-1] + 3 * (vals[1:] - vals[:-1]) / 4
+    rng = np.random.default_rng(4)
+    rand = rng.standard_normal(20000) * 2.0 ** rng.integers(-12, 8, 20000)
+    edge = np.array([448.0, 456.0, 460.0, 463.99, 464.0, 2.0 ** -10, 3 * 2.0 ** -11,
+                     2.0 ** -6 - 2.0 ** -10, 2.0 ** -6 - 2.0 ** -11])
+    v = np.concatenate([vals, -vals, mids, -mids, q1, q3, rand, edge, -edge])
+    v = v[np.abs(v) <= 464.0].astype(np.float32).astype(np.float64)   # torch's range
+    assert np.array_equal(O.round_to(v, O.E4M3), _e4m3_torch(v))
+    # Beyond 464 torch gives NaN; the quantiser saturates at +-448 instead.
+    big = np.array([464.5, 500.0, 1e6, 1e300, np.inf])
+    assert np.all(O.round_to(big, O.E4M3) == 0x7e)
+    assert np.all(O.round_to(-big, O.E4M3) == 0xfe)
+    assert O.round_to(np.array([np.nan]), O.E4M3)[0] & 0x7f == 0x7f
+
+
+def test_quant_tensor_scale_on_exact_rows():
+    # A constant row c = 2^k with eps = 0 has rstd = 1/|c| exactly, so y_j is
+    # sign(c) * gamma_j exactly; with a power-of-two scale s the code must be
+    # the e4m3 rounding of sign(c) * gamma_j / s. gamma (fp32) holds every
+    # e4m3 value, tie and quarter point.
+    _, vals = _e4m3_all_finite()
+    mids = (vals[:-1] + vals[1:]) / 2
+    q1 = vals[:-1] + (vals[1:] - vals[:-1]) / 4
+    g = np.concatenate([vals, mids, q1, [456.0, 463.0, 464.0]]).astype(np.float32)
+    N = g.size
+    for c, s in ((1.0, 1.0), (-4.0, 1.0), (0.5, 0.125), (2.0, 4.0)):
+        x = O.round_to(np.full((2, N), c), O.BF16)
+        out = O.rmsnorm_quant_fwd(x, g, 2, N, 0.0, O.BF16, O.F32, O.QUANT_TENSOR, scale=s)
+        want = _e4m3_saturating(np.sign(c) * g.astype(np.float64) / s)
+        assert np.array_equal(out["q"][0], want) and np.array_equal(out["q"][1], want), (c, s)
+        assert np.all(out["scale"] == np.float32(s))
+
+
+def test_quant_row_scale_maps_each_row_max_to_448(gen_mod):
+    M, N = 40, 300
+    x = gen_mod.normal(31, 1, M, N, O.BF16, 50.0, 7)
+    xs = O.decode(x, O.BF16).reshape(M, N)
+    xs[3] = -np.abs(xs[3])                              # a row whose extreme is negative
+    x = O.round_to(xs, O.BF16)
+    g = gen_mod.uniform(31, 4, N, -1.5, 1.5, O.BF16)    # signed weights
+    fwd = O.rmsnorm_fwd(x, g, M, N, 1e-5, O.BF16, O.BF16)
+    out = O.rmsnorm_quant_fwd(x, g, M, N, 1e-5, O.BF16, O.BF16, O.QUANT_ROW)
+    y = fwd["y_exact"]
+    s = np.abs(y).max(axis=1) / 448.0
+    np.testing.assert_allclose(out["scale_exact"], s, rtol=1e-15, atol=0)
+    assert np.array_equal(out["scale"], s.astype(np.float32))
+    assert np.array_equal(out["rstd"], fwd["rstd"])
+    deq = O.decode(out["q"], O.E4M3).reshape(M, N)
+    assert np.all(np.abs(deq).max(axis=1) == 448.0)
+    # Each code is the nearest e4m3 value of y/s: within half a step.
+    t = y / s[:, None]
+    step = np.exp2(np.maximum(np.floor(np.log2(np.maximum(np.abs(t), 2.0 ** -30))), -6) - 3)
+    assert np.all(np.abs(deq - t) <= step / 2 + 1e-12)
+    assert np.all(np.sign(deq[deq != 0]) == np.sign(t[deq != 0]))
+
+
+def test_quant_fused_and_zero_rows(gen_mod):
+    M, N = 6, 64
+    x = gen_mod.normal(32, 1, M, N, O.F16)
+    r = gen_mod.normal(32, 2, M, N, O.F16)
+    g = gen_mod.uniform(32, 4, N, 0.5, 1.5, O.F32)
+    ref = O.rmsnorm_fused_add_fwd(x, r, g, M, N, 1e-6, O.F16, O.F32)
+    out = O.rmsnorm_quant_fwd(x, g, M, N, 1e-6, O.F16, O.F32, O.QUANT_ROW, r=r)
+    assert np.array_equal(out["h"], ref["h"])
+    np.testing.assert_allclose(out["q_exact"] * out["scale_exact"][:, None], ref["y_exact"],
+                               rtol=1e-14, atol=0)
+    tq = O.rmsnorm_quant_fwd(x, g, M, N, 1e-6, O.F16, O.F32, O.QUANT_TENSOR, scale=0.01, r=r)
+    np.testing.assert_allclose(tq["q_exact"], ref["y_exact"] / np.float64(np.float32(0.01)),
+                               rtol=1e-14, atol=0)
+    # Zero weights give zero rows: scale 0 and zero codes in the per-row mode.
+    z = O.rmsnorm_quant_fwd(x, np.zeros(N, np.float32), M, N, 1e-6, O.F16, O.F32, O.QUANT_ROW)
+    assert np.all(z["scale"] == 0) and np.all(z["q"] & 0x7f == 0)
