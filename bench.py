@@ -21,7 +21,8 @@ Also reported, in the same JSON line:
                 full passes of the same batch for about --cpu-seconds;
   workloads     the other four workloads (fp32 short rows, fused residual add,
                 backward, fp16 ragged rows) and the fused-add backward, timed
-                the same way;
+                the same way, and the fp8-output forward (per-row scales at
+                the headline shape; one scale after the fused add);
   calibration   a plain device-to-device copy of the step's byte count.
 """
 
@@ -48,6 +49,8 @@ DOMINANT_KERNEL = {
     "bwd_bf16_m8192_n8192": "bwd_stage1_kernel",
     "fwd_f16_m32768_n5000_outliers": "fwd_reg_kernel",
     "fusedadd_bwd_bf16_m8192_n8192": "bwd_stage1_kernel",
+    "fwd_fp8row_bf16_m4096_n8192": "fwd_pp_kernel",
+    "fusedadd_fp8tensor_bf16_m16384_n4096_gf32": "fwd_reg_kernel",
 }
 DT_NAMES = {0: "f32", 1: "f16", 2: "bf16"}
 
@@ -85,7 +88,8 @@ class Runner:
 
         big = M * N * w.esize
         per_replica = {"fwd": 2 * big, "fused_add": 3 * big, "bwd": 3 * big,
-                       "fused_add_bwd": 4 * big}[w.kind]
+                       "fused_add_bwd": 4 * big,
+                       "quant": (2 if w.fused_quant else 1) * big + M * N}[w.kind]
         self.replicas = max(1, int(-(-rotate_bytes // per_replica))) if rotate_bytes > 0 else 1
         x0 = dev_copy(host_inputs["x"], w.x_dt)
         g = dev_copy(host_inputs["gamma"], w.g_dt)
@@ -106,8 +110,10 @@ class Runner:
             self.ws_bytes = R.rmsnorm_bwd_workspace_size(M, N, w.x_dt)
         if w.kind == "fused_add_bwd":
             dres0 = dev_copy(host_inputs["dres"], w.x_dt)
-        if w.kind == "fused_add":
+        if w.kind == "fused_add" or (w.kind == "quant" and w.fused_quant):
             r0 = dev_copy(host_inputs["r"], w.x_dt)
+        if w.kind == "quant" and w.quant_mode == 1:
+            self.tensor_scale = torch.tensor([w.tensor_scale], dtype=torch.float32, device=dev)
         for i in range(self.replicas):
             s = {"x": x0 if i == 0 else x0.clone()}
             if w.kind == "fwd":
@@ -116,6 +122,12 @@ class Runner:
             elif w.kind == "fused_add":
                 s["r"] = r0 if i == 0 else r0.clone()
                 s["y"] = torch.empty_like(x0)
+                s["rstd"] = torch.empty(M, dtype=torch.float32, device=dev) if w.store_rstd else None
+            elif w.kind == "quant":
+                s["r"] = (r0 if i == 0 else r0.clone()) if w.fused_quant else None
+                s["q"] = torch.empty(M * N, dtype=torch.uint8, device=dev)
+                s["scale"] = (self.tensor_scale if w.quant_mode == 1 else
+                              torch.empty(M, dtype=torch.float32, device=dev))
                 s["rstd"] = torch.empty(M, dtype=torch.float32, device=dev) if w.store_rstd else None
             else:
                 s["dy"] = dy0 if i == 0 else dy0.clone()
@@ -140,6 +152,10 @@ class Runner:
                 args = (p["x"], p["r"], g.data_ptr(), p["y"], p["rstd"], M, N, w.eps, w.x_dt,
                         w.g_dt, self.stream_handle)
                 self.calls.append((lib.rmsnorm_fused_add_fwd, args))
+            elif w.kind == "quant":
+                args = (p["x"], p["r"], g.data_ptr(), p["q"], p["scale"], w.quant_mode, p["rstd"],
+                        M, N, w.eps, w.x_dt, w.g_dt, self.stream_handle)
+                self.calls.append((lib.rmsnorm_quant_fwd, args))
             elif w.kind == "bwd":
                 args = (p["dy"], p["x"], p["rstd"], g.data_ptr(), p["dx"], p["dgamma"], p["ws"],
                         self.ws_bytes, M, N, w.x_dt, w.g_dt, self.stream_handle)
@@ -212,6 +228,10 @@ def cpu_baseline(w, host_inputs: dict, seconds: float) -> dict:
         def one_pass():
             O.rmsnorm_fused_add_fwd(x, host_inputs["r"], g, M, N, w.eps, w.x_dt, w.g_dt,
                                     want_exact=False)
+    elif w.kind == "quant":
+        def one_pass():
+            O.rmsnorm_quant_fwd(x, g, M, N, w.eps, w.x_dt, w.g_dt, w.quant_mode,
+                                scale=w.tensor_scale, r=host_inputs.get("r"), want_exact=False)
     else:
         # The saved rstd is an input of the backward, made outside the timing.
         rho = O.rmsnorm_fwd(x, g, M, N, w.eps, w.x_dt, w.g_dt, want_exact=False)["rstd"]

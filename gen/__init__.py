@@ -108,7 +108,7 @@ def raw_bits(seed: int, stream: int, n: int) -> np.ndarray:
 class Workload:
     """One benchmark / parity workload."""
     name: str
-    kind: str            # "fwd", "fused_add", "bwd", "fused_add_bwd"
+    kind: str            # "fwd", "fused_add", "bwd", "fused_add_bwd", "quant"
     M: int
     N: int
     x_dt: int
@@ -118,6 +118,9 @@ class Workload:
     store_rstd: bool = False
     outlier_every: int = 0      # rows i with i % outlier_every == 0 are scaled
     outlier_scale: float = 1.0
+    quant_mode: int = 0         # "quant": 1 = one tensor scale, 2 = per-row scales
+    fused_quant: bool = False   # "quant": fused residual add first
+    tensor_scale: float = 0.0125  # "quant", one tensor scale: |y| > 5.6 saturates
 
     @property
     def esize(self) -> int:
@@ -135,6 +138,13 @@ class Workload:
             return 2 * big + g + (4 * self.M if self.store_rstd else 0)
         if self.kind == "fused_add":
             return 4 * big + g + (4 * self.M if self.store_rstd else 0)
+        if self.kind == "quant":
+            # read x (and r, writing h), write the fp8 codes (1 byte each),
+            # per-row scales (read one scale per tensor).
+            n = self.M * self.N
+            extra = 4 * self.M if self.quant_mode == 2 else 4
+            io = big + (2 * big if self.fused_quant else 0) + n
+            return io + g + extra + (4 * self.M if self.store_rstd else 0)
         if self.kind == "fused_add_bwd":
             # read h, dy, dresidual, rstd, gamma; write dh, dgamma (fp32)
             return 4 * big + 4 * self.M + g + 4 * self.N
@@ -157,8 +167,14 @@ WORKLOADS = [
 ]
 # Workloads of the operations beyond the five: the fused-add backward at the
 # backward's shape (h in place of x, plus the residual stream's gradient).
+# The quantised forward (fp8 e4m3 output) at the headline shape with per-row
+# scales, and after the fused add at the fused workload's shape with one scale.
 EXTRA_WORKLOADS = [
     Workload("fusedadd_bwd_bf16_m8192_n8192", "fused_add_bwd", 8192, 8192, BF16, BF16, 1e-5, 1006),
+    Workload("fwd_fp8row_bf16_m4096_n8192", "quant", 4096, 8192, BF16, BF16, 1e-5, 1007,
+             quant_mode=2),
+    Workload("fusedadd_fp8tensor_bf16_m16384_n4096_gf32", "quant", 16384, 4096, BF16, F32, 1e-5,
+             1008, quant_mode=1, fused_quant=True),
 ]
 WORKLOADS_BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
@@ -170,7 +186,7 @@ def make_inputs(w: Workload, nthreads: int | None = None) -> dict:
     out = {"x": normal(w.seed, STREAM_X, w.M, w.N, w.x_dt, w.outlier_scale, w.outlier_every,
                        nthreads=nthreads),
            "gamma": uniform(w.seed, STREAM_GAMMA, w.N, 0.5, 1.5, w.g_dt, nthreads=nthreads)}
-    if w.kind == "fused_add":
+    if w.kind == "fused_add" or (w.kind == "quant" and w.fused_quant):
         out["r"] = normal(w.seed, STREAM_R, w.M, w.N, w.x_dt, nthreads=nthreads)
     if w.kind in ("bwd", "fused_add_bwd"):
         out["dy"] = normal(w.seed, STREAM_DY, w.M, w.N, w.x_dt, nthreads=nthreads)

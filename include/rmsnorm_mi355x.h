@@ -55,6 +55,7 @@ typedef enum {
   RMSN_ERR_OVERLAP = -5,    /* buffers overlap in a way the call forbids */
   RMSN_ERR_ALIGN = -6,      /* a pointer is not aligned to its element size */
   RMSN_ERR_EPS = -7,        /* eps negative or not finite */
+  RMSN_ERR_MODE = -8,       /* unknown quantisation mode */
   RMSN_ERR_HIP = -100       /* a kernel launch failed; see rmsnorm_last_hip_error */
 } rmsn_status;
 
@@ -86,6 +87,37 @@ int rmsnorm_fwd(const void* x, const void* gamma, void* y, float* rstd,
 int rmsnorm_fused_add_fwd(const void* x, void* residual, const void* gamma, void* y,
                           float* rstd, int64_t M, int64_t N, float eps, int x_dtype,
                           int gamma_dtype, hipStream_t stream);
+
+/* Scale modes of rmsnorm_quant_fwd. */
+typedef enum {
+  RMSN_QUANT_FP8_TENSOR = 1, /* one caller scale for the whole tensor, read */
+  RMSN_QUANT_FP8_ROW = 2     /* one scale per row, computed and written */
+} rmsn_quant_mode;
+
+/* Forward RMSNorm (optionally after the fused residual add) with an fp8
+ * output: the RMSNorm value y (fp32, never rounded to the activation type)
+ * is divided by a scale s and rounded to fp8 e4m3 in the OCP "fn" encoding
+ * (1 sign, 4 exponent bits with bias 7, 3 fraction bits, no infinity; the
+ * format the FlyDSL guide, section 3b, uses on gfx950), nearest-even, with
+ * magnitudes beyond 448 saturated to +-448. The pages name these variants
+ * ("TIRx kernels", FlashInfer ports, flashinfer.norm: rmsnorm_quant,
+ * fused_add_rmsnorm_quant) without defining them; this is the reading taken.
+ *   x, residual, gamma, rstd, eps as in rmsnorm_fwd / rmsnorm_fused_add_fwd;
+ *             residual may be NULL (plain forward) or is read as r and
+ *             overwritten with h = round(x + r), and h is normalised.
+ *   q         [M, N] bytes of e4m3 codes, written; overlaps nothing else.
+ *   scale     RMSN_QUANT_FP8_TENSOR: [1] fp32, read on the device: s, which
+ *             must be positive and finite (q = e4m3(y / s)).
+ *             RMSN_QUANT_FP8_ROW: [M] fp32, written with s_i = amax_i / 448,
+ *             amax_i = max_j |y_ij|, so each row's largest element maps to
+ *             +-448 (dequantise with q * s_i); a row with amax 0 gets s = 0 and
+ *             zero codes. Rows holding inf or NaN give unspecified codes.
+ * The kernel multiplies y by 1/s (per tensor) or 448/amax (per row) in fp32,
+ * so a code may differ from the exactly rounded one by one step where y / s
+ * lies within fp32 rounding of a tie. */
+int rmsnorm_quant_fwd(const void* x, void* residual, const void* gamma, void* q,
+                      float* scale, int quant_mode, float* rstd, int64_t M, int64_t N,
+                      float eps, int x_dtype, int gamma_dtype, hipStream_t stream);
 
 /* Bytes of device workspace rmsnorm_bwd needs for an [M, N] problem of the
  * given activation dtype: fp32 per-workgroup dgamma partials (and per-row

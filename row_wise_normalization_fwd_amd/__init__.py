@@ -2,12 +2,13 @@
 
 The C ABI (include/rmsnorm_mi355x.h) is exposed under the same names
 (``rmsnorm_fwd``, ``rmsnorm_fused_add_fwd``, ``rmsnorm_bwd``,
-``rmsnorm_fused_add_bwd``, ``rmsnorm_bwd_workspace_size``, ``rmsnorm_status_string``,
+``rmsnorm_fused_add_bwd``, ``rmsnorm_quant_fwd``, ``rmsnorm_bwd_workspace_size``,
+``rmsnorm_status_string``,
 ``rmsnorm_last_hip_error``); those functions only marshal arguments. Pointers
 may be given as integers or as torch tensors (their ``data_ptr()``); streams as
 integers or ``torch.cuda.Stream`` objects.
 
-``fwd``, ``fused_add_fwd``, ``bwd`` and ``fused_add_bwd`` are torch conveniences on top: they use
+``fwd``, ``fused_add_fwd``, ``quant_fwd``, ``bwd`` and ``fused_add_bwd`` are torch conveniences on top: they use
 torch only to allocate outputs and to pick the current stream, and every step
 of the computation runs in the library's HIP kernels. There is no fallback: if
 the library is not built, every call raises.
@@ -23,14 +24,16 @@ LIB_NAME = "librmsnorm_mi355x.so"
 LIB_PATH = os.path.join(_HERE, LIB_NAME)
 
 RMSN_F32, RMSN_F16, RMSN_BF16 = 0, 1, 2
+RMSN_QUANT_FP8_TENSOR, RMSN_QUANT_FP8_ROW = 1, 2
 RMSN_OK = 0
 STATUS_NAMES = {
     0: "RMSN_OK", -1: "RMSN_ERR_NULL", -2: "RMSN_ERR_SHAPE", -3: "RMSN_ERR_DTYPE",
     -4: "RMSN_ERR_WORKSPACE", -5: "RMSN_ERR_OVERLAP", -6: "RMSN_ERR_ALIGN",
-    -7: "RMSN_ERR_EPS", -100: "RMSN_ERR_HIP",
+    -7: "RMSN_ERR_EPS", -8: "RMSN_ERR_MODE", -100: "RMSN_ERR_HIP",
 }
-ENTRY_POINTS = ("rmsnorm_fwd", "rmsnorm_fused_add_fwd", "rmsnorm_bwd", "rmsnorm_fused_add_bwd",
-                "rmsnorm_bwd_workspace_size", "rmsnorm_status_string", "rmsnorm_last_hip_error")
+ENTRY_POINTS = ("rmsnorm_fwd", "rmsnorm_fused_add_fwd", "rmsnorm_quant_fwd", "rmsnorm_bwd",
+                "rmsnorm_fused_add_bwd", "rmsnorm_bwd_workspace_size", "rmsnorm_status_string",
+                "rmsnorm_last_hip_error")
 
 
 class RMSNormError(RuntimeError):
@@ -62,6 +65,8 @@ def load_library(path: str | None = None):
     lib.rmsnorm_fwd.restype = i32
     lib.rmsnorm_fused_add_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
     lib.rmsnorm_fused_add_fwd.restype = i32
+    lib.rmsnorm_quant_fwd.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, i64, f32, i32, i32, vp]
+    lib.rmsnorm_quant_fwd.restype = i32
     lib.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i32]
     lib.rmsnorm_bwd_workspace_size.restype = ctypes.c_size_t
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i32, i32, vp]
@@ -106,6 +111,13 @@ def rmsnorm_fused_add_fwd(x, residual, gamma, y, rstd, M, N, eps, x_dtype, gamma
                           stream) -> int:
     return load_library().rmsnorm_fused_add_fwd(_p(x), _p(residual), _p(gamma), _p(y), _p(rstd),
                                                 M, N, eps, x_dtype, gamma_dtype, _s(stream))
+
+
+def rmsnorm_quant_fwd(x, residual, gamma, q, scale, quant_mode, rstd, M, N, eps, x_dtype,
+                      gamma_dtype, stream) -> int:
+    return load_library().rmsnorm_quant_fwd(_p(x), _p(residual), _p(gamma), _p(q), _p(scale),
+                                            quant_mode, _p(rstd), M, N, eps, x_dtype,
+                                            gamma_dtype, _s(stream))
 
 
 def rmsnorm_bwd_workspace_size(M, N, x_dtype) -> int:
@@ -188,6 +200,29 @@ def fused_add_fwd(x, residual, gamma, eps: float = 1e-5, *, want_rstd: bool = Fa
     _check(rmsnorm_fused_add_fwd(x, residual, gamma, y, rstd, M, N, eps, dtype_code(x),
                                  dtype_code(gamma), stream), "rmsnorm_fused_add_fwd")
     return y, rstd
+
+
+def quant_fwd(x, gamma, eps: float = 1e-5, *, scale=None, residual=None, want_rstd: bool = False,
+              out=None, rstd=None, stream=None):
+    """fp8 e4m3 output. With ``scale`` (a 1-element fp32 device tensor) every
+    row uses it; without, per-row scales are computed and returned. With
+    ``residual`` the fused add runs first (residual <- x + residual).
+    Returns (q as torch.uint8 codes, scale, rstd or None)."""
+    import torch
+    N = gamma.numel()
+    M = _rows(x, N)
+    if residual is not None and (residual.shape != x.shape or residual.dtype != x.dtype):
+        raise ValueError("residual must match x in shape and dtype")
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    mode = RMSN_QUANT_FP8_TENSOR if scale is not None else RMSN_QUANT_FP8_ROW
+    if scale is None:
+        scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    if want_rstd and rstd is None:
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    stream = torch.cuda.current_stream(x.device) if stream is None else stream
+    _check(rmsnorm_quant_fwd(x, residual, gamma, q, scale, mode, rstd, M, N, eps, dtype_code(x),
+                             dtype_code(gamma), stream), "rmsnorm_quant_fwd")
+    return q, scale, rstd
 
 
 def bwd(dy, x, rstd, gamma, *, dx=None, dgamma=None, workspace=None, stream=None):

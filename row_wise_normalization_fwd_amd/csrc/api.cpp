@@ -89,6 +89,48 @@ int forward(bool fused, const void* x, void* residual, const void* gamma, void* 
   return finish(launch_forward(c, x_dtype));
 }
 
+// Validation of the quantised forward (fp8 output, optional fused add).
+int quant_forward(const void* x, void* residual, const void* gamma, void* q, float* scale,
+                  int mode, float* rstd, int64_t M, int64_t N, float eps, int x_dtype,
+                  int gamma_dtype, hipStream_t stream) {
+  if (!valid_pair(x_dtype, gamma_dtype)) return RMSN_ERR_DTYPE;
+  if (!shape_ok(M, N)) return RMSN_ERR_SHAPE;
+  if (!std::isfinite(eps) || eps < 0.0f) return RMSN_ERR_EPS;
+  if (mode != RMSN_QUANT_FP8_TENSOR && mode != RMSN_QUANT_FP8_ROW) return RMSN_ERR_MODE;
+  if (M == 0) return RMSN_OK;
+  if (!x || !gamma || !q || !scale) return RMSN_ERR_NULL;
+  const int es = esize_of(x_dtype), gs = esize_of(gamma_dtype);
+  if (!aligned(x, es) || !aligned(gamma, gs) || !aligned(scale, 4) ||
+      (rstd && !aligned(rstd, 4)) || (residual && !aligned(residual, es)))
+    return RMSN_ERR_ALIGN;
+  const uint64_t big = static_cast<uint64_t>(M) * static_cast<uint64_t>(N) * es;
+  const bool per_row = mode == RMSN_QUANT_FP8_ROW;
+  const Range rx = span(x, big), rg = span(gamma, static_cast<uint64_t>(N) * gs);
+  const Range rq = span(q, static_cast<uint64_t>(M) * static_cast<uint64_t>(N));
+  const Range rsc = span(scale, per_row ? static_cast<uint64_t>(M) * 4 : 4);
+  // q and the written buffers (residual, rstd, per-row scales) overlap nothing.
+  if (overlap(rq, rx) || overlap(rq, rg) || overlap(rq, rsc)) return RMSN_ERR_OVERLAP;
+  if (per_row && (overlap(rsc, rx) || overlap(rsc, rg))) return RMSN_ERR_OVERLAP;
+  if (rstd) {
+    const Range rr = span(rstd, static_cast<uint64_t>(M) * 4);
+    if (overlap(rr, rx) || overlap(rr, rg) || overlap(rr, rq) || overlap(rr, rsc))
+      return RMSN_ERR_OVERLAP;
+    if (residual && overlap(rr, span(residual, big))) return RMSN_ERR_OVERLAP;
+  }
+  if (residual) {
+    const Range rs = span(residual, big);
+    if (partial_overlap(rs, rx) || overlap(rs, rg) || overlap(rs, rq) || overlap(rs, rsc))
+      return RMSN_ERR_OVERLAP;
+  }
+  rmsn::FwdCall c{x, residual, gamma, nullptr, rstd, M, N, eps, gamma_dtype, stream,
+                  q, scale, mode};
+  switch (x_dtype) {
+    case RMSN_F32: return finish(rmsn::launch_fwd_quant_f32(c));
+    case RMSN_F16: return finish(rmsn::launch_fwd_quant_f16(c));
+    default: return finish(rmsn::launch_fwd_quant_bf16(c));
+  }
+}
+
 }  // namespace
 
 namespace rmsn {
@@ -208,6 +250,13 @@ int rmsnorm_fused_add_fwd(const void* x, void* residual, const void* gamma, void
   return forward(true, x, residual, gamma, y, rstd, M, N, eps, x_dtype, gamma_dtype, stream);
 }
 
+int rmsnorm_quant_fwd(const void* x, void* residual, const void* gamma, void* q, float* scale,
+                      int quant_mode, float* rstd, int64_t M, int64_t N, float eps, int x_dtype,
+                      int gamma_dtype, hipStream_t stream) {
+  return quant_forward(x, residual, gamma, q, scale, quant_mode, rstd, M, N, eps, x_dtype,
+                       gamma_dtype, stream);
+}
+
 size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int x_dtype) {
   return rmsn::plan_bwd(M, N, x_dtype).workspace_bytes;
 }
@@ -237,6 +286,7 @@ const char* rmsnorm_status_string(int status) {
     case RMSN_ERR_OVERLAP: return "buffers overlap in a forbidden way";
     case RMSN_ERR_ALIGN: return "pointer not aligned to its element size";
     case RMSN_ERR_EPS: return "eps must be finite and non-negative";
+    case RMSN_ERR_MODE: return "unknown quantisation mode";
     case RMSN_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown status";
   }

@@ -10,7 +10,10 @@
 //    readlane, then across the waves of a row through LDS (the XOR-butterfly-
 //    then-LDS scheme of the FlyDSL guide, section 1.1, with DPP in place of
 //    shuffles). Every lane of a group ends with the same, bitwise identical,
-//    value, and the order of additions never depends on timing.
+//    value, and the order of additions never depends on timing,
+//  * fp8 e4m3 packing for the quantised output (OCP "fn" encoding, the one
+//    gfx950's v_cvt_pk_fp8_f32 produces; the FlyDSL guide, section 3b, uses
+//    e4m3fn on gfx950), saturated at +-448.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,6 +22,7 @@
 namespace rmsn {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -170,7 +174,76 @@ __device__ __forceinline__ void load_gamma(const typename G::S* g, int off, floa
   }
 }
 
+// ------------------------------------------------------------ fp8 output
+//
+// Output modes of the forward kernels: the activation type, or fp8 e4m3 codes
+// of y / s with s one caller-given scale (kOutFp8Tensor) or max_j |y_ij| / 448
+// per row (kOutFp8Row, s written out).
+constexpr int kOutAct = 0;
+constexpr int kOutFp8Tensor = 1;
+constexpr int kOutFp8Row = 2;
+constexpr float kFp8Max = 448.0f;  // largest finite e4m3fn value
+
+// t = v * k clamped to [-448, 448] with one v_med3_f32 (inputs holding inf
+// or NaN give unspecified codes).
+__device__ __forceinline__ float fp8_arg(float v, float k) {
+  return __builtin_amdgcn_fmed3f(v * k, -kFp8Max, kFp8Max);
+}
+
+// Four fp8 codes (nearest-even) of four clamped values, lowest address first.
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// The fp8 image of one unit of E elements: E bytes, stored with one
+// instruction (8, 4 or 1 byte). pack(p, k) encodes p[e] * k.
+template <int E>
+struct Fp8Unit;
+
+template <>
+struct Fp8Unit<8> {
+  using Raw = u32x2;
+  __device__ static Raw pack(const float* o, float inv) {
+    float t[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = fp8_arg(o[e], inv);
+    return (Raw){fp8x4(t[0], t[1], t[2], t[3]), fp8x4(t[4], t[5], t[6], t[7])};
+  }
+  __device__ static void store_nt(uint8_t* p, Raw v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<Raw*>(p));
+  }
+};
+
+template <>
+struct Fp8Unit<4> {
+  using Raw = uint32_t;
+  __device__ static Raw pack(const float* o, float inv) {
+    return fp8x4(fp8_arg(o[0], inv), fp8_arg(o[1], inv), fp8_arg(o[2], inv), fp8_arg(o[3], inv));
+  }
+  __device__ static void store_nt(uint8_t* p, Raw v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<Raw*>(p));
+  }
+};
+
+template <>
+struct Fp8Unit<1> {
+  using Raw = uint8_t;
+  __device__ static Raw pack(const float* o, float inv) {
+    return static_cast<Raw>(__builtin_amdgcn_cvt_pk_fp8_f32(fp8_arg(o[0], inv), 0.0f, 0, false));
+  }
+  __device__ static void store_nt(uint8_t* p, Raw v) { __builtin_nontemporal_store(v, p); }
+};
+
 // --------------------------------------------------------------- reductions
+
+// A sum and a maximum reduced together (sum of squares and max |y| of a row):
+// one pass of lane moves and one LDS round trip for both.
+struct SumMax {
+  float s, m;
+  __device__ SumMax operator+(SumMax o) const { return {s + o.s, __builtin_fmaxf(m, o.m)}; }
+};
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -186,8 +259,17 @@ __device__ __forceinline__ double dpp(double v) {
   return __builtin_bit_cast(double, h);
 }
 
+template <int CTRL>
+__device__ __forceinline__ SumMax dpp(SumMax v) {
+  return {dpp<CTRL>(v.s), dpp<CTRL>(v.m)};
+}
+
 __device__ __forceinline__ float readlane(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+__device__ __forceinline__ SumMax readlane(SumMax v, int lane) {
+  return {readlane(v.s, lane), readlane(v.m, lane)};
 }
 
 __device__ __forceinline__ double readlane(double v, int lane) {

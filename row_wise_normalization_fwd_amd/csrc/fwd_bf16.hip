@@ -4,7 +4,8 @@
 namespace rmsn {
 
 hipError_t launch_fwd_bf16(const FwdCall& c) {
-  return c.gamma_dtype == kDtF32 ? fwd_gamma_typed<BF16, F32>(c) : fwd_gamma_typed<BF16, BF16>(c);
+  return c.gamma_dtype == kDtF32 ? fwd_gamma_typed<BF16, F32, kOutAct>(c)
+                                 : fwd_gamma_typed<BF16, BF16, kOutAct>(c);
 }
 
 }  // namespace rmsn

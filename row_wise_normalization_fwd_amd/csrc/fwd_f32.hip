@@ -3,6 +3,6 @@
 
 namespace rmsn {
 
-hipError_t launch_fwd_f32(const FwdCall& c) { return fwd_gamma_typed<F32, F32>(c); }
+hipError_t launch_fwd_f32(const FwdCall& c) { return fwd_gamma_typed<F32, F32, kOutAct>(c); }
 
 }  // namespace rmsn

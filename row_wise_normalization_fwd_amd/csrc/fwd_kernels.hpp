@@ -19,7 +19,18 @@
 // with non-temporal loads (measured faster on gfx950 when inputs are not
 // cache-resident). The re-read path keeps ordinary loads so its second pass
 // can hit in L2 / MALL.
+//
+// OUT selects the output: the activation type (y), or fp8 e4m3 codes of y / s
+// (the quantised variants of the "TIRx kernels" page's FlashInfer norm ports)
+// with s one caller scale, or s_i = max_j |y_ij| / 448 per row. For the per-row
+// scale the first pass also takes max_j |x_ij gamma_j|, reduced together with
+// the sum of squares; amax = that max * rstd then equals max_j |y_ij| as the
+// kernel computes y up to one rounding, and the clamp at 448 absorbs that.
+// The fp8 store multiplies x * gamma by one per-row factor rstd / s (rstd *
+// 448 / amax per row, rstd / s per tensor): two multiplies per element.
 #pragma once
+
+#include <type_traits>
 
 #include "device.hpp"
 
@@ -35,7 +46,25 @@ struct FwdArgs {
   int64_t M;
   int N;
   float eps;
+  uint8_t* q;    // fp8 output (OUT != kOutAct)
+  float* scale;  // kOutFp8Tensor: [1], read; kOutFp8Row: [M], written
 };
+
+// Sum-of-squares reduction type: the pair (sum, max) for the per-row scale.
+template <int OUT>
+using RedT = typename std::conditional<OUT == kOutFp8Row, SumMax, float>::type;
+
+// Inverse scale of the per-tensor mode, read once per block.
+template <class T, class G, int OUT>
+__device__ __forceinline__ float tensor_inv_scale(const FwdArgs<T, G>& a) {
+  if constexpr (OUT == kOutFp8Tensor) return 1.0f / a.scale[0];
+  else return 0.0f;
+}
+
+// Per-row mode: s = amax / 448 and the multiplier 448 / amax (0 for a zero row).
+__device__ __forceinline__ float row_inv_scale(float amax) {
+  return amax > 0.0f ? kFp8Max / amax : 0.0f;
+}
 
 // Widen unit `raw`, optionally add the residual unit and round (fused add),
 // and return the fp32 values that get normalised.
@@ -53,13 +82,15 @@ __device__ __forceinline__ void prepare_unit(typename U::Raw& raw, typename U::R
   }
 }
 
-template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool FUSED>
+template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool FUSED, int OUT>
 __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
   using U = Unit<T, VEC>;
   constexpr int E = U::E;
+  using Q = Fp8Unit<E>;
   constexpr int RPB = BLOCK / TPR;  // rows per block
   static_assert(BLOCK % TPR == 0 && BLOCK % kWave == 0, "block shape");
-  __shared__ float red[2 * (BLOCK / kWave)];
+  __shared__ RedT<OUT> red[2 * (BLOCK / kWave)];
+  const float tinv = tensor_inv_scale<T, G, OUT>(a);
 
   const int nunits = a.N / E;
   const int grp = threadIdx.x / TPR;
@@ -114,9 +145,24 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
 #pragma unroll
     for (int k = 1; k < UPT; ++k) ss = ss + part[k];
 
-    ss = row_sum<TPR, BLOCK>(ss, red, parity);
+    float inv = tinv;
+    float rs;
+    if constexpr (OUT == kOutFp8Row) {
+      float m = 0.0f;
+#pragma unroll
+      for (int k = 0; k < UPT; ++k)
+#pragma unroll
+        for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[k][e] * gam[k][e]));
+      const SumMax r = row_sum<TPR, BLOCK>(SumMax{ss, m}, red, parity);
+      rs = 1.0f / __builtin_sqrtf(r.s / static_cast<float>(a.N) + a.eps);
+      const float amax = r.m * rs;
+      inv = row_inv_scale(amax);
+      if (valid && lane == 0) a.scale[row] = amax / kFp8Max;
+    } else {
+      ss = row_sum<TPR, BLOCK>(ss, red, parity);
+      rs = 1.0f / __builtin_sqrtf(ss / static_cast<float>(a.N) + a.eps);
+    }
     parity ^= 1;
-    const float rs = 1.0f / __builtin_sqrtf(ss / static_cast<float>(a.N) + a.eps);
     if (a.rstd != nullptr && valid && lane == 0) a.rstd[row] = rs;
 
 #pragma unroll
@@ -124,9 +170,15 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
       const int u = lane + k * TPR;
       if (valid && u < nunits) {
         float o[E];
+        if constexpr (OUT == kOutAct) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = v[k][e] * rs * gam[k][e];
-        U::store_nt(a.y + off + u * E, U::narrow(o));
+          for (int e = 0; e < E; ++e) o[e] = v[k][e] * rs * gam[k][e];
+          U::store_nt(a.y + off + u * E, U::narrow(o));
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[e] = v[k][e] * gam[k][e];
+          Q::store_nt(a.q + off + u * E, Q::pack(o, rs * inv));
+        }
       }
     }
   }
@@ -142,7 +194,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
 // branches around them and the compiler waits only for the older loads.
 // Row results do not depend on G (each row's arithmetic is the same for any
 // grid), only on TPR and UPT.
-template <class T, class G, int TPR, int UPT, int BLOCK, bool FUSED>
+template <class T, class G, int TPR, int UPT, int BLOCK, bool FUSED, int OUT>
 __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
   using U = Unit<T, true>;
   using Raw = u32x4;
@@ -150,7 +202,9 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
   constexpr int RG = BLOCK / TPR;
   constexpr int GW = E * G::kSize / 16;  // 16-byte words of gamma per unit (1 or 2)
   static_assert(BLOCK % TPR == 0 && BLOCK % kWave == 0, "block shape");
-  __shared__ float red[2 * (BLOCK / kWave)];
+  static_assert(OUT == kOutAct || E == 8, "fp8 units of 8 bytes");
+  __shared__ RedT<OUT> red[2 * (BLOCK / kWave)];
+  const float tinv = tensor_inv_scale<T, G, OUT>(a);
 
   const int nunits = a.N / E;
   const int grp = threadIdx.x / TPR;
@@ -169,6 +223,13 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
     for (int w = 0; w < GW; ++w) graw[k][w] = *reinterpret_cast<const u32x4*>(gp + w * (16 / G::kSize));
   }
 
+  auto widen_gamma = [&](const u32x4* gw, float* g) {
+#pragma unroll
+    for (int w = 0; w < GW; ++w)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) G::widen_word(gw[w][q], g + w * (16 / G::kSize) + q * G::kPerWord);
+  };
+
   // Byte offset of unit k of this group's row in the iteration starting at
   // row0, or an out-of-range offset if the row or the unit does not exist.
   auto unit_offset = [&](int64_t row0, int k) -> uint32_t {
@@ -182,6 +243,16 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
   auto span_bytes = [&](int64_t row0) -> uint32_t {
     const int64_t rest = row0 < a.M ? (a.M - row0) * row_bytes : 0;
     return static_cast<uint32_t>(rest < 0x7fffffff ? rest : 0x7fffffff);
+  };
+  // Per-row fp32 outputs (rstd, scale): one lane per row stores through a
+  // buffer based at row0, out of range for lanes that do not own a row.
+  auto store_row_value = [&](float* base, int64_t row0, float val) {
+    const int64_t rest = (a.M - row0) * 4;
+    const auto r = make_rsrc(base + row0, static_cast<uint32_t>(rest < 0x7fffffff ? rest : 0x7fffffff));
+    const bool mine = lane == 0 && row0 + nblk * grp < a.M;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), r,
+                                          mine ? static_cast<uint32_t>(nblk * grp * 4) : kBufOutOfRange,
+                                          0, 0);
   };
   auto load_rows = [&](int64_t row0, Raw* rx, Raw* rr) {
     const int64_t base = (row0 < a.M ? row0 : 0) * a.N;
@@ -200,7 +271,6 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
   int parity = 0;
   auto step = [&](int64_t row0, Raw* cx, Raw* cr, Raw* nx, Raw* nr) {
     load_rows(row0 + nblk * RG, nx, nr);
-    const int64_t row = row0 + nblk * grp;
     const uint32_t n = span_bytes(row0);
     float part[UPT];
 #pragma unroll
@@ -220,34 +290,61 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
     float ss = part[0];
 #pragma unroll
     for (int k = 1; k < UPT; ++k) ss = ss + part[k];
+    [[maybe_unused]] float m = 0.0f;
+    if constexpr (OUT == kOutFp8Row) {
+#pragma unroll
+      for (int k = 0; k < UPT; ++k) {
+        float v[E], g[E];
+        U::widen(cx[k], v);
+        widen_gamma(graw[k], g);
+#pragma unroll
+        for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e] * g[e]));
+      }
+    }
     // Widen again after the reduction instead of keeping fp32 copies live.
 #pragma unroll
     for (int k = 0; k < UPT; ++k) opaque(cx[k]);
-    ss = row_sum<TPR, BLOCK>(ss, red, parity);
+    float rs, inv = tinv;
+    if constexpr (OUT == kOutFp8Row) {
+      const SumMax r = row_sum<TPR, BLOCK>(SumMax{ss, m}, red, parity);
+      rs = 1.0f / __builtin_sqrtf(r.s / static_cast<float>(a.N) + a.eps);
+      const float amax = r.m * rs;
+      inv = row_inv_scale(amax);
+      store_row_value(a.scale, row0, amax / kFp8Max);
+    } else {
+      ss = row_sum<TPR, BLOCK>(ss, red, parity);
+      rs = 1.0f / __builtin_sqrtf(ss / static_cast<float>(a.N) + a.eps);
+    }
     parity ^= 1;
-    const float rs = 1.0f / __builtin_sqrtf(ss / static_cast<float>(a.N) + a.eps);
-    const auto rsy = make_rsrc(a.y + row0 * a.N, n);
+    if constexpr (OUT == kOutAct) {
+      const auto rsy = make_rsrc(a.y + row0 * a.N, n);
 #pragma unroll
-    for (int k = 0; k < UPT; ++k) {
-      float v[E], g[E], o[E];
-      U::widen(cx[k], v);
+      for (int k = 0; k < UPT; ++k) {
+        float v[E], g[E], o[E];
+        U::widen(cx[k], v);
+        widen_gamma(graw[k], g);
 #pragma unroll
-      for (int w = 0; w < GW; ++w)
+        for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
+        buf_store16_nt(U::narrow(o), rsy, unit_offset(row0, k));
+      }
+    } else {
+      // fp8 codes: N bytes per row, 8 per unit, so offsets are half the input's.
+      const int64_t rest = row0 < a.M ? (a.M - row0) * a.N : 0;
+      const auto rsq = make_rsrc(a.q + row0 * a.N, static_cast<uint32_t>(rest < 0x7fffffff ? rest : 0x7fffffff));
+      const float kq = rs * inv;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) G::widen_word(graw[k][w][q], g + w * (16 / G::kSize) + q * G::kPerWord);
+      for (int k = 0; k < UPT; ++k) {
+        float v[E], g[E], o[E];
+        U::widen(cx[k], v);
+        widen_gamma(graw[k], g);
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
-      buf_store16_nt(U::narrow(o), rsy, unit_offset(row0, k));
+        for (int e = 0; e < E; ++e) o[e] = v[e] * g[e];
+        const uint32_t off = unit_offset(row0, k);
+        __builtin_amdgcn_raw_buffer_store_b64(Fp8Unit<8>::pack(o, kq), rsq,
+                                              off == kBufOutOfRange ? off : off >> 1, 0, kBufNT);
+      }
     }
-    if (a.rstd != nullptr) {
-      // One lane per row writes rstd, through a buffer like the rest.
-      const int64_t rest = (a.M - row0) * 4;
-      const auto rsr = make_rsrc(a.rstd + row0, static_cast<uint32_t>(rest < 0x7fffffff ? rest : 0x7fffffff));
-      const bool mine = lane == 0 && row < a.M;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rs), rsr,
-                                            mine ? static_cast<uint32_t>(nblk * grp * 4) : kBufOutOfRange,
-                                            0, 0);
-    }
+    if (a.rstd != nullptr) store_row_value(a.rstd, row0, rs);
   };
 
   Raw ax[UPT], ar[UPT], bx[UPT], br[UPT];
@@ -261,13 +358,15 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
   }
 }
 
-template <class T, class G, bool VEC, int BLOCK, int UNROLL, bool FUSED, bool CACHE>
+template <class T, class G, bool VEC, int BLOCK, int UNROLL, bool FUSED, bool CACHE, int OUT>
 __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
   using U = Unit<T, VEC>;
   using Raw = typename U::Raw;
+  using Q = Fp8Unit<U::E>;
   constexpr int E = U::E;
   constexpr int STEP = BLOCK * UNROLL;
-  __shared__ float red[2 * (BLOCK / kWave)];
+  __shared__ RedT<OUT> red[2 * (BLOCK / kWave)];
+  const float tinv = tensor_inv_scale<T, G, OUT>(a);
   extern __shared__ __align__(16) unsigned char lds_bytes[];
   Raw* cache = reinterpret_cast<Raw*>(lds_bytes);
 
@@ -276,6 +375,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
   for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x) {
     const int64_t off = row * a.N;
     float ss = 0.0f;
+    [[maybe_unused]] float m = 0.0f;
     for (int first = 0; first < nunits; first += STEP) {
       Raw raw[UNROLL];
       Raw res[UNROLL];
@@ -302,12 +402,27 @@ __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
         if (u < nunits) {
           if constexpr (FUSED) U::store_nt(a.residual + off + u * E, raw[k]);
           if constexpr (CACHE) cache[u] = raw[k];
+          if constexpr (OUT == kOutFp8Row) {
+            float g[E];
+            load_gamma<G, E, VEC>(a.gamma, u * E, g);
+#pragma unroll
+            for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e] * g[e]));
+          }
         }
       }
     }
-    ss = row_sum<BLOCK, BLOCK>(ss, red, parity);
+    float rs, inv = tinv;
+    if constexpr (OUT == kOutFp8Row) {
+      const SumMax r = row_sum<BLOCK, BLOCK>(SumMax{ss, m}, red, parity);
+      rs = 1.0f / __builtin_sqrtf(r.s / static_cast<float>(a.N) + a.eps);
+      const float amax = r.m * rs;
+      inv = row_inv_scale(amax);
+      if (threadIdx.x == 0) a.scale[row] = amax / kFp8Max;
+    } else {
+      ss = row_sum<BLOCK, BLOCK>(ss, red, parity);
+      rs = 1.0f / __builtin_sqrtf(ss / static_cast<float>(a.N) + a.eps);
+    }
     parity ^= 1;
-    const float rs = 1.0f / __builtin_sqrtf(ss / static_cast<float>(a.N) + a.eps);
     if (a.rstd != nullptr && threadIdx.x == 0) a.rstd[row] = rs;
 
     // Second pass: the rounded h (fused) was written back to `residual`; each
@@ -328,9 +443,15 @@ __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
           float v[E], g[E], o[E];
           U::widen(raw[k], v);
           load_gamma<G, E, VEC>(a.gamma, u * E, g);
+          if constexpr (OUT == kOutAct) {
 #pragma unroll
-          for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
-          U::store_nt(a.y + off + u * E, U::narrow(o));
+            for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
+            U::store_nt(a.y + off + u * E, U::narrow(o));
+          } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = v[e] * g[e];
+            Q::store_nt(a.q + off + u * E, Q::pack(o, rs * inv));
+          }
         }
       }
     }

@@ -59,11 +59,19 @@ struct FwdCall {
   float eps;
   int gamma_dtype;
   hipStream_t stream;
+  // Quantised forward only: fp8 codes, the scale array and the mode
+  // (1: one caller scale, read; 2: per-row scales, written).
+  void* q = nullptr;
+  float* scale = nullptr;
+  int out = 0;
 };
 
 hipError_t launch_fwd_f32(const FwdCall& c);
 hipError_t launch_fwd_f16(const FwdCall& c);
 hipError_t launch_fwd_bf16(const FwdCall& c);
+hipError_t launch_fwd_quant_f32(const FwdCall& c);
+hipError_t launch_fwd_quant_f16(const FwdCall& c);
+hipError_t launch_fwd_quant_bf16(const FwdCall& c);
 
 // Backward partition: G = min(M, kBwdTargetBlocks) blocks, block b owning
 // rows b, b + G, b + 2G, ... It depends only on M, which fixes the dgamma
@@ -103,6 +111,10 @@ struct BwdCall {
 hipError_t launch_bwd(const BwdCall& c);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool aligned_to(const void* p, int bytes) {
+  return reinterpret_cast<uintptr_t>(p) % static_cast<uintptr_t>(bytes) == 0;
+}
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -13,6 +13,10 @@ Tolerances (fixed here, used by every GPU test):
   * dh of the fused-add backward: as dx, with 2^-22 |dresidual| added to the
     floor for the fp32 addition of the residual gradient.
   * dgamma: |g - o| <= max(1e-3 |o|, 2^-24 S_j) with S_j = sum_i |dy x rho|.
+  * fp8 e4m3 codes: ordinal distance <= 1 from the oracle's code (the kernel
+    scales in fp32, so y / s can land on the other side of a tie); per-row
+    scales: relative error <= 1e-5; every nonzero row's largest code is
+    +-448 exactly.
 """
 
 from __future__ import annotations
@@ -121,3 +125,32 @@ def check_dgamma(got: np.ndarray, ref: dict):
     assert not bad.any(), (f"dgamma: {int(bad.sum())} columns out of tolerance; worst ratio "
                            f"{float((err / tol).max()):.3f}")
     return float(np.linalg.norm(got - o) / max(np.linalg.norm(o), 1e-300))
+
+
+def e4m3_ordinal(codes: np.ndarray) -> np.ndarray:
+    """Monotone integer image of e4m3 codes (sign-magnitude; +-0 both 0)."""
+    c = codes.astype(np.int32)
+    mag = c & 0x7f
+    return np.where(c & 0x80, -mag, mag)
+
+
+def check_fp8(got: np.ndarray, ref: dict, per_row: bool, got_scale: np.ndarray | None = None):
+    """Codes within one step of the oracle's; per-row scales and row maxima."""
+    got = got.reshape(ref["q"].shape)
+    assert not np.any((got & 0x7f) == 0x7f), "NaN code in the output"
+    d = np.abs(e4m3_ordinal(got) - e4m3_ordinal(ref["q"]))
+    if (d > 1).any():
+        idx = np.unravel_index(int(np.argmax(d)), d.shape)
+        raise AssertionError(f"fp8: {int((d > 1).sum())} codes more than one step off; worst at "
+                             f"{idx}: got {got[idx]:#04x}, oracle {ref['q'][idx]:#04x}, "
+                             f"y/s {ref['q_exact'][idx]!r}")
+    if per_row:
+        assert got_scale is not None
+        se = ref["scale_exact"]
+        err = np.abs(got_scale.astype(np.float64) - se)
+        assert np.all(err <= 1e-5 * np.abs(se)), f"scale: worst rel {float((err / np.maximum(se, 1e-300)).max())}"
+        nz = se > 0
+        top = (got & 0x7f).max(axis=1)
+        assert np.all(top[nz] == 0x7e), "a row's largest code is not 448"
+        assert np.all((got[~nz] & 0x7f) == 0)
+    return int((d == 1).sum())

@@ -170,3 +170,35 @@ def test_fused_backward_validation(lib):
     assert fbwd(dh=H + 64) == OVERLAP
     assert fbwd(dres=F) == OVERLAP             # dresidual over dgamma
     assert fbwd(dres=G + 256) == OVERLAP       # dresidual over the workspace
+
+
+MODE = -8
+QT, QR = 1, 2
+
+
+def quant(x=A, r=None, g=B, q=C, sc=D, mode=QR, rstd=E, M=64, N=256, eps=1e-5, xd=BF16, gd=BF16):
+    return R.rmsnorm_quant_fwd(x, r, g, q, sc, mode, rstd, M, N, eps, xd, gd, None)
+
+
+def test_quant_validation(lib):
+    assert quant(mode=0) == MODE
+    assert quant(mode=3) == MODE
+    assert quant(xd=F32, gd=F16) == DTYPE
+    assert quant(N=0) == SHAPE
+    assert quant(eps=float("nan")) == EPS
+    assert quant(M=0, x=None, g=None, q=None, sc=None, rstd=None) == OK
+    for k in ("x", "g", "q", "sc"):
+        assert quant(**{k: None}) == NULL, k
+    assert quant(sc=D + 2) == ALIGN
+    assert quant(x=A + 1) == ALIGN
+    assert quant(r=F + 1) == ALIGN
+    assert quant(q=A) == OVERLAP                    # q over x, even exactly
+    assert quant(q=A + 64 * 256 * 2 - 1) == OVERLAP
+    assert quant(q=B) == OVERLAP                    # q over gamma
+    assert quant(sc=C + 16) == OVERLAP              # scale inside q
+    assert quant(sc=A + 8) == OVERLAP               # per-row scale written over x
+    assert quant(rstd=C + 8) == OVERLAP             # rstd inside q
+    assert quant(rstd=D) == OVERLAP                 # rstd over the scale
+    assert quant(r=C) == OVERLAP                    # residual over q
+    assert quant(r=A + 2) == OVERLAP                # residual partially over x
+    assert R.rmsnorm_status_string(MODE) == "unknown quantisation mode"

@@ -11,8 +11,8 @@ import torch
 import gen as G
 import oracle as O
 import row_wise_normalization_fwd_amd as R
-from gpu_util import (check_dgamma, check_dx, check_output, check_rstd, to_device, to_host,
-                      TORCH_DTYPES)
+from gpu_util import (check_dgamma, check_dx, check_fp8, check_output, check_rstd, to_device,
+                      to_host, TORCH_DTYPES)
 
 pytestmark = pytest.mark.gpu
 
@@ -231,6 +231,143 @@ def test_fused_misaligned_and_aliased(pair):
     run_fused(7, 4096, *pair, seed=52, x_is_r=True)
 
 
+# ------------------------------------------------- quantised (fp8) forward
+
+QT, QR = O.QUANT_TENSOR, O.QUANT_ROW
+TENSOR_SCALE = 0.0125   # |y| above 5.6 saturates: a few elements per row do
+
+
+def run_quant(M, N, xdt, gdt, mode, seed=19, fused=False, eps=1e-5, misalign=0, q_off=0,
+              want_rstd=True, outlier_every=0, outlier_scale=1.0, tensor_scale=TENSOR_SCALE):
+    _log(f"quant M={M} N={N} x={xdt} g={gdt} mode={mode} fused={fused} misalign={misalign} "
+         f"q_off={q_off} rstd={want_rstd}")
+    x, g, r, _ = _inputs(M, N, xdt, gdt, seed, outlier_every, outlier_scale, with_r=fused)
+    ref = O.rmsnorm_quant_fwd(x, g, M, N, eps, xdt, gdt, mode,
+                              scale=tensor_scale if mode == QT else None, r=r)
+    xt, gt = _put(x, xdt, misalign), _put(g, gdt)
+    rt = _put(r, xdt, misalign) if fused else None
+    qbuf = torch.full((M * N + 64,), 0x7f, dtype=torch.uint8, device="cuda")
+    qt = qbuf[q_off:q_off + M * N]
+    if mode == QT:
+        sc = torch.tensor([tensor_scale], dtype=torch.float32, device="cuda")
+    else:
+        sc = torch.full((M,), float("nan"), device="cuda")
+    rs = torch.full((M,), float("nan"), device="cuda") if want_rstd else None
+    st = R.rmsnorm_quant_fwd(xt, rt, gt, qt, sc, mode, rs, M, N, eps, xdt, gdt, _stream())
+    assert st == 0, R.rmsnorm_status_string(st)
+    torch.cuda.synchronize()
+    q = qt.cpu().numpy().reshape(M, N)
+    steps = check_fp8(q, ref, mode == QR, to_host(sc) if mode == QR else None)
+    assert np.all(qbuf[:q_off].cpu().numpy() == 0x7f), "write before q"
+    assert np.all(qbuf[q_off + M * N:].cpu().numpy() == 0x7f), "write past q"
+    if want_rstd:
+        check_rstd(to_host(rs), ref["rstd"].astype(np.float64))
+    if fused:
+        h = to_host(rt).reshape(M, N)
+        assert np.array_equal(h.view(np.uint8), ref["h"].view(np.uint8)), "h not bit-exact"
+    return steps
+
+
+@pytest.mark.parametrize("mode", [QT, QR], ids=["tensor", "row"])
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("N", [1, 7, 64, 1000, 2048, 4096, 5000, 6152, 8191, 8192, 8193, 16384])
+def test_quant_sweep(N, pair, mode):
+    run_quant(5, N, *pair, mode, seed=1100 + N, want_rstd=(N % 2 == 0))
+    run_quant(300, N, *pair, mode, seed=1200 + N, fused=True, want_rstd=(N % 2 == 1))
+
+
+@pytest.mark.parametrize("mode", [QT, QR], ids=["tensor", "row"])
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_quant_long_rows_misaligned(pair, mode):
+    run_quant(3, N_LDS[pair[0]], *pair, mode, seed=1301)
+    run_quant(3, N_REREAD[pair[0]], *pair, mode, seed=1302, fused=True)
+    run_quant(7, 4096, *pair, mode, seed=1303, misalign=1)            # scalar units
+    run_quant(7, 4096, *pair, mode, seed=1304, q_off=1)               # q not unit-aligned
+    run_quant(7, 9000, *pair, mode, seed=1305, q_off=3, fused=True)   # long rows, scalar
+    run_quant(1000, 8192, *pair, mode, seed=1306, outlier_every=13, outlier_scale=300.0)
+
+
+def _e4m3_grid_gamma(max448: bool):
+    """fp32 gamma holding every finite e4m3 magnitude, every tie between
+    neighbours and a quarter point in each gap, with alternating signs."""
+    codes = np.arange(0, 0x7f, dtype=np.uint8)
+    vals = O.decode(codes, O.E4M3)
+    mids = (vals[:-1] + vals[1:]) / 2
+    q1 = vals[:-1] + (vals[1:] - vals[:-1]) / 4
+    g = np.concatenate([vals, mids, q1] + ([] if max448 else [[456.0, 463.0, 464.0, 600.0]]))
+    g = g * np.where(np.arange(g.size) % 2 == 0, 1.0, -1.0)
+    return g.astype(np.float32)
+
+
+@pytest.mark.parametrize("xdt", [O.F32, O.F16, O.BF16], ids=["f32", "f16", "bf16"])
+@pytest.mark.parametrize("layout", ["vec", "ragged"])
+def test_quant_rounding_is_nearest_even_at_every_tie(xdt, layout):
+    # A constant row 2^k with eps = 0 has rstd = 2^-k exactly, so the kernel's
+    # y is exactly +-gamma_j; with power-of-two scales y / s is exact too and
+    # every code must equal the oracle's bit for bit, ties included. The
+    # per-row case uses a gamma whose largest magnitude is 448 (scale 1).
+    for mode, max448, scales in ((QT, False, (1.0, 0.125, 4.0)), (QR, True, (None,))):
+        g = _e4m3_grid_gamma(max448)
+        n8 = -(-g.size // 8) * 8                 # 16-byte rows for every dtype
+        pad = n8 - g.size + (3 if layout == "ragged" else 0)
+        g = np.concatenate([g, np.zeros(pad, np.float32)])
+        N = g.size
+        for c in (1.0, -0.25, 8.0):
+            M = 3
+            x = O.round_to(np.full((M, N), c), xdt)
+            for s in scales:
+                ref = O.rmsnorm_quant_fwd(x, g, M, N, 0.0, xdt, O.F32, mode, scale=s)
+                qt = torch.empty(M * N, dtype=torch.uint8, device="cuda")
+                sc = (torch.tensor([s], dtype=torch.float32, device="cuda") if mode == QT
+                      else torch.empty(M, device="cuda"))
+                assert R.rmsnorm_quant_fwd(_put(x, xdt), None, _put(g, O.F32), qt, sc, mode,
+                                           None, M, N, 0.0, xdt, O.F32, _stream()) == 0
+                torch.cuda.synchronize()
+                got = qt.cpu().numpy().reshape(M, N)
+                bad = got != ref["q"]
+                assert not bad.any(), (f"c={c} s={s} mode={mode}: {int(bad.sum())} codes differ; "
+                                       f"first gamma {g[np.argmax(bad.any(axis=0))]!r}")
+                if mode == QR:
+                    assert np.all(to_host(sc) == 1.0)
+
+
+def test_quant_zero_rows_and_tensor_saturation():
+    M, N = 8, 4096
+    x, g, _, _ = _inputs(M, N, O.BF16, O.BF16, 1401)
+    xs = O.decode(x, O.BF16).reshape(M, N)
+    xs[2] = 0.0                                       # rstd = 1/sqrt(eps), y = 0
+    x = O.round_to(xs, O.BF16)
+    ref = O.rmsnorm_quant_fwd(x, g, M, N, 1e-5, O.BF16, O.BF16, QR)
+    qt, sc = torch.empty(M * N, dtype=torch.uint8, device="cuda"), torch.empty(M, device="cuda")
+    assert R.rmsnorm_quant_fwd(_put(x, O.BF16), None, _put(g, O.BF16), qt, sc, QR, None, M, N,
+                               1e-5, O.BF16, O.BF16, _stream()) == 0
+    torch.cuda.synchronize()
+    check_fp8(qt.cpu().numpy(), ref, True, to_host(sc))
+    assert to_host(sc)[2] == 0.0
+    # A tiny tensor scale saturates almost everything at +-448.
+    ref = O.rmsnorm_quant_fwd(x, g, M, N, 1e-5, O.BF16, O.BF16, QT, scale=1e-6)
+    st = torch.tensor([1e-6], dtype=torch.float32, device="cuda")
+    assert R.rmsnorm_quant_fwd(_put(x, O.BF16), None, _put(g, O.BF16), qt, st, QT, None, M, N,
+                               1e-5, O.BF16, O.BF16, _stream()) == 0
+    torch.cuda.synchronize()
+    got = qt.cpu().numpy().reshape(M, N)
+    assert np.array_equal(got, ref["q"])
+
+
+def test_quant_matches_plain_forward_values():
+    # Dequantised codes track the plain forward's y within one e4m3 step.
+    M, N = 256, 8192
+    x, g, _, _ = _inputs(M, N, O.BF16, O.BF16, 1402)
+    xt, gt = _put(x, O.BF16), _put(g, O.BF16)
+    y = _empty(M * N, O.BF16)
+    assert R.rmsnorm_fwd(xt, gt, y, None, M, N, 1e-5, O.BF16, O.BF16, _stream()) == 0
+    q, sc, _ = R.quant_fwd(xt.view(M, N), gt)
+    torch.cuda.synchronize()
+    yv = O.decode(to_host(y), O.BF16).reshape(M, N)
+    deq = O.decode(q.cpu().numpy(), O.E4M3).reshape(M, N) * to_host(sc)[:, None]
+    assert np.all(np.abs(deq - yv) <= np.abs(yv) / 8 + to_host(sc)[:, None] * 2.0 ** -9 + 1e-6)
+
+
 # ----------------------------------------------------------------- backward
 
 def run_bwd(M, N, xdt, gdt, seed=13, misalign=0, alias=None, gpu_rstd=False, eps=1e-5):
@@ -434,6 +571,11 @@ def test_workload_full_size(w):
         run_fused(w.M, w.N, w.x_dt, w.g_dt, eps=w.eps, seed=w.seed, want_rstd=w.store_rstd)
     elif w.kind == "fused_add_bwd":
         run_fused_bwd(w.M, w.N, w.x_dt, w.g_dt, seed=w.seed)
+    elif w.kind == "quant":
+        steps = run_quant(w.M, w.N, w.x_dt, w.g_dt, w.quant_mode, seed=w.seed, eps=w.eps,
+                          fused=w.fused_quant, want_rstd=w.store_rstd,
+                          tensor_scale=w.tensor_scale)
+        _log(f"codes one step from the oracle's: {steps}")
     else:
         floor_only = run_bwd(w.M, w.N, w.x_dt, w.g_dt, seed=w.seed, eps=w.eps)
         _log(f"dx elements passing only by the cancellation floor: {floor_only}")
