@@ -63,9 +63,11 @@ def _load():
                                                  dp, vp, dp, dp, dp, dp]
     lib.oracle_rmsnorm_quant_fwd.argtypes = [vp, vp, vp, i64, i64, f32, i32, i32, i32, f32,
                                              vp, vp, dp, dp, vp, vp]
+    lib.oracle_rmsnorm_heads_fwd.argtypes = [vp, vp, i64, i64, i64, i64, f32, i32, i32, vp]
     for fn in (lib.oracle_decode, lib.oracle_round, lib.oracle_rmsnorm_fwd,
                lib.oracle_rmsnorm_fused_add_fwd, lib.oracle_rmsnorm_bwd,
-               lib.oracle_rmsnorm_fused_add_bwd, lib.oracle_rmsnorm_quant_fwd):
+               lib.oracle_rmsnorm_fused_add_bwd, lib.oracle_rmsnorm_quant_fwd,
+               lib.oracle_rmsnorm_heads_fwd):
         fn.restype = None
     _lib = lib
     return lib
@@ -203,3 +205,23 @@ def rmsnorm_quant_fwd(x, gamma, M, N, eps, x_dt, g_dt, mode, scale=None, r=None,
         float(np.float32(scale if scale is not None else 0.0)), _ptr(out["h"]), _ptr(out["q"]),
         _ptr(out["q_exact"]), _ptr(out["scale_exact"]), _ptr(out["scale"]), _ptr(out["rstd"]))
     return out
+
+
+def rmsnorm_heads_fwd(buf, gamma, tokens, heads, head_dim, stride, eps, x_dt, g_dt, offset=0):
+    """Per-head RMSNorm of the strided [tokens, heads, head_dim] tensor that
+    starts at element ``offset`` of the 1-D storage array ``buf`` (token
+    stride ``stride`` elements). Returns (a normalised copy of buf, rstd
+    (tokens*heads,) fp32); buf itself is not modified."""
+    buf = np.array(buf, copy=True, order="C").reshape(-1)
+    if buf.dtype != storage_dtype(x_dt):
+        raise TypeError("buf: wrong storage dtype")
+    gamma = _check(gamma, g_dt, head_dim, "gamma")
+    if tokens > 0 and heads > 0:
+        last = offset + (tokens - 1) * stride + heads * head_dim
+        if offset < 0 or last > buf.size or stride < heads * head_dim:
+            raise ValueError("tensor does not fit the buffer")
+    rstd = np.empty(tokens * heads, np.float32)
+    view = buf[offset:]
+    _load().oracle_rmsnorm_heads_fwd(_ptr(view) if view.size else None, _ptr(gamma), tokens,
+                                     heads, head_dim, stride, eps, x_dt, g_dt, _ptr(rstd))
+    return buf, rstd

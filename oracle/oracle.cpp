@@ -29,6 +29,13 @@
 //     where rho_i is the rstd handed in.
 //   * Rounding to bf16 / fp16 / fp32: round to nearest, ties to even (the FlyDSL
 //     guide, section 1.1, states RNE for the bf16 pack; IEEE default otherwise).
+//   * Per-head QK-RMSNorm ("TIRx kernels", FlashInfer ports, flashinfer.norm:
+//     qk_rmsnorm, named without a definition). Reading taken: q holds
+//     [tokens, q_heads, head_dim] and k [tokens, k_heads, head_dim], each head
+//     vector of head_dim elements is one row of the forward above, with gamma
+//     of length head_dim (one for q, one for k), normalised in place. Heads of
+//     a token are contiguous; tokens are a given stride apart, so q and k may
+//     be views into one fused projection buffer.
 //   * Quantised output ("TIRx kernels", FlashInfer ports, flashinfer.norm:
 //     rmsnorm_quant and fused_add_rmsnorm_quant, named without a definition).
 //     Reading taken: the forward's value y is divided by a scale and rounded
@@ -344,6 +351,28 @@ void oracle_rmsnorm_quant_fwd(const void* x, const void* r, const void* gamma, i
       double t = s == 0.0 ? 0.0 : y[j] / s;
       if (q_exact) q_exact[i * N + j] = t;
       if (q) store_value(q, i * N + j, t, kE4M3);
+    }
+  }
+}
+
+// Per-head RMSNorm, in place, of one strided [tokens, heads, head_dim]
+// tensor x (format x_dt; token t, head h starts at element t * stride +
+// h * head_dim) with gamma[head_dim] (format g_dt). Elements outside the
+// heads are not touched. rstd_f32[tokens * heads] (optional) gets the rstd
+// of each head vector, in (token, head) order.
+void oracle_rmsnorm_heads_fwd(void* x, const void* gamma, int64_t tokens, int64_t heads,
+                              int64_t head_dim, int64_t stride, float eps, int x_dt,
+                              int g_dt, float* rstd_f32) {
+  std::vector<double> v(static_cast<size_t>(head_dim)), y(static_cast<size_t>(head_dim));
+  for (int64_t t = 0; t < tokens; ++t) {
+    for (int64_t h = 0; h < heads; ++h) {
+      const int64_t base = t * stride + h * head_dim;
+      for (int64_t j = 0; j < head_dim; ++j) v[j] = decode(x, base + j, x_dt);
+      float rs;
+      forward_row(v.data(), gamma, head_dim, eps, x_dt, g_dt, 0, y.data(), nullptr, nullptr,
+                  &rs, nullptr);
+      if (rstd_f32) rstd_f32[t * heads + h] = rs;
+      for (int64_t j = 0; j < head_dim; ++j) store_value(x, base + j, y[j], x_dt);
     }
   }
 }

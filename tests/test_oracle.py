@@ -471,3 +471,48 @@ def test_quant_fused_and_zero_rows(gen_mod):
     # Zero weights give zero rows: scale 0 and zero codes in the per-row mode.
     z = O.rmsnorm_quant_fwd(x, np.zeros(N, np.float32), M, N, 1e-6, O.F16, O.F32, O.QUANT_ROW)
     assert np.all(z["scale"] == 0) and np.all(z["q"] & 0x7f == 0)
+
+
+# ------------------------------------------------------- per-head QK-RMSNorm
+
+def test_heads_forward_on_a_fused_qkv_buffer(gen_mod):
+    # q, k, v of T tokens interleaved in one buffer (token stride S, with two
+    # padding elements); normalising q and k must equal the plain forward of
+    # the gathered head vectors, in (token, head) order, and leave v and the
+    # padding untouched.
+    T, Hq, Hk, D = 5, 4, 2, 24
+    S = (Hq + 2 * Hk) * D + 2
+    for dt, gdt in ((O.BF16, O.BF16), (O.F16, O.F32), (O.F32, O.F32)):
+        buf = gen_mod.normal(41, 1, 1, T * S, dt).reshape(-1)
+        gq = gen_mod.uniform(41, 4, D, 0.5, 1.5, gdt)
+        gk = gen_mod.uniform(42, 4, D, -1.0, 1.0, gdt)
+        out, rq = O.rmsnorm_heads_fwd(buf, gq, T, Hq, D, S, 1e-6, dt, gdt, offset=0)
+        out, rk = O.rmsnorm_heads_fwd(out, gk, T, Hk, D, S, 1e-6, dt, gdt, offset=Hq * D)
+        b2, o2 = buf.reshape(T, S), out.reshape(T, S)
+        for off, H, g, rs in ((0, Hq, gq, rq), (Hq * D, Hk, gk, rk)):
+            rows = np.ascontiguousarray(b2[:, off:off + H * D]).reshape(T * H, D)
+            ref = O.rmsnorm_fwd(rows, g, T * H, D, 1e-6, dt, gdt)
+            got = np.ascontiguousarray(o2[:, off:off + H * D]).reshape(T * H, D)
+            assert np.array_equal(got.view(np.uint8), ref["y"].view(np.uint8))
+            assert np.array_equal(rs, ref["rstd"])
+        rest = (Hq + Hk) * D
+        assert np.array_equal(o2[:, rest:].view(np.uint8), b2[:, rest:].view(np.uint8))
+
+
+def test_heads_forward_contiguous_is_the_plain_forward(gen_mod):
+    T, H, D = 7, 3, 64
+    x = gen_mod.normal(43, 1, T * H, D, O.BF16)
+    g = gen_mod.uniform(43, 4, D, 0.5, 1.5, O.BF16)
+    out, rs = O.rmsnorm_heads_fwd(x.reshape(-1), g, T, H, D, H * D, 1e-5, O.BF16, O.BF16)
+    ref = O.rmsnorm_fwd(x, g, T * H, D, 1e-5, O.BF16, O.BF16)
+    assert np.array_equal(out.reshape(T * H, D), ref["y"]) and np.array_equal(rs, ref["rstd"])
+    # Heads of one token differ: scaling head 1 of every token by 4 changes
+    # only those rstds, by exactly 1/4.
+    xs = O.decode(x, O.BF16).reshape(T, H, D)
+    xs[:, 1, :] *= 4.0
+    out2, rs2 = O.rmsnorm_heads_fwd(O.round_to(xs, O.BF16).reshape(-1), g, T, H, D, H * D,
+                                    0.0, O.BF16, O.BF16)
+    _, rs0 = O.rmsnorm_heads_fwd(x.reshape(-1), g, T, H, D, H * D, 0.0, O.BF16, O.BF16)
+    r0, r2 = rs0.reshape(T, H), rs2.reshape(T, H)
+    assert np.array_equal(r2[:, 0], r0[:, 0]) and np.array_equal(r2[:, 2], r0[:, 2])
+    assert np.array_equal(r2[:, 1], r0[:, 1] / 4)
