@@ -21,8 +21,9 @@ Also reported, in the same JSON line:
                 full passes of the same batch for about --cpu-seconds;
   workloads     the other four workloads (fp32 short rows, fused residual add,
                 backward, fp16 ragged rows) and the fused-add backward, timed
-                the same way, and the fp8-output forward (per-row scales at
-                the headline shape; one scale after the fused add);
+                the same way, the fp8-output forward (per-row scales at the
+                headline shape; one scale after the fused add) and the
+                per-head QK-norm on a fused q/k/v buffer;
   calibration   a plain device-to-device copy of the step's byte count.
 """
 
@@ -51,8 +52,14 @@ DOMINANT_KERNEL = {
     "fusedadd_bwd_bf16_m8192_n8192": "bwd_stage1_kernel",
     "fwd_fp8row_bf16_m4096_n8192": "fwd_pp_kernel",
     "fusedadd_fp8tensor_bf16_m16384_n4096_gf32": "fwd_reg_kernel",
+    "qknorm_bf16_t16384_hq32_hk8_d128": "qk_norm_kernel",
 }
 DT_NAMES = {0: "f32", 1: "f16", 2: "bf16"}
+
+
+def rows_of(w) -> int:
+    """Normalised rows per step (head vectors for the QK-norm)."""
+    return w.M * (w.heads_q + w.heads_k) if w.kind == "qk" else w.M
 
 
 def kernel_source_hash() -> str:
@@ -89,7 +96,8 @@ class Runner:
         big = M * N * w.esize
         per_replica = {"fwd": 2 * big, "fused_add": 3 * big, "bwd": 3 * big,
                        "fused_add_bwd": 4 * big,
-                       "quant": (2 if w.fused_quant else 1) * big + M * N}[w.kind]
+                       "quant": (2 if w.fused_quant else 1) * big + M * N,
+                       "qk": M * (w.heads_q + 2 * w.heads_k) * N * w.esize}[w.kind]
         self.replicas = max(1, int(-(-rotate_bytes // per_replica))) if rotate_bytes > 0 else 1
         x0 = dev_copy(host_inputs["x"], w.x_dt)
         g = dev_copy(host_inputs["gamma"], w.g_dt)
@@ -112,6 +120,9 @@ class Runner:
             dres0 = dev_copy(host_inputs["dres"], w.x_dt)
         if w.kind == "fused_add" or (w.kind == "quant" and w.fused_quant):
             r0 = dev_copy(host_inputs["r"], w.x_dt)
+        if w.kind == "qk":
+            self.gamma_k = dev_copy(host_inputs["gamma_k"], w.g_dt)
+            self.qkv_stride = (w.heads_q + 2 * w.heads_k) * N
         if w.kind == "quant" and w.quant_mode == 1:
             self.tensor_scale = torch.tensor([w.tensor_scale], dtype=torch.float32, device=dev)
         for i in range(self.replicas):
@@ -123,6 +134,8 @@ class Runner:
                 s["r"] = r0 if i == 0 else r0.clone()
                 s["y"] = torch.empty_like(x0)
                 s["rstd"] = torch.empty(M, dtype=torch.float32, device=dev) if w.store_rstd else None
+            elif w.kind == "qk":
+                pass  # in place on the fused q/k/v buffer "x"
             elif w.kind == "quant":
                 s["r"] = (r0 if i == 0 else r0.clone()) if w.fused_quant else None
                 s["q"] = torch.empty(M * N, dtype=torch.uint8, device=dev)
@@ -152,6 +165,11 @@ class Runner:
                 args = (p["x"], p["r"], g.data_ptr(), p["y"], p["rstd"], M, N, w.eps, w.x_dt,
                         w.g_dt, self.stream_handle)
                 self.calls.append((lib.rmsnorm_fused_add_fwd, args))
+            elif w.kind == "qk":
+                args = (p["x"], p["x"] + w.heads_q * N * w.esize, g.data_ptr(),
+                        self.gamma_k.data_ptr(), M, w.heads_q, w.heads_k, N, self.qkv_stride,
+                        self.qkv_stride, w.eps, w.x_dt, w.g_dt, self.stream_handle)
+                self.calls.append((lib.rmsnorm_qk_fwd, args))
             elif w.kind == "quant":
                 args = (p["x"], p["r"], g.data_ptr(), p["q"], p["scale"], w.quant_mode, p["rstd"],
                         M, N, w.eps, w.x_dt, w.g_dt, self.stream_handle)
@@ -228,6 +246,14 @@ def cpu_baseline(w, host_inputs: dict, seconds: float) -> dict:
         def one_pass():
             O.rmsnorm_fused_add_fwd(x, host_inputs["r"], g, M, N, w.eps, w.x_dt, w.g_dt,
                                     want_exact=False)
+    elif w.kind == "qk":
+        S = (w.heads_q + 2 * w.heads_k) * N
+
+        def one_pass():
+            buf, _ = O.rmsnorm_heads_fwd(x.reshape(-1), g, M, w.heads_q, N, S, w.eps, w.x_dt,
+                                         w.g_dt)
+            O.rmsnorm_heads_fwd(buf, host_inputs["gamma_k"], M, w.heads_k, N, S, w.eps, w.x_dt,
+                                w.g_dt, offset=w.heads_q * N)
     elif w.kind == "quant":
         def one_pass():
             O.rmsnorm_quant_fwd(x, g, M, N, w.eps, w.x_dt, w.g_dt, w.quant_mode,
@@ -312,7 +338,7 @@ def main() -> int:
                    "io_dtype": DT_NAMES[w.x_dt], "gamma_dtype": DT_NAMES[w.g_dt], "eps": w.eps,
                    "rstd_out": w.store_rstd, "rotation_replicas": run.replicas,
                    "algorithmic_bytes_per_step": nbytes},
-        "rows_per_s": round(w.M / (ms * 1e-3), 1),
+        "rows_per_s": round(rows_of(w) / (ms * 1e-3), 1),
         "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / PEAK_GBPS, 4),
@@ -339,7 +365,7 @@ def main() -> int:
             ob = ow.algorithmic_bytes()
             others[ow.name] = {"ms_per_step": round(oms, 6), "gbps": round(ob / (oms * 1e-3) / 1e9, 2),
                                "pct_of_peak": round(100 * ob / (oms * 1e-3) / 1e9 / PEAK_GBPS, 2),
-                               "rows_per_s": round(ow.M / (oms * 1e-3), 1),
+                               "rows_per_s": round(rows_of(ow) / (oms * 1e-3), 1),
                                "steps": k, "rotation_replicas": orun.replicas}
             if ow.kind in ("bwd", "fused_add_bwd"):
                 others[ow.name]["workspace_bytes"] = orun.ws_bytes

@@ -108,7 +108,7 @@ def raw_bits(seed: int, stream: int, n: int) -> np.ndarray:
 class Workload:
     """One benchmark / parity workload."""
     name: str
-    kind: str            # "fwd", "fused_add", "bwd", "fused_add_bwd", "quant"
+    kind: str            # "fwd", "fused_add", "bwd", "fused_add_bwd", "quant", "qk"
     M: int
     N: int
     x_dt: int
@@ -121,6 +121,8 @@ class Workload:
     quant_mode: int = 0         # "quant": 1 = one tensor scale, 2 = per-row scales
     fused_quant: bool = False   # "quant": fused residual add first
     tensor_scale: float = 0.0125  # "quant", one tensor scale: |y| > 5.6 saturates
+    heads_q: int = 0            # "qk": M tokens of heads_q + heads_k vectors of N = head_dim,
+    heads_k: int = 0            #   in a fused q/k/v buffer of (heads_q + 2 heads_k) N per token
 
     @property
     def esize(self) -> int:
@@ -138,6 +140,9 @@ class Workload:
             return 2 * big + g + (4 * self.M if self.store_rstd else 0)
         if self.kind == "fused_add":
             return 4 * big + g + (4 * self.M if self.store_rstd else 0)
+        if self.kind == "qk":
+            # read and write every q and k head vector (v is never touched)
+            return 2 * self.M * (self.heads_q + self.heads_k) * self.N * self.esize + 2 * g
         if self.kind == "quant":
             # read x (and r, writing h), write the fp8 codes (1 byte each),
             # per-row scales (read one scale per tensor).
@@ -175,6 +180,8 @@ EXTRA_WORKLOADS = [
              quant_mode=2),
     Workload("fusedadd_fp8tensor_bf16_m16384_n4096_gf32", "quant", 16384, 4096, BF16, F32, 1e-5,
              1008, quant_mode=1, fused_quant=True),
+    Workload("qknorm_bf16_t16384_hq32_hk8_d128", "qk", 16384, 128, BF16, BF16, 1e-6, 1009,
+             heads_q=32, heads_k=8),
 ]
 WORKLOADS_BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
@@ -188,6 +195,12 @@ def make_inputs(w: Workload, nthreads: int | None = None) -> dict:
            "gamma": uniform(w.seed, STREAM_GAMMA, w.N, 0.5, 1.5, w.g_dt, nthreads=nthreads)}
     if w.kind == "fused_add" or (w.kind == "quant" and w.fused_quant):
         out["r"] = normal(w.seed, STREAM_R, w.M, w.N, w.x_dt, nthreads=nthreads)
+    if w.kind == "qk":
+        # the whole fused q/k/v buffer; q's gamma is "gamma", k's "gamma_k"
+        out["x"] = normal(w.seed, STREAM_X, w.M, (w.heads_q + 2 * w.heads_k) * w.N, w.x_dt,
+                          nthreads=nthreads)
+        out["gamma_k"] = uniform(w.seed + 1, STREAM_GAMMA, w.N, -1.0, 1.0, w.g_dt,
+                                 nthreads=nthreads)
     if w.kind in ("bwd", "fused_add_bwd"):
         out["dy"] = normal(w.seed, STREAM_DY, w.M, w.N, w.x_dt, nthreads=nthreads)
     if w.kind == "fused_add_bwd":

@@ -119,6 +119,27 @@ int rmsnorm_quant_fwd(const void* x, void* residual, const void* gamma, void* q,
                       float* scale, int quant_mode, float* rstd, int64_t M, int64_t N,
                       float eps, int x_dtype, int gamma_dtype, hipStream_t stream);
 
+/* Per-head RMSNorm of q and k, in place, in one launch (QK-norm; the
+ * "TIRx kernels" page lists flashinfer.norm's qk_rmsnorm among its FlashInfer
+ * ports without a definition). Reading taken: q is [tokens, q_heads,
+ * head_dim] and k [tokens, k_heads, head_dim]; every head vector is one
+ * RMSNorm row of head_dim elements (as in rmsnorm_fwd) with its tensor's
+ * gamma[head_dim], overwritten by its normalised value.
+ *   q, k       head h of token t starts at element t * stride + h * head_dim
+ *              (heads contiguous, tokens q_stride / k_stride elements apart,
+ *              stride >= heads * head_dim). k may be NULL with k_heads == 0.
+ *              q and k may interleave inside one buffer (a fused QKV
+ *              projection) provided their per-token windows are disjoint and
+ *              share one stride; any other overlap is RMSN_ERR_OVERLAP.
+ *              Elements between windows are not touched.
+ *   q_gamma, k_gamma  [head_dim] gamma_dtype, read.
+ *   tokens >= 0, q_heads >= 1, k_heads >= 0, 1 <= head_dim <= 8192, and
+ *   tokens * heads below 2^31 for each tensor (else RMSN_ERR_SHAPE). */
+int rmsnorm_qk_fwd(void* q, void* k, const void* q_gamma, const void* k_gamma,
+                   int64_t tokens, int64_t q_heads, int64_t k_heads, int64_t head_dim,
+                   int64_t q_stride, int64_t k_stride, float eps, int x_dtype,
+                   int gamma_dtype, hipStream_t stream);
+
 /* Bytes of device workspace rmsnorm_bwd needs for an [M, N] problem of the
  * given activation dtype: fp32 per-workgroup dgamma partials (and per-row
  * scalars for rows too long to keep on chip). Pure host function; returns 0

@@ -2,13 +2,15 @@
 
 The C ABI (include/rmsnorm_mi355x.h) is exposed under the same names
 (``rmsnorm_fwd``, ``rmsnorm_fused_add_fwd``, ``rmsnorm_bwd``,
-``rmsnorm_fused_add_bwd``, ``rmsnorm_quant_fwd``, ``rmsnorm_bwd_workspace_size``,
+``rmsnorm_fused_add_bwd``, ``rmsnorm_quant_fwd``, ``rmsnorm_qk_fwd``,
+``rmsnorm_bwd_workspace_size``,
 ``rmsnorm_status_string``,
 ``rmsnorm_last_hip_error``); those functions only marshal arguments. Pointers
 may be given as integers or as torch tensors (their ``data_ptr()``); streams as
 integers or ``torch.cuda.Stream`` objects.
 
-``fwd``, ``fused_add_fwd``, ``quant_fwd``, ``bwd`` and ``fused_add_bwd`` are torch conveniences on top: they use
+``fwd``, ``fused_add_fwd``, ``quant_fwd``, ``qk_fwd``, ``bwd`` and ``fused_add_bwd`` are torch
+conveniences on top: they use
 torch only to allocate outputs and to pick the current stream, and every step
 of the computation runs in the library's HIP kernels. There is no fallback: if
 the library is not built, every call raises.
@@ -31,7 +33,8 @@ STATUS_NAMES = {
     -4: "RMSN_ERR_WORKSPACE", -5: "RMSN_ERR_OVERLAP", -6: "RMSN_ERR_ALIGN",
     -7: "RMSN_ERR_EPS", -8: "RMSN_ERR_MODE", -100: "RMSN_ERR_HIP",
 }
-ENTRY_POINTS = ("rmsnorm_fwd", "rmsnorm_fused_add_fwd", "rmsnorm_quant_fwd", "rmsnorm_bwd",
+ENTRY_POINTS = ("rmsnorm_fwd", "rmsnorm_fused_add_fwd", "rmsnorm_quant_fwd", "rmsnorm_qk_fwd",
+                "rmsnorm_bwd",
                 "rmsnorm_fused_add_bwd", "rmsnorm_bwd_workspace_size", "rmsnorm_status_string",
                 "rmsnorm_last_hip_error")
 
@@ -67,6 +70,9 @@ def load_library(path: str | None = None):
     lib.rmsnorm_fused_add_fwd.restype = i32
     lib.rmsnorm_quant_fwd.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, i64, f32, i32, i32, vp]
     lib.rmsnorm_quant_fwd.restype = i32
+    lib.rmsnorm_qk_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, i32,
+                                   vp]
+    lib.rmsnorm_qk_fwd.restype = i32
     lib.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i32]
     lib.rmsnorm_bwd_workspace_size.restype = ctypes.c_size_t
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i32, i32, vp]
@@ -118,6 +124,13 @@ def rmsnorm_quant_fwd(x, residual, gamma, q, scale, quant_mode, rstd, M, N, eps,
     return load_library().rmsnorm_quant_fwd(_p(x), _p(residual), _p(gamma), _p(q), _p(scale),
                                             quant_mode, _p(rstd), M, N, eps, x_dtype,
                                             gamma_dtype, _s(stream))
+
+
+def rmsnorm_qk_fwd(q, k, q_gamma, k_gamma, tokens, q_heads, k_heads, head_dim, q_stride,
+                   k_stride, eps, x_dtype, gamma_dtype, stream) -> int:
+    return load_library().rmsnorm_qk_fwd(_p(q), _p(k), _p(q_gamma), _p(k_gamma), tokens, q_heads,
+                                         k_heads, head_dim, q_stride, k_stride, eps, x_dtype,
+                                         gamma_dtype, _s(stream))
 
 
 def rmsnorm_bwd_workspace_size(M, N, x_dtype) -> int:
@@ -223,6 +236,29 @@ def quant_fwd(x, gamma, eps: float = 1e-5, *, scale=None, residual=None, want_rs
     _check(rmsnorm_quant_fwd(x, residual, gamma, q, scale, mode, rstd, M, N, eps, dtype_code(x),
                              dtype_code(gamma), stream), "rmsnorm_quant_fwd")
     return q, scale, rstd
+
+
+def qk_fwd(q, k, q_gamma, k_gamma=None, eps: float = 1e-6, *, stream=None):
+    """Per-head RMSNorm of q [T, Hq, D] and k [T, Hk, D] (k may be None), in
+    place. Head vectors must be contiguous and heads D apart (views of a
+    fused QKV buffer qualify); tokens may be strided. Returns (q, k)."""
+    import torch
+
+    def layout(t, name):
+        if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError(f"{name}: expected [T, H, D] with contiguous heads")
+        return t.shape[0], t.shape[1], t.shape[2], t.stride(0)
+
+    T, Hq, D, sq = layout(q, "q")
+    Hk, sk = 0, 0
+    if k is not None:
+        Tk, Hk, Dk, sk = layout(k, "k")
+        if (Tk, Dk) != (T, D) or k.dtype != q.dtype:
+            raise ValueError("k must match q in tokens, head_dim and dtype")
+    stream = torch.cuda.current_stream(q.device) if stream is None else stream
+    _check(rmsnorm_qk_fwd(q, k, q_gamma, k_gamma if k is not None else None, T, Hq, Hk, D, sq, sk,
+                          eps, dtype_code(q), dtype_code(q_gamma), stream), "rmsnorm_qk_fwd")
+    return q, k
 
 
 def bwd(dy, x, rstd, gamma, *, dx=None, dgamma=None, workspace=None, stream=None):

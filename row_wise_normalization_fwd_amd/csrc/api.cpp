@@ -131,6 +131,67 @@ int quant_forward(const void* x, void* residual, const void* gamma, void* q, flo
   }
 }
 
+// Element sets of two strided tensors (token t occupies [base + t*stride,
+// base + t*stride + len) bytes) are disjoint: their spans do not meet, or
+// they share the stride and each token window of one sits in a gap of the
+// other's lattice (q and k inside one fused projection buffer).
+bool strided_disjoint(Range a, uint64_t sa, uint64_t la, Range b, uint64_t sb, uint64_t lb) {
+  if (!overlap(a, b)) return true;
+  if (sa != sb || la + lb > sa) return false;
+  const uint64_t d = (static_cast<uint64_t>(b.lo) - static_cast<uint64_t>(a.lo)) % sa;
+  return d >= la && d + lb <= sa;
+}
+
+// Validation of the per-head QK-RMSNorm (in place on q and k).
+int qk_forward(void* q, void* k, const void* q_gamma, const void* k_gamma, int64_t tokens,
+               int64_t q_heads, int64_t k_heads, int64_t head_dim, int64_t q_stride,
+               int64_t k_stride, float eps, int x_dtype, int gamma_dtype, hipStream_t stream) {
+  if (!valid_pair(x_dtype, gamma_dtype)) return RMSN_ERR_DTYPE;
+  if (tokens < 0 || q_heads < 1 || k_heads < 0 || head_dim < 1 || head_dim > rmsn::kRegMaxN)
+    return RMSN_ERR_SHAPE;
+  if (q_stride < q_heads * head_dim || (k_heads > 0 && k_stride < k_heads * head_dim))
+    return RMSN_ERR_SHAPE;
+  if (tokens > INT32_MAX / q_heads || (k_heads > 0 && tokens > INT32_MAX / k_heads))
+    return RMSN_ERR_SHAPE;
+  const int es = esize_of(x_dtype), gs = esize_of(gamma_dtype);
+  // Spans must be addressable.
+  if (tokens > 0 && (q_stride > (INT64_MAX / 8) / tokens ||
+                     (k_heads > 0 && k_stride > (INT64_MAX / 8) / tokens)))
+    return RMSN_ERR_SHAPE;
+  if (!std::isfinite(eps) || eps < 0.0f) return RMSN_ERR_EPS;
+  if (tokens == 0) return RMSN_OK;
+  if (!q || !q_gamma || (k_heads > 0 && (!k || !k_gamma))) return RMSN_ERR_NULL;
+  if (!aligned(q, es) || !aligned(q_gamma, gs) ||
+      (k_heads > 0 && (!aligned(k, es) || !aligned(k_gamma, gs))))
+    return RMSN_ERR_ALIGN;
+  auto tensor_span = [&](const void* p, int64_t heads, int64_t stride) {
+    return span(p, static_cast<uint64_t>((tokens - 1) * stride + heads * head_dim) * es);
+  };
+  const Range rq = tensor_span(q, q_heads, q_stride);
+  const Range rgq = span(q_gamma, static_cast<uint64_t>(head_dim) * gs);
+  if (overlap(rq, rgq)) return RMSN_ERR_OVERLAP;
+  if (k_heads > 0) {
+    const Range rk = tensor_span(k, k_heads, k_stride);
+    const Range rgk = span(k_gamma, static_cast<uint64_t>(head_dim) * gs);
+    if (overlap(rk, rgk) || overlap(rq, rgk) || overlap(rk, rgq)) return RMSN_ERR_OVERLAP;
+    if (!strided_disjoint(rq, static_cast<uint64_t>(q_stride) * es,
+                          static_cast<uint64_t>(q_heads * head_dim) * es, rk,
+                          static_cast<uint64_t>(k_stride) * es,
+                          static_cast<uint64_t>(k_heads * head_dim) * es))
+      return RMSN_ERR_OVERLAP;
+  }
+  rmsn::QKCall c{{q, k_heads > 0 ? k : nullptr},
+                 {q_gamma, k_heads > 0 ? k_gamma : nullptr},
+                 {q_stride, k_stride},
+                 {q_heads, k_heads},
+                 tokens,
+                 head_dim,
+                 eps,
+                 gamma_dtype,
+                 stream};
+  return finish(rmsn::launch_qk(c, x_dtype));
+}
+
 }  // namespace
 
 namespace rmsn {
@@ -255,6 +316,14 @@ int rmsnorm_quant_fwd(const void* x, void* residual, const void* gamma, void* q,
                       int gamma_dtype, hipStream_t stream) {
   return quant_forward(x, residual, gamma, q, scale, quant_mode, rstd, M, N, eps, x_dtype,
                        gamma_dtype, stream);
+}
+
+int rmsnorm_qk_fwd(void* q, void* k, const void* q_gamma, const void* k_gamma, int64_t tokens,
+                   int64_t q_heads, int64_t k_heads, int64_t head_dim, int64_t q_stride,
+                   int64_t k_stride, float eps, int x_dtype, int gamma_dtype,
+                   hipStream_t stream) {
+  return qk_forward(q, k, q_gamma, k_gamma, tokens, q_heads, k_heads, head_dim, q_stride,
+                    k_stride, eps, x_dtype, gamma_dtype, stream);
 }
 
 size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int x_dtype) {

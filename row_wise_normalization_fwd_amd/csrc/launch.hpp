@@ -73,6 +73,23 @@ hipError_t launch_fwd_quant_f32(const FwdCall& c);
 hipError_t launch_fwd_quant_f16(const FwdCall& c);
 hipError_t launch_fwd_quant_bf16(const FwdCall& c);
 
+// Per-head QK-RMSNorm, in place: tensor 0 is q, tensor 1 is k (x[1] null or
+// heads[1] == 0 when absent). Heads of a token are contiguous, tokens are
+// stride[i] elements apart; N is head_dim (<= kRegMaxN).
+struct QKCall {
+  void* x[2];
+  const void* gamma[2];
+  int64_t stride[2];
+  int64_t heads[2];
+  int64_t tokens;
+  int64_t N;
+  float eps;
+  int gamma_dtype;
+  hipStream_t stream;
+};
+
+hipError_t launch_qk(const QKCall& c, int x_dtype);
+
 // Backward partition: G = min(M, kBwdTargetBlocks) blocks, block b owning
 // rows b, b + G, b + 2G, ... It depends only on M, which fixes the dgamma
 // summation order. The workspace holds the fp32 partial rows [G, N] and, for

@@ -202,3 +202,35 @@ def test_quant_validation(lib):
     assert quant(r=C) == OVERLAP                    # residual over q
     assert quant(r=A + 2) == OVERLAP                # residual partially over x
     assert R.rmsnorm_status_string(MODE) == "unknown quantisation mode"
+
+
+def qk(q=A, k=A + 4096 * 2, gq=E, gk=F, T=16, Hq=32, Hk=8, D=128, sq=6144, sk=6144, eps=1e-6,
+       xd=BF16, gd=BF16):
+    # Default layout: a fused QKV buffer at A, q at offset 0 and k right after
+    # q's 32 heads, token stride (32 + 8 + 8) * 128 elements.
+    return R.rmsnorm_qk_fwd(q, k, gq, gk, T, Hq, Hk, D, sq, sk, eps, xd, gd, None)
+
+
+def test_qk_validation(lib):
+    assert qk(xd=9) == DTYPE
+    assert qk(Hq=0) == SHAPE
+    assert qk(Hk=-1) == SHAPE
+    assert qk(D=0) == SHAPE
+    assert qk(D=8193, sq=10 ** 6, sk=10 ** 6) == SHAPE
+    assert qk(sq=32 * 128 - 1) == SHAPE
+    assert qk(sk=8 * 128 - 1) == SHAPE
+    assert qk(T=2 ** 26, Hq=32) == SHAPE                 # tokens * heads >= 2^31
+    assert qk(eps=-1.0) == EPS
+    assert qk(T=0, q=None, k=None, gq=None, gk=None) == OK
+    assert qk(q=None) == NULL
+    assert qk(gq=None) == NULL
+    assert qk(k=None) == NULL                            # k_heads > 0 needs k
+    assert qk(gk=None) == NULL
+    assert qk(q=A + 1) == ALIGN
+    assert qk(k=A + 8193) == ALIGN
+    assert qk(gq=E + 1) == ALIGN
+    assert qk(k=A + 4096 * 2 - 2) == OVERLAP             # k's window starts inside q's
+    assert qk(k=A + 6144 * 2 - 8 * 128 * 2 + 2) == OVERLAP   # k's window wraps into the next q
+    assert qk(sk=6144 + 8) == OVERLAP                    # strides differ, spans meet
+    assert qk(gq=A + 100) == OVERLAP                     # gamma inside the q span
+    assert qk(gk=A + 4096 * 2 + 64) == OVERLAP           # k gamma inside the k span

@@ -368,6 +368,79 @@ def test_quant_matches_plain_forward_values():
     assert np.all(np.abs(deq - yv) <= np.abs(yv) / 8 + to_host(sc)[:, None] * 2.0 ** -9 + 1e-6)
 
 
+# ------------------------------------------------------ per-head QK-RMSNorm
+
+def run_qk(T, Hq, Hk, D, xdt, gdt, layout="fused", pad=0, misalign=0, seed=23, eps=1e-6):
+    """layout "fused": q, k, v of each token interleaved in one buffer (token
+    stride (Hq + 2 Hk) D + pad); "separate": contiguous q and k buffers;
+    "q_only": no k. Every element outside the head windows must survive."""
+    _log(f"qk T={T} Hq={Hq} Hk={Hk} D={D} x={xdt} g={gdt} layout={layout} pad={pad} "
+         f"misalign={misalign}")
+    es = 4 if xdt == O.F32 else 2
+    gq = G.uniform(seed, G.STREAM_GAMMA, D, 0.5, 1.5, gdt)
+    gk = G.uniform(seed + 1, G.STREAM_GAMMA, D, -1.0, 1.0, gdt)
+    if layout == "fused":
+        S = (Hq + 2 * Hk) * D + pad
+        buf = G.normal(seed, G.STREAM_X, 1, T * S, xdt).reshape(-1)
+        want, _ = O.rmsnorm_heads_fwd(buf, gq, T, Hq, D, S, eps, xdt, gdt, offset=0)
+        want, _ = O.rmsnorm_heads_fwd(want, gk, T, Hk, D, S, eps, xdt, gdt, offset=Hq * D)
+        bt = _put(buf, xdt, misalign)
+        args = (bt.data_ptr(), bt.data_ptr() + Hq * D * es, T, Hq, Hk, D, S, S)
+        mask = np.zeros((T, S), bool)
+        mask[:, :(Hq + Hk) * D] = True
+        outs = [(bt, buf, want, mask.reshape(-1))]
+    else:
+        sq, sk = Hq * D + pad, Hk * D + pad
+        qb = G.normal(seed, G.STREAM_X, 1, T * sq, xdt).reshape(-1)
+        wq, _ = O.rmsnorm_heads_fwd(qb, gq, T, Hq, D, sq, eps, xdt, gdt)
+        qt = _put(qb, xdt, misalign)
+        mq = np.zeros((T, sq), bool)
+        mq[:, :Hq * D] = True
+        outs = [(qt, qb, wq, mq.reshape(-1))]
+        if layout == "separate":
+            kb = G.normal(seed, G.STREAM_R, 1, T * sk, xdt).reshape(-1)
+            wk, _ = O.rmsnorm_heads_fwd(kb, gk, T, Hk, D, sk, eps, xdt, gdt)
+            kt = _put(kb, xdt, misalign)
+            mk = np.zeros((T, sk), bool)
+            mk[:, :Hk * D] = True
+            outs.append((kt, kb, wk, mk.reshape(-1)))
+            args = (qt.data_ptr(), kt.data_ptr(), T, Hq, Hk, D, sq, sk)
+        else:
+            args = (qt.data_ptr(), None, T, Hq, 0, D, sq, 0)
+    q, k, T_, Hq_, Hk_, D_, sq_, sk_ = args
+    st = R.rmsnorm_qk_fwd(q, k, _put(gq, gdt), _put(gk, gdt) if k else None, T_, Hq_, Hk_, D_,
+                          sq_, sk_, eps, xdt, gdt, _stream())
+    assert st == 0, R.rmsnorm_status_string(st)
+    torch.cuda.synchronize()
+    for t, before, want, moved in outs:
+        got = to_host(t)
+        # Untouched elements bit for bit; normalised ones within the forward's tolerance.
+        if xdt == O.F32:
+            assert np.array_equal(got.view(np.uint32)[~moved], before.view(np.uint32)[~moved])
+        else:
+            assert np.array_equal(got[~moved], before[~moved])
+        exact = O.decode(want, xdt)
+        check_output(got[moved], exact[moved], want[moved], xdt, "qk")
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("D", [64, 96, 128, 256, 512])
+def test_qk_fused_buffer(D, pair):
+    run_qk(3, 32, 8, D, *pair, seed=1500 + D)
+    run_qk(257, 16, 16, D, *pair, seed=1600 + D, pad=8)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_qk_layouts_and_edges(pair):
+    run_qk(100, 8, 2, 128, *pair, layout="separate", seed=1701)
+    run_qk(100, 8, 0, 128, *pair, layout="q_only", seed=1702)
+    run_qk(9, 4, 2, 128, *pair, seed=1703, misalign=1)            # 1-element units
+    run_qk(9, 4, 2, 100, *pair, seed=1704, pad=3)                 # ragged head_dim and stride
+    run_qk(1, 1, 1, 8, *pair, seed=1705)
+    run_qk(5, 2, 1, 8192, *pair, layout="separate", seed=1706)    # longest head vector
+    run_qk(2000, 1, 1, 2, *pair, seed=1707)
+
+
 # ----------------------------------------------------------------- backward
 
 def run_bwd(M, N, xdt, gdt, seed=13, misalign=0, alias=None, gpu_rstd=False, eps=1e-5):
@@ -571,6 +644,8 @@ def test_workload_full_size(w):
         run_fused(w.M, w.N, w.x_dt, w.g_dt, eps=w.eps, seed=w.seed, want_rstd=w.store_rstd)
     elif w.kind == "fused_add_bwd":
         run_fused_bwd(w.M, w.N, w.x_dt, w.g_dt, seed=w.seed)
+    elif w.kind == "qk":
+        run_qk(w.M, w.heads_q, w.heads_k, w.N, w.x_dt, w.g_dt, seed=w.seed, eps=w.eps)
     elif w.kind == "quant":
         steps = run_quant(w.M, w.N, w.x_dt, w.g_dt, w.quant_mode, seed=w.seed, eps=w.eps,
                           fused=w.fused_quant, want_rstd=w.store_rstd,
