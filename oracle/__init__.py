@@ -64,10 +64,15 @@ def _load():
     lib.oracle_rmsnorm_quant_fwd.argtypes = [vp, vp, vp, i64, i64, f32, i32, i32, i32, f32,
                                              vp, vp, dp, dp, vp, vp]
     lib.oracle_rmsnorm_heads_fwd.argtypes = [vp, vp, i64, i64, i64, i64, f32, i32, i32, vp]
+    lib.oracle_layernorm_fwd.argtypes = [vp, vp, vp, i64, i64, f32, i32, i32, dp, vp, dp, dp,
+                                         vp, vp, dp]
+    lib.oracle_layernorm_bwd.argtypes = [vp, vp, dp, dp, vp, i64, i64, i32, i32, dp, vp, dp, dp,
+                                         dp, dp, dp, dp, dp, dp]
     for fn in (lib.oracle_decode, lib.oracle_round, lib.oracle_rmsnorm_fwd,
                lib.oracle_rmsnorm_fused_add_fwd, lib.oracle_rmsnorm_bwd,
                lib.oracle_rmsnorm_fused_add_bwd, lib.oracle_rmsnorm_quant_fwd,
-               lib.oracle_rmsnorm_heads_fwd):
+               lib.oracle_rmsnorm_heads_fwd, lib.oracle_layernorm_fwd,
+               lib.oracle_layernorm_bwd):
         fn.restype = None
     _lib = lib
     return lib
@@ -225,3 +230,48 @@ def rmsnorm_heads_fwd(buf, gamma, tokens, heads, head_dim, stride, eps, x_dt, g_
     _load().oracle_rmsnorm_heads_fwd(_ptr(view) if view.size else None, _ptr(gamma), tokens,
                                      heads, head_dim, stride, eps, x_dt, g_dt, _ptr(rstd))
     return buf, rstd
+
+
+def layernorm_fwd(x, gamma, beta, M, N, eps, x_dt, g_dt, want_exact=True):
+    """LayerNorm forward (beta may be None). Returns dict: y_exact (M,N) f64 or
+    None, y (M,N) storage, mean_exact, rstd_exact (M,) f64, mean, rstd (M,)
+    fp32, amag (M,) f64 = mean |x| per row."""
+    x = _check(x, x_dt, M * N, "x")
+    gamma = _check(gamma, g_dt, N, "gamma")
+    if beta is not None:
+        beta = _check(beta, g_dt, N, "beta")
+    out = {"y_exact": np.empty((M, N), np.float64) if want_exact else None,
+           "y": np.empty((M, N), storage_dtype(x_dt)),
+           "mean_exact": np.empty(M, np.float64), "rstd_exact": np.empty(M, np.float64),
+           "mean": np.empty(M, np.float32), "rstd": np.empty(M, np.float32),
+           "amag": np.empty(M, np.float64)}
+    _load().oracle_layernorm_fwd(_ptr(x), _ptr(gamma), _ptr(beta), M, N, eps, x_dt, g_dt,
+                                 _ptr(out["y_exact"]), _ptr(out["y"]), _ptr(out["mean_exact"]),
+                                 _ptr(out["rstd_exact"]), _ptr(out["mean"]), _ptr(out["rstd"]),
+                                 _ptr(out["amag"]))
+    return out
+
+
+def layernorm_bwd(dy, x, mean, rstd, gamma, M, N, x_dt, g_dt, want_exact=True):
+    """LayerNorm backward with saved mean / rstd (any float arrays, widened to
+    double). Returns dict: dx_exact, dx (storage), dgamma, dbeta, c1, c2, a1,
+    a2, sg, sb (all f64 but dx)."""
+    dy = _check(dy, x_dt, M * N, "dy")
+    x = _check(x, x_dt, M * N, "x")
+    gamma = _check(gamma, g_dt, N, "gamma")
+    mean = np.ascontiguousarray(mean, dtype=np.float64)
+    rstd = np.ascontiguousarray(rstd, dtype=np.float64)
+    if mean.size != M or rstd.size != M:
+        raise ValueError("mean / rstd: expected M elements")
+    out = {"dx_exact": np.empty((M, N), np.float64) if want_exact else None,
+           "dx": np.empty((M, N), storage_dtype(x_dt))}
+    for k in ("dgamma", "dbeta", "sg", "sb"):
+        out[k] = np.empty(N, np.float64)
+    for k in ("c1", "c2", "a1", "a2"):
+        out[k] = np.empty(M, np.float64)
+    _load().oracle_layernorm_bwd(_ptr(dy), _ptr(x), _ptr(mean), _ptr(rstd), _ptr(gamma), M, N,
+                                 x_dt, g_dt, _ptr(out["dx_exact"]), _ptr(out["dx"]),
+                                 _ptr(out["dgamma"]), _ptr(out["dbeta"]), _ptr(out["c1"]),
+                                 _ptr(out["c2"]), _ptr(out["a1"]), _ptr(out["a2"]),
+                                 _ptr(out["sg"]), _ptr(out["sb"]))
+    return out

@@ -29,6 +29,16 @@
 //     where rho_i is the rstd handed in.
 //   * Rounding to bf16 / fp16 / fp32: round to nearest, ties to even (the FlyDSL
 //     guide, section 1.1, states RNE for the bf16 pack; IEEE default otherwise).
+//   * LayerNorm ("Pre-built kernel library guide" (FlyDSL), section 1.1):
+//       y_ij = (x_ij - mean_i) / sqrt(var_i + eps) * gamma_j + beta_j,
+//     mean_i = (1/N) sum_j x_ij, var_i = (1/N) sum_j (x_ij - mean_i)^2 (the
+//     population variance; the section's pass 1 computes both statistics,
+//     pass 2 the affine map). The pages give no backward; the one here is
+//     the derivative of that forward with the saved mean and rstd:
+//       xhat = (x - mean) rstd,  c1 = (1/N) sum_j gamma dy,
+//       c2 = (1/N) sum_j gamma dy xhat,
+//       dx = rstd (gamma dy - c1 - xhat c2),
+//       dgamma_j = sum_i dy xhat,  dbeta_j = sum_i dy.
 //   * Per-head QK-RMSNorm ("TIRx kernels", FlashInfer ports, flashinfer.norm:
 //     qk_rmsnorm, named without a definition). Reading taken: q holds
 //     [tokens, q_heads, head_dim] and k [tokens, k_heads, head_dim], each head
@@ -373,6 +383,87 @@ void oracle_rmsnorm_heads_fwd(void* x, const void* gamma, int64_t tokens, int64_
                   &rs, nullptr);
       if (rstd_f32) rstd_f32[t * heads + h] = rs;
       for (int64_t j = 0; j < head_dim; ++j) store_value(x, base + j, y[j], x_dt);
+    }
+  }
+}
+
+// LayerNorm forward over an [M, N] array x (format x_dt) with gamma[N] and
+// beta[N] (format g_dt; beta may be null: no bias). Outputs, each optional:
+// y_exact[M*N] (double), y_bits[M*N] (rounded to x_dt), mean_exact[M],
+// rstd_exact[M] (double), mean_f32[M], rstd_f32[M] (rounded to fp32), and
+// amag[M] = (1/N) sum_j |x_ij| (a magnitude for the tests' error floors).
+void oracle_layernorm_fwd(const void* x, const void* gamma, const void* beta, int64_t M,
+                          int64_t N, float eps, int x_dt, int g_dt, double* y_exact,
+                          void* y_bits, double* mean_exact, double* rstd_exact,
+                          float* mean_f32, float* rstd_f32, double* amag) {
+  std::vector<double> v(static_cast<size_t>(N));
+  for (int64_t i = 0; i < M; ++i) {
+    double sum = 0.0, mag = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+      v[j] = decode(x, i * N + j, x_dt);
+      sum += v[j];
+      mag += std::fabs(v[j]);
+    }
+    const double mean = sum / static_cast<double>(N);
+    double sq = 0.0;
+    for (int64_t j = 0; j < N; ++j) sq += (v[j] - mean) * (v[j] - mean);
+    const double var = sq / static_cast<double>(N);
+    const double denom = std::sqrt(var + static_cast<double>(eps));
+    if (mean_exact) mean_exact[i] = mean;
+    if (rstd_exact) rstd_exact[i] = 1.0 / denom;
+    if (mean_f32) mean_f32[i] = static_cast<float>(round_to(mean, kF32));
+    if (rstd_f32) rstd_f32[i] = static_cast<float>(round_to(1.0 / denom, kF32));
+    if (amag) amag[i] = mag / static_cast<double>(N);
+    for (int64_t j = 0; j < N; ++j) {
+      double y = (v[j] - mean) / denom * decode(gamma, j, g_dt);
+      if (beta) y += decode(beta, j, g_dt);
+      if (y_exact) y_exact[i * N + j] = y;
+      if (y_bits) store_value(y_bits, i * N + j, y, x_dt);
+    }
+  }
+}
+
+// LayerNorm backward with the saved per-row mean[M] and rstd[M] (doubles:
+// the fp32 arrays the GPU receives, widened). Outputs, each optional:
+// dx_exact[M*N], dx_bits[M*N] (rounded to x_dt), dgamma[N], dbeta[N]
+// (overwritten), c1[M], c2[M], and the magnitudes a1[M] = (1/N) sum |gamma dy|,
+// a2[M] = (1/N) sum |gamma dy xhat|, sg[N] = sum_i |dy xhat|, sb[N] = sum_i |dy|.
+void oracle_layernorm_bwd(const void* dy, const void* x, const double* mean,
+                          const double* rstd, const void* gamma, int64_t M, int64_t N,
+                          int x_dt, int g_dt, double* dx_exact, void* dx_bits, double* dgamma,
+                          double* dbeta, double* c1, double* c2, double* a1, double* a2,
+                          double* sg, double* sb) {
+  for (int64_t j = 0; j < N; ++j) {
+    if (dgamma) dgamma[j] = 0.0;
+    if (dbeta) dbeta[j] = 0.0;
+    if (sg) sg[j] = 0.0;
+    if (sb) sb[j] = 0.0;
+  }
+  for (int64_t i = 0; i < M; ++i) {
+    double s1 = 0.0, s2 = 0.0, m1 = 0.0, m2 = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+      const double xhat = (decode(x, i * N + j, x_dt) - mean[i]) * rstd[i];
+      const double gdy = decode(gamma, j, g_dt) * decode(dy, i * N + j, x_dt);
+      s1 += gdy;
+      s2 += gdy * xhat;
+      m1 += std::fabs(gdy);
+      m2 += std::fabs(gdy * xhat);
+    }
+    const double k1 = s1 / static_cast<double>(N), k2 = s2 / static_cast<double>(N);
+    if (c1) c1[i] = k1;
+    if (c2) c2[i] = k2;
+    if (a1) a1[i] = m1 / static_cast<double>(N);
+    if (a2) a2[i] = m2 / static_cast<double>(N);
+    for (int64_t j = 0; j < N; ++j) {
+      const double xhat = (decode(x, i * N + j, x_dt) - mean[i]) * rstd[i];
+      const double dyv = decode(dy, i * N + j, x_dt);
+      const double d = rstd[i] * (decode(gamma, j, g_dt) * dyv - k1 - xhat * k2);
+      if (dx_exact) dx_exact[i * N + j] = d;
+      if (dx_bits) store_value(dx_bits, i * N + j, d, x_dt);
+      if (dgamma) dgamma[j] += dyv * xhat;
+      if (dbeta) dbeta[j] += dyv;
+      if (sg) sg[j] += std::fabs(dyv * xhat);
+      if (sb) sb[j] += std::fabs(dyv);
     }
   }
 }

@@ -516,3 +516,116 @@ def test_heads_forward_contiguous_is_the_plain_forward(gen_mod):
     r0, r2 = rs0.reshape(T, H), rs2.reshape(T, H)
     assert np.array_equal(r2[:, 0], r0[:, 0]) and np.array_equal(r2[:, 2], r0[:, 2])
     assert np.array_equal(r2[:, 1], r0[:, 1] / 4)
+
+
+# ------------------------------------------------------------------ LayerNorm
+
+def test_layernorm_alternating_row_closed_form():
+    # A row alternating +a, -a has mean 0 and variance a^2, so
+    # y_j = +-a / sqrt(a^2 + eps) * gamma_j + beta_j.
+    N, eps = 64, 1e-5
+    for a in (0.25, 3.0, 1000.0):
+        x = np.tile([a, -a], N // 2).reshape(1, N)
+        g = np.linspace(0.5, 1.5, N)
+        b = np.linspace(-2.0, 2.0, N)
+        out = O.layernorm_fwd(x, g, b, 1, N, eps, O.F64, O.F64)
+        sign = np.tile([1.0, -1.0], N // 2)
+        want = sign * a / np.sqrt(a * a + np.float64(np.float32(eps))) * g + b
+        np.testing.assert_allclose(out["y_exact"][0], want, rtol=1e-14, atol=1e-14)
+        assert out["mean_exact"][0] == 0.0
+
+
+def test_layernorm_output_statistics_and_invariances(gen_mod):
+    M, N = 6, 257
+    x = gen_mod.normal(51, 1, M, N, O.F64) * 3.0 + 7.0       # large mean
+    g, b = np.ones(N), np.zeros(N)
+    out = O.layernorm_fwd(x, g, b, M, N, 0.0, O.F64, O.F64)
+    y = out["y_exact"]
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-13)
+    np.testing.assert_allclose((y ** 2).mean(axis=1), 1.0, rtol=1e-13)
+    # Shift and (eps = 0) scale invariance.
+    gg = gen_mod.uniform(51, 4, N, 0.5, 1.5, O.F64)
+    bb = gen_mod.uniform(52, 4, N, -1.0, 1.0, O.F64)
+    y0 = O.layernorm_fwd(x, gg, bb, M, N, 0.0, O.F64, O.F64)["y_exact"]
+    y1 = O.layernorm_fwd(x + 1024.0, gg, bb, M, N, 0.0, O.F64, O.F64)["y_exact"]
+    y2 = O.layernorm_fwd(x * 0.125, gg, bb, M, N, 0.0, O.F64, O.F64)["y_exact"]
+    np.testing.assert_allclose(y1, y0, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(y2, y0, rtol=0, atol=1e-13)
+    # Without beta it is the RMSNorm of the centred row (same eps).
+    xc = x - x.mean(axis=1, keepdims=True)
+    ln = O.layernorm_fwd(x, gg, None, M, N, 1e-3, O.F64, O.F64)
+    rms = O.rmsnorm_fwd(xc, gg, M, N, 1e-3, O.F64, O.F64)
+    np.testing.assert_allclose(ln["y_exact"], rms["y_exact"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ln["rstd_exact"], rms["rstd_exact"], rtol=1e-13)
+
+
+def test_layernorm_brute_force_decimal(gen_mod):
+    M, N, eps = 3, 8, 1e-5
+    x = gen_mod.normal(53, 1, M, N, O.BF16)
+    g = gen_mod.uniform(53, 4, N, 0.5, 1.5, O.BF16)
+    b = gen_mod.uniform(54, 4, N, -1.0, 1.0, O.BF16)
+    xd, gd, bd = O.decode(x, O.BF16).reshape(M, N), O.decode(g, O.BF16), O.decode(b, O.BF16)
+    out = O.layernorm_fwd(x, g, b, M, N, eps, O.BF16, O.BF16)
+    ctx = decimal.Context(prec=60)
+    D = decimal.Decimal
+    for i in range(M):
+        s = sum((D(v) for v in xd[i]), D(0))
+        mean = ctx.divide(s, D(N))
+        sq = sum((ctx.multiply(D(v) - mean, D(v) - mean) for v in xd[i]), D(0))
+        denom = ctx.sqrt(ctx.add(ctx.divide(sq, D(N)), D(float(np.float32(eps)))))
+        assert abs(out["mean_exact"][i] - float(mean)) <= 1e-15 * max(1.0, abs(float(mean)))
+        for j in range(N):
+            want = ctx.add(ctx.multiply(ctx.divide(D(xd[i, j]) - mean, denom), D(gd[j])), D(bd[j]))
+            assert abs(out["y_exact"][i, j] - float(want)) <= 1e-14 * (1 + abs(float(want)))
+        assert np.float32(float(ctx.divide(D(1), denom))) == out["rstd"][i]
+
+
+def _ln_loss(x, g, b, dy, M, N, eps):
+    return float((dy * O.layernorm_fwd(x, g, b, M, N, eps, O.F64, O.F64)["y_exact"]).sum())
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-5, 0.3])
+def test_layernorm_backward_matches_finite_differences(eps, gen_mod):
+    M, N = 4, 8
+    x = gen_mod.normal(55, 1, M, N, O.F64)
+    x[2, :] += 30.0                           # a row with a large mean
+    x[3, :] *= 40.0
+    dy = gen_mod.normal(55, 3, M, N, O.F64)
+    g = gen_mod.uniform(55, 4, N, 0.5, 1.5, O.F64)
+    b = gen_mod.uniform(56, 4, N, -1.0, 1.0, O.F64)
+    f = O.layernorm_fwd(x, g, b, M, N, eps, O.F64, O.F64)
+    out = O.layernorm_bwd(dy, x, f["mean_exact"], f["rstd_exact"], g, M, N, O.F64, O.F64)
+
+    def fd(arr, idx, fn):
+        h = 1e-5 * max(1.0, abs(arr[idx]))
+        p, m = arr.copy(), arr.copy()
+        p[idx] += h
+        m[idx] -= h
+        return (fn(p) - fn(m)) / (2 * h)
+
+    fd_x = np.array([[fd(x, (i, j), lambda a: _ln_loss(a, g, b, dy, M, N, eps))
+                      for j in range(N)] for i in range(M)])
+    fd_g = np.array([fd(g, j, lambda a: _ln_loss(x, a, b, dy, M, N, eps)) for j in range(N)])
+    fd_b = np.array([fd(b, j, lambda a: _ln_loss(x, g, a, dy, M, N, eps)) for j in range(N)])
+    scale = np.abs(fd_x).max(axis=1, keepdims=True) + 1e-3
+    assert np.all(np.abs(out["dx_exact"] - fd_x) <= 1e-6 * scale)
+    np.testing.assert_allclose(out["dgamma"], fd_g, rtol=1e-7, atol=1e-9)
+    np.testing.assert_allclose(out["dbeta"], fd_b, rtol=1e-7, atol=1e-9)
+
+
+def test_layernorm_backward_invariants(gen_mod):
+    # Shift invariance: sum_j dx_ij = 0. With eps = 0, scale invariance:
+    # sum_j dx_ij (x_ij - mean_i) = 0.
+    M, N = 8, 300
+    x = gen_mod.normal(57, 1, M, N, O.BF16)
+    dy = gen_mod.normal(57, 3, M, N, O.BF16)
+    g = gen_mod.uniform(57, 4, N, 0.5, 1.5, O.BF16)
+    f = O.layernorm_fwd(x, g, None, M, N, 0.0, O.BF16, O.BF16)
+    out = O.layernorm_bwd(dy, x, f["mean_exact"], f["rstd_exact"], g, M, N, O.BF16, O.BF16)
+    dx = out["dx_exact"]
+    xc = O.decode(x, O.BF16).reshape(M, N) - f["mean_exact"][:, None]
+    mag = np.abs(dx).sum(axis=1)
+    assert np.all(np.abs(dx.sum(axis=1)) <= 1e-13 * mag)
+    assert np.all(np.abs((dx * xc).sum(axis=1)) <= 1e-12 * (np.abs(dx * xc).sum(axis=1)))
+    np.testing.assert_allclose(out["dbeta"], O.decode(dy, O.BF16).reshape(M, N).sum(axis=0),
+                               rtol=1e-15)
