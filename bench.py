@@ -22,8 +22,9 @@ Also reported, in the same JSON line:
   workloads     the other four workloads (fp32 short rows, fused residual add,
                 backward, fp16 ragged rows) and the fused-add backward, timed
                 the same way, the fp8-output forward (per-row scales at the
-                headline shape; one scale after the fused add) and the
-                per-head QK-norm on a fused q/k/v buffer;
+                headline shape; one scale after the fused add), the per-head
+                QK-norm on a fused q/k/v buffer and LayerNorm at the headline
+                shape;
   calibration   a plain device-to-device copy of the step's byte count.
 """
 
@@ -53,6 +54,7 @@ DOMINANT_KERNEL = {
     "fwd_fp8row_bf16_m4096_n8192": "fwd_pp_kernel",
     "fusedadd_fp8tensor_bf16_m16384_n4096_gf32": "fwd_reg_kernel",
     "qknorm_bf16_t16384_hq32_hk8_d128": "qk_norm_kernel",
+    "layernorm_bf16_m4096_n8192": "fwd_pp_kernel",
 }
 DT_NAMES = {0: "f32", 1: "f16", 2: "bf16"}
 
@@ -97,7 +99,8 @@ class Runner:
         per_replica = {"fwd": 2 * big, "fused_add": 3 * big, "bwd": 3 * big,
                        "fused_add_bwd": 4 * big,
                        "quant": (2 if w.fused_quant else 1) * big + M * N,
-                       "qk": M * (w.heads_q + 2 * w.heads_k) * N * w.esize}[w.kind]
+                       "qk": M * (w.heads_q + 2 * w.heads_k) * N * w.esize,
+                       "ln": 2 * big}[w.kind]
         self.replicas = max(1, int(-(-rotate_bytes // per_replica))) if rotate_bytes > 0 else 1
         x0 = dev_copy(host_inputs["x"], w.x_dt)
         g = dev_copy(host_inputs["gamma"], w.g_dt)
@@ -120,6 +123,8 @@ class Runner:
             dres0 = dev_copy(host_inputs["dres"], w.x_dt)
         if w.kind == "fused_add" or (w.kind == "quant" and w.fused_quant):
             r0 = dev_copy(host_inputs["r"], w.x_dt)
+        if w.kind == "ln":
+            self.beta = dev_copy(host_inputs["beta"], w.g_dt)
         if w.kind == "qk":
             self.gamma_k = dev_copy(host_inputs["gamma_k"], w.g_dt)
             self.qkv_stride = (w.heads_q + 2 * w.heads_k) * N
@@ -136,6 +141,10 @@ class Runner:
                 s["rstd"] = torch.empty(M, dtype=torch.float32, device=dev) if w.store_rstd else None
             elif w.kind == "qk":
                 pass  # in place on the fused q/k/v buffer "x"
+            elif w.kind == "ln":
+                s["y"] = torch.empty_like(x0)
+                s["mean"] = torch.empty(M, dtype=torch.float32, device=dev)
+                s["rstd"] = torch.empty(M, dtype=torch.float32, device=dev)
             elif w.kind == "quant":
                 s["r"] = (r0 if i == 0 else r0.clone()) if w.fused_quant else None
                 s["q"] = torch.empty(M * N, dtype=torch.uint8, device=dev)
@@ -165,6 +174,10 @@ class Runner:
                 args = (p["x"], p["r"], g.data_ptr(), p["y"], p["rstd"], M, N, w.eps, w.x_dt,
                         w.g_dt, self.stream_handle)
                 self.calls.append((lib.rmsnorm_fused_add_fwd, args))
+            elif w.kind == "ln":
+                args = (p["x"], g.data_ptr(), self.beta.data_ptr(), p["y"], p["mean"], p["rstd"],
+                        M, N, w.eps, w.x_dt, w.g_dt, self.stream_handle)
+                self.calls.append((lib.layernorm_fwd, args))
             elif w.kind == "qk":
                 args = (p["x"], p["x"] + w.heads_q * N * w.esize, g.data_ptr(),
                         self.gamma_k.data_ptr(), M, w.heads_q, w.heads_k, N, self.qkv_stride,
@@ -246,6 +259,10 @@ def cpu_baseline(w, host_inputs: dict, seconds: float) -> dict:
         def one_pass():
             O.rmsnorm_fused_add_fwd(x, host_inputs["r"], g, M, N, w.eps, w.x_dt, w.g_dt,
                                     want_exact=False)
+    elif w.kind == "ln":
+        def one_pass():
+            O.layernorm_fwd(x, g, host_inputs["beta"], M, N, w.eps, w.x_dt, w.g_dt,
+                            want_exact=False)
     elif w.kind == "qk":
         S = (w.heads_q + 2 * w.heads_k) * N
 

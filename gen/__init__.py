@@ -108,7 +108,7 @@ def raw_bits(seed: int, stream: int, n: int) -> np.ndarray:
 class Workload:
     """One benchmark / parity workload."""
     name: str
-    kind: str            # "fwd", "fused_add", "bwd", "fused_add_bwd", "quant", "qk"
+    kind: str            # "fwd", "fused_add", "bwd", "fused_add_bwd", "quant", "qk", "ln"
     M: int
     N: int
     x_dt: int
@@ -140,6 +140,9 @@ class Workload:
             return 2 * big + g + (4 * self.M if self.store_rstd else 0)
         if self.kind == "fused_add":
             return 4 * big + g + (4 * self.M if self.store_rstd else 0)
+        if self.kind == "ln":
+            # read x, gamma, beta; write y, mean, rstd
+            return 2 * big + 2 * g + 8 * self.M
         if self.kind == "qk":
             # read and write every q and k head vector (v is never touched)
             return 2 * self.M * (self.heads_q + self.heads_k) * self.N * self.esize + 2 * g
@@ -182,6 +185,7 @@ EXTRA_WORKLOADS = [
              1008, quant_mode=1, fused_quant=True),
     Workload("qknorm_bf16_t16384_hq32_hk8_d128", "qk", 16384, 128, BF16, BF16, 1e-6, 1009,
              heads_q=32, heads_k=8),
+    Workload("layernorm_bf16_m4096_n8192", "ln", 4096, 8192, BF16, BF16, 1e-5, 1010),
 ]
 WORKLOADS_BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
@@ -201,6 +205,8 @@ def make_inputs(w: Workload, nthreads: int | None = None) -> dict:
                           nthreads=nthreads)
         out["gamma_k"] = uniform(w.seed + 1, STREAM_GAMMA, w.N, -1.0, 1.0, w.g_dt,
                                  nthreads=nthreads)
+    if w.kind == "ln":
+        out["beta"] = uniform(w.seed, STREAM_DY, w.N, -1.0, 1.0, w.g_dt, nthreads=nthreads)
     if w.kind in ("bwd", "fused_add_bwd"):
         out["dy"] = normal(w.seed, STREAM_DY, w.M, w.N, w.x_dt, nthreads=nthreads)
     if w.kind == "fused_add_bwd":

@@ -1,4 +1,5 @@
-/* rmsnorm_mi355x.h -- C ABI of the row-wise RMSNorm library for MI355X (gfx950).
+/* rmsnorm_mi355x.h -- C ABI of the row-wise normalisation library for MI355X
+ * (gfx950): RMSNorm and its variants, and LayerNorm.
  *
  * The operation ("Pre-built kernel library guide" (FlyDSL), section 1.2 RMSNorm):
  * for every row i of a row-major [M, N] array,
@@ -186,6 +187,23 @@ int rmsnorm_fused_add_bwd(const void* dy, const void* h, const float* rstd,
                           float* dgamma, void* workspace, size_t workspace_bytes,
                           int64_t M, int64_t N, int x_dtype, int gamma_dtype,
                           hipStream_t stream);
+
+/* LayerNorm forward ("Pre-built kernel library guide" (FlyDSL), section 1.1,
+ * build_layernorm_module: Input, Gamma, Beta, Output): for every row i,
+ *     mean_i = (1/N) sum_j x_ij,   var_i = (1/N) sum_j (x_ij - mean_i)^2,
+ *     rstd_i = 1 / sqrt(var_i + eps),
+ *     y_ij   = (x_ij - mean_i) * rstd_i * gamma_j + beta_j
+ * with fp32 arithmetic: the mean from one row reduction, the variance from a
+ * second one over the centred values (no E[x^2] - mean^2 cancellation), and
+ * (x - mean) * rstd * gamma + beta with one fused multiply-add, rounded once.
+ *   x          [M, N] x_dtype, read.
+ *   gamma      [N] gamma_dtype, read;  beta [N] gamma_dtype, read, or NULL (0).
+ *   y          [M, N] x_dtype, written; may equal x exactly.
+ *   mean, rstd [M] fp32 each, written when not NULL (for the backward).
+ * Shapes, dtypes, alignment and errors as for rmsnorm_fwd. */
+int layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean,
+                  float* rstd, int64_t M, int64_t N, float eps, int x_dtype,
+                  int gamma_dtype, hipStream_t stream);
 
 /* Static English description of a status code ("unknown status" otherwise). */
 const char* rmsnorm_status_string(int status);

@@ -1,16 +1,17 @@
-"""Row-wise RMSNorm for MI355X (gfx950): Python binding of librmsnorm_mi355x.so.
+"""Row-wise RMSNorm (and LayerNorm) for MI355X (gfx950): Python binding of
+librmsnorm_mi355x.so.
 
 The C ABI (include/rmsnorm_mi355x.h) is exposed under the same names
 (``rmsnorm_fwd``, ``rmsnorm_fused_add_fwd``, ``rmsnorm_bwd``,
-``rmsnorm_fused_add_bwd``, ``rmsnorm_quant_fwd``, ``rmsnorm_qk_fwd``,
+``rmsnorm_fused_add_bwd``, ``rmsnorm_quant_fwd``, ``rmsnorm_qk_fwd``, ``layernorm_fwd``,
 ``rmsnorm_bwd_workspace_size``,
 ``rmsnorm_status_string``,
 ``rmsnorm_last_hip_error``); those functions only marshal arguments. Pointers
 may be given as integers or as torch tensors (their ``data_ptr()``); streams as
 integers or ``torch.cuda.Stream`` objects.
 
-``fwd``, ``fused_add_fwd``, ``quant_fwd``, ``qk_fwd``, ``bwd`` and ``fused_add_bwd`` are torch
-conveniences on top: they use
+``fwd``, ``fused_add_fwd``, ``quant_fwd``, ``qk_fwd``, ``bwd``, ``fused_add_bwd`` and
+``layernorm`` are torch conveniences on top: they use
 torch only to allocate outputs and to pick the current stream, and every step
 of the computation runs in the library's HIP kernels. There is no fallback: if
 the library is not built, every call raises.
@@ -34,7 +35,7 @@ STATUS_NAMES = {
     -7: "RMSN_ERR_EPS", -8: "RMSN_ERR_MODE", -100: "RMSN_ERR_HIP",
 }
 ENTRY_POINTS = ("rmsnorm_fwd", "rmsnorm_fused_add_fwd", "rmsnorm_quant_fwd", "rmsnorm_qk_fwd",
-                "rmsnorm_bwd",
+                "layernorm_fwd", "rmsnorm_bwd",
                 "rmsnorm_fused_add_bwd", "rmsnorm_bwd_workspace_size", "rmsnorm_status_string",
                 "rmsnorm_last_hip_error")
 
@@ -73,6 +74,8 @@ def load_library(path: str | None = None):
     lib.rmsnorm_qk_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, i32,
                                    vp]
     lib.rmsnorm_qk_fwd.restype = i32
+    lib.layernorm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+    lib.layernorm_fwd.restype = i32
     lib.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i32]
     lib.rmsnorm_bwd_workspace_size.restype = ctypes.c_size_t
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i32, i32, vp]
@@ -131,6 +134,11 @@ def rmsnorm_qk_fwd(q, k, q_gamma, k_gamma, tokens, q_heads, k_heads, head_dim, q
     return load_library().rmsnorm_qk_fwd(_p(q), _p(k), _p(q_gamma), _p(k_gamma), tokens, q_heads,
                                          k_heads, head_dim, q_stride, k_stride, eps, x_dtype,
                                          gamma_dtype, _s(stream))
+
+
+def layernorm_fwd(x, gamma, beta, y, mean, rstd, M, N, eps, x_dtype, gamma_dtype, stream) -> int:
+    return load_library().layernorm_fwd(_p(x), _p(gamma), _p(beta), _p(y), _p(mean), _p(rstd), M,
+                                        N, eps, x_dtype, gamma_dtype, _s(stream))
 
 
 def rmsnorm_bwd_workspace_size(M, N, x_dtype) -> int:
@@ -259,6 +267,24 @@ def qk_fwd(q, k, q_gamma, k_gamma=None, eps: float = 1e-6, *, stream=None):
     _check(rmsnorm_qk_fwd(q, k, q_gamma, k_gamma if k is not None else None, T, Hq, Hk, D, sq, sk,
                           eps, dtype_code(q), dtype_code(q_gamma), stream), "rmsnorm_qk_fwd")
     return q, k
+
+
+def layernorm(x, gamma, beta=None, eps: float = 1e-5, *, want_stats: bool = False, out=None,
+              stream=None):
+    """LayerNorm over the last dimension; returns (y, mean, rstd), the
+    statistics fp32 [rows] when want_stats, else None."""
+    import torch
+    N = gamma.numel()
+    M = _rows(x, N)
+    y = torch.empty_like(x) if out is None else out
+    mean = rstd = None
+    if want_stats:
+        mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    stream = torch.cuda.current_stream(x.device) if stream is None else stream
+    _check(layernorm_fwd(x, gamma, beta, y, mean, rstd, M, N, eps, dtype_code(x),
+                         dtype_code(gamma), stream), "layernorm_fwd")
+    return y, mean, rstd
 
 
 def bwd(dy, x, rstd, gamma, *, dx=None, dgamma=None, workspace=None, stream=None):

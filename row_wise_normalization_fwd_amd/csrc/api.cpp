@@ -89,6 +89,45 @@ int forward(bool fused, const void* x, void* residual, const void* gamma, void* 
   return finish(launch_forward(c, x_dtype));
 }
 
+// Validation of the LayerNorm forward.
+int ln_forward(const void* x, const void* gamma, const void* beta, void* y, float* mean,
+               float* rstd, int64_t M, int64_t N, float eps, int x_dtype, int gamma_dtype,
+               hipStream_t stream) {
+  if (!valid_pair(x_dtype, gamma_dtype)) return RMSN_ERR_DTYPE;
+  if (!shape_ok(M, N)) return RMSN_ERR_SHAPE;
+  if (!std::isfinite(eps) || eps < 0.0f) return RMSN_ERR_EPS;
+  if (M == 0) return RMSN_OK;
+  if (!x || !gamma || !y) return RMSN_ERR_NULL;
+  const int es = esize_of(x_dtype), gs = esize_of(gamma_dtype);
+  if (!aligned(x, es) || !aligned(y, es) || !aligned(gamma, gs) || (beta && !aligned(beta, gs)) ||
+      (mean && !aligned(mean, 4)) || (rstd && !aligned(rstd, 4)))
+    return RMSN_ERR_ALIGN;
+  const uint64_t big = static_cast<uint64_t>(M) * static_cast<uint64_t>(N) * es;
+  const Range rx = span(x, big), ry = span(y, big);
+  const Range rg = span(gamma, static_cast<uint64_t>(N) * gs);
+  // y may equal x exactly; the written buffers overlap nothing else.
+  if (partial_overlap(ry, rx) || overlap(ry, rg)) return RMSN_ERR_OVERLAP;
+  if (beta && overlap(ry, span(beta, static_cast<uint64_t>(N) * gs))) return RMSN_ERR_OVERLAP;
+  float* stats[2] = {mean, rstd};
+  for (float* p : stats) {
+    if (!p) continue;
+    const Range r = span(p, static_cast<uint64_t>(M) * 4);
+    if (overlap(r, rx) || overlap(r, ry) || overlap(r, rg)) return RMSN_ERR_OVERLAP;
+    if (beta && overlap(r, span(beta, static_cast<uint64_t>(N) * gs))) return RMSN_ERR_OVERLAP;
+  }
+  if (mean && rstd && overlap(span(mean, static_cast<uint64_t>(M) * 4),
+                              span(rstd, static_cast<uint64_t>(M) * 4)))
+    return RMSN_ERR_OVERLAP;
+  rmsn::FwdCall c{x, nullptr, gamma, y, rstd, M, N, eps, gamma_dtype, stream};
+  c.beta = beta;
+  c.mean = mean;
+  switch (x_dtype) {
+    case RMSN_F32: return finish(rmsn::launch_ln_fwd_f32(c));
+    case RMSN_F16: return finish(rmsn::launch_ln_fwd_f16(c));
+    default: return finish(rmsn::launch_ln_fwd_bf16(c));
+  }
+}
+
 // Validation of the quantised forward (fp8 output, optional fused add).
 int quant_forward(const void* x, void* residual, const void* gamma, void* q, float* scale,
                   int mode, float* rstd, int64_t M, int64_t N, float eps, int x_dtype,
@@ -324,6 +363,12 @@ int rmsnorm_qk_fwd(void* q, void* k, const void* q_gamma, const void* k_gamma, i
                    hipStream_t stream) {
   return qk_forward(q, k, q_gamma, k_gamma, tokens, q_heads, k_heads, head_dim, q_stride,
                     k_stride, eps, x_dtype, gamma_dtype, stream);
+}
+
+int layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean,
+                  float* rstd, int64_t M, int64_t N, float eps, int x_dtype, int gamma_dtype,
+                  hipStream_t stream) {
+  return ln_forward(x, gamma, beta, y, mean, rstd, M, N, eps, x_dtype, gamma_dtype, stream);
 }
 
 size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int x_dtype) {

@@ -27,17 +27,17 @@
 
 namespace rmsn {
 
-template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool FUSED, int OUT>
+template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool FUSED, int OUT, bool LN>
 hipError_t run_fwd_reg(const FwdArgs<T, G>& a, hipStream_t s) {
   constexpr int RPB = BLOCK / TPR;
   int64_t blocks = ceil_div(a.M, RPB);
   if (blocks > kMaxGrid) blocks = kMaxGrid;
-  fwd_reg_kernel<T, G, VEC, TPR, UPT, BLOCK, FUSED, OUT>
+  fwd_reg_kernel<T, G, VEC, TPR, UPT, BLOCK, FUSED, OUT, LN>
       <<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <class T, class G, int TPR, int UPT, int BLOCK, bool FUSED, int OUT>
+template <class T, class G, int TPR, int UPT, int BLOCK, bool FUSED, int OUT, bool LN>
 hipError_t run_fwd_pp(const FwdArgs<T, G>& a, hipStream_t s) {
   // Two blocks per CU's worth of grid: at 4096 x 8192 bf16 every block then
   // runs exactly two iterations (one prefetch), measured best among 256-1024
@@ -46,16 +46,17 @@ hipError_t run_fwd_pp(const FwdArgs<T, G>& a, hipStream_t s) {
   int64_t blocks = 2 * device_cus();
   const int64_t groups = ceil_div(a.M, RG);
   if (blocks > groups) blocks = groups;
-  fwd_pp_kernel<T, G, TPR, UPT, BLOCK, FUSED, OUT>
+  fwd_pp_kernel<T, G, TPR, UPT, BLOCK, FUSED, OUT, LN>
       <<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <class T, class G, bool VEC, int BLOCK, int UNROLL, bool FUSED, bool CACHE, int OUT>
+template <class T, class G, bool VEC, int BLOCK, int UNROLL, bool FUSED, bool CACHE, int OUT,
+          bool LN>
 hipError_t run_fwd_long(const FwdArgs<T, G>& a, hipStream_t s) {
   int64_t blocks = a.M < kMaxGrid ? a.M : kMaxGrid;
   const size_t lds = CACHE ? static_cast<size_t>(a.N) * T::kSize : 0;
-  constexpr auto kernel = fwd_long_kernel<T, G, VEC, BLOCK, UNROLL, FUSED, CACHE, OUT>;
+  constexpr auto kernel = fwd_long_kernel<T, G, VEC, BLOCK, UNROLL, FUSED, CACHE, OUT, LN>;
   if constexpr (CACHE) {
     // Allow the largest row cache once; per-launch sizes stay below it.
     const hipError_t attr =
@@ -66,7 +67,7 @@ hipError_t run_fwd_long(const FwdArgs<T, G>& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <class T, class G, bool FUSED, int OUT>
+template <class T, class G, bool FUSED, int OUT, bool LN = false>
 hipError_t fwd_typed(const FwdCall& c) {
   FwdArgs<T, G> a;
   a.x = static_cast<const typename T::S*>(c.x);
@@ -79,74 +80,85 @@ hipError_t fwd_typed(const FwdCall& c) {
   a.eps = c.eps;
   a.q = static_cast<uint8_t*>(c.q);
   a.scale = c.scale;
+  a.beta = static_cast<const typename G::S*>(c.beta);
+  a.mean = c.mean;
   hipStream_t s = c.stream;
 
   // fp8 output units are 16 / sizeof(T) bytes (8 or 4), stored with one
   // instruction, so q must be aligned to that.
   const bool out_ok = OUT == kOutAct ? aligned16(c.y) : aligned_to(c.q, 16 / T::kSize);
   const bool vec = (c.N * T::kSize) % 16 == 0 && aligned16(c.x) && out_ok &&
-                   aligned16(c.gamma) && (!FUSED || aligned16(c.residual));
+                   aligned16(c.gamma) && (!FUSED || aligned16(c.residual)) &&
+                   (!LN || c.beta == nullptr || aligned16(c.beta));
   if (c.N <= kRegMaxN) {
     if (vec) {
       constexpr int E = 16 / T::kSize;
       const int64_t units = c.N / E;
-      if (units > 1024) return run_fwd_reg<T, G, true, 512, 4, 512, FUSED, OUT>(a, s);
+      if (units > 1024) return run_fwd_reg<T, G, true, 512, 4, 512, FUSED, OUT, LN>(a, s);
       if constexpr (T::kSize == 2 && !FUSED) {
         // 16-bit rows of 769..1024 units: persistent kernel with next-row
         // prefetch; four 256-lane row groups per block for 16-bit outputs,
         // one per block for fp8 outputs (4096 x 8192 bf16, fp8 per-row
         // scales: 18.1 us vs 21.4 us with four; one scale: 17.7 vs 20.4 us;
         // bf16 output: 22.9 vs 23.5 us the other way).
+        // LayerNorm keeps beta and the mean live too and spills with four
+        // row groups, so it also takes the one-group shape.
         if (units > 768) {
-          if constexpr (OUT == kOutAct) return run_fwd_pp<T, G, 256, 4, 1024, FUSED, OUT>(a, s);
-          else return run_fwd_pp<T, G, 256, 4, 256, FUSED, OUT>(a, s);
+          if constexpr (OUT == kOutAct && !LN) return run_fwd_pp<T, G, 256, 4, 1024, FUSED, OUT, LN>(a, s);
+          else return run_fwd_pp<T, G, 256, 4, 256, FUSED, OUT, LN>(a, s);
         }
       }
       const int64_t tpr2 = next_pow2(ceil_div(units, 2));
       if (tpr2 >= 8 && 3 * units < 4 * tpr2 && units <= 3 * (tpr2 / 2)) {
         switch (tpr2 / 2) {  // 3 units on half the lanes
-          case 4: return run_fwd_reg<T, G, true, 4, 3, 256, FUSED, OUT>(a, s);
-          case 8: return run_fwd_reg<T, G, true, 8, 3, 256, FUSED, OUT>(a, s);
-          case 16: return run_fwd_reg<T, G, true, 16, 3, 256, FUSED, OUT>(a, s);
-          case 32: return run_fwd_reg<T, G, true, 32, 3, 256, FUSED, OUT>(a, s);
-          case 64: return run_fwd_reg<T, G, true, 64, 3, 256, FUSED, OUT>(a, s);
-          case 128: return run_fwd_reg<T, G, true, 128, 3, 256, FUSED, OUT>(a, s);
-          default: return run_fwd_reg<T, G, true, 256, 3, 256, FUSED, OUT>(a, s);
+          case 4: return run_fwd_reg<T, G, true, 4, 3, 256, FUSED, OUT, LN>(a, s);
+          case 8: return run_fwd_reg<T, G, true, 8, 3, 256, FUSED, OUT, LN>(a, s);
+          case 16: return run_fwd_reg<T, G, true, 16, 3, 256, FUSED, OUT, LN>(a, s);
+          case 32: return run_fwd_reg<T, G, true, 32, 3, 256, FUSED, OUT, LN>(a, s);
+          case 64: return run_fwd_reg<T, G, true, 64, 3, 256, FUSED, OUT, LN>(a, s);
+          case 128: return run_fwd_reg<T, G, true, 128, 3, 256, FUSED, OUT, LN>(a, s);
+          default: return run_fwd_reg<T, G, true, 256, 3, 256, FUSED, OUT, LN>(a, s);
         }
       }
       switch (tpr2) {
-        case 1: return run_fwd_reg<T, G, true, 1, 2, 256, FUSED, OUT>(a, s);
-        case 2: return run_fwd_reg<T, G, true, 2, 2, 256, FUSED, OUT>(a, s);
-        case 4: return run_fwd_reg<T, G, true, 4, 2, 256, FUSED, OUT>(a, s);
-        case 8: return run_fwd_reg<T, G, true, 8, 2, 256, FUSED, OUT>(a, s);
-        case 16: return run_fwd_reg<T, G, true, 16, 2, 256, FUSED, OUT>(a, s);
-        case 32: return run_fwd_reg<T, G, true, 32, 2, 256, FUSED, OUT>(a, s);
-        case 64: return run_fwd_reg<T, G, true, 64, 2, 256, FUSED, OUT>(a, s);
-        case 128: return run_fwd_reg<T, G, true, 128, 2, 256, FUSED, OUT>(a, s);
-        case 256: return run_fwd_reg<T, G, true, 256, 2, 256, FUSED, OUT>(a, s);
-        default: return run_fwd_reg<T, G, true, 512, 2, 512, FUSED, OUT>(a, s);
+        case 1: return run_fwd_reg<T, G, true, 1, 2, 256, FUSED, OUT, LN>(a, s);
+        case 2: return run_fwd_reg<T, G, true, 2, 2, 256, FUSED, OUT, LN>(a, s);
+        case 4: return run_fwd_reg<T, G, true, 4, 2, 256, FUSED, OUT, LN>(a, s);
+        case 8: return run_fwd_reg<T, G, true, 8, 2, 256, FUSED, OUT, LN>(a, s);
+        case 16: return run_fwd_reg<T, G, true, 16, 2, 256, FUSED, OUT, LN>(a, s);
+        case 32: return run_fwd_reg<T, G, true, 32, 2, 256, FUSED, OUT, LN>(a, s);
+        case 64: return run_fwd_reg<T, G, true, 64, 2, 256, FUSED, OUT, LN>(a, s);
+        case 128: return run_fwd_reg<T, G, true, 128, 2, 256, FUSED, OUT, LN>(a, s);
+        case 256: return run_fwd_reg<T, G, true, 256, 2, 256, FUSED, OUT, LN>(a, s);
+        default: return run_fwd_reg<T, G, true, 512, 2, 512, FUSED, OUT, LN>(a, s);
       }
     }
     const int64_t tpr = next_pow2(ceil_div(c.N, 8));
-    if (tpr <= 16) return run_fwd_reg<T, G, false, 16, 8, 256, FUSED, OUT>(a, s);
-    if (tpr <= 64) return run_fwd_reg<T, G, false, 64, 8, 256, FUSED, OUT>(a, s);
-    if (tpr <= 256) return run_fwd_reg<T, G, false, 256, 8, 256, FUSED, OUT>(a, s);
-    return run_fwd_reg<T, G, false, 1024, 8, 1024, FUSED, OUT>(a, s);
+    if (tpr <= 16) return run_fwd_reg<T, G, false, 16, 8, 256, FUSED, OUT, LN>(a, s);
+    if (tpr <= 64) return run_fwd_reg<T, G, false, 64, 8, 256, FUSED, OUT, LN>(a, s);
+    if (tpr <= 256) return run_fwd_reg<T, G, false, 256, 8, 256, FUSED, OUT, LN>(a, s);
+    return run_fwd_reg<T, G, false, 1024, 8, 1024, FUSED, OUT, LN>(a, s);
   }
   const int64_t row_bytes = c.N * T::kSize;
   const bool cache = row_bytes <= lds_row_budget();
   if (vec) {
-    if (!cache) return run_fwd_long<T, G, true, 1024, 4, FUSED, false, OUT>(a, s);
-    if (row_bytes <= 32 * 1024) return run_fwd_long<T, G, true, 512, 4, FUSED, true, OUT>(a, s);
-    return run_fwd_long<T, G, true, 1024, 4, FUSED, true, OUT>(a, s);
+    if (!cache) return run_fwd_long<T, G, true, 1024, 4, FUSED, false, OUT, LN>(a, s);
+    if (row_bytes <= 32 * 1024) return run_fwd_long<T, G, true, 512, 4, FUSED, true, OUT, LN>(a, s);
+    return run_fwd_long<T, G, true, 1024, 4, FUSED, true, OUT, LN>(a, s);
   }
-  if (!cache) return run_fwd_long<T, G, false, 1024, 8, FUSED, false, OUT>(a, s);
-  return run_fwd_long<T, G, false, 1024, 8, FUSED, true, OUT>(a, s);
+  if (!cache) return run_fwd_long<T, G, false, 1024, 8, FUSED, false, OUT, LN>(a, s);
+  return run_fwd_long<T, G, false, 1024, 8, FUSED, true, OUT, LN>(a, s);
 }
 
 template <class T, class G, int OUT>
 hipError_t fwd_gamma_typed(const FwdCall& c) {
   return c.residual ? fwd_typed<T, G, true, OUT>(c) : fwd_typed<T, G, false, OUT>(c);
+}
+
+// LayerNorm (plain output, no fused add).
+template <class T, class G>
+hipError_t ln_fwd_typed(const FwdCall& c) {
+  return fwd_typed<T, G, false, kOutAct, true>(c);
 }
 
 // Quantised outputs: per-tensor or per-row scale.

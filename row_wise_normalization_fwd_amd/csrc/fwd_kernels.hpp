@@ -20,6 +20,11 @@
 // cache-resident). The re-read path keeps ordinary loads so its second pass
 // can hit in L2 / MALL.
 //
+// LN turns the kernel into LayerNorm (FlyDSL guide, section 1.1): the row
+// mean comes from a first reduction, the variance from a second one over the
+// centred values still in registers (or in the LDS cache), then
+// y = (x - mean) * rstd * gamma + beta. It is used without FUSED and OUT.
+//
 // OUT selects the output: the activation type (y), or fp8 e4m3 codes of y / s
 // (the quantised variants of the "TIRx kernels" page's FlashInfer norm ports)
 // with s one caller scale, or s_i = max_j |y_ij| / 448 per row. For the per-row
@@ -48,6 +53,8 @@ struct FwdArgs {
   float eps;
   uint8_t* q;    // fp8 output (OUT != kOutAct)
   float* scale;  // kOutFp8Tensor: [1], read; kOutFp8Row: [M], written
+  const typename G::S* beta;  // LayerNorm bias (may be null)
+  float* mean;                // LayerNorm per-row mean (may be null)
 };
 
 // Sum-of-squares reduction type: the pair (sum, max) for the per-row scale.
@@ -82,13 +89,15 @@ __device__ __forceinline__ void prepare_unit(typename U::Raw& raw, typename U::R
   }
 }
 
-template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool FUSED, int OUT>
+template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool FUSED, int OUT,
+          bool LN = false>
 __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
   using U = Unit<T, VEC>;
   constexpr int E = U::E;
   using Q = Fp8Unit<E>;
   constexpr int RPB = BLOCK / TPR;  // rows per block
   static_assert(BLOCK % TPR == 0 && BLOCK % kWave == 0, "block shape");
+  static_assert(!LN || (!FUSED && OUT == kOutAct), "LayerNorm: plain output only");
   __shared__ RedT<OUT> red[2 * (BLOCK / kWave)];
   const float tinv = tensor_inv_scale<T, G, OUT>(a);
 
@@ -105,6 +114,19 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
     } else {
 #pragma unroll
       for (int e = 0; e < E; ++e) gam[k][e] = 0.0f;
+    }
+  }
+  [[maybe_unused]] float bet[LN ? UPT : 1][E];
+  if constexpr (LN) {
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const int u = lane + k * TPR;
+      if (a.beta != nullptr && u < nunits) {
+        load_gamma<G, E, VEC>(a.beta, u * E, bet[k]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) bet[k][e] = 0.0f;
+      }
     }
   }
 
@@ -137,8 +159,13 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
         if (valid && u < nunits) U::store_nt(a.residual + off + u * E, raw[k]);
       }
       float s = 0.0f;
+      if constexpr (LN) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) s = __builtin_fmaf(v[k][e], v[k][e], s);
+        for (int e = 0; e < E; ++e) s = s + v[k][e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s = __builtin_fmaf(v[k][e], v[k][e], s);
+      }
       part[k] = s;
     }
     float ss = part[0];
@@ -147,7 +174,30 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
 
     float inv = tinv;
     float rs;
-    if constexpr (OUT == kOutFp8Row) {
+    [[maybe_unused]] float mu = 0.0f;
+    if constexpr (LN) {
+      // Mean, then the sum of squared deviations of the values in registers
+      // (masked units excluded).
+      mu = row_sum<TPR, BLOCK>(ss, red, parity) / static_cast<float>(a.N);
+      parity ^= 1;
+#pragma unroll
+      for (int k = 0; k < UPT; ++k) {
+        const int u = lane + k * TPR;
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float d = v[k][e] - mu;
+          s = __builtin_fmaf(d, d, s);
+        }
+        part[k] = valid && u < nunits ? s : 0.0f;
+      }
+      float sq = part[0];
+#pragma unroll
+      for (int k = 1; k < UPT; ++k) sq = sq + part[k];
+      sq = row_sum<TPR, BLOCK>(sq, red, parity);
+      rs = 1.0f / __builtin_sqrtf(sq / static_cast<float>(a.N) + a.eps);
+      if (a.mean != nullptr && valid && lane == 0) a.mean[row] = mu;
+    } else if constexpr (OUT == kOutFp8Row) {
       float m = 0.0f;
 #pragma unroll
       for (int k = 0; k < UPT; ++k)
@@ -170,7 +220,11 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
       const int u = lane + k * TPR;
       if (valid && u < nunits) {
         float o[E];
-        if constexpr (OUT == kOutAct) {
+        if constexpr (LN) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf((v[k][e] - mu) * rs, gam[k][e], bet[k][e]);
+          U::store_nt(a.y + off + u * E, U::narrow(o));
+        } else if constexpr (OUT == kOutAct) {
 #pragma unroll
           for (int e = 0; e < E; ++e) o[e] = v[k][e] * rs * gam[k][e];
           U::store_nt(a.y + off + u * E, U::narrow(o));
@@ -194,7 +248,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
 // branches around them and the compiler waits only for the older loads.
 // Row results do not depend on G (each row's arithmetic is the same for any
 // grid), only on TPR and UPT.
-template <class T, class G, int TPR, int UPT, int BLOCK, bool FUSED, int OUT>
+template <class T, class G, int TPR, int UPT, int BLOCK, bool FUSED, int OUT, bool LN = false>
 __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
   using U = Unit<T, true>;
   using Raw = u32x4;
@@ -202,6 +256,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
   constexpr int RG = BLOCK / TPR;
   constexpr int GW = E * G::kSize / 16;  // 16-byte words of gamma per unit (1 or 2)
   static_assert(BLOCK % TPR == 0 && BLOCK % kWave == 0, "block shape");
+  static_assert(!LN || (!FUSED && OUT == kOutAct), "LayerNorm: plain output only");
   static_assert(OUT == kOutAct || E == 8, "fp8 units of 8 bytes");
   __shared__ RedT<OUT> red[2 * (BLOCK / kWave)];
   const float tinv = tensor_inv_scale<T, G, OUT>(a);
@@ -221,6 +276,22 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
     const typename G::S* gp = a.gamma + (u < nunits ? u : 0) * E;
 #pragma unroll
     for (int w = 0; w < GW; ++w) graw[k][w] = *reinterpret_cast<const u32x4*>(gp + w * (16 / G::kSize));
+  }
+  [[maybe_unused]] u32x4 braw[LN ? UPT : 1][GW];
+  if constexpr (LN) {
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const int u = lane + k * TPR;
+#pragma unroll
+      for (int w = 0; w < GW; ++w) {
+        if (a.beta != nullptr) {
+          const typename G::S* bp = a.beta + (u < nunits ? u : 0) * E;
+          braw[k][w] = *reinterpret_cast<const u32x4*>(bp + w * (16 / G::kSize));
+        } else {
+          braw[k][w] = (u32x4){0u, 0u, 0u, 0u};
+        }
+      }
+    }
   }
 
   auto widen_gamma = [&](const u32x4* gw, float* g) {
@@ -278,8 +349,13 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
       float v[E];
       prepare_unit<T, U, FUSED>(cx[k], cr[k], v);
       float s = 0.0f;
+      if constexpr (LN) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) s = __builtin_fmaf(v[e], v[e], s);
+        for (int e = 0; e < E; ++e) s = s + v[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s = __builtin_fmaf(v[e], v[e], s);
+      }
       part[k] = s;
     }
     if constexpr (FUSED) {  // h, rounded, back over the residual
@@ -305,7 +381,27 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
 #pragma unroll
     for (int k = 0; k < UPT; ++k) opaque(cx[k]);
     float rs, inv = tinv;
-    if constexpr (OUT == kOutFp8Row) {
+    [[maybe_unused]] float mu = 0.0f;
+    if constexpr (LN) {
+      mu = row_sum<TPR, BLOCK>(ss, red, parity) / static_cast<float>(a.N);
+      parity ^= 1;
+      float sq = 0.0f;
+#pragma unroll
+      for (int k = 0; k < UPT; ++k) {
+        float v[E];
+        U::widen(cx[k], v);
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float d = v[e] - mu;
+          s = __builtin_fmaf(d, d, s);
+        }
+        sq = sq + (unit_offset(row0, k) != kBufOutOfRange ? s : 0.0f);
+      }
+      sq = row_sum<TPR, BLOCK>(sq, red, parity);
+      rs = 1.0f / __builtin_sqrtf(sq / static_cast<float>(a.N) + a.eps);
+      if (a.mean != nullptr) store_row_value(a.mean, row0, mu);
+    } else if constexpr (OUT == kOutFp8Row) {
       const SumMax r = row_sum<TPR, BLOCK>(SumMax{ss, m}, red, parity);
       rs = 1.0f / __builtin_sqrtf(r.s / static_cast<float>(a.N) + a.eps);
       const float amax = r.m * rs;
@@ -323,8 +419,15 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
         float v[E], g[E], o[E];
         U::widen(cx[k], v);
         widen_gamma(graw[k], g);
+        if constexpr (LN) {
+          float bb[E];
+          widen_gamma(braw[k], bb);
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
+          for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf((v[e] - mu) * rs, g[e], bb[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
+        }
         buf_store16_nt(U::narrow(o), rsy, unit_offset(row0, k));
       }
     } else {
@@ -358,13 +461,15 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
   }
 }
 
-template <class T, class G, bool VEC, int BLOCK, int UNROLL, bool FUSED, bool CACHE, int OUT>
+template <class T, class G, bool VEC, int BLOCK, int UNROLL, bool FUSED, bool CACHE, int OUT,
+          bool LN = false>
 __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
   using U = Unit<T, VEC>;
   using Raw = typename U::Raw;
   using Q = Fp8Unit<U::E>;
   constexpr int E = U::E;
   constexpr int STEP = BLOCK * UNROLL;
+  static_assert(!LN || (!FUSED && OUT == kOutAct), "LayerNorm: plain output only");
   __shared__ RedT<OUT> red[2 * (BLOCK / kWave)];
   const float tinv = tensor_inv_scale<T, G, OUT>(a);
   extern __shared__ __align__(16) unsigned char lds_bytes[];
@@ -396,8 +501,13 @@ __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
         float v[E];
         prepare_unit<T, U, FUSED>(raw[k], res[k], v);
         float s = 0.0f;
+        if constexpr (LN) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) s = __builtin_fmaf(v[e], v[e], s);
+          for (int e = 0; e < E; ++e) s = s + v[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) s = __builtin_fmaf(v[e], v[e], s);
+        }
         ss = ss + s;
         if (u < nunits) {
           if constexpr (FUSED) U::store_nt(a.residual + off + u * E, raw[k]);
@@ -411,8 +521,43 @@ __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
         }
       }
     }
+    // Fused rows re-read the rounded h written back to `residual`; each lane
+    // re-reads only units it wrote itself.
+    const typename T::S* src = FUSED ? a.residual : a.x;
     float rs, inv = tinv;
-    if constexpr (OUT == kOutFp8Row) {
+    [[maybe_unused]] float mu = 0.0f;
+    if constexpr (LN) {
+      // Mean, then a pass over the cached (or re-read) row for the sum of
+      // squared deviations.
+      mu = row_sum<BLOCK, BLOCK>(ss, red, parity) / static_cast<float>(a.N);
+      parity ^= 1;
+      float sq = 0.0f;
+      for (int first = 0; first < nunits; first += STEP) {
+        Raw raw[UNROLL];
+#pragma unroll
+        for (int k = 0; k < UNROLL; ++k) {
+          const int u = first + threadIdx.x + k * BLOCK;
+          if constexpr (CACHE) raw[k] = u < nunits ? cache[u] : U::zero();
+          else raw[k] = u < nunits ? U::load(src + off + u * E) : U::zero();
+        }
+#pragma unroll
+        for (int k = 0; k < UNROLL; ++k) {
+          const int u = first + threadIdx.x + k * BLOCK;
+          float v[E];
+          U::widen(raw[k], v);
+          float s = 0.0f;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float d = v[e] - mu;
+            s = __builtin_fmaf(d, d, s);
+          }
+          sq = sq + (u < nunits ? s : 0.0f);
+        }
+      }
+      sq = row_sum<BLOCK, BLOCK>(sq, red, parity);
+      rs = 1.0f / __builtin_sqrtf(sq / static_cast<float>(a.N) + a.eps);
+      if (a.mean != nullptr && threadIdx.x == 0) a.mean[row] = mu;
+    } else if constexpr (OUT == kOutFp8Row) {
       const SumMax r = row_sum<BLOCK, BLOCK>(SumMax{ss, m}, red, parity);
       rs = 1.0f / __builtin_sqrtf(r.s / static_cast<float>(a.N) + a.eps);
       const float amax = r.m * rs;
@@ -425,9 +570,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
     parity ^= 1;
     if (a.rstd != nullptr && threadIdx.x == 0) a.rstd[row] = rs;
 
-    // Second pass: the rounded h (fused) was written back to `residual`; each
-    // lane re-reads only units it wrote itself.
-    const typename T::S* src = FUSED ? a.residual : a.x;
+    // Output pass.
     for (int first = 0; first < nunits; first += STEP) {
       Raw raw[UNROLL];
 #pragma unroll
@@ -443,7 +586,18 @@ __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
           float v[E], g[E], o[E];
           U::widen(raw[k], v);
           load_gamma<G, E, VEC>(a.gamma, u * E, g);
-          if constexpr (OUT == kOutAct) {
+          if constexpr (LN) {
+            float bb[E];
+            if (a.beta != nullptr) {
+              load_gamma<G, E, VEC>(a.beta, u * E, bb);
+            } else {
+#pragma unroll
+              for (int e = 0; e < E; ++e) bb[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf((v[e] - mu) * rs, g[e], bb[e]);
+            U::store_nt(a.y + off + u * E, U::narrow(o));
+          } else if constexpr (OUT == kOutAct) {
 #pragma unroll
             for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
             U::store_nt(a.y + off + u * E, U::narrow(o));

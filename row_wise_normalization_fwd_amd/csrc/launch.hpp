@@ -64,6 +64,9 @@ struct FwdCall {
   void* q = nullptr;
   float* scale = nullptr;
   int out = 0;
+  // LayerNorm only: bias (may be null) and per-row mean output (may be null).
+  const void* beta = nullptr;
+  float* mean = nullptr;
 };
 
 hipError_t launch_fwd_f32(const FwdCall& c);
@@ -72,6 +75,9 @@ hipError_t launch_fwd_bf16(const FwdCall& c);
 hipError_t launch_fwd_quant_f32(const FwdCall& c);
 hipError_t launch_fwd_quant_f16(const FwdCall& c);
 hipError_t launch_fwd_quant_bf16(const FwdCall& c);
+hipError_t launch_ln_fwd_f32(const FwdCall& c);
+hipError_t launch_ln_fwd_f16(const FwdCall& c);
+hipError_t launch_ln_fwd_bf16(const FwdCall& c);
 
 // Per-head QK-RMSNorm, in place: tensor 0 is q, tensor 1 is k (x[1] null or
 // heads[1] == 0 when absent). Heads of a token are contiguous, tokens are

@@ -13,6 +13,10 @@ Tolerances (fixed here, used by every GPU test):
   * dh of the fused-add backward: as dx, with 2^-22 |dresidual| added to the
     floor for the fp32 addition of the residual gradient.
   * dgamma: |g - o| <= max(1e-3 |o|, 2^-24 S_j) with S_j = sum_i |dy x rho|.
+  * LayerNorm y: within 1 ulp (fp32: relative 1e-5), or, where the centring
+    or beta cancel, |y - y_exact| <= 2^-18 rstd |gamma| (|x - mean| + A) +
+    2^-22 |beta| with A = mean_j |x_ij| (the fp32 mean carries an error of a
+    few 2^-24 A); mean: |m - mean| <= 2^-18 A; rstd: relative 1e-5.
   * fp8 e4m3 codes: ordinal distance <= 1 from the oracle's code (the kernel
     scales in fp32, so y / s can land on the other side of a tie); per-row
     scales: relative error <= 1e-5; every nonzero row's largest code is
@@ -154,3 +158,36 @@ def check_fp8(got: np.ndarray, ref: dict, per_row: bool, got_scale: np.ndarray |
         assert np.all(top[nz] == 0x7e), "a row's largest code is not 448"
         assert np.all((got[~nz] & 0x7f) == 0)
     return int((d == 1).sum())
+
+
+def check_layernorm(got_y, ref, x, gamma, beta, dt, got_mean=None, got_rstd=None):
+    """LayerNorm forward against the oracle (see the module docstring)."""
+    M, N = ref["y"].shape
+    got_y = got_y.reshape(M, N)
+    exact = ref["y_exact"]
+    if dt == O.F32:
+        ok_ulp = rel_error(got_y, exact) <= 1e-5
+        gotv = got_y.astype(np.float64)
+    else:
+        ok_ulp = ulp_distance16(got_y, ref["y"]) <= 1
+        gotv = O.decode(got_y, dt).reshape(M, N)
+    gdt = O.F32 if gamma.dtype == np.float32 else dt
+    gd = O.decode(gamma, gdt)
+    bd = O.decode(beta, gdt) if beta is not None else np.zeros(N)
+    xd = O.decode(x, dt).reshape(M, N)
+    rs = ref["rstd_exact"][:, None]
+    floor = (2.0 ** -18 * rs * np.abs(gd)[None, :] *
+             (np.abs(xd - ref["mean_exact"][:, None]) + ref["amag"][:, None]) +
+             2.0 ** -22 * np.abs(bd)[None, :])
+    ok_floor = np.abs(gotv - exact) <= floor
+    bad = ~(ok_ulp | ok_floor)
+    if bad.any():
+        idx = np.unravel_index(int(np.argmax(bad)), bad.shape)
+        raise AssertionError(f"layernorm y: {int(bad.sum())} elements out of tolerance; first at "
+                             f"{idx}: got {gotv[idx]!r}, exact {exact[idx]!r}, floor {floor[idx]!r}")
+    if got_mean is not None:
+        err = np.abs(got_mean.astype(np.float64) - ref["mean_exact"])
+        assert np.all(err <= 2.0 ** -18 * ref["amag"]), f"mean: worst {float(err.max())}"
+    if got_rstd is not None:
+        check_rstd(got_rstd, ref["rstd_exact"])
+    return int((~ok_ulp & ok_floor).sum())

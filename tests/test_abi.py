@@ -26,7 +26,8 @@ def _declared_functions():
             continue
         text = open(os.path.join(HEADER_DIR, fn)).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(rmsnorm_\w+)\s*\(", text, re.M)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b((?:rmsnorm|layernorm)_\w+)\s*\(",
+                            text, re.M)
     return sorted(set(names))
 
 
@@ -234,3 +235,23 @@ def test_qk_validation(lib):
     assert qk(sk=6144 + 8) == OVERLAP                    # strides differ, spans meet
     assert qk(gq=A + 100) == OVERLAP                     # gamma inside the q span
     assert qk(gk=A + 4096 * 2 + 64) == OVERLAP           # k gamma inside the k span
+
+
+def ln(x=A, g=B, b=C, y=D, mean=E, rstd=F, M=64, N=256, eps=1e-5, xd=BF16, gd=BF16):
+    return R.layernorm_fwd(x, g, b, y, mean, rstd, M, N, eps, xd, gd, None)
+
+
+def test_layernorm_validation(lib):
+    assert ln(xd=F32, gd=BF16) == DTYPE
+    assert ln(N=0) == SHAPE
+    assert ln(eps=float("inf")) == EPS
+    assert ln(M=0, x=None, g=None, b=None, y=None, mean=None, rstd=None) == OK
+    for k in ("x", "g", "y"):
+        assert ln(**{k: None}) == NULL, k
+    assert ln(b=C + 1) == ALIGN
+    assert ln(mean=E + 2) == ALIGN
+    assert ln(y=A + 2) == OVERLAP                   # partial overlap with x
+    assert ln(y=C) == OVERLAP                       # y over beta
+    assert ln(mean=A) == OVERLAP                    # mean over x
+    assert ln(rstd=E + 8) == OVERLAP                # rstd over mean
+    assert ln(mean=C + 4) == OVERLAP                # mean over beta

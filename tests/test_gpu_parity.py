@@ -11,8 +11,8 @@ import torch
 import gen as G
 import oracle as O
 import row_wise_normalization_fwd_amd as R
-from gpu_util import (check_dgamma, check_dx, check_fp8, check_output, check_rstd, to_device,
-                      to_host, TORCH_DTYPES)
+from gpu_util import (check_dgamma, check_dx, check_fp8, check_layernorm, check_output,
+                      check_rstd, to_device, to_host, TORCH_DTYPES)
 
 pytestmark = pytest.mark.gpu
 
@@ -441,6 +441,63 @@ def test_qk_layouts_and_edges(pair):
     run_qk(2000, 1, 1, 2, *pair, seed=1707)
 
 
+# ------------------------------------------------------------ LayerNorm
+
+def run_ln(M, N, xdt, gdt, seed=29, eps=1e-5, with_beta=True, stats=True, misalign=0,
+           inplace=False, shift=0.0, outlier_every=0, outlier_scale=1.0):
+    _log(f"layernorm M={M} N={N} x={xdt} g={gdt} beta={with_beta} stats={stats} "
+         f"misalign={misalign} inplace={inplace} shift={shift}")
+    x, g, _, _ = _inputs(M, N, xdt, gdt, seed, outlier_every, outlier_scale)
+    if shift:
+        x = O.round_to(O.decode(x, xdt).reshape(M, N) + shift, xdt)
+    b = G.uniform(seed, G.STREAM_DY, N, -1.0, 1.0, gdt) if with_beta else None
+    ref = O.layernorm_fwd(x, g, b, M, N, eps, xdt, gdt)
+    xt = _put(x, xdt, misalign)
+    yt = xt if inplace else _empty(M * N, xdt, misalign)
+    mt = torch.full((M,), float("nan"), device="cuda") if stats else None
+    rt = torch.full((M,), float("nan"), device="cuda") if stats else None
+    st = R.layernorm_fwd(xt, _put(g, gdt), _put(b, gdt) if with_beta else None, yt, mt, rt, M, N,
+                         eps, xdt, gdt, _stream())
+    assert st == 0, R.rmsnorm_status_string(st)
+    torch.cuda.synchronize()
+    return check_layernorm(to_host(yt), ref, x, g, b, xdt,
+                           to_host(mt) if stats else None, to_host(rt) if stats else None)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("N", [1, 7, 8, 64, 1000, 2048, 4096, 5000, 6152, 8191, 8192, 8193, 16384])
+def test_layernorm_sweep(N, pair):
+    run_ln(5, N, *pair, seed=1800 + N, with_beta=(N % 2 == 0), stats=(N % 3 != 0))
+    run_ln(300, N, *pair, seed=1900 + N)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_layernorm_long_misaligned_inplace_shifted(pair):
+    run_ln(3, N_LDS[pair[0]], *pair, seed=2001)
+    run_ln(3, N_REREAD[pair[0]], *pair, seed=2002)
+    run_ln(7, 4096, *pair, seed=2003, misalign=1)
+    run_ln(7, 9000, *pair, seed=2004, misalign=1)
+    run_ln(64, 8192, *pair, seed=2005, inplace=True)
+    run_ln(64, 4096, *pair, seed=2006, shift=30.0)          # mean far from zero
+    run_ln(1000, 8192, *pair, seed=2007, outlier_every=13, outlier_scale=300.0)
+
+
+def test_layernorm_constant_rows_give_beta():
+    # var = 0: y = beta exactly up to the tiny centring error, rstd = 1/sqrt(eps).
+    M, N = 4, 4096
+    x = O.round_to(np.full((M, N), 0.375), O.BF16)
+    g = G.uniform(3, G.STREAM_GAMMA, N, 0.5, 1.5, O.BF16)
+    b = G.uniform(3, G.STREAM_DY, N, -1.0, 1.0, O.BF16)
+    ref = O.layernorm_fwd(x, g, b, M, N, 1e-5, O.BF16, O.BF16)
+    yt, mt, rt = _empty(M * N, O.BF16), torch.empty(M, device="cuda"), torch.empty(M, device="cuda")
+    assert R.layernorm_fwd(_put(x, O.BF16), _put(g, O.BF16), _put(b, O.BF16), yt, mt, rt, M, N,
+                           1e-5, O.BF16, O.BF16, _stream()) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(yt).reshape(M, N), np.broadcast_to(b, (M, N)))
+    assert np.all(to_host(mt) == 0.375)
+    check_rstd(to_host(rt), ref["rstd_exact"])
+
+
 # ----------------------------------------------------------------- backward
 
 def run_bwd(M, N, xdt, gdt, seed=13, misalign=0, alias=None, gpu_rstd=False, eps=1e-5):
@@ -644,6 +701,8 @@ def test_workload_full_size(w):
         run_fused(w.M, w.N, w.x_dt, w.g_dt, eps=w.eps, seed=w.seed, want_rstd=w.store_rstd)
     elif w.kind == "fused_add_bwd":
         run_fused_bwd(w.M, w.N, w.x_dt, w.g_dt, seed=w.seed)
+    elif w.kind == "ln":
+        run_ln(w.M, w.N, w.x_dt, w.g_dt, seed=w.seed, eps=w.eps)
     elif w.kind == "qk":
         run_qk(w.M, w.heads_q, w.heads_k, w.N, w.x_dt, w.g_dt, seed=w.seed, eps=w.eps)
     elif w.kind == "quant":
