@@ -23,8 +23,8 @@ Also reported, in the same JSON line:
                 backward, fp16 ragged rows) and the fused-add backward, timed
                 the same way, the fp8-output forward (per-row scales at the
                 headline shape; one scale after the fused add), the per-head
-                QK-norm on a fused q/k/v buffer and LayerNorm at the headline
-                shape;
+                QK-norm on a fused q/k/v buffer, LayerNorm at the headline
+                shape and the LayerNorm backward at the backward's shape;
   calibration   a plain device-to-device copy of the step's byte count.
 """
 
@@ -55,6 +55,7 @@ DOMINANT_KERNEL = {
     "fusedadd_fp8tensor_bf16_m16384_n4096_gf32": "fwd_reg_kernel",
     "qknorm_bf16_t16384_hq32_hk8_d128": "qk_norm_kernel",
     "layernorm_bf16_m4096_n8192": "fwd_pp_kernel",
+    "layernorm_bwd_bf16_m8192_n8192": "bwd_stage1_kernel",
 }
 DT_NAMES = {0: "f32", 1: "f16", 2: "bf16"}
 
@@ -100,7 +101,7 @@ class Runner:
                        "fused_add_bwd": 4 * big,
                        "quant": (2 if w.fused_quant else 1) * big + M * N,
                        "qk": M * (w.heads_q + 2 * w.heads_k) * N * w.esize,
-                       "ln": 2 * big}[w.kind]
+                       "ln": 2 * big, "ln_bwd": 3 * big}[w.kind]
         self.replicas = max(1, int(-(-rotate_bytes // per_replica))) if rotate_bytes > 0 else 1
         x0 = dev_copy(host_inputs["x"], w.x_dt)
         g = dev_copy(host_inputs["gamma"], w.g_dt)
@@ -108,17 +109,23 @@ class Runner:
         self.sets = []
         stream = torch.cuda.current_stream(dev)
         self.stream_handle = stream.cuda_stream
-        rstd_bwd = None
-        backward = w.kind in ("bwd", "fused_add_bwd")
+        rstd_bwd = mean_bwd = None
+        backward = w.kind in ("bwd", "fused_add_bwd", "ln_bwd")
         if backward:
-            # The saved rstd comes from this library's own forward pass.
+            # The saved statistics come from this library's own forward pass.
             rstd_bwd = torch.empty(M, dtype=torch.float32, device=dev)
             tmp = torch.empty_like(x0)
-            st = R.rmsnorm_fwd(x0, g, tmp, rstd_bwd, M, N, w.eps, w.x_dt, w.g_dt, stream)
+            if w.kind == "ln_bwd":
+                mean_bwd = torch.empty(M, dtype=torch.float32, device=dev)
+                st = R.layernorm_fwd(x0, g, None, tmp, mean_bwd, rstd_bwd, M, N, w.eps, w.x_dt,
+                                     w.g_dt, stream)
+                self.ws_bytes = R.layernorm_bwd_workspace_size(M, N, w.x_dt)
+            else:
+                st = R.rmsnorm_fwd(x0, g, tmp, rstd_bwd, M, N, w.eps, w.x_dt, w.g_dt, stream)
+                self.ws_bytes = R.rmsnorm_bwd_workspace_size(M, N, w.x_dt)
             assert st == 0, R.rmsnorm_status_string(st)
             del tmp
             dy0 = dev_copy(host_inputs["dy"], w.x_dt)
-            self.ws_bytes = R.rmsnorm_bwd_workspace_size(M, N, w.x_dt)
         if w.kind == "fused_add_bwd":
             dres0 = dev_copy(host_inputs["dres"], w.x_dt)
         if w.kind == "fused_add" or (w.kind == "quant" and w.fused_quant):
@@ -159,6 +166,9 @@ class Runner:
                 s["ws"] = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
                 if w.kind == "fused_add_bwd":
                     s["dres"] = dres0 if i == 0 else dres0.clone()
+                if w.kind == "ln_bwd":
+                    s["mean"] = mean_bwd
+                    s["dbeta"] = torch.empty(N, dtype=torch.float32, device=dev)
             self.sets.append(s)
         torch.cuda.synchronize()
         # Pre-marshalled integer arguments keep the host launch path short.
@@ -187,6 +197,11 @@ class Runner:
                 args = (p["x"], p["r"], g.data_ptr(), p["q"], p["scale"], w.quant_mode, p["rstd"],
                         M, N, w.eps, w.x_dt, w.g_dt, self.stream_handle)
                 self.calls.append((lib.rmsnorm_quant_fwd, args))
+            elif w.kind == "ln_bwd":
+                args = (p["dy"], p["x"], p["mean"], p["rstd"], g.data_ptr(), p["dx"], p["dgamma"],
+                        p["dbeta"], p["ws"], self.ws_bytes, M, N, w.x_dt, w.g_dt,
+                        self.stream_handle)
+                self.calls.append((lib.layernorm_bwd, args))
             elif w.kind == "bwd":
                 args = (p["dy"], p["x"], p["rstd"], g.data_ptr(), p["dx"], p["dgamma"], p["ws"],
                         self.ws_bytes, M, N, w.x_dt, w.g_dt, self.stream_handle)
@@ -275,6 +290,12 @@ def cpu_baseline(w, host_inputs: dict, seconds: float) -> dict:
         def one_pass():
             O.rmsnorm_quant_fwd(x, g, M, N, w.eps, w.x_dt, w.g_dt, w.quant_mode,
                                 scale=w.tensor_scale, r=host_inputs.get("r"), want_exact=False)
+    elif w.kind == "ln_bwd":
+        f = O.layernorm_fwd(x, g, None, M, N, w.eps, w.x_dt, w.g_dt, want_exact=False)
+
+        def one_pass():
+            O.layernorm_bwd(host_inputs["dy"], x, f["mean"], f["rstd"], g, M, N, w.x_dt, w.g_dt,
+                            want_exact=False)
     else:
         # The saved rstd is an input of the backward, made outside the timing.
         rho = O.rmsnorm_fwd(x, g, M, N, w.eps, w.x_dt, w.g_dt, want_exact=False)["rstd"]
@@ -384,7 +405,7 @@ def main() -> int:
                                "pct_of_peak": round(100 * ob / (oms * 1e-3) / 1e9 / PEAK_GBPS, 2),
                                "rows_per_s": round(rows_of(ow) / (oms * 1e-3), 1),
                                "steps": k, "rotation_replicas": orun.replicas}
-            if ow.kind in ("bwd", "fused_add_bwd"):
+            if ow.kind in ("bwd", "fused_add_bwd", "ln_bwd"):
                 others[ow.name]["workspace_bytes"] = orun.ws_bytes
             del orun, oh
             torch.cuda.empty_cache()

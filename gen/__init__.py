@@ -108,7 +108,8 @@ def raw_bits(seed: int, stream: int, n: int) -> np.ndarray:
 class Workload:
     """One benchmark / parity workload."""
     name: str
-    kind: str            # "fwd", "fused_add", "bwd", "fused_add_bwd", "quant", "qk", "ln"
+    kind: str            # "fwd", "fused_add", "bwd", "fused_add_bwd", "quant", "qk", "ln",
+                         # "ln_bwd"
     M: int
     N: int
     x_dt: int
@@ -140,6 +141,9 @@ class Workload:
             return 2 * big + g + (4 * self.M if self.store_rstd else 0)
         if self.kind == "fused_add":
             return 4 * big + g + (4 * self.M if self.store_rstd else 0)
+        if self.kind == "ln_bwd":
+            # read x, dy, mean, rstd, gamma; write dx, dgamma, dbeta (fp32)
+            return 3 * big + 8 * self.M + g + 8 * self.N
         if self.kind == "ln":
             # read x, gamma, beta; write y, mean, rstd
             return 2 * big + 2 * g + 8 * self.M
@@ -186,6 +190,7 @@ EXTRA_WORKLOADS = [
     Workload("qknorm_bf16_t16384_hq32_hk8_d128", "qk", 16384, 128, BF16, BF16, 1e-6, 1009,
              heads_q=32, heads_k=8),
     Workload("layernorm_bf16_m4096_n8192", "ln", 4096, 8192, BF16, BF16, 1e-5, 1010),
+    Workload("layernorm_bwd_bf16_m8192_n8192", "ln_bwd", 8192, 8192, BF16, BF16, 1e-5, 1011),
 ]
 WORKLOADS_BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
@@ -207,7 +212,7 @@ def make_inputs(w: Workload, nthreads: int | None = None) -> dict:
                                  nthreads=nthreads)
     if w.kind == "ln":
         out["beta"] = uniform(w.seed, STREAM_DY, w.N, -1.0, 1.0, w.g_dt, nthreads=nthreads)
-    if w.kind in ("bwd", "fused_add_bwd"):
+    if w.kind in ("bwd", "fused_add_bwd", "ln_bwd"):
         out["dy"] = normal(w.seed, STREAM_DY, w.M, w.N, w.x_dt, nthreads=nthreads)
     if w.kind == "fused_add_bwd":
         out["dres"] = normal(w.seed, STREAM_DRES, w.M, w.N, w.x_dt, nthreads=nthreads)

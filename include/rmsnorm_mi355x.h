@@ -205,6 +205,32 @@ int layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y, f
                   float* rstd, int64_t M, int64_t N, float eps, int x_dtype,
                   int gamma_dtype, hipStream_t stream);
 
+/* Bytes of device workspace layernorm_bwd needs: two fp32 partial arrays
+ * (dgamma, dbeta) of min(M, 256) rows and, for rows longer than 8192, two
+ * doubles per row. 0 for M <= 0, N <= 0 or an unknown dtype. */
+size_t layernorm_bwd_workspace_size(int64_t M, int64_t N, int x_dtype);
+
+/* LayerNorm backward. The pages give only the forward (FlyDSL guide, section
+ * 1.1); this is its derivative with the saved per-row mean and rstd (the
+ * forward's outputs, eps already inside rstd):
+ *     xhat_ij = (x_ij - mean_i) rstd_i
+ *     c1_i = (1/N) sum_j gamma_j dy_ij,   c2_i = (1/N) sum_j gamma_j dy_ij xhat_ij
+ *     dx_ij = rstd_i (gamma_j dy_ij - c1_i - xhat_ij c2_i)
+ *     dgamma_j = sum_i dy_ij xhat_ij,     dbeta_j = sum_i dy_ij
+ * fp32 arithmetic with the row dots accumulated in double; dgamma and dbeta
+ * (fp32, OVERWRITTEN) are reduced in two fixed-order stages as in
+ * rmsnorm_bwd, so repeated calls give bit-identical results.
+ *   dy, x      [M, N] x_dtype, read.    mean, rstd [M] fp32, read.
+ *   gamma      [N] gamma_dtype, read.
+ *   dx         [M, N] x_dtype, written; may equal dy or x exactly.
+ *   dgamma     [N] fp32, written.   dbeta [N] fp32, written, or NULL (skipped).
+ *   workspace  at least layernorm_bwd_workspace_size(M, N, x_dtype) bytes,
+ *              16-byte aligned, disjoint from every other buffer. */
+int layernorm_bwd(const void* dy, const void* x, const float* mean, const float* rstd,
+                  const void* gamma, void* dx, float* dgamma, float* dbeta, void* workspace,
+                  size_t workspace_bytes, int64_t M, int64_t N, int x_dtype, int gamma_dtype,
+                  hipStream_t stream);
+
 /* Static English description of a status code ("unknown status" otherwise). */
 const char* rmsnorm_status_string(int status);
 

@@ -4,14 +4,14 @@ librmsnorm_mi355x.so.
 The C ABI (include/rmsnorm_mi355x.h) is exposed under the same names
 (``rmsnorm_fwd``, ``rmsnorm_fused_add_fwd``, ``rmsnorm_bwd``,
 ``rmsnorm_fused_add_bwd``, ``rmsnorm_quant_fwd``, ``rmsnorm_qk_fwd``, ``layernorm_fwd``,
-``rmsnorm_bwd_workspace_size``,
+``layernorm_bwd``, ``layernorm_bwd_workspace_size``, ``rmsnorm_bwd_workspace_size``,
 ``rmsnorm_status_string``,
 ``rmsnorm_last_hip_error``); those functions only marshal arguments. Pointers
 may be given as integers or as torch tensors (their ``data_ptr()``); streams as
 integers or ``torch.cuda.Stream`` objects.
 
-``fwd``, ``fused_add_fwd``, ``quant_fwd``, ``qk_fwd``, ``bwd``, ``fused_add_bwd`` and
-``layernorm`` are torch conveniences on top: they use
+``fwd``, ``fused_add_fwd``, ``quant_fwd``, ``qk_fwd``, ``bwd``, ``fused_add_bwd``,
+``layernorm`` and ``layernorm_backward`` are torch conveniences on top: they use
 torch only to allocate outputs and to pick the current stream, and every step
 of the computation runs in the library's HIP kernels. There is no fallback: if
 the library is not built, every call raises.
@@ -35,7 +35,7 @@ STATUS_NAMES = {
     -7: "RMSN_ERR_EPS", -8: "RMSN_ERR_MODE", -100: "RMSN_ERR_HIP",
 }
 ENTRY_POINTS = ("rmsnorm_fwd", "rmsnorm_fused_add_fwd", "rmsnorm_quant_fwd", "rmsnorm_qk_fwd",
-                "layernorm_fwd", "rmsnorm_bwd",
+                "layernorm_fwd", "layernorm_bwd", "layernorm_bwd_workspace_size", "rmsnorm_bwd",
                 "rmsnorm_fused_add_bwd", "rmsnorm_bwd_workspace_size", "rmsnorm_status_string",
                 "rmsnorm_last_hip_error")
 
@@ -76,6 +76,11 @@ def load_library(path: str | None = None):
     lib.rmsnorm_qk_fwd.restype = i32
     lib.layernorm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
     lib.layernorm_fwd.restype = i32
+    lib.layernorm_bwd_workspace_size.argtypes = [i64, i64, i32]
+    lib.layernorm_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.layernorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64,
+                                  i32, i32, vp]
+    lib.layernorm_bwd.restype = i32
     lib.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i32]
     lib.rmsnorm_bwd_workspace_size.restype = ctypes.c_size_t
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i32, i32, vp]
@@ -139,6 +144,17 @@ def rmsnorm_qk_fwd(q, k, q_gamma, k_gamma, tokens, q_heads, k_heads, head_dim, q
 def layernorm_fwd(x, gamma, beta, y, mean, rstd, M, N, eps, x_dtype, gamma_dtype, stream) -> int:
     return load_library().layernorm_fwd(_p(x), _p(gamma), _p(beta), _p(y), _p(mean), _p(rstd), M,
                                         N, eps, x_dtype, gamma_dtype, _s(stream))
+
+
+def layernorm_bwd_workspace_size(M, N, x_dtype) -> int:
+    return int(load_library().layernorm_bwd_workspace_size(M, N, x_dtype))
+
+
+def layernorm_bwd(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, workspace, workspace_bytes, M, N,
+                  x_dtype, gamma_dtype, stream) -> int:
+    return load_library().layernorm_bwd(_p(dy), _p(x), _p(mean), _p(rstd), _p(gamma), _p(dx),
+                                        _p(dgamma), _p(dbeta), _p(workspace), workspace_bytes, M,
+                                        N, x_dtype, gamma_dtype, _s(stream))
 
 
 def rmsnorm_bwd_workspace_size(M, N, x_dtype) -> int:
@@ -325,3 +341,25 @@ def fused_add_bwd(dy, h, rstd, gamma, dresidual=None, *, dh=None, dgamma=None, w
                                  workspace.numel(), M, N, dtype_code(h), dtype_code(gamma), stream),
            "rmsnorm_fused_add_bwd")
     return dh, dgamma
+
+
+def layernorm_backward(dy, x, mean, rstd, gamma, *, want_dbeta: bool = True, dx=None,
+                       workspace=None, stream=None):
+    """LayerNorm backward with the forward's mean and rstd; returns
+    (dx, dgamma fp32, dbeta fp32 or None)."""
+    import torch
+    N = gamma.numel()
+    M = _rows(x, N)
+    if dy.shape != x.shape or dy.dtype != x.dtype:
+        raise ValueError("dy must match x in shape and dtype")
+    dx = torch.empty_like(x) if dx is None else dx
+    dgamma = torch.empty(N, dtype=torch.float32, device=x.device)
+    dbeta = torch.empty(N, dtype=torch.float32, device=x.device) if want_dbeta else None
+    ws_bytes = layernorm_bwd_workspace_size(M, N, dtype_code(x))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    stream = torch.cuda.current_stream(x.device) if stream is None else stream
+    _check(layernorm_bwd(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, workspace,
+                         workspace.numel(), M, N, dtype_code(x), dtype_code(gamma), stream),
+           "layernorm_bwd")
+    return dx, dgamma, dbeta

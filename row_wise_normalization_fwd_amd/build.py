@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "fwd_f32.hip", "fwd_f16.hip", "fwd_bf16.hip", "fwd_quant_f32.hip",
            "fwd_quant_f16.hip", "fwd_quant_bf16.hip", "ln_fwd_f32.hip", "ln_fwd_f16.hip",
-           "ln_fwd_bf16.hip", "qk.hip", "bwd.hip"]
+           "ln_fwd_bf16.hip", "qk.hip", "bwd.hip", "ln_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

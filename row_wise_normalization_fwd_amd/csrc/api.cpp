@@ -235,6 +235,7 @@ int qk_forward(void* q, void* k, const void* q_gamma, const void* k_gamma, int64
 
 namespace rmsn {
 BwdPlan plan_bwd(int64_t M, int64_t N, int x_dtype);
+BwdPlan plan_ln_bwd(int64_t M, int64_t N, int x_dtype);
 }
 
 namespace {
@@ -279,6 +280,50 @@ int backward(const void* dy, const void* x, const float* rstd, const void* gamma
   return finish(rmsn::launch_bwd(c));
 }
 
+// Validation of the LayerNorm backward.
+int ln_backward(const void* dy, const void* x, const float* mean, const float* rstd,
+                const void* gamma, void* dx, float* dgamma, float* dbeta, void* workspace,
+                size_t workspace_bytes, int64_t M, int64_t N, int x_dtype, int gamma_dtype,
+                hipStream_t stream) {
+  if (!valid_pair(x_dtype, gamma_dtype)) return RMSN_ERR_DTYPE;
+  if (!shape_ok(M, N)) return RMSN_ERR_SHAPE;
+  if (M == 0) return RMSN_OK;
+  const rmsn::BwdPlan plan = rmsn::plan_ln_bwd(M, N, x_dtype);
+  if (!dy || !x || !mean || !rstd || !gamma || !dx || !dgamma) return RMSN_ERR_NULL;
+  if (!workspace || workspace_bytes < plan.workspace_bytes) return RMSN_ERR_WORKSPACE;
+  const int es = esize_of(x_dtype), gs = esize_of(gamma_dtype);
+  if (!aligned(dy, es) || !aligned(x, es) || !aligned(dx, es) || !aligned(gamma, gs) ||
+      !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(dgamma, 4) ||
+      (dbeta && !aligned(dbeta, 4)) || !aligned(workspace, 16))
+    return RMSN_ERR_ALIGN;
+  const uint64_t big = static_cast<uint64_t>(M) * static_cast<uint64_t>(N) * es;
+  const Range rdy = span(dy, big), rx = span(x, big), rdx = span(dx, big);
+  const Range rm = span(mean, static_cast<uint64_t>(M) * 4);
+  const Range rr = span(rstd, static_cast<uint64_t>(M) * 4);
+  const Range rg = span(gamma, static_cast<uint64_t>(N) * gs);
+  const Range rdg = span(dgamma, static_cast<uint64_t>(N) * 4);
+  const Range rw = span(workspace, plan.workspace_bytes);
+  // dx may equal dy or x exactly; the written buffers overlap nothing else.
+  if (partial_overlap(rdx, rdy) || partial_overlap(rdx, rx) || overlap(rdx, rm) ||
+      overlap(rdx, rr) || overlap(rdx, rg) || overlap(rdx, rdg) || overlap(rdx, rw))
+    return RMSN_ERR_OVERLAP;
+  const Range reads[] = {rdy, rx, rm, rr, rg};
+  for (const Range& r : reads)
+    if (overlap(rdg, r) || overlap(rw, r)) return RMSN_ERR_OVERLAP;
+  if (overlap(rdg, rw)) return RMSN_ERR_OVERLAP;
+  if (dbeta) {
+    const Range rdb = span(dbeta, static_cast<uint64_t>(N) * 4);
+    for (const Range& r : reads)
+      if (overlap(rdb, r)) return RMSN_ERR_OVERLAP;
+    if (overlap(rdb, rdx) || overlap(rdb, rdg) || overlap(rdb, rw)) return RMSN_ERR_OVERLAP;
+  }
+  rmsn::BwdCall c{dy, x, rstd, gamma, nullptr, dx, dgamma, workspace, M, N, x_dtype, gamma_dtype,
+                  plan, stream};
+  c.mean = mean;
+  c.dbeta = dbeta;
+  return finish(rmsn::launch_ln_bwd(c));
+}
+
 }  // namespace
 
 namespace rmsn {
@@ -319,6 +364,15 @@ int64_t device_cus() {
 hipError_t allow_dynamic_lds(const void* kernel, size_t bytes) {
   return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                              static_cast<int>(bytes));
+}
+
+BwdPlan plan_ln_bwd(int64_t M, int64_t N, int x_dtype) {
+  BwdPlan p = plan_bwd(M, N, x_dtype);
+  if (!p.valid) return p;
+  auto round256 = [](uint64_t b) { return (b + 255u) & ~static_cast<uint64_t>(255u); };
+  const uint64_t dots = N > kBwdOnChipN ? round256(static_cast<uint64_t>(M) * 16u) : 0u;
+  p.workspace_bytes = 2 * p.partial_bytes + static_cast<size_t>(dots);
+  return p;
 }
 
 BwdPlan plan_bwd(int64_t M, int64_t N, int x_dtype) {
@@ -388,6 +442,18 @@ int rmsnorm_fused_add_bwd(const void* dy, const void* h, const float* rstd, cons
                           int gamma_dtype, hipStream_t stream) {
   return backward(dy, h, rstd, gamma, dresidual, dh, dgamma, workspace, workspace_bytes, M, N,
                   x_dtype, gamma_dtype, stream);
+}
+
+size_t layernorm_bwd_workspace_size(int64_t M, int64_t N, int x_dtype) {
+  return rmsn::plan_ln_bwd(M, N, x_dtype).workspace_bytes;
+}
+
+int layernorm_bwd(const void* dy, const void* x, const float* mean, const float* rstd,
+                  const void* gamma, void* dx, float* dgamma, float* dbeta, void* workspace,
+                  size_t workspace_bytes, int64_t M, int64_t N, int x_dtype, int gamma_dtype,
+                  hipStream_t stream) {
+  return ln_backward(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, workspace, workspace_bytes, M,
+                     N, x_dtype, gamma_dtype, stream);
 }
 
 const char* rmsnorm_status_string(int status) {

@@ -1,0 +1,157 @@
+// Backward kernel choice and launch (stage 1 then stage 2, same stream) for
+// RMSNorm, its fused-add variant (RES) and LayerNorm (LN). Included by one
+// translation unit per operation so the instantiations compile in parallel.
+//
+// Stage 1 uses a group of TPR lanes per row with two 16-byte units per lane
+// (TPR = next power of two of ceil(units / 2), up to 1024 lanes, i.e. 16384
+// bf16 / 8192 fp32 elements; unaligned rows up to 8192 elements). Longer rows
+// take the two-pass long-row tier (row dots, then 2-D tiles). When a block owns at least two rows,
+// it runs 1024 threads, i.e. 1024 / TPR row groups whose dgamma partials are
+// combined through LDS: at 8192 x 8192 bf16 this (two 512-lane groups per
+// block, one block per CU, next-row prefetch) measured fastest among 1, 2 and
+// 4 groups, 256 to 1024 lanes per row and 256 / 384 / 512 blocks. Rows that are not 16-byte aligned use 1-element units.
+#pragma once
+
+#include "bwd_kernels.hpp"
+#include "launch.hpp"
+
+namespace rmsn {
+
+template <class T, class G, bool RES, bool LN, bool VEC, int TPR, int UPT, int BLOCK>
+hipError_t run_stage1(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s) {
+  constexpr int RG = BLOCK / TPR;
+  constexpr int E = Unit<T, VEC>::E;
+  constexpr size_t kLds = RG > 1 ? static_cast<size_t>(BLOCK) * UPT * E * sizeof(float) : 0;
+  constexpr auto kernel = bwd_stage1_kernel<T, G, VEC, TPR, UPT, BLOCK, RES, LN>;
+  if constexpr (kLds > 48 * 1024) {
+    // Raise the dynamic LDS limit (gfx950 has 160 KiB per workgroup).
+    const hipError_t attr = ensure_dynamic_lds<kernel>(kLds);
+    if (attr != hipSuccess) return attr;
+  }
+  kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), kLds, s>>>(a);
+  return hipGetLastError();
+}
+
+// Lanes per row TPR with UPT units each; a full 1024-thread block of row
+// groups when each block owns at least two rows.
+// LayerNorm keeps a second accumulator per column and spills in 1024-thread
+// blocks, so its row groups share 512-thread blocks.
+template <class T, class G, bool RES, bool LN, bool VEC, int TPR, int UPT>
+hipError_t run_stage1_rows(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s) {
+  constexpr int kFull = LN ? 512 : 1024;
+  if constexpr (TPR < kFull) {
+    if (a.M >= 2 * a.nblk) return run_stage1<T, G, RES, LN, VEC, TPR, UPT, kFull>(a, blocks, s);
+  }
+  return run_stage1<T, G, RES, LN, VEC, TPR, UPT, (TPR > 256 ? TPR : 256)>(a, blocks, s);
+}
+
+// One-pass path: returns hipErrorNotSupported when the row does not fit.
+template <class T, class G, bool RES, bool LN>
+hipError_t stage1_typed(const BwdArgs<T, G>& a, bool vec, int64_t blocks, hipStream_t s) {
+  const int64_t N = a.N;
+  if (vec) {
+    constexpr int E = 16 / T::kSize;
+    const int64_t units = N / E;
+    if (units > 2048) return hipErrorNotSupported;
+    // LayerNorm's 1024-lane rows of 16-bit data spill: two-pass tier instead
+    // (those rows are longer than 8192, so the workspace holds their dots).
+    if constexpr (LN && T::kSize == 2) {
+      if (units > 1024) return hipErrorNotSupported;
+    } else {
+      if (units > 1024) return run_stage1_rows<T, G, RES, LN, true, 1024, 2>(a, blocks, s);
+    }
+    switch (next_pow2(ceil_div(units, 2))) {
+      case 1: return run_stage1_rows<T, G, RES, LN, true, 1, 2>(a, blocks, s);
+      case 2: return run_stage1_rows<T, G, RES, LN, true, 2, 2>(a, blocks, s);
+      case 4: return run_stage1_rows<T, G, RES, LN, true, 4, 2>(a, blocks, s);
+      case 8: return run_stage1_rows<T, G, RES, LN, true, 8, 2>(a, blocks, s);
+      case 16: return run_stage1_rows<T, G, RES, LN, true, 16, 2>(a, blocks, s);
+      case 32: return run_stage1_rows<T, G, RES, LN, true, 32, 2>(a, blocks, s);
+      case 64: return run_stage1_rows<T, G, RES, LN, true, 64, 2>(a, blocks, s);
+      case 128: return run_stage1_rows<T, G, RES, LN, true, 128, 2>(a, blocks, s);
+      case 256: return run_stage1_rows<T, G, RES, LN, true, 256, 2>(a, blocks, s);
+      default: return run_stage1_rows<T, G, RES, LN, true, 512, 2>(a, blocks, s);
+    }
+  }
+  if (N > kBwdOnChipN) return hipErrorNotSupported;
+  if (N <= 512) return run_stage1<T, G, RES, LN, false, 64, 8, 256>(a, blocks, s);
+  if (N <= 2048) return run_stage1<T, G, RES, LN, false, 256, 8, 256>(a, blocks, s);
+  return run_stage1<T, G, RES, LN, false, 1024, 8, 1024>(a, blocks, s);
+}
+
+// Long-row tier: pass A (row dots), pass B (tiles). Same partition and
+// partial layout as the one-pass path.
+template <class T, class G, bool RES, bool LN, bool VEC>
+hipError_t long_rows_typed(const BwdArgs<T, G>& a, double* cdot, int64_t blocks, hipStream_t s) {
+  constexpr int kUnroll = VEC ? 4 : 8;
+  constexpr int kTileBlock = 256;
+  constexpr int kTileUpt = VEC ? 2 : 8;
+  constexpr int E = Unit<T, VEC>::E;
+  const int64_t rows = a.M < kMaxGrid ? a.M : kMaxGrid;
+  bwd_rowdot_kernel<T, G, VEC, 1024, kUnroll, LN>
+      <<<dim3(static_cast<unsigned>(rows)), dim3(1024), 0, s>>>(a, cdot);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t units = a.N / E;
+  const int64_t chunks = ceil_div(units, kTileBlock * kTileUpt);
+  bwd_tile_kernel<T, G, VEC, kTileBlock, kTileUpt, RES, LN>
+      <<<dim3(static_cast<unsigned>(chunks), static_cast<unsigned>(blocks)), dim3(kTileBlock), 0,
+         s>>>(a, cdot);
+  return hipGetLastError();
+}
+
+// Stage 2 over one partial array. Partial rows are 16-byte aligned when
+// N % 4 == 0 (the workspace and partial_bytes are).
+inline hipError_t run_stage2(const float* partial, float* out, const BwdCall& c) {
+  constexpr int kSlices = 16;
+  constexpr int kGroups = kS2Threads / kSlices;
+  if (c.N % 4 == 0) {
+    const int64_t blocks = ceil_div(c.N, 4 * kGroups);
+    bwd_stage2_kernel<4, kSlices>
+        <<<dim3(static_cast<unsigned>(blocks)), dim3(kS2Threads), 0, c.stream>>>(
+            partial, out, static_cast<int>(c.plan.blocks), static_cast<int>(c.N));
+  } else {
+    const int64_t blocks = ceil_div(c.N, kGroups);
+    bwd_stage2_kernel<1, kSlices>
+        <<<dim3(static_cast<unsigned>(blocks)), dim3(kS2Threads), 0, c.stream>>>(
+            partial, out, static_cast<int>(c.plan.blocks), static_cast<int>(c.N));
+  }
+  return hipGetLastError();
+}
+
+template <class T, class G, bool RES, bool LN>
+hipError_t bwd_typed(const BwdCall& c) {
+  BwdArgs<T, G> a;
+  a.dy = static_cast<const typename T::S*>(c.dy);
+  a.x = static_cast<const typename T::S*>(c.x);
+  a.rstd = c.rstd;
+  a.gamma = static_cast<const typename G::S*>(c.gamma);
+  a.dx = static_cast<typename T::S*>(c.dx);
+  a.dres = static_cast<const typename T::S*>(c.dres);
+  a.partial = static_cast<float*>(c.workspace);
+  a.mean = c.mean;
+  a.partial_b = LN ? reinterpret_cast<float*>(static_cast<char*>(c.workspace) +
+                                              c.plan.partial_bytes)
+                   : nullptr;
+  a.M = c.M;
+  a.N = static_cast<int>(c.N);
+  a.nblk = c.plan.blocks;
+  const bool vec = (c.N * T::kSize) % 16 == 0 && aligned16(c.dy) && aligned16(c.x) &&
+                   aligned16(c.dx) && aligned16(c.gamma);
+  const bool vec_all = vec && (!RES || aligned16(c.dres));
+  hipError_t e = stage1_typed<T, G, RES, LN>(a, vec_all, c.plan.blocks, c.stream);
+  if (e == hipErrorNotSupported) {
+    // Row dots after the partial rows (one array, two with LN).
+    double* cdot = reinterpret_cast<double*>(static_cast<char*>(c.workspace) +
+                                             (LN ? 2 : 1) * c.plan.partial_bytes);
+    e = vec_all ? long_rows_typed<T, G, RES, LN, true>(a, cdot, c.plan.blocks, c.stream)
+                : long_rows_typed<T, G, RES, LN, false>(a, cdot, c.plan.blocks, c.stream);
+  }
+  if (e != hipSuccess) return e;
+  e = run_stage2(a.partial, c.dgamma, c);
+  if (e != hipSuccess) return e;
+  if (LN && c.dbeta != nullptr) e = run_stage2(a.partial_b, c.dbeta, c);
+  return e;
+}
+
+}  // namespace rmsn

@@ -13,6 +13,14 @@
 // dres, is added to dx in fp32 before the one rounding, giving the gradient
 // of h (which is that of x and of r).
 //
+// With LN set the same kernels compute the LayerNorm backward (the derivative
+// of the FlyDSL guide's section 1.1 forward, which the pages do not give) from
+// the saved mean and rstd:
+//     xhat = (x - mean) rstd, c1 = (1/N) sum_j gamma dy, c2 = (1/N) sum_j gamma dy xhat
+//     dx = rstd (gamma dy - c1 - xhat c2), dgamma_j = sum_i dy xhat, dbeta_j = sum_i dy
+// The two row dots are reduced together; dgamma and dbeta get one partial
+// row each per block.
+//
 // The weight gradient is reduced in two stages without atomics: stage 1 gives
 // each of G blocks a fixed set of rows -- block b owns rows b, b + G, b + 2G,
 // ..., so at any moment all blocks work inside one compact window of rows
@@ -21,6 +29,8 @@
 // column in a fixed order. G depends only on M, so results are bit-
 // reproducible.
 #pragma once
+
+#include <type_traits>
 
 #include "device.hpp"
 
@@ -38,7 +48,24 @@ struct BwdArgs {
   int64_t M;
   int N;
   int64_t nblk;    // partition blocks G: block b owns rows b + G * s
+  const float* mean;  // LayerNorm: saved per-row mean
+  float* partial_b;   // LayerNorm: [G, N] fp32 dbeta partials
 };
+
+// LayerNorm per-unit pieces of the two row dots: sum gamma dy and
+// sum gamma dy xhat, fp32 within the unit.
+template <int E>
+__device__ __forceinline__ void unit_dots_ln(const float* dyv, const float* g, const float* xv,
+                                             float mu, float rho, float& s1, float& s2) {
+  s1 = 0.0f;
+  s2 = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float gdy = g[e] * dyv[e];
+    s1 = s1 + gdy;
+    s2 = __builtin_fmaf(gdy, (xv[e] - mu) * rho, s2);
+  }
+}
 
 // The row dot sum_j dy gamma x is formed per 16-byte unit in fp32 (one FMA
 // per element; for bf16 every product is exact, otherwise each step rounds
@@ -60,7 +87,7 @@ __device__ __forceinline__ float unit_dot(const float* dyv, const float* g, cons
 // current row is reduced, so loads stay in flight across rows. With RG > 1 the
 // groups' partials are combined through LDS in group order before the block
 // writes its partial row.
-template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool RES>
+template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool RES, bool LN = false>
 __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   using U = Unit<T, VEC>;
   using Raw = typename U::Raw;
@@ -68,7 +95,9 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   constexpr int RG = BLOCK / TPR;
   constexpr int COLS = TPR * UPT * E;  // columns covered by one row group
   static_assert(BLOCK % TPR == 0 && BLOCK % kWave == 0, "block shape");
-  __shared__ double red[2 * (BLOCK / kWave)];
+  static_assert(!(LN && RES), "LayerNorm backward has no residual input");
+  using Red = typename std::conditional<LN, DSum2, double>::type;
+  __shared__ Red red[2 * (BLOCK / kWave)];
   extern __shared__ __align__(16) unsigned char lds_bytes[];
   float* comb = reinterpret_cast<float*>(lds_bytes);  // [RG][COLS] when RG > 1
 
@@ -79,6 +108,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
 
   float gam[UPT][E];
   float acc[UPT][E];
+  [[maybe_unused]] float accb[LN ? UPT : 1][E];  // LayerNorm dbeta partial sums
 #pragma unroll
   for (int k = 0; k < UPT; ++k) {
     const int u = lane + k * TPR;
@@ -90,6 +120,10 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[k][e] = 0.0f;
+    if constexpr (LN) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) accb[k][e] = 0.0f;
+    }
   }
 
   // Rows handled in one iteration: row0 + nblk * g for the RG groups g. In
@@ -161,15 +195,27 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
     const int64_t off = row * a.N;
     const float rho_ld = a.rstd[valid ? row : a.M - 1];
     const float rho = valid ? rho_ld : 0.0f;
+    [[maybe_unused]] float mu = 0.0f;
+    if constexpr (LN) {
+      const float mu_ld = a.mean[valid ? row : a.M - 1];
+      mu = valid ? mu_ld : 0.0f;
+    }
     load_row(row0 + a.nblk * RG, nx, ndy, nr);
 
-    double dot = 0.0;
+    [[maybe_unused]] double dot = 0.0;
+    [[maybe_unused]] DSum2 dots{0.0, 0.0};
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       float xv[E], dyv[E];
       U::widen(cx[k], xv);
       U::widen(cdy[k], dyv);
-      dot = dot + static_cast<double>(unit_dot<E>(dyv, gam[k], xv));
+      if constexpr (LN) {
+        float s1, s2;
+        unit_dots_ln<E>(dyv, gam[k], xv, mu, rho, s1, s2);
+        dots = dots + DSum2{static_cast<double>(s1), static_cast<double>(s2)};
+      } else {
+        dot = dot + static_cast<double>(unit_dot<E>(dyv, gam[k], xv));
+      }
     }
     // Re-widen x and dy after the reduction rather than holding the fp32
     // copies across it: fewer live VGPRs, more row groups per CU.
@@ -178,21 +224,38 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
       opaque(cx[k]);
       opaque(cdy[k]);
     }
-    dot = row_sum<TPR, BLOCK>(dot, red, parity);
+    [[maybe_unused]] float kcoef = 0.0f, c1 = 0.0f, c2 = 0.0f;
+    if constexpr (LN) {
+      dots = row_sum<TPR, BLOCK>(dots, red, parity);
+      c1 = static_cast<float>(dots.a / static_cast<double>(a.N));
+      c2 = static_cast<float>(dots.b / static_cast<double>(a.N));
+    } else {
+      dot = row_sum<TPR, BLOCK>(dot, red, parity);
+      const double rd = static_cast<double>(rho);
+      kcoef = static_cast<float>(rd * rd * (dot / static_cast<double>(a.N)));
+    }
     parity ^= 1;
 
-    const double rd = static_cast<double>(rho);
-    const float kcoef = static_cast<float>(rd * rd * (dot / static_cast<double>(a.N)));
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const int u = lane + k * TPR;
       float xv[E], dyv[E], o[E];
       U::widen(cx[k], xv);
       U::widen(cdy[k], dyv);
+      if constexpr (LN) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        o[e] = rho * __builtin_fmaf(-xv[e], kcoef, gam[k][e] * dyv[e]);
-        acc[k][e] = __builtin_fmaf(dyv[e] * xv[e], rho, acc[k][e]);
+        for (int e = 0; e < E; ++e) {
+          const float xh = (xv[e] - mu) * rho;
+          o[e] = rho * (__builtin_fmaf(-xh, c2, gam[k][e] * dyv[e]) - c1);
+          acc[k][e] = __builtin_fmaf(dyv[e], xh, acc[k][e]);
+          accb[k][e] = accb[k][e] + dyv[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          o[e] = rho * __builtin_fmaf(-xv[e], kcoef, gam[k][e] * dyv[e]);
+          acc[k][e] = __builtin_fmaf(dyv[e] * xv[e], rho, acc[k][e]);
+        }
       }
       if constexpr (RES) {
         float rv[E];
@@ -219,50 +282,60 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
     step(b + a.nblk * (s0 + RG), bx, bdy, br, ax, ady, ar);
   }
 
-  float* out = a.partial + static_cast<int64_t>(blockIdx.x) * a.N;
-  if constexpr (RG == 1) {
+  // The block's partial row(s): one array (dgamma), two with LN (dbeta).
+  auto write_partial = [&](float* base, float (*sums)[E]) {
+    float* out = base + static_cast<int64_t>(blockIdx.x) * a.N;
+    if constexpr (RG == 1) {
 #pragma unroll
-    for (int k = 0; k < UPT; ++k) {
-      const int u = lane + k * TPR;
-      if (u < nunits) {
+      for (int k = 0; k < UPT; ++k) {
+        const int u = lane + k * TPR;
+        if (u < nunits) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) out[u * E + e] = acc[k][e];
+          for (int e = 0; e < E; ++e) out[u * E + e] = sums[k][e];
+        }
+      }
+    } else {
+      __syncthreads();  // the previous combine's readers are done with comb
+#pragma unroll
+      for (int k = 0; k < UPT; ++k) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) comb[grp * COLS + (k * TPR + lane) * E + e] = sums[k][e];
+      }
+      __syncthreads();
+      // Lane `lane`, unit k holds column (k * TPR + lane) * E + e, so entry c
+      // of a group's slice is column c; sum the groups in increasing order.
+      for (int c = threadIdx.x; c < nunits * E; c += BLOCK) {
+        float s = comb[c];
+        for (int g = 1; g < RG; ++g) s = s + comb[g * COLS + c];
+        out[c] = s;
       }
     }
-  } else {
-#pragma unroll
-    for (int k = 0; k < UPT; ++k) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) comb[grp * COLS + (k * TPR + lane) * E + e] = acc[k][e];
-    }
-    __syncthreads();
-    // Lane `lane`, unit k holds column (k * TPR + lane) * E + e, so entry c of
-    // a group's slice is column c; sum the groups in increasing order.
-    for (int c = threadIdx.x; c < nunits * E; c += BLOCK) {
-      float s = comb[c];
-      for (int g = 1; g < RG; ++g) s = s + comb[g * COLS + c];
-      out[c] = s;
-    }
-  }
+  };
+  write_partial(a.partial, acc);
+  if constexpr (LN) write_partial(a.partial_b, accb);
 }
 
 // Long rows (rows too long for stage 1's registers), in two passes.
 //
-// Pass A: c_i = (1/N) sum_j dy_ij gamma_j x_ij in double, one block per row,
-// looping over the row; ordinary (cacheable) loads since pass B reads the
-// same rows again.
-template <class T, class G, bool VEC, int BLOCK, int UNROLL>
+// Pass A: c_i = (1/N) sum_j dy_ij gamma_j x_ij in double (LN: c1_i and c2_i,
+// stored as cdot[2i], cdot[2i + 1]), one block per row, looping over the
+// row; ordinary (cacheable) loads since pass B reads the same rows again.
+template <class T, class G, bool VEC, int BLOCK, int UNROLL, bool LN = false>
 __global__ __launch_bounds__(BLOCK) void bwd_rowdot_kernel(BwdArgs<T, G> a, double* cdot) {
   using U = Unit<T, VEC>;
   using Raw = typename U::Raw;
   constexpr int E = U::E;
   constexpr int STEP = BLOCK * UNROLL;
-  __shared__ double red[2 * (BLOCK / kWave)];
+  using Red = typename std::conditional<LN, DSum2, double>::type;
+  __shared__ Red red[2 * (BLOCK / kWave)];
   const int nunits = a.N / E;
   int parity = 0;
   for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x) {
     const int64_t off = row * a.N;
+    [[maybe_unused]] const float rho = a.rstd[row];
+    [[maybe_unused]] const float mu = LN ? a.mean[row] : 0.0f;
     double dot = 0.0;
+    [[maybe_unused]] DSum2 dots{0.0, 0.0};
     for (int first = 0; first < nunits; first += STEP) {
       Raw rx[UNROLL], rdy[UNROLL];
 #pragma unroll
@@ -279,13 +352,27 @@ __global__ __launch_bounds__(BLOCK) void bwd_rowdot_kernel(BwdArgs<T, G> a, doub
           U::widen(rx[k], xv);
           U::widen(rdy[k], dyv);
           load_gamma<G, E, VEC>(a.gamma, u * E, g);
-          dot = dot + static_cast<double>(unit_dot<E>(dyv, g, xv));
+          if constexpr (LN) {
+            float s1, s2;
+            unit_dots_ln<E>(dyv, g, xv, mu, rho, s1, s2);
+            dots = dots + DSum2{static_cast<double>(s1), static_cast<double>(s2)};
+          } else {
+            dot = dot + static_cast<double>(unit_dot<E>(dyv, g, xv));
+          }
         }
       }
     }
-    dot = row_sum<BLOCK, BLOCK>(dot, red, parity);
+    if constexpr (LN) {
+      dots = row_sum<BLOCK, BLOCK>(dots, red, parity);
+      if (threadIdx.x == 0) {
+        cdot[2 * row] = dots.a / static_cast<double>(a.N);
+        cdot[2 * row + 1] = dots.b / static_cast<double>(a.N);
+      }
+    } else {
+      dot = row_sum<BLOCK, BLOCK>(dot, red, parity);
+      if (threadIdx.x == 0) cdot[row] = dot / static_cast<double>(a.N);
+    }
     parity ^= 1;
-    if (threadIdx.x == 0) cdot[row] = dot / static_cast<double>(a.N);
   }
 }
 
@@ -294,14 +381,16 @@ __global__ __launch_bounds__(BLOCK) void bwd_rowdot_kernel(BwdArgs<T, G> a, doub
 // the dgamma partial sums of its columns in registers over the block's rows
 // (in increasing row order) and writes them to partial[by][...]; dx uses the
 // row dots from pass A.
-template <class T, class G, bool VEC, int BLOCK, int UPT, bool RES>
+template <class T, class G, bool VEC, int BLOCK, int UPT, bool RES, bool LN = false>
 __global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const double* cdot) {
   using U = Unit<T, VEC>;
   using Raw = typename U::Raw;
   constexpr int E = U::E;
+  static_assert(!(LN && RES), "LayerNorm backward has no residual input");
   const int nunits = a.N / E;
   const int ubase = blockIdx.x * (BLOCK * UPT);
   float gam[UPT][E], acc[UPT][E];
+  [[maybe_unused]] float accb[LN ? UPT : 1][E];
 #pragma unroll
   for (int k = 0; k < UPT; ++k) {
     const int u = ubase + threadIdx.x + k * BLOCK;
@@ -313,6 +402,10 @@ __global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const 
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[k][e] = 0.0f;
+    if constexpr (LN) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) accb[k][e] = 0.0f;
+    }
   }
   for (int64_t row = blockIdx.y; row < a.M; row += a.nblk) {
     const int64_t off = row * a.N;
@@ -325,18 +418,35 @@ __global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const 
       if constexpr (RES) rr[k] = u < nunits ? U::load_nt(a.dres + off + u * E) : U::zero();
     }
     const float rho = a.rstd[row];
-    const double rd = static_cast<double>(rho);
-    const float kcoef = static_cast<float>(rd * rd * cdot[row]);
+    [[maybe_unused]] float kcoef = 0.0f, c1 = 0.0f, c2 = 0.0f, mu = 0.0f;
+    if constexpr (LN) {
+      mu = a.mean[row];
+      c1 = static_cast<float>(cdot[2 * row]);
+      c2 = static_cast<float>(cdot[2 * row + 1]);
+    } else {
+      const double rd = static_cast<double>(rho);
+      kcoef = static_cast<float>(rd * rd * cdot[row]);
+    }
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const int u = ubase + threadIdx.x + k * BLOCK;
       float xv[E], dyv[E], o[E];
       U::widen(rx[k], xv);
       U::widen(rdy[k], dyv);
+      if constexpr (LN) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        o[e] = rho * __builtin_fmaf(-xv[e], kcoef, gam[k][e] * dyv[e]);
-        acc[k][e] = __builtin_fmaf(dyv[e] * xv[e], rho, acc[k][e]);
+        for (int e = 0; e < E; ++e) {
+          const float xh = (xv[e] - mu) * rho;
+          o[e] = rho * (__builtin_fmaf(-xh, c2, gam[k][e] * dyv[e]) - c1);
+          acc[k][e] = __builtin_fmaf(dyv[e], xh, acc[k][e]);
+          accb[k][e] = accb[k][e] + dyv[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          o[e] = rho * __builtin_fmaf(-xv[e], kcoef, gam[k][e] * dyv[e]);
+          acc[k][e] = __builtin_fmaf(dyv[e] * xv[e], rho, acc[k][e]);
+        }
       }
       if constexpr (RES) {
         float rv[E];
@@ -348,12 +458,17 @@ __global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const 
     }
   }
   float* out = a.partial + static_cast<int64_t>(blockIdx.y) * a.N;
+  [[maybe_unused]] float* outb = LN ? a.partial_b + static_cast<int64_t>(blockIdx.y) * a.N : nullptr;
 #pragma unroll
   for (int k = 0; k < UPT; ++k) {
     const int u = ubase + threadIdx.x + k * BLOCK;
     if (u < nunits) {
 #pragma unroll
       for (int e = 0; e < E; ++e) out[u * E + e] = acc[k][e];
+      if constexpr (LN) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) outb[u * E + e] = accb[k][e];
+      }
     }
   }
 }

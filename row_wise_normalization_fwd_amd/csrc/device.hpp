@@ -259,6 +259,17 @@ __device__ __forceinline__ double dpp(double v) {
   return __builtin_bit_cast(double, h);
 }
 
+// Two sums reduced together (the LayerNorm backward's two row dots).
+struct DSum2 {
+  double a, b;
+  __device__ DSum2 operator+(DSum2 o) const { return {a + o.a, b + o.b}; }
+};
+
+template <int CTRL>
+__device__ __forceinline__ DSum2 dpp(DSum2 v) {
+  return {dpp<CTRL>(v.a), dpp<CTRL>(v.b)};
+}
+
 template <int CTRL>
 __device__ __forceinline__ SumMax dpp(SumMax v) {
   return {dpp<CTRL>(v.s), dpp<CTRL>(v.m)};
@@ -277,6 +288,10 @@ __device__ __forceinline__ double readlane(double v, int lane) {
   h.x = __builtin_amdgcn_readlane(h.x, lane);
   h.y = __builtin_amdgcn_readlane(h.y, lane);
   return __builtin_bit_cast(double, h);
+}
+
+__device__ __forceinline__ DSum2 readlane(DSum2 v, int lane) {
+  return {readlane(v.a, lane), readlane(v.b, lane)};
 }
 
 // DPP controls (gfx9 encoding).

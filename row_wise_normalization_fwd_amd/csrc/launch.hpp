@@ -104,10 +104,13 @@ hipError_t launch_qk(const QKCall& c, int x_dtype);
 struct BwdPlan {
   bool valid;
   int64_t blocks;  // G
-  size_t partial_bytes;    // offset of the row dots
+  size_t partial_bytes;    // bytes of one partial array (the row dots follow the arrays)
   size_t workspace_bytes;
 };
 BwdPlan plan_bwd(int64_t M, int64_t N, int x_dtype);
+// LayerNorm: two partial arrays (dgamma, dbeta), then two doubles per row
+// for rows too long to keep on chip.
+BwdPlan plan_ln_bwd(int64_t M, int64_t N, int x_dtype);
 
 constexpr int64_t kBwdTargetBlocks = 256;
 // Rows up to this many elements may use the one-pass backward (registers);
@@ -129,9 +132,12 @@ struct BwdCall {
   int gamma_dtype;
   BwdPlan plan;
   hipStream_t stream;
+  const float* mean = nullptr;  // LayerNorm: saved per-row mean
+  float* dbeta = nullptr;       // LayerNorm: bias gradient (may be null)
 };
 
 hipError_t launch_bwd(const BwdCall& c);
+hipError_t launch_ln_bwd(const BwdCall& c);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -17,6 +17,9 @@ Tolerances (fixed here, used by every GPU test):
     or beta cancel, |y - y_exact| <= 2^-18 rstd |gamma| (|x - mean| + A) +
     2^-22 |beta| with A = mean_j |x_ij| (the fp32 mean carries an error of a
     few 2^-24 A); mean: |m - mean| <= 2^-18 A; rstd: relative 1e-5.
+  * LayerNorm dx: within 1 ulp, or |dx - exact| <= 2^-18 rstd (|gamma dy| +
+    A1 + |xhat| A2) with A1 = mean_j |gamma dy|, A2 = mean_j |gamma dy xhat|;
+    dgamma / dbeta as dgamma above with S = sum_i |dy xhat| / sum_i |dy|.
   * fp8 e4m3 codes: ordinal distance <= 1 from the oracle's code (the kernel
     scales in fp32, so y / s can land on the other side of a tie); per-row
     scales: relative error <= 1e-5; every nonzero row's largest code is
@@ -190,4 +193,35 @@ def check_layernorm(got_y, ref, x, gamma, beta, dt, got_mean=None, got_rstd=None
         assert np.all(err <= 2.0 ** -18 * ref["amag"]), f"mean: worst {float(err.max())}"
     if got_rstd is not None:
         check_rstd(got_rstd, ref["rstd_exact"])
+    return int((~ok_ulp & ok_floor).sum())
+
+
+def check_layernorm_bwd(got_dx, got_dg, got_db, ref, x, dy, gamma, mean, rstd, dt):
+    """LayerNorm backward against the oracle run on the same fp32 mean/rstd."""
+    M, N = ref["dx"].shape
+    got_dx = got_dx.reshape(M, N)
+    exact = ref["dx_exact"]
+    if dt == O.F32:
+        ok_ulp = rel_error(got_dx, exact) <= 1e-5
+        gotv = got_dx.astype(np.float64)
+    else:
+        ok_ulp = ulp_distance16(got_dx, ref["dx"]) <= 1
+        gotv = O.decode(got_dx, dt).reshape(M, N)
+    gdt = O.F32 if gamma.dtype == np.float32 else dt
+    gd = O.decode(gamma, gdt)
+    xd = O.decode(x, dt).reshape(M, N)
+    dyd = O.decode(dy, dt).reshape(M, N)
+    rs = rstd.astype(np.float64)[:, None]
+    xh = (xd - mean.astype(np.float64)[:, None]) * rs
+    floor = 2.0 ** -18 * rs * (np.abs(gd[None, :] * dyd) + ref["a1"][:, None] +
+                               np.abs(xh) * ref["a2"][:, None])
+    ok_floor = np.abs(gotv - exact) <= floor
+    bad = ~(ok_ulp | ok_floor)
+    if bad.any():
+        idx = np.unravel_index(int(np.argmax(bad)), bad.shape)
+        raise AssertionError(f"layernorm dx: {int(bad.sum())} out of tolerance; first at {idx}: "
+                             f"got {gotv[idx]!r}, exact {exact[idx]!r}, floor {floor[idx]!r}")
+    check_dgamma(got_dg, {"dgamma": ref["dgamma"], "s": ref["sg"]})
+    if got_db is not None:
+        check_dgamma(got_db, {"dgamma": ref["dbeta"], "s": ref["sb"]})
     return int((~ok_ulp & ok_floor).sum())

@@ -255,3 +255,37 @@ def test_layernorm_validation(lib):
     assert ln(mean=A) == OVERLAP                    # mean over x
     assert ln(rstd=E + 8) == OVERLAP                # rstd over mean
     assert ln(mean=C + 4) == OVERLAP                # mean over beta
+
+
+def lnb(dy=A, x=B, mean=C, rstd=C + 4096, g=D, dx=E, dg=F, db=F + 65536, ws=G, wsb=None, M=64,
+        N=256, xd=BF16, gd=BF16):
+    if wsb is None:
+        wsb = R.layernorm_bwd_workspace_size(M, N, xd)
+    return R.layernorm_bwd(dy, x, mean, rstd, g, dx, dg, db, ws, wsb, M, N, xd, gd, None)
+
+
+def test_layernorm_workspace_size():
+    # Two fp32 partial arrays of min(M, 256) rows; rows longer than 8192 add
+    # two doubles per row.
+    assert R.layernorm_bwd_workspace_size(8192, 8192, BF16) == 2 * 256 * 8192 * 4
+    assert R.layernorm_bwd_workspace_size(3, 10, F32) == 2 * 256
+    assert R.layernorm_bwd_workspace_size(1000, 10000, BF16) == 2 * 256 * 10000 * 4 + 16128
+    assert R.layernorm_bwd_workspace_size(0, 10, BF16) == 0
+
+
+def test_layernorm_backward_validation(lib):
+    assert lnb(xd=4) == DTYPE
+    assert lnb(M=-1) == SHAPE
+    assert lnb(M=0, dy=None, x=None, mean=None, rstd=None, g=None, dx=None, dg=None, db=None,
+               ws=None) == OK
+    for k in ("dy", "x", "mean", "rstd", "g", "dx", "dg"):
+        assert lnb(**{k: None}) == NULL, k
+    assert lnb(ws=None) == WORKSPACE
+    assert lnb(wsb=R.layernorm_bwd_workspace_size(64, 256, BF16) - 1) == WORKSPACE
+    assert lnb(mean=C + 2) == ALIGN
+    assert lnb(db=F + 65536 + 2) == ALIGN
+    assert lnb(dx=A + 64) == OVERLAP
+    assert lnb(dx=C) == OVERLAP                      # dx over mean
+    assert lnb(db=F + 8) == OVERLAP                  # dbeta over dgamma
+    assert lnb(db=G + 16) == OVERLAP                 # dbeta in the workspace
+    assert lnb(ws=C) == OVERLAP                      # workspace over the statistics

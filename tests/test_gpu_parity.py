@@ -11,8 +11,8 @@ import torch
 import gen as G
 import oracle as O
 import row_wise_normalization_fwd_amd as R
-from gpu_util import (check_dgamma, check_dx, check_fp8, check_layernorm, check_output,
-                      check_rstd, to_device, to_host, TORCH_DTYPES)
+from gpu_util import (check_dgamma, check_dx, check_fp8, check_layernorm, check_layernorm_bwd,
+                      check_output, check_rstd, to_device, to_host, TORCH_DTYPES)
 
 pytestmark = pytest.mark.gpu
 
@@ -498,6 +498,75 @@ def test_layernorm_constant_rows_give_beta():
     check_rstd(to_host(rt), ref["rstd_exact"])
 
 
+def run_ln_bwd(M, N, xdt, gdt, seed=31, misalign=0, alias=None, gpu_stats=False, dbeta=True,
+               shift=0.0):
+    _log(f"layernorm_bwd M={M} N={N} x={xdt} g={gdt} misalign={misalign} alias={alias} "
+         f"gpu_stats={gpu_stats} dbeta={dbeta} shift={shift}")
+    x, g, _, dy = _inputs(M, N, xdt, gdt, seed, with_dy=True)
+    if shift:
+        x = O.round_to(O.decode(x, xdt).reshape(M, N) + shift, xdt)
+    xt, gt, dyt = _put(x, xdt, misalign), _put(g, gdt), _put(dy, xdt, misalign)
+    if gpu_stats:
+        mt, rt = torch.empty(M, device="cuda"), torch.empty(M, device="cuda")
+        assert R.layernorm_fwd(xt, gt, None, _empty(M * N, xdt), mt, rt, M, N, 1e-5, xdt, gdt,
+                               _stream()) == 0
+        torch.cuda.synchronize()
+        mean, rstd = to_host(mt), to_host(rt)
+    else:
+        f = O.layernorm_fwd(x, g, None, M, N, 1e-5, xdt, gdt, want_exact=False)
+        mean, rstd = f["mean"], f["rstd"]
+        mt, rt = torch.from_numpy(mean.copy()).cuda(), torch.from_numpy(rstd.copy()).cuda()
+    ref = O.layernorm_bwd(dy, x, mean, rstd, g, M, N, xdt, gdt)
+    dxt = {"dy": dyt, "x": xt}.get(alias) if alias else _empty(M * N, xdt, misalign)
+    dgt = torch.full((N,), float("nan"), device="cuda")
+    dbt = torch.full((N,), float("nan"), device="cuda") if dbeta else None
+    wsb = R.layernorm_bwd_workspace_size(M, N, xdt)
+    ws = torch.full((max(wsb, 16) // 4,), float("nan"), device="cuda")
+    st = R.layernorm_bwd(dyt, xt, mt, rt, gt, dxt, dgt, dbt, ws, wsb, M, N, xdt, gdt, _stream())
+    assert st == 0, R.rmsnorm_status_string(st)
+    torch.cuda.synchronize()
+    return check_layernorm_bwd(to_host(dxt), to_host(dgt), to_host(dbt) if dbeta else None, ref,
+                               x, dy, g, mean, rstd, xdt)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("N", [1, 7, 8, 64, 1000, 2047, 4096, 5000, 8192, 8193, 16384, 32768])
+def test_layernorm_bwd_sweep(N, pair):
+    run_ln_bwd(3, N, *pair, seed=2100 + N, dbeta=(N % 2 == 0))
+    run_ln_bwd(300, N, *pair, seed=2200 + N)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_layernorm_bwd_edges(pair):
+    run_ln_bwd(600, 20000, *pair, seed=2301)                 # two-pass tier, many rows
+    run_ln_bwd(5, 9000, *pair, seed=2302, misalign=1)        # scalar two-pass tier
+    run_ln_bwd(9, 4096, *pair, seed=2303, misalign=1)
+    run_ln_bwd(9, 4096, *pair, seed=2304, alias="dy")
+    run_ln_bwd(9, 20000, *pair, seed=2305, alias="x")
+    run_ln_bwd(257, 4096, *pair, seed=2306, shift=30.0)
+    run_ln_bwd(300, 8192, *pair, seed=2307, gpu_stats=True)
+
+
+def test_layernorm_bwd_bit_reproducible():
+    M, N = 2048, 8192
+    x, g, _, dy = _inputs(M, N, O.BF16, O.BF16, 2401, with_dy=True)
+    f = O.layernorm_fwd(x, g, None, M, N, 1e-5, O.BF16, O.BF16, want_exact=False)
+    xt, gt, dyt = _put(x, O.BF16), _put(g, O.BF16), _put(dy, O.BF16)
+    mt, rt = torch.from_numpy(f["mean"]).cuda(), torch.from_numpy(f["rstd"]).cuda()
+    wsb = R.layernorm_bwd_workspace_size(M, N, O.BF16)
+    outs = []
+    for k in range(3):
+        dxt, dgt, dbt = _empty(M * N, O.BF16), torch.empty(N, device="cuda"), torch.empty(N, device="cuda")
+        ws = torch.full((wsb // 4,), float(k), device="cuda")
+        assert R.layernorm_bwd(dyt, xt, mt, rt, gt, dxt, dgt, dbt, ws, wsb, M, N, O.BF16, O.BF16,
+                               _stream()) == 0
+        torch.cuda.synchronize()
+        outs.append([to_host(t) for t in (dxt, dgt, dbt)])
+    for o in outs[1:]:
+        for a_, b_ in zip(o, outs[0]):
+            assert np.array_equal(a_.view(np.uint8), b_.view(np.uint8))
+
+
 # ----------------------------------------------------------------- backward
 
 def run_bwd(M, N, xdt, gdt, seed=13, misalign=0, alias=None, gpu_rstd=False, eps=1e-5):
@@ -703,6 +772,8 @@ def test_workload_full_size(w):
         run_fused_bwd(w.M, w.N, w.x_dt, w.g_dt, seed=w.seed)
     elif w.kind == "ln":
         run_ln(w.M, w.N, w.x_dt, w.g_dt, seed=w.seed, eps=w.eps)
+    elif w.kind == "ln_bwd":
+        run_ln_bwd(w.M, w.N, w.x_dt, w.g_dt, seed=w.seed)
     elif w.kind == "qk":
         run_qk(w.M, w.heads_q, w.heads_k, w.N, w.x_dt, w.g_dt, seed=w.seed, eps=w.eps)
     elif w.kind == "quant":
