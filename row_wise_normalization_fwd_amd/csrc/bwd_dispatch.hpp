@@ -100,21 +100,26 @@ hipError_t long_rows_typed(const BwdArgs<T, G>& a, double* cdot, int64_t blocks,
   return hipGetLastError();
 }
 
-// Stage 2 over one partial array. Partial rows are 16-byte aligned when
-// N % 4 == 0 (the workspace and partial_bytes are).
-inline hipError_t run_stage2(const float* partial, float* out, const BwdCall& c) {
+// Stage 2 over one partial array, or two in one launch (partial2 / out2 not
+// null). Partial rows are 16-byte aligned when N % 4 == 0 (the workspace and
+// partial_bytes are).
+inline hipError_t run_stage2(const float* partial, float* out, const float* partial2,
+                             float* out2, const BwdCall& c) {
   constexpr int kSlices = 16;
   constexpr int kGroups = kS2Threads / kSlices;
+  const unsigned ny = out2 != nullptr ? 2u : 1u;
   if (c.N % 4 == 0) {
     const int64_t blocks = ceil_div(c.N, 4 * kGroups);
     bwd_stage2_kernel<4, kSlices>
-        <<<dim3(static_cast<unsigned>(blocks)), dim3(kS2Threads), 0, c.stream>>>(
-            partial, out, static_cast<int>(c.plan.blocks), static_cast<int>(c.N));
+        <<<dim3(static_cast<unsigned>(blocks), ny), dim3(kS2Threads), 0, c.stream>>>(
+            partial, out, partial2, out2, static_cast<int>(c.plan.blocks),
+            static_cast<int>(c.N));
   } else {
     const int64_t blocks = ceil_div(c.N, kGroups);
     bwd_stage2_kernel<1, kSlices>
-        <<<dim3(static_cast<unsigned>(blocks)), dim3(kS2Threads), 0, c.stream>>>(
-            partial, out, static_cast<int>(c.plan.blocks), static_cast<int>(c.N));
+        <<<dim3(static_cast<unsigned>(blocks), ny), dim3(kS2Threads), 0, c.stream>>>(
+            partial, out, partial2, out2, static_cast<int>(c.plan.blocks),
+            static_cast<int>(c.N));
   }
   return hipGetLastError();
 }
@@ -148,10 +153,8 @@ hipError_t bwd_typed(const BwdCall& c) {
                 : long_rows_typed<T, G, RES, LN, false>(a, cdot, c.plan.blocks, c.stream);
   }
   if (e != hipSuccess) return e;
-  e = run_stage2(a.partial, c.dgamma, c);
-  if (e != hipSuccess) return e;
-  if (LN && c.dbeta != nullptr) e = run_stage2(a.partial_b, c.dbeta, c);
-  return e;
+  if (LN && c.dbeta != nullptr) return run_stage2(a.partial, c.dgamma, a.partial_b, c.dbeta, c);
+  return run_stage2(a.partial, c.dgamma, nullptr, nullptr, c);
 }
 
 }  // namespace rmsn

@@ -473,7 +473,9 @@ __global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const 
   }
 }
 
-// Stage 2: dgamma_j = sum over blocks b of partial[b][j], in a fixed order.
+// Stage 2: dgamma_j = sum over blocks b of partial[b][j], in a fixed order
+// (gridDim.y == 2: the second row of blocks does the same for partial2 into
+// out2, LayerNorm's dbeta, in the same launch).
 // A 256-thread block covers 256 / SLICES column groups of CPT adjacent columns
 // (one 16-byte load per partial row when CPT == 4); each thread owns one
 // group and one of SLICES interleaved slices of partial rows (b = slice,
@@ -483,9 +485,12 @@ constexpr int kS2Threads = 256;
 
 template <int CPT, int SLICES>
 __global__ __launch_bounds__(kS2Threads) void bwd_stage2_kernel(
-    const float* __restrict__ partial, float* __restrict__ dgamma, int nblocks, int N) {
+    const float* __restrict__ partial0, float* __restrict__ out0,
+    const float* __restrict__ partial2, float* __restrict__ out2, int nblocks, int N) {
   constexpr int kGroups = kS2Threads / SLICES;  // column groups per block
   __shared__ double red[SLICES][kGroups][CPT];
+  const float* __restrict__ partial = blockIdx.y == 0 ? partial0 : partial2;
+  float* __restrict__ dgamma = blockIdx.y == 0 ? out0 : out2;
   const int grp = threadIdx.x % kGroups;
   const int slice = threadIdx.x / kGroups;
   const int col0 = (blockIdx.x * kGroups + grp) * CPT;
