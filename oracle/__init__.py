@@ -7,8 +7,9 @@ never does. The arithmetic lives in ``oracle.cpp`` (which cites the passages it
 follows); this module only marshals numpy arrays.
 
 Storage arrays are numpy ``float32`` for fp32 data, ``uint16`` bit patterns
-for fp16 / bf16 data and ``uint8`` codes for fp8 e4m3 (OCP "fn"). Type codes:
-0 = fp32, 1 = fp16, 2 = bf16, 4 = fp8 e4m3; 3 = plain float64 storage, used by
+for fp16 / bf16 data and ``uint8`` codes for fp8 e4m3 (OCP "fn"), fp4 e2m1 (one code per byte, low
+nibble) and E8M0 scales. Type codes: 0 = fp32, 1 = fp16, 2 = bf16, 4 = fp8
+e4m3, 5 = fp4 e2m1, 6 = E8M0 (decode only); 3 = plain float64 storage, used by
 the oracle's own checks (finite differences need unrounded inputs).
 """
 
@@ -20,7 +21,7 @@ import subprocess
 
 import numpy as np
 
-F32, F16, BF16, F64, E4M3 = 0, 1, 2, 3, 4
+F32, F16, BF16, F64, E4M3, E2M1, E8M0 = 0, 1, 2, 3, 4, 5, 6
 QUANT_TENSOR, QUANT_ROW = 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +69,9 @@ def _load():
                                          vp, vp, dp]
     lib.oracle_layernorm_bwd.argtypes = [vp, vp, dp, dp, vp, i64, i64, i32, i32, dp, vp, dp, dp,
                                          dp, dp, dp, dp, dp, dp]
+    lib.oracle_rmsnorm_mx_fwd.argtypes = [vp, vp, vp, i64, i64, f32, i32, i32, i32, vp, vp, dp, vp,
+                                          dp]
+    lib.oracle_rmsnorm_mx_fwd.restype = None
     for fn in (lib.oracle_decode, lib.oracle_round, lib.oracle_rmsnorm_fwd,
                lib.oracle_rmsnorm_fused_add_fwd, lib.oracle_rmsnorm_bwd,
                lib.oracle_rmsnorm_fused_add_bwd, lib.oracle_rmsnorm_quant_fwd,
@@ -79,7 +83,8 @@ def _load():
 
 
 def storage_dtype(dt: int):
-    return {F32: np.float32, F64: np.float64, E4M3: np.uint8}.get(dt, np.uint16)
+    return {F32: np.float32, F64: np.float64, E4M3: np.uint8, E2M1: np.uint8,
+            E8M0: np.uint8}.get(dt, np.uint16)
 
 
 def _ptr(a):
@@ -274,4 +279,26 @@ def layernorm_bwd(dy, x, mean, rstd, gamma, M, N, x_dt, g_dt, want_exact=True):
                                  _ptr(out["dgamma"]), _ptr(out["dbeta"]), _ptr(out["c1"]),
                                  _ptr(out["c2"]), _ptr(out["a1"]), _ptr(out["a2"]),
                                  _ptr(out["sg"]), _ptr(out["sb"]))
+    return out
+
+
+def rmsnorm_mx_fwd(x, gamma, M, N, eps, x_dt, g_dt, elem, r=None, want_exact=True):
+    """Forward with an MX block-scaled output (elem E4M3 or E2M1; N % 32 == 0).
+    Returns dict: q (M,N) element codes (one per byte), q_exact (M,N) f64 y/X
+    or None, scale (M,N/32) E8M0 codes, amax (M,N/32) f64, h (fused) or None."""
+    if N % 32:
+        raise ValueError("N must be a multiple of 32")
+    if elem not in (E4M3, E2M1):
+        raise ValueError("elem must be E4M3 or E2M1")
+    x = _check(x, x_dt, M * N, "x")
+    gamma = _check(gamma, g_dt, N, "gamma")
+    if r is not None:
+        r = _check(r, x_dt, M * N, "r")
+    out = {"q": np.empty((M, N), np.uint8),
+           "q_exact": np.empty((M, N), np.float64) if want_exact else None,
+           "scale": np.empty((M, N // 32), np.uint8), "amax": np.empty((M, N // 32), np.float64),
+           "h": np.empty((M, N), storage_dtype(x_dt)) if r is not None else None}
+    _load().oracle_rmsnorm_mx_fwd(_ptr(x), _ptr(r), _ptr(gamma), M, N, eps, x_dt, g_dt, elem,
+                                  _ptr(out["h"]), _ptr(out["q"]), _ptr(out["q_exact"]),
+                                  _ptr(out["scale"]), _ptr(out["amax"]))
     return out

@@ -39,6 +39,18 @@
 //       c2 = (1/N) sum_j gamma dy xhat,
 //       dx = rstd (gamma dy - c1 - xhat c2),
 //       dgamma_j = sum_i dy xhat,  dbeta_j = sum_i dy.
+//   * MX block-scaled output (the "TIRx kernels" page lists fp4-quantised
+//     norms, flashinfer_rmsnorm_fp4quant and add_rmsnorm_fp4quant, by name;
+//     the FlyDSL guide, section 3a, uses per-32 E8M0 scales with fp4/fp8
+//     elements on gfx950). Reading taken, after the OCP Microscaling (MX)
+//     format definition: each row is cut into blocks of 32 consecutive
+//     elements; a block's shared scale is X = 2^(floor(log2(amax)) - emax),
+//     amax = max |y| over the block and emax the exponent of the element
+//     format's largest normal (e2m1: 2, since 6 = 1.5 * 2^2; e4m3: 8, since
+//     448 = 1.75 * 2^8), stored as the E8M0 code floor(log2 amax) - emax + 127
+//     clamped to [0, 254]; every element is y / X rounded to the element
+//     format (nearest, ties to even, saturated at its largest value). A zero
+//     block gets code 0 and zero elements.
 //   * Per-head QK-RMSNorm ("TIRx kernels", FlashInfer ports, flashinfer.norm:
 //     qk_rmsnorm, named without a definition). Reading taken: q holds
 //     [tokens, q_heads, head_dim] and k [tokens, k_heads, head_dim], each head
@@ -72,6 +84,8 @@ constexpr int kF16 = 1;
 constexpr int kBF16 = 2;
 constexpr int kF64 = 3;  // plain double storage, used only by the oracle's own checks
 constexpr int kE4M3 = 4; // fp8 e4m3, OCP "fn" encoding (bias 7, no infinity, 448 max)
+constexpr int kE2M1 = 5; // fp4 e2m1 (bias 1, no infinity or NaN, 6 max), one code per byte
+constexpr int kE8M0 = 6; // MX scale: 2^(code - 127), 255 = NaN; decode only
 
 struct Format {
   int frac_bits;      // stored fraction bits
@@ -84,6 +98,7 @@ Format format_of(int dt) {
     case kF32:  return {23, -126, std::ldexp(2.0 - std::ldexp(1.0, -23), 127)};
     case kF16:  return {10, -14, 65504.0};
     case kE4M3: return {3, -6, 448.0};
+    case kE2M1: return {1, 0, 6.0};
     default:    return {7, -126, std::ldexp(2.0 - std::ldexp(1.0, -7), 127)};
   }
 }
@@ -99,6 +114,17 @@ double decode(const void* base, int64_t idx, int dt) {
     float f;
     std::memcpy(&f, static_cast<const char*>(base) + 4 * idx, 4);
     return f;
+  }
+  if (dt == kE8M0) {
+    uint8_t b = static_cast<const uint8_t*>(base)[idx];
+    return b == 255 ? NAN : std::ldexp(1.0, static_cast<int>(b) - 127);
+  }
+  if (dt == kE2M1) {
+    // 1 sign, 2 exponent (bias 1), 1 fraction bit, in the low nibble.
+    uint8_t b = static_cast<const uint8_t*>(base)[idx] & 0xf;
+    int sign = b >> 3, e = (b >> 1) & 0x3, m = b & 0x1;
+    double v = e == 0 ? 0.5 * m : std::ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -v : v;
   }
   if (dt == kE4M3) {
     // 1 sign, 4 exponent (bias 7), 3 fraction bits; exponent 15 with fraction
@@ -132,6 +158,7 @@ double decode(const void* base, int64_t idx, int dt) {
 // Round v to the nearest value of format dt, ties to even; overflow gives inf.
 double round_to(double v, int dt) {
   if (dt == kE4M3 && std::isinf(v)) return std::copysign(448.0, v);  // saturates too
+  if (dt == kE2M1 && std::isinf(v)) return std::copysign(6.0, v);
   if (dt == kF64 || v == 0.0 || !std::isfinite(v)) return v;
   Format f = format_of(dt);
   int e;
@@ -141,7 +168,8 @@ double round_to(double v, int dt) {
   double quantum = std::ldexp(1.0, lead - f.frac_bits);
   double r = std::nearbyint(v / quantum) * quantum;  // default mode: ties to even
   if (std::fabs(r) > f.max_finite)  // e4m3fn has no infinity: saturate
-    r = dt == kE4M3 ? std::copysign(f.max_finite, v) : std::copysign(INFINITY, v);
+    r = (dt == kE4M3 || dt == kE2M1) ? std::copysign(f.max_finite, v)
+                                     : std::copysign(INFINITY, v);
   return r;
 }
 
@@ -152,6 +180,16 @@ uint32_t encode(double r, int dt) {
     uint32_t u;
     std::memcpy(&u, &f, 4);
     return dt == kF32 ? u : (u >> 16);
+  }
+  if (dt == kE2M1) {
+    uint32_t sign = std::signbit(r) ? 0x8u : 0u;
+    double a = std::fabs(r);
+    if (a < 1.0) return sign | static_cast<uint32_t>(a * 2.0);  // 0 or 0.5
+    int e;
+    std::frexp(a, &e);
+    int lead = e - 1;                                            // 0, 1 or 2
+    uint32_t frac = static_cast<uint32_t>(std::ldexp(a, 1 - lead)) - 2u;
+    return sign | (static_cast<uint32_t>(lead + 1) << 1) | frac;
   }
   if (dt == kE4M3) {
     uint32_t sign = std::signbit(r) ? 0x80u : 0u;
@@ -182,7 +220,7 @@ void store_bits(void* base, int64_t idx, uint32_t bits, int dt) {
   if (dt == kF64) return;  // doubles are stored by store_value
   if (dt == kF32) {
     std::memcpy(static_cast<char*>(base) + 4 * idx, &bits, 4);
-  } else if (dt == kE4M3) {
+  } else if (dt == kE4M3 || dt == kE2M1) {
     static_cast<uint8_t*>(base)[idx] = static_cast<uint8_t>(bits);
   } else {
     uint16_t b = static_cast<uint16_t>(bits);
@@ -464,6 +502,50 @@ void oracle_layernorm_bwd(const void* dy, const void* x, const double* mean,
       if (dbeta) dbeta[j] += dyv;
       if (sg) sg[j] += std::fabs(dyv * xhat);
       if (sb) sb[j] += std::fabs(dyv);
+    }
+  }
+}
+
+// RMSNorm forward (after the fused add when r is not null) with an MX
+// block-scaled output: elem = kE4M3 (MXFP8) or kE2M1 (MXFP4); N must be a
+// multiple of 32. Outputs, each optional: h_bits[M*N] (fused), q[M*N] element
+// codes, one per byte (fp4 in the low nibble), q_exact[M*N] the value y / X
+// before rounding, scale[M*N/32] E8M0 codes, amax[M*N/32] each block's max |y|.
+void oracle_rmsnorm_mx_fwd(const void* x, const void* r, const void* gamma, int64_t M, int64_t N,
+                           float eps, int x_dt, int g_dt, int elem, void* h_bits, uint8_t* q,
+                           double* q_exact, uint8_t* scale, double* amax_out) {
+  const int emax = elem == kE2M1 ? 2 : 8;
+  const int64_t nb = N / 32;
+  std::vector<double> v(static_cast<size_t>(N)), y(static_cast<size_t>(N));
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t j = 0; j < N; ++j) {
+      double xv = decode(x, i * N + j, x_dt);
+      if (r) {
+        xv = round_to(xv + decode(r, i * N + j, x_dt), x_dt);
+        if (h_bits) store_value(h_bits, i * N + j, xv, x_dt);
+      }
+      v[j] = xv;
+    }
+    float rs;
+    forward_row(v.data(), gamma, N, eps, x_dt, g_dt, 0, y.data(), nullptr, nullptr, &rs, nullptr);
+    for (int64_t blk = 0; blk < nb; ++blk) {
+      double amax = 0.0;
+      for (int j = 0; j < 32; ++j) amax = std::fmax(amax, std::fabs(y[blk * 32 + j]));
+      int code = 0;
+      if (amax > 0.0) {
+        int e;
+        std::frexp(amax, &e);            // amax = m 2^e, m in [0.5, 1): floor(log2) = e - 1
+        code = (e - 1) - emax + 127;
+        code = code < 0 ? 0 : (code > 254 ? 254 : code);
+      }
+      if (scale) scale[i * nb + blk] = static_cast<uint8_t>(code);
+      if (amax_out) amax_out[i * nb + blk] = amax;
+      for (int j = 0; j < 32; ++j) {
+        const int64_t k = i * N + blk * 32 + j;
+        const double t = amax > 0.0 ? std::ldexp(y[blk * 32 + j], 127 - code) : 0.0;
+        if (q_exact) q_exact[k] = t;
+        if (q) store_value(q, k, t, elem);
+      }
     }
   }
 }

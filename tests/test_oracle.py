@@ -629,3 +629,90 @@ def test_layernorm_backward_invariants(gen_mod):
     assert np.all(np.abs((dx * xc).sum(axis=1)) <= 1e-12 * (np.abs(dx * xc).sum(axis=1)))
     np.testing.assert_allclose(out["dbeta"], O.decode(dy, O.BF16).reshape(M, N).sum(axis=0),
                                rtol=1e-15)
+
+
+# ------------------------------------------------- MX block-scaled output
+
+# e2m1 magnitudes by code (sign bit 3): exponent field 0 is subnormal (0, 0.5),
+# then 1, 1.5, 2, 3, 4, 6 (bias 1, one fraction bit).
+E2M1_VALUES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_decode_and_rounding_table():
+    codes = np.arange(16, dtype=np.uint8)
+    want = np.array(E2M1_VALUES + [-v for v in E2M1_VALUES])
+    got = O.decode(codes, O.E2M1)
+    assert np.array_equal(got, want) and np.signbit(got[8])
+    # Every value round-trips; every midpoint goes to the even code; quarter
+    # points go to the nearer value; beyond 6 saturates.
+    vals = np.array(E2M1_VALUES)
+    assert np.array_equal(O.round_to(vals, O.E2M1), np.arange(8))
+    mids = (vals[:-1] + vals[1:]) / 2           # 0.25 .. 5: ties
+    assert O.round_to(mids, O.E2M1).tolist() == [0, 2, 2, 4, 4, 6, 6]
+    q1 = vals[:-1] + (vals[1:] - vals[:-1]) / 4
+    q3 = vals[:-1] + 3 * (vals[1:] - vals[:-1]) / 4
+    assert O.round_to(q1, O.E2M1).tolist() == list(range(7))
+    assert O.round_to(q3, O.E2M1).tolist() == list(range(1, 8))
+    assert O.round_to(np.array([6.5, 7.0, 1e9, np.inf]), O.E2M1).tolist() == [7, 7, 7, 7]
+    assert O.round_to(np.array([-0.75, -7.0]), O.E2M1).tolist() == [10, 15]
+
+
+def test_e8m0_decode_matches_torch():
+    codes = np.arange(255, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e8m0fnu).float().numpy().astype(np.float64)
+    got = O.decode(codes, O.E8M0)
+    assert np.array_equal(got[1:], want[1:])        # code 0 is 2^-127 (fp32 keeps it)
+    assert got[0] == 2.0 ** -127 and np.isnan(O.decode(np.array([255], np.uint8), O.E8M0)[0])
+
+
+@pytest.mark.parametrize("elem,emax,top", [(O.E4M3, 8, 448.0), (O.E2M1, 2, 6.0)])
+def test_mx_block_scale_and_reconstruction(elem, emax, top, gen_mod):
+    M, N = 12, 256
+    x = gen_mod.normal(61, 1, M, N, O.BF16, 1e-3, 5)       # rows 0, 5, 10 scaled down
+    g = gen_mod.uniform(61, 4, N, -1.5, 1.5, O.BF16)
+    xs = O.decode(x, O.BF16).reshape(M, N)
+    xs[4, 64:96] = 0.0                                      # one all-zero block
+    x = O.round_to(xs, O.BF16)
+    out = O.rmsnorm_mx_fwd(x, g, M, N, 1e-5, O.BF16, O.BF16, elem)
+    y = O.rmsnorm_fwd(x, g, M, N, 1e-5, O.BF16, O.BF16)["y_exact"]
+    yb = y.reshape(M, N // 32, 32)
+    amax = np.abs(yb).max(axis=2)
+    assert np.array_equal(out["amax"], amax)
+    X = O.decode(out["scale"], O.E8M0).reshape(M, N // 32)
+    nz = amax > 0
+    # The scale is the power of two that puts the block max in [2^emax, 2^(emax+1)).
+    r = amax[nz] / X[nz]
+    assert np.all((r >= 2.0 ** emax) & (r < 2.0 ** (emax + 1)))
+    assert np.all(out["scale"][~nz] == 0) and np.all(out["q"].reshape(M, N // 32, 32)[~nz] & 0x7f == 0)
+    # Elements: nearest representable value of y / X (or the saturated top).
+    t = yb / X[:, :, None]
+    deq = O.decode(out["q"], elem).reshape(M, N // 32, 32)
+    sat = np.abs(t) > top
+    assert np.all(np.abs(deq[sat]) == top) and np.all(np.sign(deq[sat]) == np.sign(t[sat]))
+    lead = np.floor(np.log2(np.maximum(np.abs(t), 1e-300)))
+    frac_bits, min_exp = (3, -6) if elem == O.E4M3 else (1, 0)
+    step = np.exp2(np.maximum(lead, min_exp) - frac_bits)
+    assert np.all(np.abs(deq - t)[~sat] <= step[~sat] / 2 + 1e-12)
+    np.testing.assert_allclose(out["q_exact"].reshape(M, N // 32, 32), t, rtol=1e-15, atol=0)
+
+
+def test_mx_fused_and_worked_block():
+    # One hand-worked block: gamma 1, eps 0, a row of 32 values whose RMS is
+    # known exactly: x = [4, 4, ..., 4 (16 times), -2 (16 times)] -> ms = 10,
+    # y = x / sqrt(10). amax = 4 / sqrt(10) = 1.2649.. -> floor(log2) = 0.
+    N = 32
+    x = O.round_to(np.array([[4.0] * 16 + [-2.0] * 16]), O.BF16)
+    g = O.round_to(np.ones(N), O.BF16)
+    out4 = O.rmsnorm_mx_fwd(x, g, 1, N, 0.0, O.BF16, O.BF16, O.E2M1)
+    assert out4["scale"][0, 0] == 127 - 2            # X = 2^(0 - 2) = 0.25
+    # 1.2649 / 0.25 = 5.06 -> 6;  0.6325 / 0.25 = 2.53 -> 3 (negative: code 8 + 5)
+    assert out4["q"][0].tolist() == [7] * 16 + [13] * 16
+    out8 = O.rmsnorm_mx_fwd(x, g, 1, N, 0.0, O.BF16, O.BF16, O.E4M3)
+    assert out8["scale"][0, 0] == 127 - 8            # X = 2^-8
+    # 1.2649 * 256 = 323.8 -> 320 (step 32 above 256); 0.6325 * 256 = 161.9 -> 160
+    assert np.array_equal(O.decode(out8["q"][0], O.E4M3), np.array([320.0] * 16 + [-160.0] * 16))
+    # The fused variant quantises the forward of the rounded sum.
+    xr = O.round_to(np.array([[1.0] * 32]), O.BF16)
+    fused = O.rmsnorm_mx_fwd(xr, g, 1, N, 0.0, O.BF16, O.BF16, O.E2M1, r=O.round_to(
+        O.decode(x, O.BF16).reshape(1, N) - 1.0, O.BF16))
+    assert np.array_equal(fused["h"], x) and np.array_equal(fused["q"], out4["q"])
