@@ -22,7 +22,8 @@ Also reported, in the same JSON line:
   workloads     the other four workloads (fp32 short rows, fused residual add,
                 backward, fp16 ragged rows) and the fused-add backward, timed
                 the same way, the fp8-output forward (per-row scales at the
-                headline shape; one scale after the fused add), the per-head
+                headline shape; one scale after the fused add), MXFP8 and
+                MXFP4 outputs at the headline shape, the per-head
                 QK-norm on a fused q/k/v buffer, LayerNorm at the headline
                 shape and the LayerNorm backward at the backward's shape;
   calibration   a plain device-to-device copy of the step's byte count.
@@ -53,6 +54,8 @@ DOMINANT_KERNEL = {
     "fusedadd_bwd_bf16_m8192_n8192": "bwd_stage1_kernel",
     "fwd_fp8row_bf16_m4096_n8192": "fwd_pp_kernel",
     "fusedadd_fp8tensor_bf16_m16384_n4096_gf32": "fwd_reg_kernel",
+    "fwd_mxfp8_bf16_m4096_n8192": "fwd_pp_kernel",
+    "fwd_mxfp4_bf16_m4096_n8192": "fwd_pp_kernel",
     "qknorm_bf16_t16384_hq32_hk8_d128": "qk_norm_kernel",
     "layernorm_bf16_m4096_n8192": "fwd_pp_kernel",
     "layernorm_bwd_bf16_m8192_n8192": "bwd_stage1_kernel",
@@ -99,7 +102,7 @@ class Runner:
         big = M * N * w.esize
         per_replica = {"fwd": 2 * big, "fused_add": 3 * big, "bwd": 3 * big,
                        "fused_add_bwd": 4 * big,
-                       "quant": (2 if w.fused_quant else 1) * big + M * N,
+                       "quant": (2 if w.fused_quant else 1) * big + M * N,  # q <= M N bytes
                        "qk": M * (w.heads_q + 2 * w.heads_k) * N * w.esize,
                        "ln": 2 * big, "ln_bwd": 3 * big}[w.kind]
         self.replicas = max(1, int(-(-rotate_bytes // per_replica))) if rotate_bytes > 0 else 1
@@ -154,9 +157,14 @@ class Runner:
                 s["rstd"] = torch.empty(M, dtype=torch.float32, device=dev)
             elif w.kind == "quant":
                 s["r"] = (r0 if i == 0 else r0.clone()) if w.fused_quant else None
-                s["q"] = torch.empty(M * N, dtype=torch.uint8, device=dev)
-                s["scale"] = (self.tensor_scale if w.quant_mode == 1 else
-                              torch.empty(M, dtype=torch.float32, device=dev))
+                s["q"] = torch.empty(M * N // 2 if w.quant_mode == 4 else M * N,
+                                     dtype=torch.uint8, device=dev)
+                if w.quant_mode == 1:
+                    s["scale"] = self.tensor_scale
+                elif w.quant_mode == 2:
+                    s["scale"] = torch.empty(M, dtype=torch.float32, device=dev)
+                else:  # MX: E8M0 codes per 32 elements
+                    s["scale"] = torch.empty(M * N // 32, dtype=torch.uint8, device=dev)
                 s["rstd"] = torch.empty(M, dtype=torch.float32, device=dev) if w.store_rstd else None
             else:
                 s["dy"] = dy0 if i == 0 else dy0.clone()
@@ -286,6 +294,11 @@ def cpu_baseline(w, host_inputs: dict, seconds: float) -> dict:
                                          w.g_dt)
             O.rmsnorm_heads_fwd(buf, host_inputs["gamma_k"], M, w.heads_k, N, S, w.eps, w.x_dt,
                                 w.g_dt, offset=w.heads_q * N)
+    elif w.kind == "quant" and w.quant_mode >= 3:
+        def one_pass():
+            O.rmsnorm_mx_fwd(x, g, M, N, w.eps, w.x_dt, w.g_dt,
+                             O.E4M3 if w.quant_mode == 3 else O.E2M1, r=host_inputs.get("r"),
+                             want_exact=False)
     elif w.kind == "quant":
         def one_pass():
             O.rmsnorm_quant_fwd(x, g, M, N, w.eps, w.x_dt, w.g_dt, w.quant_mode,

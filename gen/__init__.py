@@ -119,7 +119,8 @@ class Workload:
     store_rstd: bool = False
     outlier_every: int = 0      # rows i with i % outlier_every == 0 are scaled
     outlier_scale: float = 1.0
-    quant_mode: int = 0         # "quant": 1 = one tensor scale, 2 = per-row scales
+    quant_mode: int = 0         # "quant": 1 = one tensor scale, 2 = per-row scales,
+                                #   3 = MXFP8, 4 = MXFP4 (E8M0 per 32 elements)
     fused_quant: bool = False   # "quant": fused residual add first
     tensor_scale: float = 0.0125  # "quant", one tensor scale: |y| > 5.6 saturates
     heads_q: int = 0            # "qk": M tokens of heads_q + heads_k vectors of N = head_dim,
@@ -154,8 +155,11 @@ class Workload:
             # read x (and r, writing h), write the fp8 codes (1 byte each),
             # per-row scales (read one scale per tensor).
             n = self.M * self.N
-            extra = 4 * self.M if self.quant_mode == 2 else 4
-            io = big + (2 * big if self.fused_quant else 0) + n
+            # q: one byte per element, half for MXFP4; scales: per tensor 4 B
+            # read, per row 4 B, MX one E8M0 byte per 32 elements
+            qbytes = n // 2 if self.quant_mode == 4 else n
+            extra = {1: 4, 2: 4 * self.M}.get(self.quant_mode, n // 32)
+            io = big + (2 * big if self.fused_quant else 0) + qbytes
             return io + g + extra + (4 * self.M if self.store_rstd else 0)
         if self.kind == "fused_add_bwd":
             # read h, dy, dresidual, rstd, gamma; write dh, dgamma (fp32)
@@ -187,6 +191,10 @@ EXTRA_WORKLOADS = [
              quant_mode=2),
     Workload("fusedadd_fp8tensor_bf16_m16384_n4096_gf32", "quant", 16384, 4096, BF16, F32, 1e-5,
              1008, quant_mode=1, fused_quant=True),
+    Workload("fwd_mxfp8_bf16_m4096_n8192", "quant", 4096, 8192, BF16, BF16, 1e-5, 1012,
+             quant_mode=3),
+    Workload("fwd_mxfp4_bf16_m4096_n8192", "quant", 4096, 8192, BF16, BF16, 1e-5, 1013,
+             quant_mode=4),
     Workload("qknorm_bf16_t16384_hq32_hk8_d128", "qk", 16384, 128, BF16, BF16, 1e-6, 1009,
              heads_q=32, heads_k=8),
     Workload("layernorm_bf16_m4096_n8192", "ln", 4096, 8192, BF16, BF16, 1e-5, 1010),

@@ -89,35 +89,51 @@ int rmsnorm_fused_add_fwd(const void* x, void* residual, const void* gamma, void
                           float* rstd, int64_t M, int64_t N, float eps, int x_dtype,
                           int gamma_dtype, hipStream_t stream);
 
-/* Scale modes of rmsnorm_quant_fwd. */
+/* Output modes of rmsnorm_quant_fwd. */
 typedef enum {
-  RMSN_QUANT_FP8_TENSOR = 1, /* one caller scale for the whole tensor, read */
-  RMSN_QUANT_FP8_ROW = 2     /* one scale per row, computed and written */
+  RMSN_QUANT_FP8_TENSOR = 1, /* fp8 e4m3, one caller scale for the whole tensor, read */
+  RMSN_QUANT_FP8_ROW = 2,    /* fp8 e4m3, one scale per row, computed and written */
+  RMSN_QUANT_MXFP8 = 3,      /* MX: e4m3 elements, E8M0 scale per 32 elements, written */
+  RMSN_QUANT_MXFP4 = 4       /* MX: e2m1 elements, E8M0 scale per 32 elements, written */
 } rmsn_quant_mode;
 
-/* Forward RMSNorm (optionally after the fused residual add) with an fp8
- * output: the RMSNorm value y (fp32, never rounded to the activation type)
- * is divided by a scale s and rounded to fp8 e4m3 in the OCP "fn" encoding
- * (1 sign, 4 exponent bits with bias 7, 3 fraction bits, no infinity; the
- * format the FlyDSL guide, section 3b, uses on gfx950), nearest-even, with
- * magnitudes beyond 448 saturated to +-448. The pages name these variants
- * ("TIRx kernels", FlashInfer ports, flashinfer.norm: rmsnorm_quant,
- * fused_add_rmsnorm_quant) without defining them; this is the reading taken.
+/* Forward RMSNorm (optionally after the fused residual add) with a
+ * quantised output. The pages name these variants ("TIRx kernels", FlashInfer
+ * ports, flashinfer.norm: rmsnorm_quant, fused_add_rmsnorm_quant,
+ * rmsnorm_fp4quant, add_rmsnorm_fp4quant) without defining them; the FlyDSL
+ * guide uses e4m3fn (OCP, not fnuz) on gfx950 (section 3b) and per-32 E8M0
+ * block scales with fp4 / fp8 elements (section 3a). Readings taken:
+ *   The RMSNorm value y (fp32, never rounded to the activation type) is
+ *   divided by a scale s and rounded to the element format, nearest-even,
+ *   saturated at its largest value: fp8 e4m3 "fn" (1 sign, 4 exponent bits,
+ *   bias 7, 3 fraction bits, no infinity, max 448) or fp4 e2m1 (1 sign, 2
+ *   exponent bits, bias 1, 1 fraction bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+ *   RMSN_QUANT_FP8_TENSOR: s = scale[0] (fp32, read on the device; positive
+ *     and finite).
+ *   RMSN_QUANT_FP8_ROW: s_i = amax_i / 448 with amax_i = max_j |y_ij|,
+ *     written to scale[i] (fp32, [M]); each row's largest element maps to
+ *     +-448; a zero row gets s = 0 and zero codes.
+ *   RMSN_QUANT_MXFP8 / RMSN_QUANT_MXFP4 (OCP Microscaling layout): each block
+ *     of 32 consecutive row elements has s = 2^(c - 127) with the E8M0 code
+ *     c = clamp(floor(log2 amax) - emax + 127, 0, 254), amax the block's
+ *     max |y| and emax 8 (e4m3) or 2 (e2m1); codes are written to scale
+ *     (uint8, [M, N / 32], row-major). A zero block gets c = 0 and zero
+ *     elements. N must be a multiple of 32 (else RMSN_ERR_SHAPE), and x,
+ *     residual and gamma 16-byte aligned, q aligned to 8 / 4 (MXFP8 with
+ *     16-bit / fp32 activations) or 4 / 2 (MXFP4) bytes (else RMSN_ERR_ALIGN).
  *   x, residual, gamma, rstd, eps as in rmsnorm_fwd / rmsnorm_fused_add_fwd;
  *             residual may be NULL (plain forward) or is read as r and
  *             overwritten with h = round(x + r), and h is normalised.
- *   q         [M, N] bytes of e4m3 codes, written; overlaps nothing else.
- *   scale     RMSN_QUANT_FP8_TENSOR: [1] fp32, read on the device: s, which
- *             must be positive and finite (q = e4m3(y / s)).
- *             RMSN_QUANT_FP8_ROW: [M] fp32, written with s_i = amax_i / 448,
- *             amax_i = max_j |y_ij|, so each row's largest element maps to
- *             +-448 (dequantise with q * s_i); a row with amax 0 gets s = 0 and
- *             zero codes. Rows holding inf or NaN give unspecified codes.
- * The kernel multiplies y by 1/s (per tensor) or 448/amax (per row) in fp32,
- * so a code may differ from the exactly rounded one by one step where y / s
- * lies within fp32 rounding of a tie. */
+ *   q         the element codes, written; overlaps nothing else. fp8 modes:
+ *             [M, N] bytes. MXFP4: [M, N / 2] bytes, element 2k in the low
+ *             nibble of byte k, element 2k + 1 in the high nibble.
+ * The kernel scales in fp32 (y / s as x * gamma * (rstd / s), or y * 2^(127 - c)
+ * exactly for MX), so a code may be one step from the exactly rounded one
+ * where y / s lies within fp32 rounding of a tie, and an MX block whose amax
+ * lies within fp32 rounding of a power of two may take the neighbouring code.
+ * Rows holding inf or NaN give unspecified codes. */
 int rmsnorm_quant_fwd(const void* x, void* residual, const void* gamma, void* q,
-                      float* scale, int quant_mode, float* rstd, int64_t M, int64_t N,
+                      void* scale, int quant_mode, float* rstd, int64_t M, int64_t N,
                       float eps, int x_dtype, int gamma_dtype, hipStream_t stream);
 
 /* Per-head RMSNorm of q and k, in place, in one launch (QK-norm; the

@@ -27,7 +27,7 @@ LIB_NAME = "librmsnorm_mi355x.so"
 LIB_PATH = os.path.join(_HERE, LIB_NAME)
 
 RMSN_F32, RMSN_F16, RMSN_BF16 = 0, 1, 2
-RMSN_QUANT_FP8_TENSOR, RMSN_QUANT_FP8_ROW = 1, 2
+RMSN_QUANT_FP8_TENSOR, RMSN_QUANT_FP8_ROW, RMSN_QUANT_MXFP8, RMSN_QUANT_MXFP4 = 1, 2, 3, 4
 RMSN_OK = 0
 STATUS_NAMES = {
     0: "RMSN_OK", -1: "RMSN_ERR_NULL", -2: "RMSN_ERR_SHAPE", -3: "RMSN_ERR_DTYPE",
@@ -301,6 +301,26 @@ def layernorm(x, gamma, beta=None, eps: float = 1e-5, *, want_stats: bool = Fals
     _check(layernorm_fwd(x, gamma, beta, y, mean, rstd, M, N, eps, dtype_code(x),
                          dtype_code(gamma), stream), "layernorm_fwd")
     return y, mean, rstd
+
+
+def mx_quant_fwd(x, gamma, eps: float = 1e-5, *, fp4: bool = False, residual=None,
+                 want_rstd: bool = False, stream=None):
+    """MX block-scaled output (N % 32 == 0): returns (q uint8 codes, E8M0 scale
+    codes [rows, N / 32] uint8, rstd or None); MXFP4 packs two codes per byte."""
+    import torch
+    N = gamma.numel()
+    M = _rows(x, N)
+    if residual is not None and (residual.shape != x.shape or residual.dtype != x.dtype):
+        raise ValueError("residual must match x in shape and dtype")
+    qshape = x.shape[:-1] + ((N // 2,) if fp4 else (N,))
+    q = torch.empty(qshape, dtype=torch.uint8, device=x.device)
+    scale = torch.empty(x.shape[:-1] + (N // 32,), dtype=torch.uint8, device=x.device)
+    rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device) if want_rstd else None
+    mode = RMSN_QUANT_MXFP4 if fp4 else RMSN_QUANT_MXFP8
+    stream = torch.cuda.current_stream(x.device) if stream is None else stream
+    _check(rmsnorm_quant_fwd(x, residual, gamma, q, scale, mode, rstd, M, N, eps, dtype_code(x),
+                             dtype_code(gamma), stream), "rmsnorm_quant_fwd")
+    return q, scale, rstd
 
 
 def bwd(dy, x, rstd, gamma, *, dx=None, dgamma=None, workspace=None, stream=None):

@@ -128,25 +128,37 @@ int ln_forward(const void* x, const void* gamma, const void* beta, void* y, floa
   }
 }
 
-// Validation of the quantised forward (fp8 output, optional fused add).
-int quant_forward(const void* x, void* residual, const void* gamma, void* q, float* scale,
+// Validation of the quantised forward (fp8 / MX output, optional fused add).
+int quant_forward(const void* x, void* residual, const void* gamma, void* q, void* scale,
                   int mode, float* rstd, int64_t M, int64_t N, float eps, int x_dtype,
                   int gamma_dtype, hipStream_t stream) {
   if (!valid_pair(x_dtype, gamma_dtype)) return RMSN_ERR_DTYPE;
   if (!shape_ok(M, N)) return RMSN_ERR_SHAPE;
   if (!std::isfinite(eps) || eps < 0.0f) return RMSN_ERR_EPS;
-  if (mode != RMSN_QUANT_FP8_TENSOR && mode != RMSN_QUANT_FP8_ROW) return RMSN_ERR_MODE;
+  if (mode < RMSN_QUANT_FP8_TENSOR || mode > RMSN_QUANT_MXFP4) return RMSN_ERR_MODE;
+  const bool mx = mode == RMSN_QUANT_MXFP8 || mode == RMSN_QUANT_MXFP4;
+  if (mx && N % 32 != 0) return RMSN_ERR_SHAPE;
   if (M == 0) return RMSN_OK;
   if (!x || !gamma || !q || !scale) return RMSN_ERR_NULL;
   const int es = esize_of(x_dtype), gs = esize_of(gamma_dtype);
-  if (!aligned(x, es) || !aligned(gamma, gs) || !aligned(scale, 4) ||
+  if (!aligned(x, es) || !aligned(gamma, gs) || (!mx && !aligned(scale, 4)) ||
       (rstd && !aligned(rstd, 4)) || (residual && !aligned(residual, es)))
     return RMSN_ERR_ALIGN;
-  const uint64_t big = static_cast<uint64_t>(M) * static_cast<uint64_t>(N) * es;
-  const bool per_row = mode == RMSN_QUANT_FP8_ROW;
+  if (mx) {
+    // MX outputs run on 16-byte units: rows, gamma and the residual 16-byte
+    // aligned, q aligned to one unit's output (E or E / 2 bytes).
+    const int unit_out = (16 / es) / (mode == RMSN_QUANT_MXFP4 ? 2 : 1);
+    if (!aligned(x, 16) || !aligned(gamma, 16) || (residual && !aligned(residual, 16)) ||
+        !aligned(q, unit_out))
+      return RMSN_ERR_ALIGN;
+  }
+  const uint64_t elems = static_cast<uint64_t>(M) * static_cast<uint64_t>(N);
+  const uint64_t big = elems * es;
+  const bool per_row = mode != RMSN_QUANT_FP8_TENSOR;  // scale written
   const Range rx = span(x, big), rg = span(gamma, static_cast<uint64_t>(N) * gs);
-  const Range rq = span(q, static_cast<uint64_t>(M) * static_cast<uint64_t>(N));
-  const Range rsc = span(scale, per_row ? static_cast<uint64_t>(M) * 4 : 4);
+  const Range rq = span(q, mode == RMSN_QUANT_MXFP4 ? elems / 2 : elems);
+  const uint64_t scale_bytes = mx ? elems / 32 : (per_row ? static_cast<uint64_t>(M) * 4 : 4);
+  const Range rsc = span(scale, scale_bytes);
   // q and the written buffers (residual, rstd, per-row scales) overlap nothing.
   if (overlap(rq, rx) || overlap(rq, rg) || overlap(rq, rsc)) return RMSN_ERR_OVERLAP;
   if (per_row && (overlap(rsc, rx) || overlap(rsc, rg))) return RMSN_ERR_OVERLAP;
@@ -161,8 +173,11 @@ int quant_forward(const void* x, void* residual, const void* gamma, void* q, flo
     if (partial_overlap(rs, rx) || overlap(rs, rg) || overlap(rs, rq) || overlap(rs, rsc))
       return RMSN_ERR_OVERLAP;
   }
-  rmsn::FwdCall c{x, residual, gamma, nullptr, rstd, M, N, eps, gamma_dtype, stream,
-                  q, scale, mode};
+  rmsn::FwdCall c{x, residual, gamma, nullptr, rstd, M, N, eps, gamma_dtype, stream};
+  c.q = q;
+  c.out = mode;
+  if (mx) c.mx = static_cast<uint8_t*>(scale);
+  else c.scale = static_cast<float*>(scale);
   switch (x_dtype) {
     case RMSN_F32: return finish(rmsn::launch_fwd_quant_f32(c));
     case RMSN_F16: return finish(rmsn::launch_fwd_quant_f16(c));
@@ -404,7 +419,7 @@ int rmsnorm_fused_add_fwd(const void* x, void* residual, const void* gamma, void
   return forward(true, x, residual, gamma, y, rstd, M, N, eps, x_dtype, gamma_dtype, stream);
 }
 
-int rmsnorm_quant_fwd(const void* x, void* residual, const void* gamma, void* q, float* scale,
+int rmsnorm_quant_fwd(const void* x, void* residual, const void* gamma, void* q, void* scale,
                       int quant_mode, float* rstd, int64_t M, int64_t N, float eps, int x_dtype,
                       int gamma_dtype, hipStream_t stream) {
   return quant_forward(x, residual, gamma, q, scale, quant_mode, rstd, M, N, eps, x_dtype,

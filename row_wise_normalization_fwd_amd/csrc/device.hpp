@@ -236,6 +236,67 @@ struct Fp8Unit<1> {
   __device__ static void store_nt(uint8_t* p, Raw v) { __builtin_nontemporal_store(v, p); }
 };
 
+// --------------------------------------------------------- MX block output
+//
+// MX outputs (OCP Microscaling layout): blocks of 32 consecutive row elements
+// share an E8M0 scale code c = clamp(floor(log2 amax) - emax + 127, 0, 254);
+// elements are y * 2^(127 - c) rounded to e4m3 (MXFP8) or e2m1 (MXFP4).
+constexpr int kOutMxFp8 = 3;
+constexpr int kOutMxFp4 = 4;
+
+// E8M0 code of a block whose largest |y| is amax >= 0: the fp32 exponent
+// field is floor(log2 amax) + 127 for normal amax (0 for zero or subnormal).
+__device__ __forceinline__ int mx_code(float amax, int emax) {
+  const int ef = static_cast<int>(__float_as_uint(amax) >> 23);
+  const int c = ef - emax;
+  return c < 0 ? 0 : c;
+}
+
+// e2m1 code of t, nearest-even, saturated at 6: the count of rounding
+// thresholds below |t| (ties at 0.25, 1.25, 2.5 and 5 go down to the even
+// code, those at 0.75, 1.75 and 3.5 up), plus the sign bit.
+__device__ __forceinline__ uint32_t fp4_code(float t) {
+  const float a = __builtin_fabsf(t);
+  const uint32_t c = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
+                     static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
+                     static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
+                     static_cast<uint32_t>(a > 5.0f);
+  return c | ((__float_as_uint(t) >> 28) & 0x8u);
+}
+
+// The fp4 image of one unit of E elements: E nibbles, element e in bits
+// [4e, 4e + 4). pack(p, k) encodes p[e] * k.
+template <int E>
+struct Fp4Unit;
+
+template <>
+struct Fp4Unit<8> {
+  using Raw = uint32_t;
+  __device__ static Raw pack(const float* o, float k) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w |= fp4_code(o[e] * k) << (4 * e);
+    return w;
+  }
+  __device__ static void store_nt(uint8_t* p, Raw v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<Raw*>(p));
+  }
+};
+
+template <>
+struct Fp4Unit<4> {
+  using Raw = uint16_t;
+  __device__ static Raw pack(const float* o, float k) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w |= fp4_code(o[e] * k) << (4 * e);
+    return static_cast<Raw>(w);
+  }
+  __device__ static void store_nt(uint8_t* p, Raw v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<Raw*>(p));
+  }
+};
+
 // --------------------------------------------------------------- reductions
 
 // A sum and a maximum reduced together (sum of squares and max |y| of a row):
@@ -320,6 +381,17 @@ __device__ __forceinline__ V group_sum(V v) {
   if constexpr (G == 64) {
     v = (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
   }
+  return v;
+}
+
+// Maximum over aligned groups of L lanes (L = 4 or 8); all 64 lanes of the
+// wave must take part.
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(L == 4 || L == 8, "group size");
+  v = __builtin_fmaxf(v, dpp<kQuadXor1>(v));
+  v = __builtin_fmaxf(v, dpp<kQuadXor2>(v));
+  if constexpr (L == 8) v = __builtin_fmaxf(v, dpp<kRowHalfMirror>(v));
   return v;
 }
 

@@ -82,14 +82,21 @@ hipError_t fwd_typed(const FwdCall& c) {
   a.scale = c.scale;
   a.beta = static_cast<const typename G::S*>(c.beta);
   a.mean = c.mean;
+  a.mx = c.mx;
   hipStream_t s = c.stream;
 
-  // fp8 output units are 16 / sizeof(T) bytes (8 or 4), stored with one
-  // instruction, so q must be aligned to that.
-  const bool out_ok = OUT == kOutAct ? aligned16(c.y) : aligned_to(c.q, 16 / T::kSize);
+  // fp8 output units are 16 / sizeof(T) bytes (8 or 4), fp4 half that, each
+  // stored with one instruction, so q must be aligned to that.
+  constexpr int kE = 16 / T::kSize;
+  const bool out_ok = OUT == kOutAct ? aligned16(c.y)
+                                     : aligned_to(c.q, OUT == kOutMxFp4 ? kE / 2 : kE);
   const bool vec = (c.N * T::kSize) % 16 == 0 && aligned16(c.x) && out_ok &&
                    aligned16(c.gamma) && (!FUSED || aligned16(c.residual)) &&
                    (!LN || c.beta == nullptr || aligned16(c.beta));
+  // MX outputs need the 16-byte unit path (the host checks the alignment).
+  if constexpr (kIsMx<OUT>) {
+    if (!vec) return hipErrorInvalidValue;
+  }
   if (c.N <= kRegMaxN) {
     if (vec) {
       constexpr int E = 16 / T::kSize;
@@ -108,8 +115,11 @@ hipError_t fwd_typed(const FwdCall& c) {
           else return run_fwd_pp<T, G, 256, 4, 256, FUSED, OUT, LN>(a, s);
         }
       }
-      const int64_t tpr2 = next_pow2(ceil_div(units, 2));
-      if (tpr2 >= 8 && 3 * units < 4 * tpr2 && units <= 3 * (tpr2 / 2)) {
+      // MX blocks span 32 / E lanes of one unit slot: at least that many lanes.
+      constexpr int64_t kMinTpr = kIsMx<OUT> ? 32 / E : 1;
+      int64_t tpr2 = next_pow2(ceil_div(units, 2));
+      if (tpr2 < kMinTpr) tpr2 = kMinTpr;
+      if (tpr2 / 2 >= kMinTpr && tpr2 >= 8 && 3 * units < 4 * tpr2 && units <= 3 * (tpr2 / 2)) {
         switch (tpr2 / 2) {  // 3 units on half the lanes
           case 4: return run_fwd_reg<T, G, true, 4, 3, 256, FUSED, OUT, LN>(a, s);
           case 8: return run_fwd_reg<T, G, true, 8, 3, 256, FUSED, OUT, LN>(a, s);
@@ -133,11 +143,13 @@ hipError_t fwd_typed(const FwdCall& c) {
         default: return run_fwd_reg<T, G, true, 512, 2, 512, FUSED, OUT, LN>(a, s);
       }
     }
-    const int64_t tpr = next_pow2(ceil_div(c.N, 8));
-    if (tpr <= 16) return run_fwd_reg<T, G, false, 16, 8, 256, FUSED, OUT, LN>(a, s);
-    if (tpr <= 64) return run_fwd_reg<T, G, false, 64, 8, 256, FUSED, OUT, LN>(a, s);
-    if (tpr <= 256) return run_fwd_reg<T, G, false, 256, 8, 256, FUSED, OUT, LN>(a, s);
-    return run_fwd_reg<T, G, false, 1024, 8, 1024, FUSED, OUT, LN>(a, s);
+    if constexpr (!kIsMx<OUT>) {
+      const int64_t tpr = next_pow2(ceil_div(c.N, 8));
+      if (tpr <= 16) return run_fwd_reg<T, G, false, 16, 8, 256, FUSED, OUT, LN>(a, s);
+      if (tpr <= 64) return run_fwd_reg<T, G, false, 64, 8, 256, FUSED, OUT, LN>(a, s);
+      if (tpr <= 256) return run_fwd_reg<T, G, false, 256, 8, 256, FUSED, OUT, LN>(a, s);
+      return run_fwd_reg<T, G, false, 1024, 8, 1024, FUSED, OUT, LN>(a, s);
+    }
   }
   const int64_t row_bytes = c.N * T::kSize;
   const bool cache = row_bytes <= lds_row_budget();
@@ -146,8 +158,11 @@ hipError_t fwd_typed(const FwdCall& c) {
     if (row_bytes <= 32 * 1024) return run_fwd_long<T, G, true, 512, 4, FUSED, true, OUT, LN>(a, s);
     return run_fwd_long<T, G, true, 1024, 4, FUSED, true, OUT, LN>(a, s);
   }
-  if (!cache) return run_fwd_long<T, G, false, 1024, 8, FUSED, false, OUT, LN>(a, s);
-  return run_fwd_long<T, G, false, 1024, 8, FUSED, true, OUT, LN>(a, s);
+  if constexpr (!kIsMx<OUT>) {
+    if (!cache) return run_fwd_long<T, G, false, 1024, 8, FUSED, false, OUT, LN>(a, s);
+    return run_fwd_long<T, G, false, 1024, 8, FUSED, true, OUT, LN>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <class T, class G, int OUT>
@@ -161,11 +176,15 @@ hipError_t ln_fwd_typed(const FwdCall& c) {
   return fwd_typed<T, G, false, kOutAct, true>(c);
 }
 
-// Quantised outputs: per-tensor or per-row scale.
+// Quantised outputs: per-tensor or per-row scale, or MX block scales.
 template <class T, class G>
 hipError_t fwd_quant_typed(const FwdCall& c) {
-  return c.out == kOutFp8Row ? fwd_gamma_typed<T, G, kOutFp8Row>(c)
-                             : fwd_gamma_typed<T, G, kOutFp8Tensor>(c);
+  switch (c.out) {
+    case kOutFp8Row: return fwd_gamma_typed<T, G, kOutFp8Row>(c);
+    case kOutMxFp8: return fwd_gamma_typed<T, G, kOutMxFp8>(c);
+    case kOutMxFp4: return fwd_gamma_typed<T, G, kOutMxFp4>(c);
+    default: return fwd_gamma_typed<T, G, kOutFp8Tensor>(c);
+  }
 }
 
 }  // namespace rmsn

@@ -25,6 +25,12 @@
 // centred values still in registers (or in the LDS cache), then
 // y = (x - mean) * rstd * gamma + beta. It is used without FUSED and OUT.
 //
+// OUT may also select an MX block-scaled output (MXFP8 / MXFP4): each block
+// of 32 consecutive elements of a row -- 32 / E consecutive lanes holding the
+// same unit slot -- takes the max |y| with lane moves, writes its E8M0 code
+// and its elements y * 2^(127 - code) as e4m3 or e2m1 codes. MX outputs run
+// on the 16-byte unit path only.
+//
 // OUT selects the output: the activation type (y), or fp8 e4m3 codes of y / s
 // (the quantised variants of the "TIRx kernels" page's FlashInfer norm ports)
 // with s one caller scale, or s_i = max_j |y_ij| / 448 per row. For the per-row
@@ -55,6 +61,30 @@ struct FwdArgs {
   float* scale;  // kOutFp8Tensor: [1], read; kOutFp8Row: [M], written
   const typename G::S* beta;  // LayerNorm bias (may be null)
   float* mean;                // LayerNorm per-row mean (may be null)
+  uint8_t* mx;                // MX outputs: E8M0 codes, [M, N / 32]
+};
+
+template <int OUT>
+constexpr bool kIsMx = OUT == kOutMxFp8 || OUT == kOutMxFp4;
+
+// MX output of one unit (E elements o of a row): the block max over the
+// 32 / E lanes holding the block (every lane of the wave must take part),
+// its E8M0 code, and the packed element codes.
+template <int OUT, int E>
+struct MxUnit {
+  static constexpr int kLanes = 32 / E;            // lanes per 32-element block
+  static constexpr int kEmax = OUT == kOutMxFp4 ? 2 : 8;
+  using Pack = typename std::conditional<OUT == kOutMxFp4, Fp4Unit<E>, Fp8Unit<E>>::type;
+  static constexpr int kBytes = OUT == kOutMxFp4 ? E / 2 : E;  // output bytes per unit
+  __device__ static int code(const float* o) {
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(o[e]));
+    return mx_code(group_max<kLanes>(m), kEmax);
+  }
+  __device__ static typename Pack::Raw pack(const float* o, int c) {
+    return Pack::pack(o, __builtin_ldexpf(1.0f, 127 - c));
+  }
 };
 
 // Sum-of-squares reduction type: the pair (sum, max) for the per-row scale.
@@ -218,7 +248,17 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const int u = lane + k * TPR;
-      if (valid && u < nunits) {
+      if constexpr (kIsMx<OUT>) {
+        using X = MxUnit<OUT, E>;
+        float o[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = v[k][e] * rs * gam[k][e];
+        const int c = X::code(o);
+        if (valid && u < nunits) {
+          X::Pack::store_nt(a.q + off * X::kBytes / E + u * X::kBytes, X::pack(o, c));
+          if (u % X::kLanes == 0) a.mx[row * (a.N / 32) + u / X::kLanes] = static_cast<uint8_t>(c);
+        }
+      } else if (valid && u < nunits) {
         float o[E];
         if constexpr (LN) {
 #pragma unroll
@@ -430,6 +470,40 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
         }
         buf_store16_nt(U::narrow(o), rsy, unit_offset(row0, k));
       }
+    } else if constexpr (kIsMx<OUT>) {
+      // MX: 8 (fp8) or 4 (fp4) output bytes per 16-byte unit, so offsets are
+      // the input's / 2 or / 4; one E8M0 code per 4 units.
+      using X = MxUnit<OUT, E>;
+      constexpr int kShift = OUT == kOutMxFp4 ? 2 : 1;
+      const int64_t rest = row0 < a.M ? (a.M - row0) * a.N : 0;
+      const int64_t qrest = (rest * X::kBytes) / E;
+      const auto rsq = make_rsrc(a.q + row0 * a.N * X::kBytes / E,
+                                 static_cast<uint32_t>(qrest < 0x7fffffff ? qrest : 0x7fffffff));
+      const int64_t nbk = a.N / 32;  // scale codes per row
+      const int64_t srest = row0 < a.M ? (a.M - row0) * nbk : 0;
+      const auto rss = make_rsrc(a.mx + row0 * nbk,
+                                 static_cast<uint32_t>(srest < 0x7fffffff ? srest : 0x7fffffff));
+#pragma unroll
+      for (int k = 0; k < UPT; ++k) {
+        float v[E], g[E], o[E];
+        U::widen(cx[k], v);
+        widen_gamma(graw[k], g);
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
+        const int c = X::code(o);
+        const uint32_t off = unit_offset(row0, k);
+        const uint32_t qoff = off == kBufOutOfRange ? off : off >> kShift;
+        if constexpr (OUT == kOutMxFp4) {
+          __builtin_amdgcn_raw_buffer_store_b32(X::pack(o, c), rsq, qoff, 0, kBufNT);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b64(X::pack(o, c), rsq, qoff, 0, kBufNT);
+        }
+        const int u = lane + k * TPR;
+        const bool first = off != kBufOutOfRange && u % X::kLanes == 0;
+        const uint32_t soff = first ? static_cast<uint32_t>(nblk * grp * nbk + u / X::kLanes)
+                                    : kBufOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(c), rss, soff, 0, 0);
+      }
     } else {
       // fp8 codes: N bytes per row, 8 per unit, so offsets are half the input's.
       const int64_t rest = row0 < a.M ? (a.M - row0) * a.N : 0;
@@ -582,7 +656,25 @@ __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
 #pragma unroll
       for (int k = 0; k < UNROLL; ++k) {
         const int u = first + threadIdx.x + k * BLOCK;
-        if (u < nunits) {
+        if constexpr (kIsMx<OUT>) {
+          // Every lane takes part in the block max (zeros past the row's end).
+          using X = MxUnit<OUT, E>;
+          float v[E], g[E], o[E];
+          U::widen(raw[k], v);
+          if (u < nunits) {
+            load_gamma<G, E, VEC>(a.gamma, u * E, g);
+          } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) g[e] = 0.0f;
+          }
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
+          const int c = X::code(o);
+          if (u < nunits) {
+            X::Pack::store_nt(a.q + off * X::kBytes / E + u * X::kBytes, X::pack(o, c));
+            if (u % X::kLanes == 0) a.mx[row * (a.N / 32) + u / X::kLanes] = static_cast<uint8_t>(c);
+          }
+        } else if (u < nunits) {
           float v[E], g[E], o[E];
           U::widen(raw[k], v);
           load_gamma<G, E, VEC>(a.gamma, u * E, g);

@@ -67,6 +67,8 @@ struct FwdCall {
   // LayerNorm only: bias (may be null) and per-row mean output (may be null).
   const void* beta = nullptr;
   float* mean = nullptr;
+  // MX outputs (out 3: MXFP8, 4: MXFP4): E8M0 codes [M, N / 32].
+  uint8_t* mx = nullptr;
 };
 
 hipError_t launch_fwd_f32(const FwdCall& c);

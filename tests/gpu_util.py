@@ -20,6 +20,10 @@ Tolerances (fixed here, used by every GPU test):
   * LayerNorm dx: within 1 ulp, or |dx - exact| <= 2^-18 rstd (|gamma dy| +
     A1 + |xhat| A2) with A1 = mean_j |gamma dy|, A2 = mean_j |gamma dy xhat|;
     dgamma / dbeta as dgamma above with S = sum_i |dy xhat| / sum_i |dy|.
+  * MX codes: E8M0 scale codes equal to the oracle's, except where the
+    block's amax lies within 2^-18 (relative) of a power of two, where the
+    neighbouring code is accepted; elements within one step of the oracle's
+    rounding of y under the kernel's scale.
   * fp8 e4m3 codes: ordinal distance <= 1 from the oracle's code (the kernel
     scales in fp32, so y / s can land on the other side of a tie); per-row
     scales: relative error <= 1e-5; every nonzero row's largest code is
@@ -225,3 +229,57 @@ def check_layernorm_bwd(got_dx, got_dg, got_db, ref, x, dy, gamma, mean, rstd, d
     if got_db is not None:
         check_dgamma(got_db, {"dgamma": ref["dbeta"], "s": ref["sb"]})
     return int((~ok_ulp & ok_floor).sum())
+
+
+def unpack_fp4(packed: np.ndarray, M: int, N: int) -> np.ndarray:
+    """[M, N/2] bytes -> [M, N] codes (element 2k in the low nibble)."""
+    p = packed.reshape(M, N // 2)
+    out = np.empty((M, N), np.uint8)
+    out[:, 0::2] = p & 0xF
+    out[:, 1::2] = p >> 4
+    return out
+
+
+def mx_ordinal(codes: np.ndarray, elem: int) -> np.ndarray:
+    c = codes.astype(np.int32)
+    if elem == O.E2M1:
+        mag, neg = c & 0x7, c & 0x8
+    else:
+        mag, neg = c & 0x7F, c & 0x80
+    return np.where(neg, -mag, mag)
+
+
+def check_mx(got_q: np.ndarray, got_scale: np.ndarray, ref: dict, elem: int):
+    """MX output against the oracle (see the module docstring). Returns the
+    number of blocks that took the neighbouring scale code."""
+    M, N = ref["q"].shape
+    nb = N // 32
+    got_q = got_q.reshape(M, N)
+    got_scale = got_scale.reshape(M, nb).astype(np.int32)
+    ref_scale = ref["scale"].astype(np.int32)
+    if elem == O.E4M3:
+        assert not np.any((got_q & 0x7F) == 0x7F), "NaN code in the output"
+    amax = ref["amax"]
+    with np.errstate(divide="ignore"):
+        l2 = np.log2(np.where(amax > 0, amax, 1.0))
+    near_pow2 = np.abs(l2 - np.round(l2)) < 2.0 ** -18
+    diff = got_scale - ref_scale
+    bad = (diff != 0) & ~(near_pow2 & (np.abs(diff) == 1))
+    if bad.any():
+        i, b = np.argwhere(bad)[0]
+        raise AssertionError(f"mx scale: {int(bad.sum())} blocks differ; first ({i}, {b}): got "
+                             f"{got_scale[i, b]}, oracle {ref_scale[i, b]}, amax {amax[i, b]!r}")
+    # Elements: re-quantise the oracle's y under the kernel's scale where it differs.
+    y = ref["q_exact"].reshape(M, nb, 32) * np.exp2(ref_scale - 127.0)[:, :, None]
+    want = ref["q"].reshape(M, nb, 32).copy()
+    moved = diff != 0
+    if moved.any():
+        t = y * np.exp2(127.0 - got_scale)[:, :, None]
+        want[moved] = O.round_to(t[moved], elem)
+    d = np.abs(mx_ordinal(got_q.reshape(M, nb, 32), elem) - mx_ordinal(want, elem))
+    if (d > 1).any():
+        i, b, j = np.argwhere(d > 1)[0]
+        raise AssertionError(f"mx elements: {int((d > 1).sum())} codes more than one step off; "
+                             f"first ({i}, {b}, {j}): got {got_q.reshape(M, nb, 32)[i, b, j]:#x}, "
+                             f"want {want[i, b, j]:#x}, y {y[i, b, j]!r}")
+    return int(moved.sum())

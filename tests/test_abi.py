@@ -183,7 +183,7 @@ def quant(x=A, r=None, g=B, q=C, sc=D, mode=QR, rstd=E, M=64, N=256, eps=1e-5, x
 
 def test_quant_validation(lib):
     assert quant(mode=0) == MODE
-    assert quant(mode=3) == MODE
+    assert quant(mode=5) == MODE
     assert quant(xd=F32, gd=F16) == DTYPE
     assert quant(N=0) == SHAPE
     assert quant(eps=float("nan")) == EPS
@@ -289,3 +289,18 @@ def test_layernorm_backward_validation(lib):
     assert lnb(db=F + 8) == OVERLAP                  # dbeta over dgamma
     assert lnb(db=G + 16) == OVERLAP                 # dbeta in the workspace
     assert lnb(ws=C) == OVERLAP                      # workspace over the statistics
+
+
+MX8, MX4 = 3, 4
+
+
+def test_mx_quant_validation(lib):
+    assert quant(mode=MX8, N=100) == SHAPE            # N % 32 != 0
+    assert quant(mode=MX4, N=33) == SHAPE
+    assert quant(mode=MX8, x=A + 2) == ALIGN          # rows must be 16-byte aligned
+    assert quant(mode=MX4, g=B + 8) == ALIGN
+    assert quant(mode=MX8, r=F + 4) == ALIGN
+    assert quant(mode=MX8, q=C + 4) == ALIGN          # 8-byte fp8 units (bf16 input)
+    assert quant(mode=MX4, q=C + 2) == ALIGN          # 4-byte fp4 units
+    assert quant(mode=MX4, sc=C + 64 * 128 - 1) == OVERLAP   # scale codes over q's last byte
+    assert quant(mode=MX8, sc=A + 8) == OVERLAP       # codes written over x

@@ -12,7 +12,8 @@ import gen as G
 import oracle as O
 import row_wise_normalization_fwd_amd as R
 from gpu_util import (check_dgamma, check_dx, check_fp8, check_layernorm, check_layernorm_bwd,
-                      check_output, check_rstd, to_device, to_host, TORCH_DTYPES)
+                      check_mx, check_output, check_rstd, to_device, to_host, unpack_fp4,
+                      TORCH_DTYPES)
 
 pytestmark = pytest.mark.gpu
 
@@ -366,6 +367,125 @@ def test_quant_matches_plain_forward_values():
     yv = O.decode(to_host(y), O.BF16).reshape(M, N)
     deq = O.decode(q.cpu().numpy(), O.E4M3).reshape(M, N) * to_host(sc)[:, None]
     assert np.all(np.abs(deq - yv) <= np.abs(yv) / 8 + to_host(sc)[:, None] * 2.0 ** -9 + 1e-6)
+
+
+# --------------------------------------------- MX block-scaled output
+
+MX_MODES = {O.E4M3: R.RMSN_QUANT_MXFP8, O.E2M1: R.RMSN_QUANT_MXFP4}
+
+
+def run_mx(M, N, xdt, gdt, elem, seed=37, fused=False, want_rstd=False, q_off=0,
+           outlier_every=0, outlier_scale=1.0):
+    _log(f"mx M={M} N={N} x={xdt} g={gdt} elem={elem} fused={fused} q_off={q_off}")
+    x, g, r, _ = _inputs(M, N, xdt, gdt, seed, outlier_every, outlier_scale, with_r=fused)
+    ref = O.rmsnorm_mx_fwd(x, g, M, N, 1e-5, xdt, gdt, elem, r=r)
+    qbytes = M * N // 2 if elem == O.E2M1 else M * N
+    qbuf = torch.full((qbytes + 64,), 0xAB, dtype=torch.uint8, device="cuda")
+    qt = qbuf[q_off:q_off + qbytes]
+    sbuf = torch.full((M * N // 32 + 64,), 0xAB, dtype=torch.uint8, device="cuda")
+    st_ = sbuf[:M * N // 32]
+    xt, gt = _put(x, xdt), _put(g, gdt)
+    rt = _put(r, xdt) if fused else None
+    rs = torch.full((M,), float("nan"), device="cuda") if want_rstd else None
+    st = R.rmsnorm_quant_fwd(xt, rt, gt, qt, st_, MX_MODES[elem], rs, M, N, 1e-5, xdt, gdt,
+                             _stream())
+    assert st == 0, R.rmsnorm_status_string(st)
+    torch.cuda.synchronize()
+    q = qt.cpu().numpy()
+    if elem == O.E2M1:
+        q = unpack_fp4(q, M, N)
+    moved = check_mx(q, st_.cpu().numpy(), ref, elem)
+    assert np.all(qbuf[:q_off].cpu().numpy() == 0xAB) and np.all(qbuf[q_off + qbytes:].cpu().numpy() == 0xAB)
+    assert np.all(sbuf[M * N // 32:].cpu().numpy() == 0xAB), "write past the scale codes"
+    if fused:
+        assert np.array_equal(to_host(rt).reshape(M, N).view(np.uint8), ref["h"].view(np.uint8))
+    if want_rstd:
+        f = O.rmsnorm_fwd(ref["h"] if fused else x, g, M, N, 1e-5, xdt, gdt, want_exact=False)
+        check_rstd(to_host(rs), f["rstd"].astype(np.float64))
+    return moved
+
+
+@pytest.mark.parametrize("elem", [O.E4M3, O.E2M1], ids=["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("N", [32, 64, 96, 1024, 4096, 5024, 8192, 8224, 16384])
+def test_mx_sweep(N, pair, elem):
+    run_mx(5, N, *pair, elem, seed=2500 + N, want_rstd=True)
+    run_mx(300, N, *pair, elem, seed=2600 + N, fused=True)
+
+
+@pytest.mark.parametrize("elem", [O.E4M3, O.E2M1], ids=["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_mx_long_rows_and_outliers(pair, elem):
+    run_mx(3, 40000, *pair, elem, seed=2701)
+    run_mx(3, 90016, *pair, elem, seed=2702, fused=True)
+    run_mx(1000, 8192, *pair, elem, seed=2703, outlier_every=13, outlier_scale=300.0, q_off=8)
+
+
+def _mx_exact_block_gamma(elem):
+    """fp32 gamma of 4 blocks of 32 whose block max puts the scale at 1: every
+    representable magnitude of the element format that fits, the ties between
+    neighbours and quarter points, with alternating signs."""
+    if elem == O.E2M1:
+        vals = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+        top = 6.5                       # saturates to 6, keeps floor(log2) = 2
+    else:
+        vals = O.decode(np.arange(0x60, 0x7F, dtype=np.uint8), O.E4M3)  # 32 .. 448
+        top = 460.0
+    mids = (vals[:-1] + vals[1:]) / 2
+    q1 = vals[:-1] + (vals[1:] - vals[:-1]) / 4
+    pool = np.concatenate([vals, mids, q1])
+    blocks = []
+    for b in range(4):
+        chunk = np.resize(np.roll(pool, 7 * b), 31)
+        blk = np.concatenate([[top], chunk]) * np.where(np.arange(32) % 2 == 0, 1.0, -1.0)
+        blocks.append(np.roll(blk, 5 * b))
+    return np.concatenate(blocks).astype(np.float32)
+
+
+@pytest.mark.parametrize("elem", [O.E4M3, O.E2M1], ids=["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("xdt", [O.F32, O.F16, O.BF16], ids=["f32", "f16", "bf16"])
+def test_mx_rounding_is_nearest_even_at_every_tie(xdt, elem):
+    # Constant rows 2^k with eps = 0 give y = +-gamma exactly; every block's
+    # max is in [2^emax, 2^(emax+1)), so the scale is 1 and each element code
+    # is the exact rounding of gamma: bit-exact, ties included.
+    g = _mx_exact_block_gamma(elem)
+    N, M = g.size, 3
+    for c in (1.0, -0.5, 4.0):
+        x = O.round_to(np.full((M, N), c), xdt)
+        ref = O.rmsnorm_mx_fwd(x, g, M, N, 0.0, xdt, O.F32, elem)
+        assert np.all(ref["scale"] == 127)
+        qb = M * N // 2 if elem == O.E2M1 else M * N
+        qt = torch.empty(qb, dtype=torch.uint8, device="cuda")
+        sc = torch.empty(M * N // 32, dtype=torch.uint8, device="cuda")
+        assert R.rmsnorm_quant_fwd(_put(x, xdt), None, _put(g, O.F32), qt, sc, MX_MODES[elem], None,
+                                   M, N, 0.0, xdt, O.F32, _stream()) == 0
+        torch.cuda.synchronize()
+        q = qt.cpu().numpy()
+        q = unpack_fp4(q, M, N) if elem == O.E2M1 else q.reshape(M, N)
+        assert np.all(sc.cpu().numpy() == 127)
+        bad = q != ref["q"]
+        assert not bad.any(), f"c={c}: {int(bad.sum())} codes differ"
+
+
+def test_mx_zero_blocks():
+    M, N = 4, 256
+    x, g, _, _ = _inputs(M, N, O.BF16, O.BF16, 2801)
+    g = O.decode(g, O.BF16)
+    g[64:128] = 0.0                                  # blocks 2 and 3 of every row are zero
+    g = O.round_to(g, O.BF16)
+    for elem in (O.E4M3, O.E2M1):
+        ref = O.rmsnorm_mx_fwd(x, g, M, N, 1e-5, O.BF16, O.BF16, elem)
+        qb = M * N // 2 if elem == O.E2M1 else M * N
+        qt = torch.empty(qb, dtype=torch.uint8, device="cuda")
+        sc = torch.empty(M * N // 32, dtype=torch.uint8, device="cuda")
+        assert R.rmsnorm_quant_fwd(_put(x, O.BF16), None, _put(g, O.BF16), qt, sc, MX_MODES[elem],
+                                   None, M, N, 1e-5, O.BF16, O.BF16, _stream()) == 0
+        torch.cuda.synchronize()
+        s_ = sc.cpu().numpy().reshape(M, N // 32)
+        assert np.all(s_[:, 2:4] == 0)
+        q = qt.cpu().numpy()
+        q = unpack_fp4(q, M, N) if elem == O.E2M1 else q.reshape(M, N)
+        check_mx(q, s_, ref, elem)
 
 
 # ------------------------------------------------------ per-head QK-RMSNorm
@@ -776,6 +896,10 @@ def test_workload_full_size(w):
         run_ln_bwd(w.M, w.N, w.x_dt, w.g_dt, seed=w.seed)
     elif w.kind == "qk":
         run_qk(w.M, w.heads_q, w.heads_k, w.N, w.x_dt, w.g_dt, seed=w.seed, eps=w.eps)
+    elif w.kind == "quant" and w.quant_mode >= 3:
+        moved = run_mx(w.M, w.N, w.x_dt, w.g_dt, O.E4M3 if w.quant_mode == 3 else O.E2M1,
+                       seed=w.seed, fused=w.fused_quant)
+        _log(f"blocks on the neighbouring scale code: {moved}")
     elif w.kind == "quant":
         steps = run_quant(w.M, w.N, w.x_dt, w.g_dt, w.quant_mode, seed=w.seed, eps=w.eps,
                           fused=w.fused_quant, want_rstd=w.store_rstd,
