@@ -252,30 +252,23 @@ __device__ __forceinline__ int mx_code(float amax, int emax) {
   return c < 0 ? 0 : c;
 }
 
-// e2m1 code of t, nearest-even, saturated at 6: the count of rounding
-// thresholds below |t| (ties at 0.25, 1.25, 2.5 and 5 go down to the even
-// code, those at 0.75, 1.75 and 3.5 up), plus the sign bit.
-__device__ __forceinline__ uint32_t fp4_code(float t) {
-  const float a = __builtin_fabsf(t);
-  const uint32_t c = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
-                     static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
-                     static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
-                     static_cast<uint32_t>(a > 5.0f);
-  return c | ((__float_as_uint(t) >> 28) & 0x8u);
-}
-
-// The fp4 image of one unit of E elements: E nibbles, element e in bits
-// [4e, 4e + 4). pack(p, k) encodes p[e] * k.
+// The fp4 (e2m1) image of one unit of E elements: E nibbles, element e in
+// bits [4e, 4e + 4). pack(p, X) encodes p[e] / X for a power-of-two block
+// scale X with gfx950's scaled conversion, which divides by the scale, rounds
+// to nearest-even and saturates at +-6 (checked against the e2m1 rounding
+// rule on every value, tie and quarter point of the format, both signs).
 template <int E>
 struct Fp4Unit;
 
 template <>
 struct Fp4Unit<8> {
   using Raw = uint32_t;
-  __device__ static Raw pack(const float* o, float k) {
+  __device__ static Raw pack(const float* o, float X) {
     uint32_t w = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w |= fp4_code(o[e] * k) << (4 * e);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, o[0], o[1], X, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, o[2], o[3], X, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, o[4], o[5], X, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, o[6], o[7], X, 3);
     return w;
   }
   __device__ static void store_nt(uint8_t* p, Raw v) {
@@ -286,10 +279,10 @@ struct Fp4Unit<8> {
 template <>
 struct Fp4Unit<4> {
   using Raw = uint16_t;
-  __device__ static Raw pack(const float* o, float k) {
+  __device__ static Raw pack(const float* o, float X) {
     uint32_t w = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w |= fp4_code(o[e] * k) << (4 * e);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, o[0], o[1], X, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, o[2], o[3], X, 1);
     return static_cast<Raw>(w);
   }
   __device__ static void store_nt(uint8_t* p, Raw v) {

@@ -82,8 +82,11 @@ struct MxUnit {
     for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(o[e]));
     return mx_code(group_max<kLanes>(m), kEmax);
   }
+  // fp8: multiply by 2^(127 - c), clamp, convert; fp4: the scaled conversion
+  // divides by X = 2^(c - 127) itself. Both scalings are exact.
   __device__ static typename Pack::Raw pack(const float* o, int c) {
-    return Pack::pack(o, __builtin_ldexpf(1.0f, 127 - c));
+    if constexpr (OUT == kOutMxFp4) return Pack::pack(o, __builtin_ldexpf(1.0f, c - 127));
+    else return Pack::pack(o, __builtin_ldexpf(1.0f, 127 - c));
   }
 };
 
