@@ -968,3 +968,65 @@ def test_graph_capture_and_replay():
         got = [to_host(t) for t in (y, rs, rt, y2, dx, dg)]
         for a, b in zip(got, want):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), rep
+
+
+def test_graph_capture_and_replay_of_every_variant():
+    # Fused-add backward, fp8 / MX outputs, QK-norm (in place) and LayerNorm
+    # forward and backward captured together; every replay must match the
+    # eager run bit for bit.
+    M, N = 256, 4096
+    x, g, r, dy = _inputs(M, N, O.BF16, O.BF16, 95, with_r=True, with_dy=True)
+    xt, gt, dyt, rt0 = _put(x, O.BF16), _put(g, O.BF16), _put(dy, O.BF16), _put(r, O.BF16)
+    rs = torch.empty(M, device="cuda")
+    assert R.rmsnorm_fwd(xt, gt, _empty(M * N, O.BF16), rs, M, N, 1e-5, O.BF16, O.BF16,
+                         _stream()) == 0
+    dres = _put(G.normal(95, G.STREAM_DRES, M, N, O.BF16), O.BF16)
+    dh, dg = _empty(M * N, O.BF16), torch.empty(N, device="cuda")
+    ws = torch.empty(R.rmsnorm_bwd_workspace_size(M, N, O.BF16), dtype=torch.uint8, device="cuda")
+    q8, s8 = torch.empty(M * N, dtype=torch.uint8, device="cuda"), torch.empty(M, device="cuda")
+    q4 = torch.empty(M * N // 2, dtype=torch.uint8, device="cuda")
+    s4 = torch.empty(M * N // 32, dtype=torch.uint8, device="cuda")
+    qkv0 = _put(G.normal(96, G.STREAM_X, 1, 64 * 48 * 128, O.BF16).reshape(-1), O.BF16)
+    qkv = qkv0.clone()
+    g128 = _put(G.uniform(96, G.STREAM_GAMMA, 128, 0.5, 1.5, O.BF16), O.BF16)
+    beta = _put(G.uniform(95, G.STREAM_DY, N, -1.0, 1.0, O.BF16), O.BF16)
+    ly, lm, lr = _empty(M * N, O.BF16), torch.empty(M, device="cuda"), torch.empty(M, device="cuda")
+    ldx, ldg, ldb = _empty(M * N, O.BF16), torch.empty(N, device="cuda"), torch.empty(N, device="cuda")
+    lws = torch.empty(R.layernorm_bwd_workspace_size(M, N, O.BF16), dtype=torch.uint8,
+                      device="cuda")
+    outs = (dh, dg, q8, s8, q4, s4, qkv, ly, lm, lr, ldx, ldg, ldb)
+
+    def run(stream):
+        assert R.rmsnorm_fused_add_bwd(dyt, xt, rs, gt, dres, dh, dg, ws, ws.numel(), M, N,
+                                       O.BF16, O.BF16, stream) == 0
+        assert R.rmsnorm_quant_fwd(xt, None, gt, q8, s8, R.RMSN_QUANT_FP8_ROW, None, M, N, 1e-5,
+                                   O.BF16, O.BF16, stream) == 0
+        assert R.rmsnorm_quant_fwd(xt, None, gt, q4, s4, R.RMSN_QUANT_MXFP4, None, M, N, 1e-5,
+                                   O.BF16, O.BF16, stream) == 0
+        assert R.rmsnorm_qk_fwd(qkv, qkv.data_ptr() + 32 * 128 * 2, g128, g128, 64, 32, 8, 128,
+                                48 * 128, 48 * 128, 1e-6, O.BF16, O.BF16, stream) == 0
+        assert R.layernorm_fwd(xt, gt, beta, ly, lm, lr, M, N, 1e-5, O.BF16, O.BF16, stream) == 0
+        assert R.layernorm_bwd(dyt, xt, lm, lr, gt, ldx, ldg, ldb, lws, lws.numel(), M, N,
+                               O.BF16, O.BF16, stream) == 0
+
+    run(_stream())
+    torch.cuda.synchronize()
+    want = [t.cpu().clone() for t in outs]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        qkv.copy_(qkv0)
+        with torch.cuda.graph(graph, stream=side):
+            run(side)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        qkv.copy_(qkv0)                   # eager work between replays
+        for t in outs:
+            if t is not qkv:
+                t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, w in zip(outs, want):
+            assert torch.equal(t.cpu().view(torch.uint8), w.view(torch.uint8)), rep
