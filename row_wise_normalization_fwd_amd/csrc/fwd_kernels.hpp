@@ -28,8 +28,8 @@
 // OUT may also select an MX block-scaled output (MXFP8 / MXFP4): each block
 // of 32 consecutive elements of a row -- 32 / E consecutive lanes holding the
 // same unit slot -- takes the max |y| with lane moves, writes its E8M0 code
-// and its elements y * 2^(127 - code) as e4m3 or e2m1 codes. MX outputs run
-// on the 16-byte unit path only.
+// and its elements y * 2^(127 - code) as e4m3 or e2m1 codes, with y computed
+// as (x * gamma) * rstd. MX outputs run on the 16-byte unit path only.
 //
 // OUT selects the output: the activation type (y), or fp8 e4m3 codes of y / s
 // (the quantised variants of the "TIRx kernels" page's FlashInfer norm ports)
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
         using X = MxUnit<OUT, E>;
         float o[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = v[k][e] * rs * gam[k][e];
+        for (int e = 0; e < E; ++e) o[e] = v[k][e] * gam[k][e] * rs;
         const int c = X::code(o);
         if (valid && u < nunits) {
           X::Pack::store_nt(a.q + off * X::kBytes / E + u * X::kBytes, X::pack(o, c));
@@ -409,20 +409,29 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
     float ss = part[0];
 #pragma unroll
     for (int k = 1; k < UPT; ++k) ss = ss + part[k];
+    // fp8 / MX outputs keep x * gamma in registers until the stores (their
+    // one-group, 256-thread blocks leave VGPRs to spare); the others widen
+    // again after the reduction instead of keeping fp32 copies live.
+    constexpr bool kKeep = OUT != kOutAct;
+    [[maybe_unused]] float p[kKeep ? UPT : 1][E];
     [[maybe_unused]] float m = 0.0f;
-    if constexpr (OUT == kOutFp8Row) {
+    if constexpr (kKeep) {
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
         float v[E], g[E];
         U::widen(cx[k], v);
         widen_gamma(graw[k], g);
 #pragma unroll
-        for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e] * g[e]));
-      }
-    }
-    // Widen again after the reduction instead of keeping fp32 copies live.
+        for (int e = 0; e < E; ++e) p[k][e] = v[e] * g[e];
+        if constexpr (OUT == kOutFp8Row) {
 #pragma unroll
-    for (int k = 0; k < UPT; ++k) opaque(cx[k]);
+          for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(p[k][e]));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < UPT; ++k) opaque(cx[k]);
+    }
     float rs, inv = tinv;
     [[maybe_unused]] float mu = 0.0f;
     if constexpr (LN) {
@@ -488,11 +497,9 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
                                  static_cast<uint32_t>(srest < 0x7fffffff ? srest : 0x7fffffff));
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
-        float v[E], g[E], o[E];
-        U::widen(cx[k], v);
-        widen_gamma(graw[k], g);
+        float o[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
+        for (int e = 0; e < E; ++e) o[e] = p[k][e] * rs;
         const int c = X::code(o);
         const uint32_t off = unit_offset(row0, k);
         const uint32_t qoff = off == kBufOutOfRange ? off : off >> kShift;
@@ -514,13 +521,8 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
       const float kq = rs * inv;
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
-        float v[E], g[E], o[E];
-        U::widen(cx[k], v);
-        widen_gamma(graw[k], g);
-#pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = v[e] * g[e];
         const uint32_t off = unit_offset(row0, k);
-        __builtin_amdgcn_raw_buffer_store_b64(Fp8Unit<8>::pack(o, kq), rsq,
+        __builtin_amdgcn_raw_buffer_store_b64(Fp8Unit<8>::pack(p[k], kq), rsq,
                                               off == kBufOutOfRange ? off : off >> 1, 0, kBufNT);
       }
     }
@@ -671,7 +673,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
             for (int e = 0; e < E; ++e) g[e] = 0.0f;
           }
 #pragma unroll
-          for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
+          for (int e = 0; e < E; ++e) o[e] = v[e] * g[e] * rs;
           const int c = X::code(o);
           if (u < nunits) {
             X::Pack::store_nt(a.q + off * X::kBytes / E + u * X::kBytes, X::pack(o, c));
