@@ -387,10 +387,17 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
     load_rows(row0 + nblk * RG, nx, nr);
     const uint32_t n = span_bytes(row0);
     float part[UPT];
+    // LayerNorm keeps the fp32 row for its variance and output passes (its
+    // one-group blocks leave VGPRs to spare).
+    [[maybe_unused]] float lv[LN ? UPT : 1][E];
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       float v[E];
       prepare_unit<T, U, FUSED>(cx[k], cr[k], v);
+      if constexpr (LN) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) lv[k][e] = v[e];
+      }
       float s = 0.0f;
       if constexpr (LN) {
 #pragma unroll
@@ -428,7 +435,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
           for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(p[k][e]));
         }
       }
-    } else {
+    } else if constexpr (!LN) {
 #pragma unroll
       for (int k = 0; k < UPT; ++k) opaque(cx[k]);
     }
@@ -440,12 +447,10 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
       float sq = 0.0f;
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
-        float v[E];
-        U::widen(cx[k], v);
         float s = 0.0f;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float d = v[e] - mu;
+          const float d = lv[k][e] - mu;
           s = __builtin_fmaf(d, d, s);
         }
         sq = sq + (unit_offset(row0, k) != kBufOutOfRange ? s : 0.0f);
@@ -469,14 +474,14 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
         float v[E], g[E], o[E];
-        U::widen(cx[k], v);
         widen_gamma(graw[k], g);
         if constexpr (LN) {
           float bb[E];
           widen_gamma(braw[k], bb);
 #pragma unroll
-          for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf((v[e] - mu) * rs, g[e], bb[e]);
+          for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf((lv[k][e] - mu) * rs, g[e], bb[e]);
         } else {
+          U::widen(cx[k], v);
 #pragma unroll
           for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
         }
