@@ -19,7 +19,10 @@ Tolerances (fixed here, used by every GPU test):
     few 2^-24 A); mean: |m - mean| <= 2^-18 A; rstd: relative 1e-5.
   * LayerNorm dx: within 1 ulp, or |dx - exact| <= 2^-18 rstd (|gamma dy| +
     A1 + |xhat| A2) with A1 = mean_j |gamma dy|, A2 = mean_j |gamma dy xhat|;
-    dgamma / dbeta as dgamma above with S = sum_i |dy xhat| / sum_i |dy|.
+    dgamma: |g - o| <= max(1e-3 |o|, (3 + R) 2^-24 S_j), S_j = sum_i |dy xhat|,
+    R = rows per partition block (xhat = (x - mean) rstd costs two fp32
+    roundings and the FMA a third, then R fp32 additions per block); dbeta
+    likewise with (1 + R) and S_j = sum_i |dy| (additions only).
   * MX codes: E8M0 scale codes equal to the oracle's, except where the
     block's amax lies within 2^-18 (relative) of a power of two, where the
     neighbouring code is accepted; elements within one step of the oracle's
@@ -225,9 +228,16 @@ def check_layernorm_bwd(got_dx, got_dg, got_db, ref, x, dy, gamma, mean, rstd, d
         idx = np.unravel_index(int(np.argmax(bad)), bad.shape)
         raise AssertionError(f"layernorm dx: {int(bad.sum())} out of tolerance; first at {idx}: "
                              f"got {gotv[idx]!r}, exact {exact[idx]!r}, floor {floor[idx]!r}")
-    check_dgamma(got_dg, {"dgamma": ref["dgamma"], "s": ref["sg"]})
-    if got_db is not None:
-        check_dgamma(got_db, {"dgamma": ref["dbeta"], "s": ref["sb"]})
+    R = -(-M // min(M, 256))  # rows per partition block
+    for name, got, o, mag, k in (("dgamma", got_dg, ref["dgamma"], ref["sg"], 3 + R),
+                                 ("dbeta", got_db, ref["dbeta"], ref["sb"], 1 + R)):
+        if got is None:
+            continue
+        tol = np.maximum(1e-3 * np.abs(o), k * 2.0 ** -24 * mag)
+        err = np.abs(got.astype(np.float64) - o)
+        bad = err > tol
+        assert not bad.any(), (f"layernorm {name}: {int(bad.sum())} columns out of tolerance; "
+                               f"worst ratio {float((err / tol).max()):.3f}")
     return int((~ok_ulp & ok_floor).sum())
 
 
