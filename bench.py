@@ -5,7 +5,8 @@ A step is one call of the hot path on one batch: by default the bf16 forward
 over a [4096, 8192] batch that also writes the fp32 per-row rstd. Inputs are
 seeded synthetic data resident in HBM before timing starts. To measure HBM
 rather than the 256 MB Infinity Cache, consecutive steps rotate over R replicas
-of every operand (R * footprint >= --rotate-bytes, 1 GiB by default).
+of every operand (R * footprint >= --rotate-bytes, 1 GiB by default); the R
+replicas of an operand are the rows of one [R, numel] allocation.
 
 Timing: W untimed warm-up steps, then exactly K steps between two HIP events
 recorded on the stream the kernels run on (torch's current stream), with a
@@ -140,44 +141,57 @@ class Runner:
             self.qkv_stride = (w.heads_q + 2 * w.heads_k) * N
         if w.kind == "quant" and w.quant_mode == 1:
             self.tensor_scale = torch.tensor([w.tensor_scale], dtype=torch.float32, device=dev)
-        for i in range(self.replicas):
-            s = {"x": x0 if i == 0 else x0.clone()}
-            if w.kind == "fwd":
-                s["y"] = torch.empty_like(x0)
-                s["rstd"] = torch.empty(M, dtype=torch.float32, device=dev) if w.store_rstd else None
-            elif w.kind == "fused_add":
-                s["r"] = r0 if i == 0 else r0.clone()
-                s["y"] = torch.empty_like(x0)
-                s["rstd"] = torch.empty(M, dtype=torch.float32, device=dev) if w.store_rstd else None
-            elif w.kind == "qk":
-                pass  # in place on the fused q/k/v buffer "x"
-            elif w.kind == "ln":
-                s["y"] = torch.empty_like(x0)
-                s["mean"] = torch.empty(M, dtype=torch.float32, device=dev)
-                s["rstd"] = torch.empty(M, dtype=torch.float32, device=dev)
-            elif w.kind == "quant":
-                s["r"] = (r0 if i == 0 else r0.clone()) if w.fused_quant else None
-                s["q"] = torch.empty(M * N // 2 if w.quant_mode == 4 else M * N,
-                                     dtype=torch.uint8, device=dev)
-                if w.quant_mode == 1:
-                    s["scale"] = self.tensor_scale
-                elif w.quant_mode == 2:
-                    s["scale"] = torch.empty(M, dtype=torch.float32, device=dev)
-                else:  # MX: E8M0 codes per 32 elements
-                    s["scale"] = torch.empty(M * N // 32, dtype=torch.uint8, device=dev)
-                s["rstd"] = torch.empty(M, dtype=torch.float32, device=dev) if w.store_rstd else None
-            else:
-                s["dy"] = dy0 if i == 0 else dy0.clone()
-                s["rstd"] = rstd_bwd
-                s["dx"] = torch.empty_like(x0)
-                s["dgamma"] = torch.empty(N, dtype=torch.float32, device=dev)
-                s["ws"] = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
-                if w.kind == "fused_add_bwd":
-                    s["dres"] = dres0 if i == 0 else dres0.clone()
-                if w.kind == "ln_bwd":
-                    s["mean"] = mean_bwd
-                    s["dbeta"] = torch.empty(N, dtype=torch.float32, device=dev)
-            self.sets.append(s)
+        # Each operand's R replicas are rows of one [R, numel] allocation, the
+        # layout of a batched tensor, so every stream is one contiguous range.
+        nrep = self.replicas
+
+        def rep_copy(src):
+            block = torch.empty((nrep, src.numel()), dtype=src.dtype, device=dev)
+            block.copy_(src.reshape(1, -1).expand(nrep, -1))
+            return list(block.unbind(0))
+
+        def rep_empty(numel, dtype):
+            return list(torch.empty((nrep, numel), dtype=dtype, device=dev).unbind(0))
+
+        def rep_opt(flag, numel, dtype):
+            return rep_empty(numel, dtype) if flag else [None] * nrep
+
+        f32, u8 = torch.float32, torch.uint8
+        cols = {"x": rep_copy(x0)}
+        if w.kind in ("fwd", "fused_add"):
+            cols["y"] = rep_empty(M * N, x0.dtype)
+            cols["rstd"] = rep_opt(w.store_rstd, M, f32)
+            if w.kind == "fused_add":
+                cols["r"] = rep_copy(r0)
+        elif w.kind == "qk":
+            pass  # in place on the fused q/k/v buffer "x"
+        elif w.kind == "ln":
+            cols["y"] = rep_empty(M * N, x0.dtype)
+            cols["mean"] = rep_empty(M, f32)
+            cols["rstd"] = rep_empty(M, f32)
+        elif w.kind == "quant":
+            cols["r"] = rep_copy(r0) if w.fused_quant else [None] * nrep
+            cols["q"] = rep_empty(M * N // 2 if w.quant_mode == 4 else M * N, u8)
+            if w.quant_mode == 1:
+                cols["scale"] = [self.tensor_scale] * nrep
+            elif w.quant_mode == 2:
+                cols["scale"] = rep_empty(M, f32)
+            else:  # MX: E8M0 codes per 32 elements
+                cols["scale"] = rep_empty(M * N // 32, u8)
+            cols["rstd"] = rep_opt(w.store_rstd, M, f32)
+        else:
+            cols["dy"] = rep_copy(dy0)
+            cols["rstd"] = [rstd_bwd] * nrep
+            cols["dx"] = rep_empty(M * N, x0.dtype)
+            cols["dgamma"] = rep_empty(N, f32)
+            cols["ws"] = rep_empty(max(self.ws_bytes, 16), u8)
+            if w.kind == "fused_add_bwd":
+                cols["dres"] = rep_copy(dres0)
+            if w.kind == "ln_bwd":
+                cols["mean"] = [mean_bwd] * nrep
+                cols["dbeta"] = rep_empty(N, f32)
+        for i in range(nrep):
+            self.sets.append({k: v[i] for k, v in cols.items()})
         torch.cuda.synchronize()
         # Pre-marshalled integer arguments keep the host launch path short.
         self.calls = []
@@ -249,8 +263,8 @@ def copy_calibration(nbytes: int, rotate_bytes: float, steps: int = 200) -> floa
     import torch
     half = nbytes // 2
     reps = max(1, int(-(-rotate_bytes // nbytes)))
-    src = [torch.empty(half, dtype=torch.uint8, device="cuda").fill_(1) for _ in range(reps)]
-    dst = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(reps)]
+    src = list(torch.ones((reps, half), dtype=torch.uint8, device="cuda").unbind(0))
+    dst = list(torch.empty((reps, half), dtype=torch.uint8, device="cuda").unbind(0))
     ms = time_steps(lambda i: dst[i % reps].copy_(src[i % reps]), steps, 20)
     del src, dst
     return 2 * half / (ms * 1e-3) / 1e9
