@@ -21,7 +21,10 @@ template <class T, class G, bool RES, bool LN, bool VEC, int TPR, int UPT, int B
 hipError_t run_stage1(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s) {
   constexpr int RG = BLOCK / TPR;
   constexpr int E = Unit<T, VEC>::E;
-  constexpr size_t kLds = RG > 1 ? static_cast<size_t>(BLOCK) * UPT * E * sizeof(float) : 0;
+  // Row-group combine buffer, and LayerNorm's gamma copy aliased with it.
+  constexpr size_t kComb = RG > 1 ? static_cast<size_t>(BLOCK) * UPT * E * sizeof(float) : 0;
+  constexpr size_t kGam = LN ? stage1_gamma_lds_bytes<TPR, UPT, E>() : 0;
+  constexpr size_t kLds = kComb > kGam ? kComb : kGam;
   constexpr auto kernel = bwd_stage1_kernel<T, G, VEC, TPR, UPT, BLOCK, RES, LN>;
   if constexpr (kLds > 48 * 1024) {
     // Raise the dynamic LDS limit (gfx950 has 160 KiB per workgroup).
@@ -33,12 +36,13 @@ hipError_t run_stage1(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s) {
 }
 
 // Lanes per row TPR with UPT units each; a full 1024-thread block of row
-// groups when each block owns at least two rows.
-// LayerNorm keeps a second accumulator per column and spills in 1024-thread
-// blocks, so its row groups share 512-thread blocks.
+// groups when each block owns at least two rows. (LayerNorm, which keeps a
+// dbeta sum per column too, fits 1024-thread blocks because it reads gamma
+// from LDS: at 8192 x 8192 bf16 stage 1 ran 70.5 us there against 74-77 us
+// with 512-thread blocks and gamma in registers.)
 template <class T, class G, bool RES, bool LN, bool VEC, int TPR, int UPT>
 hipError_t run_stage1_rows(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s) {
-  constexpr int kFull = LN ? 512 : 1024;
+  constexpr int kFull = 1024;
   if constexpr (TPR < kFull) {
     if (a.M >= 2 * a.nblk) return run_stage1<T, G, RES, LN, VEC, TPR, UPT, kFull>(a, blocks, s);
   }
@@ -53,13 +57,7 @@ hipError_t stage1_typed(const BwdArgs<T, G>& a, bool vec, int64_t blocks, hipStr
     constexpr int E = 16 / T::kSize;
     const int64_t units = N / E;
     if (units > 2048) return hipErrorNotSupported;
-    // LayerNorm's 1024-lane rows of 16-bit data spill: two-pass tier instead
-    // (those rows are longer than 8192, so the workspace holds their dots).
-    if constexpr (LN && T::kSize == 2) {
-      if (units > 1024) return hipErrorNotSupported;
-    } else {
-      if (units > 1024) return run_stage1_rows<T, G, RES, LN, true, 1024, 2>(a, blocks, s);
-    }
+    if (units > 1024) return run_stage1_rows<T, G, RES, LN, true, 1024, 2>(a, blocks, s);
     switch (next_pow2(ceil_div(units, 2))) {
       case 1: return run_stage1_rows<T, G, RES, LN, true, 1, 2>(a, blocks, s);
       case 2: return run_stage1_rows<T, G, RES, LN, true, 2, 2>(a, blocks, s);

@@ -82,11 +82,19 @@ __device__ __forceinline__ float unit_dot(const float* dyv, const float* g, cons
 
 // Stage 1. A block of BLOCK threads holds RG = BLOCK / TPR row groups; block
 // b's rows are b + G * s, and group `grp` takes s = s0 + grp for s0 = 0, RG,
-// 2 RG, ... Each lane keeps gamma and its columns' dgamma partial sums in
-// registers. The x and dy units of a group's next row are loaded before the
-// current row is reduced, so loads stay in flight across rows. With RG > 1 the
-// groups' partials are combined through LDS in group order before the block
-// writes its partial row.
+// 2 RG, ... Each lane keeps its columns' dgamma partial sums in registers, and
+// gamma too for RMSNorm; LayerNorm, which also keeps dbeta sums, reads gamma
+// from a widened copy in LDS at each use instead (16 fewer VGPRs per lane for
+// 8-element units, which lets it run at the occupancy of the RMSNorm kernel).
+// The x and dy units of a group's next row are loaded before the current row
+// is reduced, so loads stay in flight across rows. With RG > 1 the groups'
+// partials are combined through LDS in group order before the block writes
+// its partial row.
+template <int TPR, int UPT, int E>
+constexpr size_t stage1_gamma_lds_bytes() {
+  return static_cast<size_t>(TPR) * UPT * E * sizeof(float);
+}
+
 template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool RES, bool LN = false>
 __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   using U = Unit<T, VEC>;
@@ -102,21 +110,67 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   float* comb = reinterpret_cast<float*>(lds_bytes);  // [RG][COLS] when RG > 1
 
   const int nunits = a.N / E;
-  const int grp = threadIdx.x / TPR;
+  // A group of at least a wave's lanes is wave-uniform: keep its index (and
+  // the row offsets derived from it) in scalar registers.
+  const int grp = TPR >= kWave ? __builtin_amdgcn_readfirstlane(threadIdx.x / TPR)
+                               : static_cast<int>(threadIdx.x / TPR);
   const int lane = threadIdx.x % TPR;
   const int64_t b = blockIdx.x;
 
-  float gam[UPT][E];
+  // LayerNorm's gamma copy in LDS (aliases comb, which is first written after
+  // a barrier that follows the last gamma read): GP planes of GW floats per
+  // unit, plane p of unit u at (p * NU + u) * GW, so the lanes of a wave read
+  // consecutive GW-float words. Units past the row read zeros.
+  constexpr int NU = TPR * UPT;
+  constexpr int GW = E >= 4 ? 4 : E;
+  constexpr int GP = E / GW;
+  float* const glds = reinterpret_cast<float*>(lds_bytes);
+  if constexpr (LN) {
+    for (int u = threadIdx.x; u < NU; u += BLOCK) {
+      float g[E];
+      if (u < nunits) {
+        load_gamma<G, E, VEC>(a.gamma, u * E, g);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) g[e] = 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < GP; ++q)
+#pragma unroll
+        for (int w = 0; w < GW; ++w) glds[(q * NU + u) * GW + w] = g[q * GW + w];
+    }
+    __syncthreads();
+  }
+  auto gamma_lds = [&](int u, float* g) {
+#pragma unroll
+    for (int q = 0; q < GP; ++q) {
+      const float* src = glds + (q * NU + u) * GW;
+      if constexpr (GW == 4) {
+        const float4 v = *reinterpret_cast<const float4*>(src);
+        g[q * 4 + 0] = v.x;
+        g[q * 4 + 1] = v.y;
+        g[q * 4 + 2] = v.z;
+        g[q * 4 + 3] = v.w;
+      } else {
+#pragma unroll
+        for (int w = 0; w < GW; ++w) g[q * GW + w] = src[w];
+      }
+    }
+  };
+
+  [[maybe_unused]] float gam[LN ? 1 : UPT][E];
   float acc[UPT][E];
   [[maybe_unused]] float accb[LN ? UPT : 1][E];  // LayerNorm dbeta partial sums
 #pragma unroll
   for (int k = 0; k < UPT; ++k) {
     const int u = lane + k * TPR;
-    if (u < nunits) {
-      load_gamma<G, E, VEC>(a.gamma, u * E, gam[k]);
-    } else {
+    if constexpr (!LN) {
+      if (u < nunits) {
+        load_gamma<G, E, VEC>(a.gamma, u * E, gam[k]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) gam[k][e] = 0.0f;
+        for (int e = 0; e < E; ++e) gam[k][e] = 0.0f;
+      }
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[k][e] = 0.0f;
@@ -210,8 +264,9 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
       U::widen(cx[k], xv);
       U::widen(cdy[k], dyv);
       if constexpr (LN) {
-        float s1, s2;
-        unit_dots_ln<E>(dyv, gam[k], xv, mu, rho, s1, s2);
+        float s1, s2, g[E];
+        gamma_lds(lane + k * TPR, g);
+        unit_dots_ln<E>(dyv, g, xv, mu, rho, s1, s2);
         dots = dots + DSum2{static_cast<double>(s1), static_cast<double>(s2)};
       } else {
         dot = dot + static_cast<double>(unit_dot<E>(dyv, gam[k], xv));
@@ -243,10 +298,12 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
       U::widen(cx[k], xv);
       U::widen(cdy[k], dyv);
       if constexpr (LN) {
+        float g[E];
+        gamma_lds(u, g);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float xh = (xv[e] - mu) * rho;
-          o[e] = rho * (__builtin_fmaf(-xh, c2, gam[k][e] * dyv[e]) - c1);
+          o[e] = rho * (__builtin_fmaf(-xh, c2, g[e] * dyv[e]) - c1);
           acc[k][e] = __builtin_fmaf(dyv[e], xh, acc[k][e]);
           accb[k][e] = accb[k][e] + dyv[e];
         }
