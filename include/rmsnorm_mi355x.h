@@ -12,7 +12,9 @@
  *     contiguous and row-major ("contiguous 2-D ... row-major rows", FlyDSL guide
  *     section 2.2). The library never allocates, frees or synchronises.
  *   - Work is enqueued on the caller's stream and runs asynchronously; the call
- *     returns once the kernels are launched.
+ *     returns once the kernels are launched. The stream (0 for the null
+ *     stream) must belong to the current HIP device, whose memory the pointers
+ *     refer to.
  *   - Type codes (rmsn_dtype): activations x, r/h, y, dy, dx share x_dtype in
  *     {RMSN_F32, RMSN_F16, RMSN_BF16}; gamma_dtype is x_dtype or RMSN_F32 (fp32
  *     weights with 16-bit activations, FlyDSL guide section 1.2); rstd and
@@ -26,8 +28,10 @@
  *     failed launch returns RMSN_ERR_HIP and rmsnorm_last_hip_error() gives the
  *     hipError_t. Faults during execution surface at the caller's next
  *     synchronisation, as for any asynchronous HIP work.
- *   - Thread safety: the calls keep no state besides the per-thread last HIP
- *     error; concurrent calls on different buffers are safe.
+ *   - Thread safety: besides the per-thread last HIP error the calls keep only
+ *     per-device facts queried on first use (compute-unit count, LDS size per
+ *     workgroup, kernels' dynamic-LDS limits), set idempotently through
+ *     atomics; concurrent calls on different buffers are safe.
  */
 #ifndef RMSNORM_MI355X_H
 #define RMSNORM_MI355X_H
@@ -50,11 +54,13 @@ typedef enum {
 typedef enum {
   RMSN_OK = 0,
   RMSN_ERR_NULL = -1,       /* a required pointer is null */
-  RMSN_ERR_SHAPE = -2,      /* M < 0, N < 1, or M * N too large to index */
+  RMSN_ERR_SHAPE = -2,      /* M < 0, N < 1, M * N too large to index, or a
+                               call's own shape rule (MX: N % 32; QK: strides) */
   RMSN_ERR_DTYPE = -3,      /* unsupported x_dtype / gamma_dtype pair */
   RMSN_ERR_WORKSPACE = -4,  /* backward workspace null or too small */
   RMSN_ERR_OVERLAP = -5,    /* buffers overlap in a way the call forbids */
-  RMSN_ERR_ALIGN = -6,      /* a pointer is not aligned to its element size */
+  RMSN_ERR_ALIGN = -6,      /* a pointer is not aligned to its element size (or
+                               to what a call requires, e.g. MX inputs: 16 B) */
   RMSN_ERR_EPS = -7,        /* eps negative or not finite */
   RMSN_ERR_MODE = -8,       /* unknown quantisation mode */
   RMSN_ERR_HIP = -100       /* a kernel launch failed; see rmsnorm_last_hip_error */

@@ -475,11 +475,14 @@ const char* rmsnorm_status_string(int status) {
   switch (status) {
     case RMSN_OK: return "ok";
     case RMSN_ERR_NULL: return "a required pointer is null";
-    case RMSN_ERR_SHAPE: return "unsupported shape (M < 0, N < 1, or too large)";
+    case RMSN_ERR_SHAPE:
+      return "unsupported shape (a negative or zero size, too large, a stride shorter than "
+             "its heads, or N not a multiple of 32 for an MX output)";
     case RMSN_ERR_DTYPE: return "unsupported dtype combination";
     case RMSN_ERR_WORKSPACE: return "workspace missing or too small";
     case RMSN_ERR_OVERLAP: return "buffers overlap in a forbidden way";
-    case RMSN_ERR_ALIGN: return "pointer not aligned to its element size";
+    case RMSN_ERR_ALIGN:
+      return "pointer misaligned (every pointer to its element size; MX inputs to 16 bytes)";
     case RMSN_ERR_EPS: return "eps must be finite and non-negative";
     case RMSN_ERR_MODE: return "unknown quantisation mode";
     case RMSN_ERR_HIP: return "HIP kernel launch failed";
