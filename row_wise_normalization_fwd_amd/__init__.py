@@ -98,11 +98,14 @@ def load_library(path: str | None = None):
 
 
 def _p(v):
-    """Pointer argument: None, an int address, or a tensor's data_ptr()."""
+    """Pointer argument: None, an int address, or a device tensor's
+    data_ptr(). A host tensor is refused: its address would reach the GPU."""
     if v is None:
         return None
     if isinstance(v, int):
         return v or None
+    if getattr(v, "is_cuda", True) is False:
+        raise ValueError(f"a host tensor ({v.device}) was passed where device memory is required")
     return v.data_ptr() or None
 
 
@@ -197,9 +200,33 @@ def dtype_code(t) -> int:
 def _rows(t, N):
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
-    if t.shape[-1] != N:
-        raise ValueError(f"last dimension {t.shape[-1]} != N = {N}")
+    if t.dim() < 1 or t.shape[-1] != N:
+        raise ValueError(f"last dimension {tuple(t.shape)[-1:]} != N = {N}")
     return t.numel() // N
+
+
+def _args(like, *specs):
+    """Check the tensors a convenience hands to the library before any call:
+    each spec is (tensor or None, name, numel or None, dtype or None). Every
+    tensor must be contiguous, hold the stated number of elements and dtype,
+    and sit on ``like``'s device (a GPU)."""
+    for t, name, numel, dtype in specs:
+        if t is None:
+            continue
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+        if numel is not None and t.numel() != numel:
+            raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    for t, name, _, _ in specs:
+        if t is not None and (t.device != like.device or not t.is_cuda):
+            raise ValueError(f"{name}: on {t.device}; every tensor must be on the same GPU "
+                             f"(x is on {like.device})")
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
 
 
 def _check(status, where):
@@ -213,6 +240,8 @@ def fwd(x, gamma, eps: float = 1e-5, *, want_rstd: bool = False, out=None, rstd=
     import torch
     N = gamma.numel()
     M = _rows(x, N)
+    _args(x, (x, "x", None, None), (gamma, "gamma", N, None), (out, "out", M * N, x.dtype),
+          (rstd, "rstd", M, torch.float32))
     y = torch.empty_like(x) if out is None else out
     if want_rstd and rstd is None:
         rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
@@ -230,6 +259,8 @@ def fused_add_fwd(x, residual, gamma, eps: float = 1e-5, *, want_rstd: bool = Fa
     M = _rows(x, N)
     if residual.shape != x.shape or residual.dtype != x.dtype:
         raise ValueError("residual must match x in shape and dtype")
+    _args(x, (x, "x", None, None), (residual, "residual", M * N, x.dtype),
+          (gamma, "gamma", N, None), (out, "out", M * N, x.dtype), (rstd, "rstd", M, torch.float32))
     y = torch.empty_like(x) if out is None else out
     if want_rstd and rstd is None:
         rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
@@ -250,6 +281,9 @@ def quant_fwd(x, gamma, eps: float = 1e-5, *, scale=None, residual=None, want_rs
     M = _rows(x, N)
     if residual is not None and (residual.shape != x.shape or residual.dtype != x.dtype):
         raise ValueError("residual must match x in shape and dtype")
+    _args(x, (x, "x", None, None), (residual, "residual", M * N, x.dtype),
+          (gamma, "gamma", N, None), (out, "out", M * N, torch.uint8),
+          (scale, "scale", 1, torch.float32), (rstd, "rstd", M, torch.float32))
     q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
     mode = RMSN_QUANT_FP8_TENSOR if scale is not None else RMSN_QUANT_FP8_ROW
     if scale is None:
@@ -279,6 +313,13 @@ def qk_fwd(q, k, q_gamma, k_gamma=None, eps: float = 1e-6, *, stream=None):
         Tk, Hk, Dk, sk = layout(k, "k")
         if (Tk, Dk) != (T, D) or k.dtype != q.dtype:
             raise ValueError("k must match q in tokens, head_dim and dtype")
+        if k_gamma is None:
+            raise ValueError("k_gamma is required with k")
+    for t, name in ((q, "q"), (k, "k")):
+        if t is not None and (t.device != q.device or not t.is_cuda):
+            raise ValueError(f"{name}: on {t.device}; q and k must be on the same GPU")
+    _args(q, (q_gamma, "q_gamma", D, None),
+          (k_gamma if k is not None else None, "k_gamma", D, q_gamma.dtype))
     stream = torch.cuda.current_stream(q.device) if stream is None else stream
     _check(rmsnorm_qk_fwd(q, k, q_gamma, k_gamma if k is not None else None, T, Hq, Hk, D, sq, sk,
                           eps, dtype_code(q), dtype_code(q_gamma), stream), "rmsnorm_qk_fwd")
@@ -292,6 +333,8 @@ def layernorm(x, gamma, beta=None, eps: float = 1e-5, *, want_stats: bool = Fals
     import torch
     N = gamma.numel()
     M = _rows(x, N)
+    _args(x, (x, "x", None, None), (gamma, "gamma", N, None), (beta, "beta", N, gamma.dtype),
+          (out, "out", M * N, x.dtype))
     y = torch.empty_like(x) if out is None else out
     mean = rstd = None
     if want_stats:
@@ -312,6 +355,8 @@ def mx_quant_fwd(x, gamma, eps: float = 1e-5, *, fp4: bool = False, residual=Non
     M = _rows(x, N)
     if residual is not None and (residual.shape != x.shape or residual.dtype != x.dtype):
         raise ValueError("residual must match x in shape and dtype")
+    _args(x, (x, "x", None, None), (residual, "residual", M * N, x.dtype),
+          (gamma, "gamma", N, None))
     qshape = x.shape[:-1] + ((N // 2,) if fp4 else (N,))
     q = torch.empty(qshape, dtype=torch.uint8, device=x.device)
     scale = torch.empty(x.shape[:-1] + (N // 32,), dtype=torch.uint8, device=x.device)
@@ -330,13 +375,16 @@ def bwd(dy, x, rstd, gamma, *, dx=None, dgamma=None, workspace=None, stream=None
     M = _rows(x, N)
     if dy.shape != x.shape or dy.dtype != x.dtype:
         raise ValueError("dy must match x in shape and dtype")
+    _args(x, (x, "x", None, None), (dy, "dy", M * N, x.dtype), (rstd, "rstd", M, torch.float32),
+          (gamma, "gamma", N, None), (dx, "dx", M * N, x.dtype),
+          (dgamma, "dgamma", N, torch.float32), (workspace, "workspace", None, None))
     dx = torch.empty_like(x) if dx is None else dx
     dgamma = torch.empty(N, dtype=torch.float32, device=x.device) if dgamma is None else dgamma
     ws_bytes = rmsnorm_bwd_workspace_size(M, N, dtype_code(x))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     stream = torch.cuda.current_stream(x.device) if stream is None else stream
-    _check(rmsnorm_bwd(dy, x, rstd, gamma, dx, dgamma, workspace, workspace.numel(), M, N,
+    _check(rmsnorm_bwd(dy, x, rstd, gamma, dx, dgamma, workspace, _nbytes(workspace), M, N,
                        dtype_code(x), dtype_code(gamma), stream), "rmsnorm_bwd")
     return dx, dgamma
 
@@ -351,6 +399,10 @@ def fused_add_bwd(dy, h, rstd, gamma, dresidual=None, *, dh=None, dgamma=None, w
     for t in (dy, dresidual):
         if t is not None and (t.shape != h.shape or t.dtype != h.dtype):
             raise ValueError("dy / dresidual must match h in shape and dtype")
+    _args(h, (h, "h", None, None), (dy, "dy", M * N, h.dtype), (rstd, "rstd", M, torch.float32),
+          (gamma, "gamma", N, None), (dresidual, "dresidual", M * N, h.dtype),
+          (dh, "dh", M * N, h.dtype), (dgamma, "dgamma", N, torch.float32),
+          (workspace, "workspace", None, None))
     dh = torch.empty_like(h) if dh is None else dh
     dgamma = torch.empty(N, dtype=torch.float32, device=h.device) if dgamma is None else dgamma
     ws_bytes = rmsnorm_bwd_workspace_size(M, N, dtype_code(h))
@@ -358,7 +410,7 @@ def fused_add_bwd(dy, h, rstd, gamma, dresidual=None, *, dh=None, dgamma=None, w
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=h.device)
     stream = torch.cuda.current_stream(h.device) if stream is None else stream
     _check(rmsnorm_fused_add_bwd(dy, h, rstd, gamma, dresidual, dh, dgamma, workspace,
-                                 workspace.numel(), M, N, dtype_code(h), dtype_code(gamma), stream),
+                                 _nbytes(workspace), M, N, dtype_code(h), dtype_code(gamma), stream),
            "rmsnorm_fused_add_bwd")
     return dh, dgamma
 
@@ -372,6 +424,9 @@ def layernorm_backward(dy, x, mean, rstd, gamma, *, want_dbeta: bool = True, dx=
     M = _rows(x, N)
     if dy.shape != x.shape or dy.dtype != x.dtype:
         raise ValueError("dy must match x in shape and dtype")
+    _args(x, (x, "x", None, None), (dy, "dy", M * N, x.dtype), (mean, "mean", M, torch.float32),
+          (rstd, "rstd", M, torch.float32), (gamma, "gamma", N, None),
+          (dx, "dx", M * N, x.dtype), (workspace, "workspace", None, None))
     dx = torch.empty_like(x) if dx is None else dx
     dgamma = torch.empty(N, dtype=torch.float32, device=x.device)
     dbeta = torch.empty(N, dtype=torch.float32, device=x.device) if want_dbeta else None
@@ -380,6 +435,6 @@ def layernorm_backward(dy, x, mean, rstd, gamma, *, want_dbeta: bool = True, dx=
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     stream = torch.cuda.current_stream(x.device) if stream is None else stream
     _check(layernorm_bwd(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, workspace,
-                         workspace.numel(), M, N, dtype_code(x), dtype_code(gamma), stream),
+                         _nbytes(workspace), M, N, dtype_code(x), dtype_code(gamma), stream),
            "layernorm_bwd")
     return dx, dgamma, dbeta

@@ -304,3 +304,55 @@ def test_mx_quant_validation(lib):
     assert quant(mode=MX4, q=C + 2) == ALIGN          # 4-byte fp4 units
     assert quant(mode=MX4, sc=C + 64 * 128 - 1) == OVERLAP   # scale codes over q's last byte
     assert quant(mode=MX8, sc=A + 8) == OVERLAP       # codes written over x
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError, match="host tensor"):
+        R._p(torch.zeros(2))
+    x, g = torch.zeros(4, 8), torch.ones(8)
+    with pytest.raises(ValueError, match="same GPU"):
+        R.fwd(x, g)
+    with pytest.raises(ValueError, match="same GPU"):
+        R.layernorm(x, g)
+    with pytest.raises(ValueError, match="same GPU"):
+        R.bwd(torch.zeros(4, 8), x, torch.zeros(4), g)
+
+
+def test_conveniences_check_sizes_dtypes_and_layout_before_any_call():
+    """Every tensor a convenience passes on is checked for its element count,
+    dtype and contiguity first (a short out, rstd or dgamma would be written
+    past its end by the kernels; a strided one would be read wrongly)."""
+    torch = pytest.importorskip("torch")
+    x, g = torch.zeros(4, 8), torch.ones(8)
+    with pytest.raises(ValueError, match="out: 24 elements, expected 32"):
+        R.fwd(x, g, out=torch.zeros(3, 8))
+    with pytest.raises(ValueError, match="rstd: 3 elements, expected 4"):
+        R.fwd(x, g, want_rstd=True, rstd=torch.zeros(3))
+    with pytest.raises(TypeError, match="rstd: dtype"):
+        R.fwd(x, g, want_rstd=True, rstd=torch.zeros(4, dtype=torch.float64))
+    with pytest.raises(ValueError, match="gamma: must be contiguous"):
+        R.fwd(x, torch.ones(16)[::2])
+    with pytest.raises(ValueError, match="dgamma: 7 elements"):
+        R.bwd(torch.zeros(4, 8), x, torch.zeros(4), g, dgamma=torch.zeros(7))
+    with pytest.raises(ValueError, match="dy: must be contiguous"):
+        R.bwd(torch.zeros(8, 4).t(), x, torch.zeros(4), g)
+    with pytest.raises(ValueError, match="mean: 5 elements"):
+        R.layernorm_backward(torch.zeros(4, 8), x, torch.zeros(5), torch.zeros(4), g)
+    with pytest.raises(ValueError, match="beta: 9 elements"):
+        R.layernorm(x, g, torch.zeros(9))
+    with pytest.raises(ValueError, match="residual: must be contiguous"):
+        R.fused_add_fwd(x, torch.zeros(8, 4).t(), g)
+    with pytest.raises(ValueError, match="scale: 2 elements"):
+        R.quant_fwd(x, g, scale=torch.ones(2))
+    q = torch.zeros(2, 3, 8)
+    with pytest.raises(ValueError, match="k_gamma is required"):
+        R.qk_fwd(q, torch.zeros(2, 1, 8), torch.ones(8))
+    with pytest.raises(ValueError, match="same GPU"):
+        R.qk_fwd(q, None, torch.ones(8))
+
+
+def test_workspace_bytes_count_the_element_size():
+    torch = pytest.importorskip("torch")
+    assert R._nbytes(torch.empty(10, dtype=torch.float32)) == 40
+    assert R._nbytes(torch.empty(10, dtype=torch.uint8)) == 10
