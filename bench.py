@@ -27,7 +27,14 @@ Also reported, in the same JSON line:
                 MXFP4 outputs at the headline shape, the per-head
                 QK-norm on a fused q/k/v buffer, LayerNorm at the headline
                 shape and the LayerNorm backward at the backward's shape;
-  calibration   a plain device-to-device copy of the step's byte count.
+  hot_cache_gbps  the same step without rotation (inputs in the Infinity
+                Cache): context, never the value;
+  rounds        five more timing rounds of the step (>= 20 ms each after a
+                50 ms warm-up, 1 s cool-down): median / min / mean us, spread;
+  calibration   plain copies of the step's byte count: torch's device-to-device
+                copy, and a 16-byte non-temporal copy kernel
+                (librmsn_copy16.so, the practical ceiling for equal read and
+                write bytes), with value / copy16.
 """
 
 from __future__ import annotations
@@ -270,6 +277,59 @@ def copy_calibration(nbytes: int, rotate_bytes: float, steps: int = 200) -> floa
     return 2 * half / (ms * 1e-3) / 1e9
 
 
+def copy16_calibration(nbytes: int, rotate_bytes: float, steps: int = 200):
+    """GB/s of the 16-byte non-temporal copy kernel (librmsn_copy16.so) moving
+    nbytes (read + write) per step over rotated buffers laid out like the
+    workloads' (one [R, bytes] allocation per operand); None if not built."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "row_wise_normalization_fwd_amd", "librmsn_copy16.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.rmsn_calib_copy16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_void_p]
+    lib.rmsn_calib_copy16.restype = ctypes.c_int
+    half = (nbytes // 2) // 16 * 16
+    reps = max(1, int(-(-rotate_bytes // (2 * half))))
+    src = torch.ones((reps, half), dtype=torch.uint8, device="cuda")
+    dst = torch.empty((reps, half), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    ptrs = [(src[i].data_ptr(), dst[i].data_ptr()) for i in range(reps)]
+
+    def step(i):
+        s_, d_ = ptrs[i % reps]
+        if lib.rmsn_calib_copy16(s_, d_, half, stream) != 0:
+            raise RuntimeError("copy16 calibration launch failed")
+    ms = time_steps(step, steps, 20)
+    ok = torch.equal(dst[0][:4096], src[0][:4096])
+    del src, dst
+    if not ok:
+        raise RuntimeError("copy16 calibration copied wrong bytes")
+    return 2 * half / (ms * 1e-3) / 1e9
+
+
+def rounds(step, ms_per_step: float, n: int = 5, cooldown_s: float = 1.0, start: int = 0):
+    """n further timing rounds of the same step, each >= 20 ms of back-to-back
+    launches after a >= 50 ms warm-up, with a cool-down before each round:
+    median, min and mean microseconds per step and the spread."""
+    import statistics
+    k = max(50, int(0.020 / (ms_per_step * 1e-3)) + 1)
+    warm = max(10, int(0.050 / (ms_per_step * 1e-3)) + 1)
+    us = []
+    i = start
+    for r in range(n):
+        time.sleep(cooldown_s)
+        us.append(1e3 * time_steps(lambda j: step(i + j), k, warm if r == 0 else 10))
+        i += k + warm
+    med = statistics.median(us)
+    return {"rounds": n, "steps_per_round": k, "cooldown_s": cooldown_s,
+            "us_median": round(med, 3), "us_min": round(min(us), 3),
+            "us_mean": round(statistics.fmean(us), 3),
+            "spread_pct": round(100 * (max(us) - min(us)) / med, 2)}
+
+
 def load_traffic(workload: str, src_hash: str):
     """Measured HBM bytes per launch from the committed counter summary, if it
     was taken on the current kernel sources."""
@@ -357,6 +417,9 @@ def main() -> int:
     ap.add_argument("--no-others", action="store_true", help="time only the headline workload")
     ap.add_argument("--other-steps", type=int, default=0,
                     help="steps per other workload (default: enough for ~50 ms each)")
+    ap.add_argument("--rounds", type=int, default=5,
+                    help="extra timing rounds of the headline step (>= 20 ms each, 1 s "
+                         "cool-down) for median / min / mean / spread; 0 skips them")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -381,10 +444,13 @@ def main() -> int:
     ms = time_steps(run.step, args.steps, args.warmup)
     nbytes = w.algorithmic_bytes()
     gbps = nbytes / (ms * 1e-3) / 1e9
+    round_stats = (rounds(run.step, ms, n=args.rounds, start=args.steps + args.warmup)
+                   if args.rounds > 0 else None)
     hot = Runner(w, 0, host)
     hot_ms = time_steps(hot.step, max(args.steps // 2, 10), max(args.warmup // 2, 5))
     del hot
     calib = copy_calibration(2 * w.M * w.N * w.esize, args.rotate_bytes)
+    calib16 = copy16_calibration(2 * w.M * w.N * w.esize, args.rotate_bytes)
 
     result = {
         "metric": "achieved HBM GB/s (% of MI355X peak) and rows/s, RMSNorm fwd/bwd",
@@ -411,8 +477,14 @@ def main() -> int:
                      "kernel": DOMINANT_KERNEL.get(w.name, w.kind),
                      "kernel_src_hash": src_hash},
         "hot_cache_gbps": round(nbytes / (hot_ms * 1e-3) / 1e9, 2),
-        "calibration": {"copy_gbps": round(calib, 2), "what": "torch device-to-device copy, "
-                        "same read+write bytes, rotated"},
+        "rounds": round_stats,
+        "calibration": {
+            "copy_gbps": round(calib, 2),
+            "what": "torch device-to-device copy, same read+write bytes, rotated",
+            "copy16_gbps": round(calib16, 2) if calib16 else None,
+            "copy16_what": "16-byte non-temporal copy kernel (librmsn_copy16.so), same read+"
+                           "write bytes, rotated, one allocation per operand",
+            "value_over_copy16": round(gbps / calib16, 4) if calib16 else None},
     }
     del run
     torch.cuda.empty_cache()

@@ -1,4 +1,6 @@
-"""Build librmsnorm_mi355x.so (HIP kernels for gfx950 + the C ABI) in place.
+"""Build librmsnorm_mi355x.so (HIP kernels for gfx950 + the C ABI) in place,
+and librmsn_copy16.so, the benchmark's 16-byte copy kernel (a measurement
+helper outside the normalisation ABI).
 
 Each translation unit is compiled with hipcc in parallel, then linked into a
 shared library next to this file. Usable as a script:
@@ -23,6 +25,10 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["api.cpp", "fwd_f32.hip", "fwd_f16.hip", "fwd_bf16.hip", "fwd_quant_f32.hip",
            "fwd_quant_f16.hip", "fwd_quant_bf16.hip", "ln_fwd_f32.hip", "ln_fwd_f16.hip",
            "ln_fwd_bf16.hip", "qk.hip", "bwd.hip", "ln_bwd.hip"]
+
+CALIB_SOURCES = ["calib_copy.hip"]
+CALIB_LIB_NAME = "librmsn_copy16.so"
+CALIB_LIB_PATH = os.path.join(HERE, CALIB_LIB_NAME)
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -56,19 +62,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
-    with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
-        objs = list(pool.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError(f"link failed for {os.path.basename(path)}:\n{res.stderr}")
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + CALIB_SOURCES
+    jobs = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+        objs = dict(zip(srcs, pool.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB_PATH)
+    _link([objs[s] for s in CALIB_SOURCES], CALIB_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {CALIB_LIB_PATH}")
     return LIB_PATH
 
 

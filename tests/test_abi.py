@@ -356,3 +356,21 @@ def test_workspace_bytes_count_the_element_size():
     torch = pytest.importorskip("torch")
     assert R._nbytes(torch.empty(10, dtype=torch.float32)) == 40
     assert R._nbytes(torch.empty(10, dtype=torch.uint8)) == 10
+
+
+def test_copy16_calibration_library_checks_arguments_on_the_host():
+    """The benchmark's copy kernel library (not part of the normalisation ABI)
+    loads and rejects bad arguments before any HIP call."""
+    import ctypes
+    path = os.path.join(ROOT, "row_wise_normalization_fwd_amd", "librmsn_copy16.so")
+    if not os.path.exists(path):
+        pytest.skip("librmsn_copy16.so not built")
+    lib = ctypes.CDLL(path)
+    f = lib.rmsn_calib_copy16
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(A, B, 0, None) == 0              # nothing to copy: no launch
+    assert f(A, B, 15, None) == -1            # not a multiple of 16
+    assert f(A + 8, B, 16, None) == -1        # misaligned source
+    assert f(A, A + 16, 64, None) == -1       # overlapping
+    assert f(None, B, 16, None) == -1
