@@ -402,7 +402,20 @@ def cpu_baseline(w, host_inputs: dict, seconds: float) -> dict:
             "cores": 1, "kind": "oracle",
             "sample": f"{passes} full passes over the {M}x{N} batch ({el:.1f} s, single thread,"
                       f" host has {os.cpu_count()} logical CPUs)",
-            "rows_per_s": round(M * passes / el, 1)}
+            "rows_per_s": round(M * passes / el, 1),
+            "ms_per_pass": round(1e3 * el / passes, 3),
+            "host_cpu": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main() -> int:
