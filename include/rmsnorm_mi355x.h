@@ -157,7 +157,7 @@ int rmsnorm_quant_fwd(const void* x, void* residual, const void* gamma, void* q,
  *              Elements between windows are not touched.
  *   q_gamma, k_gamma  [head_dim] gamma_dtype, read.
  *   tokens >= 0, q_heads >= 1, k_heads >= 0, 1 <= head_dim <= 8192, and
- *   tokens * heads below 2^31 for each tensor (else RMSN_ERR_SHAPE). */
+ *   tokens * (q_heads + k_heads) below 2^31 (else RMSN_ERR_SHAPE). */
 int rmsnorm_qk_fwd(void* q, void* k, const void* q_gamma, const void* k_gamma,
                    int64_t tokens, int64_t q_heads, int64_t k_heads, int64_t head_dim,
                    int64_t q_stride, int64_t k_stride, float eps, int x_dtype,

@@ -205,7 +205,8 @@ int qk_forward(void* q, void* k, const void* q_gamma, const void* k_gamma, int64
     return RMSN_ERR_SHAPE;
   if (q_stride < q_heads * head_dim || (k_heads > 0 && k_stride < k_heads * head_dim))
     return RMSN_ERR_SHAPE;
-  if (tokens > INT32_MAX / q_heads || (k_heads > 0 && tokens > INT32_MAX / k_heads))
+  // Head rows (tokens * all heads) are indexed in 32 bits on the device.
+  if (q_heads > INT32_MAX - k_heads || tokens > INT32_MAX / (q_heads + k_heads))
     return RMSN_ERR_SHAPE;
   const int es = esize_of(x_dtype), gs = esize_of(gamma_dtype);
   // Spans must be addressable.

@@ -13,17 +13,13 @@ namespace {
 template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK>
 hipError_t run_qk(QKArgs<T, G> a, hipStream_t s) {
   constexpr int RPB = BLOCK / TPR;
-  // Blocks per tensor, each capped so the grid stays within kMaxGrid (the
-  // kernel strides over the rest).
-  auto blocks_for = [](uint32_t rows) -> int64_t {
-    const int64_t b = ceil_div(rows, RPB);
-    return b < kMaxGrid / 2 ? b : kMaxGrid / 2;
-  };
-  const int64_t b0 = blocks_for(a.rows[0]), b1 = blocks_for(a.rows[1]);
-  a.blocks0 = static_cast<uint32_t>(b0);
-  if (b0 + b1 == 0) return hipSuccess;
+  // One row group per head row, capped at kMaxGrid (the kernel strides over
+  // the rest).
+  int64_t blocks = ceil_div(a.rows, RPB);
+  if (blocks > kMaxGrid) blocks = kMaxGrid;
+  if (blocks == 0) return hipSuccess;
   qk_norm_kernel<T, G, VEC, TPR, UPT, BLOCK>
-      <<<dim3(static_cast<unsigned>(b0 + b1)), dim3(BLOCK), 0, s>>>(a);
+      <<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -32,15 +28,15 @@ hipError_t qk_typed(const QKCall& c) {
   QKArgs<T, G> a;
   bool vec = (c.N * T::kSize) % 16 == 0;
   for (int i = 0; i < 2; ++i) {
+    const bool present = c.x[i] != nullptr && c.heads[i] > 0;
     a.x[i] = static_cast<typename T::S*>(c.x[i]);
     a.gamma[i] = static_cast<const typename G::S*>(c.gamma[i]);
     a.stride[i] = c.stride[i];
-    a.heads[i] = static_cast<uint32_t>(c.heads[i]);
-    a.rows[i] = static_cast<uint32_t>(c.x[i] ? c.tokens * c.heads[i] : 0);
-    if (a.rows[i] != 0)
+    a.heads[i] = present ? static_cast<uint32_t>(c.heads[i]) : 0u;
+    if (present)
       vec = vec && aligned16(c.x[i]) && aligned16(c.gamma[i]) && (c.stride[i] * T::kSize) % 16 == 0;
   }
-  a.blocks0 = 0;
+  a.rows = static_cast<uint32_t>(c.tokens * (a.heads[0] + a.heads[1]));
   a.N = static_cast<int>(c.N);
   a.eps = c.eps;
   hipStream_t s = c.stream;

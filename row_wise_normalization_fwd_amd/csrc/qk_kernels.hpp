@@ -7,10 +7,15 @@
 //
 // Rows are short (64-256 elements in practice), so a group of TPR lanes owns
 // a row and a block holds BLOCK / TPR rows, as in the register forward path;
-// the reduction stays inside a wave for TPR <= 64. The first `blocks0` blocks
-// serve q and the rest k, so each block sees one tensor and loads its gamma
-// once. Row r of a tensor is token r / heads, head r % heads (32-bit
-// arithmetic: the host keeps tokens * heads below 2^31).
+// the reduction stays inside a wave for TPR <= 64. Rows walk each token's q
+// heads and then its k heads (row r: token r / H, head r % H over the
+// H = q_heads + k_heads heads, the first q_heads of them q), so in a fused
+// projection buffer every token's q and k windows are read and written as
+// one contiguous stretch (4096-token bf16 probe, 32 + 8 heads of 128: 57.4 us
+// against 61.6 us when all q rows came first and all k rows after them).
+// Each row group selects its tensor, stride and gamma per row; both gammas
+// stay in registers. Row arithmetic is 32-bit: the host keeps tokens * H
+// below 2^31.
 #pragma once
 
 #include "device.hpp"
@@ -19,12 +24,11 @@ namespace rmsn {
 
 template <class T, class G>
 struct QKArgs {
-  typename T::S* x[2];            // q, k: token 0, head 0
+  typename T::S* x[2];            // q, k: token 0, head 0 (k null when absent)
   const typename G::S* gamma[2];
   int64_t stride[2];              // elements between consecutive tokens
-  uint32_t heads[2];
-  uint32_t rows[2];               // tokens * heads (0: tensor absent)
-  uint32_t blocks0;               // blocks serving q; the rest serve k
+  uint32_t heads[2];              // q_heads, k_heads (0: no k)
+  uint32_t rows;                  // tokens * (q_heads + k_heads)
   int N;                          // head_dim
   float eps;
 };
@@ -37,41 +41,42 @@ __global__ __launch_bounds__(BLOCK) void qk_norm_kernel(QKArgs<T, G> a) {
   static_assert(BLOCK % TPR == 0 && BLOCK % kWave == 0, "block shape");
   __shared__ float red[2 * (BLOCK / kWave)];
 
-  // Block-uniform choice of the tensor.
-  const int sg = blockIdx.x < a.blocks0 ? 0 : 1;
-  const uint32_t b = sg ? blockIdx.x - a.blocks0 : blockIdx.x;
-  const uint32_t nb = sg ? gridDim.x - a.blocks0 : a.blocks0;
-  typename T::S* const x = a.x[sg];
-  const typename G::S* const gamma = a.gamma[sg];
-  const int64_t stride = a.stride[sg];
-  const uint32_t heads = a.heads[sg];
-  const uint32_t rows = a.rows[sg];
-
   const int nunits = a.N / E;
   const int grp = threadIdx.x / TPR;
   const int lane = threadIdx.x % TPR;
+  const uint32_t hq = a.heads[0];
+  const uint32_t H = hq + a.heads[1];
 
-  float gam[UPT][E];
+  float gq[UPT][E], gk[UPT][E];
 #pragma unroll
   for (int k = 0; k < UPT; ++k) {
     const int u = lane + k * TPR;
     if (u < nunits) {
-      load_gamma<G, E, VEC>(gamma, u * E, gam[k]);
+      load_gamma<G, E, VEC>(a.gamma[0], u * E, gq[k]);
+      if (a.heads[1] > 0) {
+        load_gamma<G, E, VEC>(a.gamma[1], u * E, gk[k]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) gk[k][e] = 0.0f;
+      }
     } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) gam[k][e] = 0.0f;
+      for (int e = 0; e < E; ++e) gq[k][e] = gk[k][e] = 0.0f;
     }
   }
 
   int parity = 0;
   // `base` is uniform over the block: every thread reaches every reduction.
-  for (uint64_t base = static_cast<uint64_t>(b) * RPB; base < rows;
-       base += static_cast<uint64_t>(nb) * RPB) {
+  for (uint64_t base = static_cast<uint64_t>(blockIdx.x) * RPB; base < a.rows;
+       base += static_cast<uint64_t>(gridDim.x) * RPB) {
     const uint32_t row = static_cast<uint32_t>(base) + grp;
-    const bool valid = base + grp < rows;
-    const uint32_t t = valid ? row / heads : 0;
-    const uint32_t h = valid ? row - t * heads : 0;
-    const int64_t off = static_cast<int64_t>(t) * stride + static_cast<int64_t>(h) * a.N;
+    const bool valid = base + grp < a.rows;
+    const uint32_t t = valid ? row / H : 0;
+    const uint32_t h = valid ? row - t * H : 0;
+    const bool isk = h >= hq;
+    typename T::S* const x = isk ? a.x[1] : a.x[0];
+    const int64_t off = static_cast<int64_t>(t) * (isk ? a.stride[1] : a.stride[0]) +
+                        static_cast<int64_t>(isk ? h - hq : h) * a.N;
 
     typename U::Raw raw[UPT];
 #pragma unroll
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(BLOCK) void qk_norm_kernel(QKArgs<T, G> a) {
       if (valid && u < nunits) {
         float o[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = v[k][e] * rs * gam[k][e];
+        for (int e = 0; e < E; ++e) o[e] = v[k][e] * rs * (isk ? gk[k][e] : gq[k][e]);
         U::store_nt(x + off + u * E, U::narrow(o));
       }
     }

@@ -221,6 +221,7 @@ def test_qk_validation(lib):
     assert qk(sq=32 * 128 - 1) == SHAPE
     assert qk(sk=8 * 128 - 1) == SHAPE
     assert qk(T=2 ** 26, Hq=32) == SHAPE                 # tokens * heads >= 2^31
+    assert qk(T=2 ** 31 // 40 + 1) == SHAPE             # each tensor fits; q + k rows do not
     assert qk(eps=-1.0) == EPS
     assert qk(T=0, q=None, k=None, gq=None, gk=None) == OK
     assert qk(q=None) == NULL
