@@ -26,7 +26,8 @@ Also reported, in the same JSON line:
                 headline shape; one scale after the fused add), MXFP8 and
                 MXFP4 outputs at the headline shape, the per-head
                 QK-norm on a fused q/k/v buffer, LayerNorm at the headline
-                shape and the LayerNorm backward at the backward's shape;
+                shape and the LayerNorm backward at the backward's shape,
+                and 4 rows of 2^20 bf16 elements (the split path);
   hot_cache_gbps  the same step without rotation (inputs in the Infinity
                 Cache): context, never the value;
   rounds        five more timing rounds of the step (>= 20 ms each after a
@@ -67,6 +68,7 @@ DOMINANT_KERNEL = {
     "qknorm_bf16_t16384_hq32_hk8_d128": "qk_norm_kernel",
     "layernorm_bf16_m4096_n8192": "fwd_pp_kernel",
     "layernorm_bwd_bf16_m8192_n8192": "bwd_stage1_kernel",
+    "fwd_bf16_m4_n1048576_rstd": "fwd_split_apply_kernel",
 }
 DT_NAMES = {0: "f32", 1: "f16", 2: "bf16"}
 

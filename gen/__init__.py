@@ -199,6 +199,9 @@ EXTRA_WORKLOADS = [
              heads_q=32, heads_k=8),
     Workload("layernorm_bf16_m4096_n8192", "ln", 4096, 8192, BF16, BF16, 1e-5, 1010),
     Workload("layernorm_bwd_bf16_m8192_n8192", "ln_bwd", 8192, 8192, BF16, BF16, 1e-5, 1011),
+    # A few very long rows (the forward's split path: 128 tiles per row).
+    Workload("fwd_bf16_m4_n1048576_rstd", "fwd", 4, 1 << 20, BF16, BF16, 1e-5, 1014,
+             store_rstd=True),
 ]
 WORKLOADS_BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 

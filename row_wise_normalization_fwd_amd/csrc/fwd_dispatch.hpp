@@ -23,6 +23,7 @@
 #pragma once
 
 #include "fwd_kernels.hpp"
+#include "fwd_split.hpp"
 #include "launch.hpp"
 
 namespace rmsn {
@@ -64,6 +65,33 @@ hipError_t run_fwd_long(const FwdArgs<T, G>& a, hipStream_t s) {
     if (attr != hipSuccess) return attr;
   }
   kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), lds, s>>>(a);
+  return hipGetLastError();
+}
+
+// Few rows too long for the LDS row cache: partials, finalize, apply (see
+// fwd_split.hpp). Against one block per row at bf16 (one process):
+// 256K-element rows 2.0-2.4x faster up to 16 rows, even at 128; 1M-element
+// rows 3-11x up to 32 rows, 1.5x at 128; 16M-element rows 8-51x. Rows that
+// fit the cache stay with one block per row (the split path's three launches
+// cost ~10 us there against 7-8).
+template <class T, class G, bool FUSED>
+hipError_t run_fwd_split(const FwdArgs<T, G>& f, hipStream_t s) {
+  SplitArgs<T, G> a{f.x, f.residual, f.gamma, f.y, f.rstd, f.M, f.N, f.eps, 0, 0};
+  a.chunks = static_cast<int>(ceil_div(f.N, split_chunk<T>()));
+  a.tiles = f.M * a.chunks;
+  const int64_t blocks = a.tiles < kMaxGrid ? a.tiles : kMaxGrid;
+  fwd_split_partial_kernel<T, G, FUSED>
+      <<<dim3(static_cast<unsigned>(blocks)), dim3(kSplitBlock), 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int64_t fblocks = ceil_div(f.M, kSplitBlock / kWave);
+  if (fblocks > kMaxGrid) fblocks = kMaxGrid;
+  fwd_split_finalize_kernel<T, G>
+      <<<dim3(static_cast<unsigned>(fblocks)), dim3(kSplitBlock), 0, s>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  fwd_split_apply_kernel<T, G, FUSED>
+      <<<dim3(static_cast<unsigned>(blocks)), dim3(kSplitBlock), 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -153,6 +181,11 @@ hipError_t fwd_typed(const FwdCall& c) {
   }
   const int64_t row_bytes = c.N * T::kSize;
   const bool cache = row_bytes <= lds_row_budget();
+  if constexpr (OUT == kOutAct && !LN) {
+    // y holds the split path's partials, so it must not be x itself.
+    if (vec && !cache && (FUSED || c.y != c.x) && c.M <= device_cus() / 2)
+      return run_fwd_split<T, G, FUSED>(a, s);
+  }
   if (vec) {
     if (!cache) return run_fwd_long<T, G, true, 1024, 4, FUSED, false, OUT, LN>(a, s);
     if (row_bytes <= 32 * 1024) return run_fwd_long<T, G, true, 512, 4, FUSED, true, OUT, LN>(a, s);

@@ -99,6 +99,68 @@ def test_fwd_long_rows(pair):
     run_fwd(3, N_REREAD[pair[0]] + 3, *pair, seed=33, misalign=1)  # scalar units, re-read
 
 
+# Few rows too long for the LDS cache take the split path (tiles of 256 lanes x
+# 4 units: 8192 16-bit or 4096 fp32 elements; at most half the CU count of
+# rows). Lengths give full tiles, a one-unit last tile and a partial one.
+SPLIT_N = {O.F32: [45000, 4096 * 24 + 4, 262144], O.F16: [90000, 8192 * 12 + 8, 262144],
+           O.BF16: [90000, 8192 * 12 + 8, 262144]}
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_fwd_split_rows(pair):
+    for i, N in enumerate(SPLIT_N[pair[0]]):
+        run_fwd(1, N, *pair, seed=300 + i, want_rstd=True)
+        run_fwd(9, N, *pair, seed=310 + i, want_rstd=(i % 2 == 0))
+        run_fused(2, N, *pair, seed=320 + i, want_rstd=(i % 2 == 1))
+
+
+def test_fwd_split_boundaries():
+    """Either side of the row-count switch, the in-place fallback, outlier rows."""
+    N = 90000
+    run_fwd(128, N, O.BF16, O.BF16, seed=330, want_rstd=True)   # split (256 CUs)
+    run_fwd(129, N, O.BF16, O.BF16, seed=331, want_rstd=True)   # one block per row
+    run_fwd(4, N, O.BF16, O.BF16, seed=332, inplace=True)       # y == x: one block per row
+    run_fwd(3, N, O.F16, O.F16, seed=333, outlier_every=2, outlier_scale=200.0)
+
+
+def test_fwd_split_graph_replay():
+    """The split path's three launches captured in a graph: every replay,
+    with eager work and other outputs' clearing between replays, equals the
+    eager run bit for bit."""
+    M, N = 3, 8192 * 12 + 8
+    x, g, r, _ = _inputs(M, N, O.BF16, O.BF16, 340, with_r=True)
+    xt, gt, r0 = _put(x, O.BF16), _put(g, O.BF16), _put(r, O.BF16)
+    rt = r0.clone()
+    y, rs = _empty(M * N, O.BF16), torch.empty(M, device="cuda")
+    y2 = _empty(M * N, O.BF16)
+
+    def run(stream):
+        assert R.rmsnorm_fwd(xt, gt, y, rs, M, N, 1e-5, O.BF16, O.BF16, stream) == 0
+        assert R.rmsnorm_fused_add_fwd(xt, rt, gt, y2, None, M, N, 1e-5, O.BF16, O.BF16,
+                                       stream) == 0
+
+    run(_stream())
+    torch.cuda.synchronize()
+    want = [t.cpu().clone() for t in (y, rs, y2, rt)]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        rt.copy_(r0)
+        with torch.cuda.graph(graph, stream=side):
+            run(side)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        rt.copy_(r0)
+        for t in (y, rs, y2):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, w in zip((y, rs, y2, rt), want):
+            assert torch.equal(t.cpu().view(torch.uint8), w.view(torch.uint8)), rep
+
+
 @pytest.mark.parametrize("M", [1, 2, 3, 64, 255, 4097])
 @pytest.mark.parametrize("N", [16, 64, 1000, 8192])
 def test_fwd_row_counts(M, N):
