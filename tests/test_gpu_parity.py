@@ -121,6 +121,10 @@ def test_fwd_split_boundaries():
     run_fwd(129, N, O.BF16, O.BF16, seed=331, want_rstd=True)   # one block per row
     run_fwd(4, N, O.BF16, O.BF16, seed=332, inplace=True)       # y == x: one block per row
     run_fwd(3, N, O.F16, O.F16, seed=333, outlier_every=2, outlier_scale=200.0)
+    # Fused: y may be x (the partial pass parks its sums over x, which the
+    # apply pass no longer reads), and the residual may be x.
+    run_fused(2, N, O.BF16, O.BF16, seed=334, want_rstd=True, y_is_x=True)
+    run_fused(2, N, O.BF16, O.F32, seed=335, x_is_r=True)
 
 
 def test_fwd_split_graph_replay():
@@ -245,8 +249,10 @@ def test_fwd_deterministic():
 
 # --------------------------------------------------------------- fused add
 
-def run_fused(M, N, xdt, gdt, eps=1e-5, seed=11, want_rstd=False, misalign=0, x_is_r=False):
-    _log(f"fused M={M} N={N} x={xdt} g={gdt} misalign={misalign} x_is_r={x_is_r}")
+def run_fused(M, N, xdt, gdt, eps=1e-5, seed=11, want_rstd=False, misalign=0, x_is_r=False,
+              y_is_x=False):
+    _log(f"fused M={M} N={N} x={xdt} g={gdt} misalign={misalign} x_is_r={x_is_r} "
+         f"y_is_x={y_is_x}")
     x, g, r, _ = _inputs(M, N, xdt, gdt, seed, with_r=True)
     if x_is_r:
         r = x.copy()
@@ -254,7 +260,7 @@ def run_fused(M, N, xdt, gdt, eps=1e-5, seed=11, want_rstd=False, misalign=0, x_
     rt = _put(r, xdt, misalign)
     xt = rt if x_is_r else _put(x, xdt, misalign)
     gt = _put(g, gdt)
-    yt = _empty(M * N, xdt, misalign)
+    yt = xt if y_is_x else _empty(M * N, xdt, misalign)
     st_t = torch.empty(M, device="cuda") if want_rstd else None
     st = R.rmsnorm_fused_add_fwd(xt, rt, gt, yt, st_t, M, N, eps, xdt, gdt, _stream())
     assert st == 0, R.rmsnorm_status_string(st)
@@ -292,6 +298,7 @@ def test_fused_long_rows(pair):
 def test_fused_misaligned_and_aliased(pair):
     run_fused(7, 4096, *pair, seed=51, misalign=1)
     run_fused(7, 4096, *pair, seed=52, x_is_r=True)
+    run_fused(7, 4096, *pair, seed=53, y_is_x=True)
 
 
 # ------------------------------------------------- quantised (fp8) forward
