@@ -19,7 +19,8 @@
 // for rows up to 32 KiB, 1024 above (measured at 128 MiB of bf16: 16384-
 // element rows 46 us with 512 threads vs 48 us with 256; 32768 and 65536
 // elements 48-50 us with 1024 threads and 64 / 128 KiB of LDS vs 61-63 us
-// re-reading).
+// re-reading). At most CUs / 2 rows too long for LDS take the split path
+// instead (a block per tile of the row, three launches; fwd_split.hpp).
 #pragma once
 
 #include "fwd_kernels.hpp"
