@@ -78,12 +78,40 @@ def rows_of(w) -> int:
     return w.M * (w.heads_q + w.heads_k) if w.kind == "qk" else w.M
 
 
+def _code_tokens(text: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed, so that
+    editing a comment does not void traffic figures taken on the same code.
+    String and character literals are kept verbatim."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel and ABI sources' code (comments and layout ignored)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "row_wise_normalization_fwd_amd", "csrc")
     for p in sorted(glob.glob(os.path.join(csrc, "*"))):
-        with open(p, "rb") as fh:
-            h.update(os.path.basename(p).encode() + b"\0" + fh.read())
+        with open(p, encoding="utf-8") as fh:
+            code = _code_tokens(fh.read())
+        h.update(os.path.basename(p).encode() + b"\0" + code.encode())
     return h.hexdigest()[:16]
 
 

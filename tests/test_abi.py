@@ -375,3 +375,17 @@ def test_copy16_calibration_library_checks_arguments_on_the_host():
     assert f(A + 8, B, 16, None) == -1        # misaligned source
     assert f(A, A + 16, 64, None) == -1       # overlapping
     assert f(None, B, 16, None) == -1
+
+
+def test_kernel_hash_ignores_comments_and_layout_only():
+    """The bench keys stored traffic figures to the kernel sources' code:
+    comments and whitespace do not change the key, code and literals do."""
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    base = 'int f(int a) {\n  return a + 1;  // add\n}\nconst char* s = "x // y";\n'
+    same = '/* doc */ int f(int a)\n{ return a + 1; }\n// end\nconst char* s = "x // y";'
+    assert bench._code_tokens(base) == bench._code_tokens(same)
+    for changed in (base.replace("+ 1", "+ 2"), base.replace('"x // y"', '"x / y"')):
+        assert bench._code_tokens(base) != bench._code_tokens(changed)
+    assert re.fullmatch(r"[0-9a-f]{16}", bench.kernel_source_hash())
