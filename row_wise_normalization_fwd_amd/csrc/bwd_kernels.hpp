@@ -554,18 +554,43 @@ __global__ __launch_bounds__(kS2Threads) void bwd_stage2_kernel(
   double s[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) s[c] = 0.0;
+  // A thread's partial rows are loaded kPer at a time (all of them when
+  // G <= kPer * SLICES), every load before the first add, so a chunk costs one
+  // memory round trip (the loads are non-temporal: each partial is read once).
+  // A slot past row G loads a valid row and adds 0.0 instead; the running sum
+  // starts at +0.0 and never becomes -0.0, so adding 0.0 changes no bit and
+  // the sum is the one over b in increasing order.
+  constexpr int kPer = 8;
+  typedef float F4 __attribute__((ext_vector_type(4)));
   if (col0 < N) {  // with CPT == 4, N % 4 == 0, so all four columns exist
-#pragma unroll 4
-    for (int b = slice; b < nblocks; b += SLICES) {
-      const float* p = partial + static_cast<int64_t>(b) * N + col0;
+    for (int b0 = slice; b0 < nblocks; b0 += SLICES * kPer) {
       if constexpr (CPT == 4) {
-        const float4 v = *reinterpret_cast<const float4*>(p);
-        s[0] = s[0] + static_cast<double>(v.x);
-        s[1] = s[1] + static_cast<double>(v.y);
-        s[2] = s[2] + static_cast<double>(v.z);
-        s[3] = s[3] + static_cast<double>(v.w);
+        F4 v[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+          const int b = min(b0 + q * SLICES, nblocks - 1);
+          const float* p = partial + static_cast<int64_t>(b) * N + col0;
+          v[q] = __builtin_nontemporal_load(reinterpret_cast<const F4*>(p));
+        }
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+          const bool ok = b0 + q * SLICES < nblocks;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) s[c] = s[c] + (ok ? static_cast<double>(v[q][c]) : 0.0);
+        }
       } else {
-        s[0] = s[0] + static_cast<double>(p[0]);
+        float v[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+          const int b = min(b0 + q * SLICES, nblocks - 1);
+          const float* p = partial + static_cast<int64_t>(b) * N + col0;
+          v[q] = __builtin_nontemporal_load(p);
+        }
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+          const bool ok = b0 + q * SLICES < nblocks;
+          s[0] = s[0] + (ok ? static_cast<double>(v[q]) : 0.0);
+        }
       }
     }
   }
