@@ -799,7 +799,7 @@ def test_bwd_long_rows_misaligned_and_many_rows(pair):
     run_bwd(4, 100000, *pair, seed=603, alias="dy")
 
 
-@pytest.mark.parametrize("M", [1, 255, 256, 257, 1000, 5000])
+@pytest.mark.parametrize("M", [1, 31, 33, 100, 255, 256, 257, 1000, 5000])
 def test_bwd_row_partitions(M):
     run_bwd(M, 512, O.BF16, O.BF16, seed=M)
 
