@@ -27,7 +27,10 @@ Also reported, in the same JSON line:
                 MXFP4 outputs at the headline shape, the per-head
                 QK-norm on a fused q/k/v buffer, LayerNorm at the headline
                 shape and the LayerNorm backward at the backward's shape,
-                and 4 rows of 2^20 bf16 elements (the split path);
+                and 4 rows of 2^20 bf16 elements (the split path); each
+                backward also carries stream_gbps, a reduction-free stream
+                with its reads and writes (2 or 3 inputs per output), and
+                value_over_stream;
   hot_cache_gbps  the same step without rotation (inputs in the Infinity
                 Cache): context, never the value;
   rounds        five more timing rounds of the step (>= 20 ms each after a
@@ -340,6 +343,46 @@ def copy16_calibration(nbytes: int, rotate_bytes: float, steps: int = 200):
     return 2 * half / (ms * 1e-3) / 1e9
 
 
+def stream_calibration(each: int, inputs: int, rotate_bytes: float, steps: int = 200):
+    """GB/s of librmsn_copy16.so's stream kernel reading `inputs` (2 or 3)
+    arrays of `each` bytes and writing one, per step, over rotated buffers laid
+    out like the workloads' (one [R, bytes] allocation per operand); the
+    practical ceiling for the backward's mix of reads and writes. None if the
+    library is not built."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "row_wise_normalization_fwd_amd", "librmsn_copy16.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    lib.rmsn_calib_stream.argtypes = [vp, vp, vp, vp, ctypes.c_int64, vp]
+    lib.rmsn_calib_stream.restype = ctypes.c_int
+    each = each // 16 * 16
+    reps = max(1, int(-(-rotate_bytes // ((inputs + 1) * each))))
+    ins = [torch.randint(0, 256, (reps, each), dtype=torch.uint8, device="cuda")
+           for _ in range(inputs)]
+    dst = torch.empty((reps, each), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    ptrs = [([t[i].data_ptr() for t in ins] + [None] * (3 - inputs), dst[i].data_ptr())
+            for i in range(reps)]
+
+    def step(i):
+        (a, b, c), d = ptrs[i % reps]
+        if lib.rmsn_calib_stream(a, b, c, d, each, stream) != 0:
+            raise RuntimeError("stream calibration launch failed")
+    ms = time_steps(step, steps, 20)
+    want = ins[0][0][:4096] ^ ins[1][0][:4096]
+    if inputs == 3:
+        want = want ^ ins[2][0][:4096]
+    ok = torch.equal(dst[0][:4096], want)
+    del ins, dst
+    if not ok:
+        raise RuntimeError("stream calibration wrote wrong bytes")
+    return (inputs + 1) * each / (ms * 1e-3) / 1e9
+
+
 def rounds(step, ms_per_step: float, n: int = 5, cooldown_s: float = 1.0, start: int = 0):
     """n further timing rounds of the same step, each >= 20 ms of back-to-back
     launches after a >= 50 ms warm-up, with a cool-down before each round:
@@ -551,6 +594,18 @@ def main() -> int:
                 others[ow.name]["workspace_bytes"] = orun.ws_bytes
             del orun, oh
             torch.cuda.empty_cache()
+            if ow.kind in ("bwd", "fused_add_bwd", "ln_bwd"):
+                # The same read and write streams with no arithmetic: two
+                # inputs per output (x, dy -> dx), three for the fused add's.
+                nin = 3 if ow.kind == "fused_add_bwd" else 2
+                sg = stream_calibration(ow.M * ow.N * ow.esize, nin, args.rotate_bytes)
+                if sg is not None:
+                    o = others[ow.name]
+                    o["stream_gbps"] = round(sg, 2)
+                    o["stream_what"] = (f"{nin} reads + 1 write of {ow.M}x{ow.N} {DT_NAMES[ow.x_dt]}, "
+                                        "16-byte non-temporal, rotated (librmsn_copy16.so)")
+                    o["value_over_stream"] = round(o["gbps"] / sg, 4)
+                torch.cuda.empty_cache()
         result["workloads"] = others
 
     if not args.no_cpu:
