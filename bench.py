@@ -30,7 +30,9 @@ Also reported, in the same JSON line:
                 and 4 rows of 2^20 bf16 elements (the split path); each
                 backward also carries stream_gbps, a reduction-free stream
                 with its reads and writes (2 or 3 inputs per output), and
-                value_over_stream;
+                value_over_stream; the launch-bound fp32 64 x 1024 case
+                also carries `graph`, the same call replayed 100 at a time
+                from a captured HIP graph (no host launch per call);
   hot_cache_gbps  the same step without rotation (inputs in the Infinity
                 Cache): context, never the value;
   rounds        five more timing rounds of the step (>= 20 ms each after a
@@ -383,6 +385,35 @@ def stream_calibration(each: int, inputs: int, rotate_bytes: float, steps: int =
     return (inputs + 1) * each / (ms * 1e-3) / 1e9
 
 
+def graph_replay_ms(run, calls: int = 100, replays: int = 40) -> float:
+    """Milliseconds per step when `calls` steps are captured in one HIP graph
+    (torch.cuda.CUDAGraph) and the graph is replayed: the GPU's own rate for a
+    launch-bound step, without a host launch per call."""
+    import torch
+    fn, args = run.calls[0]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        cargs = args[:-1] + (side.cuda_stream,)
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(calls):
+                if fn(*cargs) != 0:
+                    raise RuntimeError("graph capture: launch failed")
+    torch.cuda.current_stream().wait_stream(side)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / (replays * calls)
+
+
 def rounds(step, ms_per_step: float, n: int = 5, cooldown_s: float = 1.0, start: int = 0):
     """n further timing rounds of the same step, each >= 20 ms of back-to-back
     launches after a >= 50 ms warm-up, with a cool-down before each round:
@@ -592,6 +623,14 @@ def main() -> int:
                                "steps": k, "rotation_replicas": orun.replicas}
             if ow.kind in ("bwd", "fused_add_bwd", "ln_bwd"):
                 others[ow.name]["workspace_bytes"] = orun.ws_bytes
+            if ow.M * ow.N < (1 << 20):
+                # Launch-bound: the same call replayed from a captured graph.
+                gms = graph_replay_ms(orun)
+                others[ow.name]["graph"] = {
+                    "calls_per_graph": 100, "ms_per_step": round(gms, 6),
+                    "gbps": round(ob / (gms * 1e-3) / 1e9, 2),
+                    "pct_of_peak": round(100 * ob / (gms * 1e-3) / 1e9 / PEAK_GBPS, 2),
+                    "rows_per_s": round(rows_of(ow) / (gms * 1e-3), 1)}
             del orun, oh
             torch.cuda.empty_cache()
             if ow.kind in ("bwd", "fused_add_bwd", "ln_bwd"):
