@@ -236,6 +236,33 @@ struct Fp8Unit<1> {
   __device__ static void store_nt(uint8_t* p, Raw v) { __builtin_nontemporal_store(v, p); }
 };
 
+// MXFP8 element codes of E (a multiple of 4) values o: o[e] / X for a
+// power-of-two block scale X, as E / 4 words (lowest address in the low
+// byte). Each value is clamped to +-448 X (exact for a power of two), then
+// gfx950's scaled conversion divides by X, rounds to nearest-even and packs
+// two codes. The conversion reads only the exponent of X and does not
+// saturate by itself (|v / X| > 464 gives the NaN code 0x7f), hence the clamp
+// (checked on every e4m3 value, tie and neighbour of a tie, and beyond 448,
+// both signs, at scales 2^-20 to 2^30).
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+template <int E>
+__device__ __forceinline__ void fp8_scaled_words(const float* o, float X, uint32_t* w) {
+  static_assert(E % 4 == 0, "four codes per word");
+  const float lim = kFp8Max * X;
+#pragma unroll
+  for (int e = 0; e < E; e += 4) {
+    s16x2 v = {0, 0};
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, __builtin_amdgcn_fmed3f(o[e], -lim, lim),
+                                                 __builtin_amdgcn_fmed3f(o[e + 1], -lim, lim), X,
+                                                 false);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, __builtin_amdgcn_fmed3f(o[e + 2], -lim, lim),
+                                                 __builtin_amdgcn_fmed3f(o[e + 3], -lim, lim), X,
+                                                 true);
+    w[e / 4] = static_cast<uint32_t>(static_cast<uint16_t>(v[0])) |
+               (static_cast<uint32_t>(static_cast<uint16_t>(v[1])) << 16);
+  }
+}
+
 // --------------------------------------------------------- MX block output
 //
 // MX outputs (OCP Microscaling layout): blocks of 32 consecutive row elements

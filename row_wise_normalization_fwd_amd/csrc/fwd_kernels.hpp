@@ -82,11 +82,24 @@ struct MxUnit {
     for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(o[e]));
     return mx_code(group_max<kLanes>(m), kEmax);
   }
-  // fp8: multiply by 2^(127 - c), clamp, convert; fp4: the scaled conversion
-  // divides by X = 2^(c - 127) itself. Both scalings are exact.
+  // The scaled conversions divide by X = 2^(c - 127) themselves (fp8 after a
+  // clamp to +-448 X); 1-element fp8 units multiply by 2^(127 - c), clamp and
+  // convert. Every scaling is exact. (MXFP8 at 4096 x 8192 bf16: 2.1% faster
+  // with the scaled conversion than multiply, clamp, convert; same codes.)
   __device__ static typename Pack::Raw pack(const float* o, int c) {
-    if constexpr (OUT == kOutMxFp4) return Pack::pack(o, __builtin_ldexpf(1.0f, c - 127));
-    else return Pack::pack(o, __builtin_ldexpf(1.0f, 127 - c));
+    if constexpr (OUT == kOutMxFp4) {
+      return Pack::pack(o, __builtin_ldexpf(1.0f, c - 127));
+    } else if constexpr (E == 8) {
+      uint32_t w[2];
+      fp8_scaled_words<8>(o, __builtin_ldexpf(1.0f, c - 127), w);
+      return (typename Pack::Raw){w[0], w[1]};
+    } else if constexpr (E == 4) {
+      uint32_t w[1];
+      fp8_scaled_words<4>(o, __builtin_ldexpf(1.0f, c - 127), w);
+      return w[0];
+    } else {
+      return Pack::pack(o, __builtin_ldexpf(1.0f, 127 - c));
+    }
   }
 };
 
