@@ -377,6 +377,43 @@ def test_copy16_calibration_library_checks_arguments_on_the_host():
     assert f(None, B, 16, None) == -1
 
 
+def test_stream_calibration_checks_arguments_on_the_host():
+    """The benchmark's backward-ceiling stream (dst = a ^ b (^ c)) rejects bad
+    arguments before any HIP call."""
+    import ctypes
+    path = os.path.join(ROOT, "row_wise_normalization_fwd_amd", "librmsn_copy16.so")
+    if not os.path.exists(path):
+        pytest.skip("librmsn_copy16.so not built")
+    lib = ctypes.CDLL(path)
+    f = lib.rmsn_calib_stream
+    vp = ctypes.c_void_p
+    f.argtypes = [vp, vp, vp, vp, ctypes.c_int64, vp]
+    f.restype = ctypes.c_int
+    assert f(A, B, None, F, 0, None) == 0        # nothing to do: no launch
+    assert f(A, B, E, F, 0, None) == 0
+    assert f(A, B, None, F, 24, None) == -1      # not a multiple of 16
+    assert f(A + 8, B, None, F, 16, None) == -1  # misaligned input
+    assert f(A, B, E + 4, F, 16, None) == -1     # misaligned third input
+    assert f(A, B, None, F + 8, 16, None) == -1  # misaligned output
+    assert f(A, B, None, A + 16, 64, None) == -1  # output overlaps an input
+    assert f(A, B, F, F, 64, None) == -1         # output is the third input
+    assert f(None, B, None, F, 16, None) == -1
+    assert f(A, None, None, F, 16, None) == -1
+    assert f(A, B, None, None, 16, None) == -1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU; asking for more exits with a message before
+    touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+
+
 def test_kernel_hash_ignores_comments_and_layout_only():
     """The bench keys stored traffic figures to the kernel sources' code:
     comments and whitespace do not change the key, code and literals do."""
