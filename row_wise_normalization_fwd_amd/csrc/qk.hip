@@ -18,8 +18,16 @@ hipError_t run_qk(QKArgs<T, G> a, hipStream_t s) {
   int64_t blocks = ceil_div(a.rows, RPB);
   if (blocks > kMaxGrid) blocks = kMaxGrid;
   if (blocks == 0) return hipSuccess;
-  qk_norm_kernel<T, G, VEC, TPR, UPT, BLOCK>
-      <<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), 0, s>>>(a);
+  // Each wave holds kWave / TPR consecutive rows starting at a multiple of
+  // that; when both head counts are multiples of it, a wave's rows are all q
+  // or all k heads of one token.
+  constexpr uint32_t kRpw = TPR <= kWave ? kWave / TPR : 0;
+  if (kRpw != 0 && a.heads[0] % kRpw == 0 && (a.heads[0] + a.heads[1]) % kRpw == 0)
+    qk_norm_kernel<T, G, VEC, TPR, UPT, BLOCK, true>
+        <<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), 0, s>>>(a);
+  else
+    qk_norm_kernel<T, G, VEC, TPR, UPT, BLOCK, false>
+        <<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -37,6 +45,22 @@ hipError_t qk_typed(const QKCall& c) {
       vec = vec && aligned16(c.x[i]) && aligned16(c.gamma[i]) && (c.stride[i] * T::kSize) % 16 == 0;
   }
   a.rows = static_cast<uint32_t>(c.tokens * (a.heads[0] + a.heads[1]));
+  // row / H for rows below 2^31: a shift for a power of two, else
+  // umulhi(row, m) >> (l - 1) with l = ceil(log2 H), m = ceil(2^(31 + l) / H)
+  // (m < 2^32, and the error n (m - 2^(31+l)/H) / 2^(31+l) < 2^-l < 1/H).
+  {
+    const uint64_t H = a.heads[0] + a.heads[1];
+    int l = 0;
+    while ((uint64_t(1) << l) < H) ++l;
+    if ((H & (H - 1)) == 0) {
+      a.hmul = 0u;
+      a.hshift = l;
+    } else {
+      const uint64_t p2 = uint64_t(1) << (31 + l);
+      a.hmul = static_cast<uint32_t>((p2 + H - 1) / H);
+      a.hshift = l - 1;
+    }
+  }
   a.N = static_cast<int>(c.N);
   a.eps = c.eps;
   hipStream_t s = c.stream;
