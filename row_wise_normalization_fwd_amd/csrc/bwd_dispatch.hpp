@@ -103,12 +103,12 @@ hipError_t long_rows_typed(const BwdArgs<T, G>& a, double* cdot, int64_t blocks,
 // partial_bytes are).
 inline hipError_t run_stage2(const float* partial, float* out, const float* partial2,
                              float* out2, const BwdCall& c) {
-  // 32 slices of partial rows, 32 columns per block (8192 x 8192 bf16, stage
-  // 2 after stage 1 in one process: 0.2-0.3 us less than 16 slices, 2 us less
-  // than 64; 4 columns per thread beat 1 and 2). With G <= 256 each thread's
-  // 8 loads go out together: 0.2-0.4% off the whole backward against two
-  // rounds of 4.
-  constexpr int kSlices = 32;
+  // 16 slices of partial rows, 64 columns per block, each thread's 16 loads
+  // issued together (8192 x 8192 bf16, stage 2 after stage 1 in one process:
+  // the RMSNorm, fused-add and LayerNorm backwards 0.5-0.7% faster than 32
+  // slices of 8 loads, 3.5-5% faster than 64 slices; 8 slices no better than
+  // 32; 4 columns per thread beat 1 and 2).
+  constexpr int kSlices = 16;
   constexpr int kGroups = kS2Threads / kSlices;
   const unsigned ny = out2 != nullptr ? 2u : 1u;
   if (c.N % 4 == 0) {

@@ -554,13 +554,14 @@ __global__ __launch_bounds__(kS2Threads) void bwd_stage2_kernel(
   double s[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) s[c] = 0.0;
-  // A thread's partial rows are loaded kPer at a time (all of them when
-  // G <= kPer * SLICES), every load before the first add, so a chunk costs one
-  // memory round trip (the loads are non-temporal: each partial is read once).
+  // A thread's partial rows are loaded kPer = 256 / SLICES at a time (all of
+  // them, since G <= 256), every load before the first add, so a chunk costs
+  // one memory round trip (the loads are non-temporal: each partial is read
+  // once).
   // A slot past row G loads a valid row and adds 0.0 instead; the running sum
   // starts at +0.0 and never becomes -0.0, so adding 0.0 changes no bit and
   // the sum is the one over b in increasing order.
-  constexpr int kPer = 8;
+  constexpr int kPer = (256 + SLICES - 1) / SLICES;
   typedef float F4 __attribute__((ext_vector_type(4)));
   if (col0 < N) {  // with CPT == 4, N % 4 == 0, so all four columns exist
     for (int b0 = slice; b0 < nblocks; b0 += SLICES * kPer) {
