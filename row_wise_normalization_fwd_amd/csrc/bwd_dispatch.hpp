@@ -107,7 +107,8 @@ inline hipError_t run_stage2(const float* partial, float* out, const float* part
   // issued together (8192 x 8192 bf16, stage 2 after stage 1 in one process:
   // the RMSNorm, fused-add and LayerNorm backwards 0.5-0.7% faster than 32
   // slices of 8 loads, 3.5-5% faster than 64 slices; 8 slices no better than
-  // 32; 4 columns per thread beat 1 and 2).
+  // 32; 4 columns per thread beat 1 and 2; 256-thread blocks tie 128 and beat
+  // 512 by 1.3-1.9%).
   constexpr int kSlices = 16;
   constexpr int kGroups = kS2Threads / kSlices;
   const unsigned ny = out2 != nullptr ? 2u : 1u;
