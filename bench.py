@@ -165,10 +165,10 @@ class Runner:
                 mean_bwd = torch.empty(M, dtype=torch.float32, device=dev)
                 st = R.layernorm_fwd(x0, g, None, tmp, mean_bwd, rstd_bwd, M, N, w.eps, w.x_dt,
                                      w.g_dt, stream)
-                self.ws_bytes = R.layernorm_bwd_workspace_size(M, N, w.x_dt)
+                self.ws_bytes = R.layernorm_bwd_workspace_size(M, N)
             else:
                 st = R.rmsnorm_fwd(x0, g, tmp, rstd_bwd, M, N, w.eps, w.x_dt, w.g_dt, stream)
-                self.ws_bytes = R.rmsnorm_bwd_workspace_size(M, N, w.x_dt)
+                self.ws_bytes = R.rmsnorm_bwd_workspace_size(M, N)
             assert st == 0, R.rmsnorm_status_string(st)
             del tmp
             dy0 = dev_copy(host_inputs["dy"], w.x_dt)

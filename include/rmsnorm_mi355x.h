@@ -19,15 +19,30 @@
  *     {RMSN_F32, RMSN_F16, RMSN_BF16}; gamma_dtype is x_dtype or RMSN_F32 (fp32
  *     weights with 16-bit activations, FlyDSL guide section 1.2); rstd and
  *     dgamma are always fp32.
- *   - Shapes: M >= 0 rows, N >= 1 columns. M == 0 is a no-op returning RMSN_OK
+ *   - Shapes: M >= 0 rows, 1 <= N <= RMSN_MAX_N columns (else RMSN_ERR_SHAPE).
+ *     M == 0 is a no-op returning RMSN_OK
  *     (pointers are not inspected). Every pointer must be aligned to its element
  *     size; 16-byte-aligned rows (base aligned and N * element size a multiple
  *     of 16) take the vectorised path, anything else a scalar path.
  *   - Errors: argument errors are detected on the host before any HIP call and
  *     returned as negative rmsn_status codes; nothing is enqueued then. A
  *     failed launch returns RMSN_ERR_HIP and rmsnorm_last_hip_error() gives the
- *     hipError_t. Faults during execution surface at the caller's next
+ *     hipError_t (an error left on the calling thread by an earlier, unrelated
+ *     HIP call is cleared before the launch and never reported as the
+ *     library's). Faults during execution surface at the caller's next
  *     synchronisation, as for any asynchronous HIP work.
+ *   - Input domain: every finite input and every finite eps >= 0. The kernels
+ *     accumulate in fp32; a row whose fp32 statistics leave the range where
+ *     they are exact to rounding -- q = mean(x^2) + eps outside
+ *     [2^-100, FLT_MAX], which takes |x| beyond about 1.8e19, or squares that
+ *     underflow when eps is below 2^-100, or an eps near the fp32 maximum --
+ *     is recomputed in fp64 by the same launch, so results match the fp64
+ *     definition over the whole domain (LayerNorm: the same test on its
+ *     centred sum of squares). eps = 0 with an all-zero row is the
+ *     definition's 0/0: rstd = +inf and y = NaN, as in fp64; quantised codes
+ *     of such a row are unspecified. An element whose exact result is beyond
+ *     the output type's range rounds to +-inf (fp16, bf16, fp32) or saturates
+ *     (fp8, fp4). Inputs holding inf or NaN give unspecified results.
  *   - Thread safety: besides the per-thread last HIP error the calls keep only
  *     per-device facts queried on first use (compute-unit count, LDS size per
  *     workgroup, kernels' dynamic-LDS limits), set idempotently through
@@ -44,6 +59,9 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Largest row length N accepted (2^31 - 2^20). */
+#define RMSN_MAX_N 2146435072
 
 typedef enum {
   RMSN_F32 = 0,
@@ -107,8 +125,9 @@ typedef enum {
  * quantised output. The pages name these variants ("TIRx kernels", FlashInfer
  * ports, flashinfer.norm: rmsnorm_quant, fused_add_rmsnorm_quant,
  * rmsnorm_fp4quant, add_rmsnorm_fp4quant) without defining them; the FlyDSL
- * guide uses e4m3fn (OCP, not fnuz) on gfx950 (section 3b) and per-32 E8M0
- * block scales with fp4 / fp8 elements (section 3a). Readings taken:
+ * guide uses e4m3fn (OCP, not fnuz) on gfx950 (section 3b, FlashAttention
+ * fp8) and per-32 E8M0 block scales with fp4 / fp8 elements (section 3.1,
+ * Preshuffle GEMM, its MX paragraph). Readings taken:
  *   The RMSNorm value y (fp32, never rounded to the activation type) is
  *   divided by a scale s and rounded to the element format, nearest-even,
  *   saturated at its largest value: fp8 e4m3 "fn" (1 sign, 4 exponent bits,
@@ -163,11 +182,14 @@ int rmsnorm_qk_fwd(void* q, void* k, const void* q_gamma, const void* k_gamma,
                    int64_t q_stride, int64_t k_stride, float eps, int x_dtype,
                    int gamma_dtype, hipStream_t stream);
 
-/* Bytes of device workspace rmsnorm_bwd needs for an [M, N] problem of the
- * given activation dtype: fp32 per-workgroup dgamma partials (and per-row
- * scalars for rows too long to keep on chip). Pure host function; returns 0
- * for M <= 0 or N <= 0 and for an unknown dtype. */
-size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int x_dtype);
+/* Bytes of device workspace rmsnorm_bwd (and rmsnorm_fused_add_bwd) needs
+ * for an [M, N] problem, whatever the dtypes: the fp32 dgamma partials,
+ * G x N with G = max(min(M, 256), ceil(M / 64)) workgroups (rounded up to
+ * 256 bytes), and for N > 8192 a 16-byte record per row (rows longer than the
+ * one-pass kernel holds take a two-pass tier that keeps its row dots there;
+ * 16-bit rows up to 16384 elements stay one-pass and leave it unused). Pure
+ * host function; returns 0 for M <= 0, N <= 0 or N > RMSN_MAX_N. */
+size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N);
 
 /* Backward RMSNorm (FlyDSL guide section 1.2, "Backward": inputs x, gamma, dy
  * and the saved rstd, no eps since the forward baked it into rstd). With
@@ -182,11 +204,15 @@ size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int x_dtype);
  *   gamma     [N] gamma_dtype, read.
  *   dx        [M, N] x_dtype, written; may equal dy or x exactly.
  *   dgamma    [N] fp32, written.
- *   workspace at least rmsnorm_bwd_workspace_size(M, N, x_dtype) bytes of
- *             device memory, 16-byte aligned, disjoint from every other buffer;
- *             its contents on entry are ignored.
- * The workgroup partition depends only on (M, N, x_dtype), which fixes the
- * summation order. */
+ *   workspace at least rmsnorm_bwd_workspace_size(M, N) bytes of device
+ *             memory, 16-byte aligned, disjoint from every other buffer; its
+ *             contents on entry are ignored.
+ * The workgroup partition depends only on M, which fixes the summation order.
+ * A row whose fp32 row dot overflows (a product dy x or dy x gamma beyond the
+ * fp32 range) is recomputed in fp64 in the same launch. Outside that, the
+ * fp32 formula needs gamma_j dy_ij within the fp32 range, and rstd as the
+ * forward produced it (positive, finite); a row with rstd = +inf (the 0/0 of
+ * the forward) gives NaN, as in fp64. */
 int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* gamma,
                 void* dx, float* dgamma, void* workspace, size_t workspace_bytes,
                 int64_t M, int64_t N, int x_dtype, int gamma_dtype, hipStream_t stream);
@@ -228,9 +254,10 @@ int layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y, f
                   int gamma_dtype, hipStream_t stream);
 
 /* Bytes of device workspace layernorm_bwd needs: two fp32 partial arrays
- * (dgamma, dbeta) of min(M, 256) rows and, for rows longer than 8192, two
- * doubles per row. 0 for M <= 0, N <= 0 or an unknown dtype. */
-size_t layernorm_bwd_workspace_size(int64_t M, int64_t N, int x_dtype);
+ * (dgamma, dbeta) of G rows each, G as for rmsnorm_bwd_workspace_size, and,
+ * for rows longer than 8192, a 16-byte record per row. 0 for M <= 0, N <= 0
+ * or N > RMSN_MAX_N. */
+size_t layernorm_bwd_workspace_size(int64_t M, int64_t N);
 
 /* LayerNorm backward. The pages give only the forward (FlyDSL guide, section
  * 1.1); this is its derivative with the saved per-row mean and rstd (the
@@ -246,8 +273,11 @@ size_t layernorm_bwd_workspace_size(int64_t M, int64_t N, int x_dtype);
  *   gamma      [N] gamma_dtype, read.
  *   dx         [M, N] x_dtype, written; may equal dy or x exactly.
  *   dgamma     [N] fp32, written.   dbeta [N] fp32, written, or NULL (skipped).
- *   workspace  at least layernorm_bwd_workspace_size(M, N, x_dtype) bytes,
- *              16-byte aligned, disjoint from every other buffer. */
+ *   workspace  at least layernorm_bwd_workspace_size(M, N) bytes, 16-byte
+ *              aligned, disjoint from every other buffer.
+ * Domain: with the forward's mean and rstd, |xhat| <= sqrt(N), so the fp32
+ * dots hold for every finite x; the row dots need sum_j |gamma_j dy_ij|
+ * within the fp32 range (a gradient near the fp32 maximum is outside). */
 int layernorm_bwd(const void* dy, const void* x, const float* mean, const float* rstd,
                   const void* gamma, void* dx, float* dgamma, float* dbeta, void* workspace,
                   size_t workspace_bytes, int64_t M, int64_t N, int x_dtype, int gamma_dtype,

@@ -41,8 +41,8 @@
 //       dgamma_j = sum_i dy xhat,  dbeta_j = sum_i dy.
 //   * MX block-scaled output (the "TIRx kernels" page lists fp4-quantised
 //     norms, flashinfer_rmsnorm_fp4quant and add_rmsnorm_fp4quant, by name;
-//     the FlyDSL guide, section 3a, uses per-32 E8M0 scales with fp4/fp8
-//     elements on gfx950). Reading taken, after the OCP Microscaling (MX)
+//     the FlyDSL kernel library guide, section 3.1, its MX A x MXFP4 B GEMM,
+//     uses per-32 E8M0 scales with fp4/fp8 elements on gfx950). Reading taken, after the OCP Microscaling (MX)
 //     format definition: each row is cut into blocks of 32 consecutive
 //     elements; a block's shared scale is X = 2^(floor(log2(amax)) - emax),
 //     amax = max |y| over the block and emax the exponent of the element

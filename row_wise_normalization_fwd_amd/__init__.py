@@ -76,12 +76,12 @@ def load_library(path: str | None = None):
     lib.rmsnorm_qk_fwd.restype = i32
     lib.layernorm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
     lib.layernorm_fwd.restype = i32
-    lib.layernorm_bwd_workspace_size.argtypes = [i64, i64, i32]
+    lib.layernorm_bwd_workspace_size.argtypes = [i64, i64]
     lib.layernorm_bwd_workspace_size.restype = ctypes.c_size_t
     lib.layernorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64,
                                   i32, i32, vp]
     lib.layernorm_bwd.restype = i32
-    lib.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i32]
+    lib.rmsnorm_bwd_workspace_size.argtypes = [i64, i64]
     lib.rmsnorm_bwd_workspace_size.restype = ctypes.c_size_t
     lib.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i32, i32, vp]
     lib.rmsnorm_bwd.restype = i32
@@ -149,8 +149,8 @@ def layernorm_fwd(x, gamma, beta, y, mean, rstd, M, N, eps, x_dtype, gamma_dtype
                                         N, eps, x_dtype, gamma_dtype, _s(stream))
 
 
-def layernorm_bwd_workspace_size(M, N, x_dtype) -> int:
-    return int(load_library().layernorm_bwd_workspace_size(M, N, x_dtype))
+def layernorm_bwd_workspace_size(M, N) -> int:
+    return int(load_library().layernorm_bwd_workspace_size(M, N))
 
 
 def layernorm_bwd(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, workspace, workspace_bytes, M, N,
@@ -160,8 +160,8 @@ def layernorm_bwd(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, workspace, worksp
                                         N, x_dtype, gamma_dtype, _s(stream))
 
 
-def rmsnorm_bwd_workspace_size(M, N, x_dtype) -> int:
-    return int(load_library().rmsnorm_bwd_workspace_size(M, N, x_dtype))
+def rmsnorm_bwd_workspace_size(M, N) -> int:
+    return int(load_library().rmsnorm_bwd_workspace_size(M, N))
 
 
 def rmsnorm_bwd(dy, x, rstd, gamma, dx, dgamma, workspace, workspace_bytes, M, N, x_dtype,
@@ -380,7 +380,7 @@ def bwd(dy, x, rstd, gamma, *, dx=None, dgamma=None, workspace=None, stream=None
           (dgamma, "dgamma", N, torch.float32), (workspace, "workspace", None, None))
     dx = torch.empty_like(x) if dx is None else dx
     dgamma = torch.empty(N, dtype=torch.float32, device=x.device) if dgamma is None else dgamma
-    ws_bytes = rmsnorm_bwd_workspace_size(M, N, dtype_code(x))
+    ws_bytes = rmsnorm_bwd_workspace_size(M, N)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     stream = torch.cuda.current_stream(x.device) if stream is None else stream
@@ -405,7 +405,7 @@ def fused_add_bwd(dy, h, rstd, gamma, dresidual=None, *, dh=None, dgamma=None, w
           (workspace, "workspace", None, None))
     dh = torch.empty_like(h) if dh is None else dh
     dgamma = torch.empty(N, dtype=torch.float32, device=h.device) if dgamma is None else dgamma
-    ws_bytes = rmsnorm_bwd_workspace_size(M, N, dtype_code(h))
+    ws_bytes = rmsnorm_bwd_workspace_size(M, N)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=h.device)
     stream = torch.cuda.current_stream(h.device) if stream is None else stream
@@ -430,7 +430,7 @@ def layernorm_backward(dy, x, mean, rstd, gamma, *, want_dbeta: bool = True, dx=
     dx = torch.empty_like(x) if dx is None else dx
     dgamma = torch.empty(N, dtype=torch.float32, device=x.device)
     dbeta = torch.empty(N, dtype=torch.float32, device=x.device) if want_dbeta else None
-    ws_bytes = layernorm_bwd_workspace_size(M, N, dtype_code(x))
+    ws_bytes = layernorm_bwd_workspace_size(M, N)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     stream = torch.cuda.current_stream(x.device) if stream is None else stream

@@ -40,6 +40,8 @@ COMMON_FLAGS = [
     "-ffp-contract=off",          # every FMA in the kernels is written out explicitly
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
+    "-Wshadow",                   # a shadowed loop counter once silently misindexed a bitmask
+    "-Werror=shadow",
     "-Wno-unused-command-line-argument",
     "-I", INCLUDE,
     "-I", CSRC,

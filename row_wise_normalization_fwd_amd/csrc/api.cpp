@@ -39,13 +39,21 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 // Overlap that is not an exact alias of two equal-size buffers.
 bool partial_overlap(Range a, Range b) { return overlap(a, b) && !(a.lo == b.lo && a.hi == b.hi); }
 
-// M * N elements must be addressable with 64-bit offsets and N by an int.
+// M * N elements must be addressable with 64-bit offsets, and N by an int
+// with room to spare: the kernels step through a row in 32-bit unit indices
+// by up to 8192 units, which must not wrap.
 bool shape_ok(int64_t M, int64_t N) {
-  if (M < 0 || N < 1 || N > INT32_MAX) return false;
+  if (M < 0 || N < 1 || N > RMSN_MAX_N) return false;
   return M == 0 || M <= (INT64_MAX / 8) / N;
 }
 
-int finish(hipError_t e) {
+// Launch through `f` and report its error. A stale error left on the thread
+// by an earlier, unrelated HIP call is cleared first, so that it is not
+// taken for this launch's.
+template <class F>
+int launch_checked(F&& f) {
+  (void)hipGetLastError();
+  const hipError_t e = f();
   if (e != hipSuccess) {
     g_last_hip_error = static_cast<int>(e);
     return RMSN_ERR_HIP;
@@ -86,7 +94,7 @@ int forward(bool fused, const void* x, void* residual, const void* gamma, void* 
     if (partial_overlap(rs, rx) || overlap(rs, ry) || overlap(rs, rg)) return RMSN_ERR_OVERLAP;
   }
   rmsn::FwdCall c{x, residual, gamma, y, rstd, M, N, eps, gamma_dtype, stream};
-  return finish(launch_forward(c, x_dtype));
+  return launch_checked([&] { return launch_forward(c, x_dtype); });
 }
 
 // Validation of the LayerNorm forward.
@@ -122,9 +130,9 @@ int ln_forward(const void* x, const void* gamma, const void* beta, void* y, floa
   c.beta = beta;
   c.mean = mean;
   switch (x_dtype) {
-    case RMSN_F32: return finish(rmsn::launch_ln_fwd_f32(c));
-    case RMSN_F16: return finish(rmsn::launch_ln_fwd_f16(c));
-    default: return finish(rmsn::launch_ln_fwd_bf16(c));
+    case RMSN_F32: return launch_checked([&] { return rmsn::launch_ln_fwd_f32(c); });
+    case RMSN_F16: return launch_checked([&] { return rmsn::launch_ln_fwd_f16(c); });
+    default: return launch_checked([&] { return rmsn::launch_ln_fwd_bf16(c); });
   }
 }
 
@@ -179,9 +187,9 @@ int quant_forward(const void* x, void* residual, const void* gamma, void* q, voi
   if (mx) c.mx = static_cast<uint8_t*>(scale);
   else c.scale = static_cast<float*>(scale);
   switch (x_dtype) {
-    case RMSN_F32: return finish(rmsn::launch_fwd_quant_f32(c));
-    case RMSN_F16: return finish(rmsn::launch_fwd_quant_f16(c));
-    default: return finish(rmsn::launch_fwd_quant_bf16(c));
+    case RMSN_F32: return launch_checked([&] { return rmsn::launch_fwd_quant_f32(c); });
+    case RMSN_F16: return launch_checked([&] { return rmsn::launch_fwd_quant_f16(c); });
+    default: return launch_checked([&] { return rmsn::launch_fwd_quant_bf16(c); });
   }
 }
 
@@ -244,14 +252,14 @@ int qk_forward(void* q, void* k, const void* q_gamma, const void* k_gamma, int64
                  eps,
                  gamma_dtype,
                  stream};
-  return finish(rmsn::launch_qk(c, x_dtype));
+  return launch_checked([&] { return rmsn::launch_qk(c, x_dtype); });
 }
 
 }  // namespace
 
 namespace rmsn {
-BwdPlan plan_bwd(int64_t M, int64_t N, int x_dtype);
-BwdPlan plan_ln_bwd(int64_t M, int64_t N, int x_dtype);
+BwdPlan plan_bwd(int64_t M, int64_t N);
+BwdPlan plan_ln_bwd(int64_t M, int64_t N);
 }
 
 namespace {
@@ -263,7 +271,7 @@ int backward(const void* dy, const void* x, const float* rstd, const void* gamma
   if (!valid_pair(x_dtype, gamma_dtype)) return RMSN_ERR_DTYPE;
   if (!shape_ok(M, N)) return RMSN_ERR_SHAPE;
   if (M == 0) return RMSN_OK;
-  const rmsn::BwdPlan plan = rmsn::plan_bwd(M, N, x_dtype);
+  const rmsn::BwdPlan plan = rmsn::plan_bwd(M, N);
   if (!dy || !x || !rstd || !gamma || !dx || !dgamma) return RMSN_ERR_NULL;
   if (!workspace || workspace_bytes < plan.workspace_bytes) return RMSN_ERR_WORKSPACE;
   const int es = esize_of(x_dtype), gs = esize_of(gamma_dtype);
@@ -293,7 +301,7 @@ int backward(const void* dy, const void* x, const float* rstd, const void* gamma
   if (overlap(rdg, rw)) return RMSN_ERR_OVERLAP;
   rmsn::BwdCall c{dy, x, rstd, gamma, dres, dx, dgamma, workspace, M, N, x_dtype, gamma_dtype,
                   plan, stream};
-  return finish(rmsn::launch_bwd(c));
+  return launch_checked([&] { return rmsn::launch_bwd(c); });
 }
 
 // Validation of the LayerNorm backward.
@@ -304,7 +312,7 @@ int ln_backward(const void* dy, const void* x, const float* mean, const float* r
   if (!valid_pair(x_dtype, gamma_dtype)) return RMSN_ERR_DTYPE;
   if (!shape_ok(M, N)) return RMSN_ERR_SHAPE;
   if (M == 0) return RMSN_OK;
-  const rmsn::BwdPlan plan = rmsn::plan_ln_bwd(M, N, x_dtype);
+  const rmsn::BwdPlan plan = rmsn::plan_ln_bwd(M, N);
   if (!dy || !x || !mean || !rstd || !gamma || !dx || !dgamma) return RMSN_ERR_NULL;
   if (!workspace || workspace_bytes < plan.workspace_bytes) return RMSN_ERR_WORKSPACE;
   const int es = esize_of(x_dtype), gs = esize_of(gamma_dtype);
@@ -337,7 +345,7 @@ int ln_backward(const void* dy, const void* x, const float* mean, const float* r
                   plan, stream};
   c.mean = mean;
   c.dbeta = dbeta;
-  return finish(rmsn::launch_ln_bwd(c));
+  return launch_checked([&] { return rmsn::launch_ln_bwd(c); });
 }
 
 }  // namespace
@@ -382,25 +390,28 @@ hipError_t allow_dynamic_lds(const void* kernel, size_t bytes) {
                              static_cast<int>(bytes));
 }
 
-BwdPlan plan_ln_bwd(int64_t M, int64_t N, int x_dtype) {
-  BwdPlan p = plan_bwd(M, N, x_dtype);
+BwdPlan plan_ln_bwd(int64_t M, int64_t N) {
+  BwdPlan p = plan_bwd(M, N);
   if (!p.valid) return p;
-  auto round256 = [](uint64_t b) { return (b + 255u) & ~static_cast<uint64_t>(255u); };
-  const uint64_t dots = N > kBwdOnChipN ? round256(static_cast<uint64_t>(M) * 16u) : 0u;
-  p.workspace_bytes = 2 * p.partial_bytes + static_cast<size_t>(dots);
+  p.workspace_bytes = 2 * p.partial_bytes + (p.workspace_bytes - p.partial_bytes);
   return p;
 }
 
-BwdPlan plan_bwd(int64_t M, int64_t N, int x_dtype) {
+BwdPlan plan_bwd(int64_t M, int64_t N) {
   BwdPlan p{false, 0, 0, 0};
-  if (!valid_dtype(x_dtype) || M <= 0 || N <= 0) return p;
+  if (M <= 0 || N <= 0 || !shape_ok(M, N)) return p;
   p.valid = true;
+  // min(M, 256) blocks, more when a block would own over kBwdMaxRowsPerBlock
+  // rows: every partial is then an fp32 sum of at most that many rows.
   p.blocks = M < kBwdTargetBlocks ? M : kBwdTargetBlocks;
+  const int64_t by_rows = ceil_div(M, kBwdMaxRowsPerBlock);
+  if (p.blocks < by_rows) p.blocks = by_rows;
   auto round256 = [](uint64_t b) { return (b + 255u) & ~static_cast<uint64_t>(255u); };
-  // One fp32 partial row per block, then (long rows) one double per row.
+  // One fp32 partial row per block, then (rows that may take the two-pass
+  // tier) a 16-byte record per row.
   p.partial_bytes = static_cast<size_t>(
       round256(static_cast<uint64_t>(p.blocks) * static_cast<uint64_t>(N) * 4u));
-  const uint64_t dots = N > kBwdOnChipN ? round256(static_cast<uint64_t>(M) * 8u) : 0u;
+  const uint64_t dots = N > kBwdOnChipN ? round256(static_cast<uint64_t>(M) * 16u) : 0u;
   p.workspace_bytes = p.partial_bytes + static_cast<size_t>(dots);
   return p;
 }
@@ -441,8 +452,8 @@ int layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y, f
   return ln_forward(x, gamma, beta, y, mean, rstd, M, N, eps, x_dtype, gamma_dtype, stream);
 }
 
-size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N, int x_dtype) {
-  return rmsn::plan_bwd(M, N, x_dtype).workspace_bytes;
+size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N) {
+  return rmsn::plan_bwd(M, N).workspace_bytes;
 }
 
 int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* gamma, void* dx,
@@ -460,8 +471,8 @@ int rmsnorm_fused_add_bwd(const void* dy, const void* h, const float* rstd, cons
                   x_dtype, gamma_dtype, stream);
 }
 
-size_t layernorm_bwd_workspace_size(int64_t M, int64_t N, int x_dtype) {
-  return rmsn::plan_ln_bwd(M, N, x_dtype).workspace_bytes;
+size_t layernorm_bwd_workspace_size(int64_t M, int64_t N) {
+  return rmsn::plan_ln_bwd(M, N).workspace_bytes;
 }
 
 int layernorm_bwd(const void* dy, const void* x, const float* mean, const float* rstd,

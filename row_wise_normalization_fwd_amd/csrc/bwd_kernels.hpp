@@ -67,17 +67,211 @@ __device__ __forceinline__ void unit_dots_ln(const float* dyv, const float* g, c
   }
 }
 
-// The row dot sum_j dy gamma x is formed per 16-byte unit in fp32 (one FMA
-// per element; for bf16 every product is exact, otherwise each step rounds
-// once) and the unit sums are accumulated in double. The fp32 error of a
-// unit is at most E * 2^-24 of the unit's sum of |dy gamma x|, far below the
-// resolution dx needs.
+// The row dot sum_j dy gamma x is formed per 16-byte unit in fp32, one
+// multiply and one FMA per element, fma(dy x, gamma, s): for 16-bit
+// activations dy x is exact, so each step rounds once (as fma(gamma dy, x, s)
+// would with 16-bit gamma, where gamma dy is exact too), and the unit sums
+// are accumulated in double. The fp32 error of a unit is at most E * 2^-24
+// of the unit's sum of |dy gamma x|, far below the resolution dx needs. A
+// product dy x, or dy x gamma, beyond the fp32 range makes the unit sum, and
+// so the row dot, inf or NaN: that is how a row whose products overflow is
+// recognised (it is then recomputed in fp64, see rare_dx).
 template <int E>
 __device__ __forceinline__ float unit_dot(const float* dyv, const float* g, const float* xv) {
   float s = 0.0f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) s = __builtin_fmaf(g[e] * dyv[e], xv[e], s);
+  for (int e = 0; e < E; ++e) s = __builtin_fmaf(dyv[e] * xv[e], g[e], s);
   return s;
+}
+
+// fp64 view of a rare backward row: rho, and the row dot(s) over N in fp64
+// (RMSNorm: k = rho^2 c; LayerNorm: c1, c2 with xhat = (x - mean) rho).
+struct RareBwd {
+  double rho, k, c1, c2, mu;
+};
+
+// The fp64 row dots of a rare row: each(f) calls f(x, dy, gamma, ok) for
+// every element of the lane's part of the row in a fixed order; reduced with
+// row_sum (every lane that row_sum<TPR, BLOCK> needs must take part).
+template <int TPR, int BLOCK, bool LN, class Each>
+__device__ RareBwd rare_bwd_stats(const Each& each, int N, float rho, float mu, double* scratch,
+                                  int& parity) {
+  RareBwd r{static_cast<double>(rho), 0.0, 0.0, 0.0, static_cast<double>(mu)};
+  const double n = static_cast<double>(here(N));
+  if constexpr (LN) {
+    double s1 = 0.0, s2 = 0.0;
+    each([&](float x, float dy, float g, bool) {
+      const double gdy = static_cast<double>(g) * static_cast<double>(dy);
+      s1 = s1 + gdy;
+      s2 = __builtin_fma(gdy, (static_cast<double>(x) - r.mu) * r.rho, s2);
+    });
+    s1 = row_sum<TPR, BLOCK>(s1, scratch, parity);
+    parity ^= 1;
+    s2 = row_sum<TPR, BLOCK>(s2, scratch, parity);
+    parity ^= 1;
+    r.c1 = s1 / n;
+    r.c2 = s2 / n;
+  } else {
+    double s = 0.0;
+    each([&](float x, float dy, float g, bool) {
+      s = __builtin_fma(static_cast<double>(dy) * static_cast<double>(x), static_cast<double>(g), s);
+    });
+    s = row_sum<TPR, BLOCK>(s, scratch, parity);
+    parity ^= 1;
+    r.k = r.rho * r.rho * (s / n);
+  }
+  return r;
+}
+
+// One element of a rare row in fp64, each result rounded to fp32 once: dx
+// (before the residual gradient is added) and the dgamma (dg) and dbeta (db)
+// terms.
+template <bool LN>
+__device__ __forceinline__ void rare_dx(float x, float dy, float g, const RareBwd& r, float& dx,
+                                        float& dg, float& db) {
+  const double xd = static_cast<double>(x), dyd = static_cast<double>(dy);
+  const double gdy = static_cast<double>(g) * dyd;
+  if constexpr (LN) {
+    const double xh = (xd - r.mu) * r.rho;
+    dx = static_cast<float>(r.rho * (gdy - r.c1 - xh * r.c2));
+    dg = static_cast<float>(dyd * xh);
+    db = dy;
+  } else {
+    dx = static_cast<float>(r.rho * (gdy - xd * r.k));
+    dg = static_cast<float>(dyd * xd * r.rho);
+    db = 0.0f;
+  }
+}
+
+// After stage 1's row loop, for rows whose fp32 row dot overflowed ("rare",
+// marked in `mine`: bit t is the group's row of loop iteration t, row_of(t),
+// possibly past the last row). Such a row stored no dx in the loop, and its
+// dgamma (and dbeta) terms may have made the group's sums inf or NaN, so:
+//  1. each marked row is redone in fp64 (rare_bwd_stats, rare_dx): its row
+//     dot(s) reduced over the group -- for blocks of several multi-wave
+//     groups every group walks the union of the block's marks to reach the
+//     reductions -- and its dx written;
+//  2. a group with a marked row rebuilds its sums from memory in the loop's
+//     row order: every other row adds exactly the fp32 terms the loop added
+//     (same expressions, so the same bits), a marked row its fp64 terms
+//     rounded to fp32 once.
+// Runs only when some row is marked; reads x, dy (and dres) back (dx, which
+// may alias them, was not written for the marked rows).
+template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool RES, bool LN, class RowOf,
+          class GammaOf>
+__device__ void rare_bwd_after(const BwdArgs<T, G>& a, uint64_t mine, int iters, int grp, int lane,
+                               const RowOf& row_of, const GammaOf& gamma_of,
+                               float (&acc)[UPT][Unit<T, VEC>::E],
+                               float (&accb)[LN ? UPT : 1][Unit<T, VEC>::E], double* scratch,
+                               uint64_t* masks) {
+  using U = Unit<T, VEC>;
+  constexpr int E = U::E;
+  const int nunits = a.N / E;
+  uint64_t m = mine;
+  if constexpr (kBlockFlag<TPR, BLOCK>) {
+    if (threadIdx.x % TPR == 0) masks[threadIdx.x / TPR] = mine;
+    __syncthreads();
+    m = 0;
+#pragma unroll
+    for (int g = 0; g < BLOCK / TPR; ++g) m |= masks[g];
+  }
+  if (m == 0) return;  // uniform over the block (its union) or the group
+  auto units = [&](int64_t off, int k, bool ok, float* xv, float* dyv) {
+    const int64_t o = off + (lane + k * TPR) * E;
+    U::widen(ok ? U::load(a.x + o) : U::zero(), xv);
+    U::widen(ok ? U::load(a.dy + o) : U::zero(), dyv);
+  };
+
+  // 1. dx of the marked rows.
+  int parity = 0;
+  for (uint64_t w = m; w != 0; w &= w - 1) {
+    const int it = __builtin_ctzll(w);
+    const int64_t row = row_of(it);
+    const bool valid = row < a.M;
+    const int64_t off = (valid ? row : 0) * a.N;
+    const float rho = valid ? a.rstd[row] : 0.0f;
+    const float mu = LN && valid ? a.mean[row] : 0.0f;
+    auto each = [&](auto&& f) {
+#pragma unroll
+      for (int k = 0; k < UPT; ++k) {
+        const bool ok = valid && lane + k * TPR < nunits;
+        float xv[E], dyv[E], g[E];
+        units(off, k, ok, xv, dyv);
+        gamma_of(k, g);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          f(xv[e], dyv[e], g[e], ok);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    const RareBwd rb = rare_bwd_stats<TPR, BLOCK, LN>(each, a.N, rho, mu, scratch, parity);
+    if (valid && ((mine >> it) & 1)) {
+#pragma unroll
+      for (int k = 0; k < UPT; ++k) {
+        const int u = lane + k * TPR;
+        if (u < nunits) {
+          float xv[E], dyv[E], g[E], o[E];
+          units(off, k, true, xv, dyv);
+          gamma_of(k, g);
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            float dg, db;
+            rare_dx<LN>(xv[e], dyv[e], g[e], rb, o[e], dg, db);
+          }
+          if constexpr (RES) {
+            float rv[E];
+            U::widen(U::load(a.dres + off + u * E), rv);
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = o[e] + rv[e];
+          }
+          U::store_nt(a.dx + off + u * E, U::narrow(o));
+        }
+      }
+    }
+  }
+
+  // 2. The sums of a group with a marked row, rebuilt in row order.
+  if (mine == 0) return;
+#pragma unroll
+  for (int k = 0; k < UPT; ++k) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      acc[k][e] = 0.0f;
+      if constexpr (LN) accb[k][e] = 0.0f;
+    }
+  }
+  for (int it = 0; it < iters; ++it) {
+    const int64_t row = row_of(it);
+    if (row >= a.M) continue;  // the loop added zeros for it
+    const bool marked = (mine >> it) & 1;
+    const float rho = a.rstd[row];
+    const float mu = LN ? a.mean[row] : 0.0f;
+    const RareBwd rb{static_cast<double>(rho), 0.0, 0.0, 0.0, static_cast<double>(mu)};
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      if (lane + k * TPR >= nunits) continue;  // zeros in the loop too
+      float xv[E], dyv[E];
+      units(row * a.N, k, true, xv, dyv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (!marked) {  // the loop's own terms
+          if constexpr (LN) {
+            const float xh = (xv[e] - mu) * rho;
+            acc[k][e] = __builtin_fmaf(dyv[e], xh, acc[k][e]);
+            accb[k][e] = accb[k][e] + dyv[e];
+          } else {
+            acc[k][e] = __builtin_fmaf(dyv[e] * xv[e], rho, acc[k][e]);
+          }
+        } else {
+          float dx, dg, db;
+          rare_dx<LN>(xv[e], dyv[e], 0.0f, rb, dx, dg, db);
+          acc[k][e] = acc[k][e] + dg;
+          if constexpr (LN) accb[k][e] = accb[k][e] + db;
+        }
+      }
+    }
+  }
 }
 
 // Stage 1. A block of BLOCK threads holds RG = BLOCK / TPR row groups; block
@@ -106,6 +300,8 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   static_assert(!(LN && RES), "LayerNorm backward has no residual input");
   using Red = typename std::conditional<LN, DSum2, double>::type;
   __shared__ Red red[2 * (BLOCK / kWave)];
+  __shared__ double rared[LN ? 1 : 2 * (BLOCK / kWave)];  // rare rows (after the loop)
+  __shared__ uint64_t rmasks[RG];
   extern __shared__ __align__(16) unsigned char lds_bytes[];
   float* comb = reinterpret_cast<float*>(lds_bytes);  // [RG][COLS] when RG > 1
 
@@ -243,6 +439,8 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   // prefetched data is first touched inside the next call, after that call
   // has issued its own prefetch.
   int parity = 0;
+  uint64_t rare_mask = 0;  // bit t: this group's row of iteration t is rare
+  int t = 0;
   auto step = [&](int64_t row0, Raw* cx, Raw* cdy, Raw* cr, Raw* nx, Raw* ndy, Raw* nr) {
     const int64_t row = row0 + a.nblk * grp;
     const bool valid = row < a.M;
@@ -280,16 +478,23 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
       opaque(cdy[k]);
     }
     [[maybe_unused]] float kcoef = 0.0f, c1 = 0.0f, c2 = 0.0f;
+    bool rare;  // the row dot overflowed fp32: redone after the loop
     if constexpr (LN) {
       dots = row_sum<TPR, BLOCK>(dots, red, parity);
       c1 = static_cast<float>(dots.a / static_cast<double>(a.N));
       c2 = static_cast<float>(dots.b / static_cast<double>(a.N));
+      rare = false;  // LayerNorm: no fp64 redo (xhat is bounded; see the header)
     } else {
       dot = row_sum<TPR, BLOCK>(dot, red, parity);
       const double rd = static_cast<double>(rho);
       kcoef = static_cast<float>(rd * rd * (dot / static_cast<double>(a.N)));
+      rare = RareDotGate{}(dot);
     }
     parity ^= 1;
+    // A rare row stores no dx now (its dgamma terms may be inf or NaN: the
+    // group's sums are rebuilt after the loop).
+    rare_mask |= static_cast<uint64_t>(rare) << t;
+    ++t;
 
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
@@ -322,9 +527,9 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
       }
       if constexpr (VEC) {
         const auto rsdx = make_rsrc(a.dx + row0 * a.N, span_bytes(row0));
-        buf_store16_nt(U::narrow(o), rsdx, unit_offset(row0, grp, k));
+        buf_store16_nt(U::narrow(o), rsdx, rare ? kBufOutOfRange : unit_offset(row0, grp, k));
       } else {
-        if (valid && u < nunits) U::store_nt(a.dx + off + u * E, U::narrow(o));
+        if (valid && !rare && u < nunits) U::store_nt(a.dx + off + u * E, U::narrow(o));
       }
     }
   };
@@ -338,6 +543,21 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
     if (b + a.nblk * (s0 + RG) >= a.M) break;
     step(b + a.nblk * (s0 + RG), bx, bdy, br, ax, ady, ar);
   }
+
+  // Rare rows (see rare_bwd_after): their dx, and the dgamma (and dbeta) sums
+  // of every group that had one, rebuilt in row order.
+  if constexpr (!LN) rare_bwd_after<T, G, VEC, TPR, UPT, BLOCK, RES, LN>(
+      a, rare_mask, t, grp, lane,
+      [&](int it) { return b + a.nblk * (static_cast<int64_t>(RG) * it + grp); },
+      [&](int k, float* g) {
+        if constexpr (LN) {
+          gamma_lds(lane + k * TPR, g);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) g[e] = gam[k][e];
+        }
+      },
+      acc, accb, rared, rmasks);
 
   // The block's partial row(s): one array (dgamma), two with LN (dbeta).
   auto write_partial = [&](float* base, float (*sums)[E]) {
@@ -374,9 +594,15 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
 
 // Long rows (rows too long for stage 1's registers), in two passes.
 //
-// Pass A: c_i = (1/N) sum_j dy_ij gamma_j x_ij in double (LN: c1_i and c2_i,
-// stored as cdot[2i], cdot[2i + 1]), one block per row, looping over the
-// row; ordinary (cacheable) loads since pass B reads the same rows again.
+// Pass A: the row dots in double, one block per row, looping over the row;
+// ordinary (cacheable) loads since pass B reads the same rows again. Each
+// row gets a record of kDotRec doubles: RMSNorm {c, rare}, LayerNorm
+// {c1, c2}, with c = (1/N) sum_j dy gamma x (c1, c2 as in stage 1). rare = 1
+// marks an RMSNorm row whose fp32 unit dots overflowed: its c is recomputed
+// in fp64 (after the block's row loop), and pass B forms its outputs in fp64.
+// Doubles per row in pass A's record.
+constexpr int kDotRec = 2;
+
 template <class T, class G, bool VEC, int BLOCK, int UNROLL, bool LN = false>
 __global__ __launch_bounds__(BLOCK) void bwd_rowdot_kernel(BwdArgs<T, G> a, double* cdot) {
   using U = Unit<T, VEC>;
@@ -385,9 +611,12 @@ __global__ __launch_bounds__(BLOCK) void bwd_rowdot_kernel(BwdArgs<T, G> a, doub
   constexpr int STEP = BLOCK * UNROLL;
   using Red = typename std::conditional<LN, DSum2, double>::type;
   __shared__ Red red[2 * (BLOCK / kWave)];
+  __shared__ double rared[LN ? 1 : 2 * (BLOCK / kWave)];
   const int nunits = a.N / E;
   int parity = 0;
-  for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x) {
+  uint64_t rare_mask = 0;  // bit t: the block's row of iteration t overflowed
+  int t = 0;
+  for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x, ++t) {
     const int64_t off = row * a.N;
     [[maybe_unused]] const float rho = a.rstd[row];
     [[maybe_unused]] const float mu = LN ? a.mean[row] : 0.0f;
@@ -419,17 +648,44 @@ __global__ __launch_bounds__(BLOCK) void bwd_rowdot_kernel(BwdArgs<T, G> a, doub
         }
       }
     }
+    double* rec = cdot + kDotRec * row;
     if constexpr (LN) {
       dots = row_sum<BLOCK, BLOCK>(dots, red, parity);
       if (threadIdx.x == 0) {
-        cdot[2 * row] = dots.a / static_cast<double>(a.N);
-        cdot[2 * row + 1] = dots.b / static_cast<double>(a.N);
+        rec[0] = dots.a / static_cast<double>(a.N);
+        rec[1] = dots.b / static_cast<double>(a.N);
       }
     } else {
       dot = row_sum<BLOCK, BLOCK>(dot, red, parity);
-      if (threadIdx.x == 0) cdot[row] = dot / static_cast<double>(a.N);
+      const bool rare = RareDotGate{}(dot);
+      rare_mask |= static_cast<uint64_t>(rare) << t;
+      if (threadIdx.x == 0) {
+        rec[0] = dot / static_cast<double>(a.N);
+        rec[1] = rare ? 1.0 : 0.0;
+      }
     }
     parity ^= 1;
+  }
+  if constexpr (!LN) {
+    // Rows that overflowed, again in fp64 (one row per block: uniform).
+    int rparity = 0;
+    for (uint64_t w = rare_mask; w != 0; w &= w - 1) {
+      const int64_t row = blockIdx.x + static_cast<int64_t>(__builtin_ctzll(w)) * gridDim.x;
+      const int64_t off = row * a.N;
+      auto each = [&](auto&& f) {
+        for (int u = threadIdx.x; u < nunits; u += BLOCK) {
+          float xv[E], dyv[E], g[E];
+          U::widen(U::load(a.x + off + u * E), xv);
+          U::widen(U::load(a.dy + off + u * E), dyv);
+          load_gamma<G, E, VEC>(a.gamma, u * E, g);
+#pragma unroll
+          for (int e = 0; e < E; ++e) f(xv[e], dyv[e], g[e], true);
+        }
+      };
+      const RareBwd rb = rare_bwd_stats<BLOCK, BLOCK, false>(each, a.N, 1.0f, 0.0f, rared, rparity);
+      // With rho = 1 the returned k is the plain row mean c.
+      if (threadIdx.x == 0) cdot[kDotRec * row] = rb.k;
+    }
   }
 }
 
@@ -437,7 +693,10 @@ __global__ __launch_bounds__(BLOCK) void bwd_rowdot_kernel(BwdArgs<T, G> a, doub
 // by, by + G, by + 2G, ..., COLS = BLOCK * UPT * E. Each lane keeps gamma and
 // the dgamma partial sums of its columns in registers over the block's rows
 // (in increasing row order) and writes them to partial[by][...]; dx uses the
-// row dots from pass A.
+// row dots from pass A. Rows pass A marked are skipped in the loop (no dx
+// store) and, after it, get their dx in fp64, and the lane's sums are
+// rebuilt in row order with their fp64 terms (the other rows' terms with
+// the loop's own expressions, so their bits are unchanged).
 template <class T, class G, bool VEC, int BLOCK, int UPT, bool RES, bool LN = false>
 __global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const double* cdot) {
   using U = Unit<T, VEC>;
@@ -464,6 +723,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const 
       for (int e = 0; e < E; ++e) accb[k][e] = 0.0f;
     }
   }
+  bool any_rare = false;
   for (int64_t row = blockIdx.y; row < a.M; row += a.nblk) {
     const int64_t off = row * a.N;
     Raw rx[UPT], rdy[UPT], rr[UPT];
@@ -475,14 +735,18 @@ __global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const 
       if constexpr (RES) rr[k] = u < nunits ? U::load_nt(a.dres + off + u * E) : U::zero();
     }
     const float rho = a.rstd[row];
+    const double* rec = cdot + kDotRec * row;
     [[maybe_unused]] float kcoef = 0.0f, c1 = 0.0f, c2 = 0.0f, mu = 0.0f;
+    bool rare = false;
     if constexpr (LN) {
       mu = a.mean[row];
-      c1 = static_cast<float>(cdot[2 * row]);
-      c2 = static_cast<float>(cdot[2 * row + 1]);
+      c1 = static_cast<float>(rec[0]);
+      c2 = static_cast<float>(rec[1]);
     } else {
       const double rd = static_cast<double>(rho);
-      kcoef = static_cast<float>(rd * rd * cdot[row]);
+      kcoef = static_cast<float>(rd * rd * rec[0]);
+      rare = rec[1] != 0.0;
+      any_rare = any_rare || rare;
     }
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
@@ -511,7 +775,51 @@ __global__ __launch_bounds__(BLOCK) void bwd_tile_kernel(BwdArgs<T, G> a, const 
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = o[e] + rv[e];
       }
-      if (u < nunits) U::store_nt(a.dx + off + u * E, U::narrow(o));
+      if (u < nunits && !rare) U::store_nt(a.dx + off + u * E, U::narrow(o));
+    }
+  }
+  if constexpr (!LN) {
+    if (any_rare) {  // uniform: every lane sees the same records
+#pragma unroll
+      for (int k = 0; k < UPT; ++k)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[k][e] = 0.0f;
+      for (int64_t row = blockIdx.y; row < a.M; row += a.nblk) {
+        const int64_t off = row * a.N;
+        const float rho = a.rstd[row];
+        const double* rec = cdot + kDotRec * row;
+        const bool rare = rec[1] != 0.0;
+        const RareBwd rb{static_cast<double>(rho),
+                         static_cast<double>(rho) * static_cast<double>(rho) * rec[0], 0.0, 0.0,
+                         0.0};
+#pragma unroll
+        for (int k = 0; k < UPT; ++k) {
+          const int u = ubase + threadIdx.x + k * BLOCK;
+          if (u >= nunits) continue;
+          float xv[E], dyv[E], o[E];
+          U::widen(U::load(a.x + off + u * E), xv);
+          U::widen(U::load(a.dy + off + u * E), dyv);
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            if (!rare) {  // the loop's own term
+              acc[k][e] = __builtin_fmaf(dyv[e] * xv[e], rho, acc[k][e]);
+            } else {
+              float dg, db;
+              rare_dx<false>(xv[e], dyv[e], gam[k][e], rb, o[e], dg, db);
+              acc[k][e] = acc[k][e] + dg;
+            }
+          }
+          if (rare) {
+            if constexpr (RES) {
+              float rv[E];
+              U::widen(U::load(a.dres + off + u * E), rv);
+#pragma unroll
+              for (int e = 0; e < E; ++e) o[e] = o[e] + rv[e];
+            }
+            U::store_nt(a.dx + off + u * E, U::narrow(o));
+          }
+        }
+      }
     }
   }
   float* out = a.partial + static_cast<int64_t>(blockIdx.y) * a.N;

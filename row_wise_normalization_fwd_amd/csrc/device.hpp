@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace rmsn {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -153,6 +155,15 @@ __device__ __forceinline__ void buf_store16_nt(u32x4 v, __amdgpu_buffer_rsrc_t r
 template <class V>
 __device__ __forceinline__ void opaque(V& v) {
   asm volatile("" : "+v"(v));
+}
+
+// Makes the compiler treat v as defined here: values derived from it are not
+// hoisted out of a rarely taken branch (where they would hold registers for
+// the whole kernel).
+template <class V>
+__device__ __forceinline__ V here(V v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // Load E consecutive gamma values starting at element offset `off` as fp32.
@@ -351,6 +362,17 @@ __device__ __forceinline__ DSum2 dpp(DSum2 v) {
   return {dpp<CTRL>(v.a), dpp<CTRL>(v.b)};
 }
 
+// SumMax in fp64 (the fp64 pass over a row with a per-row fp8 scale).
+struct DSumMax {
+  double s, m;
+  __device__ DSumMax operator+(DSumMax o) const { return {s + o.s, __builtin_fmax(m, o.m)}; }
+};
+
+template <int CTRL>
+__device__ __forceinline__ DSumMax dpp(DSumMax v) {
+  return {dpp<CTRL>(v.s), dpp<CTRL>(v.m)};
+}
+
 template <int CTRL>
 __device__ __forceinline__ SumMax dpp(SumMax v) {
   return {dpp<CTRL>(v.s), dpp<CTRL>(v.m)};
@@ -373,6 +395,10 @@ __device__ __forceinline__ double readlane(double v, int lane) {
 
 __device__ __forceinline__ DSum2 readlane(DSum2 v, int lane) {
   return {readlane(v.a, lane), readlane(v.b, lane)};
+}
+
+__device__ __forceinline__ DSumMax readlane(DSumMax v, int lane) {
+  return {readlane(v.s, lane), readlane(v.m, lane)};
 }
 
 // DPP controls (gfx9 encoding).
@@ -440,5 +466,77 @@ __device__ __forceinline__ V row_sum(V v, V* scratch, int parity) {
     return s;
   }
 }
+
+// ------------------------------------------------------------ MX output unit
+
+template <int OUT>
+constexpr bool kIsMx = OUT == kOutMxFp8 || OUT == kOutMxFp4;
+
+// MX output of one unit (E elements o of a row): the block max over the
+// 32 / E lanes holding the block (every lane of the wave must take part),
+// its E8M0 code, and the packed element codes.
+template <int OUT, int E>
+struct MxUnit {
+  static constexpr int kLanes = 32 / E;            // lanes per 32-element block
+  static constexpr int kEmax = OUT == kOutMxFp4 ? 2 : 8;
+  using Pack = typename std::conditional<OUT == kOutMxFp4, Fp4Unit<E>, Fp8Unit<E>>::type;
+  static constexpr int kBytes = OUT == kOutMxFp4 ? E / 2 : E;  // output bytes per unit
+  __device__ static int code(const float* o) {
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(o[e]));
+    return mx_code(group_max<kLanes>(m), kEmax);
+  }
+  // The scaled conversions divide by X = 2^(c - 127) themselves (fp8 after a
+  // clamp to +-448 X); 1-element fp8 units multiply by 2^(127 - c), clamp and
+  // convert. Every scaling is exact. (MXFP8 at 4096 x 8192 bf16: 2.1% faster
+  // with the scaled conversion than multiply, clamp, convert; same codes.)
+  __device__ static typename Pack::Raw pack(const float* o, int c) {
+    if constexpr (OUT == kOutMxFp4) {
+      return Pack::pack(o, __builtin_ldexpf(1.0f, c - 127));
+    } else if constexpr (E == 8) {
+      uint32_t w[2];
+      fp8_scaled_words<8>(o, __builtin_ldexpf(1.0f, c - 127), w);
+      return (typename Pack::Raw){w[0], w[1]};
+    } else if constexpr (E == 4) {
+      uint32_t w[1];
+      fp8_scaled_words<4>(o, __builtin_ldexpf(1.0f, c - 127), w);
+      return w[0];
+    } else {
+      return Pack::pack(o, __builtin_ldexpf(1.0f, 127 - c));
+    }
+  }
+};
+
+// ------------------------------------------------------------ rare rows
+//
+// The fp32 sum of squares ss of a row is as good as its roundings whenever
+// q = ss / N + eps lies in [2^-100, FLT_MAX]: every term is non-negative, so a
+// finite total means that no partial sum overflowed, and a square rounded in
+// the subnormal range is off by at most 2^-150, i.e. the mean by at most
+// 2^-150, a relative 2^-50 of q. Outside that range -- squares that overflow
+// fp32 (|x| from about 1.8e19 up), rows whose root mean square is below about
+// 1e-15 when eps is below 2^-100 (their squares lose digits to the subnormal
+// range or vanish), an eps near the fp32 maximum -- a kernel recomputes the
+// row's statistics in fp64 and forms the row's outputs from them with the
+// scaling kept out of fp32's way (a "rare row", rare_row.hpp). Rows in range
+// never take that path, so their results do not change.
+constexpr float kRareLo = 0x1p-100f;
+
+__device__ __forceinline__ bool rare_q(float q) { return !(q >= kRareLo && q <= __FLT_MAX__); }
+
+// Backward: a row is rare when its row dot is not finite.
+struct RareDotGate {
+  __device__ bool operator()(double w) const { return !__builtin_isfinite(w); }
+  __device__ bool operator()(DSum2 w) const {
+    return !__builtin_isfinite(w.a) || !__builtin_isfinite(w.b);
+  }
+};
+
+// Blocks of several row groups of several waves each share one rare-row mask
+// (the OR of their groups' masks), so that every thread of the block takes the
+// same number of passes through the reductions of the rare-row walk.
+template <int TPR, int BLOCK>
+constexpr bool kBlockFlag = TPR > kWave && BLOCK / TPR > 1;
 
 }  // namespace rmsn

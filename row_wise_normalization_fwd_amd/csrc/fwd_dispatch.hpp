@@ -25,6 +25,7 @@
 
 #include "fwd_kernels.hpp"
 #include "fwd_split.hpp"
+#include "rare_row.hpp"
 #include "launch.hpp"
 
 namespace rmsn {
@@ -34,6 +35,10 @@ hipError_t run_fwd_reg(const FwdArgs<T, G>& a, hipStream_t s) {
   constexpr int RPB = BLOCK / TPR;
   int64_t blocks = ceil_div(a.M, RPB);
   if (blocks > kMaxGrid) blocks = kMaxGrid;
+  // At most kMaxRowIters loop iterations per row group (one bit each in the
+  // kernel's rare-row mask).
+  const int64_t min_blocks = ceil_div(a.M, RPB * kMaxRowIters);
+  if (blocks < min_blocks) blocks = min_blocks;
   fwd_reg_kernel<T, G, VEC, TPR, UPT, BLOCK, FUSED, OUT, LN>
       <<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), 0, s>>>(a);
   return hipGetLastError();
@@ -48,6 +53,8 @@ hipError_t run_fwd_pp(const FwdArgs<T, G>& a, hipStream_t s) {
   int64_t blocks = 2 * device_cus();
   const int64_t groups = ceil_div(a.M, RG);
   if (blocks > groups) blocks = groups;
+  // At most kMaxRowIters iterations per row group (the rare-row mask).
+  if (blocks < ceil_div(groups, kMaxRowIters)) blocks = ceil_div(groups, kMaxRowIters);
   fwd_pp_kernel<T, G, TPR, UPT, BLOCK, FUSED, OUT, LN>
       <<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), 0, s>>>(a);
   return hipGetLastError();
@@ -87,7 +94,7 @@ hipError_t run_fwd_split(const FwdArgs<T, G>& f, hipStream_t s) {
   if (e != hipSuccess) return e;
   int64_t fblocks = ceil_div(f.M, kSplitBlock / kWave);
   if (fblocks > kMaxGrid) fblocks = kMaxGrid;
-  fwd_split_finalize_kernel<T, G>
+  fwd_split_finalize_kernel<T, G, FUSED>
       <<<dim3(static_cast<unsigned>(fblocks)), dim3(kSplitBlock), 0, s>>>(a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -44,6 +44,7 @@
 #include <type_traits>
 
 #include "device.hpp"
+#include "rare_row.hpp"
 
 namespace rmsn {
 
@@ -64,44 +65,31 @@ struct FwdArgs {
   uint8_t* mx;                // MX outputs: E8M0 codes, [M, N / 32]
 };
 
-template <int OUT>
-constexpr bool kIsMx = OUT == kOutMxFp8 || OUT == kOutMxFp4;
-
-// MX output of one unit (E elements o of a row): the block max over the
-// 32 / E lanes holding the block (every lane of the wave must take part),
-// its E8M0 code, and the packed element codes.
-template <int OUT, int E>
-struct MxUnit {
-  static constexpr int kLanes = 32 / E;            // lanes per 32-element block
-  static constexpr int kEmax = OUT == kOutMxFp4 ? 2 : 8;
-  using Pack = typename std::conditional<OUT == kOutMxFp4, Fp4Unit<E>, Fp8Unit<E>>::type;
-  static constexpr int kBytes = OUT == kOutMxFp4 ? E / 2 : E;  // output bytes per unit
-  __device__ static int code(const float* o) {
-    float m = 0.0f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(o[e]));
-    return mx_code(group_max<kLanes>(m), kEmax);
+// The RareRow of row `row` of a forward call.
+template <class T, class G, int OUT, bool FUSED>
+__device__ __forceinline__ RareRow<T, G> rare_row_of(const FwdArgs<T, G>& a, int64_t row) {
+  const int64_t off = row * a.N;
+  RareRow<T, G> r;
+  r.src = (FUSED ? a.residual : a.x) + off;
+  r.gamma = a.gamma;
+  r.beta = a.beta;
+  r.y = a.y != nullptr ? a.y + off : nullptr;
+  r.q = nullptr;
+  r.mx = nullptr;
+  if constexpr (kIsMx<OUT>) {
+    r.q = a.q + off * MxUnit<OUT, 16 / T::kSize>::kBytes / (16 / T::kSize);
+    r.mx = a.mx + row * (a.N / 32);
+  } else if constexpr (OUT != kOutAct) {
+    r.q = a.q + off;
   }
-  // The scaled conversions divide by X = 2^(c - 127) themselves (fp8 after a
-  // clamp to +-448 X); 1-element fp8 units multiply by 2^(127 - c), clamp and
-  // convert. Every scaling is exact. (MXFP8 at 4096 x 8192 bf16: 2.1% faster
-  // with the scaled conversion than multiply, clamp, convert; same codes.)
-  __device__ static typename Pack::Raw pack(const float* o, int c) {
-    if constexpr (OUT == kOutMxFp4) {
-      return Pack::pack(o, __builtin_ldexpf(1.0f, c - 127));
-    } else if constexpr (E == 8) {
-      uint32_t w[2];
-      fp8_scaled_words<8>(o, __builtin_ldexpf(1.0f, c - 127), w);
-      return (typename Pack::Raw){w[0], w[1]};
-    } else if constexpr (E == 4) {
-      uint32_t w[1];
-      fp8_scaled_words<4>(o, __builtin_ldexpf(1.0f, c - 127), w);
-      return w[0];
-    } else {
-      return Pack::pack(o, __builtin_ldexpf(1.0f, 127 - c));
-    }
-  }
-};
+  r.rstd = a.rstd != nullptr ? a.rstd + row : nullptr;
+  r.mean = a.mean != nullptr ? a.mean + row : nullptr;
+  r.scale = OUT == kOutFp8Row ? a.scale + row : nullptr;
+  r.tinv = 0.0f;
+  r.N = a.N;
+  r.eps = a.eps;
+  return r;
+}
 
 // Sum-of-squares reduction type: the pair (sum, max) for the per-row scale.
 template <int OUT>
@@ -145,6 +133,8 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
   static_assert(BLOCK % TPR == 0 && BLOCK % kWave == 0, "block shape");
   static_assert(!LN || (!FUSED && OUT == kOutAct), "LayerNorm: plain output only");
   __shared__ RedT<OUT> red[2 * (BLOCK / kWave)];
+  __shared__ RareRedT<OUT> rared[2 * (BLOCK / kWave)];  // rare rows (after the loop)
+  __shared__ uint64_t rmasks[RPB];
   const float tinv = tensor_inv_scale<T, G, OUT>(a);
 
   const int nunits = a.N / E;
@@ -177,10 +167,12 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
   }
 
   int parity = 0;
+  uint64_t rare_mask = 0;  // bit t: this group's row of iteration t is rare
+  int t = 0;
   // `base` is uniform over the block, so every thread runs the same number of
   // iterations and reaches every reduction.
   for (int64_t base = static_cast<int64_t>(blockIdx.x) * RPB; base < a.M;
-       base += static_cast<int64_t>(gridDim.x) * RPB) {
+       base += static_cast<int64_t>(gridDim.x) * RPB, ++t) {
     const int64_t row = base + grp;
     const bool valid = row < a.M;
     const int64_t off = row * a.N;
@@ -219,8 +211,8 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
     for (int k = 1; k < UPT; ++k) ss = ss + part[k];
 
     float inv = tinv;
-    float rs;
-    [[maybe_unused]] float mu = 0.0f;
+    float rs, q;
+    [[maybe_unused]] float mu = 0.0f, amax = 0.0f;
     if constexpr (LN) {
       // Mean, then the sum of squared deviations of the values in registers
       // (masked units excluded).
@@ -241,8 +233,8 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
 #pragma unroll
       for (int k = 1; k < UPT; ++k) sq = sq + part[k];
       sq = row_sum<TPR, BLOCK>(sq, red, parity);
-      rs = 1.0f / __builtin_sqrtf(sq / static_cast<float>(a.N) + a.eps);
-      if (a.mean != nullptr && valid && lane == 0) a.mean[row] = mu;
+      q = sq / static_cast<float>(a.N) + a.eps;
+      rs = 1.0f / __builtin_sqrtf(q);
     } else if constexpr (OUT == kOutFp8Row) {
       float m = 0.0f;
 #pragma unroll
@@ -250,16 +242,27 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
 #pragma unroll
         for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[k][e] * gam[k][e]));
       const SumMax r = row_sum<TPR, BLOCK>(SumMax{ss, m}, red, parity);
-      rs = 1.0f / __builtin_sqrtf(r.s / static_cast<float>(a.N) + a.eps);
-      const float amax = r.m * rs;
+      q = r.s / static_cast<float>(a.N) + a.eps;
+      rs = 1.0f / __builtin_sqrtf(q);
+      amax = r.m * rs;
       inv = row_inv_scale(amax);
-      if (valid && lane == 0) a.scale[row] = amax / kFp8Max;
     } else {
       ss = row_sum<TPR, BLOCK>(ss, red, parity);
-      rs = 1.0f / __builtin_sqrtf(ss / static_cast<float>(a.N) + a.eps);
+      q = ss / static_cast<float>(a.N) + a.eps;
+      rs = 1.0f / __builtin_sqrtf(q);
     }
     parity ^= 1;
-    if (a.rstd != nullptr && valid && lane == 0) a.rstd[row] = rs;
+    // A rare row (see rare_q) stores nothing now; it is redone after the loop.
+    const bool rare = rare_q(q);
+    rare_mask |= static_cast<uint64_t>(rare) << t;
+    const bool keep = valid && !rare;
+    if (keep && lane == 0) {
+      if constexpr (LN) {
+        if (a.mean != nullptr) a.mean[row] = mu;
+      }
+      if constexpr (OUT == kOutFp8Row) a.scale[row] = amax / kFp8Max;
+      if (a.rstd != nullptr) a.rstd[row] = rs;
+    }
 
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
@@ -270,11 +273,11 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = v[k][e] * gam[k][e] * rs;
         const int c = X::code(o);
-        if (valid && u < nunits) {
+        if (keep && u < nunits) {
           X::Pack::store_nt(a.q + off * X::kBytes / E + u * X::kBytes, X::pack(o, c));
           if (u % X::kLanes == 0) a.mx[row * (a.N / 32) + u / X::kLanes] = static_cast<uint8_t>(c);
         }
-      } else if (valid && u < nunits) {
+      } else if (keep && u < nunits) {
         float o[E];
         if constexpr (LN) {
 #pragma unroll
@@ -292,6 +295,18 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
       }
     }
   }
+
+  rare_rows_after<T, G, VEC, TPR, BLOCK, OUT, LN>(
+      rare_mask,
+      [&](int it, RareRow<T, G>& r) {
+        const int64_t row =
+            static_cast<int64_t>(blockIdx.x) * RPB + static_cast<int64_t>(it) * gridDim.x * RPB + grp;
+        const bool ok = row < a.M;
+        r = rare_row_of<T, G, OUT, FUSED>(a, ok ? row : 0);
+        r.tinv = tinv;
+        return ok;
+      },
+      lane, rared, rmasks);
 }
 
 // Persistent register path for 16-byte-aligned rows. The grid has one block
@@ -315,6 +330,8 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
   static_assert(!LN || (!FUSED && OUT == kOutAct), "LayerNorm: plain output only");
   static_assert(OUT == kOutAct || E == 8, "fp8 units of 8 bytes");
   __shared__ RedT<OUT> red[2 * (BLOCK / kWave)];
+  __shared__ RareRedT<OUT> rared[2 * (BLOCK / kWave)];  // rare rows (after the loop)
+  __shared__ uint64_t rmasks[RG];
   const float tinv = tensor_inv_scale<T, G, OUT>(a);
 
   const int nunits = a.N / E;
@@ -377,11 +394,12 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
     return static_cast<uint32_t>(rest < 0x7fffffff ? rest : 0x7fffffff);
   };
   // Per-row fp32 outputs (rstd, scale): one lane per row stores through a
-  // buffer based at row0, out of range for lanes that do not own a row.
-  auto store_row_value = [&](float* base, int64_t row0, float val) {
+  // buffer based at row0, out of range for lanes that do not own a row (or
+  // whose row is rare).
+  auto store_row_value = [&](float* base, int64_t row0, float val, bool rare) {
     const int64_t rest = (a.M - row0) * 4;
     const auto r = make_rsrc(base + row0, static_cast<uint32_t>(rest < 0x7fffffff ? rest : 0x7fffffff));
-    const bool mine = lane == 0 && row0 + nblk * grp < a.M;
+    const bool mine = lane == 0 && !rare && row0 + nblk * grp < a.M;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), r,
                                           mine ? static_cast<uint32_t>(nblk * grp * 4) : kBufOutOfRange,
                                           0, 0);
@@ -401,6 +419,8 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
   };
 
   int parity = 0;
+  uint64_t rare_mask = 0;  // bit t: this group's row of iteration t is rare
+  int t = 0;
   auto step = [&](int64_t row0, Raw* cx, Raw* cr, Raw* nx, Raw* nr) {
     load_rows(row0 + nblk * RG, nx, nr);
     const uint32_t n = span_bytes(row0);
@@ -457,8 +477,8 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
 #pragma unroll
       for (int k = 0; k < UPT; ++k) opaque(cx[k]);
     }
-    float rs, inv = tinv;
-    [[maybe_unused]] float mu = 0.0f;
+    float rs, q, inv = tinv;
+    [[maybe_unused]] float mu = 0.0f, amax = 0.0f;
     if constexpr (LN) {
       mu = row_sum<TPR, BLOCK>(ss, red, parity) / static_cast<float>(a.N);
       parity ^= 1;
@@ -474,19 +494,30 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
         sq = sq + (unit_offset(row0, k) != kBufOutOfRange ? s : 0.0f);
       }
       sq = row_sum<TPR, BLOCK>(sq, red, parity);
-      rs = 1.0f / __builtin_sqrtf(sq / static_cast<float>(a.N) + a.eps);
-      if (a.mean != nullptr) store_row_value(a.mean, row0, mu);
+      q = sq / static_cast<float>(a.N) + a.eps;
+      rs = 1.0f / __builtin_sqrtf(q);
     } else if constexpr (OUT == kOutFp8Row) {
       const SumMax r = row_sum<TPR, BLOCK>(SumMax{ss, m}, red, parity);
-      rs = 1.0f / __builtin_sqrtf(r.s / static_cast<float>(a.N) + a.eps);
-      const float amax = r.m * rs;
+      q = r.s / static_cast<float>(a.N) + a.eps;
+      rs = 1.0f / __builtin_sqrtf(q);
+      amax = r.m * rs;
       inv = row_inv_scale(amax);
-      store_row_value(a.scale, row0, amax / kFp8Max);
     } else {
       ss = row_sum<TPR, BLOCK>(ss, red, parity);
-      rs = 1.0f / __builtin_sqrtf(ss / static_cast<float>(a.N) + a.eps);
+      q = ss / static_cast<float>(a.N) + a.eps;
+      rs = 1.0f / __builtin_sqrtf(q);
     }
     parity ^= 1;
+    // A rare row (see rare_q) stores nothing now (out-of-range offsets); it
+    // is redone after the loop.
+    const bool rare = rare_q(q);
+    rare_mask |= static_cast<uint64_t>(rare) << t;
+    ++t;
+    auto out_offset = [&](int k) { return rare ? kBufOutOfRange : unit_offset(row0, k); };
+    if constexpr (LN) {
+      if (a.mean != nullptr) store_row_value(a.mean, row0, mu, rare);
+    }
+    if constexpr (OUT == kOutFp8Row) store_row_value(a.scale, row0, amax / kFp8Max, rare);
     if constexpr (OUT == kOutAct) {
       const auto rsy = make_rsrc(a.y + row0 * a.N, n);
 #pragma unroll
@@ -503,7 +534,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
 #pragma unroll
           for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
         }
-        buf_store16_nt(U::narrow(o), rsy, unit_offset(row0, k));
+        buf_store16_nt(U::narrow(o), rsy, out_offset(k));
       }
     } else if constexpr (kIsMx<OUT>) {
       // MX: 8 (fp8) or 4 (fp4) output bytes per 16-byte unit, so offsets are
@@ -524,7 +555,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = p[k][e] * rs;
         const int c = X::code(o);
-        const uint32_t off = unit_offset(row0, k);
+        const uint32_t off = out_offset(k);
         const uint32_t qoff = off == kBufOutOfRange ? off : off >> kShift;
         if constexpr (OUT == kOutMxFp4) {
           __builtin_amdgcn_raw_buffer_store_b32(X::pack(o, c), rsq, qoff, 0, kBufNT);
@@ -544,12 +575,12 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
       const float kq = rs * inv;
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
-        const uint32_t off = unit_offset(row0, k);
+        const uint32_t off = out_offset(k);
         __builtin_amdgcn_raw_buffer_store_b64(Fp8Unit<8>::pack(p[k], kq), rsq,
                                               off == kBufOutOfRange ? off : off >> 1, 0, kBufNT);
       }
     }
-    if (a.rstd != nullptr) store_row_value(a.rstd, row0, rs);
+    if (a.rstd != nullptr) store_row_value(a.rstd, row0, rs, rare);
   };
 
   // For 16-bit gamma and an activation output the parameters are loaded
@@ -580,6 +611,16 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
     if (b + nblk * (s0 + RG) >= a.M) break;
     step(b + nblk * (s0 + RG), bx, br, ax, ar);
   }
+  rare_rows_after<T, G, true, TPR, BLOCK, OUT, LN>(
+      rare_mask,
+      [&](int it, RareRow<T, G>& r) {
+        const int64_t row = b + nblk * (static_cast<int64_t>(RG) * it + grp);
+        const bool ok = row < a.M;
+        r = rare_row_of<T, G, OUT, FUSED>(a, ok ? row : 0);
+        r.tinv = tinv;
+        return ok;
+      },
+      lane, rared, rmasks);
 }
 
 template <class T, class G, bool VEC, int BLOCK, int UNROLL, bool FUSED, bool CACHE, int OUT,
@@ -592,12 +633,13 @@ __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
   constexpr int STEP = BLOCK * UNROLL;
   static_assert(!LN || (!FUSED && OUT == kOutAct), "LayerNorm: plain output only");
   __shared__ RedT<OUT> red[2 * (BLOCK / kWave)];
+  __shared__ RareRedT<OUT> rared[2 * (BLOCK / kWave)];  // rare rows
   const float tinv = tensor_inv_scale<T, G, OUT>(a);
   extern __shared__ __align__(16) unsigned char lds_bytes[];
   Raw* cache = reinterpret_cast<Raw*>(lds_bytes);
 
   const int nunits = a.N / E;
-  int parity = 0;
+  int parity = 0, rparity = 0;
   for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x) {
     const int64_t off = row * a.N;
     float ss = 0.0f;
@@ -645,7 +687,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
     // Fused rows re-read the rounded h written back to `residual`; each lane
     // re-reads only units it wrote itself.
     const typename T::S* src = FUSED ? a.residual : a.x;
-    float rs, inv = tinv;
+    float rs, q, inv = tinv;
     [[maybe_unused]] float mu = 0.0f;
     if constexpr (LN) {
       // Mean, then a pass over the cached (or re-read) row for the sum of
@@ -676,19 +718,30 @@ __global__ __launch_bounds__(BLOCK) void fwd_long_kernel(FwdArgs<T, G> a) {
         }
       }
       sq = row_sum<BLOCK, BLOCK>(sq, red, parity);
-      rs = 1.0f / __builtin_sqrtf(sq / static_cast<float>(a.N) + a.eps);
-      if (a.mean != nullptr && threadIdx.x == 0) a.mean[row] = mu;
+      q = sq / static_cast<float>(a.N) + a.eps;
+      rs = 1.0f / __builtin_sqrtf(q);
+      if (a.mean != nullptr && threadIdx.x == 0 && !rare_q(q)) a.mean[row] = mu;
     } else if constexpr (OUT == kOutFp8Row) {
       const SumMax r = row_sum<BLOCK, BLOCK>(SumMax{ss, m}, red, parity);
-      rs = 1.0f / __builtin_sqrtf(r.s / static_cast<float>(a.N) + a.eps);
+      q = r.s / static_cast<float>(a.N) + a.eps;
+      rs = 1.0f / __builtin_sqrtf(q);
       const float amax = r.m * rs;
       inv = row_inv_scale(amax);
-      if (threadIdx.x == 0) a.scale[row] = amax / kFp8Max;
+      if (threadIdx.x == 0 && !rare_q(q)) a.scale[row] = amax / kFp8Max;
     } else {
       ss = row_sum<BLOCK, BLOCK>(ss, red, parity);
-      rs = 1.0f / __builtin_sqrtf(ss / static_cast<float>(a.N) + a.eps);
+      q = ss / static_cast<float>(a.N) + a.eps;
+      rs = 1.0f / __builtin_sqrtf(q);
     }
     parity ^= 1;
+    // One row per block, so the rare test (see rare_q) is block-uniform; a
+    // rare row is redone in fp64 from memory and skips the output pass.
+    if (rare_q(q)) {
+      RareRow<T, G> r = rare_row_of<T, G, OUT, FUSED>(a, row);
+      r.tinv = tinv;
+      rare_row<T, G, VEC, BLOCK, BLOCK, OUT, LN>(r, threadIdx.x, true, rared, rparity);
+      continue;
+    }
     if (a.rstd != nullptr && threadIdx.x == 0) a.rstd[row] = rs;
 
     // Output pass.

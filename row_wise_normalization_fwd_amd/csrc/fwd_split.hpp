@@ -11,8 +11,12 @@
 //   2. finalize: one wave per row adds the row's partials in a fixed order
 //      in fp64, forms rstd = 1 / sqrt(ss / N + eps) and writes it back into
 //      every one of the row's slots (and to the rstd output when present);
+//      a row whose ss / N + eps is out of the fp32 range the kernels trust
+//      (see rare_q) is re-read and its sum of squares recomputed in fp64,
+//      and its slots get rstd as a factor f * 2^e instead;
 //   3. apply: each tile's block reads its own slot, then writes y over the
-//      tile (x, or h from the residual, times rstd times gamma).
+//      tile (x, or h from the residual, times rstd times gamma; for such a
+//      row x 2^e times f times gamma).
 // The forward takes no workspace and the library never allocates, so y holds
 // the partials until it is written; a slot is only ever read by the block
 // that owns its region, so no block overwrites a slot another still needs.
@@ -24,6 +28,7 @@
 #pragma once
 
 #include "device.hpp"
+#include "rare_row.hpp"
 
 namespace rmsn {
 
@@ -50,6 +55,10 @@ constexpr int split_chunk() {
   return kSplitBlock * kSplitUpt * (16 / T::kSize);
 }
 
+// The tile's slot: 8 bytes at the start of its region of y (every tile holds
+// at least one 16-byte unit). The partial pass parks the tile's sum of
+// squares in the first word; finalize replaces the slot by rstd as
+// {f, e} (f an fp32, e an int32; e = 0 with f = rstd for every row in range).
 template <class T, class G>
 __device__ __forceinline__ float* split_slot(const SplitArgs<T, G>& a, int64_t row, int chunk) {
   return reinterpret_cast<float*>(a.y + row * a.N + static_cast<int64_t>(chunk) * split_chunk<T>());
@@ -102,7 +111,7 @@ __global__ __launch_bounds__(kSplitBlock) void fwd_split_partial_kernel(SplitArg
 }
 
 // One wave per row (four rows per 256-thread block).
-template <class T, class G>
+template <class T, class G, bool FUSED>
 __global__ __launch_bounds__(kSplitBlock) void fwd_split_finalize_kernel(SplitArgs<T, G> a) {
   constexpr int kRows = kSplitBlock / kWave;
   const int lane = threadIdx.x % kWave;
@@ -114,9 +123,35 @@ __global__ __launch_bounds__(kSplitBlock) void fwd_split_finalize_kernel(SplitAr
     double s = 0.0;
     for (int c = lane; c < a.chunks; c += kWave) s = s + static_cast<double>(*split_slot(a, row, c));
     s = group_sum<kWave>(s);
-    const float rs = 1.0f / __builtin_sqrtf(static_cast<float>(s) / static_cast<float>(a.N) + a.eps);
-    // Every lane's reads above feed rs, so they complete before these writes.
-    for (int c = lane; c < a.chunks; c += kWave) *split_slot(a, row, c) = rs;
+    const float q = static_cast<float>(s) / static_cast<float>(a.N) + a.eps;
+    float f = 1.0f / __builtin_sqrtf(q), rs = f;
+    int e = 0;
+    if (rare_q(q)) {
+      // The row again, in fp64 (h from the residual when fused, which the
+      // partial pass wrote in an earlier launch).
+      using U = Unit<T, true>;
+      constexpr int E = U::E;
+      const typename T::S* src = (FUSED ? a.residual : a.x) + row * a.N;
+      double d = 0.0;
+      for (int u = lane; u < a.N / E; u += kWave) {
+        float v[E];
+        U::widen(U::load(src + u * E), v);
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+          const double w = static_cast<double>(v[j]);
+          d = __builtin_fma(w, w, d);
+        }
+      }
+      d = group_sum<kWave>(d);
+      rsqrt_factor(d / static_cast<double>(a.N) + static_cast<double>(a.eps), f, e);
+      rs = __builtin_ldexpf(f, e);
+    }
+    // Every lane's reads above feed f, so they complete before these writes.
+    for (int c = lane; c < a.chunks; c += kWave) {
+      float* slot = split_slot(a, row, c);
+      slot[0] = f;
+      reinterpret_cast<int*>(slot)[1] = e;
+    }
     if (a.rstd != nullptr && lane == 0) a.rstd[row] = rs;
   }
 }
@@ -131,20 +166,38 @@ __global__ __launch_bounds__(kSplitBlock) void fwd_split_apply_kernel(SplitArgs<
     const int c = static_cast<int>(t - row * a.chunks);
     const int64_t off = row * a.N;
     const int u0 = c * (kSplitBlock * kSplitUpt);
-    const float rs = *split_slot(a, row, c);
-    // Every thread holds rs before any store can overwrite the slot.
+    const float* slot = split_slot(a, row, c);
+    const float rs = slot[0];
+    const int ex = reinterpret_cast<const int*>(slot)[1];
+    // Every thread holds the slot before any store can overwrite it.
     __syncthreads();
     const typename T::S* src = FUSED ? a.residual : a.x;
+    if (ex == 0) {  // uniform over the tile
 #pragma unroll
-    for (int k = 0; k < kSplitUpt; ++k) {
-      const int u = u0 + threadIdx.x + k * kSplitBlock;
-      if (u < nunits) {
-        float v[E], g[E], o[E];
-        U::widen(U::load_nt(src + off + u * E), v);
-        load_gamma<G, E, true>(a.gamma, u * E, g);
+      for (int k = 0; k < kSplitUpt; ++k) {
+        const int u = u0 + threadIdx.x + k * kSplitBlock;
+        if (u < nunits) {
+          float v[E], g[E], o[E];
+          U::widen(U::load_nt(src + off + u * E), v);
+          load_gamma<G, E, true>(a.gamma, u * E, g);
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
-        U::store_nt(a.y + off + u * E, U::narrow(o));
+          for (int e = 0; e < E; ++e) o[e] = v[e] * rs * g[e];
+          U::store_nt(a.y + off + u * E, U::narrow(o));
+        }
+      }
+    } else {
+      RareStats st{rs, ex, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < kSplitUpt; ++k) {
+        const int u = u0 + threadIdx.x + k * kSplitBlock;
+        if (u < nunits) {
+          float v[E], g[E], o[E];
+          U::widen(U::load_nt(src + off + u * E), v);
+          load_gamma<G, E, true>(a.gamma, u * E, g);
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[e] = rare_value<kOutAct, false>(v[e], g[e], 0.0f, st);
+          U::store_nt(a.y + off + u * E, U::narrow(o));
+        }
       }
     }
   }

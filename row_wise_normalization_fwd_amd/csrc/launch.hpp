@@ -98,23 +98,27 @@ struct QKCall {
 
 hipError_t launch_qk(const QKCall& c, int x_dtype);
 
-// Backward partition: G = min(M, kBwdTargetBlocks) blocks, block b owning
-// rows b, b + G, b + 2G, ... It depends only on M, which fixes the dgamma
-// summation order. The workspace holds the fp32 partial rows [G, N] and, for
-// rows longer than kBwdOnChipN, the per-row dots [M] (double) of the
-// two-pass long-row tier.
+// Backward partition: G = max(min(M, kBwdTargetBlocks), ceil(M /
+// kBwdMaxRowsPerBlock)) blocks, block b owning rows b, b + G, b + 2G, ... It
+// depends only on M, which fixes the dgamma summation order. The workspace
+// holds the fp32 partial rows [G, N] and, for rows longer than kBwdOnChipN,
+// a 16-byte record per row (the row dots of the two-pass long-row tier).
 struct BwdPlan {
   bool valid;
   int64_t blocks;  // G
   size_t partial_bytes;    // bytes of one partial array (the row dots follow the arrays)
   size_t workspace_bytes;
 };
-BwdPlan plan_bwd(int64_t M, int64_t N, int x_dtype);
-// LayerNorm: two partial arrays (dgamma, dbeta), then two doubles per row
-// for rows too long to keep on chip.
-BwdPlan plan_ln_bwd(int64_t M, int64_t N, int x_dtype);
+BwdPlan plan_bwd(int64_t M, int64_t N);
+// LayerNorm: two partial arrays (dgamma, dbeta), then the same per-row
+// records.
+BwdPlan plan_ln_bwd(int64_t M, int64_t N);
 
 constexpr int64_t kBwdTargetBlocks = 256;
+// Rows per partition block at most: each dgamma partial is an fp32 sum of
+// that many rows, and each stage-1 row group runs at most that many loop
+// iterations (its rare-row mask has 64 bits).
+constexpr int64_t kBwdMaxRowsPerBlock = 64;
 // Rows up to this many elements may use the one-pass backward (registers);
 // longer rows use the two-pass long-row tier when they do not fit.
 constexpr int64_t kBwdOnChipN = 8192;

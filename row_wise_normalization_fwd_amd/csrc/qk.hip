@@ -17,6 +17,9 @@ hipError_t run_qk(QKArgs<T, G> a, hipStream_t s) {
   // the rest).
   int64_t blocks = ceil_div(a.rows, RPB);
   if (blocks > kMaxGrid) blocks = kMaxGrid;
+  // At most kMaxRowIters iterations per row group (the rare-row mask).
+  const int64_t min_blocks = ceil_div(a.rows, RPB * kMaxRowIters);
+  if (blocks < min_blocks) blocks = min_blocks;
   if (blocks == 0) return hipSuccess;
   // Each wave holds kWave / TPR consecutive rows starting at a multiple of
   // that; when both head counts are multiples of it, a wave's rows are all q

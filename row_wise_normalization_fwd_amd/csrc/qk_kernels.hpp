@@ -23,6 +23,7 @@
 #pragma once
 
 #include "device.hpp"
+#include "rare_row.hpp"
 
 namespace rmsn {
 
@@ -46,6 +47,8 @@ __global__ __launch_bounds__(BLOCK) void qk_norm_kernel(QKArgs<T, G> a) {
   constexpr int RPB = BLOCK / TPR;
   static_assert(BLOCK % TPR == 0 && BLOCK % kWave == 0, "block shape");
   __shared__ float red[2 * (BLOCK / kWave)];
+  __shared__ double rared[2 * (BLOCK / kWave)];  // rare rows (after the loop)
+  __shared__ uint64_t rmasks[RPB];
 
   const int nunits = a.N / E;
   const int grp = threadIdx.x / TPR;
@@ -72,9 +75,11 @@ __global__ __launch_bounds__(BLOCK) void qk_norm_kernel(QKArgs<T, G> a) {
   }
 
   int parity = 0;
+  uint64_t rare_mask = 0;  // bit i: this group's row of loop iteration i is rare
+  int iter = 0;
   // `base` is uniform over the block: every thread reaches every reduction.
   for (uint64_t base = static_cast<uint64_t>(blockIdx.x) * RPB; base < a.rows;
-       base += static_cast<uint64_t>(gridDim.x) * RPB) {
+       base += static_cast<uint64_t>(gridDim.x) * RPB, ++iter) {
     const uint32_t row = static_cast<uint32_t>(base) + grp;
     const bool valid = base + grp < a.rows;
     const uint32_t tq = a.hmul != 0u ? (__umulhi(row, a.hmul) >> a.hshift) : (row >> a.hshift);
@@ -104,12 +109,17 @@ __global__ __launch_bounds__(BLOCK) void qk_norm_kernel(QKArgs<T, G> a) {
     }
     ss = row_sum<TPR, BLOCK>(ss, red, parity);
     parity ^= 1;
-    const float rs = 1.0f / __builtin_sqrtf(ss / static_cast<float>(a.N) + a.eps);
+    const float q = ss / static_cast<float>(a.N) + a.eps;
+    const float rs = 1.0f / __builtin_sqrtf(q);
+    // A rare row (see rare_q) stores nothing now; it is redone after the loop.
+    const bool rare = rare_q(q);
+    rare_mask |= static_cast<uint64_t>(rare) << iter;
+    const bool keep = valid && !rare;
     auto out = [&](const float (&gg)[UPT][E]) {
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
         const int u = lane + k * TPR;
-        if (valid && u < nunits) {
+        if (keep && u < nunits) {
           float o[E];
 #pragma unroll
           for (int e = 0; e < E; ++e) o[e] = v[k][e] * rs * gg[k][e];
@@ -124,7 +134,7 @@ __global__ __launch_bounds__(BLOCK) void qk_norm_kernel(QKArgs<T, G> a) {
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
         const int u = lane + k * TPR;
-        if (valid && u < nunits) {
+        if (keep && u < nunits) {
           float o[E];
 #pragma unroll
           for (int e = 0; e < E; ++e) o[e] = v[k][e] * rs * (isk ? gk[k][e] : gq[k][e]);
@@ -133,6 +143,31 @@ __global__ __launch_bounds__(BLOCK) void qk_norm_kernel(QKArgs<T, G> a) {
       }
     }
   }
+  rare_rows_after<T, G, VEC, TPR, BLOCK, kOutAct, false>(
+      rare_mask,
+      [&](int it, RareRow<T, G>& r) {
+        const uint64_t row64 = static_cast<uint64_t>(blockIdx.x) * RPB +
+                               static_cast<uint64_t>(it) * gridDim.x * RPB + grp;
+        const bool ok = row64 < a.rows;
+        const uint32_t row = ok ? static_cast<uint32_t>(row64) : 0u;
+        const uint32_t tok = a.hmul != 0u ? (__umulhi(row, a.hmul) >> a.hshift) : (row >> a.hshift);
+        const uint32_t h = row - tok * H;
+        const bool isk = h >= hq;
+        typename T::S* const x = isk ? a.x[1] : a.x[0];
+        const int64_t off = static_cast<int64_t>(tok) * (isk ? a.stride[1] : a.stride[0]) +
+                            static_cast<int64_t>(isk ? h - hq : h) * a.N;
+        r.src = x + off;
+        r.gamma = isk ? a.gamma[1] : a.gamma[0];
+        r.beta = nullptr;
+        r.y = x + off;
+        r.q = r.mx = nullptr;
+        r.rstd = r.mean = r.scale = nullptr;
+        r.tinv = 0.0f;
+        r.N = a.N;
+        r.eps = a.eps;
+        return ok;
+      },
+      lane, rared, rmasks);
 }
 
 }  // namespace rmsn

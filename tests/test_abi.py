@@ -105,24 +105,39 @@ def test_fused_validation(lib):
 
 def bwd(dy=A, x=B, rstd=C, g=D, dx=E, dg=F, ws=G, wsb=None, M=64, N=256, xd=BF16, gd=BF16):
     if wsb is None:
-        wsb = R.rmsnorm_bwd_workspace_size(M, N, xd)
+        wsb = R.rmsnorm_bwd_workspace_size(M, N)
     return R.rmsnorm_bwd(dy, x, rstd, g, dx, dg, ws, wsb, M, N, xd, gd, None)
 
 
 def test_workspace_size():
-    # One fp32 partial row per partition block, min(M, 256) blocks, rounded
-    # up to 256 bytes.
-    assert R.rmsnorm_bwd_workspace_size(8192, 8192, BF16) == 256 * 8192 * 4
-    assert R.rmsnorm_bwd_workspace_size(3, 10, F32) == 256          # 3*10*4 = 120 -> 256
-    assert R.rmsnorm_bwd_workspace_size(1000, 64, F16) == 256 * 64 * 4
-    assert R.rmsnorm_bwd_workspace_size(200, 64, F16) == 200 * 64 * 4
-    assert R.rmsnorm_bwd_workspace_size(0, 64, F16) == 0
-    assert R.rmsnorm_bwd_workspace_size(10, 0, F16) == 0
-    assert R.rmsnorm_bwd_workspace_size(10, 10, 7) == 0
-    # Rows longer than 8192 also hold one double per row (row dots), each
-    # region rounded up to 256 bytes.
-    assert R.rmsnorm_bwd_workspace_size(1000, 10000, BF16) == 256 * 10000 * 4 + 8192
-    assert R.rmsnorm_bwd_workspace_size(3, 8193, F32) == 98_560 + 256   # 98,316 -> 98,560
+    # One fp32 partial row per partition block, G = max(min(M, 256),
+    # ceil(M / 64)) blocks (every block owns at most 64 rows), rounded up to
+    # 256 bytes. The size depends on (M, N) only.
+    assert R.rmsnorm_bwd_workspace_size(8192, 8192) == 256 * 8192 * 4
+    assert R.rmsnorm_bwd_workspace_size(3, 10) == 256          # 3*10*4 = 120 -> 256
+    assert R.rmsnorm_bwd_workspace_size(1000, 64) == 256 * 64 * 4
+    assert R.rmsnorm_bwd_workspace_size(200, 64) == 200 * 64 * 4
+    assert R.rmsnorm_bwd_workspace_size(16384, 4096) == 256 * 4096 * 4     # 64 rows per block
+    assert R.rmsnorm_bwd_workspace_size(16385, 4096) == 257 * 4096 * 4     # one block more
+    assert R.rmsnorm_bwd_workspace_size(131072, 1024) == 2048 * 1024 * 4
+    assert R.rmsnorm_bwd_workspace_size(0, 64) == 0
+    assert R.rmsnorm_bwd_workspace_size(10, 0) == 0
+    assert R.rmsnorm_bwd_workspace_size(10, 2**31 - 1) == 0    # beyond RMSN_MAX_N
+    # Rows longer than 8192 also hold a 16-byte record per row (the two-pass
+    # tier's row dots), each region rounded up to 256 bytes.
+    assert R.rmsnorm_bwd_workspace_size(1000, 10000) == 256 * 10000 * 4 + 16128
+    assert R.rmsnorm_bwd_workspace_size(3, 8193) == 98_560 + 256   # 98,316 -> 98,560
+    assert R.rmsnorm_bwd_workspace_size(3, 8192) == 98_304         # no records at 8192
+
+
+def test_max_n():
+    # N up to RMSN_MAX_N (2^31 - 2^20) is accepted: the argument checks pass
+    # and the call reaches the NULL check; one more is a shape error.
+    n_max = 2**31 - 2**20
+    assert R.rmsnorm_fwd(None, None, None, None, 1, n_max + 1, 1e-5, BF16, BF16, None) == SHAPE
+    assert R.rmsnorm_fwd(None, None, None, None, 1, n_max, 1e-5, BF16, BF16, None) == NULL
+    assert R.layernorm_fwd(None, None, None, None, None, None, 1, n_max + 1, 1e-5, BF16, BF16,
+                           None) == SHAPE
 
 
 def test_backward_validation(lib):
@@ -135,7 +150,7 @@ def test_backward_validation(lib):
     for k in ("dy", "x", "rstd", "g", "dx", "dg"):
         assert bwd(**{k: None}) == NULL, k
     assert bwd(ws=None) == WORKSPACE
-    assert bwd(wsb=R.rmsnorm_bwd_workspace_size(64, 256, BF16) - 4) == WORKSPACE
+    assert bwd(wsb=R.rmsnorm_bwd_workspace_size(64, 256) - 4) == WORKSPACE
     assert bwd(dy=A + 1) == ALIGN
     assert bwd(ws=G + 8) == ALIGN
     assert bwd(dg=F + 2) == ALIGN
@@ -152,7 +167,7 @@ H = 0x80000000  # an eighth well-separated address, for dresidual
 def fbwd(dy=A, h=B, rstd=C, g=D, dres=H, dh=E, dg=F, ws=G, wsb=None, M=64, N=256, xd=BF16,
          gd=BF16):
     if wsb is None:
-        wsb = R.rmsnorm_bwd_workspace_size(M, N, xd)
+        wsb = R.rmsnorm_bwd_workspace_size(M, N)
     return R.rmsnorm_fused_add_bwd(dy, h, rstd, g, dres, dh, dg, ws, wsb, M, N, xd, gd, None)
 
 
@@ -261,17 +276,18 @@ def test_layernorm_validation(lib):
 def lnb(dy=A, x=B, mean=C, rstd=C + 4096, g=D, dx=E, dg=F, db=F + 65536, ws=G, wsb=None, M=64,
         N=256, xd=BF16, gd=BF16):
     if wsb is None:
-        wsb = R.layernorm_bwd_workspace_size(M, N, xd)
+        wsb = R.layernorm_bwd_workspace_size(M, N)
     return R.layernorm_bwd(dy, x, mean, rstd, g, dx, dg, db, ws, wsb, M, N, xd, gd, None)
 
 
 def test_layernorm_workspace_size():
-    # Two fp32 partial arrays of min(M, 256) rows; rows longer than 8192 add
-    # two doubles per row.
-    assert R.layernorm_bwd_workspace_size(8192, 8192, BF16) == 2 * 256 * 8192 * 4
-    assert R.layernorm_bwd_workspace_size(3, 10, F32) == 2 * 256
-    assert R.layernorm_bwd_workspace_size(1000, 10000, BF16) == 2 * 256 * 10000 * 4 + 16128
-    assert R.layernorm_bwd_workspace_size(0, 10, BF16) == 0
+    # Two fp32 partial arrays of G rows (as for RMSNorm); rows longer than
+    # 8192 add a 16-byte record per row.
+    assert R.layernorm_bwd_workspace_size(8192, 8192) == 2 * 256 * 8192 * 4
+    assert R.layernorm_bwd_workspace_size(3, 10) == 2 * 256
+    assert R.layernorm_bwd_workspace_size(1000, 10000) == 2 * 256 * 10000 * 4 + 16128
+    assert R.layernorm_bwd_workspace_size(131072, 1024) == 2 * 2048 * 1024 * 4
+    assert R.layernorm_bwd_workspace_size(0, 10) == 0
 
 
 def test_layernorm_backward_validation(lib):
@@ -282,7 +298,7 @@ def test_layernorm_backward_validation(lib):
     for k in ("dy", "x", "mean", "rstd", "g", "dx", "dg"):
         assert lnb(**{k: None}) == NULL, k
     assert lnb(ws=None) == WORKSPACE
-    assert lnb(wsb=R.layernorm_bwd_workspace_size(64, 256, BF16) - 1) == WORKSPACE
+    assert lnb(wsb=R.layernorm_bwd_workspace_size(64, 256) - 1) == WORKSPACE
     assert lnb(mean=C + 2) == ALIGN
     assert lnb(db=F + 65536 + 2) == ALIGN
     assert lnb(dx=A + 64) == OVERLAP

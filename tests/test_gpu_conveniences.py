@@ -126,7 +126,7 @@ def test_layernorm_conveniences():
     _same(rstd.reshape(-1), r2, "layernorm rstd")
     dx, dg, db = R.layernorm_backward(dyt, xt, mean, rstd, gt)
     dx2, dg2, db2 = torch.empty_like(xt), torch.empty(N, device="cuda"), torch.empty(N, device="cuda")
-    wsb = R.layernorm_bwd_workspace_size(M, N, BF)
+    wsb = R.layernorm_bwd_workspace_size(M, N)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     assert R.layernorm_bwd(dyt, xt, m2, r2, gt, dx2, dg2, db2, ws, wsb, M, N, BF, BF,
                            _stream()) == 0
@@ -141,7 +141,7 @@ def test_backward_conveniences():
     xt, gt, dyt = _t(x).view(SHAPE), _t(g), _t(dy).view(SHAPE)
     _, rstd = R.fwd(xt, gt, 1e-5, want_rstd=True)
     # A float32 workspace: its size in bytes, not elements, must reach the library.
-    wsb = R.rmsnorm_bwd_workspace_size(M, N, BF)
+    wsb = R.rmsnorm_bwd_workspace_size(M, N)
     ws32 = torch.empty(-(-wsb // 4), dtype=torch.float32, device="cuda")
     dx, dg = R.bwd(dyt, xt, rstd, gt, workspace=ws32)
     dx2, dg2 = torch.empty_like(xt), torch.empty(N, device="cuda")

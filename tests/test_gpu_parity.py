@@ -709,7 +709,7 @@ def run_ln_bwd(M, N, xdt, gdt, seed=31, misalign=0, alias=None, gpu_stats=False,
     dxt = {"dy": dyt, "x": xt}.get(alias) if alias else _empty(M * N, xdt, misalign)
     dgt = torch.full((N,), float("nan"), device="cuda")
     dbt = torch.full((N,), float("nan"), device="cuda") if dbeta else None
-    wsb = R.layernorm_bwd_workspace_size(M, N, xdt)
+    wsb = R.layernorm_bwd_workspace_size(M, N)
     ws = torch.full((max(wsb, 16) // 4,), float("nan"), device="cuda")
     st = R.layernorm_bwd(dyt, xt, mt, rt, gt, dxt, dgt, dbt, ws, wsb, M, N, xdt, gdt, _stream())
     assert st == 0, R.rmsnorm_status_string(st)
@@ -742,7 +742,7 @@ def test_layernorm_bwd_bit_reproducible():
     f = O.layernorm_fwd(x, g, None, M, N, 1e-5, O.BF16, O.BF16, want_exact=False)
     xt, gt, dyt = _put(x, O.BF16), _put(g, O.BF16), _put(dy, O.BF16)
     mt, rt = torch.from_numpy(f["mean"]).cuda(), torch.from_numpy(f["rstd"]).cuda()
-    wsb = R.layernorm_bwd_workspace_size(M, N, O.BF16)
+    wsb = R.layernorm_bwd_workspace_size(M, N)
     outs = []
     for k in range(3):
         dxt, dgt, dbt = _empty(M * N, O.BF16), torch.empty(N, device="cuda"), torch.empty(N, device="cuda")
@@ -773,7 +773,7 @@ def run_bwd(M, N, xdt, gdt, seed=13, misalign=0, alias=None, gpu_rstd=False, eps
     ref = O.rmsnorm_bwd(dy, x, rho, g, M, N, xdt, gdt)
     dxt = {"dy": dyt, "x": xt}.get(alias) if alias else _empty(M * N, xdt, misalign)
     dgt = torch.full((N,), float("nan"), device="cuda")
-    wsb = R.rmsnorm_bwd_workspace_size(M, N, xdt)
+    wsb = R.rmsnorm_bwd_workspace_size(M, N)
     ws = torch.full((max(wsb, 16) // 4,), float("nan"), device="cuda")  # contents must not matter
     st = R.rmsnorm_bwd(dyt, xt, rt, gt, dxt, dgt, ws, wsb, M, N, xdt, gdt, _stream())
     assert st == 0, R.rmsnorm_status_string(st)
@@ -826,7 +826,7 @@ def test_bwd_radial_direction():
     rho = O.rmsnorm_fwd(x, g, M, N, 1e-5, O.BF16, O.BF16, want_exact=False)["rstd"]
     ref = O.rmsnorm_bwd(dy, x, rho, g, M, N, O.BF16, O.BF16)
     dxt, dgt = _empty(M * N, O.BF16), torch.empty(N, device="cuda")
-    wsb = R.rmsnorm_bwd_workspace_size(M, N, O.BF16)
+    wsb = R.rmsnorm_bwd_workspace_size(M, N)
     ws = torch.empty(wsb // 4, device="cuda")
     assert R.rmsnorm_bwd(_put(dy, O.BF16), _put(x, O.BF16), torch.from_numpy(rho).cuda(),
                          _put(g, O.BF16), dxt, dgt, ws, wsb, M, N, O.BF16, O.BF16, _stream()) == 0
@@ -840,7 +840,7 @@ def test_bwd_bit_reproducible():
     x, g, _, dy = _inputs(M, N, O.BF16, O.BF16, 81, with_dy=True)
     rho = O.rmsnorm_fwd(x, g, M, N, 1e-5, O.BF16, O.BF16, want_exact=False)["rstd"]
     xt, gt, dyt, rt = _put(x, O.BF16), _put(g, O.BF16), _put(dy, O.BF16), torch.from_numpy(rho).cuda()
-    wsb = R.rmsnorm_bwd_workspace_size(M, N, O.BF16)
+    wsb = R.rmsnorm_bwd_workspace_size(M, N)
     outs = []
     for k in range(3):
         dxt, dgt = _empty(M * N, O.BF16), torch.empty(N, device="cuda")
@@ -875,7 +875,7 @@ def run_fused_bwd(M, N, xdt, gdt, seed=17, misalign=0, alias=None, with_dres=Tru
     rt = torch.from_numpy(rho.copy()).cuda()
     dht = {"dy": dyt, "h": ht, "dres": drt}.get(alias) if alias else _empty(M * N, xdt, misalign)
     dgt = torch.full((N,), float("nan"), device="cuda")
-    wsb = R.rmsnorm_bwd_workspace_size(M, N, xdt)
+    wsb = R.rmsnorm_bwd_workspace_size(M, N)
     ws = torch.full((max(wsb, 16) // 4,), float("nan"), device="cuda")
     st = R.rmsnorm_fused_add_bwd(dyt, ht, rt, gt, drt, dht, dgt, ws, wsb, M, N, xdt, gdt,
                                  _stream())
@@ -909,7 +909,7 @@ def test_fused_bwd_without_dresidual_is_plain_backward():
     h, g, _, dy = _inputs(M, N, O.BF16, O.BF16, 912, with_dy=True)
     rho = O.rmsnorm_fwd(h, g, M, N, 1e-5, O.BF16, O.BF16, want_exact=False)["rstd"]
     ht, gt, dyt, rt = _put(h, O.BF16), _put(g, O.BF16), _put(dy, O.BF16), torch.from_numpy(rho).cuda()
-    wsb = R.rmsnorm_bwd_workspace_size(M, N, O.BF16)
+    wsb = R.rmsnorm_bwd_workspace_size(M, N)
     ws = torch.empty(wsb // 4, device="cuda")
     outs = []
     for fused in (False, True):
@@ -935,7 +935,7 @@ def test_fused_bwd_zero_upstream_passes_dresidual_through():
     dres = G.normal(921, G.STREAM_DRES, M, N, O.BF16)
     rho = O.rmsnorm_fwd(h, g, M, N, 1e-5, O.BF16, O.BF16, want_exact=False)["rstd"]
     dht, dgt = _empty(M * N, O.BF16), torch.empty(N, device="cuda")
-    wsb = R.rmsnorm_bwd_workspace_size(M, N, O.BF16)
+    wsb = R.rmsnorm_bwd_workspace_size(M, N)
     ws = torch.empty(wsb // 4, device="cuda")
     assert R.rmsnorm_fused_add_bwd(_put(dy, O.BF16), _put(h, O.BF16), torch.from_numpy(rho).cuda(),
                                    _put(g, O.BF16), _put(dres, O.BF16), dht, dgt, ws, wsb, M, N,
@@ -1006,7 +1006,7 @@ def test_graph_capture_and_replay():
     rt = r0.clone()
     y, rs, y2 = _empty(M * N, O.BF16), torch.empty(M, device="cuda"), _empty(M * N, O.BF16)
     dx, dg = _empty(M * N, O.BF16), torch.empty(N, device="cuda")
-    wsb = R.rmsnorm_bwd_workspace_size(M, N, O.BF16)
+    wsb = R.rmsnorm_bwd_workspace_size(M, N)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
 
     def run(stream):
@@ -1051,7 +1051,7 @@ def test_graph_capture_and_replay_of_every_variant():
                          _stream()) == 0
     dres = _put(G.normal(95, G.STREAM_DRES, M, N, O.BF16), O.BF16)
     dh, dg = _empty(M * N, O.BF16), torch.empty(N, device="cuda")
-    ws = torch.empty(R.rmsnorm_bwd_workspace_size(M, N, O.BF16), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(R.rmsnorm_bwd_workspace_size(M, N), dtype=torch.uint8, device="cuda")
     q8, s8 = torch.empty(M * N, dtype=torch.uint8, device="cuda"), torch.empty(M, device="cuda")
     q4 = torch.empty(M * N // 2, dtype=torch.uint8, device="cuda")
     s4 = torch.empty(M * N // 32, dtype=torch.uint8, device="cuda")
@@ -1061,7 +1061,7 @@ def test_graph_capture_and_replay_of_every_variant():
     beta = _put(G.uniform(95, G.STREAM_DY, N, -1.0, 1.0, O.BF16), O.BF16)
     ly, lm, lr = _empty(M * N, O.BF16), torch.empty(M, device="cuda"), torch.empty(M, device="cuda")
     ldx, ldg, ldb = _empty(M * N, O.BF16), torch.empty(N, device="cuda"), torch.empty(N, device="cuda")
-    lws = torch.empty(R.layernorm_bwd_workspace_size(M, N, O.BF16), dtype=torch.uint8,
+    lws = torch.empty(R.layernorm_bwd_workspace_size(M, N), dtype=torch.uint8,
                       device="cuda")
     outs = (dh, dg, q8, s8, q4, s4, qkv, ly, lm, lr, ldx, ldg, ldb)
 

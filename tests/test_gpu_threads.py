@@ -37,7 +37,7 @@ def _work(x, dy, g, stream):
         y, rs = torch.empty_like(x), torch.empty(M, device="cuda")
         assert R.rmsnorm_fwd(x, g, y, rs, M, N, 1e-5, BF, BF, stream) == 0
         dx, dg = torch.empty_like(x), torch.empty(N, device="cuda")
-        wsb = R.rmsnorm_bwd_workspace_size(M, N, BF)
+        wsb = R.rmsnorm_bwd_workspace_size(M, N)
         ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
         assert R.rmsnorm_bwd(dy, x, rs, g, dx, dg, ws, wsb, M, N, BF, BF, stream) == 0
         ly, lm, lr = torch.empty_like(x), torch.empty(M, device="cuda"), torch.empty(M, device="cuda")
