@@ -63,6 +63,9 @@ extern "C" {
 /* Largest row length N accepted (2^31 - 2^20). */
 #define RMSN_MAX_N 2146435072
 
+/* Size of the fixed device buffer behind rmsnorm_bwd_noalloc (32 MiB per GPU). */
+#define RMSN_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+
 typedef enum {
   RMSN_F32 = 0,
   RMSN_F16 = 1,
@@ -81,6 +84,8 @@ typedef enum {
                                to what a call requires, e.g. MX inputs: 16 B) */
   RMSN_ERR_EPS = -7,        /* eps negative or not finite */
   RMSN_ERR_MODE = -8,       /* unknown quantisation mode */
+  RMSN_ERR_SCRATCH = -9,    /* rmsnorm_bwd_noalloc: the shape needs more than
+                               RMSN_NOALLOC_SCRATCH_BYTES of workspace */
   RMSN_ERR_HIP = -100       /* a kernel launch failed; see rmsnorm_last_hip_error */
 } rmsn_status;
 
@@ -216,6 +221,26 @@ size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N);
 int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* gamma,
                 void* dx, float* dgamma, void* workspace, size_t workspace_bytes,
                 int64_t M, int64_t N, int x_dtype, int gamma_dtype, hipStream_t stream);
+
+/* rmsnorm_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, kernels and results bit for bit, with the workspace taken
+ * from a fixed device array of RMSN_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends. The first call on a
+ * device looks up that device's copy of the array (hipGetSymbolAddress),
+ * which is when the HIP runtime may load the library's code for the device
+ * and reserve the array; no call allocates or frees memory itself, and every
+ * later call leaves device memory as it finds it. Arguments as in
+ * rmsnorm_bwd; the stream must belong to the current device.
+ *   Limit: rmsnorm_bwd_workspace_size(M, N) <= RMSN_NOALLOC_SCRATCH_BYTES,
+ *   else RMSN_ERR_SCRATCH before any HIP call (e.g. 8192 x 8192 needs 8 MiB;
+ *   N = 8192 fits up to M = 65536).
+ *   Calls that overlap in time on one GPU (several streams or threads) share
+ *   the array and race: serialise them. Nothing in it needs clearing between
+ *   calls (each call writes what it reads). */
+int rmsnorm_bwd_noalloc(const void* dy, const void* x, const float* rstd, const void* gamma,
+                        void* dx, float* dgamma, int64_t M, int64_t N, int x_dtype,
+                        int gamma_dtype, hipStream_t stream);
 
 /* Backward of the fused residual add + RMSNorm (rmsnorm_fused_add_fwd): with
  * h the saved sum (the residual buffer after the forward) and rstd its saved

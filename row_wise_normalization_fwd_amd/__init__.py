@@ -3,7 +3,8 @@ librmsnorm_mi355x.so.
 
 The C ABI (include/rmsnorm_mi355x.h) is exposed under the same names
 (``rmsnorm_fwd``, ``rmsnorm_fused_add_fwd``, ``rmsnorm_bwd``,
-``rmsnorm_fused_add_bwd``, ``rmsnorm_quant_fwd``, ``rmsnorm_qk_fwd``, ``layernorm_fwd``,
+``rmsnorm_fused_add_bwd``, ``rmsnorm_bwd_noalloc``, ``rmsnorm_quant_fwd``, ``rmsnorm_qk_fwd``,
+``layernorm_fwd``,
 ``layernorm_bwd``, ``layernorm_bwd_workspace_size``, ``rmsnorm_bwd_workspace_size``,
 ``rmsnorm_status_string``,
 ``rmsnorm_last_hip_error``); those functions only marshal arguments. Pointers
@@ -32,12 +33,13 @@ RMSN_OK = 0
 STATUS_NAMES = {
     0: "RMSN_OK", -1: "RMSN_ERR_NULL", -2: "RMSN_ERR_SHAPE", -3: "RMSN_ERR_DTYPE",
     -4: "RMSN_ERR_WORKSPACE", -5: "RMSN_ERR_OVERLAP", -6: "RMSN_ERR_ALIGN",
-    -7: "RMSN_ERR_EPS", -8: "RMSN_ERR_MODE", -100: "RMSN_ERR_HIP",
+    -7: "RMSN_ERR_EPS", -8: "RMSN_ERR_MODE", -9: "RMSN_ERR_SCRATCH", -100: "RMSN_ERR_HIP",
 }
+RMSN_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 ENTRY_POINTS = ("rmsnorm_fwd", "rmsnorm_fused_add_fwd", "rmsnorm_quant_fwd", "rmsnorm_qk_fwd",
                 "layernorm_fwd", "layernorm_bwd", "layernorm_bwd_workspace_size", "rmsnorm_bwd",
-                "rmsnorm_fused_add_bwd", "rmsnorm_bwd_workspace_size", "rmsnorm_status_string",
-                "rmsnorm_last_hip_error")
+                "rmsnorm_fused_add_bwd", "rmsnorm_bwd_workspace_size", "rmsnorm_bwd_noalloc",
+                "rmsnorm_status_string", "rmsnorm_last_hip_error")
 
 
 class RMSNormError(RuntimeError):
@@ -88,6 +90,8 @@ def load_library(path: str | None = None):
     lib.rmsnorm_fused_add_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64,
                                           i32, i32, vp]
     lib.rmsnorm_fused_add_bwd.restype = i32
+    lib.rmsnorm_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, vp]
+    lib.rmsnorm_bwd_noalloc.restype = i32
     lib.rmsnorm_status_string.argtypes = [i32]
     lib.rmsnorm_status_string.restype = ctypes.c_char_p
     lib.rmsnorm_last_hip_error.argtypes = []
@@ -169,6 +173,12 @@ def rmsnorm_bwd(dy, x, rstd, gamma, dx, dgamma, workspace, workspace_bytes, M, N
     return load_library().rmsnorm_bwd(_p(dy), _p(x), _p(rstd), _p(gamma), _p(dx), _p(dgamma),
                                       _p(workspace), workspace_bytes, M, N, x_dtype, gamma_dtype,
                                       _s(stream))
+
+
+def rmsnorm_bwd_noalloc(dy, x, rstd, gamma, dx, dgamma, M, N, x_dtype, gamma_dtype,
+                        stream) -> int:
+    return load_library().rmsnorm_bwd_noalloc(_p(dy), _p(x), _p(rstd), _p(gamma), _p(dx),
+                                              _p(dgamma), M, N, x_dtype, gamma_dtype, _s(stream))
 
 
 def rmsnorm_fused_add_bwd(dy, h, rstd, gamma, dresidual, dh, dgamma, workspace, workspace_bytes,

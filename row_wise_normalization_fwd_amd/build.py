@@ -24,7 +24,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "fwd_f32.hip", "fwd_f16.hip", "fwd_bf16.hip", "fwd_quant_f32.hip",
            "fwd_quant_f16.hip", "fwd_quant_bf16.hip", "ln_fwd_f32.hip", "ln_fwd_f16.hip",
-           "ln_fwd_bf16.hip", "qk.hip", "bwd.hip", "ln_bwd.hip"]
+           "ln_fwd_bf16.hip", "qk.hip", "bwd.hip", "ln_bwd.hip", "noalloc.hip"]
 
 CALIB_SOURCES = ["calib_copy.hip"]
 CALIB_LIB_NAME = "librmsn_copy16.so"

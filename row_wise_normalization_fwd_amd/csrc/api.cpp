@@ -463,6 +463,27 @@ int rmsnorm_bwd(const void* dy, const void* x, const float* rstd, const void* ga
                   x_dtype, gamma_dtype, stream);
 }
 
+int rmsnorm_bwd_noalloc(const void* dy, const void* x, const float* rstd, const void* gamma,
+                        void* dx, float* dgamma, int64_t M, int64_t N, int x_dtype,
+                        int gamma_dtype, hipStream_t stream) {
+  // Every host-side check that needs no HIP call comes first, so that a bad
+  // call fails the same way with or without a device.
+  if (!valid_pair(x_dtype, gamma_dtype)) return RMSN_ERR_DTYPE;
+  if (!shape_ok(M, N)) return RMSN_ERR_SHAPE;
+  if (M == 0) return RMSN_OK;
+  if (rmsn::plan_bwd(M, N).workspace_bytes > RMSN_NOALLOC_SCRATCH_BYTES) return RMSN_ERR_SCRATCH;
+  if (!dy || !x || !rstd || !gamma || !dx || !dgamma) return RMSN_ERR_NULL;
+  void* scratch = nullptr;
+  (void)hipGetLastError();
+  const hipError_t e = rmsn::noalloc_scratch(&scratch);
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return RMSN_ERR_HIP;
+  }
+  return backward(dy, x, rstd, gamma, nullptr, dx, dgamma, scratch, RMSN_NOALLOC_SCRATCH_BYTES, M,
+                  N, x_dtype, gamma_dtype, stream);
+}
+
 int rmsnorm_fused_add_bwd(const void* dy, const void* h, const float* rstd, const void* gamma,
                           const void* dresidual, void* dh, float* dgamma, void* workspace,
                           size_t workspace_bytes, int64_t M, int64_t N, int x_dtype,
@@ -497,6 +518,8 @@ const char* rmsnorm_status_string(int status) {
       return "pointer misaligned (every pointer to its element size; MX inputs to 16 bytes)";
     case RMSN_ERR_EPS: return "eps must be finite and non-negative";
     case RMSN_ERR_MODE: return "unknown quantisation mode";
+    case RMSN_ERR_SCRATCH:
+      return "shape needs more workspace than the allocation-free backward's fixed buffer";
     case RMSN_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown status";
   }

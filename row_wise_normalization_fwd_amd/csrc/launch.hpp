@@ -145,6 +145,10 @@ struct BwdCall {
 hipError_t launch_bwd(const BwdCall& c);
 hipError_t launch_ln_bwd(const BwdCall& c);
 
+// The current device's copy of the allocation-free backward's fixed scratch
+// (RMSN_NOALLOC_SCRATCH_BYTES, 256-byte aligned); looked up once per device.
+hipError_t noalloc_scratch(void** out);
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 inline bool aligned_to(const void* p, int bytes) {

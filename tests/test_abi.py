@@ -13,6 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER_DIR = os.path.join(ROOT, "include")
 
 OK, NULL, SHAPE, DTYPE, WORKSPACE, OVERLAP, ALIGN, EPS = 0, -1, -2, -3, -4, -5, -6, -7
+SCRATCH = -9
 F32, F16, BF16 = 0, 1, 2
 
 # Fake, well-separated, 256-byte-aligned "device" addresses.
@@ -52,7 +53,7 @@ def test_missing_library_fails_loudly(tmp_path):
 
 
 def test_status_strings(lib):
-    for code in (OK, NULL, SHAPE, DTYPE, WORKSPACE, OVERLAP, ALIGN, EPS, -100):
+    for code in (OK, NULL, SHAPE, DTYPE, WORKSPACE, OVERLAP, ALIGN, EPS, -8, SCRATCH, -100):
         s = R.rmsnorm_status_string(code)
         assert s and s != "unknown status"
     assert R.rmsnorm_status_string(12345) == "unknown status"
@@ -159,6 +160,33 @@ def test_backward_validation(lib):
     assert bwd(dg=A + 4) == OVERLAP
     assert bwd(ws=B + 16) == OVERLAP
     assert bwd(ws=F) == OVERLAP               # workspace over dgamma
+
+
+def nbwd(dy=A, x=B, rstd=C, g=D, dx=E, dg=F, M=64, N=256, xd=BF16, gd=BF16):
+    return R.rmsnorm_bwd_noalloc(dy, x, rstd, g, dx, dg, M, N, xd, gd, None)
+
+
+def test_noalloc_backward_host_checks(lib):
+    """The allocation-free backward rejects bad calls, and shapes whose
+    workspace exceeds its fixed buffer, before any HIP call."""
+    cap = R.RMSN_NOALLOC_SCRATCH_BYTES
+    assert cap == 32 * 1024 * 1024
+    assert nbwd(xd=5) == DTYPE
+    assert nbwd(xd=F32, gd=F16) == DTYPE
+    assert nbwd(M=-1) == SHAPE
+    assert nbwd(N=0) == SHAPE
+    assert nbwd(M=0, dy=None, x=None, rstd=None, g=None, dx=None, dg=None) == OK
+    for k in ("dy", "x", "rstd", "g", "dx", "dg"):
+        assert nbwd(**{k: None}) == NULL, k
+    # The limit is the workspace rmsnorm_bwd would need: 8192 columns fit up
+    # to 65536 rows (1024 partial rows of 32 KiB), one row more does not.
+    assert R.rmsnorm_bwd_workspace_size(65536, 8192) == cap
+    assert R.rmsnorm_bwd_workspace_size(65537, 8192) > cap
+    assert nbwd(M=65537, N=8192) == SCRATCH
+    assert nbwd(M=65537, N=8192, dy=None) == SCRATCH   # the size check comes first
+    assert nbwd(M=4096, N=32768) == SCRATCH            # 256 x 32768 x 4 B of partials
+    assert nbwd(M=1, N=2 ** 23) == SCRATCH             # one 32 MiB partial row + a record
+    assert R.rmsnorm_last_hip_error() == 0
 
 
 H = 0x80000000  # an eighth well-separated address, for dresidual
