@@ -35,12 +35,32 @@ Also reported, in the same JSON line:
                 from a captured HIP graph (no host launch per call);
   hot_cache_gbps  the same step without rotation (inputs in the Infinity
                 Cache): context, never the value;
+  graph         the same step, 100 calls over the rotation replicas captured in
+                one HIP graph and replayed: the step without host launch gaps;
   rounds        five more timing rounds of the step (>= 20 ms each after a
-                50 ms warm-up, 1 s cool-down): median / min / mean us, spread;
+                50 ms warm-up, 1 s cool-down): median / min / mean us, spread,
+                and how many rounds were timed again because the device was
+                busy before or after them (idle_check);
+  ceiling       the matching stream: a 16-byte non-temporal kernel moving the
+                step's read and write bytes in (nearly) its read:write ratio
+                (librmsn_copy16.so rmsn_calib_mix), rotated the same way, and
+                frac_of_ceiling = value / its GB/s; every large workload in
+                `workloads` carries its own ceiling and frac_of_ceiling, and
+                its own cpu_baseline (one oracle pass; best of three for the
+                64 x 1024 case);
   calibration   plain copies of the step's byte count: torch's device-to-device
                 copy, and a 16-byte non-temporal copy kernel
                 (librmsn_copy16.so, the practical ceiling for equal read and
-                write bytes), with value / copy16.
+                write bytes), with value / copy16; read-only and write-only
+                16-byte streams of the step's read and write bytes;
+  idle_check    gpu_busy_percent of this device (sysfs, matched by PCI
+                address) sampled while this process has nothing in flight:
+                before and after the main timed region, each round and each
+                other workload.
+
+Modes that do not time anything: --collect-profiles DIR runs the rocprofv3
+passes behind profiles/ as child processes, --reduce-profiles DIR writes
+profiles/ from their output.
 """
 
 from __future__ import annotations
@@ -312,20 +332,37 @@ def copy_calibration(nbytes: int, rotate_bytes: float, steps: int = 200) -> floa
     return 2 * half / (ms * 1e-3) / 1e9
 
 
+_CALIB = None
+
+
+def _calib_lib():
+    """librmsn_copy16.so (the measurement kernels), or None if not built."""
+    global _CALIB
+    if _CALIB is None:
+        import ctypes
+        path = os.path.join(ROOT, "row_wise_normalization_fwd_amd", "librmsn_copy16.so")
+        if not os.path.exists(path):
+            return None
+        lib = ctypes.CDLL(path)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.rmsn_calib_copy16.argtypes = [vp, vp, i64, vp]
+        lib.rmsn_calib_copy16.restype = i32
+        lib.rmsn_calib_stream.argtypes = [vp, vp, vp, vp, i64, vp]
+        lib.rmsn_calib_stream.restype = i32
+        lib.rmsn_calib_mix.argtypes = [vp, i32, vp, i32, i64, vp, vp]
+        lib.rmsn_calib_mix.restype = i32
+        _CALIB = lib
+    return _CALIB
+
+
 def copy16_calibration(nbytes: int, rotate_bytes: float, steps: int = 200):
     """GB/s of the 16-byte non-temporal copy kernel (librmsn_copy16.so) moving
     nbytes (read + write) per step over rotated buffers laid out like the
     workloads' (one [R, bytes] allocation per operand); None if not built."""
-    import ctypes
-
     import torch
-    path = os.path.join(ROOT, "row_wise_normalization_fwd_amd", "librmsn_copy16.so")
-    if not os.path.exists(path):
+    lib = _calib_lib()
+    if lib is None:
         return None
-    lib = ctypes.CDLL(path)
-    lib.rmsn_calib_copy16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                      ctypes.c_void_p]
-    lib.rmsn_calib_copy16.restype = ctypes.c_int
     half = (nbytes // 2) // 16 * 16
     reps = max(1, int(-(-rotate_bytes // (2 * half))))
     src = torch.ones((reps, half), dtype=torch.uint8, device="cuda")
@@ -351,16 +388,10 @@ def stream_calibration(each: int, inputs: int, rotate_bytes: float, steps: int =
     out like the workloads' (one [R, bytes] allocation per operand); the
     practical ceiling for the backward's mix of reads and writes. None if the
     library is not built."""
-    import ctypes
-
     import torch
-    path = os.path.join(ROOT, "row_wise_normalization_fwd_amd", "librmsn_copy16.so")
-    if not os.path.exists(path):
+    lib = _calib_lib()
+    if lib is None:
         return None
-    lib = ctypes.CDLL(path)
-    vp = ctypes.c_void_p
-    lib.rmsn_calib_stream.argtypes = [vp, vp, vp, vp, ctypes.c_int64, vp]
-    lib.rmsn_calib_stream.restype = ctypes.c_int
     each = each // 16 * 16
     reps = max(1, int(-(-rotate_bytes // ((inputs + 1) * each))))
     ins = [torch.randint(0, 256, (reps, each), dtype=torch.uint8, device="cuda")
@@ -385,20 +416,142 @@ def stream_calibration(each: int, inputs: int, rotate_bytes: float, steps: int =
     return (inputs + 1) * each / (ms * 1e-3) / 1e9
 
 
+# Read:write plane counts the mix stream offers (librmsn_copy16.so,
+# rmsn_calib_mix: A 16-byte reads and B 16-byte writes per unit).
+MIX_RATIOS = [(1, 0), (0, 1), (1, 1), (2, 1), (3, 1), (4, 1), (4, 3), (3, 2)]
+
+
+def mix_ratio(read_bytes: int, write_bytes: int) -> tuple[int, int]:
+    """The offered (A, B) closest to read_bytes : write_bytes (in log ratio)."""
+    import math
+    if write_bytes <= 0:
+        return (1, 0)
+    if read_bytes <= 0:
+        return (0, 1)
+    want = math.log(read_bytes / write_bytes)
+    both = [r for r in MIX_RATIOS if r[0] and r[1]]
+    return min(both, key=lambda r: abs(math.log(r[0] / r[1]) - want))
+
+
+def mix_calibration(read_bytes: int, write_bytes: int, rotate_bytes: float, steps: int = 200,
+                    ratio=None):
+    """The mix stream (16-byte non-temporal, A reads to B writes per unit with
+    (A, B) = mix_ratio(read_bytes, write_bytes) unless given) moving about
+    read_bytes in and write_bytes out per step over rotated buffers: dict with
+    gbps (its own bytes over its time), the ratio and the bytes per step; None
+    if the library is not built."""
+    import torch
+    lib = _calib_lib()
+    if lib is None:
+        return None
+    A, B = ratio or mix_ratio(read_bytes, write_bytes)
+    per_plane = read_bytes / A if A else write_bytes / B
+    n = max(64, int(per_plane // 16))
+    plane = 16 * n
+    step_bytes = (A + B) * plane
+    reps = max(1, int(-(-rotate_bytes // step_bytes)))
+    src = (torch.randint(-2 ** 31, 2 ** 31 - 1, (reps, A * n * 4), dtype=torch.int32, device="cuda")
+           if A else None)
+    dst = torch.empty((reps, B * n * 4), dtype=torch.int32, device="cuda") if B else None
+    sink = torch.empty(1024, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    ptrs = [(src[i].data_ptr() if A else None, dst[i].data_ptr() if B else None)
+            for i in range(reps)]
+
+    def step(i):
+        sp, dp = ptrs[i % reps]
+        if lib.rmsn_calib_mix(sp, A, dp, B, n, sink.data_ptr(), stream) != 0:
+            raise RuntimeError("mix calibration launch failed")
+    ms = time_steps(step, steps, 20)
+    if B:
+        # unit u writes [u, u >> 32, 0, 0] ^ (its A source chunks) to every plane
+        k = 64
+        idx = torch.zeros((k, 4), dtype=torch.int32, device="cuda")
+        idx[:, 0] = torch.arange(k, dtype=torch.int32, device="cuda")
+        want = idx
+        for a in range(A):
+            want = want ^ src[0].view(A, n, 4)[a, :k]
+        got = dst[0].view(B, n, 4)[:, :k]
+        if not all(torch.equal(got[b], want) for b in range(B)):
+            raise RuntimeError("mix calibration wrote wrong bytes")
+    del src, dst, sink
+    return {"gbps": round(step_bytes / (ms * 1e-3) / 1e9, 2), "reads_per_write":
+            f"{A}:{B}", "bytes_per_step": step_bytes, "rotation_replicas": reps}
+
+
+class BusyMonitor:
+    """Samples the device's own sysfs gpu_busy_percent (matched to device 0's
+    PCI address) while this process has nothing in flight: a sample above the
+    threshold means another process is using the GPU."""
+
+    def __init__(self, threshold_pct: int = 10):
+        import torch
+        self.threshold = threshold_pct
+        self.path = None
+        p = torch.cuda.get_device_properties(0)
+        bus, dev = getattr(p, "pci_bus_id", None), getattr(p, "pci_device_id", None)
+        dom = getattr(p, "pci_domain_id", 0) or 0
+        if bus is not None and dev is not None:
+            cand = f"/sys/bus/pci/devices/{dom:04x}:{bus:02x}:{dev:02x}.0/gpu_busy_percent"
+            if os.access(cand, os.R_OK):
+                self.path = cand
+        if self.path is None:
+            cands = {os.path.realpath(c) for c in glob.glob("/sys/class/drm/card*/device/gpu_busy_percent")
+                     if os.access(c, os.R_OK)}
+            if len(cands) == 1:
+                self.path = cands.pop()
+        self.log = []
+
+    def sample(self, n: int = 5, gap_s: float = 0.02):
+        """n readings (percent), or [] when no source is readable."""
+        if self.path is None:
+            return []
+        out = []
+        for i in range(n):
+            try:
+                with open(self.path) as fh:
+                    out.append(int(fh.read().strip()))
+            except (OSError, ValueError):
+                return out
+            if i + 1 < n:
+                time.sleep(gap_s)
+        return out
+
+    def idle(self, tag: str, settle_s: float = 0.5) -> bool:
+        """Sample and record; True when every reading is at or below the
+        threshold or there is no source. The counter is a running average
+        that decays by about a fifth every 20 ms, so it still shows this
+        process's own last kernels for a while: wait settle_s after they end
+        (half a second takes a full load below 1%) before sampling."""
+        import torch
+        torch.cuda.synchronize()
+        if self.path is not None and settle_s > 0:
+            time.sleep(settle_s)
+        vals = self.sample()
+        busy = bool(vals) and max(vals) > self.threshold
+        self.log.append({"at": tag, "busy_pct": vals, "busy": busy})
+        return not busy
+
+    def summary(self) -> dict:
+        return {"source": self.path, "threshold_pct": self.threshold,
+                "samples": len(self.log), "busy_samples": sum(r["busy"] for r in self.log),
+                "log": self.log[-12:]}
+
+
 def graph_replay_ms(run, calls: int = 100, replays: int = 40) -> float:
     """Milliseconds per step when `calls` steps are captured in one HIP graph
     (torch.cuda.CUDAGraph) and the graph is replayed: the GPU's own rate for a
-    launch-bound step, without a host launch per call."""
+    step, without a host launch per call. The captured calls cycle through the
+    runner's rotation replicas as the timed steps do."""
     import torch
-    fn, args = run.calls[0]
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        cargs = args[:-1] + (side.cuda_stream,)
         with torch.cuda.graph(graph, stream=side):
-            for _ in range(calls):
-                if fn(*cargs) != 0:
+            for i in range(calls):
+                fn, args = run.calls[i % len(run.calls)]
+                if fn(*(args[:-1] + (side.cuda_stream,))) != 0:
                     raise RuntimeError("graph capture: launch failed")
     torch.cuda.current_stream().wait_stream(side)
     for _ in range(3):
@@ -411,27 +564,44 @@ def graph_replay_ms(run, calls: int = 100, replays: int = 40) -> float:
         graph.replay()
     end.record()
     torch.cuda.synchronize()
+    del graph
     return start.elapsed_time(end) / (replays * calls)
 
 
-def rounds(step, ms_per_step: float, n: int = 5, cooldown_s: float = 1.0, start: int = 0):
+def rounds(step, ms_per_step: float, n: int = 5, cooldown_s: float = 1.0, start: int = 0,
+           monitor=None, retries: int = 2):
     """n further timing rounds of the same step, each >= 20 ms of back-to-back
     launches after a >= 50 ms warm-up, with a cool-down before each round:
-    median, min and mean microseconds per step and the spread."""
+    median, min and mean microseconds per step and the spread. With a
+    BusyMonitor, the device is sampled before and after each round; a round
+    with a busy sample is timed again (up to `retries` times) and, if still
+    busy, kept and counted as interfered."""
     import statistics
     k = max(50, int(0.020 / (ms_per_step * 1e-3)) + 1)
     warm = max(10, int(0.050 / (ms_per_step * 1e-3)) + 1)
     us = []
+    requeued = interfered = 0
     i = start
     for r in range(n):
-        time.sleep(cooldown_s)
-        us.append(1e3 * time_steps(lambda j: step(i + j), k, warm if r == 0 else 10))
-        i += k + warm
+        for attempt in range(retries + 1):
+            time.sleep(cooldown_s)
+            idle_before = monitor.idle(f"round {r} before", settle_s=0.0) if monitor else True
+            t = 1e3 * time_steps(lambda j: step(i + j), k, warm if r == 0 else 10)
+            i += k + warm
+            idle_after = monitor.idle(f"round {r} after") if monitor else True
+            if idle_before and idle_after:
+                break
+            if attempt < retries:
+                requeued += 1
+            else:
+                interfered += 1
+        us.append(t)
     med = statistics.median(us)
     return {"rounds": n, "steps_per_round": k, "cooldown_s": cooldown_s,
             "us_median": round(med, 3), "us_min": round(min(us), 3),
             "us_mean": round(statistics.fmean(us), 3),
-            "spread_pct": round(100 * (max(us) - min(us)) / med, 2)}
+            "spread_pct": round(100 * (max(us) - min(us)) / med, 2),
+            "requeued_busy": requeued, "interfered": interfered}
 
 
 def load_traffic(workload: str, src_hash: str):
@@ -447,8 +617,10 @@ def load_traffic(workload: str, src_hash: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, host_inputs: dict, seconds: float) -> dict:
-    """The fp64 oracle, as it stands, timed on one host core."""
+def cpu_baseline(w, host_inputs: dict, seconds: float, best_of: int = 1) -> dict:
+    """The fp64 oracle, as it stands, timed on one host core: passes over the
+    whole batch until `seconds` have gone by (at least one), or the best of
+    `best_of` passes (for batches too small to time one pass reliably)."""
     import oracle as O
     O._load()
     M, N = w.M, w.N
@@ -495,18 +667,28 @@ def cpu_baseline(w, host_inputs: dict, seconds: float) -> dict:
         def one_pass():
             O.rmsnorm_fused_add_bwd(host_inputs["dy"], x, rho, g, dres, M, N, w.x_dt, w.g_dt,
                                     want_exact=False)
-    passes, t0 = 0, time.perf_counter()
-    while True:
-        one_pass()
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    if best_of > 1:
+        times = []
+        for _ in range(best_of):
+            t0 = time.perf_counter()
+            one_pass()
+            times.append(time.perf_counter() - t0)
+        el, passes = min(times), 1
+        sample = (f"best of {best_of} full passes over the {M}x{N} batch (single thread, host "
+                  f"has {os.cpu_count()} logical CPUs)")
+    else:
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            one_pass()
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        sample = (f"{passes} full pass{'es' if passes > 1 else ''} over the {M}x{N} batch "
+                  f"({el:.1f} s, single thread, host has {os.cpu_count()} logical CPUs)")
     return {"value": round(w.algorithmic_bytes() * passes / el / 1e9, 4), "unit": "GB/s",
-            "cores": 1, "kind": "oracle",
-            "sample": f"{passes} full passes over the {M}x{N} batch ({el:.1f} s, single thread,"
-                      f" host has {os.cpu_count()} logical CPUs)",
-            "rows_per_s": round(M * passes / el, 1),
+            "cores": 1, "kind": "oracle", "sample": sample,
+            "rows_per_s": round(rows_of(w) * passes / el, 1),
             "ms_per_pass": round(1e3 * el / passes, 3),
             "host_cpu": _cpu_model()}
 
@@ -520,6 +702,302 @@ def _cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+# ------------------------------------------------------------- profiling
+#
+# --collect-profiles DIR runs rocprofv3 over single-workload bench runs as
+# child processes (this process never touches the GPU): a kernel trace, then
+# one counter pass per group (FETCH_SIZE, WRITE_SIZE, LDS, occupancy, VALU).
+# --reduce-profiles DIR turns their CSV output into profiles/*.md and
+# profiles/traffic_*.json. Counter passes time --steps 16 after --warmup 4
+# (their dispatches 4..19 of the workload's own kernels), the trace --steps
+# 200 after --warmup 500 (dispatches 500..699).
+
+TRACE_W, TRACE_S, PMC_W, PMC_S = 500, 200, 4, 16
+PROFILE_PASSES = {
+    "fetch": "FETCH_SIZE",
+    "write": "WRITE_SIZE",
+    "lds": "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAVE_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE",
+    "occ": "MeanOccupancyPerActiveCU",
+    "valu": "VALUBusy MemUnitStalled",
+}
+
+
+def profile_command(w, kind: str, prof_dir: str) -> str:
+    """The rocprofv3 command of one pass over workload w (repository root)."""
+    b = f"python3 bench.py --workload {w.name} --no-others --no-cpu --no-graph --rounds 0"
+    if w.M * w.N < (1 << 20):
+        b += " --rotate-bytes 0"
+    d = f"{prof_dir}/{w.name}/{kind}"
+    if kind == "trace":
+        return (f"rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o trace -- {b} "
+                f"--steps {TRACE_S} --warmup {TRACE_W}")
+    return (f"rocprofv3 --pmc {PROFILE_PASSES[kind]} --output-format csv -d {d} -o {kind} -- {b} "
+            f"--steps {PMC_S} --warmup {PMC_W}")
+
+
+def collect_profiles(prof_dir: str, names, kinds, timeout_s: int = 150) -> int:
+    """Run the passes, each in its own process group under a time limit;
+    stop at the first failure. Returns 0 or the failing pass's status."""
+    import shlex
+    import signal
+    import subprocess
+
+    import gen as G
+    env = dict(os.environ, TMPDIR="/tmp")
+    for name in names:
+        w = G.WORKLOADS_BY_NAME[name]
+        for kind in kinds:
+            cmd = profile_command(w, kind, prof_dir)
+            log = os.path.join(ROOT, prof_dir, f"{name}.{kind}.log")
+            os.makedirs(os.path.dirname(log), exist_ok=True)
+            print(f"[{time.strftime('%H:%M:%S')}] {name} {kind}", flush=True)
+            with open(log, "w") as fh:
+                proc = subprocess.Popen(shlex.split(cmd), cwd=ROOT, env=env, stdout=fh,
+                                        stderr=subprocess.STDOUT, start_new_session=True)
+                try:
+                    rc = proc.wait(timeout=timeout_s)
+                except subprocess.TimeoutExpired:
+                    os.killpg(proc.pid, signal.SIGKILL)
+                    proc.wait()
+                    rc = 124
+            if rc != 0:
+                # rocprofv3 itself may end with a segmentation fault after a
+                # complete run; accept that only when the results are there.
+                done = glob.glob(os.path.join(ROOT, prof_dir, name, kind, "*.csv"))
+                if rc == -11 or rc == 139:
+                    if done:
+                        print(f"  rocprofv3 exited {rc} after writing {len(done)} files; kept",
+                              flush=True)
+                        continue
+                print(f"  failed rc={rc}; see {log}", flush=True)
+                return rc if rc > 0 else 128 - rc
+    print(f"[{time.strftime('%H:%M:%S')}] done", flush=True)
+    return 0
+
+
+def _short_kernel(name: str) -> str:
+    s = name[5:] if name.startswith("void ") else name
+    s = s.replace("rmsn::", "")
+    depth = 0
+    for i, c in enumerate(s):
+        if c == "<":
+            depth += 1
+        elif c == ">":
+            depth -= 1
+        elif c == "(" and depth == 0:
+            return s[:i]
+    return s
+
+
+def _csv_rows(path: str):
+    import csv
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _one(pattern: str):
+    fs = glob.glob(pattern)
+    if len(fs) != 1:
+        raise RuntimeError(f"expected one file for {pattern}, found {fs}")
+    return fs[0]
+
+
+def _trace_kernels(prof: str, name: str) -> dict:
+    """{kernel: trace rows of its timed dispatches}, in launch order."""
+    rs = _csv_rows(_one(f"{prof}/{name}/trace/*_kernel_trace.csv"))
+    rs.sort(key=lambda r: int(r["Dispatch_Id"]))
+    by = {}
+    for r in rs:
+        if "rmsn::" in r["Kernel_Name"]:
+            by.setdefault(_short_kernel(r["Kernel_Name"]), []).append(r)
+    out = {k: v[TRACE_W:TRACE_W + TRACE_S] for k, v in by.items() if len(v) >= TRACE_W + TRACE_S}
+    return dict(sorted(out.items(), key=lambda kv: int(kv[1][0]["Dispatch_Id"])))
+
+
+def _counters(prof: str, name: str, kind: str, kernels) -> dict:
+    """{kernel: {counter: [values over the timed dispatches]}} ({} if absent)."""
+    fs = glob.glob(f"{prof}/{name}/{kind}/*_counter_collection.csv")
+    if len(fs) != 1:
+        return {}
+    disp = {}
+    for r in _csv_rows(fs[0]):
+        k = _short_kernel(r["Kernel_Name"])
+        if k not in kernels:
+            continue
+        d = disp.setdefault(k, {}).setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["_wg"] = int(r["Workgroup_Size"])
+    out = {}
+    for k, dd in disp.items():
+        vals = {}
+        for i in sorted(dd)[PMC_W:PMC_W + PMC_S]:
+            for c, v in dd[i].items():
+                vals.setdefault(c, []).append(v)
+        out[k] = vals
+    return out
+
+
+def _traffic_scale(prof: str):
+    """FETCH_SIZE / WRITE_SIZE scale factors from the plain copies in the
+    headline workload's counter runs: (read scale, write scale, text)."""
+    import statistics
+
+    import gen as G
+    res = {}
+    for kind, ctr in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        rs = _csv_rows(_one(f"{prof}/{HEADLINE}/{kind}/*_counter_collection.csv"))
+        grids = {}
+        for r in rs:
+            if r["Kernel_Name"] == "__amd_rocclr_copyBuffer" and r["Counter_Name"] == ctr:
+                grids.setdefault(int(r["Grid_Size"]), []).append(float(r["Counter_Value"]))
+        _, v = max(grids.items(), key=lambda kv: len(kv[1]))
+        c16 = [float(r["Counter_Value"]) for r in rs
+               if "copy16_kernel" in r["Kernel_Name"] and r["Counter_Name"] == ctr]
+        res[kind] = (statistics.median(v), len(v), statistics.median(c16) if c16 else float("nan"))
+    w = G.WORKLOADS_BY_NAME[HEADLINE]
+    true_kib = w.M * w.N * w.esize / 1024.0
+    rsc, wsc = round(true_kib / res["fetch"][0], 4), round(true_kib / res["write"][0], 4)
+    text = (f"Calibration: the headline workload's counter runs (`{profile_command(w, 'fetch', prof)}` "
+            f"and its WRITE_SIZE twin) copy {true_kib:.0f} KiB each way with torch's device copy "
+            f"(`__amd_rocclr_copyBuffer`): FETCH_SIZE {res['fetch'][0]:.1f} KiB and WRITE_SIZE "
+            f"{res['write'][0]:.1f} KiB per dispatch (median of {res['fetch'][1]} / {res['write'][1]}), "
+            f"so reads are scaled by {rsc:.4f} and writes by {wsc:.4f}. The bench's 16-byte "
+            f"non-temporal copy kernel in the same runs reads {res['fetch'][2]:.1f} KiB of "
+            f"FETCH_SIZE and {res['write'][2]:.1f} KiB of WRITE_SIZE for the same bytes.")
+    return rsc, wsc, text
+
+
+def reduce_profiles(prof: str) -> int:
+    """profiles/<kernel>__<workload>.md, profiles/traffic_<workload>.json and
+    the all-workload LDS / occupancy and VALU tables from collect_profiles'
+    output under prof (relative to the repository root)."""
+    import statistics
+
+    import gen as G
+    absprof = os.path.join(ROOT, prof)
+    outd = os.path.join(ROOT, "profiles")
+    h = kernel_source_hash()
+    rscale, wscale, cal_text = _traffic_scale(absprof)
+    lds_rows, valu_rows = [], []
+    for w in G.WORKLOADS + G.EXTRA_WORKLOADS:
+        if not os.path.isdir(f"{absprof}/{w.name}/trace"):
+            print("no profile for", w.name)
+            continue
+        ks = _trace_kernels(absprof, w.name)
+        fe = _counters(absprof, w.name, "fetch", ks)
+        wr = _counters(absprof, w.name, "write", ks)
+        ld = _counters(absprof, w.name, "lds", ks)
+        oc = _counters(absprof, w.name, "occ", ks)
+        va = _counters(absprof, w.name, "valu", ks)
+        small = w.M * w.N < (1 << 20)
+        lines = [f"# {w.name}: {' + '.join(ks)}", "",
+                 f"Workload: {w.kind}, M={w.M}, N={w.N}, x {DT_NAMES[w.x_dt]}, gamma "
+                 f"{DT_NAMES[w.g_dt]}, eps={w.eps}, rstd written: {w.store_rstd}. "
+                 + ("Inputs are not rotated (the launch-bound 64 x 1024 case, as in the bench)."
+                    if small else "Inputs rotate over >= 1 GiB of replicas (HBM, not Infinity Cache)."),
+                 "", f"Kernel sources hash (bench.py `kernel_source_hash`): `{h}`", "",
+                 "Made by `python3 bench.py --collect-profiles " + prof + " --profile-workloads "
+                 + w.name + "` then `python3 bench.py --reduce-profiles " + prof + "`, which run "
+                 "(repository root, one MI355X; each selects the workload's own dispatches inside "
+                 f"the timed loop, dispatches {TRACE_W}..{TRACE_W + TRACE_S - 1} of the trace run "
+                 f"and {PMC_W}..{PMC_W + PMC_S - 1} of the counter runs):", "",
+                 f"    {profile_command(w, 'trace', prof)}", f"    {profile_command(w, 'fetch', prof)}",
+                 f"    {profile_command(w, 'write', prof)}", "",
+                 "| kernel | timed dispatches | avg us | median us | min us | max us | VGPR_Count | "
+                 "SGPR | static LDS B | scratch B/lane |",
+                 "|---|---|---|---|---|---|---|---|---|---|"]
+        tot_us, tot_bytes, kj = 0.0, 0.0, []
+        for k, rs in ks.items():
+            d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in rs]
+            r0 = rs[0]
+            avg = statistics.mean(d)
+            tot_us += avg
+            lines.append(f"| `{k}` | {len(d)} | {avg:.2f} | {statistics.median(d):.2f} | "
+                         f"{min(d):.2f} | {max(d):.2f} | {r0['VGPR_Count']} | {r0['SGPR_Count']} | "
+                         f"{r0['LDS_Block_Size']} | {r0['Scratch_Size']} |")
+            rec = {"kernel": k, "avg_us": round(avg, 3)}
+            if k in fe and k in wr:
+                f = statistics.median(fe[k]["FETCH_SIZE"])
+                wv = statistics.median(wr[k]["WRITE_SIZE"])
+                tot_bytes += (f * rscale + wv * wscale) * 1024
+                rec.update({"fetch_kib_raw": round(f, 1), "write_kib_raw": round(wv, 1)})
+            kj.append(rec)
+            lv = ld.get(k, {})
+            if lv:
+                conf = statistics.median(lv["SQ_LDS_BANK_CONFLICT"])
+                act = statistics.median(lv["SQ_LDS_IDX_ACTIVE"])
+                gui = statistics.median(lv["GRBM_GUI_ACTIVE"])
+                occ = statistics.median(oc[k]["MeanOccupancyPerActiveCU"]) if k in oc else float("nan")
+                lds_rows.append(f"| {w.name} | `{k}` | {lv['_wg'][0]} | "
+                                f"{conf / act if act else 0.0:.4f} | {100.0 * conf / gui / 256:.3f} | "
+                                f"{occ:.2f} |")
+            if k in va:
+                valu_rows.append(f"| {w.name} | `{k}` | {statistics.median(va[k]['VALUBusy']):.1f} | "
+                                 f"{statistics.median(va[k]['MemUnitStalled']):.1f} |")
+        alg = w.algorithmic_bytes()
+        lines += ["", "Register and LDS columns are rocprofv3's kernel-trace fields. On this device "
+                  "its VGPR_Count reads the compiler's VGPR allocation halved and rounded up to a "
+                  "multiple of 4 (e.g. 52 for 97, 64 for 126), and LDS_Block_Size is the static "
+                  "allocation only (512-byte granules): dynamic LDS requested at launch is not "
+                  "included.", ""]
+        have_traffic = all("fetch_kib_raw" in j for j in kj)
+        if have_traffic:
+            lines += ["HBM traffic per step (rocprofv3 counters, median KiB per dispatch):", ""]
+            for j in kj:
+                lines.append(f"- `{j['kernel']}`: FETCH_SIZE {j['fetch_kib_raw']:.1f} KiB raw (x "
+                             f"{rscale:.4f} = {j['fetch_kib_raw'] * rscale:.1f} KiB), WRITE_SIZE "
+                             f"{j['write_kib_raw']:.1f} KiB raw (x {wscale:.4f})")
+            lines += ["", cal_text, "",
+                      f"- measured HBM bytes per step: {int(round(tot_bytes)):,} "
+                      f"({tot_bytes / alg:.4f} x algorithmic)"]
+        lines += [f"- algorithmic bytes per step: {alg:,}",
+                  f"- kernel time per step (profiled): {tot_us:.2f} us",
+                  f"- achieved (algorithmic / kernel time): {alg / (tot_us * 1e-6) / 1e9:.1f} GB/s = "
+                  f"{100 * alg / (tot_us * 1e-6) / 1e9 / PEAK_GBPS:.1f}% of {PEAK_GBPS:.0f} GB/s", ""]
+        dom = DOMINANT_KERNEL.get(w.name) or max(kj, key=lambda j: j["avg_us"])["kernel"].split("<")[0]
+        for old in glob.glob(f"{outd}/*__{w.name}.md"):
+            os.remove(old)
+        with open(f"{outd}/{dom}__{w.name}.md", "w") as fh:
+            fh.write("\n".join(lines))
+        if have_traffic:
+            rec = {"workload": w.name, "kernel_src_hash": h, "bytes_per_launch": int(round(tot_bytes)),
+                   "algorithmic_bytes": alg, "read_scale": rscale, "write_scale": wscale,
+                   "kernels": kj, "commands": [profile_command(w, "fetch", prof),
+                                               profile_command(w, "write", prof)]}
+            with open(f"{outd}/traffic_{w.name}.json", "w") as fh:
+                json.dump(rec, fh, indent=1)
+        print(f"{w.name}: {tot_us:.2f} us"
+              + (f", traffic {tot_bytes / alg:.4f}x" if have_traffic else ""))
+    w0 = G.WORKLOADS_BY_NAME[HEADLINE]
+    if lds_rows:
+        hdr = ["# LDS bank conflicts and occupancy, every workload's kernels", "",
+               f"Kernel sources hash (bench.py `kernel_source_hash`): `{h}`", "",
+               "Commands (repository root, one MI355X), for each workload W (`--rotate-bytes 0` "
+               "for the 64 x 1024 case, as the bench runs it):", "",
+               "    " + profile_command(w0, "lds", prof).replace(HEADLINE, "W"),
+               "    " + profile_command(w0, "occ", prof).replace(HEADLINE, "W"), "",
+               f"Per kernel: medians over the workload's own dispatches {PMC_W}..{PMC_W + PMC_S - 1}. "
+               "`conflict/active` = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; `conflict % GPU time` "
+               "= 100 * SQ_LDS_BANK_CONFLICT / GRBM_GUI_ACTIVE / 256 CUs; `occupancy` = "
+               "rocprofv3's MeanOccupancyPerActiveCU (resident waves per SIMD, of 8).", "",
+               "| workload | kernel | workgroup | LDS conflict/active | conflict % GPU time | "
+               "occupancy (waves / SIMD) |", "|---|---|---|---|---|---|"]
+        with open(f"{outd}/lds_occupancy__all_workloads.md", "w") as fh:
+            fh.write("\n".join(hdr + lds_rows) + "\n")
+    if valu_rows:
+        hdr = ["# VALU and memory-unit load, every workload's kernels", "",
+               f"Kernel sources hash (bench.py `kernel_source_hash`): `{h}`", "",
+               "Command (repository root, one MI355X), for each workload W:", "",
+               "    " + profile_command(w0, "valu", prof).replace(HEADLINE, "W"), "",
+               f"Medians over the workload's own dispatches {PMC_W}..{PMC_W + PMC_S - 1}. `VALUBusy` "
+               "is rocprofv3's derived share of GPU time the vector ALUs issue, `MemUnitStalled` "
+               "the share of time the vector memory unit is stalled.", "",
+               "| workload | kernel | VALUBusy % | MemUnitStalled % |", "|---|---|---|---|"]
+        with open(f"{outd}/valu_memunit__all_workloads.md", "w") as fh:
+            fh.write("\n".join(hdr + valu_rows) + "\n")
+    return 0
 
 
 def main() -> int:
@@ -537,7 +1015,33 @@ def main() -> int:
     ap.add_argument("--rounds", type=int, default=5,
                     help="extra timing rounds of the headline step (>= 20 ms each, 1 s "
                          "cool-down) for median / min / mean / spread; 0 skips them")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing (profiled runs)")
+    ap.add_argument("--collect-profiles", metavar="DIR",
+                    help="run the rocprofv3 passes into DIR (relative to the repository root) "
+                         "as child processes, then exit")
+    ap.add_argument("--profile-workloads", default="",
+                    help="comma-separated workloads for --collect-profiles (default: all)")
+    ap.add_argument("--profile-passes", default="trace,fetch,write,lds,occ,valu",
+                    help="comma-separated passes for --collect-profiles")
+    ap.add_argument("--reduce-profiles", metavar="DIR",
+                    help="write profiles/ from the rocprofv3 output under DIR, then exit")
     args = ap.parse_args()
+
+    if args.collect_profiles or args.reduce_profiles:
+        # Neither mode touches the GPU in this process.
+        import gen as G
+        if args.reduce_profiles:
+            return reduce_profiles(args.reduce_profiles)
+        names = ([n for n in args.profile_workloads.split(",") if n] or
+                 [x.name for x in G.WORKLOADS + G.EXTRA_WORKLOADS])
+        kinds = [k for k in args.profile_passes.split(",") if k]
+        bad = [n for n in names if n not in G.WORKLOADS_BY_NAME] + \
+              [k for k in kinds if k != "trace" and k not in PROFILE_PASSES]
+        if bad:
+            print(f"unknown workloads or passes: {bad}", file=sys.stderr)
+            return 2
+        return collect_profiles(args.collect_profiles, names, kinds)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -558,16 +1062,30 @@ def main() -> int:
     w = G.WORKLOADS_BY_NAME[args.workload]
     host = G.make_inputs(w)
     run = Runner(w, args.rotate_bytes, host)
+    monitor = BusyMonitor()
+    # The main timed region: wait (up to 3 s) for an idle device first, and
+    # record whether it stayed idle.
+    for _ in range(3):
+        if monitor.idle("main before"):
+            break
+        time.sleep(1.0)
     ms = time_steps(run.step, args.steps, args.warmup)
+    monitor.idle("main after")
     nbytes = w.algorithmic_bytes()
+    rbytes, wbytes = w.read_write_bytes()
     gbps = nbytes / (ms * 1e-3) / 1e9
-    round_stats = (rounds(run.step, ms, n=args.rounds, start=args.steps + args.warmup)
-                   if args.rounds > 0 else None)
+    round_stats = (rounds(run.step, ms, n=args.rounds, start=args.steps + args.warmup,
+                          monitor=monitor) if args.rounds > 0 else None)
+    graph_ms = (None if args.no_graph else
+                graph_replay_ms(run, calls=100, replays=max(5, int(0.1 / (ms * 1e-3) / 100))))
     hot = Runner(w, 0, host)
     hot_ms = time_steps(hot.step, max(args.steps // 2, 10), max(args.warmup // 2, 5))
     del hot
     calib = copy_calibration(2 * w.M * w.N * w.esize, args.rotate_bytes)
     calib16 = copy16_calibration(2 * w.M * w.N * w.esize, args.rotate_bytes)
+    read16 = mix_calibration(rbytes, 0, args.rotate_bytes)
+    write16 = mix_calibration(0, wbytes, args.rotate_bytes)
+    ceiling = mix_calibration(rbytes, wbytes, args.rotate_bytes)
 
     result = {
         "metric": "achieved HBM GB/s (% of MI355X peak) and rows/s, RMSNorm fwd/bwd",
@@ -585,7 +1103,8 @@ def main() -> int:
         "config": {"workload": w.name, "kind": w.kind, "M": w.M, "N": w.N,
                    "io_dtype": DT_NAMES[w.x_dt], "gamma_dtype": DT_NAMES[w.g_dt], "eps": w.eps,
                    "rstd_out": w.store_rstd, "rotation_replicas": run.replicas,
-                   "algorithmic_bytes_per_step": nbytes},
+                   "algorithmic_bytes_per_step": nbytes, "read_bytes": rbytes,
+                   "write_bytes": wbytes},
         "rows_per_s": round(rows_of(w) / (ms * 1e-3), 1),
         "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_GBPS,
@@ -593,6 +1112,14 @@ def main() -> int:
                      "traffic": load_traffic(w.name, src_hash),
                      "kernel": DOMINANT_KERNEL.get(w.name, w.kind),
                      "kernel_src_hash": src_hash},
+        "ceiling": ceiling,
+        "frac_of_ceiling": round(gbps / ceiling["gbps"], 4) if ceiling else None,
+        "graph": None if graph_ms is None else {
+            "calls_per_graph": 100, "ms_per_step": round(graph_ms, 6),
+            "gbps": round(nbytes / (graph_ms * 1e-3) / 1e9, 2),
+            "pct_of_peak": round(100 * nbytes / (graph_ms * 1e-3) / 1e9 / PEAK_GBPS, 2),
+            "what": "the same step, 100 calls over the rotation replicas captured in one HIP "
+                    "graph and replayed (no host launch per call)"},
         "hot_cache_gbps": round(nbytes / (hot_ms * 1e-3) / 1e9, 2),
         "rounds": round_stats,
         "calibration": {
@@ -601,7 +1128,15 @@ def main() -> int:
             "copy16_gbps": round(calib16, 2) if calib16 else None,
             "copy16_what": "16-byte non-temporal copy kernel (librmsn_copy16.so), same read+"
                            "write bytes, rotated, one allocation per operand",
-            "value_over_copy16": round(gbps / calib16, 4) if calib16 else None},
+            "value_over_copy16": round(gbps / calib16, 4) if calib16 else None,
+            "read16_gbps": read16["gbps"] if read16 else None,
+            "write16_gbps": write16["gbps"] if write16 else None,
+            "read_write_what": "16-byte non-temporal read-only and write-only streams of the "
+                               "step's read and write bytes, rotated (librmsn_copy16.so "
+                               "rmsn_calib_mix 1:0 and 0:1)",
+            "read_then_write_us": (round(1e6 * (rbytes / (read16["gbps"] * 1e9) +
+                                               wbytes / (write16["gbps"] * 1e9)), 3)
+                                   if read16 and write16 else None)},
     }
     del run
     torch.cuda.empty_cache()
@@ -612,18 +1147,22 @@ def main() -> int:
             if ow.name == w.name:
                 continue
             oh = G.make_inputs(ow)
-            orun = Runner(ow, 0 if ow.M * ow.N < (1 << 20) else args.rotate_bytes, oh)
+            small = ow.M * ow.N < (1 << 20)
+            orun = Runner(ow, 0 if small else args.rotate_bytes, oh)
             est = max(ow.algorithmic_bytes() / 6e12, 3e-6)
             k = args.other_steps or int(min(2000, max(50, 0.05 / est)))
+            monitor.idle(f"{ow.name} before")
             oms = time_steps(orun.step, k, max(k // 10, 5))
+            monitor.idle(f"{ow.name} after")
             ob = ow.algorithmic_bytes()
-            others[ow.name] = {"ms_per_step": round(oms, 6), "gbps": round(ob / (oms * 1e-3) / 1e9, 2),
-                               "pct_of_peak": round(100 * ob / (oms * 1e-3) / 1e9 / PEAK_GBPS, 2),
+            ogbps = ob / (oms * 1e-3) / 1e9
+            others[ow.name] = {"ms_per_step": round(oms, 6), "gbps": round(ogbps, 2),
+                               "pct_of_peak": round(100 * ogbps / PEAK_GBPS, 2),
                                "rows_per_s": round(rows_of(ow) / (oms * 1e-3), 1),
                                "steps": k, "rotation_replicas": orun.replicas}
             if ow.kind in ("bwd", "fused_add_bwd", "ln_bwd"):
                 others[ow.name]["workspace_bytes"] = orun.ws_bytes
-            if ow.M * ow.N < (1 << 20):
+            if small:
                 # Launch-bound: the same call replayed from a captured graph.
                 gms = graph_replay_ms(orun)
                 others[ow.name]["graph"] = {
@@ -631,24 +1170,37 @@ def main() -> int:
                     "gbps": round(ob / (gms * 1e-3) / 1e9, 2),
                     "pct_of_peak": round(100 * ob / (gms * 1e-3) / 1e9 / PEAK_GBPS, 2),
                     "rows_per_s": round(rows_of(ow) / (gms * 1e-3), 1)}
-            del orun, oh
+            del orun
             torch.cuda.empty_cache()
+            o = others[ow.name]
+            if not small:
+                # The matching stream: the workload's read and write bytes in
+                # (about) its ratio, 16-byte non-temporal, rotated.
+                ocr, ocw = ow.read_write_bytes()
+                c = mix_calibration(ocr, ocw, args.rotate_bytes)
+                if c is not None:
+                    o["ceiling"] = c
+                    o["frac_of_ceiling"] = round(ogbps / c["gbps"], 4)
+                torch.cuda.empty_cache()
             if ow.kind in ("bwd", "fused_add_bwd", "ln_bwd"):
                 # The same read and write streams with no arithmetic: two
                 # inputs per output (x, dy -> dx), three for the fused add's.
                 nin = 3 if ow.kind == "fused_add_bwd" else 2
                 sg = stream_calibration(ow.M * ow.N * ow.esize, nin, args.rotate_bytes)
                 if sg is not None:
-                    o = others[ow.name]
                     o["stream_gbps"] = round(sg, 2)
                     o["stream_what"] = (f"{nin} reads + 1 write of {ow.M}x{ow.N} {DT_NAMES[ow.x_dt]}, "
                                         "16-byte non-temporal, rotated (librmsn_copy16.so)")
                     o["value_over_stream"] = round(o["gbps"] / sg, 4)
                 torch.cuda.empty_cache()
+            if not args.no_cpu:
+                o["cpu_baseline"] = cpu_baseline(ow, oh, 0.0, best_of=3 if small else 1)
+            del oh
         result["workloads"] = others
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+    result["idle_check"] = monitor.summary()
     print(json.dumps(result), flush=True)
     return 0
 

@@ -136,6 +136,38 @@ class Workload:
 
     def algorithmic_bytes(self) -> int:
         """Each big operand read or written once, plus gamma, rstd, dgamma."""
+        r, w = self.read_write_bytes()
+        return r + w
+
+    def read_write_bytes(self) -> tuple[int, int]:
+        """algorithmic_bytes() split into the bytes read and the bytes written."""
+        big = self.M * self.N * self.esize
+        g = self.N * self.gsize
+        rstd = 4 * self.M if self.store_rstd else 0
+        if self.kind == "fwd":
+            return big + g, big + rstd
+        if self.kind == "fused_add":
+            return 2 * big + g, 2 * big + rstd
+        if self.kind == "ln_bwd":
+            return 2 * big + 8 * self.M + g, big + 8 * self.N
+        if self.kind == "ln":
+            return big + 2 * g, big + 8 * self.M
+        if self.kind == "qk":
+            half = self.M * (self.heads_q + self.heads_k) * self.N * self.esize
+            return half + 2 * g, half
+        if self.kind == "quant":
+            n = self.M * self.N
+            qbytes = n // 2 if self.quant_mode == 4 else n
+            scale_r = 4 if self.quant_mode == 1 else 0
+            scale_w = {1: 0, 2: 4 * self.M}.get(self.quant_mode, n // 32)
+            fused = big if self.fused_quant else 0
+            return big + fused + g + scale_r, fused + qbytes + scale_w + rstd
+        if self.kind == "fused_add_bwd":
+            return 3 * big + 4 * self.M + g, big + 4 * self.N
+        return 2 * big + 4 * self.M + g, big + 4 * self.N
+
+    def _algorithmic_bytes_sum(self) -> int:
+        """The same total written out operand by operand (kept to pin the split)."""
         big = self.M * self.N * self.esize
         g = self.N * self.gsize
         if self.kind == "fwd":

@@ -446,6 +446,58 @@ def test_stream_calibration_checks_arguments_on_the_host():
     assert f(A, B, None, None, 16, None) == -1
 
 
+def test_mix_calibration_checks_arguments_on_the_host():
+    """The benchmark's read/write mix stream (A reads to B writes of 16 bytes
+    per unit) rejects bad arguments before any HIP call."""
+    import ctypes
+    path = os.path.join(ROOT, "row_wise_normalization_fwd_amd", "librmsn_copy16.so")
+    if not os.path.exists(path):
+        pytest.skip("librmsn_copy16.so not built")
+    lib = ctypes.CDLL(path)
+    f = lib.rmsn_calib_mix
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    f.argtypes = [vp, i32, vp, i32, ctypes.c_int64, vp, vp]
+    f.restype = ctypes.c_int
+    assert f(A, 2, B, 1, 0, G, None) == 0        # nothing to do: no launch
+    assert f(None, 0, B, 1, 0, G, None) == 0     # write-only, empty
+    assert f(A, 1, None, 0, 0, G, None) == 0     # read-only, empty
+    assert f(A, 0, B, 0, 16, G, None) == -1      # neither reads nor writes
+    assert f(A, 5, B, 1, 16, G, None) == -1      # too many planes
+    assert f(A, 1, B, -1, 16, G, None) == -1
+    assert f(A, 1, B, 1, -1, G, None) == -1
+    assert f(None, 1, B, 1, 16, G, None) == -1   # reads need a source
+    assert f(A, 1, None, 1, 16, G, None) == -1   # writes need a destination
+    assert f(A + 8, 1, B, 1, 16, G, None) == -1  # misaligned
+    assert f(A, 1, B + 4, 1, 16, G, None) == -1
+    assert f(A, 1, B, 1, 16, None, None) == -1   # no sink
+    assert f(A, 1, B, 1, 16, G + 8, None) == -1
+    assert f(A, 2, A + 16, 1, 64, G, None) == -1  # output overlaps the source
+    assert f(A, 1, B, 1, 64, B + 512, None) == -1  # sink inside the output
+    assert f(A, 1, B, 1, 1 << 40, G, None) == -1  # absurd size
+
+
+def test_bench_mix_ratio_and_byte_split():
+    """bench.py's ceiling streams take the offered read:write ratio nearest
+    each workload's, and the workloads' read / write split adds up to their
+    algorithmic bytes."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    import gen
+    assert bench.mix_ratio(100, 0) == (1, 0)
+    assert bench.mix_ratio(0, 100) == (0, 1)
+    want = {"fwd_bf16_m4096_n8192_rstd": (1, 1), "bwd_bf16_m8192_n8192": (2, 1),
+            "fusedadd_bwd_bf16_m8192_n8192": (3, 1), "fwd_fp8row_bf16_m4096_n8192": (2, 1),
+            "fwd_mxfp8_bf16_m4096_n8192": (2, 1), "fwd_mxfp4_bf16_m4096_n8192": (4, 1),
+            "fusedadd_fp8tensor_bf16_m16384_n4096_gf32": (4, 3),
+            "layernorm_bwd_bf16_m8192_n8192": (2, 1), "fusedadd_bf16_m16384_n4096_gf32": (1, 1)}
+    for w in gen.WORKLOADS + gen.EXTRA_WORKLOADS:
+        r, wr = w.read_write_bytes()
+        assert r + wr == w.algorithmic_bytes() == w._algorithmic_bytes_sum(), w.name
+        if w.name in want:
+            assert bench.mix_ratio(r, wr) == want[w.name], w.name
+
+
 def test_bench_refuses_more_than_one_gpu():
     """bench.py runs on one GPU; asking for more exits with a message before
     touching a device."""

@@ -1099,3 +1099,26 @@ def test_graph_capture_and_replay_of_every_variant():
         torch.cuda.synchronize()
         for t, w in zip(outs, want):
             assert torch.equal(t.cpu().view(torch.uint8), w.view(torch.uint8)), rep
+
+
+def test_stale_hip_error_is_not_reported():
+    """A failed HIP runtime call made by someone else on this thread (here an
+    invalid hipSetDevice) leaves its error behind; the library's next call must
+    still return RMSN_OK, with the right output, not that stale error."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    hip.hipSetDevice.restype = ctypes.c_int
+    hip.hipGetLastError.restype = ctypes.c_int
+    M, N = 33, 4096
+    x, g, _, _ = _inputs(M, N, O.BF16, O.BF16, 1901)
+    ref = O.rmsnorm_fwd(x, g, M, N, 1e-5, O.BF16, O.BF16)
+    xt, gt, yt = _put(x, O.BF16), _put(g, O.BF16), _empty(M * N, O.BF16)
+    torch.cuda.synchronize()
+    assert hip.hipSetDevice(999) != 0          # fails on the host, launches nothing
+    st = R.rmsnorm_fwd(xt, gt, yt, None, M, N, 1e-5, O.BF16, O.BF16, _stream())
+    assert st == 0, R.rmsnorm_status_string(st)
+    torch.cuda.synchronize()
+    check_output(to_host(yt).reshape(M, N), ref["y_exact"], ref["y"], O.BF16, "y")
+    assert torch.cuda.current_device() == 0
+    hip.hipGetLastError()                       # leave nothing behind for later tests
