@@ -77,30 +77,54 @@ hipError_t run_fwd_long(const FwdArgs<T, G>& a, hipStream_t s) {
 }
 
 // Few rows too long for the LDS row cache: partials, finalize, apply (see
-// fwd_split.hpp). Against one block per row at bf16 (one process):
+// fwd_split.hpp). Three launches against one block per row at bf16 (one
+// process):
 // 256K-element rows 2.0-2.4x faster up to 16 rows, even at 128; 1M-element
 // rows 3-11x up to 32 rows, 1.5x at 128; 16M-element rows 8-51x. Rows that
 // fit the cache stay with one block per row (the split path's three launches
 // cost ~10 us there against 7-8).
+template <class T, class G, bool FUSED, bool SPREAD, bool CACHE>
+hipError_t run_fwd_split_as(const SplitArgs<T, G>& a, hipStream_t s) {
+  const int64_t blocks = a.tiles < kMaxGrid ? a.tiles : kMaxGrid;
+  fwd_split_partial_kernel<T, G, FUSED, SPREAD, CACHE>
+      <<<dim3(static_cast<unsigned>(blocks)), dim3(kSplitBlock), 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if constexpr (!SPREAD) {
+    int64_t fblocks = ceil_div(a.M, kSplitBlock / kWave);
+    if (fblocks > kMaxGrid) fblocks = kMaxGrid;
+    fwd_split_finalize_kernel<T, G, FUSED>
+        <<<dim3(static_cast<unsigned>(fblocks)), dim3(kSplitBlock), 0, s>>>(a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  fwd_split_apply_kernel<T, G, FUSED, SPREAD>
+      <<<dim3(static_cast<unsigned>(blocks)), dim3(kSplitBlock), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// Two launches (the partials spread to every tile of the row, each apply
+// block forming the row's factor itself) when every tile region, the last
+// included, holds a float per tile of the row and the partial pass writes
+// nothing that it or another block still reads (y is not x); else three.
+// x is loaded cacheable in the partial pass when the batch is at most 16 MiB,
+// so that the apply pass's second read can come from the Infinity Cache
+// (3-11% faster there, 10% slower at 32 MiB, in one process).
 template <class T, class G, bool FUSED>
 hipError_t run_fwd_split(const FwdArgs<T, G>& f, hipStream_t s) {
   SplitArgs<T, G> a{f.x, f.residual, f.gamma, f.y, f.rstd, f.M, f.N, f.eps, 0, 0};
   a.chunks = static_cast<int>(ceil_div(f.N, split_chunk<T>()));
   a.tiles = f.M * a.chunks;
-  const int64_t blocks = a.tiles < kMaxGrid ? a.tiles : kMaxGrid;
-  fwd_split_partial_kernel<T, G, FUSED>
-      <<<dim3(static_cast<unsigned>(blocks)), dim3(kSplitBlock), 0, s>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  int64_t fblocks = ceil_div(f.M, kSplitBlock / kWave);
-  if (fblocks > kMaxGrid) fblocks = kMaxGrid;
-  fwd_split_finalize_kernel<T, G, FUSED>
-      <<<dim3(static_cast<unsigned>(fblocks)), dim3(kSplitBlock), 0, s>>>(a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  fwd_split_apply_kernel<T, G, FUSED>
-      <<<dim3(static_cast<unsigned>(blocks)), dim3(kSplitBlock), 0, s>>>(a);
-  return hipGetLastError();
+  const int64_t last = f.N - static_cast<int64_t>(a.chunks - 1) * split_chunk<T>();
+  const bool spread = last * T::kSize >= 4 * static_cast<int64_t>(a.chunks) &&
+                      static_cast<const void*>(f.y) != static_cast<const void*>(f.x);
+  const bool cache = !FUSED && f.M * static_cast<int64_t>(f.N) * T::kSize <= (int64_t(16) << 20);
+  if (spread) {
+    return cache ? run_fwd_split_as<T, G, FUSED, true, !FUSED>(a, s)
+                 : run_fwd_split_as<T, G, FUSED, true, false>(a, s);
+  }
+  return cache ? run_fwd_split_as<T, G, FUSED, false, !FUSED>(a, s)
+               : run_fwd_split_as<T, G, FUSED, false, false>(a, s);
 }
 
 template <class T, class G, bool FUSED, int OUT, bool LN = false>
