@@ -158,6 +158,68 @@ def test_forward_scale_invariance(gen_mod):
                                want, rtol=1e-13)
 
 
+def test_forward_domain_edges(gen_mod):
+    """The oracle over the whole input domain, against exact power-of-two
+    scaling and the definition: fp32 rows at 2^100 (squares far beyond fp32)
+    and on the fp32 subnormal grid give the same y as the rows at scale 1;
+    rstd scales by the inverse power and rounds to +inf in fp32 once it
+    exceeds FLT_MAX; a zero row gives 0/0 = NaN at eps = 0 and 0 at eps > 0;
+    eps near FLT_MAX is added in double."""
+    M, N = 4, 64
+    z = O.round_to(gen_mod.normal(21, 1, M, N, gen_mod.F64), O.BF16)   # 8-bit mantissas
+    zd = O.decode(z, O.BF16).reshape(M, N)
+    zd[np.abs(zd) < 2.0 ** -8] = 2.0 ** -8           # keep every value on the subnormal grid below
+    g = O.round_to(gen_mod.uniform(21, 4, N, 0.5, 1.5, gen_mod.F64), O.F32)
+    base = O.rmsnorm_fwd(O.round_to(zd, O.F32), g, M, N, 0.0, O.F32, O.F32)
+    for k in (100, -130):                            # 2^-130 * 2^-8 * 2^-7: subnormal, exact
+        x = O.round_to(zd * 2.0 ** k, O.F32)
+        assert np.array_equal(O.decode(x, O.F32).reshape(M, N), zd * 2.0 ** k)
+        out = O.rmsnorm_fwd(x, g, M, N, 0.0, O.F32, O.F32)
+        assert np.array_equal(out["y_exact"], base["y_exact"]), k
+        assert np.array_equal(out["rstd_exact"], base["rstd_exact"] * 2.0 ** -k), k
+        if k < 0:  # rstd around 2^130 / rms: beyond FLT_MAX (2^128), so +inf in fp32
+            big = out["rstd_exact"] > float(np.finfo(np.float32).max)
+            assert big.any() and np.all(np.isposinf(out["rstd"][big]))
+    # Zero rows.
+    x0 = np.zeros((2, N), np.float32)
+    nan = O.rmsnorm_fwd(x0, g, 2, N, 0.0, O.F32, O.F32)
+    assert np.all(np.isnan(nan["y_exact"])) and np.all(np.isposinf(nan["rstd_exact"]))
+    eps = float(np.float32(1e-35))
+    zero = O.rmsnorm_fwd(x0, g, 2, N, eps, O.F32, O.F32)
+    assert np.all(zero["y_exact"] == 0.0)
+    assert np.all(zero["rstd_exact"] == 1.0 / math.sqrt(eps))
+    # eps near the fp32 maximum: mean(x^2) + eps exceeds FLT_MAX, in double.
+    eps = float(np.float32(3e38))
+    x = O.round_to(zd * 2.0 ** 64, O.F32)
+    out = O.rmsnorm_fwd(x, g, M, N, eps, O.F32, O.F32)
+    xd = O.decode(x, O.F32).reshape(M, N)
+    q = (xd ** 2).mean(axis=1) + eps
+    assert np.all(q > float(np.finfo(np.float32).max))
+    np.testing.assert_allclose(out["rstd_exact"], 1.0 / np.sqrt(q), rtol=1e-15)
+
+
+def test_backward_domain_scaling(gen_mod):
+    """The backward at magnitudes whose products overflow fp32, against its
+    exact scaling laws: dx is linear in dy, so dy * 2^100 gives dx * 2^100;
+    x * 2^k with rstd * 2^-k gives dx * 2^-k and the same dgamma."""
+    M, N = 3, 96
+    x = O.round_to(gen_mod.normal(22, 1, M, N, gen_mod.F64), O.BF16)
+    dy = O.round_to(gen_mod.normal(22, 3, M, N, gen_mod.F64), O.BF16)
+    g = O.round_to(gen_mod.uniform(22, 4, N, 0.5, 1.5, gen_mod.F64), O.F32)
+    rho = np.array([0.75, 1.25, 2.0])                # powers of two times short mantissas
+    base = O.rmsnorm_bwd(dy, x, rho, g, M, N, O.BF16, O.F32)
+    dyd = O.decode(dy, O.BF16)
+    big = O.rmsnorm_bwd(O.round_to(dyd * 2.0 ** 100, O.BF16), x, rho, g, M, N, O.BF16, O.F32)
+    assert np.array_equal(big["dx_exact"], base["dx_exact"] * 2.0 ** 100)
+    assert np.array_equal(big["dgamma"], base["dgamma"] * 2.0 ** 100)
+    xd = O.decode(x, O.BF16)
+    for k in (60, -60):
+        sc = O.rmsnorm_bwd(dy, O.round_to(xd * 2.0 ** k, O.BF16), rho * 2.0 ** -k, g, M, N,
+                           O.BF16, O.F32)
+        assert np.array_equal(sc["dx_exact"], base["dx_exact"] * 2.0 ** -k), k
+        assert np.array_equal(sc["dgamma"], base["dgamma"]), k
+
+
 def test_forward_brute_force_decimal(gen_mod):
     # 4 x 8 bf16 input, recomputed in 60-digit decimal arithmetic.
     M, N, eps = 4, 8, 1e-5
