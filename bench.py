@@ -484,10 +484,18 @@ class BusyMonitor:
     PCI address) while this process has nothing in flight: a sample above the
     threshold means another process is using the GPU."""
 
-    def __init__(self, threshold_pct: int = 10):
-        import torch
+    def __init__(self, threshold_pct: int = 10, path: str | None = None, sync=None):
+        """path: the counter file (found from device 0's PCI address when
+        None); sync: called before sampling (torch.cuda.synchronize when
+        None)."""
         self.threshold = threshold_pct
-        self.path = None
+        self.log = []
+        self.path = path
+        self.sync = sync
+        if path is not None:
+            return
+        import torch
+        self.sync = sync or torch.cuda.synchronize
         p = torch.cuda.get_device_properties(0)
         bus, dev = getattr(p, "pci_bus_id", None), getattr(p, "pci_device_id", None)
         dom = getattr(p, "pci_domain_id", 0) or 0
@@ -500,7 +508,6 @@ class BusyMonitor:
                      if os.access(c, os.R_OK)}
             if len(cands) == 1:
                 self.path = cands.pop()
-        self.log = []
 
     def sample(self, n: int = 5, gap_s: float = 0.02):
         """n readings (percent), or [] when no source is readable."""
@@ -523,8 +530,8 @@ class BusyMonitor:
         that decays by about a fifth every 20 ms, so it still shows this
         process's own last kernels for a while: wait settle_s after they end
         (half a second takes a full load below 1%) before sampling."""
-        import torch
-        torch.cuda.synchronize()
+        if self.sync is not None:
+            self.sync()
         if self.path is not None and settle_s > 0:
             time.sleep(settle_s)
         vals = self.sample()

@@ -498,6 +498,32 @@ def test_bench_mix_ratio_and_byte_split():
             assert bench.mix_ratio(r, wr) == want[w.name], w.name
 
 
+def test_bench_busy_monitor(tmp_path):
+    """bench.py's idle check: readings above the threshold mark a sample busy,
+    an unreadable or missing counter never does, and the log keeps the
+    readings."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    f = tmp_path / "gpu_busy_percent"
+    synced = []
+    m = bench.BusyMonitor(threshold_pct=10, path=str(f), sync=lambda: synced.append(1))
+    f.write_text("3\n")
+    assert m.idle("quiet", settle_s=0.0)
+    f.write_text("55\n")
+    assert not m.idle("busy", settle_s=0.0)
+    f.write_text("10\n")
+    assert m.idle("at the threshold", settle_s=0.0)
+    assert len(synced) == 3
+    s = m.summary()
+    assert s["samples"] == 3 and s["busy_samples"] == 1 and s["threshold_pct"] == 10
+    assert s["log"][1] == {"at": "busy", "busy_pct": [55] * 5, "busy": True}
+    f.write_text("not a number")
+    assert m.sample() == [] and m.idle("garbled", settle_s=0.0)
+    none = bench.BusyMonitor(path=str(tmp_path / "missing"), sync=None)
+    assert none.sample() == [] and none.idle("no counter", settle_s=0.0)
+
+
 def test_bench_refuses_more_than_one_gpu():
     """bench.py runs on one GPU; asking for more exits with a message before
     touching a device."""
