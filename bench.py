@@ -53,6 +53,10 @@ Also reported, in the same JSON line:
                 (librmsn_copy16.so, the practical ceiling for equal read and
                 write bytes), with value / copy16; read-only and write-only
                 16-byte streams of the step's read and write bytes;
+  parity        (with the CPU leg) the timed configuration's outputs, recomputed
+                from pristine inputs on replica 0, against the fp64 oracle on
+                64 rows spread over the batch, with the GPU tests'
+                tolerances; every workload carries its own;
   idle_check    gpu_busy_percent of this device (sysfs, matched by PCI
                 address) sampled while this process has nothing in flight:
                 before and after the main timed region, each round and each
@@ -301,6 +305,37 @@ class Runner:
         st = fn(*args)
         if st != 0:
             raise RuntimeError(f"{self.w.name}: {self.R.rmsnorm_status_string(st)}")
+
+    def pristine_outputs(self, host_inputs: dict) -> dict:
+        """Replica 0 recomputed from the workload's original inputs (the
+        timed loop overwrites the residual of a fused add and QK-norm's
+        buffer in place), outputs copied to the host as storage arrays."""
+        import numpy as np
+        import torch
+        w, s0 = self.w, self.sets[0]
+
+        def put(t, a):
+            src = torch.from_numpy(a.reshape(-1) if w.x_dt == 0 or a.dtype != np.uint16
+                                   else a.reshape(-1).view(np.int16))
+            t.copy_(src.view(t.dtype) if src.dtype != t.dtype else src)
+
+        def host(t):
+            t = t.detach().cpu()
+            if t.dtype in (torch.bfloat16, torch.float16):
+                return t.view(torch.int16).numpy().view(np.uint16).copy()
+            return t.numpy().copy()
+
+        if w.kind == "qk":
+            put(s0["x"], host_inputs["x"])
+        if s0.get("r") is not None:
+            put(s0["r"], host_inputs["r"])
+        torch.cuda.synchronize()
+        self.step(0)
+        torch.cuda.synchronize()
+        keep = {"y", "rstd", "r", "q", "scale", "dx", "dgamma", "dbeta"}
+        keep |= {"x"} if w.kind == "qk" else set()
+        keep |= {"mean"} if w.kind in ("ln", "ln_bwd") else set()
+        return {k: host(v) for k, v in s0.items() if k in keep and v is not None}
 
 
 def time_steps(step, steps: int, warmup: int) -> float:
@@ -698,6 +733,88 @@ def cpu_baseline(w, host_inputs: dict, seconds: float, best_of: int = 1) -> dict
             "rows_per_s": round(rows_of(w) * passes / el, 1),
             "ms_per_pass": round(1e3 * el / passes, 3),
             "host_cpu": _cpu_model()}
+
+
+def parity_check(w, outs: dict, host_inputs: dict, rows: int = 64) -> dict:
+    """Part of the CPU leg: the pristine step's outputs (Runner.pristine_outputs)
+    against the fp64 oracle on `rows` rows spread over the batch (every row of
+    a smaller one), with the GPU tests' tolerances (tests/gpu_util.py). The
+    backwards are checked on dx with the rstd (and mean) their timed step
+    used; dgamma and dbeta sum over every row and are left to the tests."""
+    import numpy as np
+
+    import oracle as O
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import gpu_util as U
+    M, N, xdt, gdt = w.M, w.N, w.x_dt, w.g_dt
+    idx = np.unique(np.linspace(0, M - 1, min(rows, M)).round().astype(np.int64))
+    S = int(idx.size)
+    g = host_inputs["gamma"]
+
+    def pick(a, n=N):
+        return np.ascontiguousarray(a.reshape(M, n)[idx])
+
+    try:
+        if w.kind == "fwd":
+            x = pick(host_inputs["x"])
+            ref = O.rmsnorm_fwd(x, g, S, N, w.eps, xdt, gdt)
+            U.check_output(pick(outs["y"]), ref["y_exact"], ref["y"], xdt, "y")
+            if "rstd" in outs:
+                U.check_rstd(outs["rstd"][idx], ref["rstd_exact"])
+        elif w.kind == "fused_add":
+            x, r = pick(host_inputs["x"]), pick(host_inputs["r"])
+            ref = O.rmsnorm_fused_add_fwd(x, r, g, S, N, w.eps, xdt, gdt)
+            assert np.array_equal(pick(outs["r"]), ref["h"]), "h not bit for bit"
+            U.check_output(pick(outs["y"]), ref["y_exact"], ref["y"], xdt, "y")
+        elif w.kind == "quant":
+            x = pick(host_inputs["x"])
+            r = pick(host_inputs["r"]) if w.fused_quant else None
+            if w.quant_mode >= 3:
+                elem = O.E4M3 if w.quant_mode == 3 else O.E2M1
+                ref = O.rmsnorm_mx_fwd(x, g, S, N, w.eps, xdt, gdt, elem, r=r)
+                q = pick(outs["q"], N // 2 if elem == O.E2M1 else N)
+                q = U.unpack_fp4(q, S, N) if elem == O.E2M1 else q
+                U.check_mx(q, pick(outs["scale"], N // 32), ref, elem)
+            else:
+                ref = O.rmsnorm_quant_fwd(x, g, S, N, w.eps, xdt, gdt, w.quant_mode,
+                                          scale=w.tensor_scale if w.quant_mode == 1 else None, r=r)
+                U.check_fp8(pick(outs["q"]), ref, w.quant_mode == 2,
+                            outs["scale"][idx] if w.quant_mode == 2 else None)
+            if r is not None:
+                assert np.array_equal(pick(outs["r"]), ref["h"]), "h not bit for bit"
+        elif w.kind == "qk":
+            H, Hk = w.heads_q, w.heads_k
+            sd = (H + 2 * Hk) * N
+            buf = pick(host_inputs["x"], sd)
+            want, _ = O.rmsnorm_heads_fwd(buf.reshape(-1), g, S, H, N, sd, w.eps, xdt, gdt)
+            want, _ = O.rmsnorm_heads_fwd(want, host_inputs["gamma_k"], S, Hk, N, sd, w.eps, xdt,
+                                          gdt, offset=H * N)
+            want = want.reshape(S, sd)
+            got = pick(outs["x"], sd)
+            moved = np.zeros((S, sd), bool)
+            moved[:, :(H + Hk) * N] = True
+            assert np.array_equal(got[~moved], buf[~moved]), "v heads changed"
+            U.check_output(got[moved], O.decode(want, xdt)[moved], want[moved], xdt, "qk")
+        elif w.kind == "ln":
+            x, b = pick(host_inputs["x"]), host_inputs["beta"]
+            ref = O.layernorm_fwd(x, g, b, S, N, w.eps, xdt, gdt)
+            U.check_layernorm(pick(outs["y"]), ref, x, g, b, xdt, outs["mean"][idx],
+                              outs["rstd"][idx])
+        elif w.kind in ("bwd", "fused_add_bwd"):
+            x, dy = pick(host_inputs["x"]), pick(host_inputs["dy"])
+            rho = outs["rstd"][idx].astype(np.float64)
+            dres = pick(host_inputs["dres"]) if w.kind == "fused_add_bwd" else None
+            ref = (O.rmsnorm_fused_add_bwd(dy, x, rho, g, dres, S, N, xdt, gdt)
+                   if dres is not None else O.rmsnorm_bwd(dy, x, rho, g, S, N, xdt, gdt))
+            U.check_dx(pick(outs["dx"]), ref, x, dy, g, rho, xdt, dres=dres)
+        elif w.kind == "ln_bwd":
+            x, dy = pick(host_inputs["x"]), pick(host_inputs["dy"])
+            mean, rstd = outs["mean"][idx], outs["rstd"][idx]
+            ref = O.layernorm_bwd(dy, x, mean, rstd, g, S, N, xdt, gdt)
+            U.check_layernorm_bwd(pick(outs["dx"]), None, None, ref, x, dy, g, mean, rstd, xdt)
+        return {"ok": True, "rows_checked": S, "of": M}
+    except AssertionError as e:
+        return {"ok": False, "rows_checked": S, "of": M, "error": str(e)[:300]}
 
 
 def _cpu_model() -> str:
@@ -1145,6 +1262,7 @@ def main() -> int:
                                                wbytes / (write16["gbps"] * 1e9)), 3)
                                    if read16 and write16 else None)},
     }
+    outs = None if args.no_cpu else run.pristine_outputs(host)
     del run
     torch.cuda.empty_cache()
 
@@ -1177,6 +1295,7 @@ def main() -> int:
                     "gbps": round(ob / (gms * 1e-3) / 1e9, 2),
                     "pct_of_peak": round(100 * ob / (gms * 1e-3) / 1e9 / PEAK_GBPS, 2),
                     "rows_per_s": round(rows_of(ow) / (gms * 1e-3), 1)}
+            oouts = None if args.no_cpu else orun.pristine_outputs(oh)
             del orun
             torch.cuda.empty_cache()
             o = others[ow.name]
@@ -1202,11 +1321,13 @@ def main() -> int:
                 torch.cuda.empty_cache()
             if not args.no_cpu:
                 o["cpu_baseline"] = cpu_baseline(ow, oh, 0.0, best_of=3 if small else 1)
-            del oh
+                o["parity"] = parity_check(ow, oouts, oh)
+            del oh, oouts
         result["workloads"] = others
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+        result["parity"] = parity_check(w, outs, host)
     result["idle_check"] = monitor.summary()
     print(json.dumps(result), flush=True)
     return 0

@@ -524,6 +524,42 @@ def test_bench_busy_monitor(tmp_path):
     assert none.sample() == [] and none.idle("no counter", settle_s=0.0)
 
 
+def test_bench_parity_check_plumbing():
+    """bench.py's sampled parity check accepts outputs equal to the oracle's
+    and rejects one corrupted element, for a forward, a quantised forward
+    and a backward workload shape (small sizes, CPU only)."""
+    import dataclasses
+    import sys
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    import gen
+    import oracle as O
+    base = gen.WORKLOADS_BY_NAME["fwd_bf16_m4096_n8192_rstd"]
+    w = dataclasses.replace(base, M=100, N=256)
+    h = gen.make_inputs(w)
+    ref = O.rmsnorm_fwd(h["x"], h["gamma"], w.M, w.N, w.eps, w.x_dt, w.g_dt)
+    outs = {"y": ref["y"].copy(), "rstd": ref["rstd"].copy()}
+    p = bench.parity_check(w, outs, h)
+    assert p["ok"] and p["rows_checked"] == 64 and p["of"] == 100, p
+    outs["y"].reshape(100, 256)[99, 7] ^= 0x0100       # a few ulp off in the last row
+    assert not bench.parity_check(w, outs, h)["ok"]
+    wq = dataclasses.replace(gen.WORKLOADS_BY_NAME["fwd_mxfp4_bf16_m4096_n8192"], M=20, N=256)
+    hq = gen.make_inputs(wq)
+    rq = O.rmsnorm_mx_fwd(hq["x"], hq["gamma"], 20, 256, wq.eps, wq.x_dt, wq.g_dt, O.E2M1)
+    packed = (rq["q"][:, 0::2] | (rq["q"][:, 1::2] << 4)).astype(np.uint8)
+    assert bench.parity_check(wq, {"q": packed.reshape(-1), "scale": rq["scale"].reshape(-1)},
+                              hq)["ok"]
+    wb = dataclasses.replace(gen.WORKLOADS_BY_NAME["bwd_bf16_m8192_n8192"], M=70, N=128)
+    hb = gen.make_inputs(wb)
+    rho = O.rmsnorm_fwd(hb["x"], hb["gamma"], 70, 128, wb.eps, wb.x_dt, wb.g_dt)["rstd"]
+    rb = O.rmsnorm_bwd(hb["dy"], hb["x"], rho, hb["gamma"], 70, 128, wb.x_dt, wb.g_dt)
+    ob = {"dx": rb["dx"].copy(), "rstd": rho}
+    assert bench.parity_check(wb, ob, hb)["ok"]
+    ob["dx"].reshape(70, 128)[0, 0] ^= 0x4000         # a wildly wrong element
+    assert not bench.parity_check(wb, ob, hb)["ok"]
+
+
 def test_bench_refuses_more_than_one_gpu():
     """bench.py runs on one GPU; asking for more exits with a message before
     touching a device."""
