@@ -533,9 +533,12 @@ struct RareDotGate {
   }
 };
 
-// Blocks of several row groups of several waves each share one rare-row mask
-// (the OR of their groups' masks), so that every thread of the block takes the
-// same number of passes through the reductions of the rare-row walk.
+// Blocks of several row groups of several waves each, whose row reductions
+// are block-wide (row_sum's barrier): a rare-row walk reduced over the group
+// must be reached by every group of the block. The forward kernels' walks
+// reduce each rare row within one wave instead; the backward's stage 1,
+// which ends in a block-wide combine anyway, has its groups walk the union
+// of their marks.
 template <int TPR, int BLOCK>
 constexpr bool kBlockFlag = TPR > kWave && BLOCK / TPR > 1;
 

@@ -134,7 +134,6 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
   static_assert(!LN || (!FUSED && OUT == kOutAct), "LayerNorm: plain output only");
   __shared__ RedT<OUT> red[2 * (BLOCK / kWave)];
   __shared__ RareRedT<OUT> rared[2 * (BLOCK / kWave)];  // rare rows (after the loop)
-  __shared__ uint64_t rmasks[RPB];
   const float tinv = tensor_inv_scale<T, G, OUT>(a);
 
   const int nunits = a.N / E;
@@ -303,7 +302,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
     }
   }
 
-  rare_rows_after<T, G, VEC, TPR, BLOCK, OUT, LN>(
+  rare_rows_walk<T, G, VEC, TPR, BLOCK, OUT, LN>(
       rare_mask,
       [&](int it, RareRow<T, G>& r) {
         const int64_t row = bx * RPB + static_cast<int64_t>(it) * gridDim.x * RPB + grp;
@@ -312,7 +311,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
         r.tinv = tinv;
         return ok;
       },
-      lane, rared, rmasks);
+      lane, rared);
 }
 
 // Persistent register path for 16-byte-aligned rows. The grid has one block
@@ -337,7 +336,6 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
   static_assert(OUT == kOutAct || E == 8, "fp8 units of 8 bytes");
   __shared__ RedT<OUT> red[2 * (BLOCK / kWave)];
   __shared__ RareRedT<OUT> rared[2 * (BLOCK / kWave)];  // rare rows (after the loop)
-  __shared__ uint64_t rmasks[RG];
   const float tinv = tensor_inv_scale<T, G, OUT>(a);
 
   const int nunits = a.N / E;
@@ -617,7 +615,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
     if (b + nblk * (s0 + RG) >= a.M) break;
     step(b + nblk * (s0 + RG), bx, br, ax, ar);
   }
-  rare_rows_after<T, G, true, TPR, BLOCK, OUT, LN>(
+  rare_rows_walk<T, G, true, TPR, BLOCK, OUT, LN>(
       rare_mask,
       [&](int it, RareRow<T, G>& r) {
         const int64_t row = b + nblk * (static_cast<int64_t>(RG) * it + grp);
@@ -626,7 +624,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
         r.tinv = tinv;
         return ok;
       },
-      lane, rared, rmasks);
+      lane, rared);
 }
 
 template <class T, class G, bool VEC, int BLOCK, int UNROLL, bool FUSED, bool CACHE, int OUT,

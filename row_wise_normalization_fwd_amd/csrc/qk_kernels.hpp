@@ -48,7 +48,6 @@ __global__ __launch_bounds__(BLOCK) void qk_norm_kernel(QKArgs<T, G> a) {
   static_assert(BLOCK % TPR == 0 && BLOCK % kWave == 0, "block shape");
   __shared__ float red[2 * (BLOCK / kWave)];
   __shared__ double rared[2 * (BLOCK / kWave)];  // rare rows (after the loop)
-  __shared__ uint64_t rmasks[RPB];
 
   const int nunits = a.N / E;
   const int grp = threadIdx.x / TPR;
@@ -143,7 +142,7 @@ __global__ __launch_bounds__(BLOCK) void qk_norm_kernel(QKArgs<T, G> a) {
       }
     }
   }
-  rare_rows_after<T, G, VEC, TPR, BLOCK, kOutAct, false>(
+  rare_rows_walk<T, G, VEC, TPR, BLOCK, kOutAct, false>(
       rare_mask,
       [&](int it, RareRow<T, G>& r) {
         const uint64_t row64 = static_cast<uint64_t>(blockIdx.x) * RPB +
@@ -167,7 +166,7 @@ __global__ __launch_bounds__(BLOCK) void qk_norm_kernel(QKArgs<T, G> a) {
         r.eps = a.eps;
         return ok;
       },
-      lane, rared, rmasks);
+      lane, rared);
 }
 
 }  // namespace rmsn

@@ -4,7 +4,7 @@
 // The forward kernels do not handle such a row inside their row loops: the
 // loop only tests the row, withholds its stores (the fused add's h is still
 // written) and sets bit t (the loop iteration) in a 64-bit mask. After the
-// loop, rare_rows_after redoes the marked rows one by one with rare_row, so
+// loop, rare_rows_walk redoes the marked rows one by one with rare_row, so
 // none of that code competes for registers with the loop. rare_row re-reads
 // the row (x, or h from the residual buffer; nothing of the row has been
 // written yet, also when y aliases x), gamma and beta from memory, forms the
@@ -296,27 +296,47 @@ __device__ void rare_row(const RareRow<T, G>& r, int lane, bool store, RareRedT<
 
 // After a kernel's row loop: redo the rows marked in `mine` (bit t: the
 // group's row of loop iteration t, as row_of(t, r) gives it; row_of returns
-// false when the group had no row in that iteration). For blocks of several
-// multi-wave groups, every group walks the union of the block's marks
-// (`masks`: one LDS word per group) so all of them reach the reductions.
+// false when the group had no row in that iteration). `mine` is the same in
+// every lane of the group. In blocks of several multi-wave groups a row
+// reduced over the whole group would take block-wide barriers, which every
+// group must then reach, so the groups would first have to exchange their
+// marks -- one more barrier after the loop even when nothing is rare, and it
+// holds the block (and the next block on its CU) until the last stores are
+// acknowledged. There the group's waves instead take its rare rows in
+// turn, one row per wave, reduced within the wave.
 template <class T, class G, bool VEC, int TPR, int BLOCK, int OUT, bool LN, class RowOf>
-__device__ void rare_rows_after(uint64_t mine, const RowOf& row_of, int lane,
-                                RareRedT<OUT>* scratch, uint64_t* masks) {
-  uint64_t m = mine;
-  if constexpr (kBlockFlag<TPR, BLOCK>) {
-    if (threadIdx.x % TPR == 0) masks[threadIdx.x / TPR] = mine;
-    __syncthreads();
-    m = 0;
-#pragma unroll
-    for (int g = 0; g < BLOCK / TPR; ++g) m |= masks[g];
-  }
+__device__ void rare_rows_walk(uint64_t mine, const RowOf& row_of, int lane,
+                               RareRedT<OUT>* scratch) {
   int parity = 0;
-  while (m != 0) {
-    const int t = __builtin_ctzll(m);
-    m &= m - 1;
-    RareRow<T, G> r;
-    const bool valid = row_of(t, r);
-    rare_row<T, G, VEC, TPR, BLOCK, OUT, LN>(r, lane, valid && ((mine >> t) & 1), scratch, parity);
+  if constexpr (TPR >= kWave) {
+    // A group of whole waves: the mask is wave-uniform, so the walk branches
+    // on scalar registers (as does the test that skips it).
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(mine >> 32));
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(mine));
+    mine = (static_cast<uint64_t>(hi) << 32) | lo;
+  }
+  if constexpr (kBlockFlag<TPR, BLOCK>) {
+    constexpr int kWavesPerRow = TPR / kWave;
+    const int wg = lane / kWave;  // this wave within the group
+    uint64_t m = mine;
+    for (int j = 0; m != 0; ++j) {
+      const int t = __builtin_ctzll(m);
+      m &= m - 1;
+      if (j % kWavesPerRow == wg) {
+        RareRow<T, G> r;
+        const bool valid = row_of(t, r);
+        rare_row<T, G, VEC, kWave, kWave, OUT, LN>(r, __lane_id(), valid, scratch, parity);
+      }
+    }
+  } else {
+    uint64_t m = mine;
+    while (m != 0) {
+      const int t = __builtin_ctzll(m);
+      m &= m - 1;
+      RareRow<T, G> r;
+      const bool valid = row_of(t, r);
+      rare_row<T, G, VEC, TPR, BLOCK, OUT, LN>(r, lane, valid, scratch, parity);
+    }
   }
 }
 

@@ -120,8 +120,8 @@ def domain_cases(xdt, kind):
 
 
 # Shapes per kernel family (16-bit units): register rows, several rows per
-# block (64, 1000), two 128-lane groups per block sharing the rare-row flags
-# (2048 16-bit / 1024 fp32), one 512-lane group (4096), the persistent
+# block (64, 1000), two 128-lane groups per block, whose rare rows are each
+# redone by one wave (2048 16-bit / 1024 fp32), one 512-lane group (4096), the persistent
 # 8192-wide kernel over several iterations per row group, and LDS-cached and
 # re-read long rows.
 FWD_SHAPES = [(37, 64), (20000, 64), (37, 1000), (45, 1024), (45, 2048), (45, 4096), (29, 5000),
@@ -135,6 +135,58 @@ def test_fwd_domain(kind, shape, pair):
     M, N = shape
     for i, (scales, eps) in enumerate(domain_cases(pair[0], kind)):
         run_domain_fwd(M, N, *pair, scales, eps, seed=N + i)
+
+
+def test_fwd_rare_rows_outnumber_group_waves():
+    """Four rows in five overflow the fp32 sum of squares, over six loop
+    iterations per row group of the persistent 8192-wide kernel (four
+    256-lane groups per block): a group's waves take its rare rows in turn,
+    so most groups have more rare rows than waves."""
+    run_domain_fwd(12288, 8192, O.BF16, O.BF16, [1.0, 1e20, 1e30, 1e37, 1e30], 1e-5, seed=77)
+
+
+def test_fwd_rare_rows_in_late_iterations():
+    """Rare rows in loop iterations 0 to 39 of the persistent 8192-wide kernel:
+    81920 rows give every row group 40 iterations (512 blocks of four groups
+    on 256 CUs: row r is in iteration r // 2048), so the rare-row mask's bit
+    31 and its high word are used. The batch is 1024 seeded rows repeated;
+    the rare rows and a sample of the others are checked against the oracle,
+    and every other row bit for bit against a batch without rare rows."""
+    M, N, dt = 81920, 8192, O.BF16
+    _log(f"late-iteration rare rows M={M} N={N}")
+    base = G.normal(101, G.STREAM_X, 1024, N, dt)
+    g = G.uniform(101, G.STREAM_GAMMA, N, 0.5, 1.5, dt)
+    gt = _put(g, dt)
+    rare = np.array(sorted({2048 * t + k for t in (0, 1, 30, 31, 32, 33, 39)
+                            for k in (0, 1, 517, 1023, 1500, 2047)}))
+    scale = np.where(np.arange(rare.size) % 2 == 0, 1e30, 1e37)[:, None]
+    xr = O.round_to(O.decode(base[rare % 1024], dt) * scale, dt)
+
+    def run(xt):
+        yt = torch.empty_like(xt)
+        rt = torch.full((M,), -1.0, device="cuda")
+        st = R.rmsnorm_fwd(xt, gt, yt, rt, M, N, 1e-5, dt, dt, _stream())
+        assert st == 0, R.rmsnorm_status_string(st)
+        torch.cuda.synchronize()
+        return yt, rt
+
+    xt = to_device(base, dt).repeat(M // 1024, 1)
+    y0, r0 = run(xt)
+    xt[torch.from_numpy(rare).cuda()] = to_device(xr, dt)
+    y1, r1 = run(xt)
+    ref = O.rmsnorm_fwd(xr, g, rare.size, N, 1e-5, dt, dt)
+    idx = torch.from_numpy(rare).cuda()
+    check_output(to_host(y1[idx]), ref["y_exact"], ref["y"], dt, "rare y")
+    check_rstd(to_host(r1[idx]), ref["rstd_exact"])
+    keep = torch.ones(M, dtype=torch.bool, device="cuda")
+    keep[idx] = False
+    assert torch.equal(y1[keep].view(torch.int16), y0[keep].view(torch.int16)), "ordinary rows changed"
+    assert torch.equal(r1[keep].view(torch.int32), r0[keep].view(torch.int32))
+    sample = np.setdiff1d(np.random.default_rng(5).choice(M, 64, replace=False), rare)
+    sref = O.rmsnorm_fwd(base[sample % 1024], g, sample.size, N, 1e-5, dt, dt)
+    sidx = torch.from_numpy(sample).cuda()
+    check_output(to_host(y1[sidx]), sref["y_exact"], sref["y"], dt, "ordinary y")
+    check_rstd(to_host(r1[sidx]), sref["rstd_exact"])
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
