@@ -128,8 +128,27 @@ template <class T, class G, bool FUSED>
 __device__ __forceinline__ void split_row_factor(const SplitArgs<T, G>& a, int64_t row, int lane,
                                                  const float* parts, int64_t stride, float& f,
                                                  int& e, float& rs) {
+  // Lane l adds partials l, l + 64, l + 128, ... in that order, four loads
+  // at a time issued together (indices past the row clamped to its last
+  // tile, so none is behind a branch) to share one memory round trip; rows of
+  // up to 256 tiles take one batch. A slot past the row adds +0.0, which
+  // changes no bit: partials are sums of squares, so the sum starts at +0.0
+  // and never becomes -0.0.
+  constexpr int kBatch = 4;
   double s = 0.0;
-  for (int c = lane; c < a.chunks; c += kWave) s = s + static_cast<double>(parts[c * stride]);
+  auto batch = [&](int c0) {
+    float v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int c = c0 + j * kWave;
+      v[j] = parts[static_cast<int64_t>(c < a.chunks ? c : a.chunks - 1) * stride];
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      s = s + (c0 + j * kWave < a.chunks ? static_cast<double>(v[j]) : 0.0);
+  };
+  batch(lane);
+  for (int c0 = lane + kBatch * kWave; c0 < a.chunks; c0 += kBatch * kWave) batch(c0);
   s = group_sum<kWave>(s);
   const float q = static_cast<float>(s) / static_cast<float>(a.N) + a.eps;
   f = 1.0f / __builtin_sqrtf(q);
@@ -156,22 +175,42 @@ __device__ __forceinline__ void split_row_factor(const SplitArgs<T, G>& a, int64
   }
 }
 
-// The tile's gamma (0 past the row).
+// The tile's gamma as its raw 16-byte words (zeros past the row): loaded
+// early, with x, and widened (split_tile_gamma) once it is needed, so that
+// its round trip overlaps the others.
 template <class T, class G>
-__device__ __forceinline__ void split_tile_gamma(const SplitArgs<T, G>& a, int u0,
-                                                 float (&g)[kSplitUpt][Unit<T, true>::E]) {
+struct SplitGamma {
+  static constexpr int kWords = Unit<T, true>::E * G::kSize / 16;  // 1 or 2 per unit
+  u32x4 w[kSplitUpt][kWords];
+};
+
+template <class T, class G>
+__device__ __forceinline__ void split_tile_gamma_load(const SplitArgs<T, G>& a, int u0,
+                                                      SplitGamma<T, G>& r) {
   constexpr int E = Unit<T, true>::E;
   const int nunits = a.N / E;
 #pragma unroll
   for (int k = 0; k < kSplitUpt; ++k) {
     const int u = u0 + threadIdx.x + k * kSplitBlock;
-    if (u < nunits) {
-      load_gamma<G, E, true>(a.gamma, u * E, g[k]);
-    } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) g[k][e] = 0.0f;
-    }
+    for (int c = 0; c < SplitGamma<T, G>::kWords; ++c)
+      r.w[k][c] = u < nunits
+          ? *reinterpret_cast<const u32x4*>(a.gamma + u * E + c * (16 / G::kSize))
+          : (u32x4){0u, 0u, 0u, 0u};
   }
+}
+
+// The tile's gamma widened to fp32.
+template <class T, class G>
+__device__ __forceinline__ void split_tile_gamma(const SplitGamma<T, G>& r,
+                                                 float (&g)[kSplitUpt][Unit<T, true>::E]) {
+#pragma unroll
+  for (int k = 0; k < kSplitUpt; ++k)
+#pragma unroll
+    for (int c = 0; c < SplitGamma<T, G>::kWords; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        G::widen_word(r.w[k][c][w], g[k] + c * (16 / G::kSize) + w * G::kPerWord);
 }
 
 // y over the tile from its units (x, or h when fused), its gamma and the
@@ -300,6 +339,8 @@ __global__ __launch_bounds__(kSplitBlock) void fwd_split_apply_kernel(SplitArgs<
       const int u = u0 + threadIdx.x + k * kSplitBlock;
       raw[k] = u < nunits ? U::load_nt(src + off + u * E) : U::zero();
     }
+    SplitGamma<T, G> graw;
+    split_tile_gamma_load<T, G>(a, u0, graw);
     float f;
     int ex;
     if constexpr (SPREAD) {
@@ -326,7 +367,7 @@ __global__ __launch_bounds__(kSplitBlock) void fwd_split_apply_kernel(SplitArgs<
     // region it came from (and before the next tile's factor replaces it).
     __syncthreads();
     float g[kSplitUpt][E];
-    split_tile_gamma<T, G>(a, u0, g);
+    split_tile_gamma<T, G>(graw, g);
     split_tile_store<T, G>(a, off, u0, raw, g, f, ex);
   }
 }

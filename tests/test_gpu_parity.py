@@ -127,6 +127,16 @@ def test_fwd_split_boundaries():
     run_fused(2, N, O.BF16, O.F32, seed=335, x_is_r=True)
 
 
+def test_fwd_split_many_tiles():
+    """Rows of more than 256 tiles, whose factor adds its partials in several
+    batches of four per lane: two launches where the last tile holds a slot
+    for every tile of the row, three (the finalize pass) where it does not."""
+    run_fwd(2, 8192 * 300 + 4096, O.BF16, O.BF16, seed=336, want_rstd=True)  # 301 tiles, two
+    run_fwd(2, 8192 * 300 + 8, O.BF16, O.BF16, seed=337, want_rstd=True)     # 301 tiles, three
+    run_fwd(1, 4096 * 700 + 4, O.F32, O.F32, seed=338, want_rstd=True)       # 701 tiles, three
+    run_fused(2, 8192 * 520 + 4096, O.BF16, O.BF16, seed=339, want_rstd=True)  # 521 tiles
+
+
 def test_fwd_split_graph_replay():
     """The split path's three launches captured in a graph: every replay,
     with eager work and other outputs' clearing between replays, equals the
