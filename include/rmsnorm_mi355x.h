@@ -189,11 +189,13 @@ int rmsnorm_qk_fwd(void* q, void* k, const void* q_gamma, const void* k_gamma,
 
 /* Bytes of device workspace rmsnorm_bwd (and rmsnorm_fused_add_bwd) needs
  * for an [M, N] problem, whatever the dtypes: the fp32 dgamma partials,
- * G x N with G = max(min(M, 256), ceil(M / 64)) workgroups (rounded up to
- * 256 bytes), and for N > 8192 a 16-byte record per row (rows longer than the
- * one-pass kernel holds take a two-pass tier that keeps its row dots there;
- * 16-bit rows up to 16384 elements stay one-pass and leave it unused). Pure
- * host function; returns 0 for M <= 0, N <= 0 or N > RMSN_MAX_N. */
+ * G x N (rounded up to 256 bytes) with G = max(min(M, T), ceil(M / 64))
+ * partial rows, T = 256 for N <= 16384 and ceil(2^22 / N) above (such rows
+ * take the two-pass tier, which runs column tiles x G workgroups), and for
+ * N > 8192 a 16-byte record per row (rows longer than the one-pass kernel
+ * holds keep their row dots there; 16-bit rows up to 16384 elements stay
+ * one-pass and leave it unused). Pure host function; returns 0 for M <= 0,
+ * N <= 0 or N > RMSN_MAX_N. */
 size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N);
 
 /* Backward RMSNorm (FlyDSL guide section 1.2, "Backward": inputs x, gamma, dy
@@ -212,8 +214,8 @@ size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N);
  *   workspace at least rmsnorm_bwd_workspace_size(M, N) bytes of device
  *             memory, 16-byte aligned, disjoint from every other buffer; its
  *             contents on entry are ignored.
- * The workgroup partition depends only on M, which fixes the summation order.
- * A row whose fp32 row dot overflows (a product dy x or dy x gamma beyond the
+ * The workgroup partition depends only on M and N, which fixes the summation
+ * order. A row whose fp32 row dot overflows (a product dy x or dy x gamma beyond the
  * fp32 range) is recomputed in fp64 in the same launch. Outside that, the
  * fp32 formula needs gamma_j dy_ij within the fp32 range, and rstd as the
  * forward produced it (positive, finite); a row with rstd = +inf (the 0/0 of

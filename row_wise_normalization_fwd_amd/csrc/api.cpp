@@ -401,9 +401,12 @@ BwdPlan plan_bwd(int64_t M, int64_t N) {
   BwdPlan p{false, 0, 0, 0};
   if (M <= 0 || N <= 0 || !shape_ok(M, N)) return p;
   p.valid = true;
-  // min(M, 256) blocks, more when a block would own over kBwdMaxRowsPerBlock
-  // rows: every partial is then an fp32 sum of at most that many rows.
-  p.blocks = M < kBwdTargetBlocks ? M : kBwdTargetBlocks;
+  // min(M, 256) blocks (long rows: enough for about kBwdLongTiles tiles),
+  // more when a block would own over kBwdMaxRowsPerBlock rows: every partial
+  // is then an fp32 sum of at most that many rows.
+  const int64_t target =
+      N > kBwdLongN ? ceil_div(kBwdLongTiles * kBwdTileCols, N) : kBwdTargetBlocks;
+  p.blocks = M < target ? M : target;
   const int64_t by_rows = ceil_div(M, kBwdMaxRowsPerBlock);
   if (p.blocks < by_rows) p.blocks = by_rows;
   auto round256 = [](uint64_t b) { return (b + 255u) & ~static_cast<uint64_t>(255u); };

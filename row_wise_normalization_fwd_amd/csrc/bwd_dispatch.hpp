@@ -85,6 +85,7 @@ hipError_t long_rows_typed(const BwdArgs<T, G>& a, double* cdot, int64_t blocks,
   constexpr int kTileBlock = 256;
   constexpr int kTileUpt = VEC ? 2 : 8;
   constexpr int E = Unit<T, VEC>::E;
+  static_assert(kTileBlock * kTileUpt * E <= kBwdTileCols, "the partition assumes narrower tiles");
   const int64_t rows = a.M < kMaxGrid ? a.M : kMaxGrid;
   bwd_rowdot_kernel<T, G, VEC, 1024, kUnroll, LN>
       <<<dim3(static_cast<unsigned>(rows)), dim3(1024), 0, s>>>(a, cdot);

@@ -26,7 +26,7 @@
 // ..., so at any moment all blocks work inside one compact window of rows
 // (measured 10% faster than contiguous row ranges at 8192 x 8192 bf16) -- and
 // writes one fp32 partial row per block; stage 2 sums the partials of each
-// column in a fixed order. G depends only on M, so results are bit-
+// column in a fixed order. G depends only on M and N, so results are bit-
 // reproducible.
 #pragma once
 

@@ -13,7 +13,9 @@
 // block. Rows that are not 16-byte aligned use 1-element units (up to 8 per
 // lane). Non-fused 16-bit rows of 769 to 1024 units (N in (6144, 8192]) use
 // the persistent fwd_pp_kernel instead (4096 x 8192 bf16: 22.0-22.6 us vs
-// 23.7-24.0 us; it did not help the fused add or 625-unit rows). Longer rows:
+// 23.7-24.0 us; it did not help the fused add or 625-unit rows), and so do
+// plain rows of 1537..4096 units (N in (12288, 32768] 16-bit, (8192, 16384]
+// fp32) with 512 or 1024 lanes per row. Other longer rows:
 // one block per row, parked in LDS when the row fits the
 // device's per-workgroup LDS (160 KiB on gfx950), else re-read; 512 threads
 // for rows up to 32 KiB, 1024 above (measured at 128 MiB of bf16: 16384-
@@ -209,6 +211,23 @@ hipError_t fwd_typed(const FwdCall& c) {
       if (tpr <= 64) return run_fwd_reg<T, G, false, 64, 8, 256, FUSED, OUT, LN>(a, s);
       if (tpr <= 256) return run_fwd_reg<T, G, false, 256, 8, 256, FUSED, OUT, LN>(a, s);
       return run_fwd_reg<T, G, false, 1024, 8, 1024, FUSED, OUT, LN>(a, s);
+    }
+  }
+  if constexpr (!FUSED && OUT == kOutAct && !LN) {
+    // Rows of 1537..4096 16-byte units: the persistent kernel with 512 or
+    // 1024 lanes per row and three or four units per lane, chosen to leave
+    // few lanes idle. Against the LDS-row kernel, alternating in one process
+    // (rows rotated over >= 1 GiB): bf16 2048 x 16384 22.0-22.2 us vs
+    // 24.7-24.9, 2048 x 24576 35.8-36.0 vs 37.3-37.5, 1024 x 32768 23.3-23.5
+    // vs 25.4-25.6, 20480 and 14000 +1-2%; fp32 4096 x 8196 47.7-47.9 vs
+    // 52.1-52.9, 2048 x 12288 +4%, 16384 +0.6%. Shorter rows stay with the
+    // LDS-row kernel: 512 lanes of three units lost 5-7% at 8200 and 10000
+    // bf16 elements and gained 1.7% only at a full 12288.
+    if (vec) {
+      const int64_t units = c.N / (16 / T::kSize);
+      if (units > 1536 && units <= 2048) return run_fwd_pp<T, G, 512, 4, 1024, FUSED, OUT, LN>(a, s);
+      if (units > 2048 && units <= 3072) return run_fwd_pp<T, G, 1024, 3, 1024, FUSED, OUT, LN>(a, s);
+      if (units > 3072 && units <= 4096) return run_fwd_pp<T, G, 1024, 4, 1024, FUSED, OUT, LN>(a, s);
     }
   }
   const int64_t row_bytes = c.N * T::kSize;

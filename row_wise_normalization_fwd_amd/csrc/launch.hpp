@@ -98,11 +98,18 @@ struct QKCall {
 
 hipError_t launch_qk(const QKCall& c, int x_dtype);
 
-// Backward partition: G = max(min(M, kBwdTargetBlocks), ceil(M /
-// kBwdMaxRowsPerBlock)) blocks, block b owning rows b, b + G, b + 2G, ... It
-// depends only on M, which fixes the dgamma summation order. The workspace
-// holds the fp32 partial rows [G, N] and, for rows longer than kBwdOnChipN,
-// a 16-byte record per row (the row dots of the two-pass long-row tier).
+// Backward partition: G blocks, block b owning rows b, b + G, b + 2G, ...,
+// each writing one fp32 partial row of dgamma (and dbeta). Rows of up to
+// kBwdLongN elements: G = max(min(M, kBwdTargetBlocks), ceil(M /
+// kBwdMaxRowsPerBlock)), one stage-1 block per partial row. Longer rows
+// always take the two-pass long-row tier, whose tile pass runs (column tiles
+// of at most kBwdTileCols elements) x G blocks, so there G = max(min(M,
+// ceil(kBwdLongTiles * kBwdTileCols / N)), ceil(M / kBwdMaxRowsPerBlock))
+// keeps about kBwdLongTiles blocks busy with far fewer partial rows (their
+// write and re-read was otherwise up to twice the input: 64 rows of 2^20).
+// G depends only on M and N, which fixes the dgamma summation order. The
+// workspace holds the fp32 partial rows [G, N] and, for rows longer than
+// kBwdOnChipN, a 16-byte record per row (the long-row tier's row dots).
 struct BwdPlan {
   bool valid;
   int64_t blocks;  // G
@@ -122,6 +129,13 @@ constexpr int64_t kBwdMaxRowsPerBlock = 64;
 // Rows up to this many elements may use the one-pass backward (registers);
 // longer rows use the two-pass long-row tier when they do not fit.
 constexpr int64_t kBwdOnChipN = 8192;
+// Rows longer than this take the long-row tier whatever their type (the
+// one-pass limit is 16384 elements for 16-bit rows, kBwdOnChipN for fp32).
+constexpr int64_t kBwdLongN = 16384;
+// The long-row tier's tile pass: at most this many elements per column tile
+// (256 lanes x 2 units of 8 16-bit elements), and about this many blocks.
+constexpr int64_t kBwdTileCols = 4096;
+constexpr int64_t kBwdLongTiles = 1024;
 
 struct BwdCall {
   const void* dy;

@@ -129,6 +129,16 @@ def test_workspace_size():
     assert R.rmsnorm_bwd_workspace_size(1000, 10000) == 256 * 10000 * 4 + 16128
     assert R.rmsnorm_bwd_workspace_size(3, 8193) == 98_560 + 256   # 98,316 -> 98,560
     assert R.rmsnorm_bwd_workspace_size(3, 8192) == 98_304         # no records at 8192
+    # Rows longer than 16384 (always the two-pass tier, column tiles x G
+    # workgroups): G = max(min(M, ceil(2^22 / N)), ceil(M / 64)).
+    assert R.rmsnorm_bwd_workspace_size(4096, 16384) == 256 * 16384 * 4 + 4096 * 16
+    assert R.rmsnorm_bwd_workspace_size(4096, 16385) == 256 * 16385 * 4 + 4096 * 16  # 2^22/16385 -> 256
+    assert R.rmsnorm_bwd_workspace_size(2048, 32768) == 128 * 32768 * 4 + 2048 * 16
+    assert R.rmsnorm_bwd_workspace_size(512, 131072) == 32 * 131072 * 4 + 512 * 16
+    assert R.rmsnorm_bwd_workspace_size(64, 1 << 20) == 4 * (1 << 20) * 4 + 1024
+    assert R.rmsnorm_bwd_workspace_size(3, 1 << 21) == 2 * (1 << 21) * 4 + 256
+    assert R.rmsnorm_bwd_workspace_size(100000, 20000) == 125_040_128 + 1_600_000  # 64 rows; 1563 * 20000 * 4 rounded up
+    assert R.layernorm_bwd_workspace_size(512, 131072) == 2 * 32 * 131072 * 4 + 512 * 16
 
 
 def test_max_n():
@@ -184,7 +194,7 @@ def test_noalloc_backward_host_checks(lib):
     assert R.rmsnorm_bwd_workspace_size(65537, 8192) > cap
     assert nbwd(M=65537, N=8192) == SCRATCH
     assert nbwd(M=65537, N=8192, dy=None) == SCRATCH   # the size check comes first
-    assert nbwd(M=4096, N=32768) == SCRATCH            # 256 x 32768 x 4 B of partials
+    assert nbwd(M=8192, N=65536) == SCRATCH            # 128 x 65536 x 4 B of partials + records
     assert nbwd(M=1, N=2 ** 23) == SCRATCH             # one 32 MiB partial row + a record
     assert R.rmsnorm_last_hip_error() == 0
 

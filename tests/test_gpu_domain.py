@@ -121,11 +121,12 @@ def domain_cases(xdt, kind):
 
 # Shapes per kernel family (16-bit units): register rows, several rows per
 # block (64, 1000), two 128-lane groups per block, whose rare rows are each
-# redone by one wave (2048 16-bit / 1024 fp32), one 512-lane group (4096), the persistent
-# 8192-wide kernel over several iterations per row group, and LDS-cached and
-# re-read long rows.
+# redone by one wave (2048 16-bit / 1024 fp32), one 512-lane group (4096),
+# the persistent kernel over several iterations per row group (8192; 16384
+# and 32768 16-bit / fp32 16384 with 512- and 1024-lane groups), and
+# LDS-cached and re-read long rows.
 FWD_SHAPES = [(37, 64), (20000, 64), (37, 1000), (45, 1024), (45, 2048), (45, 4096), (29, 5000),
-              (5000, 8192), (3, 20000), (3, 45000)]
+              (5000, 8192), (1030, 16384), (520, 32768), (3, 20000), (3, 45000)]
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
@@ -480,7 +481,7 @@ def test_dgamma_long_m_strict_bound():
     column of dgamma meets max(1e-3 |o|, 2^-24 sum_i |dy x rho|) with no
     widening for the number of rows."""
     M, N, xdt = 131072, 1024, O.BF16
-    assert -(-M // partition_blocks(M)) == 64
+    assert -(-M // partition_blocks(M, N)) == 64
     _log(f"dgamma long M={M} N={N}")
     x = G.normal(21, G.STREAM_X, M, N, xdt)
     dy = G.normal(21, G.STREAM_DY, M, N, xdt)

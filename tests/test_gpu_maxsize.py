@@ -228,7 +228,7 @@ def test_maxsize_backward(res):
     col = _period_sum(lambda k: O.rmsnorm_bwd(dy[:k], x[:k], rho[:k], g, k, N, xdt, gdt,
                                               want_exact=False), M)
     # At most 64 rows per stage-1 partial: the unwidened bound holds.
-    assert -(-M // partition_blocks(M)) <= 64
+    assert -(-M // partition_blocks(M, N)) <= 64
     check_dgamma(to_host(dgt), {"dgamma": col("dgamma"), "s": col("s")})
 
 
@@ -259,7 +259,7 @@ def test_maxsize_layernorm_backward():
                         rstd[src], xdt)
     col = _period_sum(lambda k: O.layernorm_bwd(dy[:k], x[:k], mean[:k], rstd[:k], g, k, N, xdt,
                                                 gdt, want_exact=False), M)
-    Rp = -(-M // partition_blocks(M))
+    Rp = -(-M // partition_blocks(M, N))
     check_column_sum("layernorm dgamma", to_host(dgt), col("dgamma"), col("sg"), 3 + Rp)
     check_column_sum("layernorm dbeta", to_host(dbt), col("dbeta"), col("sb"), 1 + Rp)
 

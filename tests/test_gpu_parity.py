@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 PAIRS = [(O.F32, O.F32), (O.F16, O.F16), (O.F16, O.F32), (O.BF16, O.BF16), (O.BF16, O.F32)]
 PAIR_IDS = ["f32", "f16", "f16_gf32", "bf16", "bf16_gf32"]
 N_SWEEP = [1, 7, 8, 63, 64, 1000, 1024, 2047, 2048, 4096, 4999, 5000, 5001, 6152, 7000, 8191, 8192, 8193,
-           12288, 16384, 32768]
+           8196, 12288, 12296, 16384, 20000, 24576, 28000, 32760, 32768]
 N_LDS = {O.F32: 20000, O.F16: 40000, O.BF16: 40000}      # 80 KB rows: LDS-cached, 1024 threads
 N_REREAD = {O.F32: 45000, O.F16: 90000, O.BF16: 90000}   # 180 KB rows: beyond 160 KiB of LDS
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "exact_rows.txt")
@@ -89,6 +89,22 @@ def run_fwd(M, N, xdt, gdt, eps=1e-5, seed=7, want_rstd=True, misalign=0, inplac
 def test_fwd_sweep(N, pair):
     run_fwd(3, N, *pair, seed=100 + N)
     run_fwd(67, N, *pair, seed=200 + N, want_rstd=False)
+
+
+# Rows of 1537..4096 16-byte units take the persistent kernel with 512 or
+# 1024 lanes per row (16-bit N in (12288, 32768], fp32 N in (8192, 16384]):
+# enough rows that groups run several loop iterations, the last one ragged.
+PP_LONG = {O.F32: [(1500, 8196), (1100, 12288), (1030, 16384)],
+           O.F16: [(2100, 16384), (1100, 20000), (1030, 32760)],
+           O.BF16: [(2100, 14000), (1100, 24576), (1030, 32768)]}
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_fwd_persistent_long_rows(pair):
+    for i, (M, N) in enumerate(PP_LONG[pair[0]]):
+        run_fwd(M, N, *pair, seed=40 + i, want_rstd=(i % 2 == 0))
+    M, N = PP_LONG[pair[0]][-1]
+    run_fwd(M, N, *pair, seed=44, inplace=True)
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
