@@ -190,12 +190,13 @@ int rmsnorm_qk_fwd(void* q, void* k, const void* q_gamma, const void* k_gamma,
 /* Bytes of device workspace rmsnorm_bwd (and rmsnorm_fused_add_bwd) needs
  * for an [M, N] problem, whatever the dtypes: the fp32 dgamma partials,
  * G x N (rounded up to 256 bytes) with G = max(min(M, T), ceil(M / 64))
- * partial rows, T = 256 for N <= 16384 and ceil(2^22 / N) above (such rows
+ * partial rows, T = 256 for N <= 32768 and ceil(2^22 / N) above (such rows
  * take the two-pass tier, which runs column tiles x G workgroups), and for
  * N > 8192 a 16-byte record per row (rows longer than the one-pass kernel
- * holds keep their row dots there; 16-bit rows up to 16384 elements stay
- * one-pass and leave it unused). Pure host function; returns 0 for M <= 0,
- * N <= 0 or N > RMSN_MAX_N. */
+ * holds keep their row dots there; rows of up to 4096 16-byte units --
+ * 32768 16-bit / 16384 fp32 elements, 24576 for the 16-bit fused add, 16384
+ * for 16-bit LayerNorm -- stay one-pass and leave it unused). Pure host
+ * function; returns 0 for M <= 0, N <= 0 or N > RMSN_MAX_N. */
 size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N);
 
 /* Backward RMSNorm (FlyDSL guide section 1.2, "Backward": inputs x, gamma, dy

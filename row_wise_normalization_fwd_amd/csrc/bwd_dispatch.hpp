@@ -4,8 +4,10 @@
 //
 // Stage 1 uses a group of TPR lanes per row with two 16-byte units per lane
 // (TPR = next power of two of ceil(units / 2), up to 1024 lanes, i.e. 16384
-// bf16 / 8192 fp32 elements; unaligned rows up to 8192 elements). Longer rows
-// take the two-pass long-row tier (row dots, then 2-D tiles). When a block owns at least two rows,
+// bf16 / 8192 fp32 elements; unaligned rows up to 8192 elements), then 1024
+// lanes of three or four units (up to 4096 units: 32768 16-bit / 16384 fp32
+// elements; see stage1_typed). Longer rows take the two-pass long-row tier
+// (row dots, then 2-D tiles). When a block owns at least two rows,
 // it runs 1024 threads, i.e. 1024 / TPR row groups whose dgamma partials are
 // combined through LDS: at 8192 x 8192 bf16 this (two 512-lane groups per
 // block, one block per CU, next-row prefetch) measured fastest among 1, 2 and
@@ -17,15 +19,16 @@
 
 namespace rmsn {
 
-template <class T, class G, bool RES, bool LN, bool VEC, int TPR, int UPT, int BLOCK>
+template <class T, class G, bool RES, bool LN, bool VEC, int TPR, int UPT, int BLOCK, bool PF = true>
 hipError_t run_stage1(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s) {
   constexpr int RG = BLOCK / TPR;
   constexpr int E = Unit<T, VEC>::E;
   // Row-group combine buffer, and LayerNorm's gamma copy aliased with it.
   constexpr size_t kComb = RG > 1 ? static_cast<size_t>(BLOCK) * UPT * E * sizeof(float) : 0;
-  constexpr size_t kGam = LN ? stage1_gamma_lds_bytes<TPR, UPT, E>() : 0;
+  constexpr size_t kGam =
+      stage1_gamma_in_lds<LN, UPT>() ? stage1_gamma_lds_bytes<TPR, UPT, E>() : 0;
   constexpr size_t kLds = kComb > kGam ? kComb : kGam;
-  constexpr auto kernel = bwd_stage1_kernel<T, G, VEC, TPR, UPT, BLOCK, RES, LN>;
+  constexpr auto kernel = bwd_stage1_kernel<T, G, VEC, TPR, UPT, BLOCK, RES, LN, PF>;
   if constexpr (kLds > 48 * 1024) {
     // Raise the dynamic LDS limit (gfx950 has 160 KiB per workgroup).
     const hipError_t attr = ensure_dynamic_lds<kernel>(kLds);
@@ -56,7 +59,20 @@ hipError_t stage1_typed(const BwdArgs<T, G>& a, bool vec, int64_t blocks, hipStr
   if (vec) {
     constexpr int E = 16 / T::kSize;
     const int64_t units = N / E;
-    if (units > 2048) return hipErrorNotSupported;
+    if (units > 2048) {
+      // 1024 lanes of three units with next-row prefetch, or of four units
+      // without it (two register sets of four would not fit 128 VGPRs), gamma
+      // read from LDS. The 16-bit fused add (dresidual is a third operand)
+      // fits only three units without prefetch; the 16-bit LayerNorm kernel
+      // spills even then and takes the two-pass tier.
+      if constexpr (T::kSize == 4 || (!RES && !LN)) {
+        if (units <= 3072) return run_stage1<T, G, RES, LN, true, 1024, 3, 1024, true>(a, blocks, s);
+        if (units <= 4096) return run_stage1<T, G, RES, LN, true, 1024, 4, 1024, false>(a, blocks, s);
+      } else if constexpr (RES) {
+        if (units <= 3072) return run_stage1<T, G, RES, LN, true, 1024, 3, 1024, false>(a, blocks, s);
+      }
+      return hipErrorNotSupported;
+    }
     if (units > 1024) return run_stage1_rows<T, G, RES, LN, true, 1024, 2>(a, blocks, s);
     switch (next_pow2(ceil_div(units, 2))) {
       case 1: return run_stage1_rows<T, G, RES, LN, true, 1, 2>(a, blocks, s);

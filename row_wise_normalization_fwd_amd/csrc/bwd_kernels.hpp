@@ -284,17 +284,27 @@ __device__ void rare_bwd_after(const BwdArgs<T, G>& a, uint64_t mine, int iters,
 // is reduced, so loads stay in flight across rows. With RG > 1 the groups'
 // partials are combined through LDS in group order before the block writes
 // its partial row.
+// Gamma is read from a widened copy in LDS (GL) by LayerNorm, and by the
+// RMSNorm kernels for rows of more than two units per lane, whose operands
+// leave no room for it in registers.
+template <bool LN, int UPT>
+constexpr bool stage1_gamma_in_lds() {
+  return LN || UPT > 2;
+}
+
 template <int TPR, int UPT, int E>
 constexpr size_t stage1_gamma_lds_bytes() {
   return static_cast<size_t>(TPR) * UPT * E * sizeof(float);
 }
 
-template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool RES, bool LN = false>
+template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool RES, bool LN = false,
+          bool PF = true>
 __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   using U = Unit<T, VEC>;
   using Raw = typename U::Raw;
   constexpr int E = U::E;
   constexpr int RG = BLOCK / TPR;
+  constexpr bool GL = stage1_gamma_in_lds<LN, UPT>();
   constexpr int COLS = TPR * UPT * E;  // columns covered by one row group
   static_assert(BLOCK % TPR == 0 && BLOCK % kWave == 0, "block shape");
   static_assert(!(LN && RES), "LayerNorm backward has no residual input");
@@ -313,15 +323,16 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   const int lane = threadIdx.x % TPR;
   const int64_t b = blockIdx.x;
 
-  // LayerNorm's gamma copy in LDS (aliases comb, which is first written after
-  // a barrier that follows the last gamma read): GP planes of GW floats per
-  // unit, plane p of unit u at (p * NU + u) * GW, so the lanes of a wave read
-  // consecutive GW-float words. Units past the row read zeros.
+  // The gamma copy in LDS, for LayerNorm and for rows of more than two units
+  // per lane (GL; it aliases comb, which is first written after a barrier
+  // that follows the last gamma read): GP planes of GW floats per unit, plane
+  // p of unit u at (p * NU + u) * GW, so the lanes of a wave read consecutive
+  // GW-float words. Units past the row read zeros.
   constexpr int NU = TPR * UPT;
   constexpr int GW = E >= 4 ? 4 : E;
   constexpr int GP = E / GW;
   float* const glds = reinterpret_cast<float*>(lds_bytes);
-  if constexpr (LN) {
+  if constexpr (GL) {
     for (int u = threadIdx.x; u < NU; u += BLOCK) {
       float g[E];
       if (u < nunits) {
@@ -354,13 +365,13 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
     }
   };
 
-  [[maybe_unused]] float gam[LN ? 1 : UPT][E];
+  [[maybe_unused]] float gam[GL ? 1 : UPT][E];
   float acc[UPT][E];
   [[maybe_unused]] float accb[LN ? UPT : 1][E];  // LayerNorm dbeta partial sums
 #pragma unroll
   for (int k = 0; k < UPT; ++k) {
     const int u = lane + k * TPR;
-    if constexpr (!LN) {
+    if constexpr (!GL) {
       if (u < nunits) {
         load_gamma<G, E, VEC>(a.gamma, u * E, gam[k]);
       } else {
@@ -437,7 +448,8 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   // One row per group and call: consume (cx, cdy), prefetch the group's next
   // row into (nx, ndy). The loop below alternates two register sets, so the
   // prefetched data is first touched inside the next call, after that call
-  // has issued its own prefetch.
+  // has issued its own prefetch. Without PF (rows whose two register sets
+  // would not fit) the call loads its own row first and waits for it.
   int parity = 0;
   uint64_t rare_mask = 0;  // bit t: this group's row of iteration t is rare
   int t = 0;
@@ -452,7 +464,11 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
       const float mu_ld = a.mean[valid ? row : a.M - 1];
       mu = valid ? mu_ld : 0.0f;
     }
-    load_row(row0 + a.nblk * RG, nx, ndy, nr);
+    if constexpr (PF) {
+      load_row(row0 + a.nblk * RG, nx, ndy, nr);
+    } else {
+      load_row(row0, cx, cdy, cr);
+    }
 
     [[maybe_unused]] double dot = 0.0;
     [[maybe_unused]] DSum2 dots{0.0, 0.0};
@@ -466,6 +482,10 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
         gamma_lds(lane + k * TPR, g);
         unit_dots_ln<E>(dyv, g, xv, mu, rho, s1, s2);
         dots = dots + DSum2{static_cast<double>(s1), static_cast<double>(s2)};
+      } else if constexpr (GL) {
+        float g[E];
+        gamma_lds(lane + k * TPR, g);
+        dot = dot + static_cast<double>(unit_dot<E>(dyv, g, xv));
       } else {
         dot = dot + static_cast<double>(unit_dot<E>(dyv, gam[k], xv));
       }
@@ -513,9 +533,16 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
           accb[k][e] = accb[k][e] + dyv[e];
         }
       } else {
+        float g[E];
+        if constexpr (GL) {
+          gamma_lds(u, g);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) g[e] = gam[k][e];
+        }
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          o[e] = rho * __builtin_fmaf(-xv[e], kcoef, gam[k][e] * dyv[e]);
+          o[e] = rho * __builtin_fmaf(-xv[e], kcoef, g[e] * dyv[e]);
           acc[k][e] = __builtin_fmaf(dyv[e] * xv[e], rho, acc[k][e]);
         }
       }
@@ -535,7 +562,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   };
 
   Raw ax[UPT], ady[UPT], ar[UPT], bx[UPT], bdy[UPT], br[UPT];
-  load_row(b, ax, ady, ar);
+  if constexpr (PF) load_row(b, ax, ady, ar);
   // Trip counts are uniform over the block, so every thread reaches every
   // reduction.
   for (int64_t s0 = 0; b + a.nblk * s0 < a.M; s0 += 2 * RG) {
@@ -550,7 +577,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
       a, rare_mask, t, grp, lane,
       [&](int it) { return b + a.nblk * (static_cast<int64_t>(RG) * it + grp); },
       [&](int k, float* g) {
-        if constexpr (LN) {
+        if constexpr (GL) {
           gamma_lds(lane + k * TPR, g);
         } else {
 #pragma unroll

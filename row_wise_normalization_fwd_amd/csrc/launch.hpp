@@ -101,7 +101,8 @@ hipError_t launch_qk(const QKCall& c, int x_dtype);
 // Backward partition: G blocks, block b owning rows b, b + G, b + 2G, ...,
 // each writing one fp32 partial row of dgamma (and dbeta). Rows of up to
 // kBwdLongN elements: G = max(min(M, kBwdTargetBlocks), ceil(M /
-// kBwdMaxRowsPerBlock)), one stage-1 block per partial row. Longer rows
+// kBwdMaxRowsPerBlock)), one stage-1 block per partial row (when the row
+// takes the one-pass kernel). Longer rows
 // always take the two-pass long-row tier, whose tile pass runs (column tiles
 // of at most kBwdTileCols elements) x G blocks, so there G = max(min(M,
 // ceil(kBwdLongTiles * kBwdTileCols / N)), ceil(M / kBwdMaxRowsPerBlock))
@@ -129,9 +130,10 @@ constexpr int64_t kBwdMaxRowsPerBlock = 64;
 // Rows up to this many elements may use the one-pass backward (registers);
 // longer rows use the two-pass long-row tier when they do not fit.
 constexpr int64_t kBwdOnChipN = 8192;
-// Rows longer than this take the long-row tier whatever their type (the
-// one-pass limit is 16384 elements for 16-bit rows, kBwdOnChipN for fp32).
-constexpr int64_t kBwdLongN = 16384;
+// Rows longer than this take the long-row tier whatever their type and
+// operation (4096 16-byte units: 32768 16-bit elements is the longest
+// one-pass row).
+constexpr int64_t kBwdLongN = 32768;
 // The long-row tier's tile pass: at most this many elements per column tile
 // (256 lanes x 2 units of 8 16-bit elements), and about this many blocks.
 constexpr int64_t kBwdTileCols = 4096;

@@ -159,9 +159,9 @@ def check_column_sum(name: str, got: np.ndarray, o: np.ndarray, mag: np.ndarray,
 
 def partition_blocks(M: int, N: int) -> int:
     """Backward partition blocks G for M rows of N: min(M, T) with T = 256,
-    or ceil(2^22 / N) for rows longer than 16384 (the long-row tier's tiles),
+    or ceil(2^22 / N) for rows longer than 32768 (the long-row tier's tiles),
     more when a block would own over 64 rows (the library's rule, restated)."""
-    target = 256 if N <= 16384 else -(-(1 << 22) // N)
+    target = 256 if N <= 32768 else -(-(1 << 22) // N)
     return max(min(M, target), -(-M // 64))
 
 

@@ -246,7 +246,7 @@ void run_abi() {
   for (int64_t M : {1, 3, 255, 256, 257, 16384, 16385, 131072})
     for (int64_t N : {1, 7, 8192, 8193, 100000}) {
       const size_t ws = rmsnorm_bwd_workspace_size(M, N), lws = layernorm_bwd_workspace_size(M, N);
-      const int64_t target = N > 16384 ? ((int64_t(1) << 22) + N - 1) / N : 256;
+      const int64_t target = N > 32768 ? ((int64_t(1) << 22) + N - 1) / N : 256;
       const int64_t by_rows = (M + 63) / 64;
       const int64_t blocks = (M < target ? M : target) > by_rows ? (M < target ? M : target) : by_rows;
       CHECK(ws >= static_cast<size_t>(blocks * N * 4));

@@ -129,11 +129,12 @@ def test_workspace_size():
     assert R.rmsnorm_bwd_workspace_size(1000, 10000) == 256 * 10000 * 4 + 16128
     assert R.rmsnorm_bwd_workspace_size(3, 8193) == 98_560 + 256   # 98,316 -> 98,560
     assert R.rmsnorm_bwd_workspace_size(3, 8192) == 98_304         # no records at 8192
-    # Rows longer than 16384 (always the two-pass tier, column tiles x G
+    # Rows longer than 32768 (always the two-pass tier, column tiles x G
     # workgroups): G = max(min(M, ceil(2^22 / N)), ceil(M / 64)).
     assert R.rmsnorm_bwd_workspace_size(4096, 16384) == 256 * 16384 * 4 + 4096 * 16
-    assert R.rmsnorm_bwd_workspace_size(4096, 16385) == 256 * 16385 * 4 + 4096 * 16  # 2^22/16385 -> 256
-    assert R.rmsnorm_bwd_workspace_size(2048, 32768) == 128 * 32768 * 4 + 2048 * 16
+    assert R.rmsnorm_bwd_workspace_size(2048, 32768) == 256 * 32768 * 4 + 2048 * 16
+    assert R.rmsnorm_bwd_workspace_size(2048, 32769) == 128 * 32769 * 4 + 2048 * 16
+    assert R.rmsnorm_bwd_workspace_size(2048, 40000) == 105 * 40000 * 4 + 2048 * 16
     assert R.rmsnorm_bwd_workspace_size(512, 131072) == 32 * 131072 * 4 + 512 * 16
     assert R.rmsnorm_bwd_workspace_size(64, 1 << 20) == 4 * (1 << 20) * 4 + 1024
     assert R.rmsnorm_bwd_workspace_size(3, 1 << 21) == 2 * (1 << 21) * 4 + 256

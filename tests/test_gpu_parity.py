@@ -745,7 +745,8 @@ def run_ln_bwd(M, N, xdt, gdt, seed=31, misalign=0, alias=None, gpu_stats=False,
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
-@pytest.mark.parametrize("N", [1, 7, 8, 64, 1000, 2047, 4096, 5000, 8192, 8193, 16384, 32768])
+@pytest.mark.parametrize("N", [1, 7, 8, 64, 1000, 2047, 4096, 5000, 8192, 8193, 12288, 16384,
+                               32768])
 def test_layernorm_bwd_sweep(N, pair):
     run_ln_bwd(3, N, *pair, seed=2100 + N, dbeta=(N % 2 == 0))
     run_ln_bwd(300, N, *pair, seed=2200 + N)
@@ -810,10 +811,12 @@ def run_bwd(M, N, xdt, gdt, seed=13, misalign=0, alias=None, gpu_rstd=False, eps
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
-@pytest.mark.parametrize("N", [1, 7, 8, 64, 1000, 2047, 4096, 5000, 8192, 8193, 16384, 16392,
-                               32768, 40000])
+@pytest.mark.parametrize("N", [1, 7, 8, 64, 1000, 2047, 4096, 5000, 8192, 8193, 8196, 12288,
+                               16384, 16392, 24576, 24584, 32768, 40000])
 def test_bwd_sweep(N, pair):
-    # N > 16384 (bf16/fp16) or > 8192 (fp32) takes the two-pass long-row tier.
+    # One pass up to 4096 16-byte units (1024 lanes of two, three with
+    # prefetch, or four without: 32768 16-bit / 16384 fp32 elements), the
+    # two-pass long-row tier beyond.
     run_bwd(3, N, *pair, seed=400 + N)
     run_bwd(70, N, *pair, seed=500 + N)
 
@@ -912,7 +915,8 @@ def run_fused_bwd(M, N, xdt, gdt, seed=17, misalign=0, alias=None, with_dres=Tru
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
-@pytest.mark.parametrize("N", [1, 7, 64, 1000, 4096, 5000, 8192, 8193, 16384, 32768])
+@pytest.mark.parametrize("N", [1, 7, 64, 1000, 4096, 5000, 8192, 8193, 12288, 16384, 20000, 24576,
+                               32768])
 def test_fused_bwd_sweep(N, pair):
     run_fused_bwd(3, N, *pair, seed=700 + N)
     run_fused_bwd(300, N, *pair, seed=800 + N)
