@@ -229,6 +229,30 @@ hipError_t fwd_typed(const FwdCall& c) {
       if (units > 2048 && units <= 3072) return run_fwd_pp<T, G, 1024, 3, 1024, FUSED, OUT, LN>(a, s);
       if (units > 3072 && units <= 4096) return run_fwd_pp<T, G, 1024, 4, 1024, FUSED, OUT, LN>(a, s);
     }
+  } else if constexpr (T::kSize == 2) {
+    // The other 16-bit outputs of rows of 1537..4096 units, where measured
+    // faster than the LDS-row kernel (bf16, 2048 x 16384 / 2048 x 24576 /
+    // 1024 x 32768, alternating in one process): the fused add with 1024
+    // lanes of four units (32768: 48.7-49.3 us vs 50.8-50.9; three units
+    // gained 1% at 24576 and lost 3.5% at 16384, so shorter rows stay);
+    // LayerNorm with one 512-lane group of four units per block or 1024
+    // lanes of three (26.6 vs 29.2 us, 38.7-39.1 vs 44.9-46.2; four units
+    // spill); fp8 (18.7 vs 25.7 us, 31.3 vs 46.1-46.7; four units of 1024
+    // lanes spill) and MX outputs (MXFP4 17.3-17.5 vs 21.6, 28.1-28.3 vs
+    // 37.9-38.7, 22.0-22.2 vs 25.7-25.9) with the same shapes, MX also with
+    // 1024 lanes of four. Not the fused add into fp8 / MX.
+    if (vec) {
+      const int64_t units = c.N / 8;
+      if constexpr (FUSED && OUT == kOutAct) {
+        if (units > 3072 && units <= 4096) return run_fwd_pp<T, G, 1024, 4, 1024, FUSED, OUT, LN>(a, s);
+      } else if constexpr (!FUSED) {
+        if (units > 1536 && units <= 2048) return run_fwd_pp<T, G, 512, 4, 512, FUSED, OUT, LN>(a, s);
+        if (units > 2048 && units <= 3072) return run_fwd_pp<T, G, 1024, 3, 1024, FUSED, OUT, LN>(a, s);
+        if constexpr (kIsMx<OUT>) {
+          if (units > 3072 && units <= 4096) return run_fwd_pp<T, G, 1024, 4, 1024, FUSED, OUT, LN>(a, s);
+        }
+      }
+    }
   }
   const int64_t row_bytes = c.N * T::kSize;
   const bool cache = row_bytes <= lds_row_budget();
