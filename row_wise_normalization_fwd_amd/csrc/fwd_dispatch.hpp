@@ -7,10 +7,14 @@
 // 16-byte units per operand (measured best at 4096 x 8192 bf16 among 1, 2, 4
 // and 8 units per lane, with or without a prefetching persistent loop), and
 // rows of up to 1024 units use up to 512 lanes; longer register rows (fp32,
-// N <= 8192) use 4 units on 512 lanes. When that leaves over a third of the
-// lanes idle, half the lanes with 3 units each is used instead (at 32768 x
-// 5000 fp16, 625 units: 256 x 3 measured 7% faster than 512 x 2). Short rows pack BLOCK / TPR rows per
-// block. Rows that are not 16-byte aligned use 1-element units (up to 8 per
+// N <= 8192) use 4 units on 512 lanes. Whenever the row fits half the lanes
+// with 3 units each, that is used instead, leaving fewer lanes idle (at
+// 32768 x 5000 fp16, 625 units: 256 x 3 measured 7% faster than 512 x 2;
+// bf16 16384 x 5632 61.1-61.4 us vs 77.4-78.1, 16384 x 6144 66.4-67.1 vs
+// 77.9-78.7, 32768 x 2816 +5.5%, 65536 x 1408 +6%, 1536 +2.6%, fp32 2816
+// +1.4%, against 2 units on the full lanes; LayerNorm, fp8 and MX outputs
+// 10-40% at 2816, 5632 and 6144 bf16; not the fused add, see below). Short
+// rows pack BLOCK / TPR rows per block. Rows that are not 16-byte aligned use 1-element units (up to 8 per
 // lane). Non-fused 16-bit rows of 769 to 1024 units (N in (6144, 8192]) use
 // the persistent fwd_pp_kernel instead (4096 x 8192 bf16: 22.0-22.6 us vs
 // 23.7-24.0 us; it did not help the fused add or 625-unit rows), and so do
@@ -181,7 +185,11 @@ hipError_t fwd_typed(const FwdCall& c) {
       constexpr int64_t kMinTpr = kIsMx<OUT> ? 32 / E : 1;
       int64_t tpr2 = next_pow2(ceil_div(units, 2));
       if (tpr2 < kMinTpr) tpr2 = kMinTpr;
-      if (tpr2 / 2 >= kMinTpr && tpr2 >= 8 && 3 * units < 4 * tpr2 && units <= 3 * (tpr2 / 2)) {
+      // Three units on half the lanes whenever the row fits them; the fused
+      // add only where two units would idle over a third of the lanes (three
+      // measured 1-4.5% slower for it at 2816, 5632 and 6144 bf16).
+      const bool three = units <= 3 * (tpr2 / 2) && (!FUSED || 3 * units < 4 * tpr2);
+      if (tpr2 / 2 >= kMinTpr && tpr2 >= 8 && three) {
         switch (tpr2 / 2) {  // 3 units on half the lanes
           case 4: return run_fwd_reg<T, G, true, 4, 3, 256, FUSED, OUT, LN>(a, s);
           case 8: return run_fwd_reg<T, G, true, 8, 3, 256, FUSED, OUT, LN>(a, s);

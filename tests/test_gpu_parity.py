@@ -19,7 +19,10 @@ pytestmark = pytest.mark.gpu
 
 PAIRS = [(O.F32, O.F32), (O.F16, O.F16), (O.F16, O.F32), (O.BF16, O.BF16), (O.BF16, O.F32)]
 PAIR_IDS = ["f32", "f16", "f16_gf32", "bf16", "bf16_gf32"]
-N_SWEEP = [1, 7, 8, 63, 64, 1000, 1024, 2047, 2048, 4096, 4999, 5000, 5001, 6152, 7000, 8191, 8192, 8193,
+# 96 ... 6144: rows that fit half the lanes with three units each (every
+# group size from 8 to 512 lanes at 16-bit).
+N_SWEEP = [1, 7, 8, 63, 64, 96, 192, 384, 768, 1000, 1024, 1536, 2047, 2048, 3072, 4096, 4999, 5000,
+           5001, 5632, 6144, 6152, 7000, 8191, 8192, 8193,
            8196, 12288, 12296, 16384, 20000, 24576, 28000, 32760, 32768]
 N_LDS = {O.F32: 20000, O.F16: 40000, O.BF16: 40000}      # 80 KB rows: LDS-cached, 1024 threads
 N_REREAD = {O.F32: 45000, O.F16: 90000, O.BF16: 90000}   # 180 KB rows: beyond 160 KiB of LDS
@@ -382,8 +385,8 @@ def run_quant(M, N, xdt, gdt, mode, seed=19, fused=False, eps=1e-5, misalign=0, 
 
 @pytest.mark.parametrize("mode", [QT, QR], ids=["tensor", "row"])
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
-@pytest.mark.parametrize("N", [1, 7, 64, 1000, 2048, 4096, 5000, 6152, 8191, 8192, 8193, 12296,
-                               16384, 20000, 24576])
+@pytest.mark.parametrize("N", [1, 7, 64, 768, 1000, 1536, 2048, 3072, 4096, 5000, 6144, 6152, 8191,
+                               8192, 8193, 12296, 16384, 20000, 24576])
 def test_quant_sweep(N, pair, mode):
     run_quant(5, N, *pair, mode, seed=1100 + N, want_rstd=(N % 2 == 0))
     run_quant(300, N, *pair, mode, seed=1200 + N, fused=True, want_rstd=(N % 2 == 1))
@@ -519,8 +522,8 @@ def run_mx(M, N, xdt, gdt, elem, seed=37, fused=False, want_rstd=False, q_off=0,
 
 @pytest.mark.parametrize("elem", [O.E4M3, O.E2M1], ids=["mxfp8", "mxfp4"])
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
-@pytest.mark.parametrize("N", [32, 64, 96, 1024, 4096, 5024, 8192, 8224, 12320, 16384, 20000,
-                               24576, 28000, 32768])
+@pytest.mark.parametrize("N", [32, 64, 96, 768, 1024, 1536, 3072, 4096, 5024, 6144, 8192, 8224,
+                               12320, 16384, 20000, 24576, 28000, 32768])
 def test_mx_sweep(N, pair, elem):
     run_mx(5, N, *pair, elem, seed=2500 + N, want_rstd=True)
     run_mx(300, N, *pair, elem, seed=2600 + N, fused=True)
@@ -698,8 +701,8 @@ def run_ln(M, N, xdt, gdt, seed=29, eps=1e-5, with_beta=True, stats=True, misali
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
-@pytest.mark.parametrize("N", [1, 7, 8, 64, 1000, 2048, 4096, 5000, 6152, 8191, 8192, 8193, 12296,
-                               16384, 20000, 24576])
+@pytest.mark.parametrize("N", [1, 7, 8, 64, 384, 1000, 1536, 2048, 3072, 4096, 5000, 6144, 6152,
+                               8191, 8192, 8193, 12296, 16384, 20000, 24576])
 def test_layernorm_sweep(N, pair):
     run_ln(5, N, *pair, seed=1800 + N, with_beta=(N % 2 == 0), stats=(N % 3 != 0))
     run_ln(300, N, *pair, seed=1900 + N)
