@@ -221,6 +221,27 @@ hipError_t fwd_typed(const FwdCall& c) {
       return run_fwd_reg<T, G, false, 1024, 8, 1024, FUSED, OUT, LN>(a, s);
     }
   }
+  if constexpr (T::kSize == 2) {
+    // 16-bit rows of 1025..1536 units (N in (8192, 12288]): the fused add on
+    // 512 lanes of three units (bf16 8192 x 10240 108.0 vs 112.5-112.9 us
+    // on the LDS-row kernel, 4096 x 12288 66.9 vs 68.9); LayerNorm, fp8 and
+    // MX outputs on the persistent kernel, one 512-lane group of three units
+    // per block (LayerNorm 10240 59.1 vs 73.7-74.3 us, 8200 49.8-50.2 vs
+    // 64.2-67.2; per-row fp8 10240 49.1-49.4 vs 61.3-62.8, 12288 28.0-28.4
+    // vs 37.0-37.3; MXFP4 10240 42.8-43.9 vs 55.3-56.6, 8224 38.8-38.9 vs
+    // 50.9-51.5). The plain forward stays on the LDS-row kernel, which both
+    // of those shapes lost to (3-9% at 8200 and 10240).
+    if (vec) {
+      const int64_t units = c.N / 8;
+      if (units > 1024 && units <= 1536) {
+        if constexpr (FUSED && OUT == kOutAct) {
+          return run_fwd_reg<T, G, true, 512, 3, 512, FUSED, OUT, LN>(a, s);
+        } else if constexpr (!FUSED && (LN || OUT != kOutAct)) {
+          return run_fwd_pp<T, G, 512, 3, 512, FUSED, OUT, LN>(a, s);
+        }
+      }
+    }
+  }
   if constexpr (!FUSED && OUT == kOutAct && !LN) {
     // Rows of 1537..4096 16-byte units: the persistent kernel with 512 or
     // 1024 lanes per row and three or four units per lane, chosen to leave

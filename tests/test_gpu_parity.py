@@ -117,6 +117,9 @@ def test_other_outputs_persistent_long_rows(pair):
     1024 x 3), fp8 (512 x 4, 1024 x 3) and MX outputs (also 1024 x 4) of
     long rows on the persistent kernel, over several loop iterations."""
     run_fused(1030, 32768, *pair, seed=45, want_rstd=True)
+    run_ln(1100, 12288, *pair, seed=52)
+    run_quant(1100, 10240, *pair, QR, seed=53)
+    run_mx(1100, 10240, *pair, O.E2M1, seed=54)
     run_ln(1100, 16384, *pair, seed=46)
     run_ln(1030, 20000, *pair, seed=47, with_beta=False)
     run_quant(1100, 16384, *pair, QR, seed=48, want_rstd=True)
@@ -327,8 +330,8 @@ def run_fused(M, N, xdt, gdt, eps=1e-5, seed=11, want_rstd=False, misalign=0, x_
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
-@pytest.mark.parametrize("N", [1, 7, 64, 1000, 2048, 4096, 5000, 8191, 8192, 8193, 16384, 24576,
-                               28000, 32768])
+@pytest.mark.parametrize("N", [1, 7, 64, 1000, 2048, 4096, 5000, 8191, 8192, 8193, 8200, 10240,
+                               12288, 16384, 24576, 28000, 32768])
 def test_fused_sweep(N, pair):
     run_fused(5, N, *pair, seed=300 + N, want_rstd=(N % 2 == 0))
 
@@ -386,7 +389,7 @@ def run_quant(M, N, xdt, gdt, mode, seed=19, fused=False, eps=1e-5, misalign=0, 
 @pytest.mark.parametrize("mode", [QT, QR], ids=["tensor", "row"])
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
 @pytest.mark.parametrize("N", [1, 7, 64, 768, 1000, 1536, 2048, 3072, 4096, 5000, 6144, 6152, 8191,
-                               8192, 8193, 12296, 16384, 20000, 24576])
+                               8192, 8193, 8200, 10240, 12288, 12296, 16384, 20000, 24576])
 def test_quant_sweep(N, pair, mode):
     run_quant(5, N, *pair, mode, seed=1100 + N, want_rstd=(N % 2 == 0))
     run_quant(300, N, *pair, mode, seed=1200 + N, fused=True, want_rstd=(N % 2 == 1))
@@ -523,7 +526,7 @@ def run_mx(M, N, xdt, gdt, elem, seed=37, fused=False, want_rstd=False, q_off=0,
 @pytest.mark.parametrize("elem", [O.E4M3, O.E2M1], ids=["mxfp8", "mxfp4"])
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
 @pytest.mark.parametrize("N", [32, 64, 96, 768, 1024, 1536, 3072, 4096, 5024, 6144, 8192, 8224,
-                               12320, 16384, 20000, 24576, 28000, 32768])
+                               10240, 12288, 12320, 16384, 20000, 24576, 28000, 32768])
 def test_mx_sweep(N, pair, elem):
     run_mx(5, N, *pair, elem, seed=2500 + N, want_rstd=True)
     run_mx(300, N, *pair, elem, seed=2600 + N, fused=True)
@@ -702,7 +705,7 @@ def run_ln(M, N, xdt, gdt, seed=29, eps=1e-5, with_beta=True, stats=True, misali
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
 @pytest.mark.parametrize("N", [1, 7, 8, 64, 384, 1000, 1536, 2048, 3072, 4096, 5000, 6144, 6152,
-                               8191, 8192, 8193, 12296, 16384, 20000, 24576])
+                               8191, 8192, 8193, 8200, 10240, 12288, 12296, 16384, 20000, 24576])
 def test_layernorm_sweep(N, pair):
     run_ln(5, N, *pair, seed=1800 + N, with_beta=(N % 2 == 0), stats=(N % 3 != 0))
     run_ln(300, N, *pair, seed=1900 + N)
