@@ -54,10 +54,15 @@ template <class T, class G, int TPR, int UPT, int BLOCK, bool FUSED, int OUT, bo
 hipError_t run_fwd_pp(const FwdArgs<T, G>& a, hipStream_t s) {
   // Two blocks per CU's worth of grid: at 4096 x 8192 bf16 every block then
   // runs exactly two iterations (one prefetch), measured best among 256-1024
-  // blocks.
+  // blocks. 1024-thread blocks (one resident per CU) with at most three row
+  // groups per CU take one block per CU instead, so all of them run at once
+  // and each still prefetches (bf16 x 8192: 1536 rows 10.0 vs 12.2 us, 2048
+  // 11.0 vs 14.1, 3072 17.2 vs 19.3; 1024 x 16384 10.9 vs 13.4; 512 x 32768
+  // 11.8 vs 13.3; from 3584 rows of 8192 two per CU are ahead again).
   constexpr int RG = BLOCK / TPR;
-  int64_t blocks = 2 * device_cus();
   const int64_t groups = ceil_div(a.M, RG);
+  const int64_t cus = device_cus();
+  int64_t blocks = BLOCK == 1024 && groups <= 3 * cus ? cus : 2 * cus;
   if (blocks > groups) blocks = groups;
   // At most kMaxRowIters iterations per row group (the rare-row mask).
   if (blocks < ceil_div(groups, kMaxRowIters)) blocks = ceil_div(groups, kMaxRowIters);
@@ -177,7 +182,15 @@ hipError_t fwd_typed(const FwdCall& c) {
         // LayerNorm keeps beta and the mean live too and spills with four
         // row groups, so it also takes the one-group shape.
         if (units > 768) {
-          if constexpr (OUT == kOutAct && !LN) return run_fwd_pp<T, G, 256, 4, 1024, FUSED, OUT, LN>(a, s);
+          if constexpr (OUT == kOutAct && !LN) {
+            // Beyond 16 rows per CU the persistent grid needs several rounds
+            // of blocks, and one 256-lane row per block of the register
+            // kernel is faster (bf16 x 8192: 6144 rows 34.6 vs 35.6 us,
+            // 12288 65.8 vs 68.6, 16384 86.6-87.4 vs 91.9-92.6; x 7168, 12288
+            // rows 58.6 vs 64.2), while at 4096 rows it is 7-8% slower.
+            if (a.M > 16 * device_cus()) return run_fwd_reg<T, G, true, 256, 4, 256, FUSED, OUT, LN>(a, s);
+            return run_fwd_pp<T, G, 256, 4, 1024, FUSED, OUT, LN>(a, s);
+          }
           else return run_fwd_pp<T, G, 256, 4, 256, FUSED, OUT, LN>(a, s);
         }
       }

@@ -122,11 +122,12 @@ def domain_cases(xdt, kind):
 # Shapes per kernel family (16-bit units): register rows, several rows per
 # block (64, 1000), two 128-lane groups per block, whose rare rows are each
 # redone by one wave (2048 16-bit / 1024 fp32), one 512-lane group (4096),
-# the persistent kernel over several iterations per row group (8192; 16384
-# and 32768 16-bit / fp32 16384 with 512- and 1024-lane groups), and
+# the persistent kernel over several iterations per row group (8192 up to
+# 4096 rows, beyond that one 256-lane row per block; 16384 and 32768 16-bit
+# / fp32 16384 with 512- and 1024-lane groups), and
 # LDS-cached and re-read long rows.
 FWD_SHAPES = [(37, 64), (20000, 64), (37, 1000), (45, 1024), (45, 2048), (45, 4096), (29, 5000),
-              (5000, 8192), (1030, 16384), (520, 32768), (3, 20000), (3, 45000)]
+              (2600, 8192), (5000, 8192), (1030, 16384), (520, 32768), (3, 20000), (3, 45000)]
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
@@ -140,26 +141,27 @@ def test_fwd_domain(kind, shape, pair):
 
 def test_fwd_rare_rows_outnumber_group_waves():
     """Four rows in five overflow the fp32 sum of squares, over six loop
-    iterations per row group of the persistent 8192-wide kernel (four
-    256-lane groups per block): a group's waves take its rare rows in turn,
+    iterations per row group of the persistent kernel at 16384 elements (two
+    512-lane groups per block): a group's waves take its rare rows in turn,
     so most groups have more rare rows than waves."""
-    run_domain_fwd(12288, 8192, O.BF16, O.BF16, [1.0, 1e20, 1e30, 1e37, 1e30], 1e-5, seed=77)
+    run_domain_fwd(6144, 16384, O.BF16, O.BF16, [1.0, 1e20, 1e30, 1e37, 1e30], 1e-5, seed=77)
 
 
 def test_fwd_rare_rows_in_late_iterations():
-    """Rare rows in loop iterations 0 to 39 of the persistent 8192-wide kernel:
-    81920 rows give every row group 40 iterations (512 blocks of four groups
-    on 256 CUs: row r is in iteration r // 2048), so the rare-row mask's bit
-    31 and its high word are used. The batch is 1024 seeded rows repeated;
-    the rare rows and a sample of the others are checked against the oracle,
-    and every other row bit for bit against a batch without rare rows."""
-    M, N, dt = 81920, 8192, O.BF16
+    """Rare rows in loop iterations 0 to 39 of the persistent kernel at 16384
+    elements: 40960 rows give every row group 40 iterations (512 blocks of
+    two 512-lane groups on 256 CUs: row r is in iteration r // 1024), so the
+    rare-row mask's bit 31 and its high word are used. The batch is 1024
+    seeded rows repeated; the rare rows and a sample of the others are
+    checked against the oracle, and every other row bit for bit against a
+    batch without rare rows."""
+    M, N, dt = 40960, 16384, O.BF16
     _log(f"late-iteration rare rows M={M} N={N}")
     base = G.normal(101, G.STREAM_X, 1024, N, dt)
     g = G.uniform(101, G.STREAM_GAMMA, N, 0.5, 1.5, dt)
     gt = _put(g, dt)
-    rare = np.array(sorted({2048 * t + k for t in (0, 1, 30, 31, 32, 33, 39)
-                            for k in (0, 1, 517, 1023, 1500, 2047)}))
+    rare = np.array(sorted({1024 * t + k for t in (0, 1, 30, 31, 32, 33, 39)
+                            for k in (0, 1, 517, 700, 1023)}))
     scale = np.where(np.arange(rare.size) % 2 == 0, 1e30, 1e37)[:, None]
     xr = O.round_to(O.decode(base[rare % 1024], dt) * scale, dt)
 

@@ -98,14 +98,16 @@ def _period_sum(fn, M):
 
 # ------------------------------------------------------------------ forward
 
-@pytest.mark.parametrize("kind", ["persistent", "register", "long"])
+@pytest.mark.parametrize("kind", ["wide", "register", "persistent"])
 def test_maxsize_forward(kind):
-    """bf16 rows over the three forward kernels: 8192 (persistent), 4096 with
-    an fp32 gamma and the fused residual add (register), 16384 (long rows)."""
+    """bf16 rows over the forward kernels at over 2^32 bytes: 8192 (this many
+    rows take the register kernel, one 256-lane row of four units per
+    block), 4096 with an fp32 gamma and the fused residual add (register,
+    two units), 16384 (the persistent kernel, 512-lane row groups)."""
     xdt = O.BF16
-    N, gdt, fused = {"persistent": (8192, O.BF16, False), "register": (4096, O.F32, True),
-                     "long": (16384, O.BF16, False)}[kind]
-    M = _rows_for(N, 2, 7919 if kind != "long" else 613)
+    N, gdt, fused = {"wide": (8192, O.BF16, False), "register": (4096, O.F32, True),
+                     "persistent": (16384, O.BF16, False)}[kind]
+    M = _rows_for(N, 2, 7919 if kind != "persistent" else 613)
     _log(f"maxsize fwd {kind} M={M} N={N} fused={fused}")
     x = G.normal(41, G.STREAM_X, P, N, xdt)
     r = G.normal(41, G.STREAM_R, P, N, xdt) if fused else None
