@@ -194,6 +194,36 @@ hipError_t fwd_typed(const FwdCall& c) {
           else return run_fwd_pp<T, G, 256, 4, 256, FUSED, OUT, LN>(a, s);
         }
       }
+      if constexpr (T::kSize == 2 && !FUSED && (LN || OUT != kOutAct)) {
+        // LayerNorm, fp8 and MX outputs of shorter rows (64..256 lanes of the
+        // register kernel's shape): the persistent kernel, one row group per
+        // 256-thread block (or several for narrower groups), measured against the register kernel at 64 MiB
+        // of bf16 per operand, alternating in one process: LayerNorm 3-30%
+        // faster from 1024 to 6144 elements (2560: 26.7 vs 33.4 us, 5120:
+        // 25.7 vs 33.4), so it takes every such shape; MX 10-18% faster on
+        // the three-unit shapes (1536, 2560, 3072, 5120, 6144) but 3-4%
+        // slower on the two-unit ones, fp8 2-6% faster on three units and
+        // 7-11% slower on two, so those take only the three-unit shapes.
+        const int64_t t2 = next_pow2(ceil_div(units, 2));
+        const bool th = t2 >= 8 && units <= 3 * (t2 / 2);
+        const int64_t tp = th ? t2 / 2 : t2;
+        if (tp >= 64 && tp <= 256 && (LN || th)) {
+          if (th) {
+            switch (tp) {
+              case 64: return run_fwd_pp<T, G, 64, 3, 256, FUSED, OUT, LN>(a, s);
+              case 128: return run_fwd_pp<T, G, 128, 3, 256, FUSED, OUT, LN>(a, s);
+              default: return run_fwd_pp<T, G, 256, 3, 256, FUSED, OUT, LN>(a, s);
+            }
+          }
+          if constexpr (LN) {
+            switch (tp) {
+              case 64: return run_fwd_pp<T, G, 64, 2, 256, FUSED, OUT, LN>(a, s);
+              case 128: return run_fwd_pp<T, G, 128, 2, 256, FUSED, OUT, LN>(a, s);
+              default: return run_fwd_pp<T, G, 256, 2, 256, FUSED, OUT, LN>(a, s);
+            }
+          }
+        }
+      }
       // MX blocks span 32 / E lanes of one unit slot: at least that many lanes.
       constexpr int64_t kMinTpr = kIsMx<OUT> ? 32 / E : 1;
       int64_t tpr2 = next_pow2(ceil_div(units, 2));
