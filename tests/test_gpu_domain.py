@@ -446,8 +446,8 @@ def run_domain_bwd(M, N, xdt, gdt, xscales, dyscales, seed, res=False, gpu_rstd=
 # wide rows (1024 lanes of three units with prefetch, four without: 20000,
 # 24584, 32768 16-bit; the fused add of 16-bit rows takes three units only),
 # and the long-row tier (fp32 beyond 16384, 16-bit beyond 32768).
-BWD_SHAPES = [(37, 64), (45, 1024), (700, 4096), (700, 8192), (9, 12288), (5, 20000),
-              (300, 24584), (300, 32768), (130, 40000)]
+BWD_SHAPES = [(37, 64), (45, 1024), (700, 1536), (500, 3072), (700, 4096), (700, 8192), (9, 12288),
+              (5, 20000), (300, 24584), (300, 32768), (130, 40000)]
 
 
 @pytest.mark.parametrize("pair", [(O.F32, O.F32), (O.BF16, O.BF16), (O.BF16, O.F32)],

@@ -836,8 +836,8 @@ def run_bwd(M, N, xdt, gdt, seed=13, misalign=0, alias=None, gpu_rstd=False, eps
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
-@pytest.mark.parametrize("N", [1, 7, 8, 64, 1000, 2047, 4096, 5000, 8192, 8193, 8196, 12288,
-                               16384, 16392, 24576, 24584, 32768, 40000])
+@pytest.mark.parametrize("N", [1, 7, 8, 64, 768, 1000, 1536, 2047, 2560, 3072, 4096, 5000, 8192,
+                               8193, 8196, 12288, 16384, 16392, 24576, 24584, 32768, 40000])
 def test_bwd_sweep(N, pair):
     # One pass up to 4096 16-byte units (1024 lanes of two, three with
     # prefetch, or four without: 32768 16-bit / 16384 fp32 elements), the
