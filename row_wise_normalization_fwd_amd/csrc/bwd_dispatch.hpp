@@ -63,12 +63,14 @@ hipError_t stage1_typed(const BwdArgs<T, G>& a, bool vec, int64_t blocks, hipStr
       // 1024 lanes of three units with next-row prefetch, or of four units
       // without it (two register sets of four would not fit 128 VGPRs), gamma
       // read from LDS. The 16-bit fused add (dresidual is a third operand)
-      // fits only three units without prefetch; the 16-bit LayerNorm kernel
-      // spills even then and takes the two-pass tier.
+      // fits only three units without prefetch. The 16-bit LayerNorm kernel
+      // spills 16-17 VGPRs even then, yet runs 14-21% faster than the
+      // two-pass tier (bf16 2048 x 20480 78.5 vs 90.3 us, 2048 x 24576 85.2
+      // vs 99.4), so it takes three units too; with four it spills far more.
       if constexpr (T::kSize == 4 || (!RES && !LN)) {
         if (units <= 3072) return run_stage1<T, G, RES, LN, true, 1024, 3, 1024, true>(a, blocks, s);
         if (units <= 4096) return run_stage1<T, G, RES, LN, true, 1024, 4, 1024, false>(a, blocks, s);
-      } else if constexpr (RES) {
+      } else {
         if (units <= 3072) return run_stage1<T, G, RES, LN, true, 1024, 3, 1024, false>(a, blocks, s);
       }
       return hipErrorNotSupported;
