@@ -194,8 +194,8 @@ int rmsnorm_qk_fwd(void* q, void* k, const void* q_gamma, const void* k_gamma,
  * take the two-pass tier, which runs column tiles x G workgroups), and for
  * N > 8192 a 16-byte record per row (rows longer than the one-pass kernel
  * holds keep their row dots there; rows of up to 4096 16-byte units --
- * 32768 16-bit / 16384 fp32 elements, 24576 for the 16-bit fused add and
- * LayerNorm -- stay one-pass and leave it unused). Pure host
+ * 32768 16-bit / 16384 fp32 elements, 24576 for 16-bit LayerNorm -- stay
+ * one-pass and leave it unused). Pure host
  * function; returns 0 for M <= 0, N <= 0 or N > RMSN_MAX_N. */
 size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N);
 

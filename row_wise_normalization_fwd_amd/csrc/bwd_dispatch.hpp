@@ -66,12 +66,18 @@ hipError_t stage1_typed(const BwdArgs<T, G>& a, bool vec, int64_t blocks, hipStr
       // fits only three units without prefetch. The 16-bit LayerNorm kernel
       // spills 16-17 VGPRs even then, yet runs 14-21% faster than the
       // two-pass tier (bf16 2048 x 20480 78.5 vs 90.3 us, 2048 x 24576 85.2
-      // vs 99.4), so it takes three units too; with four it spills far more.
+      // vs 99.4), so it takes three units too; with four it spills 84-93 and
+      // is 35% slower than that tier. The fused add with four units spills
+      // 12-14 and is 27-32% faster than it (2048 x 28672 101 vs 128 us,
+      // 2048 x 32768 110 vs 145.6).
       if constexpr (T::kSize == 4 || (!RES && !LN)) {
         if (units <= 3072) return run_stage1<T, G, RES, LN, true, 1024, 3, 1024, true>(a, blocks, s);
         if (units <= 4096) return run_stage1<T, G, RES, LN, true, 1024, 4, 1024, false>(a, blocks, s);
       } else {
         if (units <= 3072) return run_stage1<T, G, RES, LN, true, 1024, 3, 1024, false>(a, blocks, s);
+        if constexpr (RES) {
+          if (units <= 4096) return run_stage1<T, G, RES, LN, true, 1024, 4, 1024, false>(a, blocks, s);
+        }
       }
       return hipErrorNotSupported;
     }
