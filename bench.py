@@ -1124,6 +1124,47 @@ def reduce_profiles(prof: str) -> int:
     return 0
 
 
+# Widths and operations of the --scan mode (bf16 activations and gamma).
+SCAN_WIDTHS = [256, 512, 768, 1024, 1536, 2048, 2560, 3072, 3584, 4096, 5120, 6144, 7168, 8192,
+               10240, 12288, 14336, 16384, 20480, 24576, 28672, 32768]
+SCAN_OPS = {"fwd": {"kind": "fwd"}, "fused_add": {"kind": "fused_add"}, "ln": {"kind": "ln"},
+            "fp8row": {"kind": "quant", "quant_mode": 2}, "mxfp4": {"kind": "quant", "quant_mode": 4},
+            "bwd": {"kind": "bwd"}, "fused_add_bwd": {"kind": "fused_add_bwd"},
+            "ln_bwd": {"kind": "ln_bwd"}}
+
+
+def scan(mib: int, rotate_bytes: float, steps: int, warmup: int, ops=None,
+         widths=None) -> int:
+    """Every operation of SCAN_OPS over SCAN_WIDTHS, bf16, with M = mib MiB /
+    (2 N) rows: one line per (operation, width) as it is timed, then a table
+    of % of the 8 TB/s peak (algorithmic bytes / event-timed step)."""
+    import torch
+
+    import gen as G
+
+    ops = ops or list(SCAN_OPS)
+    widths = widths or SCAN_WIDTHS
+    table = {}
+    for op in ops:
+        extra = SCAN_OPS[op]
+        for n in widths:
+            m = max(1, (mib << 20) // (2 * n))
+            w = G.Workload(f"scan_{op}_m{m}_n{n}", extra["kind"], m, n, G.BF16, G.BF16, 1e-5,
+                           9000 + n, quant_mode=extra.get("quant_mode", 0))
+            run = Runner(w, rotate_bytes, G.make_inputs(w))
+            ms = time_steps(run.step, steps, warmup)
+            pct = w.algorithmic_bytes() / (ms * 1e-3) / 1e9 / (PEAK_GBPS / 100.0)
+            table[(op, n)] = pct
+            print(f"scan {op} M={m} N={n}: {ms * 1e3:.2f} us {pct:.1f}%", flush=True)
+            del run
+            torch.cuda.empty_cache()
+    print("\n| N | " + " | ".join(ops) + " |")
+    print("|---|" + "---|" * len(ops))
+    for n in widths:
+        print(f"| {n} | " + " | ".join(f"{table[(op, n)]:.1f}" for op in ops) + " |")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -1148,6 +1189,12 @@ def main() -> int:
                     help="comma-separated workloads for --collect-profiles (default: all)")
     ap.add_argument("--profile-passes", default="trace,fetch,write,lds,occ,valu",
                     help="comma-separated passes for --collect-profiles")
+    ap.add_argument("--scan", action="store_true",
+                    help="time every operation over a ladder of row widths (bf16, --scan-mib "
+                         "MiB per operand) and print a table of %% of peak, then exit")
+    ap.add_argument("--scan-mib", type=int, default=64)
+    ap.add_argument("--scan-ops", default="", help="comma-separated subset of the scan's operations")
+    ap.add_argument("--scan-widths", default="", help="comma-separated row widths for --scan")
     ap.add_argument("--reduce-profiles", metavar="DIR",
                     help="write profiles/ from the rocprofv3 output under DIR, then exit")
     args = ap.parse_args()
@@ -1181,6 +1228,14 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.scan:
+        ops = [o for o in args.scan_ops.split(",") if o]
+        if any(o not in SCAN_OPS for o in ops):
+            print(f"unknown scan operations: {ops}; choose from {list(SCAN_OPS)}", file=sys.stderr)
+            return 2
+        widths = [int(v) for v in args.scan_widths.split(",") if v]
+        return scan(args.scan_mib, args.rotate_bytes, max(1, args.steps // 20), args.warmup // 10,
+                    ops, widths)
     src_hash = kernel_source_hash()
 
     w = G.WORKLOADS_BY_NAME[args.workload]
