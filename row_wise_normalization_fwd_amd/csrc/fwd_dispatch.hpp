@@ -319,10 +319,11 @@ hipError_t fwd_typed(const FwdCall& c) {
     // gained 1% at 24576 and lost 3.5% at 16384, so shorter rows stay);
     // LayerNorm with one 512-lane group of four units per block or 1024
     // lanes of three (26.6 vs 29.2 us, 38.7-39.1 vs 44.9-46.2; four units
-    // spill); fp8 (18.7 vs 25.7 us, 31.3 vs 46.1-46.7; four units of 1024
-    // lanes spill) and MX outputs (MXFP4 17.3-17.5 vs 21.6, 28.1-28.3 vs
-    // 37.9-38.7, 22.0-22.2 vs 25.7-25.9) with the same shapes, MX also with
-    // 1024 lanes of four. Not the fused add into fp8 / MX.
+    // spill); fp8 (18.7 vs 25.7 us, 31.3 vs 46.1-46.7) and MX outputs (MXFP4
+    // 17.3-17.5 vs 21.6, 28.1-28.3 vs 37.9-38.7, 22.0-22.2 vs 25.7-25.9) with
+    // the same shapes, and both with 1024 lanes of four (per-row fp8 1170 x
+    // 28672 26.3 vs 31.6 us, 1232 x 26624 26.7 vs 30.6; per-tensor 6% faster).
+    // Not the fused add into fp8 / MX.
     if (vec) {
       const int64_t units = c.N / 8;
       if constexpr (FUSED && OUT == kOutAct) {
@@ -330,7 +331,7 @@ hipError_t fwd_typed(const FwdCall& c) {
       } else if constexpr (!FUSED) {
         if (units > 1536 && units <= 2048) return run_fwd_pp<T, G, 512, 4, 512, FUSED, OUT, LN>(a, s);
         if (units > 2048 && units <= 3072) return run_fwd_pp<T, G, 1024, 3, 1024, FUSED, OUT, LN>(a, s);
-        if constexpr (kIsMx<OUT>) {
+        if constexpr (OUT != kOutAct) {
           if (units > 3072 && units <= 4096) return run_fwd_pp<T, G, 1024, 4, 1024, FUSED, OUT, LN>(a, s);
         }
       }

@@ -459,22 +459,35 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
 #pragma unroll
     for (int k = 1; k < UPT; ++k) ss = ss + part[k];
     // fp8 / MX outputs keep x * gamma in registers until the stores (their
-    // one-group, 256-thread blocks leave VGPRs to spare); the others widen
-    // again after the reduction instead of keeping fp32 copies live.
-    constexpr bool kKeep = OUT != kOutAct;
+    // one-group, 256-thread blocks leave VGPRs to spare). fp8 with four units
+    // of 1024 lanes, where the 32 fp32 copies spilled, forms the product again
+    // from the packed words after the reduction (the same multiply on the same
+    // operands, as the other outputs do): 1024 x 32768 bf16 per-row 25.5-26.1
+    // vs 30.2-30.5 us on the LDS-row kernel, per-tensor 21.3-21.6 vs
+    // 22.6-23.0. MX keeps its copies there (recomputing lost 0.3-1.7%).
+    constexpr bool kQuant = OUT != kOutAct;
+    constexpr bool kKeep = kQuant && !(BLOCK == 1024 && UPT >= 4 && !kIsMx<OUT>);
+    auto xg = [&](int k, float (&o)[E]) {
+      float v[E], g[E];
+      U::widen(cx[k], v);
+      widen_gamma(graw[k], g);
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = v[e] * g[e];
+    };
     [[maybe_unused]] float p[kKeep ? UPT : 1][E];
     [[maybe_unused]] float m = 0.0f;
-    if constexpr (kKeep) {
+    if constexpr (kQuant) {
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
-        float v[E], g[E];
-        U::widen(cx[k], v);
-        widen_gamma(graw[k], g);
+        float o[E];
+        xg(k, o);
+        if constexpr (kKeep) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) p[k][e] = v[e] * g[e];
+          for (int e = 0; e < E; ++e) p[k][e] = o[e];
+        }
         if constexpr (OUT == kOutFp8Row) {
 #pragma unroll
-          for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(p[k][e]));
+          for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(o[e]));
         }
       }
     } else if constexpr (!LN) {
@@ -556,8 +569,14 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
         float o[E];
+        if constexpr (kKeep) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = p[k][e] * rs;
+          for (int e = 0; e < E; ++e) o[e] = p[k][e];
+        } else {
+          xg(k, o);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = o[e] * rs;
         const int c = X::code(o);
         const uint32_t off = out_offset(k);
         const uint32_t qoff = off == kBufOutOfRange ? off : off >> kShift;
@@ -580,7 +599,14 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
         const uint32_t off = out_offset(k);
-        __builtin_amdgcn_raw_buffer_store_b64(Fp8Unit<8>::pack(p[k], kq), rsq,
+        float o[E];
+        if constexpr (kKeep) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[e] = p[k][e];
+        } else {
+          xg(k, o);
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(Fp8Unit<8>::pack(o, kq), rsq,
                                               off == kBufOutOfRange ? off : off >> 1, 0, kBufNT);
       }
     }

@@ -389,7 +389,8 @@ def run_quant(M, N, xdt, gdt, mode, seed=19, fused=False, eps=1e-5, misalign=0, 
 @pytest.mark.parametrize("mode", [QT, QR], ids=["tensor", "row"])
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
 @pytest.mark.parametrize("N", [1, 7, 64, 768, 1000, 1536, 2048, 3072, 4096, 5000, 6144, 6152, 8191,
-                               8192, 8193, 8200, 10240, 12288, 12296, 16384, 20000, 24576])
+                               8192, 8193, 8200, 10240, 12288, 12296, 16384, 20000, 24576, 28672,
+                               32768])
 def test_quant_sweep(N, pair, mode):
     run_quant(5, N, *pair, mode, seed=1100 + N, want_rstd=(N % 2 == 0))
     run_quant(300, N, *pair, mode, seed=1200 + N, fused=True, want_rstd=(N % 2 == 1))
