@@ -66,8 +66,13 @@ hipError_t run_fwd_pp(const FwdArgs<T, G>& a, hipStream_t s) {
   if (blocks > groups) blocks = groups;
   // At most kMaxRowIters iterations per row group (the rare-row mask).
   if (blocks < ceil_div(groups, kMaxRowIters)) blocks = ceil_div(groups, kMaxRowIters);
-  fwd_pp_kernel<T, G, TPR, UPT, BLOCK, FUSED, OUT, LN>
-      <<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), 0, s>>>(a);
+  constexpr size_t lds = pp_param_lds_bytes<T, G, TPR, UPT, BLOCK, LN>();
+  constexpr auto kernel = fwd_pp_kernel<T, G, TPR, UPT, BLOCK, FUSED, OUT, LN>;
+  if constexpr (lds > 0) {
+    const hipError_t attr = ensure_dynamic_lds<kernel>(lds);
+    if (attr != hipSuccess) return attr;
+  }
+  kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -323,7 +328,11 @@ hipError_t fwd_typed(const FwdCall& c) {
     // 17.3-17.5 vs 21.6, 28.1-28.3 vs 37.9-38.7, 22.0-22.2 vs 25.7-25.9) with
     // the same shapes, and both with 1024 lanes of four (per-row fp8 1170 x
     // 28672 26.3 vs 31.6 us, 1232 x 26624 26.7 vs 30.6; per-tensor 6% faster).
-    // Not the fused add into fp8 / MX.
+    // LayerNorm with 16-bit gamma takes 1024 lanes of four (gamma and beta in
+    // LDS) when at least 7/8 of the lanes' units hold the row: 1024 x 32768
+    // 28.8-29.3 vs 32.7-33.9 us, 1170 x 28672 29.5-30.1 vs 31.0-31.2, but
+    // 1290 x 26000 (3250 units) 34.7-36.4 vs 33.0-34.7. Not the fused add
+    // into fp8 / MX.
     if (vec) {
       const int64_t units = c.N / 8;
       if constexpr (FUSED && OUT == kOutAct) {
@@ -333,6 +342,8 @@ hipError_t fwd_typed(const FwdCall& c) {
         if (units > 2048 && units <= 3072) return run_fwd_pp<T, G, 1024, 3, 1024, FUSED, OUT, LN>(a, s);
         if constexpr (OUT != kOutAct) {
           if (units > 3072 && units <= 4096) return run_fwd_pp<T, G, 1024, 4, 1024, FUSED, OUT, LN>(a, s);
+        } else if constexpr (LN && G::kSize == 2) {
+          if (units >= 3584 && units <= 4096) return run_fwd_pp<T, G, 1024, 4, 1024, FUSED, OUT, LN>(a, s);
         }
       }
     }

@@ -324,6 +324,20 @@ __global__ __launch_bounds__(BLOCK) void fwd_reg_kernel(FwdArgs<T, G> a) {
 // branches around them and the compiler waits only for the older loads.
 // Row results do not depend on G (each row's arithmetic is the same for any
 // grid), only on TPR and UPT.
+//
+// LayerNorm rows of one 1024-lane group of four units with 16-bit x and
+// gamma keep the packed gamma and beta words in LDS (dynamic, 128 KiB; one
+// such block fits a CU, where its VGPRs allow only one anyway) instead of 32
+// VGPRs, which spilled. Each thread reads back only the slots it wrote (unit
+// lane + k * TPR at slot k * TPR + lane, consecutive lanes on consecutive
+// 16-byte words), so no barrier guards them. Returns the dynamic LDS bytes.
+template <class T, class G, int TPR, int UPT, int BLOCK, bool LN>
+constexpr size_t pp_param_lds_bytes() {
+  return LN && TPR == BLOCK && BLOCK == 1024 && UPT >= 4 && T::kSize == 2 && G::kSize == 2
+             ? static_cast<size_t>(2) * UPT * TPR * 16
+             : 0;
+}
+
 template <class T, class G, int TPR, int UPT, int BLOCK, bool FUSED, int OUT, bool LN = false>
 __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
   using U = Unit<T, true>;
@@ -348,16 +362,26 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
   // Gamma (and LayerNorm's beta) stay packed in registers and are widened
   // where they are used. load_params() issues their loads; see the loop
   // below for where.
-  u32x4 graw[UPT][GW];
-  [[maybe_unused]] u32x4 braw[LN ? UPT : 1][GW];
+  constexpr bool kPL = pp_param_lds_bytes<T, G, TPR, UPT, BLOCK, LN>() > 0;
+  static_assert(!kPL || GW == 1, "one word per unit in LDS");
+  extern __shared__ __align__(16) unsigned char pp_lds[];
+  [[maybe_unused]] u32x4* const plds = reinterpret_cast<u32x4*>(pp_lds);  // [2][UPT][TPR]
+  u32x4 graw[kPL ? 1 : UPT][GW];
+  [[maybe_unused]] u32x4 braw[LN && !kPL ? UPT : 1][GW];
   auto load_params = [&]() {
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const int u = lane + k * TPR;
       const typename G::S* gp = a.gamma + (u < nunits ? u : 0) * E;
 #pragma unroll
-      for (int w = 0; w < GW; ++w)
-        graw[k][w] = *reinterpret_cast<const u32x4*>(gp + w * (16 / G::kSize));
+      for (int w = 0; w < GW; ++w) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(gp + w * (16 / G::kSize));
+        if constexpr (kPL) {
+          plds[k * TPR + lane] = v;
+        } else {
+          graw[k][w] = v;
+        }
+      }
     }
     if constexpr (LN) {
 #pragma unroll
@@ -365,22 +389,43 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
         const int u = lane + k * TPR;
 #pragma unroll
         for (int w = 0; w < GW; ++w) {
+          u32x4 v = (u32x4){0u, 0u, 0u, 0u};
           if (a.beta != nullptr) {
             const typename G::S* bp = a.beta + (u < nunits ? u : 0) * E;
-            braw[k][w] = *reinterpret_cast<const u32x4*>(bp + w * (16 / G::kSize));
+            v = *reinterpret_cast<const u32x4*>(bp + w * (16 / G::kSize));
+          }
+          if constexpr (kPL) {
+            plds[(UPT + k) * TPR + lane] = v;
           } else {
-            braw[k][w] = (u32x4){0u, 0u, 0u, 0u};
+            braw[k][w] = v;
           }
         }
       }
     }
   };
 
-  auto widen_gamma = [&](const u32x4* gw, float* g) {
+  auto widen_words = [&](const u32x4* gw, float* g) {
 #pragma unroll
     for (int w = 0; w < GW; ++w)
 #pragma unroll
       for (int q = 0; q < 4; ++q) G::widen_word(gw[w][q], g + w * (16 / G::kSize) + q * G::kPerWord);
+  };
+  // Gamma (and beta) of unit lane + k * TPR, widened.
+  auto widen_g = [&](int k, float* g) {
+    if constexpr (kPL) {
+      const u32x4 w = plds[k * TPR + lane];
+      widen_words(&w, g);
+    } else {
+      widen_words(graw[k], g);
+    }
+  };
+  [[maybe_unused]] auto widen_b = [&](int k, float* g) {
+    if constexpr (kPL) {
+      const u32x4 w = plds[(UPT + k) * TPR + lane];
+      widen_words(&w, g);
+    } else {
+      widen_words(braw[k], g);
+    }
   };
 
   // Byte offset of unit k of this group's row in the iteration starting at
@@ -430,13 +475,23 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
     const uint32_t n = span_bytes(row0);
     float part[UPT];
     // LayerNorm keeps the fp32 row for its variance and output passes (its
-    // one-group blocks leave VGPRs to spare).
-    [[maybe_unused]] float lv[LN ? UPT : 1][E];
+    // one-group blocks leave VGPRs to spare), except with four units of 1024
+    // lanes, where it widens the packed words again at each pass (exact).
+    constexpr bool kLv = LN && !(BLOCK == 1024 && UPT >= 4);
+    [[maybe_unused]] float lv[kLv ? UPT : 1][E];
+    auto row_unit = [&](int k, float (&o)[E]) {
+      if constexpr (kLv) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = lv[k][e];
+      } else {
+        U::widen(cx[k], o);
+      }
+    };
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       float v[E];
       prepare_unit<T, U, FUSED>(cx[k], cr[k], v);
-      if constexpr (LN) {
+      if constexpr (kLv) {
 #pragma unroll
         for (int e = 0; e < E; ++e) lv[k][e] = v[e];
       }
@@ -470,7 +525,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
     auto xg = [&](int k, float (&o)[E]) {
       float v[E], g[E];
       U::widen(cx[k], v);
-      widen_gamma(graw[k], g);
+      widen_g(k, g);
 #pragma unroll
       for (int e = 0; e < E; ++e) o[e] = v[e] * g[e];
     };
@@ -490,7 +545,7 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
           for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(o[e]));
         }
       }
-    } else if constexpr (!LN) {
+    } else if constexpr (!kLv) {
 #pragma unroll
       for (int k = 0; k < UPT; ++k) opaque(cx[k]);
     }
@@ -502,10 +557,11 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
       float sq = 0.0f;
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
-        float s = 0.0f;
+        float s = 0.0f, v[E];
+        row_unit(k, v);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float d = lv[k][e] - mu;
+          const float d = v[e] - mu;
           s = __builtin_fmaf(d, d, s);
         }
         sq = sq + (unit_offset(row0, k) != kBufOutOfRange ? s : 0.0f);
@@ -540,12 +596,13 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
 #pragma unroll
       for (int k = 0; k < UPT; ++k) {
         float v[E], g[E], o[E];
-        widen_gamma(graw[k], g);
+        widen_g(k, g);
         if constexpr (LN) {
           float bb[E];
-          widen_gamma(braw[k], bb);
+          widen_b(k, bb);
+          row_unit(k, v);
 #pragma unroll
-          for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf((lv[k][e] - mu) * rs, g[e], bb[e]);
+          for (int e = 0; e < E; ++e) o[e] = __builtin_fmaf((v[e] - mu) * rs, g[e], bb[e]);
         } else {
           U::widen(cx[k], v);
 #pragma unroll
@@ -626,12 +683,14 @@ __global__ __launch_bounds__(BLOCK) void fwd_pp_kernel(FwdArgs<T, G> a) {
   if constexpr (!kParamsAfterRows) load_params();
   load_rows(b, ax, ar);
   if constexpr (kParamsAfterRows) load_params();
+  if constexpr (!kPL) {
 #pragma unroll
-  for (int k = 0; k < UPT; ++k) {
+    for (int k = 0; k < UPT; ++k) {
 #pragma unroll
-    for (int w = 0; w < GW; ++w) {
-      opaque(graw[k][w]);
-      if constexpr (LN) opaque(braw[k][w]);
+      for (int w = 0; w < GW; ++w) {
+        opaque(graw[k][w]);
+        if constexpr (LN) opaque(braw[k][w]);
+      }
     }
   }
   // Trip counts are uniform over the block, so every thread reaches every
