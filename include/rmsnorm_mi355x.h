@@ -282,9 +282,10 @@ int layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y, f
                   int gamma_dtype, hipStream_t stream);
 
 /* Bytes of device workspace layernorm_bwd needs: two fp32 partial arrays
- * (dgamma, dbeta) of G rows each, G as for rmsnorm_bwd_workspace_size, and,
- * for rows longer than 8192, a 16-byte record per row. 0 for M <= 0, N <= 0
- * or N > RMSN_MAX_N. */
+ * (dgamma, dbeta) of G rows each, G as for rmsnorm_bwd_workspace_size
+ * except that T = ceil(2^22 / N) from N > 24576 on (where 16-bit LayerNorm
+ * rows take the two-pass tier), and, for rows longer than 8192, a 16-byte
+ * record per row. 0 for M <= 0, N <= 0 or N > RMSN_MAX_N. */
 size_t layernorm_bwd_workspace_size(int64_t M, int64_t N);
 
 /* LayerNorm backward. The pages give only the forward (FlyDSL guide, section
