@@ -43,7 +43,7 @@ hipError_t run_stage1(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s) {
 // dbeta sum per column too, fits 1024-thread blocks because it reads gamma
 // from LDS: at 8192 x 8192 bf16 stage 1 ran 70.5 us there against 74-77 us
 // with 512-thread blocks and gamma in registers.)
-template <class T, class G, bool RES, bool LN, bool VEC, int TPR, int UPT>
+template <class T, class G, bool RES, bool LN, bool VEC, int TPR, int UPT, bool PF = true>
 hipError_t run_stage1_rows(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s) {
   // Small groups use 256-thread blocks: with at most 64 rows per partial, a
   // 1024-thread block of 8..64 groups runs each group about once, with no
@@ -54,9 +54,9 @@ hipError_t run_stage1_rows(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s
   // LayerNorm there loses 5-12% and keeps 1024 threads.
   constexpr int kFull = TPR <= 64 || (TPR == 128 && !LN) ? 256 : 1024;
   if constexpr (TPR < kFull) {
-    if (a.M >= 2 * a.nblk) return run_stage1<T, G, RES, LN, VEC, TPR, UPT, kFull>(a, blocks, s);
+    if (a.M >= 2 * a.nblk) return run_stage1<T, G, RES, LN, VEC, TPR, UPT, kFull, PF>(a, blocks, s);
   }
-  return run_stage1<T, G, RES, LN, VEC, TPR, UPT, (TPR > 256 ? TPR : 256)>(a, blocks, s);
+  return run_stage1<T, G, RES, LN, VEC, TPR, UPT, (TPR > 256 ? TPR : 256), PF>(a, blocks, s);
 }
 
 // One-pass path: returns hipErrorNotSupported when the row does not fit.
@@ -100,6 +100,14 @@ hipError_t stage1_typed(const BwdArgs<T, G>& a, bool vec, int64_t blocks, hipStr
         if (t2 == 128) return run_stage1_rows<T, G, RES, LN, true, 64, 3>(a, blocks, s);
         return run_stage1_rows<T, G, RES, LN, true, 128, 3>(a, blocks, s);
       }
+    }
+    if constexpr (LN && T::kSize == 2) {
+      // 16-bit LayerNorm rows of 129..192 units (1032..1536 elements): 64
+      // lanes of three units without prefetch (256-thread blocks), which fits
+      // the registers, instead of 128 lanes of two (bf16 1536 at 64 MiB per
+      // operand 50.4-51.1 vs 59.9-60.8 us). Wider groups of three lost 8-16%
+      // (2560..12288 elements), spilling in 1024-thread blocks.
+      if (units > 128 && units <= 192) return run_stage1_rows<T, G, RES, LN, true, 64, 3, false>(a, blocks, s);
     }
     if (units > 1024) return run_stage1_rows<T, G, RES, LN, true, 1024, 2>(a, blocks, s);
     switch (next_pow2(ceil_div(units, 2))) {
