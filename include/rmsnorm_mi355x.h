@@ -194,7 +194,8 @@ int rmsnorm_qk_fwd(void* q, void* k, const void* q_gamma, const void* k_gamma,
  * take the two-pass tier, which runs column tiles x G workgroups), and for
  * N > 8192 a 16-byte record per row (rows longer than the one-pass kernel
  * holds keep their row dots there; rows of up to 4096 16-byte units --
- * 32768 16-bit / 16384 fp32 elements, 24576 for 16-bit LayerNorm -- stay
+ * 32768 16-bit / 16384 fp32 elements, 24576 for 16-bit LayerNorm with fp32
+ * gamma -- stay
  * one-pass and leave it unused). Pure host
  * function; returns 0 for M <= 0, N <= 0 or N > RMSN_MAX_N. */
 size_t rmsnorm_bwd_workspace_size(int64_t M, int64_t N);
@@ -282,10 +283,9 @@ int layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y, f
                   int gamma_dtype, hipStream_t stream);
 
 /* Bytes of device workspace layernorm_bwd needs: two fp32 partial arrays
- * (dgamma, dbeta) of G rows each, G as for rmsnorm_bwd_workspace_size
- * except that T = ceil(2^22 / N) from N > 24576 on (where 16-bit LayerNorm
- * rows take the two-pass tier), and, for rows longer than 8192, a 16-byte
- * record per row. 0 for M <= 0, N <= 0 or N > RMSN_MAX_N. */
+ * (dgamma, dbeta) of G rows each, G as for rmsnorm_bwd_workspace_size, and,
+ * for rows longer than 8192, a 16-byte record per row. 0 for M <= 0, N <= 0
+ * or N > RMSN_MAX_N. */
 size_t layernorm_bwd_workspace_size(int64_t M, int64_t N);
 
 /* LayerNorm backward. The pages give only the forward (FlyDSL guide, section

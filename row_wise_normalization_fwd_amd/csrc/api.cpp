@@ -391,24 +391,21 @@ hipError_t allow_dynamic_lds(const void* kernel, size_t bytes) {
 }
 
 BwdPlan plan_ln_bwd(int64_t M, int64_t N) {
-  BwdPlan p = plan_partition(M, N, kBwdLnLongN);
+  BwdPlan p = plan_bwd(M, N);
   if (!p.valid) return p;
   p.workspace_bytes = 2 * p.partial_bytes + (p.workspace_bytes - p.partial_bytes);
   return p;
 }
 
-BwdPlan plan_bwd(int64_t M, int64_t N) { return plan_partition(M, N, kBwdLongN); }
-
-BwdPlan plan_partition(int64_t M, int64_t N, int64_t long_n) {
+BwdPlan plan_bwd(int64_t M, int64_t N) {
   BwdPlan p{false, 0, 0, 0};
   if (M <= 0 || N <= 0 || !shape_ok(M, N)) return p;
   p.valid = true;
-  // min(M, 256) blocks (rows longer than long_n: enough for about
-  // kBwdLongTiles tiles), more when a block would own over
-  // kBwdMaxRowsPerBlock rows: every partial is then an fp32 sum of at most
-  // that many rows.
+  // min(M, 256) blocks (long rows: enough for about kBwdLongTiles tiles),
+  // more when a block would own over kBwdMaxRowsPerBlock rows: every partial
+  // is then an fp32 sum of at most that many rows.
   const int64_t target =
-      N > long_n ? ceil_div(kBwdLongTiles * kBwdTileCols, N) : kBwdTargetBlocks;
+      N > kBwdLongN ? ceil_div(kBwdLongTiles * kBwdTileCols, N) : kBwdTargetBlocks;
   p.blocks = M < target ? M : target;
   const int64_t by_rows = ceil_div(M, kBwdMaxRowsPerBlock);
   if (p.blocks < by_rows) p.blocks = by_rows;

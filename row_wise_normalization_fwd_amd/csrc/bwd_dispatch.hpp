@@ -23,10 +23,14 @@ template <class T, class G, bool RES, bool LN, bool VEC, int TPR, int UPT, int B
 hipError_t run_stage1(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s) {
   constexpr int RG = BLOCK / TPR;
   constexpr int E = Unit<T, VEC>::E;
-  // Row-group combine buffer, and LayerNorm's gamma copy aliased with it.
+  // Row-group combine buffer, and LayerNorm's gamma copy (or its dbeta sums)
+  // aliased with it.
   constexpr size_t kComb = RG > 1 ? static_cast<size_t>(BLOCK) * UPT * E * sizeof(float) : 0;
   constexpr size_t kGam =
-      stage1_gamma_in_lds<LN, UPT>() ? stage1_gamma_lds_bytes<TPR, UPT, E>() : 0;
+      stage1_gamma_in_lds<T, G, VEC, TPR, UPT, BLOCK, LN>() ||
+              stage1_dbeta_in_lds<T, G, VEC, TPR, UPT, BLOCK, LN>()
+          ? stage1_gamma_lds_bytes<TPR, UPT, E>()
+          : 0;
   constexpr size_t kLds = kComb > kGam ? kComb : kGam;
   constexpr auto kernel = bwd_stage1_kernel<T, G, VEC, TPR, UPT, BLOCK, RES, LN, PF>;
   if constexpr (kLds > 48 * 1024) {
@@ -73,16 +77,21 @@ hipError_t stage1_typed(const BwdArgs<T, G>& a, bool vec, int64_t blocks, hipStr
       // fits only three units without prefetch. The 16-bit LayerNorm kernel
       // spills 16-17 VGPRs even then, yet runs 14-21% faster than the
       // two-pass tier (bf16 2048 x 20480 78.5 vs 90.3 us, 2048 x 24576 85.2
-      // vs 99.4), so it takes three units too; with four it spills 84-93 and
-      // is 35% slower than that tier. The fused add with four units spills
-      // 12-14 and is 27-32% faster than it (2048 x 28672 101 vs 128 us,
-      // 2048 x 32768 110 vs 145.6).
+      // vs 99.4), so it takes three units too; with four it spilled 84-93 and
+      // was 35% slower than that tier. With 16-bit gamma it keeps its dbeta
+      // sums in LDS instead (stage1_dbeta_in_lds), spilling 8 VGPRs with
+      // three units and 15-17 with four, which beats the two-pass tier (bf16
+      // 1024 x 32768 66.3 vs 71.5 us, 1170 x 28672 68.6 vs 75.1) and the
+      // spilling three-unit shape (2048 x 16392 65.7 vs 73.1, 1365 x 24576
+      // 63.9 vs 68.4). The fused add with four units spills 12-14 and is
+      // 27-32% faster than that tier (2048 x 28672 101 vs 128 us, 2048 x
+      // 32768 110 vs 145.6).
       if constexpr (T::kSize == 4 || (!RES && !LN)) {
         if (units <= 3072) return run_stage1<T, G, RES, LN, true, 1024, 3, 1024, true>(a, blocks, s);
         if (units <= 4096) return run_stage1<T, G, RES, LN, true, 1024, 4, 1024, false>(a, blocks, s);
       } else {
         if (units <= 3072) return run_stage1<T, G, RES, LN, true, 1024, 3, 1024, false>(a, blocks, s);
-        if constexpr (RES) {
+        if constexpr (RES || (LN && G::kSize == 2)) {
           if (units <= 4096) return run_stage1<T, G, RES, LN, true, 1024, 4, 1024, false>(a, blocks, s);
         }
       }

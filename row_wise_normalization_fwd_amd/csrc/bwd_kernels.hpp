@@ -284,12 +284,21 @@ __device__ void rare_bwd_after(const BwdArgs<T, G>& a, uint64_t mine, int iters,
 // is reduced, so loads stay in flight across rows. With RG > 1 the groups'
 // partials are combined through LDS in group order before the block writes
 // its partial row.
-// Gamma is read from a widened copy in LDS (GL) by LayerNorm, and by the
-// RMSNorm kernels for rows of more than two units per lane, whose operands
-// leave no room for it in registers.
-template <bool LN, int UPT>
+// 16-bit LayerNorm rows of one 1024-lane group of four units (BL) keep their
+// dbeta sums in LDS (128 KiB, each thread's own slots) and gamma packed in 16
+// VGPRs: with both sum arrays and gamma's fp32 copy (the LDS it would take is
+// the dbeta sums' now) the shape spilled 84-93 bytes.
+template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool LN>
+constexpr bool stage1_dbeta_in_lds() {
+  return LN && VEC && TPR == BLOCK && BLOCK == 1024 && UPT >= 3 && T::kSize == 2 && G::kSize == 2;
+}
+
+// Gamma is read from a widened copy in LDS (GL) by LayerNorm (but BL rows),
+// and by the RMSNorm kernels for rows of more than two units per lane, whose
+// operands leave no room for it in registers.
+template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool LN>
 constexpr bool stage1_gamma_in_lds() {
-  return LN || UPT > 2;
+  return (LN || UPT > 2) && !stage1_dbeta_in_lds<T, G, VEC, TPR, UPT, BLOCK, LN>();
 }
 
 template <int TPR, int UPT, int E>
@@ -304,10 +313,12 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
   using Raw = typename U::Raw;
   constexpr int E = U::E;
   constexpr int RG = BLOCK / TPR;
-  constexpr bool GL = stage1_gamma_in_lds<LN, UPT>();
+  constexpr bool BL = stage1_dbeta_in_lds<T, G, VEC, TPR, UPT, BLOCK, LN>();
+  constexpr bool GL = stage1_gamma_in_lds<T, G, VEC, TPR, UPT, BLOCK, LN>();
   constexpr int COLS = TPR * UPT * E;  // columns covered by one row group
   static_assert(BLOCK % TPR == 0 && BLOCK % kWave == 0, "block shape");
   static_assert(!(LN && RES), "LayerNorm backward has no residual input");
+  static_assert(!stage1_dbeta_in_lds<T, G, VEC, TPR, UPT, BLOCK, LN>() || U::E == 8, "BL: 8-element units");
   using Red = typename std::conditional<LN, DSum2, double>::type;
   __shared__ Red red[2 * (BLOCK / kWave)];
   __shared__ double rared[LN ? 1 : 2 * (BLOCK / kWave)];  // rare rows (after the loop)
@@ -365,13 +376,20 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
     }
   };
 
-  [[maybe_unused]] float gam[GL ? 1 : UPT][E];
+  [[maybe_unused]] float gam[GL || BL ? 1 : UPT][E];
+  [[maybe_unused]] u32x4 gpk[BL ? UPT : 1];  // BL: gamma, packed
   float acc[UPT][E];
-  [[maybe_unused]] float accb[LN ? UPT : 1][E];  // LayerNorm dbeta partial sums
+  [[maybe_unused]] float accb[LN && !BL ? UPT : 1][E];  // LayerNorm dbeta partial sums
+  // BL: the dbeta sums of unit lane + k * TPR, elements 4h..4h+3, at float4
+  // (k * 2 + h) * TPR + lane (consecutive lanes on consecutive 16-byte words).
+  [[maybe_unused]] float4* const bsum = reinterpret_cast<float4*>(lds_bytes);
 #pragma unroll
   for (int k = 0; k < UPT; ++k) {
     const int u = lane + k * TPR;
-    if constexpr (!GL) {
+    if constexpr (BL) {
+      gpk[k] = u < nunits ? *reinterpret_cast<const u32x4*>(a.gamma + u * E)
+                          : (u32x4){0u, 0u, 0u, 0u};
+    } else if constexpr (!GL) {
       if (u < nunits) {
         load_gamma<G, E, VEC>(a.gamma, u * E, gam[k]);
       } else {
@@ -381,11 +399,23 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[k][e] = 0.0f;
-    if constexpr (LN) {
+    if constexpr (BL) {
+      bsum[(k * 2 + 0) * TPR + lane] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      bsum[(k * 2 + 1) * TPR + lane] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    } else if constexpr (LN) {
 #pragma unroll
       for (int e = 0; e < E; ++e) accb[k][e] = 0.0f;
     }
   }
+  // LayerNorm's gamma for unit lane + k * TPR, widened.
+  [[maybe_unused]] auto gamma_ln = [&](int k, float* g) {
+    if constexpr (BL) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) G::widen_word(gpk[k][w], g + w * G::kPerWord);
+    } else {
+      gamma_lds(lane + k * TPR, g);
+    }
+  };
 
   // Rows handled in one iteration: row0 + nblk * g for the RG groups g. In
   // the vector case the iteration's operands are reached through buffer
@@ -470,6 +500,10 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
       load_row(row0, cx, cdy, cr);
     }
 
+    if constexpr (BL) {  // widen gamma at each use, not once for the loop
+#pragma unroll
+      for (int k = 0; k < UPT; ++k) opaque(gpk[k]);
+    }
     [[maybe_unused]] double dot = 0.0;
     [[maybe_unused]] DSum2 dots{0.0, 0.0};
 #pragma unroll
@@ -479,7 +513,7 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
       U::widen(cdy[k], dyv);
       if constexpr (LN) {
         float s1, s2, g[E];
-        gamma_lds(lane + k * TPR, g);
+        gamma_ln(k, g);
         unit_dots_ln<E>(dyv, g, xv, mu, rho, s1, s2);
         dots = dots + DSum2{static_cast<double>(s1), static_cast<double>(s2)};
       } else if constexpr (GL) {
@@ -524,13 +558,23 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
       U::widen(cdy[k], dyv);
       if constexpr (LN) {
         float g[E];
-        gamma_lds(u, g);
+        gamma_ln(k, g);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float xh = (xv[e] - mu) * rho;
           o[e] = rho * (__builtin_fmaf(-xh, c2, g[e] * dyv[e]) - c1);
           acc[k][e] = __builtin_fmaf(dyv[e], xh, acc[k][e]);
-          accb[k][e] = accb[k][e] + dyv[e];
+        }
+        if constexpr (BL) {
+          float4* const p = bsum + (k * 2) * TPR + lane;
+          float4 lo = p[0], hi = p[TPR];
+          lo.x = lo.x + dyv[0]; lo.y = lo.y + dyv[1]; lo.z = lo.z + dyv[2]; lo.w = lo.w + dyv[3];
+          hi.x = hi.x + dyv[4]; hi.y = hi.y + dyv[5]; hi.z = hi.z + dyv[6]; hi.w = hi.w + dyv[7];
+          p[0] = lo;
+          p[TPR] = hi;
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) accb[k][e] = accb[k][e] + dyv[e];
         }
       } else {
         float g[E];
@@ -616,7 +660,17 @@ __global__ __launch_bounds__(BLOCK) void bwd_stage1_kernel(BwdArgs<T, G> a) {
     }
   };
   write_partial(a.partial, acc);
-  if constexpr (LN) write_partial(a.partial_b, accb);
+  if constexpr (BL) {
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const float4 lo = bsum[(k * 2) * TPR + lane], hi = bsum[(k * 2 + 1) * TPR + lane];
+      acc[k][0] = lo.x; acc[k][1] = lo.y; acc[k][2] = lo.z; acc[k][3] = lo.w;
+      acc[k][4] = hi.x; acc[k][5] = hi.y; acc[k][6] = hi.z; acc[k][7] = hi.w;
+    }
+    write_partial(a.partial_b, acc);
+  } else if constexpr (LN) {
+    write_partial(a.partial_b, accb);
+  }
 }
 
 // Long rows (rows too long for stage 1's registers), in two passes.

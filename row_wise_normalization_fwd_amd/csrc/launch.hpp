@@ -100,7 +100,7 @@ hipError_t launch_qk(const QKCall& c, int x_dtype);
 
 // Backward partition: G blocks, block b owning rows b, b + G, b + 2G, ...,
 // each writing one fp32 partial row of dgamma (and dbeta). Rows of up to
-// kBwdLongN elements (LayerNorm: kBwdLnLongN): G = max(min(M, kBwdTargetBlocks), ceil(M /
+// kBwdLongN elements: G = max(min(M, kBwdTargetBlocks), ceil(M /
 // kBwdMaxRowsPerBlock)), one stage-1 block per partial row (when the row
 // takes the one-pass kernel). Longer rows
 // always take the two-pass long-row tier, whose tile pass runs (column tiles
@@ -119,10 +119,8 @@ struct BwdPlan {
 };
 BwdPlan plan_bwd(int64_t M, int64_t N);
 // LayerNorm: two partial arrays (dgamma, dbeta), then the same per-row
-// records; the long-row partition from kBwdLnLongN elements on.
+// records.
 BwdPlan plan_ln_bwd(int64_t M, int64_t N);
-// The partition with the long-row target for rows longer than long_n.
-BwdPlan plan_partition(int64_t M, int64_t N, int64_t long_n);
 
 constexpr int64_t kBwdTargetBlocks = 256;
 // Rows per partition block at most: each dgamma partial is an fp32 sum of
@@ -136,10 +134,6 @@ constexpr int64_t kBwdOnChipN = 8192;
 // operation (4096 16-byte units: 32768 16-bit elements is the longest
 // one-pass row).
 constexpr int64_t kBwdLongN = 32768;
-// LayerNorm's 16-bit rows take the long-row tier beyond this many elements
-// (its one-pass limit), so its partition follows that tier from there on:
-// 1024 x 32768 bf16 71.8 vs 81.2 us with 128 partial rows instead of 256.
-constexpr int64_t kBwdLnLongN = 24576;
 // The long-row tier's tile pass: at most this many elements per column tile
 // (256 lanes x 2 units of 8 16-bit elements), and about this many blocks.
 constexpr int64_t kBwdTileCols = 4096;

@@ -157,12 +157,11 @@ def check_column_sum(name: str, got: np.ndarray, o: np.ndarray, mag: np.ndarray,
     return float(np.linalg.norm(got - o) / max(np.linalg.norm(o), 1e-300))
 
 
-def partition_blocks(M: int, N: int, layernorm: bool = False) -> int:
+def partition_blocks(M: int, N: int) -> int:
     """Backward partition blocks G for M rows of N: min(M, T) with T = 256,
-    or ceil(2^22 / N) for rows longer than 32768 (LayerNorm: 24576; the
-    long-row tier's tiles), more when a block would own over 64 rows (the
-    library's rule, restated)."""
-    target = 256 if N <= (24576 if layernorm else 32768) else -(-(1 << 22) // N)
+    or ceil(2^22 / N) for rows longer than 32768 (the long-row tier's tiles),
+    more when a block would own over 64 rows (the library's rule, restated)."""
+    target = 256 if N <= 32768 else -(-(1 << 22) // N)
     return max(min(M, target), -(-M // 64))
 
 
@@ -262,7 +261,7 @@ def check_layernorm_bwd(got_dx, got_dg, got_db, ref, x, dy, gamma, mean, rstd, d
         idx = np.unravel_index(int(np.argmax(bad)), bad.shape)
         raise AssertionError(f"layernorm dx: {int(bad.sum())} out of tolerance; first at {idx}: "
                              f"got {gotv[idx]!r}, exact {exact[idx]!r}, floor {floor[idx]!r}")
-    R = -(-M // partition_blocks(M, N, layernorm=True))  # rows per partition block
+    R = -(-M // partition_blocks(M, N))  # rows per partition block
     for name, got, o, mag, k in (("dgamma", got_dg, ref["dgamma"], ref["sg"], 3 + R),
                                  ("dbeta", got_db, ref["dbeta"], ref["sb"], 1 + R)):
         if got is not None:

@@ -326,12 +326,11 @@ def test_layernorm_workspace_size():
     assert R.layernorm_bwd_workspace_size(3, 10) == 2 * 256
     assert R.layernorm_bwd_workspace_size(1000, 10000) == 2 * 256 * 10000 * 4 + 16128
     assert R.layernorm_bwd_workspace_size(131072, 1024) == 2 * 2048 * 1024 * 4
-    # From 24577 elements LayerNorm partitions as the long-row tier does:
-    # ceil(2^22 / N) partial rows (128 at 32768, 171 at 24584), 256 up to
-    # 24576; RMSNorm keeps 256 up to 32768.
-    assert R.layernorm_bwd_workspace_size(1024, 24576) == 2 * 256 * 24576 * 4 + 1024 * 16
-    assert R.layernorm_bwd_workspace_size(1024, 24584) == 2 * (171 * 24584 * 4 + 160) + 1024 * 16
-    assert R.layernorm_bwd_workspace_size(1024, 32768) == 2 * 128 * 32768 * 4 + 1024 * 16
+    # LayerNorm partitions as RMSNorm does: 256 partial rows up to 32768
+    # elements, ceil(2^22 / N) beyond (128 at 32776).
+    assert R.layernorm_bwd_workspace_size(1024, 24584) == 2 * 256 * 24584 * 4 + 1024 * 16
+    assert R.layernorm_bwd_workspace_size(1024, 32768) == 2 * 256 * 32768 * 4 + 1024 * 16
+    assert R.layernorm_bwd_workspace_size(1024, 32776) == 2 * (128 * 32776 * 4) + 1024 * 16
     assert R.rmsnorm_bwd_workspace_size(1024, 32768) == 256 * 32768 * 4 + 1024 * 16
     assert R.layernorm_bwd_workspace_size(0, 10) == 0
 

@@ -261,7 +261,7 @@ def test_maxsize_layernorm_backward():
                         rstd[src], xdt)
     col = _period_sum(lambda k: O.layernorm_bwd(dy[:k], x[:k], mean[:k], rstd[:k], g, k, N, xdt,
                                                 gdt, want_exact=False), M)
-    Rp = -(-M // partition_blocks(M, N, layernorm=True))
+    Rp = -(-M // partition_blocks(M, N))
     check_column_sum("layernorm dgamma", to_host(dgt), col("dgamma"), col("sg"), 3 + Rp)
     check_column_sum("layernorm dbeta", to_host(dbt), col("dbeta"), col("sb"), 1 + Rp)
 
