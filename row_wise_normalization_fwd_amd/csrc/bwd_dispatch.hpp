@@ -115,8 +115,15 @@ hipError_t stage1_typed(const BwdArgs<T, G>& a, bool vec, int64_t blocks, hipStr
       // lanes of three units without prefetch (256-thread blocks), which fits
       // the registers, instead of 128 lanes of two (bf16 1536 at 64 MiB per
       // operand 50.4-51.1 vs 59.9-60.8 us). Wider groups of three lost 8-16%
-      // (2560..12288 elements), spilling in 1024-thread blocks.
+      // (2560..12288 elements), spilling in 1024-thread blocks. Groups of 16
+      // or 32 lanes of three take rows that fill at least 15/16 of their
+      // units (384 elements 47.8-48.2 vs 50.5-51.0 us, 768 41.9 vs 46.4-46.5);
+      // rows that fill fewer were as fast or slower (344: 65.3-65.7 either
+      // way, 680: 60.2 vs 58.0-59.4, 264: 79.9 vs 74.2, 520: 60.4 vs 57.5), and 128
+      // lanes of three lost 22-26% even in 256-thread blocks.
       if (units > 128 && units <= 192) return run_stage1_rows<T, G, RES, LN, true, 64, 3, false>(a, blocks, s);
+      if (units >= 45 && units <= 48) return run_stage1_rows<T, G, RES, LN, true, 16, 3, false>(a, blocks, s);
+      if (units >= 90 && units <= 96) return run_stage1_rows<T, G, RES, LN, true, 32, 3, false>(a, blocks, s);
     }
     if (units > 1024) return run_stage1_rows<T, G, RES, LN, true, 1024, 2>(a, blocks, s);
     switch (next_pow2(ceil_div(units, 2))) {

@@ -773,8 +773,8 @@ def run_ln_bwd(M, N, xdt, gdt, seed=31, misalign=0, alias=None, gpu_stats=False,
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
-@pytest.mark.parametrize("N", [1, 7, 8, 64, 1000, 1032, 1280, 1536, 2047, 4096, 5000, 8192, 8193,
-                               12288, 16384, 20000, 24576, 24584, 32768])
+@pytest.mark.parametrize("N", [1, 7, 8, 64, 344, 360, 384, 680, 720, 768, 1000, 1032, 1280, 1536, 2047, 4096,
+                               5000, 8192, 8193, 12288, 16384, 20000, 24576, 24584, 32768])
 def test_layernorm_bwd_sweep(N, pair):
     run_ln_bwd(3, N, *pair, seed=2100 + N, dbeta=(N % 2 == 0))
     run_ln_bwd(300, N, *pair, seed=2200 + N)
