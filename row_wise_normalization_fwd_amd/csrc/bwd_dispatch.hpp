@@ -55,8 +55,13 @@ hipError_t run_stage1_rows(const BwdArgs<T, G>& a, int64_t blocks, hipStream_t s
   // CU. Measured on bf16 at 64 MiB per operand: groups of up to 64 lanes
   // (256..1024 elements) RMSNorm 4-13% faster, fused add 2-11%, LayerNorm
   // 4-31%; 128-lane groups (1536..3072) RMSNorm and fused add up to 9%, while
-  // LayerNorm there loses 5-12% and keeps 1024 threads.
-  constexpr int kFull = TPR <= 64 || (TPR == 128 && !LN) ? 256 : 1024;
+  // LayerNorm there loses 5-12% and keeps 1024 threads. 16-bit groups of 16
+  // or 32 lanes take 128-thread blocks, eight or sixteen rows per group
+  // (256 elements: 48.2 vs 51.9 us, fused add 60.5 vs 67.4, LayerNorm 50.3
+  // vs 53.8; 512: 1-3.5% faster); 8- and 64-lane groups lost 5-31% there.
+  constexpr int kFull = T::kSize == 2 && (TPR == 16 || TPR == 32)  ? 128
+                        : TPR <= 64 || (TPR == 128 && !LN)         ? 256
+                                                                   : 1024;
   if constexpr (TPR < kFull) {
     if (a.M >= 2 * a.nblk) return run_stage1<T, G, RES, LN, VEC, TPR, UPT, kFull, PF>(a, blocks, s);
   }

@@ -862,6 +862,16 @@ def test_bwd_row_partitions(M):
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("M,N", [(5000, 136), (3000, 192), (2000, 256), (1000, 384), (1200, 512)])
+def test_bwd_narrow_rows_many_per_block(M, N, pair):
+    """Narrow rows with M >= 2G: several row groups per stage-1 block, each
+    taking several rows of its partial."""
+    run_bwd(M, N, *pair, seed=M + N)
+    run_fused_bwd(M, N, *pair, seed=M + N + 1)
+    run_ln_bwd(M, N, *pair, seed=M + N + 2)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
 def test_bwd_misaligned_and_aliased(pair):
     run_bwd(9, 4096, *pair, seed=61, misalign=1)
     run_bwd(9, 4096, *pair, seed=62, alias="dy")
