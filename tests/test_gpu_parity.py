@@ -862,10 +862,12 @@ def test_bwd_row_partitions(M):
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
-@pytest.mark.parametrize("M,N", [(5000, 136), (3000, 192), (2000, 256), (1000, 384), (1200, 512)])
+@pytest.mark.parametrize("M,N", [(5000, 136), (3000, 192), (2000, 256), (1000, 384), (1200, 512),
+                                 (20000, 256), (17000, 1000)])
 def test_bwd_narrow_rows_many_per_block(M, N, pair):
     """Narrow rows with M >= 2G: several row groups per stage-1 block, each
-    taking several rows of its partial."""
+    taking several rows of its partial; M > 16384 gives over 256 partial rows
+    (stage 2's 64-slice form)."""
     run_bwd(M, N, *pair, seed=M + N)
     run_fused_bwd(M, N, *pair, seed=M + N + 1)
     run_ln_bwd(M, N, *pair, seed=M + N + 2)
