@@ -222,9 +222,14 @@ hipError_t fwd_typed(const FwdCall& c) {
             return run_fwd_pp<T, G, 128, 4, 256, FUSED, OUT, LN>(a, s);
           }
         }
-        if (tp >= 64 && tp <= 256 && (LN || th)) {
+        // LayerNorm's three-unit shapes of 16 and 32 lanes too (384 elements
+        // 27.4 vs 28.9 us, 640 26.1 vs 31.5, 768 25.4 vs 27.8); its two-unit
+        // shapes there lost 5-7% (256, 512) and stay on the register kernel.
+        if (tp >= (LN && th ? 16 : 64) && tp <= 256 && (LN || th)) {
           if (th) {
             switch (tp) {
+              case 16: return run_fwd_pp<T, G, 16, 3, 256, FUSED, OUT, LN>(a, s);
+              case 32: return run_fwd_pp<T, G, 32, 3, 256, FUSED, OUT, LN>(a, s);
               case 64: return run_fwd_pp<T, G, 64, 3, 256, FUSED, OUT, LN>(a, s);
               case 128: return run_fwd_pp<T, G, 128, 3, 256, FUSED, OUT, LN>(a, s);
               default: return run_fwd_pp<T, G, 256, 3, 256, FUSED, OUT, LN>(a, s);

@@ -705,9 +705,9 @@ def run_ln(M, N, xdt, gdt, seed=29, eps=1e-5, with_beta=True, stats=True, misali
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
-@pytest.mark.parametrize("N", [1, 7, 8, 64, 384, 1000, 1536, 2048, 3072, 4096, 5000, 6144, 6152,
-                               8191, 8192, 8193, 8200, 10240, 12288, 12296, 16384, 20000, 24576,
-                               26000, 28672, 32768])
+@pytest.mark.parametrize("N", [1, 7, 8, 64, 264, 384, 520, 640, 768, 1000, 1536, 2048, 3072, 4096,
+                               5000, 6144, 6152, 8191, 8192, 8193, 8200, 10240, 12288, 12296, 16384,
+                               20000, 24576, 26000, 28672, 32768])
 def test_layernorm_sweep(N, pair):
     run_ln(5, N, *pair, seed=1800 + N, with_beta=(N % 2 == 0), stats=(N % 3 != 0))
     run_ln(300, N, *pair, seed=1900 + N)
