@@ -213,11 +213,15 @@ hipError_t fwd_typed(const FwdCall& c) {
         const bool th = t2 >= 8 && units <= 3 * (t2 / 2);
         const int64_t tp = th ? t2 / 2 : t2;
         if constexpr (!LN) {
-          // fp8 / MX rows of a two-unit shape on 128 or 256 lanes: four units
-          // on half the lanes of the persistent kernel (MXFP4 2048 / 3584 /
-          // 4096 elements 10-13% faster, fp8 0.4 / 3 / 8%; the register
-          // kernel with four units lost 4-11%).
-          if (!th && (tp == 128 || tp == 256)) {
+          // fp8 / MX rows of a two-unit shape on 64, 128 or 256 lanes: four
+          // units on half the lanes of the persistent kernel (MXFP4 2048 /
+          // 3584 / 4096 elements 10-13% faster, fp8 0.4 / 3 / 8%; the
+          // register kernel with four units lost 4-11%; at 1024 elements and
+          // 64 MiB per operand fp8 per-row 7.8%, MXFP4 10.9%, MXFP8 6.9%,
+          // within 1% or better at 16 MiB). 16 and 32 lanes (256, 512
+          // elements) lost 2-29% that way.
+          if (!th && (tp == 64 || tp == 128 || tp == 256)) {
+            if (tp == 64) return run_fwd_pp<T, G, 32, 4, 256, FUSED, OUT, LN>(a, s);
             if (tp == 128) return run_fwd_pp<T, G, 64, 4, 256, FUSED, OUT, LN>(a, s);
             return run_fwd_pp<T, G, 128, 4, 256, FUSED, OUT, LN>(a, s);
           }

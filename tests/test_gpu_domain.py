@@ -273,7 +273,7 @@ def test_fused_domain(N, pair):
 
 # ------------------------------------------------------- quantised outputs
 
-@pytest.mark.parametrize("N", [2048, 3072, 4096, 8192, 10240, 16384, 20000, 28672, 32768])
+@pytest.mark.parametrize("N", [1000, 2048, 3072, 4096, 8192, 10240, 16384, 20000, 28672, 32768])
 @pytest.mark.parametrize("mode", [O.QUANT_TENSOR, O.QUANT_ROW], ids=["tensor", "row"])
 def test_fp8_domain(mode, N):
     M, xdt, gdt = (2100 if N == 8192 else 70), O.BF16, O.BF16
@@ -298,7 +298,7 @@ def test_fp8_domain(mode, N):
         check_rstd(to_host(rt), ref["rstd"].astype(np.float64))
 
 
-@pytest.mark.parametrize("N", [1536, 2048, 4096, 6144, 8192, 10240, 16384, 20000, 32768])
+@pytest.mark.parametrize("N", [1024, 1536, 2048, 4096, 6144, 8192, 10240, 16384, 20000, 32768])
 @pytest.mark.parametrize("elem", [O.E4M3, O.E2M1], ids=["mxfp8", "mxfp4"])
 def test_mx_domain(elem, N):
     M, xdt, gdt = (2100 if N == 8192 else 70), O.BF16, O.BF16

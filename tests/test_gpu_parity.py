@@ -526,7 +526,7 @@ def run_mx(M, N, xdt, gdt, elem, seed=37, fused=False, want_rstd=False, q_off=0,
 
 @pytest.mark.parametrize("elem", [O.E4M3, O.E2M1], ids=["mxfp8", "mxfp4"])
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
-@pytest.mark.parametrize("N", [32, 64, 96, 768, 1024, 1536, 3072, 4096, 5024, 6144, 8192, 8224,
+@pytest.mark.parametrize("N", [32, 64, 96, 768, 800, 1024, 1536, 3072, 4096, 5024, 6144, 8192, 8224,
                                10240, 12288, 12320, 16384, 20000, 24576, 28000, 32768])
 def test_mx_sweep(N, pair, elem):
     run_mx(5, N, *pair, elem, seed=2500 + N, want_rstd=True)
