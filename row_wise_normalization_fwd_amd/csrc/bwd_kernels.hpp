@@ -284,10 +284,11 @@ __device__ void rare_bwd_after(const BwdArgs<T, G>& a, uint64_t mine, int iters,
 // is reduced, so loads stay in flight across rows. With RG > 1 the groups'
 // partials are combined through LDS in group order before the block writes
 // its partial row.
-// 16-bit LayerNorm rows of one 1024-lane group of four units (BL) keep their
-// dbeta sums in LDS (128 KiB, each thread's own slots) and gamma packed in 16
-// VGPRs: with both sum arrays and gamma's fp32 copy (the LDS it would take is
-// the dbeta sums' now) the shape spilled 84-93 bytes.
+// 16-bit LayerNorm rows of one 1024-lane group of three or four units (BL)
+// keep their dbeta sums in LDS (96 or 128 KiB, each thread's own slots) and
+// gamma packed in registers: with both sum arrays in registers and gamma's
+// fp32 copy in LDS (the space the dbeta sums take now) four units spilled
+// 84-93 bytes and three 64-68.
 template <class T, class G, bool VEC, int TPR, int UPT, int BLOCK, bool LN>
 constexpr bool stage1_dbeta_in_lds() {
   return LN && VEC && TPR == BLOCK && BLOCK == 1024 && UPT >= 3 && T::kSize == 2 && G::kSize == 2;
